@@ -1,0 +1,397 @@
+/*
+ * pa_ref.c — CPU oracle (fp64) for paged-attention decode.  TEST INFRASTRUCTURE ONLY.
+ * What each function follows is stated in pa_ref.h; this file is plain C99 + pthreads.
+ *
+ * Parity pins (tests/test_oracle_*.py): the pages' block-table example, dense attention
+ * (a separate routine fed with unpaged keys), torch's scaled_dot_product_attention in
+ * fp64, closed forms, physical-block permutation and prefix-sharing invariances, the
+ * partition merge, and NaN poison in every slot the method must not read.
+ */
+#define _GNU_SOURCE
+#include "pa_ref.h"
+
+#include <math.h>
+#include <pthread.h>
+#include <stdlib.h>
+#include <string.h>
+#include <unistd.h>
+
+static int elem_bytes(int32_t dtype) { return dtype == PA_REF_F32 ? 4 : 2; }
+
+/* ---------------------------------------------------------------- element conversion */
+
+/* IEEE binary16: 1 sign, 5 exponent (bias 15), 10 fraction bits. */
+static double f16_bits_to_double(uint16_t h) {
+  int sign = h >> 15, e = (h >> 10) & 0x1f, m = h & 0x3ff;
+  double v;
+  if (e == 0)
+    v = ldexp((double)m, -24); /* subnormal: m * 2^-24 */
+  else if (e == 31)
+    v = m ? NAN : INFINITY;
+  else
+    v = ldexp((double)(m | 0x400), e - 25); /* (1.m) * 2^(e-15) = (1024+m) * 2^(e-25) */
+  return sign ? -v : v;
+}
+
+/* bfloat16 is the upper half of an IEEE binary32. */
+static double bf16_bits_to_double(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+static double load_elem(const void* base, int32_t dtype, int64_t idx) {
+  if (dtype == PA_REF_F32) {
+    float f;
+    memcpy(&f, (const char*)base + 4 * idx, 4);
+    return (double)f;
+  }
+  uint16_t h;
+  memcpy(&h, (const char*)base + 2 * idx, 2);
+  return dtype == PA_REF_F16 ? f16_bits_to_double(h) : bf16_bits_to_double(h);
+}
+
+void pa_ref_to_double(const void* src, int32_t dtype, int64_t n, double* dst) {
+  for (int64_t i = 0; i < n; ++i) dst[i] = load_elem(src, dtype, i);
+}
+
+/* ---------------------------------------------------------------- pool layout */
+
+int64_t pa_ref_k_offset(const pa_ref_geom* g, int64_t block, int32_t kv_head, int32_t token,
+                        int32_t dim) {
+  const int64_t x = 16 / elem_bytes(g->dtype);
+  const int64_t chunks = g->head_dim / x;
+  return (((block * g->num_kv_heads + kv_head) * chunks + dim / x) * g->block_size + token) * x +
+         dim % x;
+}
+
+int64_t pa_ref_v_offset(const pa_ref_geom* g, int64_t block, int32_t kv_head, int32_t token,
+                        int32_t dim) {
+  return ((block * g->num_kv_heads + kv_head) * (int64_t)g->head_dim + dim) * g->block_size +
+         token;
+}
+
+static int geom_ok(const pa_ref_geom* g) {
+  if (!g || g->num_seqs < 0 || g->num_q_heads <= 0 || g->num_kv_heads <= 0 || g->head_dim <= 0 ||
+      g->block_size <= 0 || g->num_blocks <= 0 || g->max_blocks_per_seq < 0)
+    return 0;
+  if (g->dtype < PA_REF_F32 || g->dtype > PA_REF_BF16) return 0;
+  if (g->num_q_heads % g->num_kv_heads) return 0;
+  if (g->head_dim % (16 / elem_bytes(g->dtype))) return 0;
+  return 1;
+}
+
+/* ---------------------------------------------------------------- reshape_and_cache */
+
+int32_t pa_ref_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                                 const int64_t* slot_mapping, int64_t num_tokens,
+                                 const pa_ref_geom* g) {
+  if (!geom_ok(g) || num_tokens < 0) return -1;
+  const int e = elem_bytes(g->dtype);
+  const int64_t pool_slots = (int64_t)g->num_blocks * g->block_size;
+  for (int64_t i = 0; i < num_tokens; ++i) {
+    const int64_t slot = slot_mapping[i];
+    if (slot < 0) continue; /* padding token */
+    if (slot >= pool_slots) return -1;
+    const int64_t block = slot / g->block_size;
+    const int32_t offset = (int32_t)(slot % g->block_size);
+    for (int32_t h = 0; h < g->num_kv_heads; ++h) {
+      for (int32_t d = 0; d < g->head_dim; ++d) {
+        const int64_t src = (i * g->num_kv_heads + h) * (int64_t)g->head_dim + d;
+        memcpy((char*)k_cache + e * pa_ref_k_offset(g, block, h, offset, d),
+               (const char*)key + e * src, e);
+        memcpy((char*)v_cache + e * pa_ref_v_offset(g, block, h, offset, d),
+               (const char*)value + e * src, e);
+      }
+    }
+  }
+  return 0;
+}
+
+/* ---------------------------------------------------------------- row bookkeeping */
+
+typedef struct {
+  int32_t seq;      /* sequence the row belongs to */
+  int32_t last_key; /* highest visible key position (-1: no keys) */
+} row_info;
+
+static int find_row(const int32_t* context_lens, const int32_t* qsl, int32_t num_seqs,
+                    int32_t num_q_rows, int32_t r, row_info* out) {
+  if (r < 0 || r >= num_q_rows) return -1;
+  int32_t s, n, j;
+  if (qsl == NULL) {
+    if (r >= num_seqs) return -1;
+    s = r;
+    n = 1;
+    j = 0;
+  } else {
+    s = -1;
+    for (int32_t t = 0; t < num_seqs; ++t)
+      if (qsl[t] <= r && r < qsl[t + 1]) {
+        s = t;
+        break;
+      }
+    if (s < 0) return -1;
+    n = qsl[s + 1] - qsl[s];
+    j = r - qsl[s];
+  }
+  const int32_t ctx = context_lens[s];
+  if (ctx < 0) return -1;
+  out->seq = s;
+  /* The n rows of this step are the last n positions of the context: row j sits at
+   * ctx - n + j and sees keys [0, ctx - n + j].  A negative position sees no key. */
+  out->last_key = ctx - n + j;
+  return 0;
+}
+
+/* Keys [t0, t1) of sequence s, KV head kvh: scores x[t - t0] = scale * q . k_t. */
+static void scores(double* x, const double* qv, const void* k_cache, const int32_t* bt_row,
+                   int32_t kvh, int32_t t0, int32_t t1, double scale, const pa_ref_geom* g) {
+  for (int32_t t = t0; t < t1; ++t) {
+    const int64_t block = bt_row[t / g->block_size]; /* logical block -> physical block */
+    const int32_t off = t % g->block_size;
+    double dot = 0.0;
+    for (int32_t d = 0; d < g->head_dim; ++d)
+      dot += qv[d] * load_elem(k_cache, g->dtype, pa_ref_k_offset(g, block, kvh, off, d));
+    x[t - t0] = scale * dot;
+  }
+}
+
+/* Softmax over x[0..n) (max-subtracted, two passes) and the weighted sum of V rows. */
+static void softmax_v(double* out, double* m_out, double* l_out, const double* x, double* w,
+                      const void* v_cache, const int32_t* bt_row, int32_t kvh, int32_t t0,
+                      int32_t n, const pa_ref_geom* g) {
+  const int32_t D = g->head_dim;
+  for (int32_t d = 0; d < D; ++d) out[d] = 0.0;
+  if (n <= 0) {
+    *m_out = -INFINITY;
+    *l_out = 0.0;
+    return;
+  }
+  double m = x[0];
+  for (int32_t i = 1; i < n; ++i)
+    if (x[i] > m) m = x[i];
+  double l = 0.0;
+  for (int32_t i = 0; i < n; ++i) {
+    w[i] = exp(x[i] - m);
+    l += w[i];
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t t = t0 + i;
+    const int64_t block = bt_row[t / g->block_size];
+    const int32_t off = t % g->block_size;
+    for (int32_t d = 0; d < D; ++d)
+      out[d] += w[i] * load_elem(v_cache, g->dtype, pa_ref_v_offset(g, block, kvh, off, d));
+  }
+  for (int32_t d = 0; d < D; ++d) out[d] /= l;
+  *m_out = m;
+  *l_out = l;
+}
+
+/* ---------------------------------------------------------------- threaded driver */
+
+typedef struct {
+  /* inputs */
+  const void *q, *k_cache, *v_cache;
+  const int32_t *block_tables, *context_lens, *qsl, *rows;
+  int32_t num_q_rows, num_sel;
+  double scale;
+  const pa_ref_geom* g;
+  int32_t partition_size, max_partitions; /* partition_size <= 0: whole context */
+  /* outputs */
+  double *out, *lse, *o_part, *m_part, *l_part;
+  /* work split */
+  int32_t tid, nthreads;
+  int32_t status;
+} job;
+
+static void* run_job(void* arg) {
+  job* J = (job*)arg;
+  const pa_ref_geom* g = J->g;
+  const int32_t D = g->head_dim, Hq = g->num_q_heads, grp = g->num_q_heads / g->num_kv_heads;
+  const int32_t max_keys = g->max_blocks_per_seq * g->block_size;
+  double* qv = (double*)malloc(sizeof(double) * D);
+  double* x = (double*)malloc(sizeof(double) * (max_keys > 0 ? max_keys : 1));
+  double* w = (double*)malloc(sizeof(double) * (max_keys > 0 ? max_keys : 1));
+  J->status = 0;
+  /* work item = (selected row k, query head h), interleaved over threads */
+  const int64_t items = (int64_t)J->num_sel * Hq;
+  for (int64_t it = J->tid; it < items; it += J->nthreads) {
+    const int32_t k = (int32_t)(it / Hq), h = (int32_t)(it % Hq);
+    const int32_t r = J->rows ? J->rows[k] : k;
+    row_info ri;
+    if (find_row(J->context_lens, J->qsl, g->num_seqs, J->num_q_rows, r, &ri) ||
+        ri.last_key >= max_keys) { /* a context longer than its block-table row */
+      J->status = -1;
+      break;
+    }
+    const int32_t* bt_row = J->block_tables + (int64_t)ri.seq * g->max_blocks_per_seq;
+    const int32_t kvh = h / grp; /* GQA: contiguous groups of query heads share a KV head */
+    for (int32_t d = 0; d < D; ++d)
+      qv[d] = load_elem(J->q, g->dtype, ((int64_t)r * Hq + h) * D + d);
+    const int32_t nkeys = ri.last_key >= 0 ? ri.last_key + 1 : 0;
+    if (J->partition_size <= 0) {
+      double m, l;
+      double* o = J->out + ((int64_t)k * Hq + h) * D;
+      scores(x, qv, J->k_cache, bt_row, kvh, 0, nkeys, J->scale, g);
+      softmax_v(o, &m, &l, x, w, J->v_cache, bt_row, kvh, 0, nkeys, g);
+      if (J->lse) J->lse[(int64_t)k * Hq + h] = nkeys > 0 ? m + log(l) : -INFINITY;
+    } else {
+      const int32_t P = J->max_partitions, ps = J->partition_size;
+      if ((int64_t)(nkeys + ps - 1) / ps > P) {
+        J->status = -1;
+        break;
+      }
+      for (int32_t p = 0; p < P; ++p) {
+        const int64_t pi = ((int64_t)k * Hq + h) * P + p;
+        const int32_t t0 = p * ps;
+        const int32_t t1 = t0 + ps < nkeys ? t0 + ps : nkeys;
+        const int32_t n = t1 > t0 ? t1 - t0 : 0;
+        if (n > 0) scores(x, qv, J->k_cache, bt_row, kvh, t0, t1, J->scale, g);
+        softmax_v(J->o_part + pi * D, &J->m_part[pi], &J->l_part[pi], x, w, J->v_cache, bt_row,
+                  kvh, t0, n, g);
+      }
+    }
+  }
+  free(qv);
+  free(x);
+  free(w);
+  return NULL;
+}
+
+static int32_t run_all(job* proto, int32_t num_threads) {
+  if (num_threads <= 0) num_threads = (int32_t)sysconf(_SC_NPROCESSORS_ONLN);
+  if (num_threads < 1) num_threads = 1;
+  if (num_threads > 256) num_threads = 256;
+  job* jobs = (job*)malloc(sizeof(job) * num_threads);
+  pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * num_threads);
+  for (int32_t t = 0; t < num_threads; ++t) {
+    jobs[t] = *proto;
+    jobs[t].tid = t;
+    jobs[t].nthreads = num_threads;
+  }
+  for (int32_t t = 1; t < num_threads; ++t) pthread_create(&th[t], NULL, run_job, &jobs[t]);
+  run_job(&jobs[0]);
+  int32_t status = jobs[0].status;
+  for (int32_t t = 1; t < num_threads; ++t) {
+    pthread_join(th[t], NULL);
+    if (jobs[t].status) status = jobs[t].status;
+  }
+  free(jobs);
+  free(th);
+  return status;
+}
+
+int32_t pa_ref_paged_attention(double* out, double* lse, const void* q, const void* k_cache,
+                               const void* v_cache, const int32_t* block_tables,
+                               const int32_t* context_lens, const int32_t* query_start_loc,
+                               int32_t num_q_rows, double scale, const pa_ref_geom* g,
+                               const int32_t* rows, int32_t num_rows, int32_t num_threads) {
+  if (!geom_ok(g) || !out || num_q_rows < 0) return -1;
+  job J;
+  memset(&J, 0, sizeof(J));
+  J.q = q;
+  J.k_cache = k_cache;
+  J.v_cache = v_cache;
+  J.block_tables = block_tables;
+  J.context_lens = context_lens;
+  J.qsl = query_start_loc;
+  J.rows = rows;
+  J.num_q_rows = num_q_rows;
+  J.num_sel = rows ? num_rows : num_q_rows;
+  J.scale = scale;
+  J.g = g;
+  J.out = out;
+  J.lse = lse;
+  return run_all(&J, num_threads);
+}
+
+int32_t pa_ref_partition_attention(double* o_part, double* m_part, double* l_part, const void* q,
+                                   const void* k_cache, const void* v_cache,
+                                   const int32_t* block_tables, const int32_t* context_lens,
+                                   const int32_t* query_start_loc, int32_t num_q_rows,
+                                   double scale, int32_t partition_size, int32_t max_partitions,
+                                   const pa_ref_geom* g, const int32_t* rows, int32_t num_rows,
+                                   int32_t num_threads) {
+  if (!geom_ok(g) || partition_size <= 0 || max_partitions <= 0 || num_q_rows < 0) return -1;
+  job J;
+  memset(&J, 0, sizeof(J));
+  J.q = q;
+  J.k_cache = k_cache;
+  J.v_cache = v_cache;
+  J.block_tables = block_tables;
+  J.context_lens = context_lens;
+  J.qsl = query_start_loc;
+  J.rows = rows;
+  J.num_q_rows = num_q_rows;
+  J.num_sel = rows ? num_rows : num_q_rows;
+  J.scale = scale;
+  J.g = g;
+  J.partition_size = partition_size;
+  J.max_partitions = max_partitions;
+  J.o_part = o_part;
+  J.m_part = m_part;
+  J.l_part = l_part;
+  return run_all(&J, num_threads);
+}
+
+/* ---------------------------------------------------------------- partition merge */
+
+void pa_ref_merge_partitions(double* out, double* lse, const double* o_part, const double* m_part,
+                             const double* l_part, int64_t num_items, int32_t head_dim,
+                             int32_t max_partitions) {
+  const int32_t D = head_dim, P = max_partitions;
+  for (int64_t i = 0; i < num_items; ++i) {
+    const double* m = m_part + i * P;
+    const double* l = l_part + i * P;
+    double* o = out + i * D;
+    double M = -INFINITY;
+    for (int32_t p = 0; p < P; ++p)
+      if (l[p] > 0.0 && m[p] > M) M = m[p];
+    for (int32_t d = 0; d < D; ++d) o[d] = 0.0;
+    if (M == -INFINITY) { /* no keys at all */
+      if (lse) lse[i] = -INFINITY;
+      continue;
+    }
+    double L = 0.0;
+    for (int32_t p = 0; p < P; ++p) {
+      if (!(l[p] > 0.0)) continue;
+      const double wp = l[p] * exp(m[p] - M); /* partition weight relative to the global max */
+      L += wp;
+      for (int32_t d = 0; d < D; ++d) o[d] += wp * o_part[(i * P + p) * D + d];
+    }
+    for (int32_t d = 0; d < D; ++d) o[d] /= L;
+    if (lse) lse[i] = M + log(L);
+  }
+}
+
+/* ---------------------------------------------------------------- dense attention */
+
+void pa_ref_dense_attention(double* out, double* lse, const double* q, const double* k,
+                            const double* v, int32_t n, int32_t d, double scale) {
+  for (int32_t j = 0; j < d; ++j) out[j] = 0.0;
+  if (n <= 0) {
+    if (lse) *lse = -INFINITY;
+    return;
+  }
+  double* x = (double*)malloc(sizeof(double) * n);
+  for (int32_t i = 0; i < n; ++i) {
+    double dot = 0.0;
+    for (int32_t j = 0; j < d; ++j) dot += q[j] * k[(int64_t)i * d + j];
+    x[i] = scale * dot;
+  }
+  double m = x[0];
+  for (int32_t i = 1; i < n; ++i)
+    if (x[i] > m) m = x[i];
+  double l = 0.0;
+  for (int32_t i = 0; i < n; ++i) {
+    x[i] = exp(x[i] - m);
+    l += x[i];
+  }
+  for (int32_t i = 0; i < n; ++i)
+    for (int32_t j = 0; j < d; ++j) out[j] += x[i] * v[(int64_t)i * d + j];
+  for (int32_t j = 0; j < d; ++j) out[j] /= l;
+  if (lse) *lse = m + log(l);
+  free(x);
+}

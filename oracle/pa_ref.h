@@ -1,0 +1,115 @@
+/*
+ * pa_ref.h — CPU oracle for paged-attention decode and the paged KV-cache write.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This is the slow, obviously-correct fp64 definition the
+ * GPU library is checked against.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load it.  It shares no code, header, table or
+ * constant with the GPU library (paged_kv_cache_445_amd/csrc): both sides implement
+ * the same pool layout independently, from its written definition below.
+ *
+ * Sources (web pages; cited by title and section):
+ *   [DD]  "vLLM 深度拆解：当 KV Cache 学会「分页」" (chenxutan.com/d/4801.html)
+ *         §2.2 attention formula and the decode I/O argument;
+ *         §3.3 block-table lookup walk with the context-length stop;
+ *         §6.2 kernel argument list (output, query, k_cache, v_cache, block_tables,
+ *              context_lens) and the `* scale` on the score.
+ *   [AR1] "vLLM 架构源码解析 第1篇" (wazhb.com, 2026-07-06)
+ *         §3.3.2 query_start_loc / slot_mapping metadata;
+ *         §3.3.3 reshape_and_cache(k, v, kv_cache, slot_mapping) runs before
+ *                paged_attention(q, kv_cache, block_tables, context_lens);
+ *         §4.2   logical = i // block_size, offset = i % block_size, 16-token blocks.
+ *   [CI]  "2. 核心思想" (ai-infra.cypggs.com) — Block Table: a 2-D buffer
+ *         [max_num_reqs, max_num_blocks_per_req].
+ *
+ * Readings where the pages are silent (each also listed in the design doc):
+ *   - GQA: query head h reads KV head h / (Hq / Hkv) (contiguous groups).
+ *   - Multi-query rows: a sequence s with n_s = qsl[s+1] - qsl[s] query rows has its
+ *     context_lens entry counting those rows; row j sits at position ctx - n_s + j and
+ *     sees keys [0, ctx - n_s + j] (causal).  A decode row is the case n_s = 1.
+ *   - A row with no keys (ctx = 0) has output 0 and lse = -inf.
+ *   - slot = physical_block * block_size + offset; slot < 0 means "skip this token".
+ *
+ * Pool layout (the GPU library's ABI defines the same layout; written out here on
+ * its own).  elem = 4 (fp32) or 2 (fp16, bf16) bytes, X = 16 / elem:
+ *   K pool: [num_blocks][num_kv_heads][head_dim / X][block_size][X]
+ *   V pool: [num_blocks][num_kv_heads][head_dim][block_size]
+ * The V layout is the pages' [num_blocks, num_heads, head_size, block_size] ([DD] §6.2);
+ * K splits head_size into 16-byte chunks so that one token's chunk is 16 bytes.
+ *
+ * Precision: every stored element is converted exactly to double; scores, the
+ * softmax and the weighted sum are evaluated in double in ascending key order.
+ */
+#ifndef PA_REF_H
+#define PA_REF_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { PA_REF_F32 = 0, PA_REF_F16 = 1, PA_REF_BF16 = 2 };
+
+typedef struct {
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t num_blocks;
+  int32_t max_blocks_per_seq; /* block_tables row stride */
+  int32_t dtype;              /* PA_REF_F32 / PA_REF_F16 / PA_REF_BF16: q, K, V, key, value */
+} pa_ref_geom;
+
+/* Element offset (in elements, not bytes) of K[block][kv_head][token][dim] / V[...]. */
+int64_t pa_ref_k_offset(const pa_ref_geom* g, int64_t block, int32_t kv_head, int32_t token, int32_t dim);
+int64_t pa_ref_v_offset(const pa_ref_geom* g, int64_t block, int32_t kv_head, int32_t token, int32_t dim);
+
+/* Exact conversion of n stored elements to double. */
+void pa_ref_to_double(const void* src, int32_t dtype, int64_t n, double* dst);
+
+/* reshape_and_cache ([AR1] §3.3.3): for every token i with slot_mapping[i] >= 0, copy the
+ * bits of key[i][h][:] / value[i][h][:] into the pools at block = slot / block_size,
+ * offset = slot % block_size.  Returns 0, or -1 on a slot outside the pool. */
+int32_t pa_ref_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                                 const int64_t* slot_mapping, int64_t num_tokens, const pa_ref_geom* g);
+
+/* Paged attention ([DD] §2.2, §3.3, §6.2): for each selected query row r and query head h,
+ * out[k][h][:] = softmax(scale * q . K^T) . V over the row's visible keys, gathered through
+ * block_tables; lse[k][h] = max + ln(sum).  query_start_loc may be NULL (row r = seq r).
+ * rows == NULL selects all num_q_rows rows, in order; otherwise rows[k] (k < num_rows).
+ * out: [num_selected][Hq][D]; lse: [num_selected][Hq] or NULL.
+ * num_threads <= 0 uses every online core.  Returns 0, or -1 on bad arguments. */
+int32_t pa_ref_paged_attention(double* out, double* lse, const void* q, const void* k_cache,
+                               const void* v_cache, const int32_t* block_tables,
+                               const int32_t* context_lens, const int32_t* query_start_loc,
+                               int32_t num_q_rows, double scale, const pa_ref_geom* g,
+                               const int32_t* rows, int32_t num_rows, int32_t num_threads);
+
+/* Split-context partials: the same attention restricted to the keys of partition p,
+ * tokens [p*partition_size, (p+1)*partition_size) ∩ visible keys.
+ *   o_part [num_selected][Hq][max_partitions][D]  per-partition softmax-normalised output
+ *   m_part [num_selected][Hq][max_partitions]     max scaled score in the partition
+ *   l_part [num_selected][Hq][max_partitions]     sum of exp(score - m) in the partition
+ * An empty partition has o = 0, m = -inf, l = 0.  Returns -1 if a row needs more than
+ * max_partitions partitions. */
+int32_t pa_ref_partition_attention(double* o_part, double* m_part, double* l_part, const void* q,
+                                   const void* k_cache, const void* v_cache,
+                                   const int32_t* block_tables, const int32_t* context_lens,
+                                   const int32_t* query_start_loc, int32_t num_q_rows,
+                                   double scale, int32_t partition_size, int32_t max_partitions,
+                                   const pa_ref_geom* g, const int32_t* rows, int32_t num_rows,
+                                   int32_t num_threads);
+
+/* Log-sum-exp merge of num_items independent partial sets (each with P partitions of D). */
+void pa_ref_merge_partitions(double* out, double* lse, const double* o_part, const double* m_part,
+                             const double* l_part, int64_t num_items, int32_t head_dim,
+                             int32_t max_partitions);
+
+/* Dense (unpaged) attention of one query over n contiguous keys: k, v are [n][d] doubles. */
+void pa_ref_dense_attention(double* out, double* lse, const double* q, const double* k,
+                            const double* v, int32_t n, int32_t d, double scale);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
