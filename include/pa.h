@@ -1,0 +1,154 @@
+/*
+ * pa.h — paged-attention decode for MI355X (gfx950): the C ABI of libpa.so.
+ *
+ * The operation ("vLLM 深度拆解：当 KV Cache 学会「分页」" §2.2, §3.3, §6.2; "vLLM 架构源码解析
+ * 第1篇" §3.3.3): each step first scatters the new tokens' K and V into a pool of
+ * fixed-size physical blocks (reshape_and_cache), then computes, for every query row r and
+ * query head h,
+ *
+ *     out[r][h] = softmax(scale * q[r][h] . K^T) . V
+ *
+ * over the row's visible keys, gathered block by block through a per-sequence block table.
+ *
+ * Conventions shared by every entry point
+ *   - All array arguments are DEVICE pointers into caller-owned memory, except `geom`
+ *     (host).  The library allocates, frees and synchronises nothing; every launch is
+ *     enqueued on `stream` (a hipStream_t; NULL = the default stream).
+ *   - Arrays are dense, row-major, and 16-byte aligned.
+ *   - Errors: arguments are checked on the host before any launch and reported as a
+ *     pa_status; nothing is launched on error.  A failed launch returns PA_ERR_HIP.
+ *     Device-resident values (block ids < num_blocks, context_lens <= max_blocks_per_seq
+ *     * block_size, unique slots) are the caller's contract and are not checked.
+ *   - block_size is 16 ("vLLM 架构源码解析 第1篇" §4.2: 16-token blocks).  head_dim is 64 or 128.
+ *     kv_dtype is PA_F32, PA_F16 or PA_BF16; q, key, value and both pools share it.
+ *
+ * Pool layout (part of this ABI).  elem = 4 (fp32) or 2 bytes, X = 16 / elem:
+ *   k_cache: [num_blocks][num_kv_heads][head_dim / X][block_size][X]
+ *   v_cache: [num_blocks][num_kv_heads][head_dim][block_size]
+ * v_cache is the pages' [num_blocks, num_heads, head_size, block_size] ("vLLM 深度拆解"
+ * §6.2); k_cache splits head_size into 16-byte chunks so one token's chunk is one 16-byte
+ * load and the 16 tokens of a chunk are 256 contiguous bytes.
+ *
+ * Rows and positions.  query_start_loc ("vLLM 架构源码解析 第1篇" §3.3.2) is NULL when every sequence has one
+ * query row (row r belongs to sequence r, num_q_rows == num_seqs), else an int32 [S + 1]
+ * prefix array: sequence s owns rows [qsl[s], qsl[s+1]).  context_lens[s] counts every
+ * token of s including this step's rows; row j of an n-row sequence sits at position
+ * ctx - n + j and sees keys [0, ctx - n + j] (causal).  A row with no visible key
+ * produces 0.  Query head h reads KV head h / (num_q_heads / num_kv_heads).
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_NULL = -1,        /* a required pointer is NULL */
+  PA_ERR_SHAPE = -2,       /* inconsistent sizes (negative counts, Hq % Hkv != 0, ...) */
+  PA_ERR_UNSUPPORTED = -3, /* a valid but unimplemented combination (head_dim, dtype, ...) */
+  PA_ERR_WORKSPACE = -4,   /* workspace missing or smaller than pa_workspace_size() */
+  PA_ERR_HIP = -5          /* a HIP launch failed (hipGetLastError after the launch) */
+} pa_status;
+
+/* Geometry shared by all calls (host struct, read during the call only). */
+typedef struct {
+  int32_t num_seqs;           /* S */
+  int32_t num_q_heads;        /* Hq */
+  int32_t num_kv_heads;       /* Hkv; Hq % Hkv == 0, Hq / Hkv <= 16 */
+  int32_t head_dim;           /* D: 64 or 128 */
+  int32_t block_size;         /* tokens per physical block: 16 */
+  int32_t num_blocks;         /* NB: blocks in each pool */
+  int32_t max_blocks_per_seq; /* MB: row stride of block_tables */
+  int32_t kv_dtype;           /* pa_dtype of q, key, value, k_cache, v_cache */
+  int32_t out_dtype;          /* pa_dtype of out: kv_dtype or PA_F32 */
+} pa_geom;
+
+/* Bytes of one pool (K or V): num_blocks * num_kv_heads * head_dim * block_size * elem.
+ * Returns 0 for an invalid geometry. */
+size_t pa_kv_cache_bytes(const pa_geom* geom);
+
+/*
+ * Cache write ("vLLM 架构源码解析 第1篇" §3.3.3 reshape_and_cache(k, v, kv_cache,
+ * slot_mapping); slot arithmetic from §4.2's `//` and `%`).  For every token t with
+ * slot_mapping[t] >= 0: block = slot / block_size, offset = slot % block_size, and for every
+ * KV head g the bits of key[t][g][:] / value[t][g][:] are copied to k_cache / v_cache at
+ * (block, g, offset).  Negative slots are skipped (padding).
+ *   key, value     [num_tokens][num_kv_heads][head_dim], kv_dtype
+ *   k_cache, v_cache  the pools (layout above), written in place
+ *   slot_mapping   int64 [num_tokens]; slots must be unique and < num_blocks * block_size
+ * num_tokens == 0 is a no-op.  Writes into a block shared by several sequences are the
+ * caller's responsibility (copy-on-write happens before this call).
+ */
+pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                               const int64_t* slot_mapping, int64_t num_tokens,
+                               const pa_geom* geom, void* stream);
+
+/* Workspace bytes pa_decode needs for this geometry and row count (0 is never returned
+ * for a valid geometry; returns 0 for an invalid one). */
+size_t pa_workspace_size(const pa_geom* geom, int32_t num_q_rows);
+
+/*
+ * Full decode step ("vLLM 深度拆解" §2.2 formula, §3.3 block walk, §6.2 arguments:
+ * output, query, k_cache, v_cache, block_tables, context_lens, scale).
+ *   out           [num_q_rows][num_q_heads][head_dim], out_dtype
+ *   q             [num_q_rows][num_q_heads][head_dim], kv_dtype
+ *   block_tables  int32 [num_seqs][max_blocks_per_seq]: logical block j of sequence s lives
+ *                 in physical block block_tables[s * max_blocks_per_seq + j]
+ *   context_lens  int32 [num_seqs]
+ *   query_start_loc  int32 [num_seqs + 1] or NULL (see "Rows and positions")
+ *   scale         multiplies q . k (normally 1 / sqrt(head_dim))
+ *   workspace     device scratch of at least pa_workspace_size(geom, num_q_rows) bytes,
+ *                 used for split-context partials; contents need no initialisation
+ * Long contexts are split across wavefronts and merged by log-sum-exp inside this call.
+ * Sequences with several rows (query_start_loc) need a 16-bit kv_dtype and a query group
+ * Hq / Hkv that divides 16; otherwise PA_ERR_UNSUPPORTED.
+ */
+pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* context_lens,
+                    const int32_t* query_start_loc, int32_t num_q_rows, float scale,
+                    void* workspace, size_t workspace_bytes, const pa_geom* geom, void* stream);
+
+/*
+ * Split-context partials (flash-decoding) for decode rows: one query row per sequence
+ * (row r = sequence r, num_q_rows == num_seqs).  Partition p of a row is its key positions
+ * [p * partition_size, (p + 1) * partition_size) below context_lens[r].
+ *   tmp_out     float [num_q_rows][num_q_heads][max_partitions][head_dim]: the partition's
+ *               softmax-normalised output
+ *   max_logits  float [num_q_rows][num_q_heads][max_partitions]: max of scale * q . k over
+ *               the partition's keys
+ *   exp_sums    float [num_q_rows][num_q_heads][max_partitions]: sum of
+ *               exp(scale * q . k - max_logits) over those keys
+ * Partitions with no key get max_logits = -inf and exp_sums = 0; their tmp_out entries are
+ * not written.  partition_size is a positive multiple of 32; max_partitions must cover the
+ * longest possible context: max_partitions * partition_size >= max_blocks_per_seq * block_size.
+ */
+pa_status pa_decode_partitioned(float* tmp_out, float* max_logits, float* exp_sums,
+                                const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* block_tables, const int32_t* context_lens,
+                                int32_t num_q_rows, float scale, int32_t partition_size,
+                                int32_t max_partitions, const pa_geom* geom, void* stream);
+
+/*
+ * Log-sum-exp merge of pa_decode_partitioned's output: over the partitions with
+ * exp_sums > 0, M = max_p max_logits[p], w_p = exp_sums[p] * exp(max_logits[p] - M) and
+ * out = sum_p w_p * tmp_out[p] / sum_p w_p.  Rows with no key get 0.  Arguments as in
+ * pa_decode_partitioned; out [num_q_rows][num_q_heads][head_dim] in out_dtype.
+ */
+pa_status pa_decode_reduce(void* out, const float* tmp_out, const float* max_logits,
+                           const float* exp_sums, int32_t num_q_rows, int32_t max_partitions,
+                           const pa_geom* geom, void* stream);
+
+/* Static description of a status code. */
+const char* pa_status_str(pa_status status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PA_H */

@@ -1,0 +1,213 @@
+// decode_mfma.hip — paged-attention decode for grouped-query heads on the matrix cores.
+//
+// Same method as the vector kernel ("vLLM 深度拆解：当 KV Cache 学会「分页」" §2.2 formula, §3.3
+// block-table walk with the context-length stop, §6.2 arguments and scale), but one work
+// segment is a (sequence, KV head) pair and all G = Hq / Hkv query heads that share the KV
+// head are scored together: per 32-token unit (two 16-token blocks) the wavefront runs
+//   S^T = K . Q^T  as 2 x (D/32) MFMA 16x16x32  (M = 16 tokens, N = 16 head columns, G used)
+//   O  += P . V    as (D/16) MFMA 16x16x32     (M = 16 head rows, N = 16 dims, K = 32 tokens)
+// Each K and V byte is read once for all G heads.
+//
+// Operand layouts, the token permutation that keeps scores in place, and the hi/lo split
+// of P are described in pa_mfma.h.
+#include "pa_device.h"
+#include "pa_internal.h"
+#include "pa_mfma.h"
+
+namespace pa {
+
+// All query heads of KV head g for sequence s over the units [u0, u1) (32 tokens each).
+template <int DT, int D>
+__device__ void mfma_attend(const DecodeArgs& a, int s, int g, int u0, int u1, int ctx,
+                            MfmaState<DT, D>& st) {
+  using C = MfmaCfg<DT, D>;
+  using T = op8_t<DT>;
+  const int lane = lane_id();
+  const int r = lane >> 4, n = lane & 15;
+  const int G = a.num_q_heads / a.num_kv_heads;
+  const int row = a.qsl ? a.qsl[s] : s;
+
+  T qb[C::NKK];
+  {
+    const char* qp = reinterpret_cast<const char*>(a.q) +
+                     ((int64_t)row * a.num_q_heads + (int64_t)g * G + n) * D * C::E;
+#pragma unroll
+    for (int kk = 0; kk < C::NKK; ++kk) {
+      const uint4 v = n < G ? ld16(qp + (4 * kk + r) * 16) : make_uint4(0, 0, 0, 0);
+      qb[kk] = __builtin_bit_cast(T, v);
+    }
+  }
+  MfmaLaneOffsets<DT, D> o;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int t = 8 * (n >> 2) + 4 * b + (n & 3);  // unit token of S-block row n
+    o.kt[b] = t >> 4;
+#pragma unroll
+    for (int kk = 0; kk < C::NKK; ++kk) o.k[b][kk] = ((4 * kk + r) * 16 + (t & 15)) * 16;
+  }
+  o.vt = r >> 1;
+#pragma unroll
+  for (int j = 0; j < C::NJ; ++j) o.v[j] = ((16 * j + n) * 16 + 8 * (r & 1)) * C::E;
+
+  const int64_t blk_stride = (int64_t)a.num_kv_heads * C::TILE;
+  const char* kc = reinterpret_cast<const char*>(a.k_cache) + (int64_t)g * C::TILE;
+  const char* vc = reinterpret_cast<const char*>(a.v_cache) + (int64_t)g * C::TILE;
+  const int32_t* bt_row = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+  const int nblk = (ctx + kBlock - 1) / kBlock;
+
+  st.m = -INFINITY;
+  st.l = 0.f;
+#pragma unroll
+  for (int j = 0; j < C::NJ; ++j) st.acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  constexpr int WU = kWave / 2;  // units whose table entries fit one VGPR window
+  for (int wb = u0; wb < u1; wb += WU) {
+    const int we = min(u1, wb + WU);
+    const int e0 = 2 * wb;
+    const int btv = (e0 + lane < min(nblk, 2 * we)) ? bt_row[e0 + lane] : 0;
+    uint4 kb[C::DEPTH][2][C::NKK], vb[C::DEPTH][C::NJ];
+    auto issue = [&](int slot, int u) {
+      const int ia = 2 * (u - wb);
+      const int64_t ba = readlane(btv, ia);
+      // a unit whose second block lies past the context reads its first block again
+      // (all of its tokens are masked)
+      const int64_t bb = (2 * u + 1 < nblk) ? (int64_t)readlane(btv, ia + 1) : ba;
+      mfma_load<DT, D>(kb[slot], vb[slot], kc + ba * blk_stride, kc + bb * blk_stride,
+                       vc + ba * blk_stride, vc + bb * blk_stride, o);
+    };
+#pragma unroll
+    for (int b = 0; b < C::DEPTH - 1; ++b)
+      if (wb + b < we) issue(b, wb + b);
+    for (int u = wb; u < we; u += C::DEPTH) {
+#pragma unroll
+      for (int b = 0; b < C::DEPTH; ++b) {
+        const int ut = u + b;
+        if (ut < we) {
+          const int un = ut + C::DEPTH - 1;
+          if (un < we) issue((b + C::DEPTH - 1) % C::DEPTH, un);
+          const int valid = ctx - ut * kMfmaUnit;
+          if (valid >= kMfmaUnit)
+            mfma_unit<DT, D, false, false>(st, kb[b], vb[b], qb, a.scale_log2, kMfmaUnit - 1,
+                                           kMfmaUnit);
+          else
+            mfma_unit<DT, D, true, false>(st, kb[b], vb[b], qb, a.scale_log2, valid - 1, valid);
+        }
+      }
+    }
+  }
+}
+
+template <int DT, int D, int MODE>
+__global__ __launch_bounds__(kWG) void mfma_decode_kernel(DecodeArgs a) {
+  extern __shared__ int32_t lds[];
+  int32_t* base = lds;
+  int32_t* tmp = lds + a.num_seqs + 1;
+  const int wave = threadIdx.x / kWave;
+  const int lane = lane_id();
+  const int segs = a.num_kv_heads;
+  const int G = a.num_q_heads / a.num_kv_heads;
+  const int S = a.num_seqs;
+  const int64_t W = (int64_t)gridDim.x * kWavesPerWG;
+  const int64_t w = (int64_t)blockIdx.x * kWavesPerWG + wave;
+
+  if constexpr (MODE == MODE_EVEN) {
+    PlanIn pin{a.context_lens, a.qsl, S, kMfmaUnit};
+    build_plan(base, tmp, pin);
+    const int64_t total = (int64_t)base[S] * segs;
+    const int64_t lo = range_lo(total, w, W), hi = range_lo(total, w + 1, W);
+    for (int64_t i = lo; i < hi;) {
+      const int s = find_seq(base, S, i, segs);
+      const int nu = base[s + 1] - base[s];
+      const int64_t sbase = (int64_t)base[s] * segs;
+      const int g = (int)((i - sbase) / nu);
+      const int64_t seg0 = sbase + (int64_t)g * nu;
+      const int64_t pe = min(hi, seg0 + nu);
+      const int u0 = (int)(i - seg0), u1 = (int)(pe - seg0);
+      const int ctx = a.context_lens[s];
+      MfmaState<DT, D> st;
+      mfma_attend<DT, D>(a, s, g, u0, u1, ctx, st);
+      if (u0 == 0 && u1 == nu) {
+        const int row = a.qsl ? a.qsl[s] : s;
+        const int64_t ob = ((int64_t)row * a.num_q_heads + (int64_t)g * G) * D;
+        mfma_emit<DT, D>(st, G, nullptr, nullptr, nullptr, D, a.out, ob, D, a.out_f32);
+      } else {
+        const int64_t slot = w * 2 + (i == lo ? 0 : 1);
+        mfma_emit<DT, D>(st, G, a.part_o + slot * G * D, a.part_m + slot * G,
+                         a.part_l + slot * G, D, nullptr, 0, 0, false);
+      }
+      i = pe;
+    }
+  } else {
+    const int PU = a.partition_units;  // 32-token units per partition
+    const int P = a.max_partitions;
+    PlanIn pin{a.context_lens, nullptr, S, PU * kMfmaUnit};
+    build_plan(base, tmp, pin);
+    const int64_t nent = (int64_t)S * a.num_q_heads * P;
+    for (int64_t e = (int64_t)blockIdx.x * kWG + threadIdx.x; e < nent; e += (int64_t)gridDim.x * kWG) {
+      const int p = (int)(e % P);
+      const int s = (int)(e / ((int64_t)P * a.num_q_heads));
+      if (p >= base[s + 1] - base[s]) {
+        a.part_m[e] = -INFINITY;
+        a.part_l[e] = 0.f;
+      }
+    }
+    const int64_t total = (int64_t)base[S] * segs;
+    for (int64_t i = w; i < total; i += W) {
+      const int s = find_seq(base, S, i, segs);
+      const int np = base[s + 1] - base[s];
+      const int64_t sbase = (int64_t)base[s] * segs;
+      const int g = (int)((i - sbase) / np);
+      const int p = (int)(i - sbase - (int64_t)g * np);
+      const int ctx = a.context_lens[s];
+      const int nu = (ctx + kMfmaUnit - 1) / kMfmaUnit;
+      const int u0 = p * PU, u1 = min(nu, u0 + PU);
+      MfmaState<DT, D> st;
+      mfma_attend<DT, D>(a, s, g, u0, u1, ctx, st);
+      // tmp_out [row][h][P][D]: consecutive heads are P * D apart
+      const int64_t e0 = ((int64_t)s * a.num_q_heads + (int64_t)g * G) * P + p;
+      mfma_emit<DT, D>(st, G, a.part_o + e0 * D, a.part_m + e0, a.part_l + e0, (int64_t)P * D,
+                       nullptr, 0, 0, false);
+    }
+  }
+  (void)lane;
+}
+
+template <int DT, int MODE>
+static hipError_t launch_d(const DecodeArgs& a, int grid, hipStream_t st) {
+  const size_t lds = (size_t)(a.num_seqs + 1 + kWG) * sizeof(int32_t);
+  if (a.head_dim == 64)
+    hipLaunchKernelGGL((mfma_decode_kernel<DT, 64, MODE>), dim3(grid), dim3(kWG), lds, st, a);
+  else
+    hipLaunchKernelGGL((mfma_decode_kernel<DT, 128, MODE>), dim3(grid), dim3(kWG), lds, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_mfma_decode(int dt, int mode, const DecodeArgs& a, int grid, hipStream_t st) {
+  if (mode == MODE_EVEN) {
+    if (dt == DT_F16) return launch_d<DT_F16, MODE_EVEN>(a, grid, st);
+    return launch_d<DT_BF16, MODE_EVEN>(a, grid, st);
+  }
+  if (dt == DT_F16) return launch_d<DT_F16, MODE_PARTITION>(a, grid, st);
+  return launch_d<DT_BF16, MODE_PARTITION>(a, grid, st);
+}
+
+template <int DT, int MODE>
+static int occ(int head_dim, int lds) {
+  int nb = 0;
+  hipError_t e;
+  if (head_dim == 64)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, mfma_decode_kernel<DT, 64, MODE>, kWG, lds);
+  else
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, mfma_decode_kernel<DT, 128, MODE>, kWG, lds);
+  return e == hipSuccess && nb > 0 ? nb : 1;
+}
+
+int mfma_decode_max_blocks_per_cu(int dt, int head_dim, int mode, int lds_bytes) {
+  if (mode == MODE_EVEN)
+    return dt == DT_F16 ? occ<DT_F16, MODE_EVEN>(head_dim, lds_bytes)
+                        : occ<DT_BF16, MODE_EVEN>(head_dim, lds_bytes);
+  return dt == DT_F16 ? occ<DT_F16, MODE_PARTITION>(head_dim, lds_bytes)
+                      : occ<DT_BF16, MODE_PARTITION>(head_dim, lds_bytes);
+}
+
+}  // namespace pa

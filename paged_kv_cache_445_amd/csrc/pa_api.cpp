@@ -1,0 +1,289 @@
+// pa_api.cpp — the C entry points of libpa.so (include/pa.h): argument checks, kernel choice,
+// grid sizing and launches.  Nothing here allocates, frees or synchronises device memory.
+#include <hip/hip_runtime.h>
+#include <stdlib.h>
+
+#include <atomic>
+#include <cmath>
+
+#include "../../include/pa.h"
+#include "pa_internal.h"
+
+namespace pa {
+hipError_t launch_chunk(int dt, const DecodeArgs& a, int grid, hipStream_t st);
+}
+
+namespace {
+
+constexpr int kMaxSeqs = 8192;  // the split kernels keep one int per sequence in LDS
+constexpr int kMaxDevices = 64;
+
+size_t elem_bytes(int dt) { return dt == PA_F32 ? 4 : 2; }
+
+bool dtype_ok(int dt) { return dt == PA_F32 || dt == PA_F16 || dt == PA_BF16; }
+
+pa_status check_geom(const pa_geom* g) {
+  if (!g) return PA_ERR_NULL;
+  if (g->num_seqs < 0 || g->num_q_heads <= 0 || g->num_kv_heads <= 0 || g->head_dim <= 0 ||
+      g->block_size <= 0 || g->num_blocks <= 0 || g->max_blocks_per_seq <= 0)
+    return PA_ERR_SHAPE;
+  if (g->num_q_heads % g->num_kv_heads) return PA_ERR_SHAPE;
+  if (!dtype_ok(g->kv_dtype) || !dtype_ok(g->out_dtype)) return PA_ERR_UNSUPPORTED;
+  if (g->out_dtype != g->kv_dtype && g->out_dtype != PA_F32) return PA_ERR_UNSUPPORTED;
+  if (g->block_size != pa::kBlock) return PA_ERR_UNSUPPORTED;
+  if (g->head_dim != 64 && g->head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (g->num_q_heads / g->num_kv_heads > 16) return PA_ERR_UNSUPPORTED;
+  if (g->num_seqs > kMaxSeqs) return PA_ERR_UNSUPPORTED;
+  return PA_OK;
+}
+
+int current_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  return dev;
+}
+
+int cu_count() {
+  static std::atomic<int> cache[kMaxDevices];
+  const int dev = current_device();
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// optional override of resident workgroups per CU for the split kernels (tuning)
+int wg_per_cu_override() {
+  static int v = [] {
+    const char* s = getenv("PA_DECODE_WG_PER_CU");
+    return s ? atoi(s) : 0;
+  }();
+  return v;
+}
+
+bool use_mfma(const pa_geom* g) {
+  return g->kv_dtype != PA_F32 && g->num_q_heads / g->num_kv_heads >= 2;
+}
+
+int lds_bytes(const pa_geom* g) { return (g->num_seqs + 1 + pa::kWG) * (int)sizeof(int32_t); }
+
+// workgroups of the split kernel: every CU full at the kernel's occupancy
+int split_grid(const pa_geom* g, int mode) {
+  static std::atomic<int> cache[kMaxDevices][2][3][2][2];
+  const int dev = current_device();
+  const int path = use_mfma(g) ? 1 : 0;
+  const int di = g->head_dim == 64 ? 0 : 1;
+  std::atomic<int>& c = cache[dev][path][g->kv_dtype][di][mode];
+  int occ = c.load(std::memory_order_relaxed);
+  if (occ <= 0) {
+    const int lds = (kMaxSeqs + 1 + pa::kWG) * (int)sizeof(int32_t);  // worst case
+    occ = path ? pa::mfma_decode_max_blocks_per_cu(g->kv_dtype, g->head_dim, mode, lds)
+               : pa::valu_decode_max_blocks_per_cu(g->kv_dtype, g->head_dim, mode, lds);
+    c.store(occ, std::memory_order_relaxed);
+  }
+  const int o = wg_per_cu_override();
+  if (o > 0 && o < occ) occ = o;
+  return cu_count() * occ;
+}
+
+struct SplitShape {
+  int segs, heads_per_seg, unit;
+};
+
+SplitShape split_shape(const pa_geom* g) {
+  if (use_mfma(g)) return {g->num_kv_heads, g->num_q_heads / g->num_kv_heads, pa::kMfmaUnit};
+  return {g->num_q_heads, 1, pa::kValuUnit};
+}
+
+size_t even_workspace_bytes(const pa_geom* g, int grid) {
+  const SplitShape sh = split_shape(g);
+  const size_t slots = (size_t)grid * pa::kWavesPerWG * 2 * sh.heads_per_seg;
+  return slots * ((size_t)g->head_dim + 2) * sizeof(float);
+}
+
+pa_status hip_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
+
+float scale_to_log2(float scale) { return scale * 1.4426950408889634f; }
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_str(pa_status s) {
+  switch (s) {
+    case PA_OK: return "ok";
+    case PA_ERR_NULL: return "a required pointer is NULL";
+    case PA_ERR_SHAPE: return "inconsistent sizes";
+    case PA_ERR_UNSUPPORTED: return "unsupported head_dim / block_size / dtype / group combination";
+    case PA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PA_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+size_t pa_kv_cache_bytes(const pa_geom* g) {
+  if (check_geom(g) != PA_OK) return 0;
+  return (size_t)g->num_blocks * g->num_kv_heads * g->head_dim * g->block_size *
+         elem_bytes(g->kv_dtype);
+}
+
+pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                               const int64_t* slot_mapping, int64_t num_tokens,
+                               const pa_geom* g, void* stream) {
+  const pa_status gs = check_geom(g);
+  if (gs != PA_OK) return gs;
+  if (num_tokens < 0) return PA_ERR_SHAPE;
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !k_cache || !v_cache || !slot_mapping) return PA_ERR_NULL;
+  const int64_t X = 16 / (int64_t)elem_bytes(g->kv_dtype);
+  const int64_t threads = num_tokens * g->num_kv_heads * (g->head_dim / X + g->head_dim);
+  if ((threads + 255) / 256 > 0x7fffffffLL) return PA_ERR_SHAPE;
+  pa::ReshapeArgs a{key, value, k_cache, v_cache, slot_mapping, num_tokens, g->num_kv_heads,
+                    g->head_dim};
+  return hip_status(pa::launch_reshape(g->kv_dtype, a, (hipStream_t)stream));
+}
+
+size_t pa_workspace_size(const pa_geom* g, int32_t num_q_rows) {
+  if (check_geom(g) != PA_OK || num_q_rows < 0) return 0;
+  return even_workspace_bytes(g, split_grid(g, pa::MODE_EVEN));
+}
+
+pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* context_lens,
+                    const int32_t* query_start_loc, int32_t num_q_rows, float scale,
+                    void* workspace, size_t workspace_bytes, const pa_geom* g, void* stream) {
+  const pa_status gs = check_geom(g);
+  if (gs != PA_OK) return gs;
+  if (num_q_rows < 0) return PA_ERR_SHAPE;
+  if (!query_start_loc && num_q_rows != g->num_seqs) return PA_ERR_SHAPE;
+  if (g->num_seqs == 0 || num_q_rows == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_NULL;
+  if (!std::isfinite(scale)) return PA_ERR_SHAPE;
+  const int G = g->num_q_heads / g->num_kv_heads;
+  if (query_start_loc && (g->kv_dtype == PA_F32 || 16 % G != 0)) return PA_ERR_UNSUPPORTED;
+  hipStream_t st = (hipStream_t)stream;
+
+  const int grid = split_grid(g, pa::MODE_EVEN);
+  const size_t need = even_workspace_bytes(g, grid);
+  if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
+  const SplitShape sh = split_shape(g);
+  const size_t slots = (size_t)grid * pa::kWavesPerWG * 2 * sh.heads_per_seg;
+  float* part_o = static_cast<float*>(workspace);
+  float* part_m = part_o + slots * g->head_dim;
+  float* part_l = part_m + slots;
+
+  pa::DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.qsl = query_start_loc;
+  a.part_o = part_o;
+  a.part_m = part_m;
+  a.part_l = part_l;
+  a.num_seqs = g->num_seqs;
+  a.num_q_heads = g->num_q_heads;
+  a.num_kv_heads = g->num_kv_heads;
+  a.head_dim = g->head_dim;
+  a.max_blocks_per_seq = g->max_blocks_per_seq;
+  a.out_f32 = g->out_dtype == PA_F32 && g->kv_dtype != PA_F32;
+  a.scale_log2 = scale_to_log2(scale);
+
+  hipError_t e = use_mfma(g) ? pa::launch_mfma_decode(g->kv_dtype, pa::MODE_EVEN, a, grid, st)
+                             : pa::launch_valu_decode(g->kv_dtype, pa::MODE_EVEN, a, grid, st);
+  if (e != hipSuccess) return PA_ERR_HIP;
+
+  pa::EvenReduceArgs r{};
+  r.out = out;
+  r.part_o = part_o;
+  r.part_m = part_m;
+  r.part_l = part_l;
+  r.context_lens = context_lens;
+  r.qsl = query_start_loc;
+  r.num_seqs = g->num_seqs;
+  r.num_q_heads = g->num_q_heads;
+  r.num_kv_heads = g->num_kv_heads;
+  r.head_dim = g->head_dim;
+  r.segs = sh.segs;
+  r.heads_per_seg = sh.heads_per_seg;
+  r.unit_tokens = sh.unit;
+  r.num_waves = grid * pa::kWavesPerWG;
+  r.out_f32 = a.out_f32;
+  const int64_t items = (int64_t)g->num_seqs * sh.segs;
+  const int rgrid = (int)(items < (int64_t)cu_count() * 8 ? items : (int64_t)cu_count() * 8);
+  e = pa::launch_even_reduce(g->kv_dtype, r, rgrid, st);
+  if (e != hipSuccess) return PA_ERR_HIP;
+
+  if (query_start_loc) {
+    e = pa::launch_chunk(g->kv_dtype, a, cu_count() * 4, st);
+    if (e != hipSuccess) return PA_ERR_HIP;
+  }
+  return PA_OK;
+}
+
+pa_status pa_decode_partitioned(float* tmp_out, float* max_logits, float* exp_sums,
+                                const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* block_tables, const int32_t* context_lens,
+                                int32_t num_q_rows, float scale, int32_t partition_size,
+                                int32_t max_partitions, const pa_geom* g, void* stream) {
+  const pa_status gs = check_geom(g);
+  if (gs != PA_OK) return gs;
+  if (num_q_rows != g->num_seqs) return PA_ERR_SHAPE;
+  if (partition_size <= 0 || partition_size % pa::kMfmaUnit || max_partitions <= 0)
+    return PA_ERR_SHAPE;
+  if ((int64_t)max_partitions * partition_size < (int64_t)g->max_blocks_per_seq * g->block_size)
+    return PA_ERR_SHAPE;
+  if (g->num_seqs == 0) return PA_OK;
+  if (!tmp_out || !max_logits || !exp_sums || !q || !k_cache || !v_cache || !block_tables ||
+      !context_lens)
+    return PA_ERR_NULL;
+  if (!std::isfinite(scale)) return PA_ERR_SHAPE;
+  pa::DecodeArgs a{};
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.part_o = tmp_out;
+  a.part_m = max_logits;
+  a.part_l = exp_sums;
+  a.num_seqs = g->num_seqs;
+  a.num_q_heads = g->num_q_heads;
+  a.num_kv_heads = g->num_kv_heads;
+  a.head_dim = g->head_dim;
+  a.max_blocks_per_seq = g->max_blocks_per_seq;
+  a.scale_log2 = scale_to_log2(scale);
+  a.max_partitions = max_partitions;
+  const bool mf = use_mfma(g);
+  a.partition_units = partition_size / (mf ? pa::kMfmaUnit : pa::kValuUnit);
+  const int grid = split_grid(g, pa::MODE_PARTITION);
+  hipError_t e = mf ? pa::launch_mfma_decode(g->kv_dtype, pa::MODE_PARTITION, a, grid, (hipStream_t)stream)
+                    : pa::launch_valu_decode(g->kv_dtype, pa::MODE_PARTITION, a, grid, (hipStream_t)stream);
+  return hip_status(e);
+}
+
+pa_status pa_decode_reduce(void* out, const float* tmp_out, const float* max_logits,
+                           const float* exp_sums, int32_t num_q_rows, int32_t max_partitions,
+                           const pa_geom* g, void* stream) {
+  const pa_status gs = check_geom(g);
+  if (gs != PA_OK) return gs;
+  if (num_q_rows < 0 || max_partitions <= 0) return PA_ERR_SHAPE;
+  if (num_q_rows == 0) return PA_OK;
+  if (!out || !tmp_out || !max_logits || !exp_sums) return PA_ERR_NULL;
+  pa::PartReduceArgs a{};
+  a.out = out;
+  a.tmp_out = tmp_out;
+  a.max_logits = max_logits;
+  a.exp_sums = exp_sums;
+  a.num_items = (int64_t)num_q_rows * g->num_q_heads;
+  a.head_dim = g->head_dim;
+  a.max_partitions = max_partitions;
+  a.out_f32 = g->out_dtype == PA_F32 && g->kv_dtype != PA_F32;
+  return hip_status(pa::launch_part_reduce(g->kv_dtype, a, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,104 @@
+// pa_internal.h — kernel argument blocks and launchers inside libpa.so (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+constexpr int kWave = 64;
+constexpr int kWavesPerWG = 4;
+constexpr int kWG = kWave * kWavesPerWG;
+constexpr int kBlock = 16;  // tokens per physical block
+
+enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
+
+// How a split kernel distributes and emits its work.
+enum SplitMode : int {
+  // pa_decode: every wave owns an equal share of the flattened unit list; a segment that
+  // lies inside one wave is written to `out`, the pieces of a segment that crosses wave
+  // boundaries are written to the per-wave slots of the workspace and merged afterwards.
+  MODE_EVEN = 0,
+  // pa_decode_partitioned: fixed partitions of `partition_units` units; every (seq,
+  // segment, partition) is one item, written to tmp_out / max_logits / exp_sums.
+  MODE_PARTITION = 1,
+};
+
+struct DecodeArgs {
+  void* out;                // [rows][Hq][D], out dtype
+  const void* q;            // [rows][Hq][D]
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* qsl;       // NULL: one row per sequence
+  float* part_o;            // MODE_EVEN: [W][2][G][D]; MODE_PARTITION: tmp_out [rows][Hq][P][D]
+  float* part_m;            // MODE_EVEN: [W][2][G];    MODE_PARTITION: max_logits [rows][Hq][P]
+  float* part_l;            // MODE_EVEN: [W][2][G];    MODE_PARTITION: exp_sums   [rows][Hq][P]
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t max_blocks_per_seq;
+  int32_t out_f32;          // 1: out is fp32; 0: out has the KV dtype
+  float scale_log2;         // scale * log2(e): scores are kept in the base-2 domain
+  int32_t partition_units;  // MODE_PARTITION: units per partition
+  int32_t max_partitions;   // MODE_PARTITION
+};
+
+struct ReshapeArgs {
+  const void* key;
+  const void* value;
+  void* k_cache;
+  void* v_cache;
+  const int64_t* slot_mapping;
+  int64_t num_tokens;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+};
+
+struct EvenReduceArgs {
+  void* out;
+  const float* part_o;
+  const float* part_m;
+  const float* part_l;
+  const int32_t* context_lens;
+  const int32_t* qsl;
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t segs;         // segments per sequence in the split kernel (Hkv or Hq)
+  int32_t heads_per_seg;
+  int32_t unit_tokens;
+  int32_t num_waves;    // W of the split kernel
+  int32_t out_f32;
+};
+
+struct PartReduceArgs {
+  void* out;
+  const float* tmp_out;
+  const float* max_logits;
+  const float* exp_sums;
+  int64_t num_items;  // rows * Hq
+  int32_t head_dim;
+  int32_t max_partitions;
+  int32_t out_f32;
+};
+
+// launchers (return hipSuccess or the launch error)
+hipError_t launch_reshape(int dt, const ReshapeArgs& a, hipStream_t st);
+// VALU kernel: one query head per segment (segs = Hq), any head_dim in {64, 128}
+hipError_t launch_valu_decode(int dt, int mode, const DecodeArgs& a, int grid, hipStream_t st);
+int valu_decode_max_blocks_per_cu(int dt, int head_dim, int mode, int lds_bytes);
+// MFMA kernel: one kv head (all G query heads) per segment, 16-bit dtypes
+hipError_t launch_mfma_decode(int dt, int mode, const DecodeArgs& a, int grid, hipStream_t st);
+int mfma_decode_max_blocks_per_cu(int dt, int head_dim, int mode, int lds_bytes);
+hipError_t launch_even_reduce(int dt, const EvenReduceArgs& a, int grid, hipStream_t st);
+hipError_t launch_part_reduce(int dt, const PartReduceArgs& a, hipStream_t st);
+
+// unit sizes (tokens) of the split kernels
+constexpr int kValuUnit = 16;
+constexpr int kMfmaUnit = 32;
+
+}  // namespace pa

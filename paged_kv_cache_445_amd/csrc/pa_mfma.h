@@ -1,0 +1,204 @@
+// pa_mfma.h — matrix-core building blocks of the decode and chunk kernels (gfx950).
+//
+// One 32-token unit (two 16-token blocks of one KV head) against 16 query columns:
+//   S^T = K . Q^T  as 2 x (D/32) MFMA 16x16x32  (M = 16 tokens, N = 16 query columns)
+//   O  += P . V    as (D/16) MFMA 16x16x32     (M = 16 query columns, N = 16 dims, K = 32 tokens)
+// with a streamed (online) softmax per query column in between.
+//
+// Operand layouts (gfx950 v_mfma_f32_16x16x32_{bf16,f16}): lane l supplies A[l%16][8(l/16)..+8]
+// and B[8(l/16)..+8][l%16] and receives D[4(l/16)+i][l%16], i < 4.
+//   * The M row m of S-block b is unit token 8(m/4) + 4b + m%4, so lane l (r = l/16) ends up
+//     with the scores of tokens 8r..8r+7 for column l%16 — exactly the P operand slots it
+//     supplies to the P.V product (A[column][8r..8r+7]).  No score moves between lanes.
+//   * V tiles are [D][16 tokens] in the pool, so the B operand of the P.V product (tokens
+//     8r..8r+7 of one dimension) is one 16-byte load.
+//   * K tiles are [D/8][16][8]: a token's 8-element chunk, the A operand of S^T, is one
+//     16-byte load.
+// P is fed to the matrix core as hi + lo 16-bit parts (two products), which keeps the
+// rounding of the weights near 2^-16 relative instead of 2^-8 (bf16) or 2^-11 (fp16).
+#pragma once
+
+#include <math.h>
+
+#include <type_traits>
+
+#include "pa_device.h"
+
+namespace pa {
+
+template <int DT, int D>
+struct MfmaCfg {
+  static constexpr int E = 2;
+  static constexpr int NKK = D / 32;  // MFMAs over the head dimension per S-block
+  static constexpr int NJ = D / 16;   // MFMAs over output dims per unit
+  static constexpr int64_t TILE = 16LL * D * E;
+  static constexpr int DEPTH = 2;
+};
+
+template <int DT>
+using op8_t = typename std::conditional<DT == DT_BF16, bf16x8_t, f16x8_t>::type;
+
+template <int DT>
+__device__ __forceinline__ f32x4_t mfma(const op8_t<DT>& a, const op8_t<DT>& b, f32x4_t c) {
+  if constexpr (DT == DT_BF16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+template <int DT, int D>
+struct MfmaState {
+  float m;  // running max of head lane%16 (base-2 domain)
+  float l;  // this lane's share of the running sum of head lane%16
+  f32x4_t acc[MfmaCfg<DT, D>::NJ];  // O[head 4(l/16)+i][dim 16 j + l%16]
+};
+
+template <int DT, int D>
+using MfmaK = uint4[2][MfmaCfg<DT, D>::NKK];
+template <int DT, int D>
+using MfmaV = uint4[MfmaCfg<DT, D>::NJ];
+template <int DT, int D>
+using MfmaQ = op8_t<DT>[MfmaCfg<DT, D>::NKK];
+
+template <int DT, int D>
+struct MfmaLaneOffsets {
+  int k[2][MfmaCfg<DT, D>::NKK];  // byte offset inside the K tile, per S-block b and kk
+  int kt[2];                      // which tile of the unit (0 / 1) S-block b's token is in
+  int v[MfmaCfg<DT, D>::NJ];      // byte offset inside the V tile
+  int vt;                         // which tile of the unit this lane's V tokens are in
+};
+
+template <int DT, int D>
+__device__ __forceinline__ void mfma_load(MfmaK<DT, D>& kb, MfmaV<DT, D>& vb, const char* k0,
+                                          const char* k1, const char* v0, const char* v1,
+                                          const MfmaLaneOffsets<DT, D>& o) {
+  using C = MfmaCfg<DT, D>;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const char* kt = o.kt[b] ? k1 : k0;
+#pragma unroll
+    for (int kk = 0; kk < C::NKK; ++kk) kb[b][kk] = ld16(kt + o.k[b][kk]);
+  }
+  const char* vt = o.vt ? v1 : v0;
+#pragma unroll
+  for (int j = 0; j < C::NJ; ++j) vb[j] = ld16(vt + o.v[j]);
+}
+
+// One unit.  MASK: tokens 8r + k > lim (lim: last visible unit token of this lane's query
+// column; may differ per column) get no weight, and V elements of tokens >= vvalid (uniform:
+// tokens of the unit that hold written data) are zeroed so poison never reaches the sums.
+// SAFE: a column may have seen no key yet (its running max is still -inf).
+template <int DT, int D, bool MASK, bool SAFE>
+__device__ __forceinline__ void mfma_unit(MfmaState<DT, D>& st, const MfmaK<DT, D>& kb,
+                                          MfmaV<DT, D>& vb, const MfmaQ<DT, D>& qb,
+                                          float scale_log2, int lim, int vvalid) {
+  using C = MfmaCfg<DT, D>;
+  using T = op8_t<DT>;
+  const int lane = lane_id();
+  const int r = lane >> 4;
+  f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < C::NKK; ++kk) {
+    s0 = mfma<DT>(__builtin_bit_cast(T, kb[0][kk]), qb[kk], s0);
+    s1 = mfma<DT>(__builtin_bit_cast(T, kb[1][kk]), qb[kk], s1);
+  }
+  float s[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    s[i] = s0[i] * scale_log2;
+    s[4 + i] = s1[i] * scale_log2;
+  }
+  if (MASK) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (8 * r + k > lim) s[k] = -INFINITY;
+    // zero the V elements of tokens past the written context (0 * NaN is NaN)
+    const int kv = min(8, max(0, vvalid - 8 * r));
+    const uint32_t m0 = (0 < kv ? 0xffffu : 0u) | (1 < kv ? 0xffff0000u : 0u);
+    const uint32_t m1 = (2 < kv ? 0xffffu : 0u) | (3 < kv ? 0xffff0000u : 0u);
+    const uint32_t m2 = (4 < kv ? 0xffffu : 0u) | (5 < kv ? 0xffff0000u : 0u);
+    const uint32_t m3 = (6 < kv ? 0xffffu : 0u) | (7 < kv ? 0xffff0000u : 0u);
+#pragma unroll
+    for (int j = 0; j < C::NJ; ++j) {
+      vb[j].x &= m0;
+      vb[j].y &= m1;
+      vb[j].z &= m2;
+      vb[j].w &= m3;
+    }
+  }
+  float mx = s[0];
+#pragma unroll
+  for (int k = 1; k < 8; ++k) mx = fmaxf(mx, s[k]);
+  mx = cross_rows_max(mx);
+  const float mnew = fmaxf(st.m, mx);
+  // SAFE: a column with no visible key so far keeps m = -inf, weight 0, and alpha 1
+  const float mref = (SAFE && mnew == -INFINITY) ? 0.f : mnew;
+  const float alpha = __builtin_amdgcn_exp2f(st.m - mref);
+  float psum = 0.f;
+  T phi, plo;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float p = __builtin_amdgcn_exp2f(s[k] - mref);
+    psum += p;
+    if constexpr (DT == DT_BF16) {
+      const __bf16 h = (__bf16)p;
+      phi[k] = h;
+      plo[k] = (__bf16)(p - (float)h);
+    } else {
+      const _Float16 h = (_Float16)p;
+      phi[k] = h;
+      plo[k] = (_Float16)(p - (float)h);
+    }
+  }
+  st.l = st.l * alpha + psum;
+  st.m = mnew;
+  // rescale the output rows (heads 4r + i) by their own alpha
+  float a4[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) a4[i] = shfl(alpha, 4 * r + i);
+#pragma unroll
+  for (int j = 0; j < C::NJ; ++j) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) st.acc[j][i] *= a4[i];
+    st.acc[j] = mfma<DT>(phi, __builtin_bit_cast(T, vb[j]), st.acc[j]);
+    st.acc[j] = mfma<DT>(plo, __builtin_bit_cast(T, vb[j]), st.acc[j]);
+  }
+}
+
+// Write the first G query columns of a finished piece: the normalised output (to `out`,
+// column c at out_base + c * out_col_stride, or to a partial slot, column c at
+// po + c * po_col_stride), plus each column's max / sum for partial slots.  A column that
+// saw no key writes 0.
+template <int DT, int D>
+__device__ __forceinline__ void mfma_emit(const MfmaState<DT, D>& st, int G, float* po, float* pm,
+                                          float* pl, int64_t po_col_stride, void* out,
+                                          int64_t out_base, int64_t out_col_stride, bool out_f32) {
+  using C = MfmaCfg<DT, D>;
+  const int lane = lane_id();
+  const int r = lane >> 4, n = lane & 15;
+  const float ltot = cross_rows_sum(st.l);  // sum of head n over the four lane rows
+  const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+  float inv4[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) inv4[i] = shfl(inv, 4 * r + i);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int hh = 4 * r + i;
+    if (hh < G) {
+#pragma unroll
+      for (int j = 0; j < C::NJ; ++j) {
+        const float v = st.acc[j][i] * inv4[i];
+        if (po)
+          po[hh * po_col_stride + 16 * j + n] = v;
+        else
+          store_out<DT>(out, out_base + (int64_t)hh * out_col_stride + 16 * j + n, v, out_f32);
+      }
+    }
+  }
+  if (pm && r == 0 && n < G) {
+    pm[n * (po_col_stride / D)] = st.m * 0.69314718055994531f;
+    pl[n * (po_col_stride / D)] = ltot;
+  }
+}
+
+}  // namespace pa

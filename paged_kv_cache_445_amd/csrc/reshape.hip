@@ -1,0 +1,64 @@
+// reshape.hip — the paged KV-cache write ("vLLM 架构源码解析 第1篇" §3.3.3: reshape_and_cache
+// scatters this step's K and V into the block pool at slot_mapping before attention; the
+// block / offset split of a slot is §4.2's `//` and `%` by the 16-token block size).
+//
+// One thread per 16-byte K chunk, then one thread per V element.  Consecutive threads read
+// consecutive input bytes (coalesced loads); K chunk stores are 16-byte stores into the
+// token's row of each 256-byte chunk plane; V stores are single elements into the token's
+// column of each dimension row.  The copy is a bit copy: no conversion.
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+
+template <int DT>
+__global__ __launch_bounds__(256) void reshape_and_cache_kernel(ReshapeArgs a) {
+  constexpr int E = DtInfo<DT>::bytes;
+  constexpr int X = DtInfo<DT>::x;
+  const int H = a.num_kv_heads, D = a.head_dim, NCH = D / X;
+  const int64_t nk = a.num_tokens * H * NCH;
+  const int64_t nv = a.num_tokens * H * D;
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (tid < nk) {
+    const int64_t t = tid / (H * NCH);
+    const int rem = (int)(tid - t * H * NCH);
+    const int g = rem / NCH, c = rem - g * NCH;
+    const int64_t slot = a.slot_mapping[t];
+    if (slot < 0) return;  // padding token
+    const int64_t blk = slot / kBlock;
+    const int off = (int)(slot - blk * kBlock);
+    const uint4 v = ld16(reinterpret_cast<const char*>(a.key) + ((t * H + g) * D + c * X) * E);
+    char* dst = reinterpret_cast<char*>(a.k_cache) +
+                ((((blk * H + g) * NCH + c) * kBlock + off) * 16);
+    *reinterpret_cast<uint4*>(dst) = v;
+  } else if (tid < nk + nv) {
+    const int64_t e = tid - nk;
+    const int64_t t = e / (H * D);
+    const int rem = (int)(e - t * H * D);
+    const int g = rem / D, d = rem - g * D;
+    const int64_t slot = a.slot_mapping[t];
+    if (slot < 0) return;
+    const int64_t blk = slot / kBlock;
+    const int off = (int)(slot - blk * kBlock);
+    const int64_t dst = ((blk * H + g) * D + d) * kBlock + off;
+    if constexpr (E == 4)
+      reinterpret_cast<uint32_t*>(a.v_cache)[dst] = reinterpret_cast<const uint32_t*>(a.value)[e];
+    else
+      reinterpret_cast<uint16_t*>(a.v_cache)[dst] = reinterpret_cast<const uint16_t*>(a.value)[e];
+  }
+}
+
+hipError_t launch_reshape(int dt, const ReshapeArgs& a, hipStream_t st) {
+  const int X = dt == DT_F32 ? 4 : 8;
+  const int64_t threads = a.num_tokens * a.num_kv_heads * (a.head_dim / X + a.head_dim);
+  const int64_t grid = (threads + 255) / 256;
+  if (grid == 0) return hipSuccess;
+  switch (dt) {
+    case DT_F32: hipLaunchKernelGGL(reshape_and_cache_kernel<DT_F32>, dim3((unsigned)grid), dim3(256), 0, st, a); break;
+    case DT_F16: hipLaunchKernelGGL(reshape_and_cache_kernel<DT_F16>, dim3((unsigned)grid), dim3(256), 0, st, a); break;
+    default:     hipLaunchKernelGGL(reshape_and_cache_kernel<DT_BF16>, dim3((unsigned)grid), dim3(256), 0, st, a); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace pa
