@@ -1,0 +1,244 @@
+"""Paged-attention decode benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--workload llama7b_f16]
+
+One step is one pass of the whole hot path over one synthetic decode batch resident in
+HBM: the cache write of the step's new tokens (pa_reshape_and_cache) followed by
+attention over every sequence's paged context (pa_decode).  Several copies of the K/V
+pools are rotated between steps so that no step finds the previous step's blocks in the
+256 MB last-level cache: every step reads its KV bytes from HBM.
+
+Prints ONE JSON line.  `value` is the effective KV-read bandwidth of the whole step:
+algorithmic KV bytes (every context token's K and V read once per KV head) divided by
+the step time.  `roofline` rates pa_decode alone (its kernels timed with HIP events on the
+stream they run on) against the 8 TB/s HBM peak.  `cpu_baseline` times the fp64 CPU
+oracle on the same batch on the host cores.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+# rocprof-derived HBM traffic of the decode kernels, with the hash of the sources it was
+# measured on; reported only while those sources are unchanged
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_{workload}.txt")
+KERNEL_SOURCES = ["pa_device.h", "pa_internal.h", "pa_mfma.h", "decode_valu.hip",
+                  "decode_mfma.hip", "reduce.hip", "chunk.hip", "pa_api.cpp"]
+
+DESCRIPTIONS = {
+    "llama7b_f16": "LLaMA-7B-shaped decode: 32 seqs x 32 heads (MHA), head_dim 128, fp16 KV, "
+                   "block 16, ctx U[256,2048], 8192-block pool, permuted block table",
+    "gqa_long_bf16": "GQA decode: 64 seqs, 64 q / 8 kv heads, head_dim 128, bf16 KV, block 16, "
+                     "ctx log-uniform [128,32768]",
+    "prefix_shared_f16": "prefix-shared decode: 128 seqs x 32 heads, head_dim 128, fp16 KV, "
+                         "32 shared leading blocks + private tail U[16,1024]",
+    "mixed_chunked_bf16": "mixed step: 8 x 512-row causal chunks + 120 decode rows, 32 q / 8 kv "
+                          "heads, head_dim 128, bf16 KV",
+    "tiny_f32": "tiny decode: 4 seqs x 4 heads, head_dim 64, fp32 KV",
+}
+
+
+def sources_digest():
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "paged_kv_cache_445_amd", "csrc", name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def read_traffic(workload):
+    """HBM bytes per pa_decode call from a committed rocprof counter summary, or None."""
+    path = TRAFFIC_FILE.format(workload=workload)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_sha = re.search(r"^source_sha256:\s*([0-9a-f]{64})", text, re.M)
+    m_b = re.search(r"^hbm_bytes_per_call:\s*([0-9.eE+]+)", text, re.M)
+    if not m_sha or not m_b or m_sha.group(1) != sources_digest():
+        return None
+    return float(m_b.group(1))
+
+
+def cpu_baseline(b, min_seconds, threads):
+    """fp64 oracle over the whole batch, repeated until min_seconds have passed.  The
+    oracle's pools are written by its own cache write from the batch's token records."""
+    import oracle
+    from paged_kv_cache_445_amd import workloads as W
+    g = oracle.make_geom(b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim, b.num_blocks,
+                         b.max_blocks_per_seq, b.dtype, b.block_size)
+    kp = W.nan_pool(b.k_pool_shape(), b.dtype)
+    vp = W.nan_pool(b.v_pool_shape(), b.dtype)
+    oracle.reshape_and_cache(b.key, b.value, kp, vp, b.slot, g)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.paged_attention(b.q, kp, vp, b.block_tables, b.context_lens, b.query_start_loc,
+                               b.scale, g, threads=threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    per = el / reps
+    return {"value": round(b.kv_bytes() / per / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"the whole {b.name} batch ({b.num_q_rows} rows x {b.num_q_heads} heads, "
+                      f"{b.kv_bytes() / 1e6:.1f} MB of KV), {reps} passes in {el:.1f} s "
+                      f"({per * 1e3:.1f} ms per pass, {b.num_seqs * b.num_q_heads / per:.0f} "
+                      f"seq-heads/s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="llama7b_f16",
+                    choices=sorted(DESCRIPTIONS))
+    ap.add_argument("--copies", type=int, default=0,
+                    help="K/V pool copies rotated between steps (0: enough for >= 1 GiB)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="wall time of the CPU-oracle leg (0 skips it)")
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="oracle threads (0: min(16, host cores))")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="after the timed steps, copy a MIB-sized device buffer 3 times "
+                         "(a reference kernel of known traffic for HBM byte counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the decode shards by KV head with no exchange inside attention, so there is "
+              "no multi-GPU step to time here)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_445_amd import workloads as W
+    from paged_kv_cache_445_amd.device_batch import DeviceBatch
+    from paged_kv_cache_445_amd import pa
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    print(f"[bench] building workload {args.workload}", file=sys.stderr, flush=True)
+    b = W.make(args.workload)
+    kv_bytes = b.kv_bytes()
+    db = DeviceBatch(b, device=dev)
+    db.prefill()
+    torch.cuda.synchronize()
+    # the history staging tensors are not needed after the pools are written
+    db.key_hist = db.value_hist = db.slot_hist = None
+
+    copies = args.copies or max(2, math.ceil((1 << 30) / kv_bytes) + 1)
+    pools = [(db.k_cache, db.v_cache)] + [(db.k_cache.clone(), db.v_cache.clone())
+                                           for _ in range(copies - 1)]
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        kc, vc = pools[i % copies]
+        pa.reshape_and_cache(db.key_new, db.value_new, kc, vc, db.slot_new, db.geom)
+        if ev is not None:
+            ev[0].record(stream)
+        pa.decode(db.out, db.q, kc, vc, db.block_tables, db.context_lens, db.qsl, db.scale,
+                  db.workspace, db.geom)
+        if ev is not None:
+            ev[1].record(stream)
+
+    print(f"[bench] warmup {args.warmup} steps, {copies} pool copies", file=sys.stderr,
+          flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dec_ms = [a.elapsed_time(c) for a, c in evs]
+    print(f"[bench] timed {args.steps} steps in {wall:.4f} s", file=sys.stderr, flush=True)
+
+    ms_per_step = wall * 1e3 / args.steps
+    dec_avg_ms = float(np.mean(dec_ms))
+    seq_heads = b.num_q_rows * b.num_q_heads
+    value = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = kv_bytes / (dec_avg_ms * 1e-3) / 1e9
+    traffic = read_traffic(args.workload)
+
+    if args.copy_calibration > 0:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] copy calibration: 3 x {n} bytes", file=sys.stderr, flush=True)
+        del src, dst
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        threads = args.cpu_threads or min(16, os.cpu_count() or 1)
+        print(f"[bench] cpu oracle leg, {threads} threads", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(b, args.cpu_seconds, threads)
+
+    line = {
+        "metric": "paged-attn decode: effective KV-read HBM GB/s (% of peak) and seq-heads/sec",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16" if b.dtype == "f16" else b.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload,
+            "description": DESCRIPTIONS[args.workload],
+            "num_seqs": b.num_seqs, "num_q_rows": b.num_q_rows,
+            "num_q_heads": b.num_q_heads, "num_kv_heads": b.num_kv_heads,
+            "head_dim": b.head_dim, "block_size": b.block_size,
+            "kv_dtype": b.dtype, "accumulate": "f32",
+            "context_tokens": int(b.context_lens.astype(np.int64).sum()),
+            "kv_bytes_per_step": kv_bytes,
+            "pool_copies_rotated": copies,
+        },
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "seq_heads_per_s": round(seq_heads / (ms_per_step * 1e-3), 1),
+        "pa_decode_us": round(dec_avg_ms * 1e3, 3),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "pa_decode (decode kernel + partial merge)",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -113,30 +113,51 @@ __global__ __launch_bounds__(kWG) void mfma_decode_kernel(DecodeArgs a) {
   if constexpr (MODE == MODE_EVEN) {
     PlanIn pin{a.context_lens, a.qsl, S, kMfmaUnit};
     build_plan(base, tmp, pin);
-    const int64_t total = (int64_t)base[S] * segs;
-    const int64_t lo = range_lo(total, w, W), hi = range_lo(total, w + 1, W);
+    zero_empty_rows<DT>(pin, a.out, a.num_q_heads, D, w, W, a.out_f32);
+    // units: (sequence, group of kWavesPerWG heads, unit); workgroups split them evenly and
+    // wave i of a workgroup runs head i of each group
+    const int groups = (a.num_kv_heads + kWavesPerWG - 1) / kWavesPerWG;
+    const int64_t total = (int64_t)base[S] * groups;
+    const int64_t NK = min((int64_t)gridDim.x, total);  // workgroups with a share
+    const int64_t k = blockIdx.x;
+    MergeDesc* desc = static_cast<MergeDesc*>(a.desc);
+    if (k >= NK) {
+      write_desc(desc, w, 0, -1, false);
+      return;
+    }
+    const int64_t lo = range_lo(total, k, NK), hi = range_lo(total, k + 1, NK);
+    bool split_here = false;  // a split segment starts in this share (its last piece)
     for (int64_t i = lo; i < hi;) {
-      const int s = find_seq(base, S, i, segs);
+      const int s = find_seq(base, S, i, groups);
       const int nu = base[s + 1] - base[s];
-      const int64_t sbase = (int64_t)base[s] * segs;
-      const int g = (int)((i - sbase) / nu);
-      const int64_t seg0 = sbase + (int64_t)g * nu;
+      const int64_t sbase = (int64_t)base[s] * groups;
+      const int grp = (int)((i - sbase) / nu);
+      const int64_t seg0 = sbase + (int64_t)grp * nu;
       const int64_t pe = min(hi, seg0 + nu);
-      const int u0 = (int)(i - seg0), u1 = (int)(pe - seg0);
-      const int ctx = a.context_lens[s];
-      MfmaState<DT, D> st;
-      mfma_attend<DT, D>(a, s, g, u0, u1, ctx, st);
-      if (u0 == 0 && u1 == nu) {
+      const int g = grp * kWavesPerWG + wave;  // this wave's KV head
+      if (g < a.num_kv_heads) {
+        const int u0 = (int)(i - seg0), u1 = (int)(pe - seg0);
+        const int ctx = a.context_lens[s];
+        MfmaState<DT, D> st;
+        mfma_attend<DT, D>(a, s, g, u0, u1, ctx, st);
         const int row = a.qsl ? a.qsl[s] : s;
         const int64_t ob = ((int64_t)row * a.num_q_heads + (int64_t)g * G) * D;
-        mfma_emit<DT, D>(st, G, nullptr, nullptr, nullptr, D, a.out, ob, D, a.out_f32);
-      } else {
-        const int64_t slot = w * 2 + (i == lo ? 0 : 1);
-        mfma_emit<DT, D>(st, G, a.part_o + slot * G * D, a.part_m + slot * G,
-                         a.part_l + slot * G, D, nullptr, 0, 0, false);
+        if (u0 == 0 && u1 == nu) {
+          mfma_emit<DT, D>(st, G, nullptr, nullptr, nullptr, D, a.out, ob, D, a.out_f32);
+        } else {
+          const int64_t slot = w * 2 + (i == lo ? 0 : 1);
+          mfma_emit<DT, D>(st, G, a.part_o + slot * G * D, a.part_m + slot * G,
+                           a.part_l + slot * G, D, nullptr, 0, 0, false);
+          if (seg0 >= lo && seg0 + nu > hi) {
+            const SplitSeg sg = split_seg(total, NK, seg0, seg0 + nu - 1, wave);
+            write_desc(desc, w, ob, (int)sg.k1, sg.k0_later);
+            split_here = true;
+          }
+        }
       }
       i = pe;
     }
+    if (!split_here) write_desc(desc, w, 0, -1, false);
   } else {
     const int PU = a.partition_units;  // 32-token units per partition
     const int P = a.max_partitions;

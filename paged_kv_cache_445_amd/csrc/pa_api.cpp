@@ -6,7 +6,7 @@
 #include <atomic>
 #include <cmath>
 
-#include "../../include/pa.h"
+#include "pa.h"
 #include "pa_internal.h"
 
 namespace pa {
@@ -54,7 +54,8 @@ int cu_count() {
   return n;
 }
 
-// optional override of resident workgroups per CU for the split kernels (tuning)
+// optional choice of resident workgroups per CU for the split kernels (tuning; capped at the
+// kernel's occupancy)
 int wg_per_cu_override() {
   static int v = [] {
     const char* s = getenv("PA_DECODE_WG_PER_CU");
@@ -67,25 +68,40 @@ bool use_mfma(const pa_geom* g) {
   return g->kv_dtype != PA_F32 && g->num_q_heads / g->num_kv_heads >= 2;
 }
 
-int lds_bytes(const pa_geom* g) { return (g->num_seqs + 1 + pa::kWG) * (int)sizeof(int32_t); }
+// LDS of the split kernels: the per-sequence plan (num_seqs + 1 ints) and a scan buffer.
+// Occupancy is evaluated for num_seqs rounded up to a power of two, so a handful of cached
+// values covers every batch size.
+int seq_bucket(int num_seqs) {
+  int b = 0;
+  while ((1 << b) < num_seqs + 1) ++b;
+  return b;  // (1 << b) >= num_seqs + 1; b <= 14 for kMaxSeqs = 8192
+}
+
+int bucket_lds_bytes(int bucket) { return ((1 << bucket) + pa::kWG) * (int)sizeof(int32_t); }
+
+// resident workgroups per CU for pa_decode's even split (vector path, matrix-core path)
+constexpr int kEvenWgPerCu[2] = {1, 2};
 
 // workgroups of the split kernel: every CU full at the kernel's occupancy
 int split_grid(const pa_geom* g, int mode) {
-  static std::atomic<int> cache[kMaxDevices][2][3][2][2];
+  static std::atomic<int> cache[kMaxDevices][2][3][2][2][15];
   const int dev = current_device();
   const int path = use_mfma(g) ? 1 : 0;
   const int di = g->head_dim == 64 ? 0 : 1;
-  std::atomic<int>& c = cache[dev][path][g->kv_dtype][di][mode];
+  const int bk = seq_bucket(g->num_seqs);
+  std::atomic<int>& c = cache[dev][path][g->kv_dtype][di][mode][bk];
   int occ = c.load(std::memory_order_relaxed);
   if (occ <= 0) {
-    const int lds = (kMaxSeqs + 1 + pa::kWG) * (int)sizeof(int32_t);  // worst case
+    const int lds = bucket_lds_bytes(bk);
     occ = path ? pa::mfma_decode_max_blocks_per_cu(g->kv_dtype, g->head_dim, mode, lds)
                : pa::valu_decode_max_blocks_per_cu(g->kv_dtype, g->head_dim, mode, lds);
     c.store(occ, std::memory_order_relaxed);
   }
+  // The even split streams best with few resident workgroups per CU: each of them reads
+  // four adjacent heads of a block at a time, and more of them only add split pieces.
   const int o = wg_per_cu_override();
-  if (o > 0 && o < occ) occ = o;
-  return cu_count() * occ;
+  const int want = o > 0 ? o : (mode == pa::MODE_EVEN ? kEvenWgPerCu[path] : occ);
+  return cu_count() * (want < occ ? want : occ);
 }
 
 struct SplitShape {
@@ -97,10 +113,17 @@ SplitShape split_shape(const pa_geom* g) {
   return {g->num_q_heads, 1, pa::kValuUnit};
 }
 
+// pa_decode's workspace: one merge descriptor per wave of the split grid, then two partial
+// slots per wave: o [W][2][G][D], m [W][2][G], l [W][2][G].
+size_t desc_bytes(int grid) {
+  const size_t n = (size_t)grid * pa::kWavesPerWG * sizeof(pa::MergeDesc);
+  return (n + 255) / 256 * 256;
+}
+
 size_t even_workspace_bytes(const pa_geom* g, int grid) {
   const SplitShape sh = split_shape(g);
   const size_t slots = (size_t)grid * pa::kWavesPerWG * 2 * sh.heads_per_seg;
-  return slots * ((size_t)g->head_dim + 2) * sizeof(float);
+  return desc_bytes(grid) + slots * ((size_t)g->head_dim + 2) * sizeof(float);
 }
 
 pa_status hip_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
@@ -170,7 +193,7 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
   const SplitShape sh = split_shape(g);
   const size_t slots = (size_t)grid * pa::kWavesPerWG * 2 * sh.heads_per_seg;
-  float* part_o = static_cast<float*>(workspace);
+  float* part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + desc_bytes(grid));
   float* part_m = part_o + slots * g->head_dim;
   float* part_l = part_m + slots;
 
@@ -185,6 +208,7 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   a.part_o = part_o;
   a.part_m = part_m;
   a.part_l = part_l;
+  a.desc = workspace;
   a.num_seqs = g->num_seqs;
   a.num_q_heads = g->num_q_heads;
   a.num_kv_heads = g->num_kv_heads;
@@ -197,25 +221,17 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
                              : pa::launch_valu_decode(g->kv_dtype, pa::MODE_EVEN, a, grid, st);
   if (e != hipSuccess) return PA_ERR_HIP;
 
-  pa::EvenReduceArgs r{};
-  r.out = out;
-  r.part_o = part_o;
-  r.part_m = part_m;
-  r.part_l = part_l;
-  r.context_lens = context_lens;
-  r.qsl = query_start_loc;
-  r.num_seqs = g->num_seqs;
-  r.num_q_heads = g->num_q_heads;
-  r.num_kv_heads = g->num_kv_heads;
-  r.head_dim = g->head_dim;
-  r.segs = sh.segs;
-  r.heads_per_seg = sh.heads_per_seg;
-  r.unit_tokens = sh.unit;
-  r.num_waves = grid * pa::kWavesPerWG;
-  r.out_f32 = a.out_f32;
-  const int64_t items = (int64_t)g->num_seqs * sh.segs;
-  const int rgrid = (int)(items < (int64_t)cu_count() * 8 ? items : (int64_t)cu_count() * 8);
-  e = pa::launch_even_reduce(g->kv_dtype, r, rgrid, st);
+  pa::MergeArgs m{};
+  m.out = out;
+  m.part_o = part_o;
+  m.part_m = part_m;
+  m.part_l = part_l;
+  m.desc = workspace;
+  m.num_waves = grid * pa::kWavesPerWG;
+  m.rows = sh.heads_per_seg;
+  m.head_dim = g->head_dim;
+  m.out_f32 = a.out_f32;
+  e = pa::launch_merge(g->kv_dtype, m, st);
   if (e != hipSuccess) return PA_ERR_HIP;
 
   if (query_start_loc) {

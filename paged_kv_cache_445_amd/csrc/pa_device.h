@@ -7,6 +7,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 
 #include "pa_internal.h"
@@ -112,17 +113,30 @@ __device__ __forceinline__ float row16_sum(float v) {
 __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, kWave); }
 __device__ __forceinline__ float shfl(float v, int src) { return __shfl(v, src, kWave); }
 
-// sum over lanes {l, l^16, l^32, l^48}: the four DPP rows
-__device__ __forceinline__ float cross_rows_sum(float v) {
-  v += shfl_xor(v, 16);
-  v += shfl_xor(v, 32);
-  return v;
+// v[l] + v[l ^ 16] and v[l] + v[l ^ 32] through the gfx950 lane-swap instructions:
+// v_permlane16_swap exchanges the odd rows of its first operand with the even rows of its
+// second, v_permlane32_swap the upper half of the first with the lower half of the second.
+// With both operands equal to v, the two results hold v and its partner lane's value.
+__device__ __forceinline__ float xor16_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
-__device__ __forceinline__ float cross_rows_max(float v) {
-  v = fmaxf(v, shfl_xor(v, 16));
-  v = fmaxf(v, shfl_xor(v, 32));
-  return v;
+__device__ __forceinline__ float xor32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
+__device__ __forceinline__ float xor16_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// sum / max over lanes {l, l^16, l^32, l^48}: the four DPP rows
+__device__ __forceinline__ float cross_rows_sum(float v) { return xor32_sum(xor16_sum(v)); }
+__device__ __forceinline__ float cross_rows_max(float v) { return xor32_max(xor16_max(v)); }
 
 __device__ __forceinline__ int readlane(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
 __device__ __forceinline__ float readlane(float v, int l) {
@@ -149,6 +163,20 @@ __device__ __forceinline__ int32_t seq_units(const PlanIn& p, int s) {
   if (rows != 1) return 0;  // multi-row sequences are not split-context work
   const int32_t ctx = p.context_lens[s];
   return ctx > 0 ? (ctx + p.unit_tokens - 1) / p.unit_tokens : 0;
+}
+
+// Decode rows (sequences with one query row) whose context is empty get a zero output;
+// wave w of W handles sequences w, w + W, ...
+template <int DT>
+__device__ void zero_empty_rows(const PlanIn& p, void* out, int Hq, int D, int64_t w, int64_t W,
+                                bool out_f32) {
+  for (int64_t s = w; s < p.num_seqs; s += W) {
+    const int32_t rows = p.qsl ? p.qsl[s + 1] - p.qsl[s] : 1;
+    if (rows != 1 || p.context_lens[s] > 0) continue;
+    const int64_t row = p.qsl ? p.qsl[s] : s;
+    for (int e = __lane_id(); e < Hq * D; e += kWave)
+      store_out<DT>(out, row * Hq * D + e, 0.f, out_f32);
+  }
 }
 
 // base[0..S] in LDS; `tmp` is kWG ints of LDS.  Must be called by all threads of the WG.
@@ -195,9 +223,126 @@ __device__ __forceinline__ int find_seq(const int32_t* base, int S, int64_t i, i
   return lo;
 }
 
-// even split of [0, total) over W waves: wave w owns [range_lo(w), range_lo(w+1))
+// Even split of [0, total) over W waves (W <= total, so every share is non-empty): wave w
+// owns [range_lo(w), range_lo(w + 1)); unit i belongs to wave owner(i).
 __device__ __forceinline__ int64_t range_lo(int64_t total, int64_t w, int64_t W) {
   return (total * w) / W;
+}
+__device__ __forceinline__ int64_t owner(int64_t total, int64_t i, int64_t W) {
+  return ((i + 1) * W - 1) / total;
+}
+
+// Split-segment bookkeeping of the even split.  The split is over workgroups: workgroup k
+// owns units [range_lo(k), range_lo(k + 1)) of the flattened (sequence, head group, unit)
+// list, and wave i of the workgroup runs head i of every group.  A segment (one sequence and
+// head group) occupying units [seg0, seg1] that crosses a workgroup boundary has one piece in
+// each workgroup k0..k1 (k0 = owner(seg0), k1 = owner(seg1)); wave i's piece of workgroup k
+// sits in partial slot 2 (4k + i) + 0 when it is the first piece of k's share and + 1
+// otherwise (only k0's piece can be a later piece).  Wave i of k0 records the segment in its
+// descriptor; the merge kernel that follows combines the pieces of that wave's head.
+struct SplitSeg {
+  int64_t k0, k1;
+  bool k0_later;  // k0's piece is not the first piece of k0's share
+  int wave;       // wave index inside the workgroups (the head within the group)
+};
+
+__device__ __forceinline__ SplitSeg split_seg(int64_t total, int64_t NK, int64_t seg0,
+                                              int64_t seg1, int wave) {
+  SplitSeg r;
+  r.k0 = owner(total, seg0, NK);
+  r.k1 = owner(total, seg1, NK);
+  r.k0_later = range_lo(total, r.k0, NK) < seg0;
+  r.wave = wave;
+  return r;
+}
+
+__device__ __forceinline__ int64_t piece_slot(const SplitSeg& sg, int64_t k) {
+  return 2 * (kWavesPerWG * k + sg.wave) + ((k == sg.k0 && sg.k0_later) ? 1 : 0);
+}
+
+// Lane 0 of wave w writes its descriptor (called once per wave and launch).  k1 < 0: none.
+__device__ __forceinline__ void write_desc(MergeDesc* desc, int64_t w, int64_t out_base, int k1,
+                                           bool k0_later) {
+  if (__lane_id() == 0) {
+    MergeDesc d;
+    d.out_base = out_base;
+    d.k1 = k1;
+    d.k0_later = k0_later ? 1 : 0;
+    desc[w] = d;
+  }
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// Log-sum-exp merge of a split segment's pieces (one wave).  Each slot holds `rows` (<= MR)
+// rows (query heads) of a softmax-normalised output o [rows][D], its max m (natural-log
+// domain) and sum l; merged row r goes to out[out_base + r * D + d].  Lane p fetches the
+// (m, l) of piece p for every row at once, then every lane accumulates its output elements
+// (64 j + lane of the rows x D block) over the pieces, so a batch of up to 64 pieces costs
+// two dependent loads.
+template <int DT, int D, int MR>
+__device__ void merge_pieces(const float* part_o, const float* part_m, const float* part_l,
+                             int rows, const SplitSeg& sg, void* out, int64_t out_base,
+                             bool out_f32) {
+  constexpr int NE = MR * D / kWave;  // output elements per lane at rows == MR
+  const int lane = __lane_id();
+  const int np = (int)(sg.k1 - sg.k0 + 1);
+  const int ne = rows * D / kWave;
+  float M[MR], L[MR], acc[NE];
+#pragma unroll
+  for (int r = 0; r < MR; ++r) {
+    M[r] = -INFINITY;
+    L[r] = 0.f;
+  }
+#pragma unroll
+  for (int j = 0; j < NE; ++j) acc[j] = 0.f;
+  for (int p0 = 0; p0 < np; p0 += kWave) {
+    const int pn = min(kWave, np - p0);
+    const bool act = lane < pn;
+    const int64_t my = act ? piece_slot(sg, sg.k0 + p0 + lane) * rows : 0;
+    float m[MR], l[MR], wt[MR], sc[MR];
+#pragma unroll
+    for (int r = 0; r < MR; ++r) {
+      m[r] = (act && r < rows) ? part_m[my + r] : -INFINITY;
+      l[r] = (act && r < rows) ? part_l[my + r] : 0.f;
+    }
+#pragma unroll
+    for (int r = 0; r < MR; ++r) {
+      if (r < rows) {
+        const float mn = fmaxf(M[r], wave_max(m[r]));
+        sc[r] = M[r] == -INFINITY ? 0.f : __expf(M[r] - mn);
+        wt[r] = act ? l[r] * __expf(m[r] - mn) : 0.f;
+        L[r] = L[r] * sc[r] + wave_sum(wt[r]);
+        M[r] = mn;
+      } else {
+        sc[r] = 0.f;
+        wt[r] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NE; ++j) acc[j] *= sc[64 * j / D];
+    for (int p = 0; p < pn; ++p) {
+      const int64_t base = piece_slot(sg, sg.k0 + p0 + p) * rows * D + lane;
+      float o[NE];
+#pragma unroll
+      for (int j = 0; j < NE; ++j) o[j] = j < ne ? part_o[base + 64 * j] : 0.f;
+#pragma unroll
+      for (int j = 0; j < NE; ++j) {
+        const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt[64 * j / D]), p));
+        acc[j] = fmaf(w, o[j], acc[j]);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NE; ++j)
+    if (j < ne) store_out<DT>(out, out_base + 64 * j + lane, acc[j] / L[64 * j / D], out_f32);
 }
 
 }  // namespace pa

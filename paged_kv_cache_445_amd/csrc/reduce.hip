@@ -11,60 +11,21 @@
 
 namespace pa {
 
-// Merge for pa_decode's even split.  For every decode sequence s and segment g: if the
-// segment's units all fell inside one wavefront's share, that wave already wrote the
-// output; otherwise each wave w0..w1 touching it left one partial in slot
-// (w, first piece ? 0 : 1) and this kernel merges them.  Decode rows with no key get 0.
-template <int DT>
-__global__ __launch_bounds__(kWG) void even_reduce_kernel(EvenReduceArgs a) {
-  extern __shared__ int32_t lds[];
-  int32_t* base = lds;
-  int32_t* tmp = lds + a.num_seqs + 1;
-  const int S = a.num_seqs;
-  PlanIn pin{a.context_lens, a.qsl, S, a.unit_tokens};
-  build_plan(base, tmp, pin);
-  const int64_t T = (int64_t)base[S] * a.segs;
-  const int64_t W = a.num_waves;
-  const int hp = a.heads_per_seg, D = a.head_dim;
-  const int64_t items = (int64_t)S * a.segs;
-  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
-    const int s = (int)(it / a.segs), g = (int)(it % a.segs);
-    const int rows = a.qsl ? a.qsl[s + 1] - a.qsl[s] : 1;
-    if (rows != 1) continue;  // multi-row sequences are written by the chunk kernel
-    const int row = a.qsl ? a.qsl[s] : s;
-    const int nu = base[s + 1] - base[s];
-    const int64_t ob = ((int64_t)row * a.num_q_heads + (int64_t)g * hp) * D;
-    if (nu == 0) {  // no visible key
-      for (int e = threadIdx.x; e < hp * D; e += kWG) store_out<DT>(a.out, ob + e, 0.f, a.out_f32);
-      continue;
-    }
-    const int64_t seg0 = (int64_t)base[s] * a.segs + (int64_t)g * nu;
-    const int64_t seg1 = seg0 + nu - 1;
-    // wave owning flattened unit i: largest w with floor(w T / W) <= i
-    const int64_t w0 = ((seg0 + 1) * W - 1) / T;
-    const int64_t w1 = ((seg1 + 1) * W - 1) / T;
-    if (w0 == w1) continue;
-    const bool w0_second = range_lo(T, w0, W) < seg0;
-    // (when there are fewer units than waves, some waves own nothing and wrote no slot)
-    for (int e = threadIdx.x; e < hp * D; e += kWG) {
-      const int hh = e / D, d = e - hh * D;
-      float M = -INFINITY;
-      for (int64_t w = w0; w <= w1; ++w) {
-        if (range_lo(T, w, W) == range_lo(T, w + 1, W)) continue;
-        const int64_t slot = w * 2 + ((w == w0 && w0_second) ? 1 : 0);
-        M = fmaxf(M, a.part_m[slot * hp + hh]);
-      }
-      float L = 0.f, acc = 0.f;
-      for (int64_t w = w0; w <= w1; ++w) {
-        if (range_lo(T, w, W) == range_lo(T, w + 1, W)) continue;
-        const int64_t slot = w * 2 + ((w == w0 && w0_second) ? 1 : 0);
-        const float wp = a.part_l[slot * hp + hh] * __expf(a.part_m[slot * hp + hh] - M);
-        L += wp;
-        acc += wp * a.part_o[(slot * hp + hh) * D + d];
-      }
-      store_out<DT>(a.out, ob + e, acc / L, a.out_f32);
-    }
-  }
+// Second kernel of pa_decode: wave w (head w % 4 of workgroup w / 4 of the split kernel)
+// merges the split segment that starts in that workgroup's share for its head, if any.
+template <int DT, int D, int MR>
+__global__ __launch_bounds__(kWG) void merge_kernel(MergeArgs a) {
+  const int64_t w = (int64_t)blockIdx.x * kWavesPerWG + threadIdx.x / kWave;
+  if (w >= a.num_waves) return;
+  const MergeDesc d = static_cast<const MergeDesc*>(a.desc)[w];
+  if (d.k1 < 0) return;
+  SplitSeg sg;
+  sg.k0 = w / kWavesPerWG;
+  sg.k1 = d.k1;
+  sg.k0_later = d.k0_later != 0;
+  sg.wave = (int)(w % kWavesPerWG);
+  merge_pieces<DT, D, MR>(a.part_o, a.part_m, a.part_l, a.rows, sg, a.out, d.out_base,
+                          a.out_f32);
 }
 
 // pa_decode_reduce: one wavefront per (row, head), lanes over the head dimension.
@@ -93,15 +54,31 @@ __global__ __launch_bounds__(kWG) void part_reduce_kernel(PartReduceArgs a) {
   }
 }
 
-hipError_t launch_even_reduce(int dt, const EvenReduceArgs& a, int grid, hipStream_t st) {
-  const size_t lds = (size_t)(a.num_seqs + 1 + kWG) * sizeof(int32_t);
+template <int DT, int D>
+static void launch_merge_d(const MergeArgs& a, int grid, hipStream_t st) {
+  if (a.rows == 1)
+    hipLaunchKernelGGL((merge_kernel<DT, D, 1>), dim3(grid), dim3(kWG), 0, st, a);
+  else
+    hipLaunchKernelGGL((merge_kernel<DT, D, 16>), dim3(grid), dim3(kWG), 0, st, a);
+}
+
+template <int DT>
+static void launch_merge_t(const MergeArgs& a, int grid, hipStream_t st) {
+  if (a.head_dim == 64)
+    launch_merge_d<DT, 64>(a, grid, st);
+  else
+    launch_merge_d<DT, 128>(a, grid, st);
+}
+
+hipError_t launch_merge(int dt, const MergeArgs& a, hipStream_t st) {
+  const int grid = (a.num_waves + kWavesPerWG - 1) / kWavesPerWG;
   if (grid <= 0) return hipSuccess;
   if (dt == DT_F32)
-    hipLaunchKernelGGL(even_reduce_kernel<DT_F32>, dim3(grid), dim3(kWG), lds, st, a);
+    launch_merge_t<DT_F32>(a, grid, st);
   else if (dt == DT_F16)
-    hipLaunchKernelGGL(even_reduce_kernel<DT_F16>, dim3(grid), dim3(kWG), lds, st, a);
+    launch_merge_t<DT_F16>(a, grid, st);
   else
-    hipLaunchKernelGGL(even_reduce_kernel<DT_BF16>, dim3(grid), dim3(kWG), lds, st, a);
+    launch_merge_t<DT_BF16>(a, grid, st);
   return hipGetLastError();
 }
 

@@ -172,6 +172,33 @@ def test_physical_permutation_and_repeat_are_bitwise(dev):
         assert np.array_equal(run_gpu(dev, c).out_host(), ref)
 
 
+def test_shared_garbage_workspace(dev):
+    """One workspace, filled with garbage bytes, serves two geometries (vector and
+    matrix-core paths) in alternation without clearing; every call matches the oracle."""
+    import torch
+    rng = np.random.default_rng(11)
+    batches = [W.build_batch("ws_mha", "f16", rng.integers(1, 3000, size=24), np.ones(24), 8, 8,
+                             128, rng),
+               W.build_batch("ws_gqa", "bf16", rng.integers(1, 5000, size=9), np.ones(9), 16, 2,
+                             128, rng)]
+    dbs = [dev.DeviceBatch(b) for b in batches]
+    ws = torch.full((max(db.workspace.numel() for db in dbs),), 0xFF, dtype=torch.uint8,
+                    device="cuda")
+    wants = []
+    for b, db in zip(batches, dbs):
+        db.prefill()
+        db.write_new()
+        db.workspace = ws
+        kp, vp = H.oracle_pools(b)
+        wants.append(H.oracle_attention(b, kp, vp)[0])
+    for rep in range(3):
+        for b, db, want in zip(batches, dbs, wants):
+            db.out.zero_()
+            db.attend()
+            torch.cuda.synchronize()
+            check_out(db.out_host(), want, TOL[b.dtype], f"{b.name} call {rep}")
+
+
 # ----------------------------------------------------------------- split-context partials
 
 @pytest.mark.parametrize("dtype,Hq,Hkv,ps", [("bf16", 16, 2, 512), ("f16", 8, 8, 256),
