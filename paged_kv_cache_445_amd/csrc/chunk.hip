@@ -6,23 +6,35 @@
 // written by reshape_and_cache first, §3.3.3); row j sits at position ctx - n + j and attends
 // keys [0, ctx - n + j] (causal).  Decode rows (n = 1) are left to the decode kernels.
 //
-// Work item = (sequence, KV head g, block of 16 query columns), a column being one (row, head)
-// pair: 16 / G consecutive rows x the G query heads of g.  A wavefront streams the item's
-// keys in 32-token units through the matrix-core unit of pa_mfma.h with a per-column
-// causal limit.
+// Work item = (sequence, KV head g, block of 128 query columns), a column being one (row,
+// head) pair: 128 / G consecutive rows x the G query heads of g.  The workgroup stages each
+// 32-token K/V unit in LDS once and its four waves each run 32 columns over it through the
+// matrix-core step of pa_mfma.h, so one unit read from memory serves 128 columns.
 #include "pa_device.h"
 #include "pa_internal.h"
 #include "pa_mfma.h"
 
 namespace pa {
 
+constexpr int kChunkBlocks = 2;                       // 16-column MFMA blocks per wave
+constexpr int kWaveCols = 16 * kChunkBlocks;          // query columns per wave
+constexpr int kItemCols = kWaveCols * kWavesPerWG;    // query columns per workgroup
+
+template <int D>
+struct ChunkTile {
+  static constexpr int TILE = 16 * D * 2;                  // one block of one KV head, bytes
+  static constexpr int UNIT = 4 * TILE;                    // K and V of a 32-token unit
+  static constexpr int LOADS = UNIT / (kWG * 16);          // 16-byte loads per thread per unit
+  static constexpr int CPT = TILE / 16;                    // 16-byte chunks per tile
+};
+
 struct ChunkPlanIn {
   const int32_t* qsl;
   int32_t num_seqs;
-  int32_t rows_per_block;
+  int32_t rows_per_item;
 };
 
-// column blocks per sequence: ceil(n / rows_per_block) for multi-row sequences, else 0
+// work items per sequence: ceil(n / rows_per_item) for multi-row sequences, else 0
 __device__ inline void build_chunk_plan(int32_t* base, int32_t* tmp, const ChunkPlanIn& p) {
   const int t = threadIdx.x;
   const int S = p.num_seqs;
@@ -31,7 +43,7 @@ __device__ inline void build_chunk_plan(int32_t* base, int32_t* tmp, const Chunk
   int32_t sum = 0;
   for (int s = s0; s < s1; ++s) {
     const int32_t n = p.qsl[s + 1] - p.qsl[s];
-    const int32_t u = n > 1 ? (n + p.rows_per_block - 1) / p.rows_per_block : 0;
+    const int32_t u = n > 1 ? (n + p.rows_per_item - 1) / p.rows_per_item : 0;
     base[s] = u;
     sum += u;
   }
@@ -53,137 +65,195 @@ __device__ inline void build_chunk_plan(int32_t* base, int32_t* tmp, const Chunk
   __syncthreads();
 }
 
+// One work item: rows [j0, j0 + kItemCols / G) of multi-row sequence s for KV head g.  The
+// workgroup streams the item's keys in 32-token units: every unit (K and V of two blocks) is
+// loaded once by the whole workgroup into one of two LDS buffers, and each wave then runs
+// its 32 query columns (two 16-column MFMA blocks, per-column causal limits) over it.
 template <int DT, int D>
-__device__ void chunk_item(const DecodeArgs& a, int s, int g, int cb) {
+__device__ void chunk_item(const DecodeArgs& a, int s, int g, int cb, char* lds_units) {
   using C = MfmaCfg<DT, D>;
+  using CT = ChunkTile<D>;
   using T = op8_t<DT>;
+  constexpr int NCB = kChunkBlocks;
   const int lane = lane_id();
+  const int wave = threadIdx.x / kWave;
   const int r = lane >> 4, n = lane & 15;
   const int G = a.num_q_heads / a.num_kv_heads;
-  const int RB = kWave / 4 / G;  // rows per 16-column block
-  const int q0 = a.qsl[s], nrows = a.qsl[s + 1] - q0;
-  const int ctx = a.context_lens[s];
-  const int j0 = cb * RB;
-  const int jend = min(nrows, j0 + RB);
-  const int first_pos = ctx - nrows + j0;    // smallest last-visible key of the block
-  const int last_pos = ctx - nrows + jend - 1;
-  // this lane's query column
-  const int jc = j0 + n / G, hc = n % G;
-  const bool col_ok = jc < jend;
-  const int pos_c = col_ok ? ctx - nrows + jc : -1;
+  const int q0 = __builtin_amdgcn_readfirstlane(a.qsl[s]);
+  const int nrows = __builtin_amdgcn_readfirstlane(a.qsl[s + 1]) - q0;
+  const int ctx = __builtin_amdgcn_readfirstlane(a.context_lens[s]);
+  const int RW = kWaveCols / G;                    // rows per wave
+  const int j0g = cb * (kItemCols / G);            // first row of the workgroup
+  const int jendg = min(nrows, j0g + kItemCols / G);
+  const int j0 = j0g + wave * RW;                  // first row of this wave
+  const int jend = min(jendg, j0 + RW);
+  const int nkeys_g = ctx - nrows + jendg;         // keys any column of the item may see
+  const int nkeys_w = jend > j0 ? ctx - nrows + jend : 0;  // ... of this wave's columns
 
-  T qb[C::NKK];
-  {
+  T qb[NCB][C::NKK];
+  int pos[NCB];     // this lane's column's last visible key (-1: column past the rows)
+  int first[NCB];   // smallest last-visible key over the block's columns (uniform)
+  bool full[NCB];   // every column of the block is a real row (uniform)
+  bool live[NCB];   // the block has a real row (uniform)
+#pragma unroll
+  for (int c = 0; c < NCB; ++c) {
+    const int col = 16 * c + n;
+    const int jc = j0 + col / G, hc = col % G;
+    const bool ok = jc < jend;
+    pos[c] = ok ? ctx - nrows + jc : -1;
+    first[c] = ctx - nrows + j0 + (16 * c) / G;
+    full[c] = j0 + (16 * c + 15) / G < jend;
+    live[c] = j0 + (16 * c) / G < jend;
     const char* qp = reinterpret_cast<const char*>(a.q) +
                      ((int64_t)(q0 + jc) * a.num_q_heads + (int64_t)g * G + hc) * D * C::E;
 #pragma unroll
     for (int kk = 0; kk < C::NKK; ++kk) {
-      const uint4 v = col_ok ? ld16(qp + (4 * kk + r) * 16) : make_uint4(0, 0, 0, 0);
-      qb[kk] = __builtin_bit_cast(T, v);
+      const uint4 v = ok ? ld16(qp + (4 * kk + r) * 16) : make_uint4(0, 0, 0, 0);
+      qb[c][kk] = __builtin_bit_cast(T, v);
     }
   }
-  MfmaLaneOffsets<DT, D> o;
+  MfmaState<DT, D> st[NCB];
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const int t = 8 * (n >> 2) + 4 * b + (n & 3);
-    o.kt[b] = t >> 4;
+  for (int c = 0; c < NCB; ++c) {
+    st[c].m = -INFINITY;
+    st[c].l = 0.f;
 #pragma unroll
-    for (int kk = 0; kk < C::NKK; ++kk) o.k[b][kk] = ((4 * kk + r) * 16 + (t & 15)) * 16;
+    for (int j = 0; j < C::NJ; ++j) st[c].acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
-  o.vt = r >> 1;
-#pragma unroll
-  for (int j = 0; j < C::NJ; ++j) o.v[j] = ((16 * j + n) * 16 + 8 * (r & 1)) * C::E;
 
+  const MfmaLaneOffsets<DT, D> o = mfma_offsets<DT, D>();
   const int64_t blk_stride = (int64_t)a.num_kv_heads * C::TILE;
   const char* kc = reinterpret_cast<const char*>(a.k_cache) + (int64_t)g * C::TILE;
   const char* vc = reinterpret_cast<const char*>(a.v_cache) + (int64_t)g * C::TILE;
   const int32_t* bt_row = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
-  const int nkeys = last_pos + 1;            // keys any column of the block may see
-  const int nblk = (nkeys + kBlock - 1) / kBlock;
-  const int nu = (nkeys + kMfmaUnit - 1) / kMfmaUnit;
+  const int nblk = (nkeys_g + kBlock - 1) / kBlock;
+  const int nu = (nkeys_g + kMfmaUnit - 1) / kMfmaUnit;
 
-  MfmaState<DT, D> st;
-  st.m = -INFINITY;
-  st.l = 0.f;
+  // this thread's share of a unit: chunk k * kWG + threadIdx.x of the four tiles
+  // [K block a, K block b, V block a, V block b]
+  int ld_tile[CT::LOADS], ld_off[CT::LOADS];
 #pragma unroll
-  for (int j = 0; j < C::NJ; ++j) st.acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < CT::LOADS; ++k) {
+    const int c = k * kWG + threadIdx.x;
+    ld_tile[k] = c / CT::CPT;
+    ld_off[k] = (c % CT::CPT) * 16;
+  }
+  int win0 = 0, win1 = 0, wbase = -1;  // block-table windows of 64 entries: [wbase, wbase + 128)
+  auto load_unit = [&](uint4* regs, int u) {
+    const int e = 2 * u;
+    if (wbase < 0 || e >= wbase + 128) {  // uniform; happens every 64 units
+      wbase = e;
+      win0 = (e + lane < nblk) ? bt_row[e + lane] : 0;
+      win1 = (e + 64 + lane < nblk) ? bt_row[e + 64 + lane] : 0;
+    }
+    const int ia = e - wbase;
+    const int64_t ba = ia < 64 ? readlane(win0, ia) : readlane(win1, ia - 64);
+    // a second block past the keys is replaced by the first (its tokens are masked)
+    const int64_t bb = e + 1 < nblk ? (ia + 1 < 64 ? readlane(win0, ia + 1) : readlane(win1, ia + 1 - 64)) : ba;
+#pragma unroll
+    for (int k = 0; k < CT::LOADS; ++k) {
+      const int t = ld_tile[k];
+      const char* base = (t & 2 ? vc : kc) + (t & 1 ? bb : ba) * blk_stride;
+      regs[k] = ld16(base + ld_off[k]);
+    }
+  };
+  auto store_unit = [&](const uint4* regs, int buf) {
+#pragma unroll
+    for (int k = 0; k < CT::LOADS; ++k)
+      *reinterpret_cast<uint4*>(lds_units + buf * CT::UNIT + ld_tile[k] * CT::TILE + ld_off[k]) = regs[k];
+  };
 
-  constexpr int WU = kWave / 2;
-  for (int wb = 0; wb < nu; wb += WU) {
-    const int we = min(nu, wb + WU);
-    const int e0 = 2 * wb;
-    const int btv = (e0 + lane < min(nblk, 2 * we)) ? bt_row[e0 + lane] : 0;
-    uint4 kb[C::DEPTH][2][C::NKK], vb[C::DEPTH][C::NJ];
-    auto issue = [&](int slot, int u) {
-      const int ia = 2 * (u - wb);
-      const int64_t ba = readlane(btv, ia);
-      const int64_t bb = (2 * u + 1 < nblk) ? (int64_t)readlane(btv, ia + 1) : ba;
-      mfma_load<DT, D>(kb[slot], vb[slot], kc + ba * blk_stride, kc + bb * blk_stride,
-                       vc + ba * blk_stride, vc + bb * blk_stride, o);
-    };
+  uint4 regs[CT::LOADS];
+  load_unit(regs, 0);
+  store_unit(regs, 0);
+  __syncthreads();
+  for (int u = 0; u < nu; ++u) {
+    const bool more = u + 1 < nu;
+    if (more) load_unit(regs, u + 1);
+    const int t0 = u * kMfmaUnit;
+    if (t0 < nkeys_w) {  // uniform: this wave's columns see keys of this unit
+      const char* ub = lds_units + (u & 1) * CT::UNIT;
+      MfmaK<DT, D> kb;
+      MfmaV<DT, D> vb;
 #pragma unroll
-    for (int b = 0; b < C::DEPTH - 1; ++b)
-      if (wb + b < we) issue(b, wb + b);
-    for (int u = wb; u < we; u += C::DEPTH) {
+      for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int b = 0; b < C::DEPTH; ++b) {
-        const int ut = u + b;
-        if (ut < we) {
-          const int un = ut + C::DEPTH - 1;
-          if (un < we) issue((b + C::DEPTH - 1) % C::DEPTH, un);
-          const int t0 = ut * kMfmaUnit;
-          if (t0 + kMfmaUnit - 1 <= first_pos && jend - j0 == RB)
-            mfma_unit<DT, D, false, true>(st, kb[b], vb[b], qb, a.scale_log2, kMfmaUnit - 1,
-                                          kMfmaUnit);
-          else
-            mfma_unit<DT, D, true, true>(st, kb[b], vb[b], qb, a.scale_log2, pos_c - t0,
-                                         nkeys - t0);
-        }
+        for (int kk = 0; kk < C::NKK; ++kk)
+          kb[b][kk] = *reinterpret_cast<const uint4*>(ub + o.kt[b] * CT::TILE + o.k[b][kk]);
+#pragma unroll
+      for (int j = 0; j < C::NJ; ++j)
+        vb[j] = *reinterpret_cast<const uint4*>(ub + (2 + o.vt) * CT::TILE + o.v[j]);
+#pragma unroll
+      for (int c = 0; c < NCB; ++c) {
+        if (!live[c]) continue;
+        if (t0 + kMfmaUnit - 1 <= first[c] && full[c])
+          mfma_unit<DT, D, false, true>(st[c], kb, vb, qb[c], a.scale_log2, kMfmaUnit - 1,
+                                        kMfmaUnit);
+        else
+          mfma_unit<DT, D, true, true>(st[c], kb, vb, qb[c], a.scale_log2, pos[c] - t0,
+                                       nkeys_g - t0);
       }
     }
+    if (more) store_unit(regs, (u + 1) & 1);
+    __syncthreads();
   }
 
-  // emit: output column c = 4r + i of the P.V tile is (row j0 + c / G, head c % G)
-  const float ltot = cross_rows_sum(st.l);
-  const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+  // emit: lane (r, n) holds dimensions 16 j + 4 r + i of column 16 c + n, which is
+  // (row j0 + col / G, head col % G)
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = 4 * r + i;
-    const float inv_c = shfl(inv, c);
-    const int jr = j0 + c / G, hr = c % G;
+  for (int c = 0; c < NCB; ++c) {
+    const float ltot = cross_rows_sum(st[c].l);
+    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+    const int col = 16 * c + n;
+    const int jr = j0 + col / G, hr = col % G;
     if (jr < jend) {
       const int64_t ob = ((int64_t)(q0 + jr) * a.num_q_heads + (int64_t)g * G + hr) * D;
 #pragma unroll
-      for (int j = 0; j < C::NJ; ++j) store_out<DT>(a.out, ob + 16 * j + n, st.acc[j][i] * inv_c, a.out_f32);
+      for (int j = 0; j < C::NJ; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          store_out<DT>(a.out, ob + 16 * j + 4 * r + i, st[c].acc[j][i] * inv, a.out_f32);
     }
   }
 }
 
+// Work items, one per workgroup: (KV head, sequence, column block) with the KV head slowest,
+// column blocks last-to-first (the longest causal ranges first).  With XCD-local numbering
+// each XCD works through a contiguous range of items, i.e. mostly one KV head across all
+// sequences, and the items of one (sequence, KV head) that re-read its K/V run together
+// on one XCD.
 template <int DT, int D>
-__global__ __launch_bounds__(kWG) void chunk_kernel(DecodeArgs a) {
-  extern __shared__ int32_t lds[];
-  int32_t* base = lds;
-  int32_t* tmp = lds + a.num_seqs + 1;
+__global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(2))) void chunk_kernel(DecodeArgs a) {
+  extern __shared__ __align__(16) char lds_raw[];
+  char* lds_units = lds_raw;  // two unit buffers
+  int32_t* base = reinterpret_cast<int32_t*>(lds_raw + 2 * ChunkTile<D>::UNIT);
+  int32_t* tmp = base + a.num_seqs + 1;
   const int G = a.num_q_heads / a.num_kv_heads;
   const int S = a.num_seqs;
-  ChunkPlanIn pin{a.qsl, S, kWave / 4 / G};
+  ChunkPlanIn pin{a.qsl, S, kItemCols / G};
   build_chunk_plan(base, tmp, pin);
-  const int segs = a.num_kv_heads;
-  const int64_t total = (int64_t)base[S] * segs;
-  const int64_t W = (int64_t)gridDim.x * kWavesPerWG;
-  const int64_t w = (int64_t)blockIdx.x * kWavesPerWG + threadIdx.x / kWave;
-  for (int64_t i = w; i < total; i += W) {
-    const int s = find_seq(base, S, i, segs);
+  const int64_t per_head = base[S];
+  const int64_t total = per_head * a.num_kv_heads;
+  for (int64_t i = xcd_local_block(blockIdx.x, gridDim.x); i < total; i += gridDim.x) {
+    const int g = (int)(i / per_head);
+    const int64_t k = i - (int64_t)g * per_head;
+    const int s = find_seq(base, S, k, 1);
     const int nb = base[s + 1] - base[s];
-    const int64_t sbase = (int64_t)base[s] * segs;
-    const int g = (int)((i - sbase) / nb);
-    const int cb = (int)(i - sbase - (int64_t)g * nb);
-    chunk_item<DT, D>(a, s, g, cb);
+    const int cb = nb - 1 - (int)(k - base[s]);
+    chunk_item<DT, D>(a, s, g, cb, lds_units);
+    __syncthreads();  // the unit buffers are reused by the next item
   }
 }
 
-hipError_t launch_chunk(int dt, const DecodeArgs& a, int grid, hipStream_t st) {
-  const size_t lds = (size_t)(a.num_seqs + 1 + kWG) * sizeof(int32_t);
+hipError_t launch_chunk(int dt, const DecodeArgs& a, int num_q_rows, hipStream_t st) {
+  // one workgroup per work item: at most ceil(rows / rows_per_item) + num_seqs items per KV
+  // head; a multiple of the XCD count keeps the XCD-local numbering on
+  const int rpi = kItemCols / (a.num_q_heads / a.num_kv_heads);
+  const int64_t items = ((int64_t)(num_q_rows + rpi - 1) / rpi + a.num_seqs) * a.num_kv_heads;
+  const int64_t wgs = (items + kXcds - 1) / kXcds * kXcds;
+  const int grid = (int)(wgs < (1 << 20) ? wgs : (1 << 20) / kXcds * kXcds);
+  const size_t lds = (size_t)2 * (a.head_dim == 64 ? ChunkTile<64>::UNIT : ChunkTile<128>::UNIT) +
+                     (size_t)(a.num_seqs + 1 + kWG) * sizeof(int32_t);
   if (grid <= 0) return hipSuccess;
   if (dt == DT_F16) {
     if (a.head_dim == 64)

@@ -24,8 +24,14 @@ __device__ void mfma_attend(const DecodeArgs& a, int s, int g, int u0, int u1, i
   using T = op8_t<DT>;
   const int lane = lane_id();
   const int r = lane >> 4, n = lane & 15;
+  // every per-piece value is wave-uniform: keep it in scalar registers
+  s = __builtin_amdgcn_readfirstlane(s);
+  g = __builtin_amdgcn_readfirstlane(g);
+  u0 = __builtin_amdgcn_readfirstlane(u0);
+  u1 = __builtin_amdgcn_readfirstlane(u1);
+  ctx = __builtin_amdgcn_readfirstlane(ctx);
   const int G = a.num_q_heads / a.num_kv_heads;
-  const int row = a.qsl ? a.qsl[s] : s;
+  const int row = __builtin_amdgcn_readfirstlane(a.qsl ? a.qsl[s] : s);
 
   T qb[C::NKK];
   {
@@ -37,64 +43,18 @@ __device__ void mfma_attend(const DecodeArgs& a, int s, int g, int u0, int u1, i
       qb[kk] = __builtin_bit_cast(T, v);
     }
   }
-  MfmaLaneOffsets<DT, D> o;
-#pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const int t = 8 * (n >> 2) + 4 * b + (n & 3);  // unit token of S-block row n
-    o.kt[b] = t >> 4;
-#pragma unroll
-    for (int kk = 0; kk < C::NKK; ++kk) o.k[b][kk] = ((4 * kk + r) * 16 + (t & 15)) * 16;
-  }
-  o.vt = r >> 1;
-#pragma unroll
-  for (int j = 0; j < C::NJ; ++j) o.v[j] = ((16 * j + n) * 16 + 8 * (r & 1)) * C::E;
-
-  const int64_t blk_stride = (int64_t)a.num_kv_heads * C::TILE;
-  const char* kc = reinterpret_cast<const char*>(a.k_cache) + (int64_t)g * C::TILE;
-  const char* vc = reinterpret_cast<const char*>(a.v_cache) + (int64_t)g * C::TILE;
-  const int32_t* bt_row = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
-  const int nblk = (ctx + kBlock - 1) / kBlock;
-
   st.m = -INFINITY;
   st.l = 0.f;
 #pragma unroll
   for (int j = 0; j < C::NJ; ++j) st.acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  constexpr int WU = kWave / 2;  // units whose table entries fit one VGPR window
-  for (int wb = u0; wb < u1; wb += WU) {
-    const int we = min(u1, wb + WU);
-    const int e0 = 2 * wb;
-    const int btv = (e0 + lane < min(nblk, 2 * we)) ? bt_row[e0 + lane] : 0;
-    uint4 kb[C::DEPTH][2][C::NKK], vb[C::DEPTH][C::NJ];
-    auto issue = [&](int slot, int u) {
-      const int ia = 2 * (u - wb);
-      const int64_t ba = readlane(btv, ia);
-      // a unit whose second block lies past the context reads its first block again
-      // (all of its tokens are masked)
-      const int64_t bb = (2 * u + 1 < nblk) ? (int64_t)readlane(btv, ia + 1) : ba;
-      mfma_load<DT, D>(kb[slot], vb[slot], kc + ba * blk_stride, kc + bb * blk_stride,
-                       vc + ba * blk_stride, vc + bb * blk_stride, o);
-    };
-#pragma unroll
-    for (int b = 0; b < C::DEPTH - 1; ++b)
-      if (wb + b < we) issue(b, wb + b);
-    for (int u = wb; u < we; u += C::DEPTH) {
-#pragma unroll
-      for (int b = 0; b < C::DEPTH; ++b) {
-        const int ut = u + b;
-        if (ut < we) {
-          const int un = ut + C::DEPTH - 1;
-          if (un < we) issue((b + C::DEPTH - 1) % C::DEPTH, un);
-          const int valid = ctx - ut * kMfmaUnit;
-          if (valid >= kMfmaUnit)
-            mfma_unit<DT, D, false, false>(st, kb[b], vb[b], qb, a.scale_log2, kMfmaUnit - 1,
-                                           kMfmaUnit);
-          else
-            mfma_unit<DT, D, true, false>(st, kb[b], vb[b], qb, a.scale_log2, valid - 1, valid);
-        }
-      }
-    }
-  }
+  mfma_stream<DT, D>(a, s, g, u0, u1, ctx, [&](MfmaK<DT, D>& kb, MfmaV<DT, D>& vb, int u) {
+    const int valid = ctx - u * kMfmaUnit;
+    if (valid >= kMfmaUnit)
+      mfma_unit<DT, D, false, false>(st, kb, vb, qb, a.scale_log2, kMfmaUnit - 1, kMfmaUnit);
+    else
+      mfma_unit<DT, D, true, false>(st, kb, vb, qb, a.scale_log2, valid - 1, valid);
+  });
 }
 
 template <int DT, int D, int MODE>

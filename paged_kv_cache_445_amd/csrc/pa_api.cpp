@@ -10,7 +10,7 @@
 #include "pa_internal.h"
 
 namespace pa {
-hipError_t launch_chunk(int dt, const DecodeArgs& a, int grid, hipStream_t st);
+hipError_t launch_chunk(int dt, const DecodeArgs& a, int num_q_rows, hipStream_t st);
 }
 
 namespace {
@@ -235,7 +235,7 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   if (e != hipSuccess) return PA_ERR_HIP;
 
   if (query_start_loc) {
-    e = pa::launch_chunk(g->kv_dtype, a, cu_count() * 4, st);
+    e = pa::launch_chunk(g->kv_dtype, a, num_q_rows, st);
     if (e != hipSuccess) return PA_ERR_HIP;
   }
   return PA_OK;

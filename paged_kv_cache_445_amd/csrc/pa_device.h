@@ -143,6 +143,19 @@ __device__ __forceinline__ float readlane(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
 
+// ---------------------------------------------------------------- XCD-aware numbering
+//
+// The dispatcher hands consecutive workgroups to the 8 XCDs in turn (workgroup b runs on
+// XCD b % 8), and each XCD has its own L2.  Renumbering b -> (b % 8) * ceil(n / 8) + b / 8
+// makes consecutive logical workgroups share an XCD, so work that re-reads the same K/V
+// (neighbouring logical workgroups) finds it in one L2.  The map is a bijection of
+// [0, n) whenever n % 8 == 0 and is the identity otherwise; it only affects locality.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_local_block(int b, int n) {
+  if (n % kXcds) return b;
+  return (b % kXcds) * (n / kXcds) + b / kXcds;
+}
+
 // ---------------------------------------------------------------- work plan
 //
 // The split kernels walk a flattened list of work units: for every decode sequence s

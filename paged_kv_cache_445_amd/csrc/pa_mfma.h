@@ -1,17 +1,20 @@
 // pa_mfma.h — matrix-core building blocks of the decode and chunk kernels (gfx950).
 //
 // One 32-token unit (two 16-token blocks of one KV head) against 16 query columns:
-//   S^T = K . Q^T  as 2 x (D/32) MFMA 16x16x32  (M = 16 tokens, N = 16 query columns)
-//   O  += P . V    as (D/16) MFMA 16x16x32     (M = 16 query columns, N = 16 dims, K = 32 tokens)
-// with a streamed (online) softmax per query column in between.
+//   S^T = K . Q^T    as 2 x (D/32) MFMA 16x16x32  (M = 16 tokens, N = 16 query columns)
+//   O^T += V^T . P^T as (D/16) MFMA 16x16x32     (M = 16 dims, N = 16 query columns, K = 32 tokens)
+// with a streamed (online) softmax per query column in between.  Both products keep the
+// query column in N, so every lane's scores, running max / sum and output accumulators
+// belong to its own column l%16: the softmax rescale needs no cross-lane traffic.
 //
 // Operand layouts (gfx950 v_mfma_f32_16x16x32_{bf16,f16}): lane l supplies A[l%16][8(l/16)..+8]
 // and B[8(l/16)..+8][l%16] and receives D[4(l/16)+i][l%16], i < 4.
 //   * The M row m of S-block b is unit token 8(m/4) + 4b + m%4, so lane l (r = l/16) ends up
-//     with the scores of tokens 8r..8r+7 for column l%16 — exactly the P operand slots it
-//     supplies to the P.V product (A[column][8r..8r+7]).  No score moves between lanes.
-//   * V tiles are [D][16 tokens] in the pool, so the B operand of the P.V product (tokens
-//     8r..8r+7 of one dimension) is one 16-byte load.
+//     with the scores of tokens 8r..8r+7 for column l%16 — exactly the P^T operand slots it
+//     supplies to the V^T.P^T product (B[8r..8r+7][column]).  No score moves between lanes.
+//   * V tiles are [D][16 tokens] in the pool, so the A operand of the V^T.P^T product
+//     (tokens 8r..8r+7 of one dimension) is one 16-byte load.  The lane receives dimensions
+//     16j + 4r + i (i < 4) of its column.
 //   * K tiles are [D/8][16][8]: a token's 8-element chunk, the A operand of S^T, is one
 //     16-byte load.
 // P is fed to the matrix core as hi + lo 16-bit parts (two products), which keeps the
@@ -50,7 +53,7 @@ template <int DT, int D>
 struct MfmaState {
   float m;  // running max of head lane%16 (base-2 domain)
   float l;  // this lane's share of the running sum of head lane%16
-  f32x4_t acc[MfmaCfg<DT, D>::NJ];  // O[head 4(l/16)+i][dim 16 j + l%16]
+  f32x4_t acc[MfmaCfg<DT, D>::NJ];  // O[column l%16][dim 16 j + 4(l/16) + i]
 };
 
 template <int DT, int D>
@@ -152,16 +155,85 @@ __device__ __forceinline__ void mfma_unit(MfmaState<DT, D>& st, const MfmaK<DT, 
   }
   st.l = st.l * alpha + psum;
   st.m = mnew;
-  // rescale the output rows (heads 4r + i) by their own alpha
-  float a4[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) a4[i] = shfl(alpha, 4 * r + i);
+  // rescale this column's outputs by its own alpha, then add V^T . P^T
 #pragma unroll
   for (int j = 0; j < C::NJ; ++j) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) st.acc[j][i] *= a4[i];
-    st.acc[j] = mfma<DT>(phi, __builtin_bit_cast(T, vb[j]), st.acc[j]);
-    st.acc[j] = mfma<DT>(plo, __builtin_bit_cast(T, vb[j]), st.acc[j]);
+    for (int i = 0; i < 4; ++i) st.acc[j][i] *= alpha;
+    st.acc[j] = mfma<DT>(__builtin_bit_cast(T, vb[j]), phi, st.acc[j]);
+    st.acc[j] = mfma<DT>(__builtin_bit_cast(T, vb[j]), plo, st.acc[j]);
+  }
+}
+
+// Lane offsets of the unit operands (see the layout notes at the top of this file).
+template <int DT, int D>
+__device__ __forceinline__ MfmaLaneOffsets<DT, D> mfma_offsets() {
+  using C = MfmaCfg<DT, D>;
+  const int lane = lane_id();
+  const int r = lane >> 4, n = lane & 15;
+  MfmaLaneOffsets<DT, D> o;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int t = 8 * (n >> 2) + 4 * b + (n & 3);  // unit token of S-block row n
+    o.kt[b] = t >> 4;
+#pragma unroll
+    for (int kk = 0; kk < C::NKK; ++kk) o.k[b][kk] = ((4 * kk + r) * 16 + (t & 15)) * 16;
+  }
+  o.vt = r >> 1;
+#pragma unroll
+  for (int j = 0; j < C::NJ; ++j) o.v[j] = ((16 * j + n) * 16 + 8 * (r & 1)) * C::E;
+  return o;
+}
+
+// Stream the 32-token units [u0, u1) of KV head g of sequence s (context ctx) through
+// unit(kb, vb, u).  Units are walked in chunks of 64: both 64-entry block-table windows of
+// a chunk are loaded before its loop, and the loop is a two-stage software pipeline (the
+// loads of unit u + 1 are in flight while unit u is computed) in which every path into a
+// unit has the same loads outstanding, so its wait covers only that unit.  All arguments
+// must be wave-uniform.
+template <int DT, int D, class F>
+__device__ __forceinline__ void mfma_stream(const DecodeArgs& a, int s, int g, int u0, int u1,
+                                            int ctx, F&& unit) {
+  using C = MfmaCfg<DT, D>;
+  const int lane = lane_id();
+  const MfmaLaneOffsets<DT, D> o = mfma_offsets<DT, D>();
+  const int64_t blk_stride = (int64_t)a.num_kv_heads * C::TILE;
+  const char* kc = reinterpret_cast<const char*>(a.k_cache) + (int64_t)g * C::TILE;
+  const char* vc = reinterpret_cast<const char*>(a.v_cache) + (int64_t)g * C::TILE;
+  const int32_t* bt_row = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+  const int nblk = (ctx + kBlock - 1) / kBlock;
+  for (int c0 = u0; c0 < u1; c0 += 64) {
+    const int c1 = min(u1, c0 + 64);
+    const int b0 = 2 * c0, bend = min(nblk, 2 * c1);
+    const int win0 = (b0 + lane < bend) ? bt_row[b0 + lane] : 0;
+    const int win1 = (b0 + 64 + lane < bend) ? bt_row[b0 + 64 + lane] : 0;
+    auto blk = [&](int e) -> int64_t { return e < 64 ? readlane(win0, e) : readlane(win1, e - 64); };
+    auto issue = [&](MfmaK<DT, D>& kb, MfmaV<DT, D>& vb, int u) {
+      const int e = 2 * (u - c0);
+      const int64_t ba = blk(e);
+      // a unit whose second block lies past the context reads its first block again (all of
+      // its tokens are masked)
+      const int64_t bb = (2 * u + 1 < nblk) ? blk(e + 1) : ba;
+      mfma_load<DT, D>(kb, vb, kc + ba * blk_stride, kc + bb * blk_stride, vc + ba * blk_stride,
+                       vc + bb * blk_stride, o);
+    };
+    MfmaK<DT, D> ka, kb;
+    MfmaV<DT, D> va, vb;
+    issue(ka, va, c0);
+    int u = c0;
+    for (; u + 2 < c1; u += 2) {
+      issue(kb, vb, u + 1);
+      unit(ka, va, u);
+      issue(ka, va, u + 2);
+      unit(kb, vb, u + 1);
+    }
+    if (u + 1 < c1) {
+      issue(kb, vb, u + 1);
+      unit(ka, va, u);
+      unit(kb, vb, u + 1);
+    } else {
+      unit(ka, va, u);
+    }
   }
 }
 
@@ -176,22 +248,19 @@ __device__ __forceinline__ void mfma_emit(const MfmaState<DT, D>& st, int G, flo
   using C = MfmaCfg<DT, D>;
   const int lane = lane_id();
   const int r = lane >> 4, n = lane & 15;
-  const float ltot = cross_rows_sum(st.l);  // sum of head n over the four lane rows
+  const float ltot = cross_rows_sum(st.l);  // sum of column n over the four lane rows
   const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-  float inv4[4];
+  if (n < G) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) inv4[i] = shfl(inv, 4 * r + i);
+    for (int j = 0; j < C::NJ; ++j) {
+      const int d = 16 * j + 4 * r;  // this lane's four consecutive dimensions
+      const f32x4_t v = st.acc[j] * inv;
+      if (po) {
+        *reinterpret_cast<f32x4_t*>(po + n * po_col_stride + d) = v;
+      } else {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int hh = 4 * r + i;
-    if (hh < G) {
-#pragma unroll
-      for (int j = 0; j < C::NJ; ++j) {
-        const float v = st.acc[j][i] * inv4[i];
-        if (po)
-          po[hh * po_col_stride + 16 * j + n] = v;
-        else
-          store_out<DT>(out, out_base + (int64_t)hh * out_col_stride + 16 * j + n, v, out_f32);
+        for (int i = 0; i < 4; ++i)
+          store_out<DT>(out, out_base + (int64_t)n * out_col_stride + d + i, v[i], out_f32);
       }
     }
   }
