@@ -28,6 +28,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "f32": 157.3}  # dense; fp32 on the VALU
 # rocprof-derived HBM traffic of the decode kernels, with the hash of the sources it was
 # measured on; reported only while those sources are unchanged
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_{workload}.txt")
@@ -69,9 +70,27 @@ def read_traffic(workload):
     return float(m_b.group(1))
 
 
-def cpu_baseline(b, min_seconds, threads):
-    """fp64 oracle over the whole batch, repeated until min_seconds have passed.  The
-    oracle's pools are written by its own cache write from the batch's token records."""
+def row_keys(b):
+    """Visible keys of every query row (its position + 1)."""
+    import numpy as np
+    n = b.rows_per_seq()
+    keys = []
+    for s in range(b.num_seqs):
+        ctx = int(b.context_lens[s])
+        keys.extend(range(ctx - int(n[s]) + 1, ctx + 1))
+    return np.asarray(keys, dtype=np.int64)
+
+
+def attention_flops(b):
+    """QK^T and P.V multiply-adds of one pass: 4 * head_dim flops per (row, head, key)."""
+    return int(row_keys(b).sum()) * b.num_q_heads * 4 * b.head_dim
+
+
+def cpu_baseline(b, min_seconds, threads, max_key_heads=3e8):
+    """fp64 oracle over the batch, repeated until min_seconds have passed.  The oracle's
+    pools are written by its own cache write from the batch's token records.  Batches
+    larger than max_key_heads (row, head, key) triples run on an evenly spaced row sample."""
+    import numpy as np
     import oracle
     from paged_kv_cache_445_amd import workloads as W
     g = oracle.make_geom(b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim, b.num_blocks,
@@ -79,21 +98,32 @@ def cpu_baseline(b, min_seconds, threads):
     kp = W.nan_pool(b.k_pool_shape(), b.dtype)
     vp = W.nan_pool(b.v_pool_shape(), b.dtype)
     oracle.reshape_and_cache(b.key, b.value, kp, vp, b.slot, g)
+    keys = row_keys(b)
+    total = float(keys.sum()) * b.num_q_heads
+    rows = None
+    frac = 1.0
+    if total > max_key_heads:
+        step = int(np.ceil(total / max_key_heads))
+        rows = np.arange(0, b.num_q_rows, step, dtype=np.int32)
+        frac = float(keys[rows].sum()) / float(keys.sum())
     reps, t0 = 0, time.perf_counter()
     while True:
         oracle.paged_attention(b.q, kp, vp, b.block_tables, b.context_lens, b.query_start_loc,
-                               b.scale, g, threads=threads)
+                               b.scale, g, rows=rows, threads=threads)
         reps += 1
         el = time.perf_counter() - t0
         if el >= min_seconds:
             break
-    per = el / reps
+    per = el / reps / frac  # seconds for the whole batch at the sampled rate
+    what = (f"the whole {b.name} batch ({b.num_q_rows} rows" if rows is None else
+            f"every {int(rows[1] - rows[0]) if len(rows) > 1 else 1}th row of {b.name} "
+            f"({len(rows)} of {b.num_q_rows} rows, {100 * frac:.1f}% of the key-heads")
     return {"value": round(b.kv_bytes() / per / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"the whole {b.name} batch ({b.num_q_rows} rows x {b.num_q_heads} heads, "
-                      f"{b.kv_bytes() / 1e6:.1f} MB of KV), {reps} passes in {el:.1f} s "
-                      f"({per * 1e3:.1f} ms per pass, {b.num_seqs * b.num_q_heads / per:.0f} "
-                      f"seq-heads/s)"}
+            "sample": f"{what} x {b.num_q_heads} heads, {b.kv_bytes() / 1e6:.1f} MB of KV in "
+                      f"the batch), {reps} passes in {el:.1f} s; scaled to the whole batch: "
+                      f"{per * 1e3:.1f} ms per pass, {b.num_q_rows * b.num_q_heads / per:.0f} "
+                      f"row-heads/s"}
 
 
 def main():
@@ -180,8 +210,20 @@ def main():
     dec_avg_ms = float(np.mean(dec_ms))
     seq_heads = b.num_q_rows * b.num_q_heads
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
-    achieved = kv_bytes / (dec_avg_ms * 1e-3) / 1e9
-    traffic = read_traffic(args.workload)
+    flops = attention_flops(b)
+    # HBM must deliver each distinct cached token once (a shared prefix is read from HBM
+    # once and then from cache)
+    hbm_bytes = b.kv_unique_bytes()
+    # the bound of pa_decode: HBM for the KV bytes, or the matrix cores for its flops
+    t_hbm = hbm_bytes / (HBM_PEAK_GBS * 1e9)
+    t_mfma = flops / (MFMA_PEAK_TFLOPS[b.dtype] * 1e12)
+    if t_mfma > t_hbm:
+        bound, achieved, peak, punit = "mfma", flops / (dec_avg_ms * 1e-3) / 1e12, \
+            MFMA_PEAK_TFLOPS[b.dtype], "TFLOP/s"
+    else:
+        bound, achieved, peak, punit = "hbm", hbm_bytes / (dec_avg_ms * 1e-3) / 1e9, \
+            HBM_PEAK_GBS, "GB/s"
+    traffic = read_traffic(args.workload) if bound == "hbm" else None
 
     if args.copy_calibration > 0:
         n = args.copy_calibration << 20
@@ -221,18 +263,21 @@ def main():
             "kv_dtype": b.dtype, "accumulate": "f32",
             "context_tokens": int(b.context_lens.astype(np.int64).sum()),
             "kv_bytes_per_step": kv_bytes,
+            "kv_unique_bytes_per_step": hbm_bytes,
+            "attention_flops_per_step": flops,
             "pool_copies_rotated": copies,
         },
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "seq_heads_per_s": round(seq_heads / (ms_per_step * 1e-3), 1),
         "pa_decode_us": round(dec_avg_ms * 1e3, 3),
         "roofline": {
-            "bound": "hbm",
-            "kernel": "pa_decode (decode kernel + partial merge)",
+            "bound": bound,
+            "kernel": "pa_decode (decode kernel + partial merge"
+                      + (" + chunk kernel)" if b.query_start_loc is not None else ")"),
             "achieved": round(achieved, 2),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "peak": peak,
+            "unit": punit,
+            "frac": round(achieved / peak, 4),
             "traffic": traffic,
         },
         "cpu_baseline": cpu,

@@ -132,6 +132,12 @@ class Batch:
         return int(self.context_lens.astype(np.int64).sum()) * self.num_kv_heads * \
             self.head_dim * 2 * ELEM_BYTES[self.dtype]
 
+    def kv_unique_bytes(self) -> int:
+        """KV bytes of the distinct cached tokens a pass reads: a token shared by several
+        sequences (a common prefix block) counts once."""
+        distinct = np.unique(np.concatenate(self.seq_tokens)) if self.num_seqs else []
+        return int(len(distinct)) * self.num_kv_heads * self.head_dim * 2 * ELEM_BYTES[self.dtype]
+
     def step_slots(self) -> np.ndarray:
         return self.slot[self.new]
 
