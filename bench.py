@@ -10,9 +10,11 @@ pools are rotated between steps so that no step finds the previous step's blocks
 
 Prints ONE JSON line.  `value` is the effective KV-read bandwidth of the whole step:
 algorithmic KV bytes (every context token's K and V read once per KV head) divided by
-the step time.  `roofline` rates pa_decode alone (its kernels timed with HIP events on the
-stream they run on) against the 8 TB/s HBM peak.  `cpu_baseline` times the fp64 CPU
-oracle on the same batch on the host cores.
+the wall time per step of the timed region.  `roofline` rates pa_decode alone: right after
+the timed steps the same pa_decode calls run back to back between one pair of HIP events
+on the stream they run on, and their average duration is compared with the 8 TB/s HBM
+peak (or the matrix-core peak when the flops dominate).  `cpu_baseline` times the fp64
+CPU oracle on the same batch on the host cores.
 """
 import argparse
 import hashlib
@@ -179,32 +181,46 @@ def main():
 
     stream = torch.cuda.current_stream()
 
-    def step(i, ev=None):
+    def write(i):
         kc, vc = pools[i % copies]
         pa.reshape_and_cache(db.key_new, db.value_new, kc, vc, db.slot_new, db.geom)
-        if ev is not None:
-            ev[0].record(stream)
+
+    def decode(i):
+        kc, vc = pools[i % copies]
         pa.decode(db.out, db.q, kc, vc, db.block_tables, db.context_lens, db.qsl, db.scale,
                   db.workspace, db.geom)
-        if ev is not None:
-            ev[1].record(stream)
 
     print(f"[bench] warmup {args.warmup} steps, {copies} pool copies", file=sys.stderr,
           flush=True)
     for i in range(args.warmup):
-        step(i)
+        write(i)
+        decode(i)
     torch.cuda.synchronize()
 
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    # timed region: K whole steps (cache write + decode), nothing else on the stream
+    ev_steps = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev_steps[0].record(stream)
     for i in range(args.steps):
-        step(args.warmup + i, evs[i])
+        write(args.warmup + i)
+        decode(args.warmup + i)
+    ev_steps[1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    dec_ms = [a.elapsed_time(c) for a, c in evs]
-    print(f"[bench] timed {args.steps} steps in {wall:.4f} s", file=sys.stderr, flush=True)
+    print(f"[bench] timed {args.steps} steps in {wall:.4f} s "
+          f"(events: {ev_steps[0].elapsed_time(ev_steps[1]):.3f} ms)", file=sys.stderr, flush=True)
+
+    # pa_decode's own duration: the same calls back to back between one pair of HIP events
+    # on the stream it runs on (an event between two kernels stalls the next dispatch, so
+    # per-call events would add their own gap to every call)
+    ev_dec = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    ev_dec[0].record(stream)
+    for i in range(args.steps):
+        decode(args.warmup + i)
+    ev_dec[1].record(stream)
+    torch.cuda.synchronize()
+    dec_ms = [ev_dec[0].elapsed_time(ev_dec[1]) / args.steps]
 
     ms_per_step = wall * 1e3 / args.steps
     dec_avg_ms = float(np.mean(dec_ms))

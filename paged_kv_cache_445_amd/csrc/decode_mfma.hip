@@ -71,57 +71,54 @@ __global__ __launch_bounds__(kWG) void mfma_decode_kernel(DecodeArgs a) {
   const int64_t w = (int64_t)blockIdx.x * kWavesPerWG + wave;
 
   if constexpr (MODE == MODE_EVEN) {
-    PlanIn pin{a.context_lens, a.qsl, S, kMfmaUnit};
+    PlanIn pin{a.context_lens, a.qsl, S, kMfmaUnit, a.seg_extra};
     build_plan(base, tmp, pin);
     zero_empty_rows<DT>(pin, a.out, a.num_q_heads, D, w, W, a.out_f32);
-    // units: (sequence, group of kWavesPerWG heads, unit); workgroups split them evenly and
-    // wave i of a workgroup runs head i of each group
+    // units: (sequence, group of kWavesPerWG KV heads, unit); wave i runs KV head i of each
+    // group
     const int groups = (a.num_kv_heads + kWavesPerWG - 1) / kWavesPerWG;
-    const int64_t total = (int64_t)base[S] * groups;
-    const int64_t NK = min((int64_t)gridDim.x, total);  // workgroups with a share
-    const int64_t k = blockIdx.x;
+    const Part part = make_part((int64_t)base[S] * groups, gridDim.x);
     MergeDesc* desc = static_cast<MergeDesc*>(a.desc);
-    if (k >= NK) {
-      write_desc(desc, w, 0, -1, false);
-      return;
-    }
-    const int64_t lo = range_lo(total, k, NK), hi = range_lo(total, k + 1, NK);
-    bool split_here = false;  // a split segment starts in this share (its last piece)
-    for (int64_t i = lo; i < hi;) {
-      const int s = find_seq(base, S, i, groups);
-      const int nu = base[s + 1] - base[s];
-      const int64_t sbase = (int64_t)base[s] * groups;
-      const int grp = (int)((i - sbase) / nu);
-      const int64_t seg0 = sbase + (int64_t)grp * nu;
-      const int64_t pe = min(hi, seg0 + nu);
-      const int g = grp * kWavesPerWG + wave;  // this wave's KV head
-      if (g < a.num_kv_heads) {
-        const int u0 = (int)(i - seg0), u1 = (int)(pe - seg0);
-        const int ctx = a.context_lens[s];
-        MfmaState<DT, D> st;
-        mfma_attend<DT, D>(a, s, g, u0, u1, ctx, st);
-        const int row = a.qsl ? a.qsl[s] : s;
-        const int64_t ob = ((int64_t)row * a.num_q_heads + (int64_t)g * G) * D;
-        if (u0 == 0 && u1 == nu) {
-          mfma_emit<DT, D>(st, G, nullptr, nullptr, nullptr, D, a.out, ob, D, a.out_f32);
-        } else {
-          const int64_t slot = w * 2 + (i == lo ? 0 : 1);
-          mfma_emit<DT, D>(st, G, a.part_o + slot * G * D, a.part_m + slot * G,
-                           a.part_l + slot * G, D, nullptr, 0, 0, false);
-          if (seg0 >= lo && seg0 + nu > hi) {
-            const SplitSeg sg = split_seg(total, NK, seg0, seg0 + nu - 1, wave);
-            write_desc(desc, w, ob, (int)sg.k1, sg.k0_later);
-            split_here = true;
+    even_split_drive(part, desc, [&](int64_t o, int64_t lo, int64_t hi) {
+      const int64_t ow = kWavesPerWG * o + wave;  // this wave's descriptor and slot pair
+      bool split_here = false;  // a split segment starts in this share (its last piece)
+      for (int64_t i = lo; i < hi;) {
+        const int s = find_seq(base, S, i, groups);
+        const int seglen = base[s + 1] - base[s];
+        const int nu = seglen - a.seg_extra;  // real units; the rest only balance the split
+        const int64_t sbase = (int64_t)base[s] * groups;
+        const int grp = (int)((i - sbase) / seglen);
+        const int64_t seg0 = sbase + (int64_t)grp * seglen;
+        const int64_t pe = min(hi, seg0 + seglen);
+        const int g = grp * kWavesPerWG + wave;  // this wave's KV head
+        const int u0 = (int)(i - seg0), u1 = (int)min(pe - seg0, (int64_t)nu);
+        if (g < a.num_kv_heads && u0 < nu) {
+          const int ctx = a.context_lens[s];
+          MfmaState<DT, D> st;
+          mfma_attend<DT, D>(a, s, g, u0, u1, ctx, st);
+          const int row = a.qsl ? a.qsl[s] : s;
+          const int64_t ob = ((int64_t)row * a.num_q_heads + (int64_t)g * G) * D;
+          if (u0 == 0 && u1 == nu) {
+            mfma_emit<DT, D>(st, G, nullptr, nullptr, nullptr, D, a.out, ob, D, a.out_f32);
+          } else {
+            const int64_t slot = ow * 2 + (i == lo ? 0 : 1);
+            mfma_emit<DT, D>(st, G, a.part_o + slot * G * D, a.part_m + slot * G,
+                             a.part_l + slot * G, D, nullptr, 0, 0, false);
+            if (seg0 >= lo && seg0 + nu > hi) {  // the real units continue in the next share
+              const SplitSeg sg = split_seg(part, seg0, seg0 + nu - 1, wave);
+              write_desc(desc, ow, ob, (int)sg.k1, sg.k0_later);
+              split_here = true;
+            }
           }
         }
+        i = pe;
       }
-      i = pe;
-    }
-    if (!split_here) write_desc(desc, w, 0, -1, false);
+      if (!split_here) write_desc(desc, ow, 0, -1, false);
+    });
   } else {
     const int PU = a.partition_units;  // 32-token units per partition
     const int P = a.max_partitions;
-    PlanIn pin{a.context_lens, nullptr, S, PU * kMfmaUnit};
+    PlanIn pin{a.context_lens, nullptr, S, PU * kMfmaUnit, 0};
     build_plan(base, tmp, pin);
     const int64_t nent = (int64_t)S * a.num_q_heads * P;
     for (int64_t e = (int64_t)blockIdx.x * kWG + threadIdx.x; e < nent; e += (int64_t)gridDim.x * kWG) {

@@ -256,63 +256,59 @@ __global__ __launch_bounds__(kWG) void valu_decode_kernel(DecodeArgs a) {
   const int64_t w = (int64_t)blockIdx.x * kWavesPerWG + wave;
 
   if constexpr (MODE == MODE_EVEN) {
-    PlanIn pin{a.context_lens, a.qsl, S, kValuUnit};
+    PlanIn pin{a.context_lens, a.qsl, S, kValuUnit, a.seg_extra};
     build_plan(base, tmp, pin);
     zero_empty_rows<DT>(pin, a.out, a.num_q_heads, D, w, W, a.out_f32);
-    // units: (sequence, group of kWavesPerWG heads, unit); workgroups split them evenly and
-    // wave i of a workgroup runs head i of each group
+    // units: (sequence, group of kWavesPerWG heads, tile); wave i runs head i of each group
     const int groups = (a.num_q_heads + kWavesPerWG - 1) / kWavesPerWG;
-    const int64_t total = (int64_t)base[S] * groups;
-    const int64_t NK = min((int64_t)gridDim.x, total);  // workgroups with a share
-    const int64_t k = blockIdx.x;
+    const Part part = make_part((int64_t)base[S] * groups, gridDim.x);
     MergeDesc* desc = static_cast<MergeDesc*>(a.desc);
-    if (k >= NK) {
-      write_desc(desc, w, 0, -1, false);
-      return;
-    }
-    const int64_t lo = range_lo(total, k, NK), hi = range_lo(total, k + 1, NK);
-    bool split_here = false;  // a split segment starts in this share (its last piece)
-    for (int64_t i = lo; i < hi;) {
-      const int s = find_seq(base, S, i, groups);
-      const int nt = base[s + 1] - base[s];
-      const int64_t sbase = (int64_t)base[s] * groups;
-      const int grp = (int)((i - sbase) / nt);
-      const int64_t seg0 = sbase + (int64_t)grp * nt;
-      const int64_t pe = min(hi, seg0 + nt);
-      const int h = grp * kWavesPerWG + wave;  // this wave's head
-      if (h < a.num_q_heads) {
-        const int t0 = (int)(i - seg0), t1 = (int)(pe - seg0);
-        const int ctx = a.context_lens[s];
-        VState<DT, D> st;
-        valu_attend<DT, D>(a, s, h, t0, t1, ctx, st, pw);
-        const float l = v_finish<DT, D>(st);
-        const float inv = 1.f / l;
-        const int row = a.qsl ? a.qsl[s] : s;
-        const int64_t ob = ((int64_t)row * a.num_q_heads + h) * D;
-        if (t0 == 0 && t1 == nt) {
-          v_store<DT, D>(st, inv, a.out, ob, a.out_f32);
-        } else {
-          const int64_t slot = w * 2 + (i == lo ? 0 : 1);
-          v_store_f32<DT, D>(st, inv, a.part_o + slot * D);
-          if (lane == 0) {
-            a.part_m[slot] = st.m * 0.69314718055994531f;  // natural-log domain
-            a.part_l[slot] = l;
-          }
-          if (seg0 >= lo && seg0 + nt > hi) {
-            const SplitSeg sg = split_seg(total, NK, seg0, seg0 + nt - 1, wave);
-            write_desc(desc, w, ob, (int)sg.k1, sg.k0_later);
-            split_here = true;
+    even_split_drive(part, desc, [&](int64_t o, int64_t lo, int64_t hi) {
+      const int64_t ow = kWavesPerWG * o + wave;  // this wave's descriptor and slot pair
+      bool split_here = false;  // a split segment starts in this share (its last piece)
+      for (int64_t i = lo; i < hi;) {
+        const int s = find_seq(base, S, i, groups);
+        const int seglen = base[s + 1] - base[s];
+        const int nt = seglen - a.seg_extra;  // real tiles; the rest only balance the split
+        const int64_t sbase = (int64_t)base[s] * groups;
+        const int grp = (int)((i - sbase) / seglen);
+        const int64_t seg0 = sbase + (int64_t)grp * seglen;
+        const int64_t pe = min(hi, seg0 + seglen);
+        const int h = grp * kWavesPerWG + wave;  // this wave's head
+        const int t0 = (int)(i - seg0), t1 = (int)min(pe - seg0, (int64_t)nt);
+        if (h < a.num_q_heads && t0 < nt) {
+          const int ctx = a.context_lens[s];
+          VState<DT, D> st;
+          valu_attend<DT, D>(a, s, h, t0, t1, ctx, st, pw);
+          const float l = v_finish<DT, D>(st);
+          const float inv = 1.f / l;
+          const int row = a.qsl ? a.qsl[s] : s;
+          const int64_t ob = ((int64_t)row * a.num_q_heads + h) * D;
+          if (t0 == 0 && t1 == nt) {
+            v_store<DT, D>(st, inv, a.out, ob, a.out_f32);
+          } else {
+            const int64_t slot = ow * 2 + (i == lo ? 0 : 1);
+            v_store_f32<DT, D>(st, inv, a.part_o + slot * D);
+            if (lane == 0) {
+              a.part_m[slot] = st.m * 0.69314718055994531f;  // natural-log domain
+              a.part_l[slot] = l;
+            }
+            if (seg0 >= lo && seg0 + nt > hi) {  // the real tiles continue in the next share
+              const SplitSeg sg = split_seg(part, seg0, seg0 + nt - 1, wave);
+              write_desc(desc, ow, ob, (int)sg.k1, sg.k0_later);
+              split_here = true;
+            }
           }
         }
+        i = pe;
       }
-      i = pe;
-    }
-    if (!split_here) write_desc(desc, w, 0, -1, false);
+      if (!split_here) write_desc(desc, ow, 0, -1, false);
+    });
   } else {
     // fixed partitions; rows are sequences (no query_start_loc in this mode)
     const int PU = a.partition_units;  // tiles per partition
     const int P = a.max_partitions;
-    PlanIn pin{a.context_lens, nullptr, S, PU * kBlock};
+    PlanIn pin{a.context_lens, nullptr, S, PU * kBlock, 0};
     build_plan(base, tmp, pin);
     // partitions past the context: max_logits = -inf, exp_sums = 0
     const int64_t nent = (int64_t)S * a.num_q_heads * P;

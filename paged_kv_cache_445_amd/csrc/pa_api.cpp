@@ -54,6 +54,17 @@ int cu_count() {
   return n;
 }
 
+// balancing units per segment of pa_decode's even split (vector path, matrix-core path): the
+// cost of starting a piece, in units of work; optional override for tuning
+constexpr int kSegExtra[2] = {2, 1};
+int seg_extra_override() {
+  static int v = [] {
+    const char* s = getenv("PA_DECODE_SEG_EXTRA");
+    return s ? atoi(s) : -1;
+  }();
+  return v;
+}
+
 // optional choice of resident workgroups per CU for the split kernels (tuning; capped at the
 // kernel's occupancy)
 int wg_per_cu_override() {
@@ -193,6 +204,7 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
   const SplitShape sh = split_shape(g);
   const size_t slots = (size_t)grid * pa::kWavesPerWG * 2 * sh.heads_per_seg;
+  void* desc = workspace;
   float* part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + desc_bytes(grid));
   float* part_m = part_o + slots * g->head_dim;
   float* part_l = part_m + slots;
@@ -208,7 +220,7 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   a.part_o = part_o;
   a.part_m = part_m;
   a.part_l = part_l;
-  a.desc = workspace;
+  a.desc = desc;
   a.num_seqs = g->num_seqs;
   a.num_q_heads = g->num_q_heads;
   a.num_kv_heads = g->num_kv_heads;
@@ -216,6 +228,7 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   a.max_blocks_per_seq = g->max_blocks_per_seq;
   a.out_f32 = g->out_dtype == PA_F32 && g->kv_dtype != PA_F32;
   a.scale_log2 = scale_to_log2(scale);
+  a.seg_extra = seg_extra_override() >= 0 ? seg_extra_override() : kSegExtra[use_mfma(g) ? 1 : 0];
 
   hipError_t e = use_mfma(g) ? pa::launch_mfma_decode(g->kv_dtype, pa::MODE_EVEN, a, grid, st)
                              : pa::launch_valu_decode(g->kv_dtype, pa::MODE_EVEN, a, grid, st);
@@ -226,7 +239,7 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   m.part_o = part_o;
   m.part_m = part_m;
   m.part_l = part_l;
-  m.desc = workspace;
+  m.desc = desc;
   m.num_waves = grid * pa::kWavesPerWG;
   m.rows = sh.heads_per_seg;
   m.head_dim = g->head_dim;

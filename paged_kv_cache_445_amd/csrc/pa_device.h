@@ -169,13 +169,18 @@ struct PlanIn {
   const int32_t* qsl;  // NULL: one row per sequence
   int32_t num_seqs;
   int32_t unit_tokens;
+  int32_t extra;       // balancing units appended to every non-empty segment (no work)
 };
 
+// units of sequence s in the flattened list: its real units ceil(ctx / unit_tokens), plus
+// `extra` trailing units that stand for the cost of starting a piece (a share that takes a
+// segment boundary gets that many fewer real units; a share that starts inside them has
+// nothing to do for that segment)
 __device__ __forceinline__ int32_t seq_units(const PlanIn& p, int s) {
   const int32_t rows = p.qsl ? p.qsl[s + 1] - p.qsl[s] : 1;
   if (rows != 1) return 0;  // multi-row sequences are not split-context work
   const int32_t ctx = p.context_lens[s];
-  return ctx > 0 ? (ctx + p.unit_tokens - 1) / p.unit_tokens : 0;
+  return ctx > 0 ? (ctx + p.unit_tokens - 1) / p.unit_tokens + p.extra : 0;
 }
 
 // Decode rows (sequences with one query row) whose context is empty get a zero output;
@@ -236,35 +241,49 @@ __device__ __forceinline__ int find_seq(const int32_t* base, int S, int64_t i, i
   return lo;
 }
 
-// Even split of [0, total) over W waves (W <= total, so every share is non-empty): wave w
-// owns [range_lo(w), range_lo(w + 1)); unit i belongs to wave owner(i).
-__device__ __forceinline__ int64_t range_lo(int64_t total, int64_t w, int64_t W) {
-  return (total * w) / W;
-}
-__device__ __forceinline__ int64_t owner(int64_t total, int64_t i, int64_t W) {
-  return ((i + 1) * W - 1) / total;
-}
-
-// Split-segment bookkeeping of the even split.  The split is over workgroups: workgroup k
-// owns units [range_lo(k), range_lo(k + 1)) of the flattened (sequence, head group, unit)
-// list, and wave i of the workgroup runs head i of every group.  A segment (one sequence and
-// head group) occupying units [seg0, seg1] that crosses a workgroup boundary has one piece in
-// each workgroup k0..k1 (k0 = owner(seg0), k1 = owner(seg1)); wave i's piece of workgroup k
-// sits in partial slot 2 (4k + i) + 0 when it is the first piece of k's share and + 1
-// otherwise (only k0's piece can be a later piece).  Wave i of k0 records the segment in its
-// descriptor; the merge kernel that follows combines the pieces of that wave's head.
-struct SplitSeg {
-  int64_t k0, k1;
-  bool k0_later;  // k0's piece is not the first piece of k0's share
-  int wave;       // wave index inside the workgroups (the head within the group)
+// The flattened (sequence, head group, unit) list [0, total) is split evenly over the NK
+// workgroups that get work (NK = min(workgroups, total), so every share is non-empty):
+// workgroup ("owner") o owns [part_lo(o), part_lo(o + 1)), and wave i of it takes head i of
+// every group of that range.
+struct Part {
+  int64_t total;  // units
+  int64_t NK;     // owners
 };
 
-__device__ __forceinline__ SplitSeg split_seg(int64_t total, int64_t NK, int64_t seg0,
-                                              int64_t seg1, int wave) {
+__device__ __forceinline__ Part make_part(int64_t total, int64_t workgroups) {
+  Part p;
+  p.total = total;
+  p.NK = min(workgroups, total);
+  return p;
+}
+
+// first unit of owner o (o in [0, NK]; part_lo(NK) == total)
+__device__ __forceinline__ int64_t part_lo(const Part& p, int64_t o) {
+  return p.NK ? (p.total * o) / p.NK : 0;
+}
+// owner of unit u (u < total)
+__device__ __forceinline__ int64_t part_owner(const Part& p, int64_t u) {
+  return ((u + 1) * p.NK - 1) / p.total;
+}
+
+// Split-segment bookkeeping.  A segment (one sequence and head group) whose real units
+// [seg0, seg1] cross an owner boundary has one piece in each owner o0..o1 (o0 = owner of
+// seg0, o1 = owner of seg1); wave i's piece of owner o sits in partial slot
+// 2 (4o + i) + 0 when it is the first piece of o's range and + 1 otherwise (only o0's piece
+// can be a later piece).  Wave i of o0's workgroup records the segment in the descriptor of
+// (o0, i); the merge kernel that follows combines the pieces of that wave's head.
+struct SplitSeg {
+  int64_t k0, k1;  // first and last owner
+  bool k0_later;   // k0's piece is not the first piece of k0's range
+  int wave;        // wave index inside the workgroups (the head within the group)
+};
+
+__device__ __forceinline__ SplitSeg split_seg(const Part& p, int64_t seg0, int64_t seg1,
+                                              int wave) {
   SplitSeg r;
-  r.k0 = owner(total, seg0, NK);
-  r.k1 = owner(total, seg1, NK);
-  r.k0_later = range_lo(total, r.k0, NK) < seg0;
+  r.k0 = part_owner(p, seg0);
+  r.k1 = part_owner(p, seg1);
+  r.k0_later = part_lo(p, r.k0) < seg0;
   r.wave = wave;
   return r;
 }
@@ -283,6 +302,18 @@ __device__ __forceinline__ void write_desc(MergeDesc* desc, int64_t w, int64_t o
     d.k0_later = k0_later ? 1 : 0;
     desc[w] = d;
   }
+}
+
+// Runs the workgroup's share: range(o, lo, hi) processes owner o's units (every wave its
+// own head) and writes each wave's descriptor of owner o; a workgroup without a share writes
+// its descriptors invalid, so a launch leaves no descriptor of an earlier one behind.
+template <class F>
+__device__ __forceinline__ void even_split_drive(const Part& p, MergeDesc* desc, F&& range) {
+  const int64_t k = blockIdx.x;
+  if (k < p.NK)
+    range(k, part_lo(p, k), part_lo(p, k + 1));
+  else
+    write_desc(desc, kWavesPerWG * k + threadIdx.x / kWave, 0, -1, false);
 }
 
 __device__ __forceinline__ float wave_max(float v) {

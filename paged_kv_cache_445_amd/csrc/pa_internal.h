@@ -46,6 +46,7 @@ struct DecodeArgs {
   float scale_log2;         // scale * log2(e): scores are kept in the base-2 domain
   int32_t partition_units;  // MODE_PARTITION: units per partition
   int32_t max_partitions;   // MODE_PARTITION
+  int32_t seg_extra;        // MODE_EVEN: balancing units per segment (see PlanIn)
 };
 
 struct ReshapeArgs {
