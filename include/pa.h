@@ -105,12 +105,15 @@ size_t pa_workspace_size(const pa_geom* geom, int32_t num_q_rows);
  *   query_start_loc  int32 [num_seqs + 1] or NULL (see "Rows and positions")
  *   scale         multiplies q . k (normally 1 / sqrt(head_dim))
  *   workspace     device scratch of at least pa_workspace_size(geom, num_q_rows) bytes for
- *                 split-context partials and their merge records; its contents need no
- *                 initialisation and it may be reused across calls and geometries.  Calls
- *                 that may run concurrently must not share a workspace.
- * Long contexts are split across wavefronts: one kernel computes the pieces (and every
- * unsplit (sequence, head) directly), a second merges the split ones by log-sum-exp; a
- * third runs the multi-row sequences when query_start_loc is given.
+ *                 split-context partials and their arrival counters.  Zero-fill it once
+ *                 before its first use (e.g. hipMemset after allocating it): every call
+ *                 leaves the counters at zero again, so the workspace can then be reused
+ *                 across calls and geometries on the same device without clearing it.
+ *                 Calls that may run concurrently must not share a workspace.
+ * The (sequence, head) work is split evenly over the workgroups of one kernel; a long
+ * context crossing a split boundary is computed in pieces, and the piece that finishes last
+ * merges them by log-sum-exp inside the same kernel.  A second kernel runs the multi-row
+ * sequences when query_start_loc is given.
  * Sequences with several rows (query_start_loc) need a 16-bit kv_dtype and a query group
  * Hq / Hkv that divides 16; otherwise PA_ERR_UNSUPPORTED.
  */

@@ -57,6 +57,70 @@ __device__ void mfma_attend(const DecodeArgs& a, int s, int g, int u0, int u1, i
   });
 }
 
+// A piece of a split segment (all G heads of one KV head): publish it, or, as the
+// segment's last arrival, merge every piece and write the output.  Each lane merges its own
+// head column n and dimensions 16 j + 4 r .. + 3, so no lanes interact.
+template <int DT, int D>
+__device__ void m_split_finish(const DecodeArgs& a, const MfmaState<DT, D>& st, int G,
+                               const SplitSeg& sg, int64_t self, int32_t* cnt, int seen,
+                               int64_t ob) {
+  using C = MfmaCfg<DT, D>;
+  constexpr int NE = 4 * C::NJ;
+  const int lane = lane_id();
+  const int r = lane >> 4, n = lane & 15;
+  const bool col = n < G;
+  const CohBuf bo = coh_buf(a.part_o), bm = coh_buf(a.part_m), bl = coh_buf(a.part_l);
+  // this piece's partial as published: normalised output, max (natural log), sum
+  const float ltot = cross_rows_sum(st.l);  // sum of column n over the four lane rows
+  const float inv = 1.f / ltot;
+  const float mine_m = st.m * 0.69314718055994531f;
+  f32x4_t mine_o[C::NJ];
+#pragma unroll
+  for (int j = 0; j < C::NJ; ++j) mine_o[j] = st.acc[j] * inv;
+  const bool last = split_arrive(cnt, (int)(sg.k1 - sg.k0), seen, [&] {
+    const int64_t slot = piece_slot(sg, self);
+    if (col) {
+#pragma unroll
+      for (int j = 0; j < C::NJ; ++j) coh_store4(bo, (slot * G + n) * D + 16 * j + 4 * r, mine_o[j]);
+      if (r == 0) {
+        coh_store(bm, slot * G + n, mine_m);
+        coh_store(bl, slot * G + n, ltot);
+      }
+    }
+  });
+  if (!last) return;
+  float L, U[NE];
+  merge_ordered<NE, 2>(L, U, sg.k0, sg.k1, [&](int64_t k, float& m, float& lk, float (&ov)[NE]) {
+    if (k == self || !col) {
+      m = mine_m;
+      lk = ltot;
+#pragma unroll
+      for (int j = 0; j < C::NJ; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ov[4 * j + i] = mine_o[j][i];
+      return;
+    }
+    const int64_t slot = piece_slot(sg, k);
+    m = coh_load(bm, slot * G + n);
+    lk = coh_load(bl, slot * G + n);
+#pragma unroll
+    for (int j = 0; j < C::NJ; ++j) {
+      const f32x4_t v = coh_load4(bo, (slot * G + n) * D + 16 * j + 4 * r);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ov[4 * j + i] = v[i];
+    }
+  });
+  if (col) {
+    const float rinv = 1.f / L;
+#pragma unroll
+    for (int j = 0; j < C::NJ; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        store_out<DT>(a.out, ob + (int64_t)n * D + 16 * j + 4 * r + i, U[4 * j + i] * rinv, a.out_f32);
+  }
+  counter_reset(cnt);
+}
+
 template <int DT, int D, int MODE>
 __global__ __launch_bounds__(kWG) void mfma_decode_kernel(DecodeArgs a) {
   extern __shared__ int32_t lds[];
@@ -78,10 +142,7 @@ __global__ __launch_bounds__(kWG) void mfma_decode_kernel(DecodeArgs a) {
     // group
     const int groups = (a.num_kv_heads + kWavesPerWG - 1) / kWavesPerWG;
     const Part part = make_part((int64_t)base[S] * groups, gridDim.x);
-    MergeDesc* desc = static_cast<MergeDesc*>(a.desc);
-    even_split_drive(part, desc, [&](int64_t o, int64_t lo, int64_t hi) {
-      const int64_t ow = kWavesPerWG * o + wave;  // this wave's descriptor and slot pair
-      bool split_here = false;  // a split segment starts in this share (its last piece)
+    even_split_drive(part, [&](int64_t o, int64_t lo, int64_t hi) {
       for (int64_t i = lo; i < hi;) {
         const int s = find_seq(base, S, i, groups);
         const int seglen = base[s + 1] - base[s];
@@ -94,26 +155,26 @@ __global__ __launch_bounds__(kWG) void mfma_decode_kernel(DecodeArgs a) {
         const int u0 = (int)(i - seg0), u1 = (int)min(pe - seg0, (int64_t)nu);
         if (g < a.num_kv_heads && u0 < nu) {
           const int ctx = a.context_lens[s];
-          MfmaState<DT, D> st;
-          mfma_attend<DT, D>(a, s, g, u0, u1, ctx, st);
           const int row = a.qsl ? a.qsl[s] : s;
           const int64_t ob = ((int64_t)row * a.num_q_heads + (int64_t)g * G) * D;
-          if (u0 == 0 && u1 == nu) {
-            mfma_emit<DT, D>(st, G, nullptr, nullptr, nullptr, D, a.out, ob, D, a.out_f32);
-          } else {
-            const int64_t slot = ow * 2 + (i == lo ? 0 : 1);
-            mfma_emit<DT, D>(st, G, a.part_o + slot * G * D, a.part_m + slot * G,
-                             a.part_l + slot * G, D, nullptr, 0, 0, false);
-            if (seg0 >= lo && seg0 + nu > hi) {  // the real units continue in the next share
-              const SplitSeg sg = split_seg(part, seg0, seg0 + nu - 1, wave);
-              write_desc(desc, ow, ob, (int)sg.k1, sg.k0_later);
-              split_here = true;
-            }
+          const bool whole = u0 == 0 && u1 == nu;
+          SplitSeg sg{};
+          int32_t* cnt = nullptr;
+          int seen = 0;
+          if (!whole) {
+            sg = split_seg(part, seg0, seg0 + nu - 1, wave);
+            cnt = a.counters + kWavesPerWG * sg.k0 + wave;
+            seen = counter_peek(cnt);  // consumed after the units
           }
+          MfmaState<DT, D> st;
+          mfma_attend<DT, D>(a, s, g, u0, u1, ctx, st);
+          if (whole)
+            mfma_emit<DT, D>(st, G, nullptr, nullptr, nullptr, D, a.out, ob, D, a.out_f32);
+          else
+            m_split_finish<DT, D>(a, st, G, sg, o, cnt, seen, ob);
         }
         i = pe;
       }
-      if (!split_here) write_desc(desc, ow, 0, -1, false);
     });
   } else {
     const int PU = a.partition_units;  // 32-token units per partition

@@ -240,6 +240,57 @@ __device__ __forceinline__ void v_store_f32(const VState<DT, D>& st, float inv, 
   }
 }
 
+// A piece of a split segment: publish it, or (if it is the segment's last arrival) merge
+// every piece and write the output.  Lanes of a dimension row hold the same full sum after
+// v_finish, so each lane reads and merges its own dimensions.
+template <int DT, int D>
+__device__ void v_split_finish(const DecodeArgs& a, VState<DT, D>& st, float l,
+                               const SplitSeg& sg, int64_t self, int32_t* cnt, int seen,
+                               int64_t ob) {
+  using C = VCfg<DT, D>;
+  const int lane = lane_id();
+  const CohBuf bo = coh_buf(a.part_o), bm = coh_buf(a.part_m), bl = coh_buf(a.part_l);
+  const int dim0 = lane / C::LPD;  // dimension j * DPL + dim0 of load j
+  // this piece's partial as published: normalised output, max (natural log), sum
+  const float inv = 1.f / l;
+  const float mine_m = st.m * 0.69314718055994531f;
+  float mine_o[C::NV];
+#pragma unroll
+  for (int j = 0; j < C::NV; ++j) mine_o[j] = st.acc[j] * inv;
+  const bool last = split_arrive(cnt, (int)(sg.k1 - sg.k0), seen, [&] {
+    const int64_t slot = piece_slot(sg, self);
+    if (lane % C::LPD == 0) {
+#pragma unroll
+      for (int j = 0; j < C::NV; ++j) coh_store(bo, slot * D + j * C::DPL + dim0, mine_o[j]);
+    }
+    if (lane == 0) {
+      coh_store(bm, slot, mine_m);
+      coh_store(bl, slot, l);
+    }
+  });
+  if (!last) return;
+  float L, U[C::NV];
+  merge_ordered<C::NV, 4>(L, U, sg.k0, sg.k1,
+                          [&](int64_t k, float& m, float& lk, float (&ov)[C::NV]) {
+    if (k == self) {
+      m = mine_m;
+      lk = l;
+#pragma unroll
+      for (int j = 0; j < C::NV; ++j) ov[j] = mine_o[j];
+      return;
+    }
+    const int64_t slot = piece_slot(sg, k);
+    m = coh_load(bm, slot);
+    lk = coh_load(bl, slot);
+#pragma unroll
+    for (int j = 0; j < C::NV; ++j) ov[j] = coh_load(bo, slot * D + j * C::DPL + dim0);
+  });
+#pragma unroll
+  for (int j = 0; j < C::NV; ++j) st.acc[j] = U[j];
+  v_store<DT, D>(st, 1.f / L, a.out, ob, a.out_f32);
+  counter_reset(cnt);
+}
+
 template <int DT, int D, int MODE>
 __global__ __launch_bounds__(kWG) void valu_decode_kernel(DecodeArgs a) {
   // LDS: one 16-float weight slot per wave (first, for 16-byte alignment), then the plan
@@ -262,10 +313,7 @@ __global__ __launch_bounds__(kWG) void valu_decode_kernel(DecodeArgs a) {
     // units: (sequence, group of kWavesPerWG heads, tile); wave i runs head i of each group
     const int groups = (a.num_q_heads + kWavesPerWG - 1) / kWavesPerWG;
     const Part part = make_part((int64_t)base[S] * groups, gridDim.x);
-    MergeDesc* desc = static_cast<MergeDesc*>(a.desc);
-    even_split_drive(part, desc, [&](int64_t o, int64_t lo, int64_t hi) {
-      const int64_t ow = kWavesPerWG * o + wave;  // this wave's descriptor and slot pair
-      bool split_here = false;  // a split segment starts in this share (its last piece)
+    even_split_drive(part, [&](int64_t o, int64_t lo, int64_t hi) {
       for (int64_t i = lo; i < hi;) {
         const int s = find_seq(base, S, i, groups);
         const int seglen = base[s + 1] - base[s];
@@ -278,31 +326,28 @@ __global__ __launch_bounds__(kWG) void valu_decode_kernel(DecodeArgs a) {
         const int t0 = (int)(i - seg0), t1 = (int)min(pe - seg0, (int64_t)nt);
         if (h < a.num_q_heads && t0 < nt) {
           const int ctx = a.context_lens[s];
+          const int row = a.qsl ? a.qsl[s] : s;
+          const int64_t ob = ((int64_t)row * a.num_q_heads + h) * D;
+          const bool whole = t0 == 0 && t1 == nt;
+          SplitSeg sg{};
+          int32_t* cnt = nullptr;
+          int seen = 0;
+          if (!whole) {
+            sg = split_seg(part, seg0, seg0 + nt - 1, wave);
+            cnt = a.counters + kWavesPerWG * sg.k0 + wave;
+            seen = counter_peek(cnt);  // consumed after the tiles
+          }
           VState<DT, D> st;
           valu_attend<DT, D>(a, s, h, t0, t1, ctx, st, pw);
           const float l = v_finish<DT, D>(st);
-          const float inv = 1.f / l;
-          const int row = a.qsl ? a.qsl[s] : s;
-          const int64_t ob = ((int64_t)row * a.num_q_heads + h) * D;
-          if (t0 == 0 && t1 == nt) {
-            v_store<DT, D>(st, inv, a.out, ob, a.out_f32);
+          if (whole) {
+            v_store<DT, D>(st, 1.f / l, a.out, ob, a.out_f32);
           } else {
-            const int64_t slot = ow * 2 + (i == lo ? 0 : 1);
-            v_store_f32<DT, D>(st, inv, a.part_o + slot * D);
-            if (lane == 0) {
-              a.part_m[slot] = st.m * 0.69314718055994531f;  // natural-log domain
-              a.part_l[slot] = l;
-            }
-            if (seg0 >= lo && seg0 + nt > hi) {  // the real tiles continue in the next share
-              const SplitSeg sg = split_seg(part, seg0, seg0 + nt - 1, wave);
-              write_desc(desc, ow, ob, (int)sg.k1, sg.k0_later);
-              split_here = true;
-            }
+            v_split_finish<DT, D>(a, st, l, sg, o, cnt, seen, ob);
           }
         }
         i = pe;
       }
-      if (!split_here) write_desc(desc, ow, 0, -1, false);
     });
   } else {
     // fixed partitions; rows are sequences (no query_start_loc in this mode)

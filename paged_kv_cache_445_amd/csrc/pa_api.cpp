@@ -111,8 +111,10 @@ int split_grid(const pa_geom* g, int mode) {
   // The even split streams best with few resident workgroups per CU: each of them reads
   // four adjacent heads of a block at a time, and more of them only add split pieces.
   const int o = wg_per_cu_override();
-  const int want = o > 0 ? o : (mode == pa::MODE_EVEN ? kEvenWgPerCu[path] : occ);
-  return cu_count() * (want < occ ? want : occ);
+  int want = o > 0 ? o : (mode == pa::MODE_EVEN ? kEvenWgPerCu[path] : occ);
+  if (want > occ) want = occ;
+  if (want > pa::kMaxWgPerCu) want = pa::kMaxWgPerCu;  // the workspace's counters cover this
+  return cu_count() * want;
 }
 
 struct SplitShape {
@@ -124,17 +126,19 @@ SplitShape split_shape(const pa_geom* g) {
   return {g->num_q_heads, 1, pa::kValuUnit};
 }
 
-// pa_decode's workspace: one merge descriptor per wave of the split grid, then two partial
-// slots per wave: o [W][2][G][D], m [W][2][G], l [W][2][G].
-size_t desc_bytes(int grid) {
-  const size_t n = (size_t)grid * pa::kWavesPerWG * sizeof(pa::MergeDesc);
+// pa_decode's workspace: one arrival counter per wave of the largest split grid the device
+// can have (so the counters sit at the same place for every geometry and stay zero between
+// calls), then two partial slots per wave of this geometry's grid: o [W][2][G][D],
+// m [W][2][G], l [W][2][G].
+size_t counter_bytes() {
+  const size_t n = (size_t)cu_count() * pa::kMaxWgPerCu * pa::kWavesPerWG * sizeof(int32_t);
   return (n + 255) / 256 * 256;
 }
 
 size_t even_workspace_bytes(const pa_geom* g, int grid) {
   const SplitShape sh = split_shape(g);
   const size_t slots = (size_t)grid * pa::kWavesPerWG * 2 * sh.heads_per_seg;
-  return desc_bytes(grid) + slots * ((size_t)g->head_dim + 2) * sizeof(float);
+  return counter_bytes() + slots * ((size_t)g->head_dim + 2) * sizeof(float);
 }
 
 pa_status hip_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
@@ -204,8 +208,8 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
   const SplitShape sh = split_shape(g);
   const size_t slots = (size_t)grid * pa::kWavesPerWG * 2 * sh.heads_per_seg;
-  void* desc = workspace;
-  float* part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + desc_bytes(grid));
+  int32_t* counters = static_cast<int32_t*>(workspace);
+  float* part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + counter_bytes());
   float* part_m = part_o + slots * g->head_dim;
   float* part_l = part_m + slots;
 
@@ -220,7 +224,7 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   a.part_o = part_o;
   a.part_m = part_m;
   a.part_l = part_l;
-  a.desc = desc;
+  a.counters = counters;
   a.num_seqs = g->num_seqs;
   a.num_q_heads = g->num_q_heads;
   a.num_kv_heads = g->num_kv_heads;
@@ -232,19 +236,6 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
 
   hipError_t e = use_mfma(g) ? pa::launch_mfma_decode(g->kv_dtype, pa::MODE_EVEN, a, grid, st)
                              : pa::launch_valu_decode(g->kv_dtype, pa::MODE_EVEN, a, grid, st);
-  if (e != hipSuccess) return PA_ERR_HIP;
-
-  pa::MergeArgs m{};
-  m.out = out;
-  m.part_o = part_o;
-  m.part_m = part_m;
-  m.part_l = part_l;
-  m.desc = desc;
-  m.num_waves = grid * pa::kWavesPerWG;
-  m.rows = sh.heads_per_seg;
-  m.head_dim = g->head_dim;
-  m.out_f32 = a.out_f32;
-  e = pa::launch_merge(g->kv_dtype, m, st);
   if (e != hipSuccess) return PA_ERR_HIP;
 
   if (query_start_loc) {

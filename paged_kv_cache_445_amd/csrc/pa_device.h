@@ -270,8 +270,8 @@ __device__ __forceinline__ int64_t part_owner(const Part& p, int64_t u) {
 // [seg0, seg1] cross an owner boundary has one piece in each owner o0..o1 (o0 = owner of
 // seg0, o1 = owner of seg1); wave i's piece of owner o sits in partial slot
 // 2 (4o + i) + 0 when it is the first piece of o's range and + 1 otherwise (only o0's piece
-// can be a later piece).  Wave i of o0's workgroup records the segment in the descriptor of
-// (o0, i); the merge kernel that follows combines the pieces of that wave's head.
+// can be a later piece).  Every owner has at most one segment that starts in its range and
+// continues past it, so counter 4 o0 + i of the workspace belongs to that segment alone.
 struct SplitSeg {
   int64_t k0, k1;  // first and last owner
   bool k0_later;   // k0's piece is not the first piece of k0's range
@@ -292,101 +292,138 @@ __device__ __forceinline__ int64_t piece_slot(const SplitSeg& sg, int64_t k) {
   return 2 * (kWavesPerWG * k + sg.wave) + ((k == sg.k0 && sg.k0_later) ? 1 : 0);
 }
 
-// Lane 0 of wave w writes its descriptor (called once per wave and launch).  k1 < 0: none.
-__device__ __forceinline__ void write_desc(MergeDesc* desc, int64_t w, int64_t out_base, int k1,
-                                           bool k0_later) {
-  if (__lane_id() == 0) {
-    MergeDesc d;
-    d.out_base = out_base;
-    d.k1 = k1;
-    d.k0_later = k0_later ? 1 : 0;
-    desc[w] = d;
-  }
-}
-
-// Runs the workgroup's share: range(o, lo, hi) processes owner o's units (every wave its
-// own head) and writes each wave's descriptor of owner o; a workgroup without a share writes
-// its descriptors invalid, so a launch leaves no descriptor of an earlier one behind.
+// Runs the workgroup's share: range(o, lo, hi) processes owner o's units, every wave its
+// own head.
 template <class F>
-__device__ __forceinline__ void even_split_drive(const Part& p, MergeDesc* desc, F&& range) {
+__device__ __forceinline__ void even_split_drive(const Part& p, F&& range) {
   const int64_t k = blockIdx.x;
-  if (k < p.NK)
-    range(k, part_lo(p, k), part_lo(p, k + 1));
-  else
-    write_desc(desc, kWavesPerWG * k + threadIdx.x / kWave, 0, -1, false);
+  if (k < p.NK) range(k, part_lo(p, k), part_lo(p, k + 1));
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+// ---- in-kernel merge of split segments ----
+// The pieces of a split segment are computed by different workgroups, often on different
+// XCDs, whose L2 caches are not kept coherent with each other.  A piece therefore publishes
+// its partial (softmax-normalised o, max m in the natural-log domain, sum l) with
+// device-scope stores (cache policy sc1: written through to the device's point of
+// coherence, and counted as done only once they are there), waits for them to complete, and
+// then arrives at the segment's counter with a device-scope atomic add.  The piece that
+// arrives last (or that finds every other piece already arrived) reads the others back with
+// device-scope loads, which never hit a stale L2 line, merges them with its own registers
+// and writes the output.  This is a release/acquire handshake restricted to the data it
+// orders, so no L2 of the device is written back or invalidated as a whole.  The merging
+// wave returns the counter to zero, which keeps a workspace ready for the next call.
+constexpr int kCohPolicy = 16;  // buffer-op cache policy: sc1 (device scope)
+
+struct CohBuf {
+  __amdgpu_buffer_rsrc_t r;
+};
+
+__device__ __forceinline__ CohBuf coh_buf(const float* base) {
+  // raw 32-bit buffer: stride 0, the largest record count, 32-bit data format
+  return {__builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, 0x7fffffff, 0x00020000)};
 }
-__device__ __forceinline__ float wave_sum(float v) {
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+__device__ __forceinline__ float coh_load(const CohBuf& b, int64_t elem) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(b.r, (int)(4 * elem), 0, kCohPolicy));
+}
+__device__ __forceinline__ f32x4_t coh_load4(const CohBuf& b, int64_t elem) {
+  return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(b.r, (int)(4 * elem), 0, kCohPolicy));
+}
+__device__ __forceinline__ void coh_store(const CohBuf& b, int64_t elem, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), b.r, (int)(4 * elem), 0, kCohPolicy);
+}
+__device__ __forceinline__ void coh_store4(const CohBuf& b, int64_t elem, f32x4_t v) {
+  typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), b.r, (int)(4 * elem), 0, kCohPolicy);
 }
 
-// Log-sum-exp merge of a split segment's pieces (one wave).  Each slot holds `rows` (<= MR)
-// rows (query heads) of a softmax-normalised output o [rows][D], its max m (natural-log
-// domain) and sum l; merged row r goes to out[out_base + r * D + d].  Lane p fetches the
-// (m, l) of piece p for every row at once, then every lane accumulates its output elements
-// (64 j + lane of the rows x D block) over the pieces, so a batch of up to 64 pieces costs
-// two dependent loads.
-template <int DT, int D, int MR>
-__device__ void merge_pieces(const float* part_o, const float* part_m, const float* part_l,
-                             int rows, const SplitSeg& sg, void* out, int64_t out_base,
-                             bool out_f32) {
-  constexpr int NE = MR * D / kWave;  // output elements per lane at rows == MR
-  const int lane = __lane_id();
-  const int np = (int)(sg.k1 - sg.k0 + 1);
-  const int ne = rows * D / kWave;
-  float M[MR], L[MR], acc[NE];
+// Device-scope read of a segment counter (every lane gets the value; not yet made uniform,
+// so the read can be issued well before it is used).
+__device__ __forceinline__ int counter_peek(int32_t* c) {
+  return __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wave-uniform: true in exactly one of the segment's pieces, the one that merges.  `others`
+// is the number of other pieces, `seen` an earlier counter_peek of c, and `publish` writes
+// this piece's partial with device-scope stores; it is skipped when every other piece has
+// already arrived (that piece merges from its registers and nobody reads its slot).
+template <class Pub>
+__device__ __forceinline__ bool split_arrive(int32_t* c, int others, int seen, Pub&& publish) {
+  seen = __builtin_amdgcn_readfirstlane(seen);
+  if (seen == others) return true;
+  seen = __builtin_amdgcn_readfirstlane(counter_peek(c));
+  if (seen == others) return true;
+  publish();
+  // every store of this wave, the partial included, has reached the point of coherence
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  int old = 0;
+  if (__lane_id() == 0) old = __hip_atomic_fetch_add(c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __builtin_amdgcn_readfirstlane(old) == others;
+}
+
+__device__ __forceinline__ void counter_reset(int32_t* c) {
+  if (__lane_id() == 0) __hip_atomic_store(c, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Log-sum-exp merge, per lane, of NE output elements of one row over the pieces k0..k1 in
+// that order: fetch(k, m, l, o) gives piece k's max (natural-log domain), sum and
+// normalised output, by device-scope loads or, for the merging piece itself, from the
+// registers it would have published.  The arithmetic depends only on the pieces' values and
+// the fixed order, so every call gives the same bits whichever piece merges.  Pieces are
+// fetched B at a time into two alternating batches, so the loads of the next batch are in
+// flight while the current one is combined.  Returns the merged output in U and its sum in L
+// (the output is U / L).
+template <int NE, int B>
+struct MergeBatch {
+  float m[B], l[B], o[B][NE];
+};
+
+template <int NE, int B, class Fetch>
+__device__ __forceinline__ void merge_ordered(float& L, float (&U)[NE], int64_t k0, int64_t k1,
+                                              Fetch&& fetch) {
+  const int n = (int)(k1 - k0 + 1);
+  float M = -INFINITY;
+  L = 0.f;
 #pragma unroll
-  for (int r = 0; r < MR; ++r) {
-    M[r] = -INFINITY;
-    L[r] = 0.f;
-  }
+  for (int e = 0; e < NE; ++e) U[e] = 0.f;
+  auto load = [&](MergeBatch<NE, B>& bt, int q0) {
 #pragma unroll
-  for (int j = 0; j < NE; ++j) acc[j] = 0.f;
-  for (int p0 = 0; p0 < np; p0 += kWave) {
-    const int pn = min(kWave, np - p0);
-    const bool act = lane < pn;
-    const int64_t my = act ? piece_slot(sg, sg.k0 + p0 + lane) * rows : 0;
-    float m[MR], l[MR], wt[MR], sc[MR];
-#pragma unroll
-    for (int r = 0; r < MR; ++r) {
-      m[r] = (act && r < rows) ? part_m[my + r] : -INFINITY;
-      l[r] = (act && r < rows) ? part_l[my + r] : 0.f;
-    }
-#pragma unroll
-    for (int r = 0; r < MR; ++r) {
-      if (r < rows) {
-        const float mn = fmaxf(M[r], wave_max(m[r]));
-        sc[r] = M[r] == -INFINITY ? 0.f : __expf(M[r] - mn);
-        wt[r] = act ? l[r] * __expf(m[r] - mn) : 0.f;
-        L[r] = L[r] * sc[r] + wave_sum(wt[r]);
-        M[r] = mn;
+    for (int b = 0; b < B; ++b) {
+      if (q0 + b < n) {
+        fetch(k0 + q0 + b, bt.m[b], bt.l[b], bt.o[b]);
       } else {
-        sc[r] = 0.f;
-        wt[r] = 0.f;
+        bt.m[b] = -INFINITY;
+        bt.l[b] = 0.f;
+#pragma unroll
+        for (int e = 0; e < NE; ++e) bt.o[b][e] = 0.f;
       }
     }
+  };
+  auto combine = [&](const MergeBatch<NE, B>& bt) {
+    float mn = M;
 #pragma unroll
-    for (int j = 0; j < NE; ++j) acc[j] *= sc[64 * j / D];
-    for (int p = 0; p < pn; ++p) {
-      const int64_t base = piece_slot(sg, sg.k0 + p0 + p) * rows * D + lane;
-      float o[NE];
+    for (int b = 0; b < B; ++b) mn = fmaxf(mn, bt.m[b]);
+    const float s = M == -INFINITY ? 0.f : __expf(M - mn);
+    L *= s;
 #pragma unroll
-      for (int j = 0; j < NE; ++j) o[j] = j < ne ? part_o[base + 64 * j] : 0.f;
+    for (int e = 0; e < NE; ++e) U[e] *= s;
 #pragma unroll
-      for (int j = 0; j < NE; ++j) {
-        const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt[64 * j / D]), p));
-        acc[j] = fmaf(w, o[j], acc[j]);
-      }
+    for (int b = 0; b < B; ++b) {
+      const float w = bt.m[b] == -INFINITY ? 0.f : bt.l[b] * __expf(bt.m[b] - mn);
+      L += w;
+#pragma unroll
+      for (int e = 0; e < NE; ++e) U[e] = fmaf(w, bt.o[b][e], U[e]);
     }
+    M = mn;
+  };
+  MergeBatch<NE, B> ba, bb;
+  load(ba, 0);
+  for (int q0 = 0; q0 < n; q0 += 2 * B) {
+    if (q0 + B < n) load(bb, q0 + B);
+    combine(ba);
+    if (q0 + B >= n) break;
+    if (q0 + 2 * B < n) load(ba, q0 + 2 * B);
+    combine(bb);
   }
-#pragma unroll
-  for (int j = 0; j < NE; ++j)
-    if (j < ne) store_out<DT>(out, out_base + 64 * j + lane, acc[j] / L[64 * j / D], out_f32);
 }
 
 }  // namespace pa

@@ -15,10 +15,9 @@ enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
 
 // How a split kernel distributes and emits its work.
 enum SplitMode : int {
-  // pa_decode: every wave owns an equal share of the flattened unit list; a segment that
-  // lies inside one wave is written to `out`, the pieces of a segment that crosses wave
-  // boundaries are written to the per-wave slots of the workspace and merged by a second
-  // kernel.
+  // pa_decode: every workgroup owns an equal share of the flattened unit list; a segment
+  // that lies inside one share is written to `out`; the pieces of a segment that crosses
+  // share boundaries are merged inside the kernel by the piece that finishes last.
   MODE_EVEN = 0,
   // pa_decode_partitioned: fixed partitions of `partition_units` units; every (seq,
   // segment, partition) is one item, written to tmp_out / max_logits / exp_sums.
@@ -36,7 +35,7 @@ struct DecodeArgs {
   float* part_o;            // MODE_EVEN: [W][2][G][D]; MODE_PARTITION: tmp_out [rows][Hq][P][D]
   float* part_m;            // MODE_EVEN: [W][2][G];    MODE_PARTITION: max_logits [rows][Hq][P]
   float* part_l;            // MODE_EVEN: [W][2][G];    MODE_PARTITION: exp_sums   [rows][Hq][P]
-  void* desc;               // MODE_EVEN: [W] MergeDesc, every entry written by every launch
+  int32_t* counters;        // MODE_EVEN: [W] arrival counters, zero before and after a call
   int32_t num_seqs;
   int32_t num_q_heads;
   int32_t num_kv_heads;
@@ -60,26 +59,6 @@ struct ReshapeArgs {
   int32_t head_dim;
 };
 
-// Per-wave record of pa_decode's split kernel, read by its merge kernel: the split segment that starts in the wave's
-// share (w1 < 0: none).
-struct MergeDesc {
-  int64_t out_base;  // element offset of the segment's first output row (this wave's head)
-  int32_t k1;        // last workgroup holding a piece; < 0: no split segment starts here
-  int32_t k0_later;
-};
-
-struct MergeArgs {
-  void* out;
-  const float* part_o;
-  const float* part_m;
-  const float* part_l;
-  const void* desc;
-  int32_t num_waves;  // waves of the split kernel
-  int32_t rows;       // query heads per wave's segment (1 or G)
-  int32_t head_dim;
-  int32_t out_f32;
-};
-
 struct PartReduceArgs {
   void* out;
   const float* tmp_out;
@@ -100,7 +79,9 @@ int valu_decode_max_blocks_per_cu(int dt, int head_dim, int mode, int lds_bytes)
 hipError_t launch_mfma_decode(int dt, int mode, const DecodeArgs& a, int grid, hipStream_t st);
 int mfma_decode_max_blocks_per_cu(int dt, int head_dim, int mode, int lds_bytes);
 hipError_t launch_part_reduce(int dt, const PartReduceArgs& a, hipStream_t st);
-hipError_t launch_merge(int dt, const MergeArgs& a, hipStream_t st);
+
+// resident workgroups per CU at most (32 waves of 64 lanes): bounds the even split's grid
+constexpr int kMaxWgPerCu = 8;
 
 // unit sizes (tokens) of the split kernels
 constexpr int kValuUnit = 16;

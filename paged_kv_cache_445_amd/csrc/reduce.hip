@@ -11,23 +11,6 @@
 
 namespace pa {
 
-// Second kernel of pa_decode: wave w (head w % 4 of workgroup w / 4 of the split kernel)
-// merges the split segment that starts in that workgroup's share for its head, if any.
-template <int DT, int D, int MR>
-__global__ __launch_bounds__(kWG) void merge_kernel(MergeArgs a) {
-  const int64_t w = (int64_t)blockIdx.x * kWavesPerWG + threadIdx.x / kWave;
-  if (w >= a.num_waves) return;
-  const MergeDesc d = static_cast<const MergeDesc*>(a.desc)[w];
-  if (d.k1 < 0) return;
-  SplitSeg sg;
-  sg.k0 = w / kWavesPerWG;
-  sg.k1 = d.k1;
-  sg.k0_later = d.k0_later != 0;
-  sg.wave = (int)(w % kWavesPerWG);
-  merge_pieces<DT, D, MR>(a.part_o, a.part_m, a.part_l, a.rows, sg, a.out, d.out_base,
-                          a.out_f32);
-}
-
 // pa_decode_reduce: one wavefront per (row, head), lanes over the head dimension.
 template <int DT>
 __global__ __launch_bounds__(kWG) void part_reduce_kernel(PartReduceArgs a) {
@@ -52,34 +35,6 @@ __global__ __launch_bounds__(kWG) void part_reduce_kernel(PartReduceArgs a) {
     }
     store_out<DT>(a.out, item * D + d, L > 0.f ? acc / L : 0.f, a.out_f32);
   }
-}
-
-template <int DT, int D>
-static void launch_merge_d(const MergeArgs& a, int grid, hipStream_t st) {
-  if (a.rows == 1)
-    hipLaunchKernelGGL((merge_kernel<DT, D, 1>), dim3(grid), dim3(kWG), 0, st, a);
-  else
-    hipLaunchKernelGGL((merge_kernel<DT, D, 16>), dim3(grid), dim3(kWG), 0, st, a);
-}
-
-template <int DT>
-static void launch_merge_t(const MergeArgs& a, int grid, hipStream_t st) {
-  if (a.head_dim == 64)
-    launch_merge_d<DT, 64>(a, grid, st);
-  else
-    launch_merge_d<DT, 128>(a, grid, st);
-}
-
-hipError_t launch_merge(int dt, const MergeArgs& a, hipStream_t st) {
-  const int grid = (a.num_waves + kWavesPerWG - 1) / kWavesPerWG;
-  if (grid <= 0) return hipSuccess;
-  if (dt == DT_F32)
-    launch_merge_t<DT_F32>(a, grid, st);
-  else if (dt == DT_F16)
-    launch_merge_t<DT_F16>(a, grid, st);
-  else
-    launch_merge_t<DT_BF16>(a, grid, st);
-  return hipGetLastError();
 }
 
 hipError_t launch_part_reduce(int dt, const PartReduceArgs& a, hipStream_t st) {

@@ -55,7 +55,8 @@ class DeviceBatch:
         self.out = torch.zeros((b.num_q_rows, b.num_q_heads, b.head_dim), dtype=out_dt,
                                device=dev)
         ws = pa.workspace_size(self.geom, b.num_q_rows)
-        self.workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=dev)
+        # zeroed once: pa_decode keeps its arrival counters at zero between calls
+        self.workspace = torch.zeros(max(ws, 16), dtype=torch.uint8, device=dev)
         self.scale = float(b.scale)
 
     # ------------------------------------------------------------------ the method

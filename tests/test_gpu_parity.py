@@ -173,9 +173,9 @@ def test_physical_permutation_and_repeat_are_bitwise(dev):
 
 
 def test_shared_workspace_reuse(dev):
-    """One workspace serves two geometries (vector and matrix-core paths) in alternation.
-    Before every call it is overwritten with garbage (merge records and partial slots need
-    no initialisation); every call matches the oracle."""
+    """One workspace, zero-filled once, serves two geometries (vector and matrix-core paths)
+    in alternation: every call must leave its arrival counters at zero for the next one, and
+    every call matches the oracle."""
     import torch
     rng = np.random.default_rng(11)
     batches = [W.build_batch("ws_mha", "f16", rng.integers(1, 3000, size=24), np.ones(24), 8, 8,
@@ -193,7 +193,6 @@ def test_shared_workspace_reuse(dev):
         wants.append(H.oracle_attention(b, kp, vp)[0])
     for rep in range(3):
         for b, db, want in zip(batches, dbs, wants):
-            ws.fill_(0xFF)
             db.out.zero_()
             db.attend()
             torch.cuda.synchronize()
