@@ -69,7 +69,6 @@ __device__ void m_split_finish(const DecodeArgs& a, const MfmaState<DT, D>& st, 
   const int lane = lane_id();
   const int r = lane >> 4, n = lane & 15;
   const bool col = n < G;
-  const CohBuf bo = coh_buf(a.part_o), bm = coh_buf(a.part_m), bl = coh_buf(a.part_l);
   // this piece's partial as published: normalised output, max (natural log), sum
   const float ltot = cross_rows_sum(st.l);  // sum of column n over the four lane rows
   const float inv = 1.f / ltot;
@@ -80,43 +79,46 @@ __device__ void m_split_finish(const DecodeArgs& a, const MfmaState<DT, D>& st, 
   const bool last = split_arrive(cnt, (int)(sg.k1 - sg.k0), seen, [&] {
     const int64_t slot = piece_slot(sg, self);
     if (col) {
+      float* po = a.part_o + slot * G * D;  // wave-uniform base of the slot
 #pragma unroll
-      for (int j = 0; j < C::NJ; ++j) coh_store4(bo, (slot * G + n) * D + 16 * j + 4 * r, mine_o[j]);
+      for (int j = 0; j < C::NJ; ++j) coh_store4(po, n * D + 16 * j + 4 * r, mine_o[j]);
       if (r == 0) {
-        coh_store(bm, slot * G + n, mine_m);
-        coh_store(bl, slot * G + n, ltot);
+        coh_store(a.part_m + slot * G + n, mine_m);
+        coh_store(a.part_l + slot * G + n, ltot);
       }
     }
   });
   if (!last) return;
-  float L, U[NE];
-  merge_ordered<NE, 2>(L, U, sg.k0, sg.k1, [&](int64_t k, float& m, float& lk, float (&ov)[NE]) {
+  float L[1], U[1][NE];
+  merge_ordered<1, NE, 2>(L, U, sg.k0, sg.k1,
+                          [&](int64_t k, float (&m)[1], float (&lk)[1], float (&ov)[1][NE]) {
     if (k == self || !col) {
-      m = mine_m;
-      lk = ltot;
+      m[0] = mine_m;
+      lk[0] = ltot;
 #pragma unroll
       for (int j = 0; j < C::NJ; ++j)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ov[4 * j + i] = mine_o[j][i];
+        for (int i = 0; i < 4; ++i) ov[0][4 * j + i] = mine_o[j][i];
       return;
     }
     const int64_t slot = piece_slot(sg, k);
-    m = coh_load(bm, slot * G + n);
-    lk = coh_load(bl, slot * G + n);
+    m[0] = coh_load(a.part_m + slot * G + n);
+    lk[0] = coh_load(a.part_l + slot * G + n);
+    const float* po = a.part_o + slot * G * D;  // wave-uniform base of the slot
 #pragma unroll
     for (int j = 0; j < C::NJ; ++j) {
-      const f32x4_t v = coh_load4(bo, (slot * G + n) * D + 16 * j + 4 * r);
+      const f32x4_t v = coh_load4(po, n * D + 16 * j + 4 * r);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ov[4 * j + i] = v[i];
+      for (int i = 0; i < 4; ++i) ov[0][4 * j + i] = v[i];
     }
   });
   if (col) {
-    const float rinv = 1.f / L;
+    const float rinv = 1.f / L[0];
 #pragma unroll
     for (int j = 0; j < C::NJ; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        store_out<DT>(a.out, ob + (int64_t)n * D + 16 * j + 4 * r + i, U[4 * j + i] * rinv, a.out_f32);
+        store_out<DT>(a.out, ob + (int64_t)n * D + 16 * j + 4 * r + i, U[0][4 * j + i] * rinv, a.out_f32);
   }
   counter_reset(cnt);
 }

@@ -1,5 +1,5 @@
-// decode_valu.hip — paged-attention decode on the vector ALUs, one query head per work
-// segment (multi-head attention; also the generic path for fp32).
+// decode_valu.hip — paged-attention decode on the vector ALUs for multi-head attention (and
+// the generic path for fp32): every wave runs HPW query heads of a work segment.
 //
 // The method ("vLLM 深度拆解：当 KV Cache 学会「分页」" §3.3 and §6.2): for every block of the
 // sequence, look up its physical id in the block table, read the block's K and V, score
@@ -20,8 +20,11 @@
 //     the LPD lanes of a dimension are summed once per piece of work.
 //   The 16 softmax weights of a tile go through a 64-byte LDS slot of the wave; each lane
 //   reads back the X weights of its token group.
-//   Block-table entries sit one per lane in a 64-tile window (the next window is loaded
-//   ahead) and reach the scalar unit by readlane.
+//   Block-table entries sit one per lane in a 64-tile window and reach the scalar unit by
+//   readlane.
+// A wave runs the heads h0 + 4 j (j < HPW) of a segment tile by tile, head after head, so the
+// four waves of a workgroup read 4 HPW adjacent heads of one block (16 KiB per head quartet
+// for 16-bit K and as much for V) back to back before they move to the next block.
 #include <math.h>
 
 #include "pa_device.h"
@@ -132,80 +135,107 @@ __device__ __forceinline__ void v_tile(VState<DT, D>& st, VTile<DT, D>& t, const
   }
 }
 
-// Attention of query head h of sequence s over its tiles [t0, t1).  The tiles are walked in
-// chunks of 128: both 64-entry block-table windows of a chunk are loaded before its
-// pipelined tile loop, so the loop itself only waits for tile loads.
-template <int DT, int D>
-__device__ void valu_attend(const DecodeArgs& a, int s, int h, int t0, int t1, int ctx,
-                            VState<DT, D>& st, float* pw) {
+// Attention of query heads h0 + 4 j (j < HPW) of sequence s over its tiles [t0, t1).  The
+// tiles are walked in chunks of 128, whose 64-entry block-table windows are loaded before
+// the chunk's pipelined loop, so the loop itself only waits for tile loads.  A step is one
+// tile of one head; the loads of the next step are in flight while a step is computed.
+template <int DT, int D, int HPW>
+__device__ void valu_attend(const DecodeArgs& a, int s, int h0, int t0, int t1, int ctx,
+                            VState<DT, D> (&st)[HPW], float* pw) {
   using C = VCfg<DT, D>;
   const int lane = lane_id();
   // every per-piece value is wave-uniform: keep it in scalar registers
   s = __builtin_amdgcn_readfirstlane(s);
-  h = __builtin_amdgcn_readfirstlane(h);
+  h0 = __builtin_amdgcn_readfirstlane(h0);
   t0 = __builtin_amdgcn_readfirstlane(t0);
   t1 = __builtin_amdgcn_readfirstlane(t1);
   ctx = __builtin_amdgcn_readfirstlane(ctx);
   const int G = a.num_q_heads / a.num_kv_heads;
-  const int kvh = h / G;
   const int row = __builtin_amdgcn_readfirstlane(a.qsl ? a.qsl[s] : s);
   const int off = 16 * lane;
-  uint4 qv[C::NK];
-  {
+  uint4 qv[HPW][C::NK];
+  const char* kc[HPW];
+  const char* vc[HPW];
+#pragma unroll
+  for (int j = 0; j < HPW; ++j) {
+    const int h = h0 + 4 * j;
     const char* qp = reinterpret_cast<const char*>(a.q) + ((int64_t)row * a.num_q_heads + h) * D * C::E;
 #pragma unroll
-    for (int i = 0; i < C::NK; ++i) qv[i] = ld16(qp + 16 * (4 * i + (lane >> 4)));
+    for (int i = 0; i < C::NK; ++i) qv[j][i] = ld16(qp + 16 * (4 * i + (lane >> 4)));
+    const int64_t kvh = h / G;
+    kc[j] = reinterpret_cast<const char*>(a.k_cache) + kvh * C::TILE;
+    vc[j] = reinterpret_cast<const char*>(a.v_cache) + kvh * C::TILE;
+    st[j].m = -INFINITY;
+    st[j].l = 0.f;
+#pragma unroll
+    for (int e = 0; e < C::NV; ++e) st[j].acc[e] = 0.f;
   }
   const int64_t blk_stride = (int64_t)a.num_kv_heads * C::TILE;
-  const char* kc = reinterpret_cast<const char*>(a.k_cache) + (int64_t)kvh * C::TILE;
-  const char* vc = reinterpret_cast<const char*>(a.v_cache) + (int64_t)kvh * C::TILE;
   const int32_t* bt_row = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
-
-  st.m = -INFINITY;
-  st.l = 0.f;
-#pragma unroll
-  for (int j = 0; j < C::NV; ++j) st.acc[j] = 0.f;
 
   for (int c0 = t0; c0 < t1; c0 += 128) {
     const int c1 = min(t1, c0 + 128);
     const int win0 = (c0 + lane < c1) ? bt_row[c0 + lane] : 0;
     const int win1 = (c0 + 64 + lane < c1) ? bt_row[c0 + 64 + lane] : 0;
-    auto issue = [&](VTile<DT, D>& t, int tt) {
+    auto issue = [&](VTile<DT, D>& t, int tt, int j) {
       const int idx = tt - c0;
       const int64_t blk = idx < 64 ? readlane(win0, idx) : readlane(win1, idx - 64);
-      v_issue<DT, D>(t, kc + blk * blk_stride, vc + blk * blk_stride, off);
+      v_issue<DT, D>(t, kc[j] + blk * blk_stride, vc[j] + blk * blk_stride, off);
     };
-    auto tile = [&](VTile<DT, D>& t, int tt) {
+    auto step = [&](VTile<DT, D>& t, int tt, int j) {
       const int valid = ctx - tt * kBlock;
       if (valid >= kBlock)
-        v_tile<DT, D, false>(st, t, qv, a.scale_log2, kBlock, pw);
+        v_tile<DT, D, false>(st[j], t, qv[j], a.scale_log2, kBlock, pw);
       else
-        v_tile<DT, D, true>(st, t, qv, a.scale_log2, valid, pw);
+        v_tile<DT, D, true>(st[j], t, qv[j], a.scale_log2, valid, pw);
     };
-    // two-stage software pipeline: the loads of tile tt + 1 are in flight while tile tt is
-    // computed.  The steady-state loop always issues, so every path into a tile has the
-    // same loads outstanding and the wait before it covers only that tile.
+    // Two-stage software pipeline over steps.  The steady-state loop always issues, so every
+    // path into a step has the same loads outstanding and the wait before it covers only
+    // that step; the last tiles of a chunk are peeled.
     VTile<DT, D> ta, tb;
-    issue(ta, c0);
+    issue(ta, c0, 0);
     int tt = c0;
-    for (; tt + 2 < c1; tt += 2) {
-      issue(tb, tt + 1);
-      tile(ta, tt);
-      issue(ta, tt + 2);
-      tile(tb, tt + 1);
-    }
-    if (tt + 1 < c1) {
-      issue(tb, tt + 1);
-      tile(ta, tt);
-      tile(tb, tt + 1);
+    if constexpr (HPW == 1) {
+      for (; tt + 2 < c1; tt += 2) {
+        issue(tb, tt + 1, 0);
+        step(ta, tt, 0);
+        issue(ta, tt + 2, 0);
+        step(tb, tt + 1, 0);
+      }
+      if (tt + 1 < c1) {
+        issue(tb, tt + 1, 0);
+        step(ta, tt, 0);
+        step(tb, tt + 1, 0);
+      } else {
+        step(ta, tt, 0);
+      }
     } else {
-      tile(ta, tt);
+      static_assert(HPW % 2 == 0, "steps alternate between two tile buffers");
+      for (; tt + 1 < c1; ++tt) {
+        static_for<0, HPW>([&](auto J) {
+          constexpr int j = decltype(J)::value;
+          VTile<DT, D>& cur = (j % 2 == 0) ? ta : tb;
+          VTile<DT, D>& nxt = (j % 2 == 0) ? tb : ta;
+          if constexpr (j + 1 < HPW)
+            issue(nxt, tt, j + 1);
+          else
+            issue(nxt, tt + 1, 0);
+          step(cur, tt, j);
+        });
+      }
+      static_for<0, HPW>([&](auto J) {
+        constexpr int j = decltype(J)::value;
+        VTile<DT, D>& cur = (j % 2 == 0) ? ta : tb;
+        VTile<DT, D>& nxt = (j % 2 == 0) ? tb : ta;
+        if constexpr (j + 1 < HPW) issue(nxt, tt, j + 1);
+        step(cur, tt, j);
+      });
     }
   }
 }
 
 // Finish a piece: combine the lanes of each dimension row and the per-token sums; returns
-// the total l (every lane).  Afterwards lanes with lane % LPD == 0 hold full dimension sums.
+// the total l (every lane).  Afterwards every lane holds full sums for its dimensions.
 template <int DT, int D>
 __device__ __forceinline__ float v_finish(VState<DT, D>& st) {
   using C = VCfg<DT, D>;
@@ -217,16 +247,16 @@ __device__ __forceinline__ float v_finish(VState<DT, D>& st) {
   return row16_sum(st.l);
 }
 
-// Store a finished piece's normalised output: dimension j * DPL + lane / LPD of each load j.
+// Store a finished head's output scaled by inv: dimension j * DPL + lane / LPD of each load j.
 template <int DT, int D>
-__device__ __forceinline__ void v_store(const VState<DT, D>& st, float inv, void* out,
-                                        int64_t base, bool out_f32) {
+__device__ __forceinline__ void v_store(const float (&acc)[VCfg<DT, D>::NV], float inv,
+                                        void* out, int64_t base, bool out_f32) {
   using C = VCfg<DT, D>;
   const int lane = lane_id();
   if (lane % C::LPD == 0) {
 #pragma unroll
     for (int j = 0; j < C::NV; ++j)
-      store_out<DT>(out, base + j * C::DPL + lane / C::LPD, st.acc[j] * inv, out_f32);
+      store_out<DT>(out, base + j * C::DPL + lane / C::LPD, acc[j] * inv, out_f32);
   }
 }
 
@@ -240,58 +270,72 @@ __device__ __forceinline__ void v_store_f32(const VState<DT, D>& st, float inv, 
   }
 }
 
-// A piece of a split segment: publish it, or (if it is the segment's last arrival) merge
-// every piece and write the output.  Lanes of a dimension row hold the same full sum after
-// v_finish, so each lane reads and merges its own dimensions.
-template <int DT, int D>
-__device__ void v_split_finish(const DecodeArgs& a, VState<DT, D>& st, float l,
-                               const SplitSeg& sg, int64_t self, int32_t* cnt, int seen,
-                               int64_t ob) {
+// A piece of a split segment (heads h0 + 4 j): publish it, or (if it is the segment's last
+// arrival) merge every piece and write the output.  Every lane holds full sums for its
+// dimensions after v_finish, so each lane reads and merges its own dimensions of every head.
+// Slot rows: head j of a piece is row (slot HPW + j) of the partial arrays.
+template <int DT, int D, int HPW>
+__device__ void v_split_finish(const DecodeArgs& a, const VState<DT, D> (&st)[HPW],
+                               const float (&l)[HPW], const SplitSeg& sg, int64_t self,
+                               int32_t* cnt, int seen, int64_t ob0) {
   using C = VCfg<DT, D>;
   const int lane = lane_id();
-  const CohBuf bo = coh_buf(a.part_o), bm = coh_buf(a.part_m), bl = coh_buf(a.part_l);
-  const int dim0 = lane / C::LPD;  // dimension j * DPL + dim0 of load j
+  const int dim0 = lane / C::LPD;  // dimension e * DPL + dim0 of load e
   // this piece's partial as published: normalised output, max (natural log), sum
-  const float inv = 1.f / l;
-  const float mine_m = st.m * 0.69314718055994531f;
-  float mine_o[C::NV];
+  float mine_m[HPW], mine_o[HPW][C::NV];
 #pragma unroll
-  for (int j = 0; j < C::NV; ++j) mine_o[j] = st.acc[j] * inv;
+  for (int j = 0; j < HPW; ++j) {
+    const float inv = 1.f / l[j];
+    mine_m[j] = st[j].m * 0.69314718055994531f;
+#pragma unroll
+    for (int e = 0; e < C::NV; ++e) mine_o[j][e] = st[j].acc[e] * inv;
+  }
   const bool last = split_arrive(cnt, (int)(sg.k1 - sg.k0), seen, [&] {
-    const int64_t slot = piece_slot(sg, self);
-    if (lane % C::LPD == 0) {
+    const int64_t row0 = piece_slot(sg, self) * HPW;
 #pragma unroll
-      for (int j = 0; j < C::NV; ++j) coh_store(bo, slot * D + j * C::DPL + dim0, mine_o[j]);
-    }
-    if (lane == 0) {
-      coh_store(bm, slot, mine_m);
-      coh_store(bl, slot, l);
+    for (int j = 0; j < HPW; ++j) {
+      if (lane % C::LPD == 0) {
+#pragma unroll
+        for (int e = 0; e < C::NV; ++e)
+          coh_store(a.part_o + (row0 + j) * D + e * C::DPL + dim0, mine_o[j][e]);
+      }
+      if (lane == 0) {
+        coh_store(a.part_m + row0 + j, mine_m[j]);
+        coh_store(a.part_l + row0 + j, l[j]);
+      }
     }
   });
   if (!last) return;
-  float L, U[C::NV];
-  merge_ordered<C::NV, 4>(L, U, sg.k0, sg.k1,
-                          [&](int64_t k, float& m, float& lk, float (&ov)[C::NV]) {
-    if (k == self) {
-      m = mine_m;
-      lk = l;
+  float L[HPW], U[HPW][C::NV];
+  merge_ordered<HPW, C::NV, (HPW > 2 ? 1 : 2)>(
+      L, U, sg.k0, sg.k1,
+      [&](int64_t k, float (&m)[HPW], float (&lk)[HPW], float (&ov)[HPW][C::NV]) {
+        if (k == self) {
 #pragma unroll
-      for (int j = 0; j < C::NV; ++j) ov[j] = mine_o[j];
-      return;
-    }
-    const int64_t slot = piece_slot(sg, k);
-    m = coh_load(bm, slot);
-    lk = coh_load(bl, slot);
+          for (int j = 0; j < HPW; ++j) {
+            m[j] = mine_m[j];
+            lk[j] = l[j];
 #pragma unroll
-    for (int j = 0; j < C::NV; ++j) ov[j] = coh_load(bo, slot * D + j * C::DPL + dim0);
-  });
+            for (int e = 0; e < C::NV; ++e) ov[j][e] = mine_o[j][e];
+          }
+          return;
+        }
+        const int64_t row0 = piece_slot(sg, k) * HPW;
 #pragma unroll
-  for (int j = 0; j < C::NV; ++j) st.acc[j] = U[j];
-  v_store<DT, D>(st, 1.f / L, a.out, ob, a.out_f32);
+        for (int j = 0; j < HPW; ++j) {
+          m[j] = coh_load(a.part_m + row0 + j);
+          lk[j] = coh_load(a.part_l + row0 + j);
+#pragma unroll
+          for (int e = 0; e < C::NV; ++e)
+            ov[j][e] = coh_load(a.part_o + (row0 + j) * D + e * C::DPL + dim0);
+        }
+      });
+#pragma unroll
+  for (int j = 0; j < HPW; ++j) v_store<DT, D>(U[j], 1.f / L[j], a.out, ob0 + 4 * j * D, a.out_f32);
   counter_reset(cnt);
 }
 
-template <int DT, int D, int MODE>
+template <int DT, int D, int MODE, int HPW>
 __global__ __launch_bounds__(kWG) void valu_decode_kernel(DecodeArgs a) {
   // LDS: one 16-float weight slot per wave (first, for 16-byte alignment), then the plan
   // (S + 1 ints) and the scan buffer (kWG ints)
@@ -302,7 +346,6 @@ __global__ __launch_bounds__(kWG) void valu_decode_kernel(DecodeArgs a) {
   float* pw = reinterpret_cast<float*>(lds) + 16 * wave;
   int32_t* base = lds + 16 * kWavesPerWG;
   int32_t* tmp = base + S + 1;
-  const int segs = a.num_q_heads;
   const int64_t W = (int64_t)gridDim.x * kWavesPerWG;
   const int64_t w = (int64_t)blockIdx.x * kWavesPerWG + wave;
 
@@ -310,8 +353,9 @@ __global__ __launch_bounds__(kWG) void valu_decode_kernel(DecodeArgs a) {
     PlanIn pin{a.context_lens, a.qsl, S, kValuUnit, a.seg_extra};
     build_plan(base, tmp, pin);
     zero_empty_rows<DT>(pin, a.out, a.num_q_heads, D, w, W, a.out_f32);
-    // units: (sequence, group of kWavesPerWG heads, tile); wave i runs head i of each group
-    const int groups = (a.num_q_heads + kWavesPerWG - 1) / kWavesPerWG;
+    // units: (sequence, group of 4 HPW heads, tile); wave i runs heads i + 4 j of each group
+    constexpr int GH = kWavesPerWG * HPW;
+    const int groups = (a.num_q_heads + GH - 1) / GH;
     const Part part = make_part((int64_t)base[S] * groups, gridDim.x);
     even_split_drive(part, [&](int64_t o, int64_t lo, int64_t hi) {
       for (int64_t i = lo; i < hi;) {
@@ -322,12 +366,12 @@ __global__ __launch_bounds__(kWG) void valu_decode_kernel(DecodeArgs a) {
         const int grp = (int)((i - sbase) / seglen);
         const int64_t seg0 = sbase + (int64_t)grp * seglen;
         const int64_t pe = min(hi, seg0 + seglen);
-        const int h = grp * kWavesPerWG + wave;  // this wave's head
+        const int h0 = grp * GH + wave;  // this wave's first head (HPW > 1: all exist)
         const int t0 = (int)(i - seg0), t1 = (int)min(pe - seg0, (int64_t)nt);
-        if (h < a.num_q_heads && t0 < nt) {
+        if (h0 < a.num_q_heads && t0 < nt) {
           const int ctx = a.context_lens[s];
           const int row = a.qsl ? a.qsl[s] : s;
-          const int64_t ob = ((int64_t)row * a.num_q_heads + h) * D;
+          const int64_t ob0 = ((int64_t)row * a.num_q_heads + h0) * D;
           const bool whole = t0 == 0 && t1 == nt;
           SplitSeg sg{};
           int32_t* cnt = nullptr;
@@ -337,13 +381,17 @@ __global__ __launch_bounds__(kWG) void valu_decode_kernel(DecodeArgs a) {
             cnt = a.counters + kWavesPerWG * sg.k0 + wave;
             seen = counter_peek(cnt);  // consumed after the tiles
           }
-          VState<DT, D> st;
-          valu_attend<DT, D>(a, s, h, t0, t1, ctx, st, pw);
-          const float l = v_finish<DT, D>(st);
+          VState<DT, D> st[HPW];
+          valu_attend<DT, D, HPW>(a, s, h0, t0, t1, ctx, st, pw);
+          float l[HPW];
+#pragma unroll
+          for (int j = 0; j < HPW; ++j) l[j] = v_finish<DT, D>(st[j]);
           if (whole) {
-            v_store<DT, D>(st, 1.f / l, a.out, ob, a.out_f32);
+#pragma unroll
+            for (int j = 0; j < HPW; ++j)
+              v_store<DT, D>(st[j].acc, 1.f / l[j], a.out, ob0 + 4 * j * D, a.out_f32);
           } else {
-            v_split_finish<DT, D>(a, st, l, sg, o, cnt, seen, ob);
+            v_split_finish<DT, D, HPW>(a, st, l, sg, o, cnt, seen, ob0);
           }
         }
         i = pe;
@@ -365,6 +413,7 @@ __global__ __launch_bounds__(kWG) void valu_decode_kernel(DecodeArgs a) {
         a.part_l[e] = 0.f;
       }
     }
+    const int segs = a.num_q_heads;
     const int64_t total = (int64_t)base[S] * segs;
     for (int64_t i = w; i < total; i += W) {
       const int s = find_seq(base, S, i, segs);
@@ -375,14 +424,14 @@ __global__ __launch_bounds__(kWG) void valu_decode_kernel(DecodeArgs a) {
       const int ctx = a.context_lens[s];
       const int nt = (ctx + kBlock - 1) / kBlock;
       const int t0 = p * PU, t1 = min(nt, t0 + PU);
-      VState<DT, D> st;
-      valu_attend<DT, D>(a, s, h, t0, t1, ctx, st, pw);
-      const float l = v_finish<DT, D>(st);
+      VState<DT, D> st[1];
+      valu_attend<DT, D, 1>(a, s, h, t0, t1, ctx, st, pw);
+      const float l = v_finish<DT, D>(st[0]);
       const float inv = 1.f / l;
       const int64_t e = ((int64_t)s * a.num_q_heads + h) * P + p;
-      v_store_f32<DT, D>(st, inv, a.part_o + e * D);
+      v_store_f32<DT, D>(st[0], inv, a.part_o + e * D);
       if (lane == 0) {
-        a.part_m[e] = st.m * 0.69314718055994531f;
+        a.part_m[e] = st[0].m * 0.69314718055994531f;
         a.part_l[e] = l;
       }
     }
@@ -393,13 +442,31 @@ static size_t valu_lds_bytes(int num_seqs) {
   return (size_t)(num_seqs + 1 + kWG) * sizeof(int32_t) + kWavesPerWG * 16 * sizeof(float);
 }
 
+template <int DT, int D, int MODE, int HPW>
+static void launch_k(const DecodeArgs& a, int grid, size_t lds, hipStream_t st) {
+  hipLaunchKernelGGL((valu_decode_kernel<DT, D, MODE, HPW>), dim3(grid), dim3(kWG), lds, st, a);
+}
+
+template <int DT, int D, int MODE>
+static void launch_hpw(const DecodeArgs& a, int grid, size_t lds, hipStream_t st) {
+  if constexpr (MODE == MODE_EVEN) {
+    // fp32 queries fill twice the registers: at most two heads per wave
+    if constexpr (DT != DT_F32) {
+      if (a.heads_per_wave == 8) return launch_k<DT, D, MODE, 8>(a, grid, lds, st);
+      if (a.heads_per_wave == 4) return launch_k<DT, D, MODE, 4>(a, grid, lds, st);
+    }
+    if (a.heads_per_wave == 2) return launch_k<DT, D, MODE, 2>(a, grid, lds, st);
+  }
+  launch_k<DT, D, MODE, 1>(a, grid, lds, st);
+}
+
 template <int DT, int MODE>
 static hipError_t launch_d(const DecodeArgs& a, int grid, hipStream_t st) {
   const size_t lds = valu_lds_bytes(a.num_seqs);
   if (a.head_dim == 64)
-    hipLaunchKernelGGL((valu_decode_kernel<DT, 64, MODE>), dim3(grid), dim3(kWG), lds, st, a);
+    launch_hpw<DT, 64, MODE>(a, grid, lds, st);
   else
-    hipLaunchKernelGGL((valu_decode_kernel<DT, 128, MODE>), dim3(grid), dim3(kWG), lds, st, a);
+    launch_hpw<DT, 128, MODE>(a, grid, lds, st);
   return hipGetLastError();
 }
 
@@ -414,27 +481,40 @@ hipError_t launch_valu_decode(int dt, int mode, const DecodeArgs& a, int grid, h
   return launch_d<DT_BF16, MODE_PARTITION>(a, grid, st);
 }
 
-template <int DT, int MODE>
-static int occ(int head_dim, int lds) {
+// resident workgroups per CU of the kernel that `hpw` selects
+template <int DT, int MODE, int HPW>
+static int occ_k(int head_dim, int lds) {
   int n = 0;
   hipError_t e;
   if (head_dim == 64)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, valu_decode_kernel<DT, 64, MODE>, kWG, lds);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, valu_decode_kernel<DT, 64, MODE, HPW>, kWG, lds);
   else
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, valu_decode_kernel<DT, 128, MODE>, kWG, lds);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, valu_decode_kernel<DT, 128, MODE, HPW>, kWG, lds);
   return e == hipSuccess && n > 0 ? n : 1;
 }
 
-int valu_decode_max_blocks_per_cu(int dt, int head_dim, int mode, int lds_bytes) {
+template <int DT, int MODE>
+static int occ(int head_dim, int hpw, int lds) {
+  if constexpr (MODE == MODE_EVEN) {
+    if constexpr (DT != DT_F32) {
+      if (hpw == 8) return occ_k<DT, MODE, 8>(head_dim, lds);
+      if (hpw == 4) return occ_k<DT, MODE, 4>(head_dim, lds);
+    }
+    if (hpw == 2) return occ_k<DT, MODE, 2>(head_dim, lds);
+  }
+  return occ_k<DT, MODE, 1>(head_dim, lds);
+}
+
+int valu_decode_max_blocks_per_cu(int dt, int head_dim, int hpw, int mode, int lds_bytes) {
   const int lds = lds_bytes + kWavesPerWG * 16 * (int)sizeof(float);
   if (mode == MODE_EVEN) {
-    if (dt == DT_F32) return occ<DT_F32, MODE_EVEN>(head_dim, lds);
-    if (dt == DT_F16) return occ<DT_F16, MODE_EVEN>(head_dim, lds);
-    return occ<DT_BF16, MODE_EVEN>(head_dim, lds);
+    if (dt == DT_F32) return occ<DT_F32, MODE_EVEN>(head_dim, hpw, lds);
+    if (dt == DT_F16) return occ<DT_F16, MODE_EVEN>(head_dim, hpw, lds);
+    return occ<DT_BF16, MODE_EVEN>(head_dim, hpw, lds);
   }
-  if (dt == DT_F32) return occ<DT_F32, MODE_PARTITION>(head_dim, lds);
-  if (dt == DT_F16) return occ<DT_F16, MODE_PARTITION>(head_dim, lds);
-  return occ<DT_BF16, MODE_PARTITION>(head_dim, lds);
+  if (dt == DT_F32) return occ<DT_F32, MODE_PARTITION>(head_dim, 1, lds);
+  if (dt == DT_F16) return occ<DT_F16, MODE_PARTITION>(head_dim, 1, lds);
+  return occ<DT_BF16, MODE_PARTITION>(head_dim, 1, lds);
 }
 
 }  // namespace pa

@@ -93,19 +93,46 @@ int bucket_lds_bytes(int bucket) { return ((1 << bucket) + pa::kWG) * (int)sizeo
 // resident workgroups per CU for pa_decode's even split (vector path, matrix-core path)
 constexpr int kEvenWgPerCu[2] = {1, 2};
 
+// Query heads per wave of the vector path's even split: a wave runs heads h0 + 4 j
+// (j < HPW), so a workgroup reads 4 HPW adjacent heads of a block back to back, which the
+// HBM serves faster than the same bytes in smaller pieces.  Larger groups also mean fewer,
+// longer segments, and once there are fewer segments than workgroups every segment is cut
+// into several pieces whose merge costs more than the locality gains.  So: the largest of
+// 8, 4, 2 whose head groups tile num_q_heads exactly and leave at least one segment per
+// workgroup (fp32: at most 2, its queries fill twice the registers), else 1; optional cap
+// for tuning.
+int heads_per_wave(const pa_geom* g) {
+  static const int v = [] {
+    const char* s = getenv("PA_DECODE_HPW");
+    return s ? atoi(s) : 0;
+  }();
+  const int cap = g->kv_dtype == PA_F32 ? 2 : 8;
+  const int o = wg_per_cu_override();
+  const int64_t workgroups = (int64_t)cu_count() * (o > 0 ? o : kEvenWgPerCu[0]);
+  for (int h = 8; h >= 2; h /= 2) {
+    if (h > cap || (v > 0 && h > v) || g->num_q_heads % (pa::kWavesPerWG * h)) continue;
+    const int64_t segments = (int64_t)g->num_seqs * (g->num_q_heads / (pa::kWavesPerWG * h));
+    if (segments >= workgroups) return h;
+  }
+  return 1;
+}
+
+int hpw_index(int hpw) { return hpw == 8 ? 3 : hpw == 4 ? 2 : hpw == 2 ? 1 : 0; }
+
 // workgroups of the split kernel: every CU full at the kernel's occupancy
 int split_grid(const pa_geom* g, int mode) {
-  static std::atomic<int> cache[kMaxDevices][2][3][2][2][15];
+  static std::atomic<int> cache[kMaxDevices][2][3][2][2][4][15];
   const int dev = current_device();
   const int path = use_mfma(g) ? 1 : 0;
   const int di = g->head_dim == 64 ? 0 : 1;
   const int bk = seq_bucket(g->num_seqs);
-  std::atomic<int>& c = cache[dev][path][g->kv_dtype][di][mode][bk];
+  const int hpw = path == 0 && mode == pa::MODE_EVEN ? heads_per_wave(g) : 1;
+  std::atomic<int>& c = cache[dev][path][g->kv_dtype][di][mode][hpw_index(hpw)][bk];
   int occ = c.load(std::memory_order_relaxed);
   if (occ <= 0) {
     const int lds = bucket_lds_bytes(bk);
     occ = path ? pa::mfma_decode_max_blocks_per_cu(g->kv_dtype, g->head_dim, mode, lds)
-               : pa::valu_decode_max_blocks_per_cu(g->kv_dtype, g->head_dim, mode, lds);
+               : pa::valu_decode_max_blocks_per_cu(g->kv_dtype, g->head_dim, hpw, mode, lds);
     c.store(occ, std::memory_order_relaxed);
   }
   // The even split streams best with few resident workgroups per CU: each of them reads
@@ -123,22 +150,25 @@ struct SplitShape {
 
 SplitShape split_shape(const pa_geom* g) {
   if (use_mfma(g)) return {g->num_kv_heads, g->num_q_heads / g->num_kv_heads, pa::kMfmaUnit};
-  return {g->num_q_heads, 1, pa::kValuUnit};
+  const int hpw = heads_per_wave(g);
+  return {g->num_q_heads / hpw, hpw, pa::kValuUnit};
 }
 
 // pa_decode's workspace: one arrival counter per wave of the largest split grid the device
 // can have (so the counters sit at the same place for every geometry and stay zero between
 // calls), then two partial slots per wave of this geometry's grid: o [W][2][G][D],
-// m [W][2][G], l [W][2][G].
+// m [W][2][G], l [W][2][G] (G: heads per wave).
 size_t counter_bytes() {
   const size_t n = (size_t)cu_count() * pa::kMaxWgPerCu * pa::kWavesPerWG * sizeof(int32_t);
   return (n + 255) / 256 * 256;
 }
 
+size_t even_slots(const pa_geom* g, int grid) {
+  return (size_t)grid * pa::kWavesPerWG * 2 * split_shape(g).heads_per_seg;
+}
+
 size_t even_workspace_bytes(const pa_geom* g, int grid) {
-  const SplitShape sh = split_shape(g);
-  const size_t slots = (size_t)grid * pa::kWavesPerWG * 2 * sh.heads_per_seg;
-  return counter_bytes() + slots * ((size_t)g->head_dim + 2) * sizeof(float);
+  return counter_bytes() + even_slots(g, grid) * ((size_t)g->head_dim + 2) * sizeof(float);
 }
 
 pa_status hip_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
@@ -206,8 +236,7 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   const int grid = split_grid(g, pa::MODE_EVEN);
   const size_t need = even_workspace_bytes(g, grid);
   if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
-  const SplitShape sh = split_shape(g);
-  const size_t slots = (size_t)grid * pa::kWavesPerWG * 2 * sh.heads_per_seg;
+  const size_t slots = even_slots(g, grid);
   int32_t* counters = static_cast<int32_t*>(workspace);
   float* part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + counter_bytes());
   float* part_m = part_o + slots * g->head_dim;
@@ -232,7 +261,9 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   a.max_blocks_per_seq = g->max_blocks_per_seq;
   a.out_f32 = g->out_dtype == PA_F32 && g->kv_dtype != PA_F32;
   a.scale_log2 = scale_to_log2(scale);
-  a.seg_extra = seg_extra_override() >= 0 ? seg_extra_override() : kSegExtra[use_mfma(g) ? 1 : 0];
+  const int path = use_mfma(g) ? 1 : 0;
+  a.seg_extra = seg_extra_override() >= 0 ? seg_extra_override() : kSegExtra[path];
+  a.heads_per_wave = path == 0 ? heads_per_wave(g) : 1;
 
   hipError_t e = use_mfma(g) ? pa::launch_mfma_decode(g->kv_dtype, pa::MODE_EVEN, a, grid, st)
                              : pa::launch_valu_decode(g->kv_dtype, pa::MODE_EVEN, a, grid, st);

@@ -10,6 +10,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "pa_internal.h"
 
 namespace pa {
@@ -261,7 +263,7 @@ __device__ __forceinline__ Part make_part(int64_t total, int64_t workgroups) {
 __device__ __forceinline__ int64_t part_lo(const Part& p, int64_t o) {
   return p.NK ? (p.total * o) / p.NK : 0;
 }
-// owner of unit u (u < total)
+// owner of unit u (u < total): the largest o with part_lo(o) <= u
 __device__ __forceinline__ int64_t part_owner(const Part& p, int64_t u) {
   return ((u + 1) * p.NK - 1) / p.total;
 }
@@ -312,32 +314,33 @@ __device__ __forceinline__ void even_split_drive(const Part& p, F&& range) {
 // and writes the output.  This is a release/acquire handshake restricted to the data it
 // orders, so no L2 of the device is written back or invalidated as a whole.  The merging
 // wave returns the counter to zero, which keeps a workspace ready for the next call.
-constexpr int kCohPolicy = 16;  // buffer-op cache policy: sc1 (device scope)
+constexpr int kCohPolicy = 16;  // buffer-op cache policy: sc1 (device scope), as the
+                                // compiler gives device-scope atomic loads and stores
 
-struct CohBuf {
-  __amdgpu_buffer_rsrc_t r;
-};
-
-__device__ __forceinline__ CohBuf coh_buf(const float* base) {
-  // raw 32-bit buffer: stride 0, the largest record count, 32-bit data format
-  return {__builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, 0x7fffffff, 0x00020000)};
+// single floats through 64-bit addresses
+__device__ __forceinline__ float coh_load(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ float coh_load(const CohBuf& b, int64_t elem) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(b.r, (int)(4 * elem), 0, kCohPolicy));
+__device__ __forceinline__ void coh_store(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ f32x4_t coh_load4(const CohBuf& b, int64_t elem) {
-  return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(b.r, (int)(4 * elem), 0, kCohPolicy));
+// four consecutive floats at element offset e (< 2^29) of a wave-uniform base, as one
+// buffer access
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coh_rsrc(const float* base) {
+  // raw buffer: stride 0, the largest record count, 32-bit data format
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, 0x7fffffff, 0x00020000);
 }
-__device__ __forceinline__ void coh_store(const CohBuf& b, int64_t elem, float v) {
-  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), b.r, (int)(4 * elem), 0, kCohPolicy);
+__device__ __forceinline__ f32x4_t coh_load4(const float* base, int e) {
+  return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(coh_rsrc(base), 4 * e, 0, kCohPolicy));
 }
-__device__ __forceinline__ void coh_store4(const CohBuf& b, int64_t elem, f32x4_t v) {
+__device__ __forceinline__ void coh_store4(float* base, int e, f32x4_t v) {
   typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), b.r, (int)(4 * elem), 0, kCohPolicy);
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), coh_rsrc(base), 4 * e, 0, kCohPolicy);
 }
 
 // Device-scope read of a segment counter (every lane gets the value; not yet made uniform,
-// so the read can be issued well before it is used).
+// so the read can be issued well before it is used: a split piece reads it before its first
+// unit, and again when it ends if the first value did not show every other piece arrived).
 __device__ __forceinline__ int counter_peek(int32_t* c) {
   return __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -348,10 +351,8 @@ __device__ __forceinline__ int counter_peek(int32_t* c) {
 // already arrived (that piece merges from its registers and nobody reads its slot).
 template <class Pub>
 __device__ __forceinline__ bool split_arrive(int32_t* c, int others, int seen, Pub&& publish) {
-  seen = __builtin_amdgcn_readfirstlane(seen);
-  if (seen == others) return true;
-  seen = __builtin_amdgcn_readfirstlane(counter_peek(c));
-  if (seen == others) return true;
+  if (__builtin_amdgcn_readfirstlane(seen) == others) return true;
+  if (__builtin_amdgcn_readfirstlane(counter_peek(c)) == others) return true;  // a fresh look
   publish();
   // every store of this wave, the partial included, has reached the point of coherence
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -364,58 +365,68 @@ __device__ __forceinline__ void counter_reset(int32_t* c) {
   if (__lane_id() == 0) __hip_atomic_store(c, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Log-sum-exp merge, per lane, of NE output elements of one row over the pieces k0..k1 in
-// that order: fetch(k, m, l, o) gives piece k's max (natural-log domain), sum and
+// Log-sum-exp merge, per lane, of R rows of NE output elements over the pieces k0..k1 in
+// that order: fetch(k, m, l, o) gives piece k's per-row max (natural-log domain), sum and
 // normalised output, by device-scope loads or, for the merging piece itself, from the
 // registers it would have published.  The arithmetic depends only on the pieces' values and
 // the fixed order, so every call gives the same bits whichever piece merges.  Pieces are
 // fetched B at a time into two alternating batches, so the loads of the next batch are in
-// flight while the current one is combined.  Returns the merged output in U and its sum in L
-// (the output is U / L).
-template <int NE, int B>
+// flight while the current one is combined.  Returns each row's merged output in U and its
+// sum in L (the output is U / L).
+template <int R, int NE, int B>
 struct MergeBatch {
-  float m[B], l[B], o[B][NE];
+  float m[B][R], l[B][R], o[B][R][NE];
 };
 
-template <int NE, int B, class Fetch>
-__device__ __forceinline__ void merge_ordered(float& L, float (&U)[NE], int64_t k0, int64_t k1,
-                                              Fetch&& fetch) {
+template <int R, int NE, int B, class Fetch>
+__device__ __forceinline__ void merge_ordered(float (&L)[R], float (&U)[R][NE], int64_t k0,
+                                              int64_t k1, Fetch&& fetch) {
   const int n = (int)(k1 - k0 + 1);
-  float M = -INFINITY;
-  L = 0.f;
+  float M[R];
 #pragma unroll
-  for (int e = 0; e < NE; ++e) U[e] = 0.f;
-  auto load = [&](MergeBatch<NE, B>& bt, int q0) {
+  for (int r = 0; r < R; ++r) {
+    M[r] = -INFINITY;
+    L[r] = 0.f;
+#pragma unroll
+    for (int e = 0; e < NE; ++e) U[r][e] = 0.f;
+  }
+  auto load = [&](MergeBatch<R, NE, B>& bt, int q0) {
 #pragma unroll
     for (int b = 0; b < B; ++b) {
       if (q0 + b < n) {
         fetch(k0 + q0 + b, bt.m[b], bt.l[b], bt.o[b]);
       } else {
-        bt.m[b] = -INFINITY;
-        bt.l[b] = 0.f;
 #pragma unroll
-        for (int e = 0; e < NE; ++e) bt.o[b][e] = 0.f;
+        for (int r = 0; r < R; ++r) {
+          bt.m[b][r] = -INFINITY;
+          bt.l[b][r] = 0.f;
+#pragma unroll
+          for (int e = 0; e < NE; ++e) bt.o[b][r][e] = 0.f;
+        }
       }
     }
   };
-  auto combine = [&](const MergeBatch<NE, B>& bt) {
-    float mn = M;
+  auto combine = [&](const MergeBatch<R, NE, B>& bt) {
 #pragma unroll
-    for (int b = 0; b < B; ++b) mn = fmaxf(mn, bt.m[b]);
-    const float s = M == -INFINITY ? 0.f : __expf(M - mn);
-    L *= s;
+    for (int r = 0; r < R; ++r) {
+      float mn = M[r];
 #pragma unroll
-    for (int e = 0; e < NE; ++e) U[e] *= s;
+      for (int b = 0; b < B; ++b) mn = fmaxf(mn, bt.m[b][r]);
+      const float s = M[r] == -INFINITY ? 0.f : __expf(M[r] - mn);
+      L[r] *= s;
 #pragma unroll
-    for (int b = 0; b < B; ++b) {
-      const float w = bt.m[b] == -INFINITY ? 0.f : bt.l[b] * __expf(bt.m[b] - mn);
-      L += w;
+      for (int e = 0; e < NE; ++e) U[r][e] *= s;
 #pragma unroll
-      for (int e = 0; e < NE; ++e) U[e] = fmaf(w, bt.o[b][e], U[e]);
+      for (int b = 0; b < B; ++b) {
+        const float w = bt.m[b][r] == -INFINITY ? 0.f : bt.l[b][r] * __expf(bt.m[b][r] - mn);
+        L[r] += w;
+#pragma unroll
+        for (int e = 0; e < NE; ++e) U[r][e] = fmaf(w, bt.o[b][r][e], U[r][e]);
+      }
+      M[r] = mn;
     }
-    M = mn;
   };
-  MergeBatch<NE, B> ba, bb;
+  MergeBatch<R, NE, B> ba, bb;
   load(ba, 0);
   for (int q0 = 0; q0 < n; q0 += 2 * B) {
     if (q0 + B < n) load(bb, q0 + B);
@@ -423,6 +434,15 @@ __device__ __forceinline__ void merge_ordered(float& L, float (&U)[NE], int64_t 
     if (q0 + B >= n) break;
     if (q0 + 2 * B < n) load(ba, q0 + 2 * B);
     combine(bb);
+  }
+}
+
+// Calls f(std::integral_constant<int, i>) for i = 0 .. N-1, unrolled: i is a constant in f.
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
   }
 }
 

@@ -35,7 +35,7 @@ struct DecodeArgs {
   float* part_o;            // MODE_EVEN: [W][2][G][D]; MODE_PARTITION: tmp_out [rows][Hq][P][D]
   float* part_m;            // MODE_EVEN: [W][2][G];    MODE_PARTITION: max_logits [rows][Hq][P]
   float* part_l;            // MODE_EVEN: [W][2][G];    MODE_PARTITION: exp_sums   [rows][Hq][P]
-  int32_t* counters;        // MODE_EVEN: [W] arrival counters, zero before and after a call
+  int32_t* counters;        // MODE_EVEN: [4 o + i] arrival counters, zero before and after a call
   int32_t num_seqs;
   int32_t num_q_heads;
   int32_t num_kv_heads;
@@ -46,6 +46,7 @@ struct DecodeArgs {
   int32_t partition_units;  // MODE_PARTITION: units per partition
   int32_t max_partitions;   // MODE_PARTITION
   int32_t seg_extra;        // MODE_EVEN: balancing units per segment (see PlanIn)
+  int32_t heads_per_wave;   // MODE_EVEN, vector kernel: query heads per wave (1, 2, 4, 8)
 };
 
 struct ReshapeArgs {
@@ -74,7 +75,7 @@ struct PartReduceArgs {
 hipError_t launch_reshape(int dt, const ReshapeArgs& a, hipStream_t st);
 // VALU kernel: one query head per segment (segs = Hq), any head_dim in {64, 128}
 hipError_t launch_valu_decode(int dt, int mode, const DecodeArgs& a, int grid, hipStream_t st);
-int valu_decode_max_blocks_per_cu(int dt, int head_dim, int mode, int lds_bytes);
+int valu_decode_max_blocks_per_cu(int dt, int head_dim, int hpw, int mode, int lds_bytes);
 // MFMA kernel: one kv head (all G query heads) per segment, 16-bit dtypes
 hipError_t launch_mfma_decode(int dt, int mode, const DecodeArgs& a, int grid, hipStream_t st);
 int mfma_decode_max_blocks_per_cu(int dt, int head_dim, int mode, int lds_bytes);

@@ -199,11 +199,16 @@ def test_shared_workspace_reuse(dev):
             check_out(db.out_host(), want, TOL[b.dtype], f"{b.name} call {rep}")
 
 
-@pytest.mark.parametrize("dtype,Hq,Hkv", [("f16", 8, 8), ("bf16", 16, 2), ("f16", 12, 4)])
-def test_many_ragged_sequences(dev, dtype, Hq, Hkv):
-    """300 sequences of 1..3000 tokens: shares that cross many segment boundaries."""
-    rng = np.random.default_rng(300 + Hq)
-    b = W.build_batch("many", dtype, rng.integers(1, 3001, size=300), np.ones(300), Hq, Hkv, 128,
+@pytest.mark.parametrize("dtype,Hq,Hkv,D", [("f16", 8, 8, 128), ("bf16", 16, 2, 128),
+                                            ("f16", 12, 4, 128), ("f16", 32, 32, 128),
+                                            ("bf16", 16, 16, 128), ("bf16", 32, 32, 64),
+                                            ("f16", 16, 16, 64)])
+def test_many_ragged_sequences(dev, dtype, Hq, Hkv, D):
+    """300 sequences of 1..3000 tokens: shares that cross many segment boundaries.  With
+    this many sequences the multi-head path runs 2, 4 or 8 heads per wave (8, 16 or 32
+    heads), so every head grouping of its kernel is covered."""
+    rng = np.random.default_rng(300 + Hq + D)
+    b = W.build_batch("many", dtype, rng.integers(1, 3001, size=300), np.ones(300), Hq, Hkv, D,
                       rng)
     db, got, want = parity(dev, b)
     for _ in range(3):  # repeated calls: identical bits whichever workgroup took which chunk
