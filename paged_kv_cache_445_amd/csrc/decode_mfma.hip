@@ -87,7 +87,7 @@ __device__ void m_split_finish(const DecodeArgs& a, const MfmaState<DT, D>& st, 
         coh_store(a.part_l + slot * G + n, ltot);
       }
     }
-  });
+  }, [] {});
   if (!last) return;
   float L[1], U[1][NE];
   merge_ordered<1, NE, 2>(L, U, sg.k0, sg.k1,

@@ -135,65 +135,109 @@ __device__ __forceinline__ void v_tile(VState<DT, D>& st, VTile<DT, D>& t, const
   }
 }
 
-// Attention of query heads h0 + 4 j (j < HPW) of sequence s over its tiles [t0, t1).  The
-// tiles are walked in chunks of 128, whose 64-entry block-table windows are loaded before
-// the chunk's pipelined loop, so the loop itself only waits for tile loads.  A step is one
-// tile of one head; the loads of the next step are in flight while a step is computed.
+// A piece: query heads h0 + 4 j (j < HPW) of sequence s over its tiles [t0, t1).  Every
+// field is wave-uniform.
+struct VPiece {
+  int s, h0, t0, t1, ctx;
+};
+
+// The loads a piece needs before its tile loop: the block-table window of its first chunk,
+// the query of its heads and its first step (tile t0 of head h0).  They are issued while
+// the previous piece ends, so a wave moves from piece to piece without draining its loads.
 template <int DT, int D, int HPW>
-__device__ void valu_attend(const DecodeArgs& a, int s, int h0, int t0, int t1, int ctx,
-                            VState<DT, D> (&st)[HPW], float* pw) {
+struct VStart {
+  int win0, win1;  // entries t0 + lane and t0 + 64 + lane of the block table
+  uint4 q[HPW][VCfg<DT, D>::NK];
+  VTile<DT, D> first;
+};
+
+// Block-table window of the first chunk of p (tiles t0 .. t0 + 127).
+__device__ __forceinline__ void v_window(const DecodeArgs& a, const VPiece& p, int& win0,
+                                         int& win1) {
+  const int lane = lane_id();
+  const int32_t* bt_row = a.block_tables + (int64_t)p.s * a.max_blocks_per_seq;
+  const int c1 = min(p.t1, p.t0 + 128);
+  win0 = (p.t0 + lane < c1) ? bt_row[p.t0 + lane] : 0;
+  win1 = (p.t0 + 64 + lane < c1) ? bt_row[p.t0 + 64 + lane] : 0;
+}
+
+template <int DT, int D>
+__device__ __forceinline__ const char* v_head_base(const void* pool, const DecodeArgs& a, int h) {
+  const int64_t kvh = h / (a.num_q_heads / a.num_kv_heads);
+  return reinterpret_cast<const char*>(pool) + kvh * VCfg<DT, D>::TILE;
+}
+
+// Issue the query and first-step loads of p (vs.win0 / win1 already hold its window).
+template <int DT, int D, int HPW>
+__device__ __forceinline__ void v_start(const DecodeArgs& a, const VPiece& p,
+                                        VStart<DT, D, HPW>& vs) {
+  using C = VCfg<DT, D>;
+  const int lane = lane_id();
+  const int row = a.qsl ? a.qsl[p.s] : p.s;
+#pragma unroll
+  for (int j = 0; j < HPW; ++j) {
+    const char* qp = reinterpret_cast<const char*>(a.q) +
+                     ((int64_t)row * a.num_q_heads + p.h0 + 4 * j) * D * C::E;
+#pragma unroll
+    for (int i = 0; i < C::NK; ++i) vs.q[j][i] = ld16(qp + 16 * (4 * i + (lane >> 4)));
+  }
+  const int64_t blk = readlane(vs.win0, 0);
+  const int64_t off = blk * a.num_kv_heads * C::TILE;
+  v_issue<DT, D>(vs.first, v_head_base<DT, D>(a.k_cache, a, p.h0) + off,
+                 v_head_base<DT, D>(a.v_cache, a, p.h0) + off, 16 * lane);
+}
+
+// Attention of piece p, whose start loads vs are in flight.  The tiles are walked in chunks
+// of 128, each with its 64-entry block-table windows in registers before its pipelined
+// loop (the first chunk's come with vs), so the loop itself only waits for tile loads.  A
+// step is one tile of one head; the loads of the next step are in flight while a step is
+// computed.
+template <int DT, int D, int HPW>
+__device__ void valu_run(const DecodeArgs& a, VPiece p, VStart<DT, D, HPW>& vs,
+                         VState<DT, D> (&st)[HPW], float* pw) {
   using C = VCfg<DT, D>;
   const int lane = lane_id();
   // every per-piece value is wave-uniform: keep it in scalar registers
-  s = __builtin_amdgcn_readfirstlane(s);
-  h0 = __builtin_amdgcn_readfirstlane(h0);
-  t0 = __builtin_amdgcn_readfirstlane(t0);
-  t1 = __builtin_amdgcn_readfirstlane(t1);
-  ctx = __builtin_amdgcn_readfirstlane(ctx);
-  const int G = a.num_q_heads / a.num_kv_heads;
-  const int row = __builtin_amdgcn_readfirstlane(a.qsl ? a.qsl[s] : s);
+  p.s = __builtin_amdgcn_readfirstlane(p.s);
+  p.h0 = __builtin_amdgcn_readfirstlane(p.h0);
+  p.t0 = __builtin_amdgcn_readfirstlane(p.t0);
+  p.t1 = __builtin_amdgcn_readfirstlane(p.t1);
+  p.ctx = __builtin_amdgcn_readfirstlane(p.ctx);
   const int off = 16 * lane;
-  uint4 qv[HPW][C::NK];
   const char* kc[HPW];
   const char* vc[HPW];
 #pragma unroll
   for (int j = 0; j < HPW; ++j) {
-    const int h = h0 + 4 * j;
-    const char* qp = reinterpret_cast<const char*>(a.q) + ((int64_t)row * a.num_q_heads + h) * D * C::E;
-#pragma unroll
-    for (int i = 0; i < C::NK; ++i) qv[j][i] = ld16(qp + 16 * (4 * i + (lane >> 4)));
-    const int64_t kvh = h / G;
-    kc[j] = reinterpret_cast<const char*>(a.k_cache) + kvh * C::TILE;
-    vc[j] = reinterpret_cast<const char*>(a.v_cache) + kvh * C::TILE;
+    kc[j] = v_head_base<DT, D>(a.k_cache, a, p.h0 + 4 * j);
+    vc[j] = v_head_base<DT, D>(a.v_cache, a, p.h0 + 4 * j);
     st[j].m = -INFINITY;
     st[j].l = 0.f;
 #pragma unroll
     for (int e = 0; e < C::NV; ++e) st[j].acc[e] = 0.f;
   }
   const int64_t blk_stride = (int64_t)a.num_kv_heads * C::TILE;
-  const int32_t* bt_row = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+  const int32_t* bt_row = a.block_tables + (int64_t)p.s * a.max_blocks_per_seq;
 
-  for (int c0 = t0; c0 < t1; c0 += 128) {
-    const int c1 = min(t1, c0 + 128);
-    const int win0 = (c0 + lane < c1) ? bt_row[c0 + lane] : 0;
-    const int win1 = (c0 + 64 + lane < c1) ? bt_row[c0 + 64 + lane] : 0;
+  // one chunk [c0, c1); FIRST: its first step is already in flight in vs.first
+  auto chunk = [&](int c0, int c1, int win0, int win1, auto first) {
     auto issue = [&](VTile<DT, D>& t, int tt, int j) {
       const int idx = tt - c0;
       const int64_t blk = idx < 64 ? readlane(win0, idx) : readlane(win1, idx - 64);
       v_issue<DT, D>(t, kc[j] + blk * blk_stride, vc[j] + blk * blk_stride, off);
     };
     auto step = [&](VTile<DT, D>& t, int tt, int j) {
-      const int valid = ctx - tt * kBlock;
+      const int valid = p.ctx - tt * kBlock;
       if (valid >= kBlock)
-        v_tile<DT, D, false>(st[j], t, qv[j], a.scale_log2, kBlock, pw);
+        v_tile<DT, D, false>(st[j], t, vs.q[j], a.scale_log2, kBlock, pw);
       else
-        v_tile<DT, D, true>(st[j], t, qv[j], a.scale_log2, valid, pw);
+        v_tile<DT, D, true>(st[j], t, vs.q[j], a.scale_log2, valid, pw);
     };
-    // Two-stage software pipeline over steps.  The steady-state loop always issues, so every
-    // path into a step has the same loads outstanding and the wait before it covers only
-    // that step; the last tiles of a chunk are peeled.
-    VTile<DT, D> ta, tb;
-    issue(ta, c0, 0);
+    // Two-stage software pipeline over steps.  The steady-state loop always issues, so
+    // every path into a step has the same loads outstanding and the wait before it covers
+    // only that step; the last tiles of the chunk are peeled.
+    VTile<DT, D>& ta = vs.first;
+    VTile<DT, D> tb;
+    if constexpr (!decltype(first)::value) issue(ta, c0, 0);
     int tt = c0;
     if constexpr (HPW == 1) {
       for (; tt + 2 < c1; tt += 2) {
@@ -231,6 +275,13 @@ __device__ void valu_attend(const DecodeArgs& a, int s, int h0, int t0, int t1, 
         step(cur, tt, j);
       });
     }
+  };
+  chunk(p.t0, min(p.t1, p.t0 + 128), vs.win0, vs.win1, std::true_type{});
+  for (int c0 = p.t0 + 128; c0 < p.t1; c0 += 128) {
+    const int c1 = min(p.t1, c0 + 128);
+    const int win0 = (c0 + lane < c1) ? bt_row[c0 + lane] : 0;
+    const int win1 = (c0 + 64 + lane < c1) ? bt_row[c0 + 64 + lane] : 0;
+    chunk(c0, c1, win0, win1, std::false_type{});
   }
 }
 
@@ -271,13 +322,14 @@ __device__ __forceinline__ void v_store_f32(const VState<DT, D>& st, float inv, 
 }
 
 // A piece of a split segment (heads h0 + 4 j): publish it, or (if it is the segment's last
-// arrival) merge every piece and write the output.  Every lane holds full sums for its
+// arrival) merge every piece and write the output; `between` (the next piece's start loads)
+// runs once, as early as the arrival protocol allows.  Every lane holds full sums for its
 // dimensions after v_finish, so each lane reads and merges its own dimensions of every head.
 // Slot rows: head j of a piece is row (slot HPW + j) of the partial arrays.
-template <int DT, int D, int HPW>
+template <int DT, int D, int HPW, class Between>
 __device__ void v_split_finish(const DecodeArgs& a, const VState<DT, D> (&st)[HPW],
                                const float (&l)[HPW], const SplitSeg& sg, int64_t self,
-                               int32_t* cnt, int seen, int64_t ob0) {
+                               int32_t* cnt, int seen, int64_t ob0, Between&& between) {
   using C = VCfg<DT, D>;
   const int lane = lane_id();
   const int dim0 = lane / C::LPD;  // dimension e * DPL + dim0 of load e
@@ -304,7 +356,7 @@ __device__ void v_split_finish(const DecodeArgs& a, const VState<DT, D> (&st)[HP
         coh_store(a.part_l + row0 + j, l[j]);
       }
     }
-  });
+  }, between);
   if (!last) return;
   float L[HPW], U[HPW][C::NV];
   merge_ordered<HPW, C::NV, (HPW > 2 ? 1 : 2)>(
@@ -358,31 +410,63 @@ __global__ __launch_bounds__(kWG) void valu_decode_kernel(DecodeArgs a) {
     const int groups = (a.num_q_heads + GH - 1) / GH;
     const Part part = make_part((int64_t)base[S] * groups, gridDim.x);
     even_split_drive(part, [&](int64_t o, int64_t lo, int64_t hi) {
-      for (int64_t i = lo; i < hi;) {
-        const int s = find_seq(base, S, i, groups);
-        const int seglen = base[s + 1] - base[s];
-        const int nt = seglen - a.seg_extra;  // real tiles; the rest only balance the split
-        const int64_t sbase = (int64_t)base[s] * groups;
+      // this wave's piece of the segment that unit i of the range belongs to
+      struct Unit {
+        VPiece p;
+        int nt;           // real tiles of the segment
+        int64_t seg0, end;  // the segment's first unit, the piece's end in the range
+        bool run;           // real heads and real tiles
+      };
+      auto at = [&](int64_t i) {
+        Unit u;
+        u.p.s = find_seq(base, S, i, groups);
+        const int seglen = base[u.p.s + 1] - base[u.p.s];
+        u.nt = seglen - a.seg_extra;  // real tiles; the rest only balance the split
+        const int64_t sbase = (int64_t)base[u.p.s] * groups;
         const int grp = (int)((i - sbase) / seglen);
-        const int64_t seg0 = sbase + (int64_t)grp * seglen;
-        const int64_t pe = min(hi, seg0 + seglen);
-        const int h0 = grp * GH + wave;  // this wave's first head (HPW > 1: all exist)
-        const int t0 = (int)(i - seg0), t1 = (int)min(pe - seg0, (int64_t)nt);
-        if (h0 < a.num_q_heads && t0 < nt) {
-          const int ctx = a.context_lens[s];
-          const int row = a.qsl ? a.qsl[s] : s;
-          const int64_t ob0 = ((int64_t)row * a.num_q_heads + h0) * D;
-          const bool whole = t0 == 0 && t1 == nt;
+        u.seg0 = sbase + (int64_t)grp * seglen;
+        u.end = min(hi, u.seg0 + seglen);
+        u.p.h0 = grp * GH + wave;  // this wave's first head (HPW > 1: all exist)
+        u.p.t0 = (int)(i - u.seg0);
+        u.p.t1 = (int)min(u.end - u.seg0, (int64_t)u.nt);
+        u.run = u.p.h0 < a.num_q_heads && u.p.t0 < u.nt;
+        u.p.ctx = u.run ? a.context_lens[u.p.s] : 0;
+        return u;
+      };
+      VStart<DT, D, HPW> vs;
+      Unit cur = at(lo);
+      if (cur.run) {
+        v_window(a, cur.p, vs.win0, vs.win1);
+        v_start<DT, D, HPW>(a, cur.p, vs);
+      }
+      for (;;) {
+        const bool more = cur.end < hi;
+        Unit nxt{};
+        if (more) nxt = at(cur.end);
+        const bool nrun = more && nxt.run;
+        int nw0 = 0, nw1 = 0;  // the next piece's window, read before this piece's tiles
+        if (nrun) v_window(a, nxt.p, nw0, nw1);
+        auto start_next = [&] {
+          if (nrun) {
+            vs.win0 = nw0;
+            vs.win1 = nw1;
+            v_start<DT, D, HPW>(a, nxt.p, vs);
+          }
+        };
+        if (cur.run) {
+          const int row = a.qsl ? a.qsl[cur.p.s] : cur.p.s;
+          const int64_t ob0 = ((int64_t)row * a.num_q_heads + cur.p.h0) * D;
+          const bool whole = cur.p.t0 == 0 && cur.p.t1 == cur.nt;
           SplitSeg sg{};
           int32_t* cnt = nullptr;
           int seen = 0;
           if (!whole) {
-            sg = split_seg(part, seg0, seg0 + nt - 1, wave);
+            sg = split_seg(part, cur.seg0, cur.seg0 + cur.nt - 1, wave);
             cnt = a.counters + kWavesPerWG * sg.k0 + wave;
             seen = counter_peek(cnt);  // consumed after the tiles
           }
           VState<DT, D> st[HPW];
-          valu_attend<DT, D, HPW>(a, s, h0, t0, t1, ctx, st, pw);
+          valu_run<DT, D, HPW>(a, cur.p, vs, st, pw);
           float l[HPW];
 #pragma unroll
           for (int j = 0; j < HPW; ++j) l[j] = v_finish<DT, D>(st[j]);
@@ -390,11 +474,20 @@ __global__ __launch_bounds__(kWG) void valu_decode_kernel(DecodeArgs a) {
 #pragma unroll
             for (int j = 0; j < HPW; ++j)
               v_store<DT, D>(st[j].acc, 1.f / l[j], a.out, ob0 + 4 * j * D, a.out_f32);
+            start_next();
+          } else if constexpr (HPW <= 2) {
+            v_split_finish<DT, D, HPW>(a, st, l, sg, o, cnt, seen, ob0, start_next);
           } else {
-            v_split_finish<DT, D, HPW>(a, st, l, sg, o, cnt, seen, ob0);
+            // with four or more heads the next piece's queries and a merge do not fit in
+            // the registers together: start it once this piece is done
+            v_split_finish<DT, D, HPW>(a, st, l, sg, o, cnt, seen, ob0, [] {});
+            start_next();
           }
+        } else {
+          start_next();
         }
-        i = pe;
+        if (!more) break;
+        cur = nxt;
       }
     });
   } else {
@@ -425,7 +518,11 @@ __global__ __launch_bounds__(kWG) void valu_decode_kernel(DecodeArgs a) {
       const int nt = (ctx + kBlock - 1) / kBlock;
       const int t0 = p * PU, t1 = min(nt, t0 + PU);
       VState<DT, D> st[1];
-      valu_attend<DT, D, 1>(a, s, h, t0, t1, ctx, st, pw);
+      const VPiece pc{s, h, t0, t1, ctx};
+      VStart<DT, D, 1> vs;
+      v_window(a, pc, vs.win0, vs.win1);
+      v_start<DT, D, 1>(a, pc, vs);
+      valu_run<DT, D, 1>(a, pc, vs, st, pw);
       const float l = v_finish<DT, D>(st[0]);
       const float inv = 1.f / l;
       const int64_t e = ((int64_t)s * a.num_q_heads + h) * P + p;

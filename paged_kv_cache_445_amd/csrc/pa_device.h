@@ -349,10 +349,19 @@ __device__ __forceinline__ int counter_peek(int32_t* c) {
 // is the number of other pieces, `seen` an earlier counter_peek of c, and `publish` writes
 // this piece's partial with device-scope stores; it is skipped when every other piece has
 // already arrived (that piece merges from its registers and nobody reads its slot).
-template <class Pub>
-__device__ __forceinline__ bool split_arrive(int32_t* c, int others, int seen, Pub&& publish) {
-  if (__builtin_amdgcn_readfirstlane(seen) == others) return true;
-  if (__builtin_amdgcn_readfirstlane(counter_peek(c)) == others) return true;  // a fresh look
+// `between` runs exactly once, before any wait for this protocol's own memory operations
+// but after the stores of the partial are issued, so that loads it issues (the wave's next
+// piece) travel together with them.
+template <class Pub, class Between>
+__device__ __forceinline__ bool split_arrive(int32_t* c, int others, int seen, Pub&& publish,
+                                             Between&& between) {
+  if (__builtin_amdgcn_readfirstlane(seen) == others) {
+    between();
+    return true;
+  }
+  const int fresh = counter_peek(c);  // a fresh look
+  between();
+  if (__builtin_amdgcn_readfirstlane(fresh) == others) return true;
   publish();
   // every store of this wave, the partial included, has reached the point of coherence
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
