@@ -143,7 +143,7 @@ __global__ __launch_bounds__(kWG) void mfma_decode_kernel(DecodeArgs a) {
     // units: (sequence, group of kWavesPerWG KV heads, unit); wave i runs KV head i of each
     // group
     const int groups = (a.num_kv_heads + kWavesPerWG - 1) / kWavesPerWG;
-    const Part part = make_part((int64_t)base[S] * groups, gridDim.x);
+    const Part part = make_part((int64_t)base[S] * groups, gridDim.x, a.odd_skew);
     even_split_drive(part, [&](int64_t o, int64_t lo, int64_t hi) {
       for (int64_t i = lo; i < hi;) {
         const int s = find_seq(base, S, i, groups);

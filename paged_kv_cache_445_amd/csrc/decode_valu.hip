@@ -408,7 +408,7 @@ __global__ __launch_bounds__(kWG) void valu_decode_kernel(DecodeArgs a) {
     // units: (sequence, group of 4 HPW heads, tile); wave i runs heads i + 4 j of each group
     constexpr int GH = kWavesPerWG * HPW;
     const int groups = (a.num_q_heads + GH - 1) / GH;
-    const Part part = make_part((int64_t)base[S] * groups, gridDim.x);
+    const Part part = make_part((int64_t)base[S] * groups, gridDim.x, a.odd_skew);
     even_split_drive(part, [&](int64_t o, int64_t lo, int64_t hi) {
       // this wave's piece of the segment that unit i of the range belongs to
       struct Unit {

@@ -75,6 +75,20 @@ int wg_per_cu_override() {
   return v;
 }
 
+// Per mille of the even split's work moved from the workgroups on odd XCDs to those on even
+// XCDs (see make_part).  On gfx950 the odd XCDs finish the decode's random 4 KiB tile reads
+// about 7% later than the even ones, whichever data they are given (measured per XCD with
+// the kernel's own read pattern); a sweep of this shift put the shortest decode at 5 to
+// 6.5%.  Optional override for tuning.
+constexpr int kOddSkew = 55;
+int odd_skew() {
+  static const int v = [] {
+    const char* s = getenv("PA_DECODE_ODD_SKEW");
+    return s ? atoi(s) : -1;
+  }();
+  return v >= 0 ? v : kOddSkew;
+}
+
 bool use_mfma(const pa_geom* g) {
   return g->kv_dtype != PA_F32 && g->num_q_heads / g->num_kv_heads >= 2;
 }
@@ -264,6 +278,7 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   const int path = use_mfma(g) ? 1 : 0;
   a.seg_extra = seg_extra_override() >= 0 ? seg_extra_override() : kSegExtra[path];
   a.heads_per_wave = path == 0 ? heads_per_wave(g) : 1;
+  a.odd_skew = odd_skew();
 
   hipError_t e = use_mfma(g) ? pa::launch_mfma_decode(g->kv_dtype, pa::MODE_EVEN, a, grid, st)
                              : pa::launch_valu_decode(g->kv_dtype, pa::MODE_EVEN, a, grid, st);

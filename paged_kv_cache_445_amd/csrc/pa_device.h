@@ -243,29 +243,48 @@ __device__ __forceinline__ int find_seq(const int32_t* base, int S, int64_t i, i
   return lo;
 }
 
-// The flattened (sequence, head group, unit) list [0, total) is split evenly over the NK
-// workgroups that get work (NK = min(workgroups, total), so every share is non-empty):
-// workgroup ("owner") o owns [part_lo(o), part_lo(o + 1)), and wave i of it takes head i of
-// every group of that range.
+// The flattened (sequence, head group, unit) list [0, total) is split over the NK workgroups
+// that get work (NK = min(workgroups, total)): workgroup ("owner") o owns
+// [part_lo(o), part_lo(o + 1)), and wave i of it takes head i of every group of that range.
+// Shares are proportional to a weight per owner: we for even o, wo for odd o.  Workgroups
+// are dispatched to the XCDs round robin (workgroup o runs on XCD o mod 8), and on gfx950
+// the odd XCDs stream this access pattern measurably slower than the even ones, so the odd
+// owners get slightly less work; the weights stay equal unless every share keeps at least
+// four units, which keeps every share non-empty.
 struct Part {
-  int64_t total;  // units
-  int64_t NK;     // owners
+  int64_t total;   // units
+  int64_t NK;      // owners
+  int64_t we, wo;  // weights of even and odd owners
 };
 
-__device__ __forceinline__ Part make_part(int64_t total, int64_t workgroups) {
+// odd_skew: per mille taken from odd owners' weights and given to even owners'
+__device__ __forceinline__ Part make_part(int64_t total, int64_t workgroups, int odd_skew) {
   Part p;
   p.total = total;
   p.NK = min(workgroups, total);
+  const bool skew = odd_skew > 0 && odd_skew < 500 && total >= 4 * p.NK;
+  p.we = skew ? 1000 + odd_skew : 1000;
+  p.wo = skew ? 1000 - odd_skew : 1000;
   return p;
+}
+
+// summed weight of owners [0, o)
+__device__ __forceinline__ int64_t part_weight(const Part& p, int64_t o) {
+  return ((o + 1) >> 1) * p.we + (o >> 1) * p.wo;
 }
 
 // first unit of owner o (o in [0, NK]; part_lo(NK) == total)
 __device__ __forceinline__ int64_t part_lo(const Part& p, int64_t o) {
-  return p.NK ? (p.total * o) / p.NK : 0;
+  return p.NK ? p.total * part_weight(p, o) / part_weight(p, p.NK) : 0;
 }
-// owner of unit u (u < total): the largest o with part_lo(o) <= u
+// owner of unit u (u < total): the largest o with part_lo(o) <= u, i.e. with
+// part_weight(o) <= X below
 __device__ __forceinline__ int64_t part_owner(const Part& p, int64_t u) {
-  return ((u + 1) * p.NK - 1) / p.total;
+  const int64_t X = ((u + 1) * part_weight(p, p.NK) - 1) / p.total;
+  const int64_t pair = p.we + p.wo;
+  const int64_t m = X / pair;
+  const int64_t o = 2 * m + (X - m * pair >= p.we ? 1 : 0);
+  return min(o, p.NK - 1);
 }
 
 // Split-segment bookkeeping.  A segment (one sequence and head group) whose real units

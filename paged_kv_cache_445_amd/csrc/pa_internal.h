@@ -47,6 +47,7 @@ struct DecodeArgs {
   int32_t max_partitions;   // MODE_PARTITION
   int32_t seg_extra;        // MODE_EVEN: balancing units per segment (see PlanIn)
   int32_t heads_per_wave;   // MODE_EVEN, vector kernel: query heads per wave (1, 2, 4, 8)
+  int32_t odd_skew;         // MODE_EVEN: per mille of work moved from odd to even workgroups
 };
 
 struct ReshapeArgs {
