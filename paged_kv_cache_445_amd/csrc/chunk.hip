@@ -35,34 +35,11 @@ struct ChunkPlanIn {
 };
 
 // work items per sequence: ceil(n / rows_per_item) for multi-row sequences, else 0
-__device__ inline void build_chunk_plan(int32_t* base, int32_t* tmp, const ChunkPlanIn& p) {
-  const int t = threadIdx.x;
-  const int S = p.num_seqs;
-  const int per = (S + kWG - 1) / kWG;
-  const int s0 = t * per, s1 = min(S, s0 + per);
-  int32_t sum = 0;
-  for (int s = s0; s < s1; ++s) {
+__device__ inline void build_chunk_plan(int32_t* base, const ChunkPlanIn& p) {
+  wave_plan(base, p.num_seqs, [&](int s) {
     const int32_t n = p.qsl[s + 1] - p.qsl[s];
-    const int32_t u = n > 1 ? (n + p.rows_per_item - 1) / p.rows_per_item : 0;
-    base[s] = u;
-    sum += u;
-  }
-  tmp[t] = sum;
-  __syncthreads();
-  for (int off = 1; off < kWG; off <<= 1) {
-    const int32_t v = t >= off ? tmp[t - off] : 0;
-    __syncthreads();
-    tmp[t] += v;
-    __syncthreads();
-  }
-  int32_t run = tmp[t] - sum;
-  for (int s = s0; s < s1; ++s) {
-    const int32_t u = base[s];
-    base[s] = run;
-    run += u;
-  }
-  if (t == kWG - 1) base[S] = tmp[kWG - 1];
-  __syncthreads();
+    return n > 1 ? (n + p.rows_per_item - 1) / p.rows_per_item : 0;
+  });
 }
 
 // One work item: rows [j0, j0 + kItemCols / G) of multi-row sequence s for KV head g.  The
@@ -227,11 +204,10 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(2))) void c
   extern __shared__ __align__(16) char lds_raw[];
   char* lds_units = lds_raw;  // two unit buffers
   int32_t* base = reinterpret_cast<int32_t*>(lds_raw + 2 * ChunkTile<D>::UNIT);
-  int32_t* tmp = base + a.num_seqs + 1;
   const int G = a.num_q_heads / a.num_kv_heads;
   const int S = a.num_seqs;
   ChunkPlanIn pin{a.qsl, S, kItemCols / G};
-  build_chunk_plan(base, tmp, pin);
+  build_chunk_plan(base, pin);
   const int64_t per_head = base[S];
   const int64_t total = per_head * a.num_kv_heads;
   for (int64_t i = xcd_local_block(blockIdx.x, gridDim.x); i < total; i += gridDim.x) {
@@ -253,7 +229,7 @@ hipError_t launch_chunk(int dt, const DecodeArgs& a, int num_q_rows, hipStream_t
   const int64_t wgs = (items + kXcds - 1) / kXcds * kXcds;
   const int grid = (int)(wgs < (1 << 20) ? wgs : (1 << 20) / kXcds * kXcds);
   const size_t lds = (size_t)2 * (a.head_dim == 64 ? ChunkTile<64>::UNIT : ChunkTile<128>::UNIT) +
-                     (size_t)(a.num_seqs + 1 + kWG) * sizeof(int32_t);
+                     (size_t)(a.num_seqs + 1) * sizeof(int32_t);
   if (grid <= 0) return hipSuccess;
   if (dt == DT_F16) {
     if (a.head_dim == 64)

@@ -127,7 +127,6 @@ template <int DT, int D, int MODE>
 __global__ __launch_bounds__(kWG) void mfma_decode_kernel(DecodeArgs a) {
   extern __shared__ int32_t lds[];
   int32_t* base = lds;
-  int32_t* tmp = lds + a.num_seqs + 1;
   const int wave = threadIdx.x / kWave;
   const int lane = lane_id();
   const int segs = a.num_kv_heads;
@@ -138,7 +137,7 @@ __global__ __launch_bounds__(kWG) void mfma_decode_kernel(DecodeArgs a) {
 
   if constexpr (MODE == MODE_EVEN) {
     PlanIn pin{a.context_lens, a.qsl, S, kMfmaUnit, a.seg_extra};
-    build_plan(base, tmp, pin);
+    build_plan(base, pin);
     zero_empty_rows<DT>(pin, a.out, a.num_q_heads, D, w, W, a.out_f32);
     // units: (sequence, group of kWavesPerWG KV heads, unit); wave i runs KV head i of each
     // group
@@ -182,7 +181,7 @@ __global__ __launch_bounds__(kWG) void mfma_decode_kernel(DecodeArgs a) {
     const int PU = a.partition_units;  // 32-token units per partition
     const int P = a.max_partitions;
     PlanIn pin{a.context_lens, nullptr, S, PU * kMfmaUnit, 0};
-    build_plan(base, tmp, pin);
+    build_plan(base, pin);
     const int64_t nent = (int64_t)S * a.num_q_heads * P;
     for (int64_t e = (int64_t)blockIdx.x * kWG + threadIdx.x; e < nent; e += (int64_t)gridDim.x * kWG) {
       const int p = (int)(e % P);
@@ -215,7 +214,7 @@ __global__ __launch_bounds__(kWG) void mfma_decode_kernel(DecodeArgs a) {
 
 template <int DT, int MODE>
 static hipError_t launch_d(const DecodeArgs& a, int grid, hipStream_t st) {
-  const size_t lds = (size_t)(a.num_seqs + 1 + kWG) * sizeof(int32_t);
+  const size_t lds = (size_t)(a.num_seqs + 1) * sizeof(int32_t);
   if (a.head_dim == 64)
     hipLaunchKernelGGL((mfma_decode_kernel<DT, 64, MODE>), dim3(grid), dim3(kWG), lds, st, a);
   else

@@ -390,20 +390,19 @@ __device__ void v_split_finish(const DecodeArgs& a, const VState<DT, D> (&st)[HP
 template <int DT, int D, int MODE, int HPW>
 __global__ __launch_bounds__(kWG) void valu_decode_kernel(DecodeArgs a) {
   // LDS: one 16-float weight slot per wave (first, for 16-byte alignment), then the plan
-  // (S + 1 ints) and the scan buffer (kWG ints)
+  // (S + 1 ints)
   extern __shared__ __align__(16) int32_t lds[];
   const int S = a.num_seqs;
   const int lane = lane_id();
   const int wave = threadIdx.x / kWave;
   float* pw = reinterpret_cast<float*>(lds) + 16 * wave;
   int32_t* base = lds + 16 * kWavesPerWG;
-  int32_t* tmp = base + S + 1;
   const int64_t W = (int64_t)gridDim.x * kWavesPerWG;
   const int64_t w = (int64_t)blockIdx.x * kWavesPerWG + wave;
 
   if constexpr (MODE == MODE_EVEN) {
     PlanIn pin{a.context_lens, a.qsl, S, kValuUnit, a.seg_extra};
-    build_plan(base, tmp, pin);
+    build_plan(base, pin);
     zero_empty_rows<DT>(pin, a.out, a.num_q_heads, D, w, W, a.out_f32);
     // units: (sequence, group of 4 HPW heads, tile); wave i runs heads i + 4 j of each group
     constexpr int GH = kWavesPerWG * HPW;
@@ -495,7 +494,7 @@ __global__ __launch_bounds__(kWG) void valu_decode_kernel(DecodeArgs a) {
     const int PU = a.partition_units;  // tiles per partition
     const int P = a.max_partitions;
     PlanIn pin{a.context_lens, nullptr, S, PU * kBlock, 0};
-    build_plan(base, tmp, pin);
+    build_plan(base, pin);
     // partitions past the context: max_logits = -inf, exp_sums = 0
     const int64_t nent = (int64_t)S * a.num_q_heads * P;
     for (int64_t e = (int64_t)blockIdx.x * kWG + threadIdx.x; e < nent; e += (int64_t)gridDim.x * kWG) {
@@ -536,7 +535,7 @@ __global__ __launch_bounds__(kWG) void valu_decode_kernel(DecodeArgs a) {
 }
 
 static size_t valu_lds_bytes(int num_seqs) {
-  return (size_t)(num_seqs + 1 + kWG) * sizeof(int32_t) + kWavesPerWG * 16 * sizeof(float);
+  return (size_t)(num_seqs + 1) * sizeof(int32_t) + kWavesPerWG * 16 * sizeof(float);
 }
 
 template <int DT, int D, int MODE, int HPW>

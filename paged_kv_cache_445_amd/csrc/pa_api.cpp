@@ -93,7 +93,7 @@ bool use_mfma(const pa_geom* g) {
   return g->kv_dtype != PA_F32 && g->num_q_heads / g->num_kv_heads >= 2;
 }
 
-// LDS of the split kernels: the per-sequence plan (num_seqs + 1 ints) and a scan buffer.
+// LDS of the split kernels: the per-sequence plan (num_seqs + 1 ints).
 // Occupancy is evaluated for num_seqs rounded up to a power of two, so a handful of cached
 // values covers every batch size.
 int seq_bucket(int num_seqs) {
@@ -102,7 +102,7 @@ int seq_bucket(int num_seqs) {
   return b;  // (1 << b) >= num_seqs + 1; b <= 14 for kMaxSeqs = 8192
 }
 
-int bucket_lds_bytes(int bucket) { return ((1 << bucket) + pa::kWG) * (int)sizeof(int32_t); }
+int bucket_lds_bytes(int bucket) { return (1 << bucket) * (int)sizeof(int32_t); }
 
 // resident workgroups per CU for pa_decode's even split (vector path, matrix-core path)
 constexpr int kEvenWgPerCu[2] = {1, 2};

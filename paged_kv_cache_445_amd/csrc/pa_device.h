@@ -199,35 +199,42 @@ __device__ void zero_empty_rows(const PlanIn& p, void* out, int Hq, int D, int64
   }
 }
 
-// base[0..S] in LDS; `tmp` is kWG ints of LDS.  Must be called by all threads of the WG.
-__device__ inline void build_plan(int32_t* base, int32_t* tmp, const PlanIn& p) {
-  const int t = threadIdx.x;
-  const int S = p.num_seqs;
-  const int per = (S + kWG - 1) / kWG;
-  const int s0 = t * per, s1 = min(S, s0 + per);
-  int32_t sum = 0;
-  for (int s = s0; s < s1; ++s) {
-    const int32_t u = seq_units(p, s);
-    base[s] = u;  // units for now, prefix below
-    sum += u;
+// Exclusive prefix sums of units(s) over s < S into base[0..S] (LDS): the first wave of the
+// workgroup reads 256 sequences at a time (four independent loads per lane) and scans them
+// with lane shuffles; one barrier publishes the result.  Must be called by every thread.
+template <class Units>
+__device__ inline void wave_plan(int32_t* base, int S, Units&& units) {
+  if (threadIdx.x < kWave) {
+    const int lane = threadIdx.x;
+    int32_t run = 0;
+    for (int c = 0; c < S; c += 4 * kWave) {
+      int32_t u[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int s = c + k * kWave + lane;
+        u[k] = s < S ? units(s) : 0;
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        int32_t incl = u[k];
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+          const int32_t v = __shfl_up(incl, d, kWave);
+          if (lane >= d) incl += v;
+        }
+        const int s = c + k * kWave + lane;
+        if (s < S) base[s] = run + incl - u[k];
+        run += __shfl(incl, kWave - 1, kWave);
+      }
+    }
+    if (lane == 0) base[S] = run;
   }
-  tmp[t] = sum;
   __syncthreads();
-  // inclusive Hillis-Steele scan of the kWG partial sums
-  for (int off = 1; off < kWG; off <<= 1) {
-    const int32_t v = t >= off ? tmp[t - off] : 0;
-    __syncthreads();
-    tmp[t] += v;
-    __syncthreads();
-  }
-  int32_t run = tmp[t] - sum;  // exclusive prefix of this thread's range
-  for (int s = s0; s < s1; ++s) {
-    const int32_t u = base[s];
-    base[s] = run;
-    run += u;
-  }
-  if (t == kWG - 1) base[S] = tmp[kWG - 1];
-  __syncthreads();
+}
+
+// base[0..S] in LDS: exclusive prefix sums of seq_units.  Must be called by all threads.
+__device__ inline void build_plan(int32_t* base, const PlanIn& p) {
+  wave_plan(base, p.num_seqs, [&](int s) { return seq_units(p, s); });
 }
 
 // largest s in [0, S) with base[s] * segs <= i  (requires i < base[S] * segs)
