@@ -288,7 +288,7 @@ def main():
         "pa_decode_us": round(dec_avg_ms * 1e3, 3),
         "roofline": {
             "bound": bound,
-            "kernel": "pa_decode (decode kernel + partial merge"
+            "kernel": "pa_decode (decode kernel with in-kernel split merge"
                       + (" + chunk kernel)" if b.query_start_loc is not None else ")"),
             "achieved": round(achieved, 2),
             "peak": peak,
