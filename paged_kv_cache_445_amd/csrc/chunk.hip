@@ -44,8 +44,9 @@ __device__ inline void build_chunk_plan(int32_t* base, const ChunkPlanIn& p) {
 
 // One work item: rows [j0, j0 + kItemCols / G) of multi-row sequence s for KV head g.  The
 // workgroup streams the item's keys in 32-token units: every unit (K and V of two blocks) is
-// loaded once by the whole workgroup into one of two LDS buffers, and each wave then runs
-// its 32 query columns (two 16-column MFMA blocks, per-column causal limits) over it.
+// loaded once by the whole workgroup, two units ahead, into one of two LDS buffers, and each
+// wave then runs its 32 query columns (two 16-column MFMA blocks, per-column causal limits)
+// over it.
 template <int DT, int D>
 __device__ void chunk_item(const DecodeArgs& a, int s, int g, int cb, char* lds_units) {
   using C = MfmaCfg<DT, D>;
@@ -140,40 +141,68 @@ __device__ void chunk_item(const DecodeArgs& a, int s, int g, int cb, char* lds_
       *reinterpret_cast<uint4*>(lds_units + buf * CT::UNIT + ld_tile[k] * CT::TILE + ld_off[k]) = regs[k];
   };
 
-  uint4 regs[CT::LOADS];
-  load_unit(regs, 0);
-  store_unit(regs, 0);
-  __syncthreads();
-  for (int u = 0; u < nu; ++u) {
-    const bool more = u + 1 < nu;
-    if (more) load_unit(regs, u + 1);
+  // Unit pipeline: the loads of unit u + 2 go out at the start of step u, unit u is computed
+  // from LDS buffer u % 2, and unit u + 1 (loaded since the start of step u - 1, so two
+  // compute phases ago) is stored into the other buffer at the end of the step.  Even units
+  // are staged in ra, odd ones in rb.  Loads and stores run on every step (past the last unit
+  // they repeat it and the result is never read), and the barrier between steps does not wait
+  // for outstanding loads, so the compiler's wait before each store covers only that unit.
+  auto barrier = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+  const int ulast = nu - 1;
+  auto compute = [&](int u) {
     const int t0 = u * kMfmaUnit;
-    if (t0 < nkeys_w) {  // uniform: this wave's columns see keys of this unit
+    if (u < nu && t0 < nkeys_w) {  // uniform: this wave's columns see keys of this unit
       const char* ub = lds_units + (u & 1) * CT::UNIT;
+      // scores of both column blocks from K, then P . V from V: K and V are never live together
       MfmaK<DT, D> kb;
-      MfmaV<DT, D> vb;
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int kk = 0; kk < C::NKK; ++kk)
-          kb[b][kk] = *reinterpret_cast<const uint4*>(ub + o.kt[b] * CT::TILE + o.k[b][kk]);
+          kb[b][kk] = *reinterpret_cast<const uint4*>(ub + o.kt[b] * CT::TILE + o.koff(b, kk));
+      bool masked[NCB];
+      MfmaP<DT> pp[NCB];
+#pragma unroll
+      for (int c = 0; c < NCB; ++c) {
+        masked[c] = !(t0 + kMfmaUnit - 1 <= first[c] && full[c]);
+        if (!live[c]) continue;
+        if (!masked[c])
+          pp[c] = mfma_scores<DT, D, false, true>(st[c], kb, qb[c], a.scale_log2, kMfmaUnit - 1);
+        else
+          pp[c] = mfma_scores<DT, D, true, true>(st[c], kb, qb[c], a.scale_log2, pos[c] - t0);
+      }
+      MfmaV<DT, D> vb;
 #pragma unroll
       for (int j = 0; j < C::NJ; ++j)
-        vb[j] = *reinterpret_cast<const uint4*>(ub + (2 + o.vt) * CT::TILE + o.v[j]);
+        vb[j] = *reinterpret_cast<const uint4*>(ub + (2 + o.vt) * CT::TILE + o.voff(j));
+      // V is masked in place for the first block that needs it; the masked tokens are the
+      // same for every column, so later blocks may use it either way
 #pragma unroll
       for (int c = 0; c < NCB; ++c) {
         if (!live[c]) continue;
-        if (t0 + kMfmaUnit - 1 <= first[c] && full[c])
-          mfma_unit<DT, D, false, true>(st[c], kb, vb, qb[c], a.scale_log2, kMfmaUnit - 1,
-                                        kMfmaUnit);
+        if (!masked[c])
+          mfma_pv<DT, D, false>(st[c], vb, pp[c], kMfmaUnit);
         else
-          mfma_unit<DT, D, true, true>(st[c], kb, vb, qb[c], a.scale_log2, pos[c] - t0,
-                                       nkeys_g - t0);
+          mfma_pv<DT, D, true>(st[c], vb, pp[c], nkeys_g - t0);
       }
     }
-    if (more) store_unit(regs, (u + 1) & 1);
-    __syncthreads();
+  };
+  uint4 ra[CT::LOADS], rb[CT::LOADS];
+  load_unit(ra, 0);
+  load_unit(rb, min(1, ulast));
+  store_unit(ra, 0);
+  barrier();
+  for (int u = 0; u < nu; u += 2) {
+    load_unit(ra, min(u + 2, ulast));
+    compute(u);
+    store_unit(rb, 1);
+    barrier();
+    load_unit(rb, min(u + 3, ulast));
+    compute(u + 1);
+    store_unit(ra, 0);
+    barrier();
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the repeated loads past the last unit
 
   // emit: lane (r, n) holds dimensions 16 j + 4 r + i of column 16 c + n, which is
   // (row j0 + col / G, head col % G)
@@ -194,28 +223,81 @@ __device__ void chunk_item(const DecodeArgs& a, int s, int g, int cb, char* lds_
   }
 }
 
-// Work items, one per workgroup: (KV head, sequence, column block) with the KV head slowest,
-// column blocks last-to-first (the longest causal ranges first).  With XCD-local numbering
-// each XCD works through a contiguous range of items, i.e. mostly one KV head across all
-// sequences, and the items of one (sequence, KV head) that re-read its K/V run together
-// on one XCD.
+// Most multi-row sequences whose items are ordered longest first (see chunk_kernel).
+constexpr int kMaxOrdered = 256;
+
+// Work items, one per workgroup.  Items differ in length by up to the longest context over
+// the shortest, and workgroups start in index order as earlier ones finish, so the items are
+// numbered longest first: multi-row sequences by decreasing number of prior keys, within a
+// sequence column blocks last to first (the longest causal ranges first), and the KV heads
+// of one (sequence, column block) consecutively.  With more than kMaxOrdered multi-row
+// sequences the items keep the sequence order instead, KV head slowest, numbered XCD-locally
+// so that each XCD works through mostly one KV head.
 template <int DT, int D>
 __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(2))) void chunk_kernel(DecodeArgs a) {
   extern __shared__ __align__(16) char lds_raw[];
   char* lds_units = lds_raw;  // two unit buffers
   int32_t* base = reinterpret_cast<int32_t*>(lds_raw + 2 * ChunkTile<D>::UNIT);
+  int32_t* order = base + a.num_seqs + 1;  // [kMaxOrdered] multi-row sequences, longest first
+  int32_t* rbase = order + kMaxOrdered;    // [kMaxOrdered + 1] item prefix in that order
+  int32_t* pkeys = rbase + kMaxOrdered + 1;  // [kMaxOrdered] prior keys of order[] entries
+  int32_t* count = pkeys + kMaxOrdered;
   const int G = a.num_q_heads / a.num_kv_heads;
   const int S = a.num_seqs;
+  const int Hkv = a.num_kv_heads;
   ChunkPlanIn pin{a.qsl, S, kItemCols / G};
   build_chunk_plan(base, pin);
   const int64_t per_head = base[S];
-  const int64_t total = per_head * a.num_kv_heads;
-  for (int64_t i = xcd_local_block(blockIdx.x, gridDim.x); i < total; i += gridDim.x) {
-    const int g = (int)(i / per_head);
-    const int64_t k = i - (int64_t)g * per_head;
-    const int s = find_seq(base, S, k, 1);
-    const int nb = base[s + 1] - base[s];
-    const int cb = nb - 1 - (int)(k - base[s]);
+  const int64_t total = per_head * Hkv;
+
+  // collect the multi-row sequences (any order), then rank them by prior keys (ties: index)
+  if (threadIdx.x == 0) *count = 0;
+  __syncthreads();
+  for (int t = threadIdx.x; t < S; t += kWG) {
+    if (base[t + 1] > base[t]) {
+      const int slot = atomicAdd(count, 1);
+      if (slot < kMaxOrdered) {
+        order[slot] = t;
+        pkeys[slot] = a.context_lens[t] - (a.qsl[t + 1] - a.qsl[t]);
+      }
+    }
+  }
+  __syncthreads();
+  const int M = *count;
+  const bool ordered = M <= kMaxOrdered;
+  if (ordered) {
+    int mine = -1, rank = 0;
+    if (threadIdx.x < M) {
+      mine = order[threadIdx.x];
+      const int pm = pkeys[threadIdx.x];
+      for (int k = 0; k < M; ++k) {
+        const int o = order[k], po = pkeys[k];
+        rank += (po > pm || (po == pm && o < mine)) ? 1 : 0;
+      }
+    }
+    __syncthreads();
+    if (mine >= 0) order[rank] = mine;
+    __syncthreads();
+    wave_plan(rbase, M, [&](int r) { return (base[order[r] + 1] - base[order[r]]) * Hkv; });
+  }
+
+  for (int64_t i = ordered ? (int64_t)blockIdx.x : xcd_local_block(blockIdx.x, gridDim.x);
+       i < total; i += gridDim.x) {
+    int s, g, cb;
+    if (ordered) {
+      const int rk = find_seq(rbase, M, i, 1);
+      s = order[rk];
+      const int k = (int)(i - rbase[rk]);
+      const int nb = base[s + 1] - base[s];
+      cb = nb - 1 - k / Hkv;
+      g = k % Hkv;
+    } else {
+      g = (int)(i / per_head);
+      const int64_t k = i - (int64_t)g * per_head;
+      s = find_seq(base, S, k, 1);
+      const int nb = base[s + 1] - base[s];
+      cb = nb - 1 - (int)(k - base[s]);
+    }
     chunk_item<DT, D>(a, s, g, cb, lds_units);
     __syncthreads();  // the unit buffers are reused by the next item
   }
@@ -229,7 +311,7 @@ hipError_t launch_chunk(int dt, const DecodeArgs& a, int num_q_rows, hipStream_t
   const int64_t wgs = (items + kXcds - 1) / kXcds * kXcds;
   const int grid = (int)(wgs < (1 << 20) ? wgs : (1 << 20) / kXcds * kXcds);
   const size_t lds = (size_t)2 * (a.head_dim == 64 ? ChunkTile<64>::UNIT : ChunkTile<128>::UNIT) +
-                     (size_t)(a.num_seqs + 1) * sizeof(int32_t);
+                     (size_t)(a.num_seqs + 1 + 3 * kMaxOrdered + 2) * sizeof(int32_t);
   if (grid <= 0) return hipSuccess;
   if (dt == DT_F16) {
     if (a.head_dim == 64)

@@ -63,12 +63,17 @@ using MfmaV = uint4[MfmaCfg<DT, D>::NJ];
 template <int DT, int D>
 using MfmaQ = op8_t<DT>[MfmaCfg<DT, D>::NKK];
 
+// Per-lane byte offsets of the unit operands.  Inside a tile the offsets of the other
+// 16-byte pieces differ from these by compile-time steps (kk: 1 KiB, j: 256 elements), so
+// they become immediate offsets of the loads instead of registers.
 template <int DT, int D>
 struct MfmaLaneOffsets {
-  int k[2][MfmaCfg<DT, D>::NKK];  // byte offset inside the K tile, per S-block b and kk
-  int kt[2];                      // which tile of the unit (0 / 1) S-block b's token is in
-  int v[MfmaCfg<DT, D>::NJ];      // byte offset inside the V tile
-  int vt;                         // which tile of the unit this lane's V tokens are in
+  int k[2];   // offset inside the K tile of S-block b's piece kk = 0
+  int kt[2];  // which tile of the unit (0 / 1) S-block b's token is in
+  int v;      // offset inside the V tile of piece j = 0
+  int vt;     // which tile of the unit this lane's V tokens are in
+  __device__ __forceinline__ int koff(int b, int kk) const { return k[b] + 1024 * kk; }
+  __device__ __forceinline__ int voff(int j) const { return v + 256 * MfmaCfg<DT, D>::E * j; }
 };
 
 template <int DT, int D>
@@ -80,21 +85,30 @@ __device__ __forceinline__ void mfma_load(MfmaK<DT, D>& kb, MfmaV<DT, D>& vb, co
   for (int b = 0; b < 2; ++b) {
     const char* kt = o.kt[b] ? k1 : k0;
 #pragma unroll
-    for (int kk = 0; kk < C::NKK; ++kk) kb[b][kk] = ld16(kt + o.k[b][kk]);
+    for (int kk = 0; kk < C::NKK; ++kk) kb[b][kk] = ld16(kt + o.koff(b, kk));
   }
   const char* vt = o.vt ? v1 : v0;
 #pragma unroll
-  for (int j = 0; j < C::NJ; ++j) vb[j] = ld16(vt + o.v[j]);
+  for (int j = 0; j < C::NJ; ++j) vb[j] = ld16(vt + o.voff(j));
 }
 
-// One unit.  MASK: tokens 8r + k > lim (lim: last visible unit token of this lane's query
-// column; may differ per column) get no weight, and V elements of tokens >= vvalid (uniform:
-// tokens of the unit that hold written data) are zeroed so poison never reaches the sums.
-// SAFE: a column may have seen no key yet (its running max is still -inf).
+// The two halves of one unit for one 16-column block.  mfma_scores computes S^T = K . Q^T,
+// masks tokens 8r + k > lim (MASK; lim: last visible unit token of this lane's query column,
+// may differ per column), updates the running max and sum and returns the block's weights P
+// (as hi + lo 16-bit parts) and the rescale factor of its outputs.  mfma_pv zeroes the V
+// elements of tokens >= vvalid (MASK; uniform: tokens of the unit that hold written data, so
+// poison never reaches the sums) and adds V^T . P^T to the rescaled outputs.  SAFE: a column
+// may have seen no key yet (its running max is still -inf).
+template <int DT>
+struct MfmaP {
+  op8_t<DT> hi, lo;
+  float alpha;
+};
+
 template <int DT, int D, bool MASK, bool SAFE>
-__device__ __forceinline__ void mfma_unit(MfmaState<DT, D>& st, const MfmaK<DT, D>& kb,
-                                          MfmaV<DT, D>& vb, const MfmaQ<DT, D>& qb,
-                                          float scale_log2, int lim, int vvalid) {
+__device__ __forceinline__ MfmaP<DT> mfma_scores(MfmaState<DT, D>& st, const MfmaK<DT, D>& kb,
+                                                 const MfmaQ<DT, D>& qb, float scale_log2,
+                                                 int lim) {
   using C = MfmaCfg<DT, D>;
   using T = op8_t<DT>;
   const int lane = lane_id();
@@ -105,17 +119,59 @@ __device__ __forceinline__ void mfma_unit(MfmaState<DT, D>& st, const MfmaK<DT, 
     s0 = mfma<DT>(__builtin_bit_cast(T, kb[0][kk]), qb[kk], s0);
     s1 = mfma<DT>(__builtin_bit_cast(T, kb[1][kk]), qb[kk], s1);
   }
+  // raw scores q . k; the scale enters through the exponent's fma, and the largest scaled
+  // score is the scale times the largest raw score (the smallest one for a negative scale)
+  const bool pos = scale_log2 >= 0.f;
   float s[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    s[i] = s0[i] * scale_log2;
-    s[4 + i] = s1[i] * scale_log2;
+    s[i] = s0[i];
+    s[4 + i] = s1[i];
   }
   if (MASK) {
+    const float none = pos ? -INFINITY : INFINITY;  // scales to -inf: weight 0
 #pragma unroll
     for (int k = 0; k < 8; ++k)
-      if (8 * r + k > lim) s[k] = -INFINITY;
+      if (8 * r + k > lim) s[k] = none;
+  }
+  float ext = s[0];
+#pragma unroll
+  for (int k = 1; k < 8; ++k) ext = pos ? fmaxf(ext, s[k]) : fminf(ext, s[k]);
+  ext = pos ? cross_rows_max(ext) : -cross_rows_max(-ext);
+  const float mx = ext == (pos ? -INFINITY : INFINITY) ? -INFINITY : ext * scale_log2;
+  const float mnew = fmaxf(st.m, mx);
+  // SAFE: a column with no visible key so far keeps m = -inf, weight 0, and alpha 1
+  const float mref = (SAFE && mnew == -INFINITY) ? 0.f : mnew;
+  MfmaP<DT> p;
+  p.alpha = __builtin_amdgcn_exp2f(st.m - mref);
+  float psum = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float w = __builtin_amdgcn_exp2f(fmaf(s[k], scale_log2, -mref));
+    psum += w;
+    if constexpr (DT == DT_BF16) {
+      const __bf16 h = (__bf16)w;
+      p.hi[k] = h;
+      p.lo[k] = (__bf16)(w - (float)h);
+    } else {
+      const _Float16 h = (_Float16)w;
+      p.hi[k] = h;
+      p.lo[k] = (_Float16)(w - (float)h);
+    }
+  }
+  st.l = st.l * p.alpha + psum;
+  st.m = mnew;
+  return p;
+}
+
+template <int DT, int D, bool MASK>
+__device__ __forceinline__ void mfma_pv(MfmaState<DT, D>& st, MfmaV<DT, D>& vb,
+                                        const MfmaP<DT>& p, int vvalid) {
+  using C = MfmaCfg<DT, D>;
+  using T = op8_t<DT>;
+  if (MASK) {
     // zero the V elements of tokens past the written context (0 * NaN is NaN)
+    const int r = lane_id() >> 4;
     const int kv = min(8, max(0, vvalid - 8 * r));
     const uint32_t m0 = (0 < kv ? 0xffffu : 0u) | (1 < kv ? 0xffff0000u : 0u);
     const uint32_t m1 = (2 < kv ? 0xffffu : 0u) | (3 < kv ? 0xffff0000u : 0u);
@@ -129,40 +185,29 @@ __device__ __forceinline__ void mfma_unit(MfmaState<DT, D>& st, const MfmaK<DT, 
       vb[j].w &= m3;
     }
   }
-  float mx = s[0];
+  // rescale this column's outputs by its own alpha (skipped when no column's max moved, as
+  // is usual once a column has seen a few hundred keys: multiplying by 1 changes nothing),
+  // then add V^T . P^T
+  if (__builtin_amdgcn_ballot_w64(p.alpha != 1.f)) {
 #pragma unroll
-  for (int k = 1; k < 8; ++k) mx = fmaxf(mx, s[k]);
-  mx = cross_rows_max(mx);
-  const float mnew = fmaxf(st.m, mx);
-  // SAFE: a column with no visible key so far keeps m = -inf, weight 0, and alpha 1
-  const float mref = (SAFE && mnew == -INFINITY) ? 0.f : mnew;
-  const float alpha = __builtin_amdgcn_exp2f(st.m - mref);
-  float psum = 0.f;
-  T phi, plo;
+    for (int j = 0; j < C::NJ; ++j)
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const float p = __builtin_amdgcn_exp2f(s[k] - mref);
-    psum += p;
-    if constexpr (DT == DT_BF16) {
-      const __bf16 h = (__bf16)p;
-      phi[k] = h;
-      plo[k] = (__bf16)(p - (float)h);
-    } else {
-      const _Float16 h = (_Float16)p;
-      phi[k] = h;
-      plo[k] = (_Float16)(p - (float)h);
-    }
+      for (int i = 0; i < 4; ++i) st.acc[j][i] *= p.alpha;
   }
-  st.l = st.l * alpha + psum;
-  st.m = mnew;
-  // rescale this column's outputs by its own alpha, then add V^T . P^T
 #pragma unroll
   for (int j = 0; j < C::NJ; ++j) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) st.acc[j][i] *= alpha;
-    st.acc[j] = mfma<DT>(__builtin_bit_cast(T, vb[j]), phi, st.acc[j]);
-    st.acc[j] = mfma<DT>(__builtin_bit_cast(T, vb[j]), plo, st.acc[j]);
+    st.acc[j] = mfma<DT>(__builtin_bit_cast(T, vb[j]), p.hi, st.acc[j]);
+    st.acc[j] = mfma<DT>(__builtin_bit_cast(T, vb[j]), p.lo, st.acc[j]);
   }
+}
+
+// One unit: scores, softmax update and P . V for one 16-column block.
+template <int DT, int D, bool MASK, bool SAFE>
+__device__ __forceinline__ void mfma_unit(MfmaState<DT, D>& st, const MfmaK<DT, D>& kb,
+                                          MfmaV<DT, D>& vb, const MfmaQ<DT, D>& qb,
+                                          float scale_log2, int lim, int vvalid) {
+  const MfmaP<DT> p = mfma_scores<DT, D, MASK, SAFE>(st, kb, qb, scale_log2, lim);
+  mfma_pv<DT, D, MASK>(st, vb, p, vvalid);
 }
 
 // Lane offsets of the unit operands (see the layout notes at the top of this file).
@@ -176,12 +221,10 @@ __device__ __forceinline__ MfmaLaneOffsets<DT, D> mfma_offsets() {
   for (int b = 0; b < 2; ++b) {
     const int t = 8 * (n >> 2) + 4 * b + (n & 3);  // unit token of S-block row n
     o.kt[b] = t >> 4;
-#pragma unroll
-    for (int kk = 0; kk < C::NKK; ++kk) o.k[b][kk] = ((4 * kk + r) * 16 + (t & 15)) * 16;
+    o.k[b] = (r * 16 + (t & 15)) * 16;  // chunk 4 kk + r of token t: + 1 KiB per kk
   }
   o.vt = r >> 1;
-#pragma unroll
-  for (int j = 0; j < C::NJ; ++j) o.v[j] = ((16 * j + n) * 16 + 8 * (r & 1)) * C::E;
+  o.v = (n * 16 + 8 * (r & 1)) * C::E;  // dimension 16 j + n: + 256 elements per j
   return o;
 }
 
