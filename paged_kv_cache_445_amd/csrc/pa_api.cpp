@@ -5,6 +5,7 @@
 
 #include <atomic>
 #include <cmath>
+#include <mutex>
 
 #include "pa.h"
 #include "pa_internal.h"
@@ -187,6 +188,31 @@ size_t even_workspace_bytes(const pa_geom* g, int grid) {
 
 pa_status hip_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
 
+// A second stream per device for the multi-row (chunk) kernel, so that it runs beside the
+// decode kernel of the same call: the two write disjoint rows and the chunk kernel is bound
+// by the matrix cores, the decode kernel by HBM.  Created once per device at default
+// priority; its two events fork the caller's stream into it and join it back.  The mutex
+// orders concurrent calls that share the events (their chunk kernels then run one after
+// the other on the side stream).
+struct SideStream {
+  std::once_flag once;
+  hipError_t err = hipSuccess;
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  std::mutex mu;
+};
+
+SideStream* side_stream(int dev) {
+  static SideStream sides[kMaxDevices];
+  SideStream& s = sides[dev];
+  std::call_once(s.once, [&] {
+    s.err = hipStreamCreateWithFlags(&s.stream, hipStreamNonBlocking);
+    if (s.err == hipSuccess) s.err = hipEventCreateWithFlags(&s.fork, hipEventDisableTiming);
+    if (s.err == hipSuccess) s.err = hipEventCreateWithFlags(&s.join, hipEventDisableTiming);
+  });
+  return s.err == hipSuccess ? &s : nullptr;
+}
+
 float scale_to_log2(float scale) { return scale * 1.4426950408889634f; }
 
 }  // namespace
@@ -280,15 +306,24 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   a.heads_per_wave = path == 0 ? heads_per_wave(g) : 1;
   a.odd_skew = odd_skew();
 
-  hipError_t e = use_mfma(g) ? pa::launch_mfma_decode(g->kv_dtype, pa::MODE_EVEN, a, grid, st)
-                             : pa::launch_valu_decode(g->kv_dtype, pa::MODE_EVEN, a, grid, st);
-  if (e != hipSuccess) return PA_ERR_HIP;
+  auto decode = [&] {
+    return use_mfma(g) ? pa::launch_mfma_decode(g->kv_dtype, pa::MODE_EVEN, a, grid, st)
+                       : pa::launch_valu_decode(g->kv_dtype, pa::MODE_EVEN, a, grid, st);
+  };
+  if (!query_start_loc) return hip_status(decode());
 
-  if (query_start_loc) {
-    e = pa::launch_chunk(g->kv_dtype, a, num_q_rows, st);
-    if (e != hipSuccess) return PA_ERR_HIP;
-  }
-  return PA_OK;
+  // multi-row sequences: the chunk kernel on the side stream, forked from and joined back
+  // into the caller's stream around the decode kernel
+  SideStream* side = side_stream(current_device());
+  if (!side) return PA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(side->mu);
+  hipError_t e = hipEventRecord(side->fork, st);
+  if (e == hipSuccess) e = hipStreamWaitEvent(side->stream, side->fork, 0);
+  if (e == hipSuccess) e = pa::launch_chunk(g->kv_dtype, a, num_q_rows, side->stream);
+  const hipError_t ed = decode();
+  if (e == hipSuccess) e = hipEventRecord(side->join, side->stream);
+  if (e == hipSuccess) e = hipStreamWaitEvent(st, side->join, 0);
+  return e == hipSuccess && ed == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
 pa_status pa_decode_partitioned(float* tmp_out, float* max_logits, float* exp_sums,
