@@ -152,6 +152,26 @@ def test_multi_row_chunks_small(dev):
         parity(dev, b)
 
 
+def test_multi_row_many_sequences(dev):
+    """More multi-row sequences than the chunk kernel orders longest first (256): its items
+    then keep the sequence order.  300 sequences of 2..40 rows beside 40 decode rows."""
+    rng = np.random.default_rng(515)
+    n = np.concatenate([rng.integers(2, 41, size=300), np.ones(40, dtype=np.int64)])
+    prior = rng.integers(0, 400, size=n.size)
+    b = W.build_batch("many_chunks", "bf16", prior + n, n, 32, 8, 128, rng)
+    parity(dev, b)
+
+
+def test_multi_row_longest_first_ordering(dev):
+    """Multi-row sequences whose prior contexts tie and differ (the longest-first numbering
+    ranks ties by sequence index), 256 of them exactly."""
+    rng = np.random.default_rng(516)
+    n = rng.integers(2, 20, size=256)
+    prior = rng.choice([0, 100, 100, 900], size=256)
+    b = W.build_batch("ordered_chunks", "f16", prior + n, n, 16, 4, 128, rng)
+    parity(dev, b)
+
+
 # ----------------------------------------------------------------- invariances on the GPU
 
 def test_physical_permutation_and_repeat_are_bitwise(dev):
