@@ -47,6 +47,13 @@ DESCRIPTIONS = {
     "mixed_chunked_bf16": "mixed step: 8 x 512-row causal chunks + 120 decode rows, 32 q / 8 kv "
                           "heads, head_dim 128, bf16 KV",
     "tiny_f32": "tiny decode: 4 seqs x 4 heads, head_dim 64, fp32 KV",
+    "spec_verify_f16": "speculative verify step: 32 seqs x 6 causal rows (last token + 5 "
+                       "drafts) x 32 heads (MHA), head_dim 128, fp16 KV, prior ctx U[256,2048]",
+    "spec_verify_gqa_bf16": "speculative verify step: 64 seqs x 4 causal rows, 32 q / 8 kv "
+                            "heads, head_dim 128, bf16 KV, prior ctx U[512,4096]",
+    "cow_copy_f16": "copy-on-write block copies: 256 (source, destination) pairs of LLaMA-7B "
+                    "blocks (32 kv heads x 128 x 16 tokens fp16, 128 KiB per pool) in an "
+                    "8192-block pool",
 }
 
 
@@ -128,6 +135,87 @@ def cpu_baseline(b, min_seconds, threads, max_key_heads=3e8):
                       f"row-heads/s"}
 
 
+def bench_copy(args):
+    """pa_copy_blocks alone: one step is one call over COPY_PAIRS block pairs; value is the
+    HBM bytes it must move (every pair reads and writes one block of each pool)."""
+    import numpy as np
+    import torch
+    from paged_kv_cache_445_amd import pa
+    dev = torch.device("cuda:0")
+    NB, Hkv, D, pairs = 8192, 32, 128, 256
+    rng = np.random.default_rng(4457)
+    g = pa.geom(1, Hkv, Hkv, D, NB, 1, torch.float16)
+    shape_k, shape_v = (NB, Hkv, D // 8, 16, 8), (NB, Hkv, D, 16)
+    copies = args.copies or 3
+    pools = [(torch.randn(shape_k, device=dev, dtype=torch.float16),
+              torch.randn(shape_v, device=dev, dtype=torch.float16)) for _ in range(copies)]
+    # sources in the lower half of the pool, distinct destinations in the upper half
+    maps = []
+    for _ in range(copies):
+        src = rng.choice(NB // 2, size=pairs, replace=False)
+        dst = NB // 2 + rng.choice(NB // 2, size=pairs, replace=False)
+        maps.append(torch.from_numpy(np.stack([src, dst], 1).astype(np.int64)).to(dev))
+    block_bytes = Hkv * 16 * D * 2
+    moved = pairs * 2 * 2 * block_bytes  # K and V, read and written
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        kc, vc = pools[i % copies]
+        pa.copy_blocks(kc, vc, maps[i % copies], g)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    call_ms = ev[0].elapsed_time(ev[1]) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+    achieved = moved / (call_ms * 1e-3) / 1e9
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        # the oracle's copy (one thread, element by element through the layout) on a
+        # 512-block host pool of the same geometry, the same number of pairs
+        import oracle
+        og = oracle.make_geom(1, Hkv, Hkv, D, 512, 1, "f16")
+        kp = np.zeros((512, Hkv, D // 8, 16, 8), dtype=np.float16)
+        vp = np.zeros((512, Hkv, D, 16), dtype=np.float16)
+        m = np.stack([rng.choice(256, size=pairs, replace=False),
+                      256 + rng.choice(256, size=pairs, replace=False)], 1)
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.copy_blocks(kp, vp, m, og)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= min(args.cpu_seconds, 10.0):
+                break
+        cpu = {"value": round(moved * reps / el / 1e9, 4), "unit": "GB/s", "cores": 1,
+               "kind": "oracle",
+               "sample": f"{pairs} pairs of the same blocks in a 512-block host pool, {reps} "
+                         f"calls in {el:.1f} s"}
+    line = {
+        "metric": "copy-on-write block copy: HBM GB/s (read + write)",
+        "value": round(moved / (ms_per_step * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "cow_copy_f16", "description": DESCRIPTIONS["cow_copy_f16"],
+                   "pairs": pairs, "bytes_per_step": moved, "pool_copies_rotated": copies},
+        "pa_copy_blocks_us": round(call_ms * 1e3, 3),
+        "roofline": {"bound": "hbm", "kernel": "pa_copy_blocks", "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -164,6 +252,8 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.workload == "cow_copy_f16":
+        return bench_copy(args)
 
     print(f"[bench] building workload {args.workload}", file=sys.stderr, flush=True)
     b = W.make(args.workload)

@@ -90,6 +90,21 @@ pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_cache
                                const int64_t* slot_mapping, int64_t num_tokens,
                                const pa_geom* geom, void* stream);
 
+/*
+ * Block copy for copy-on-write ("vLLM 架构源码解析 第1篇" §4.3.2: samples forked from one
+ * prompt share its blocks; a sample that is about to write into a block other sequences
+ * still reference first gets a new block holding a copy of it).  For every pair p,
+ * physical block block_mapping[2p] (source) is copied bit for bit onto physical block
+ * block_mapping[2p + 1] (destination) in both pools, for every KV head.
+ *   k_cache, v_cache  the pools (layout above), written in place
+ *   block_mapping     int64 [num_pairs][2]: source, destination
+ * A pair with an id outside [0, num_blocks) is skipped.  Destinations must be distinct and
+ * no destination may be the source of another pair of the same call (the copies run in
+ * parallel); this is the caller's contract and is not checked.  num_pairs == 0 is a no-op.
+ */
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping,
+                         int64_t num_pairs, const pa_geom* geom, void* stream);
+
 /* Workspace bytes pa_decode needs for this geometry and row count (0 is never returned
  * for a valid geometry; returns 0 for an invalid one). */
 size_t pa_workspace_size(const pa_geom* geom, int32_t num_q_rows);

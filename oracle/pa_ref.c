@@ -109,6 +109,27 @@ int32_t pa_ref_reshape_and_cache(const void* key, const void* value, void* k_cac
   return 0;
 }
 
+/* ---------------------------------------------------------------- copy-on-write block copy */
+
+int32_t pa_ref_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping,
+                           int64_t num_pairs, const pa_ref_geom* g) {
+  if (!geom_ok(g) || num_pairs < 0) return -1;
+  const int e = elem_bytes(g->dtype);
+  for (int64_t p = 0; p < num_pairs; ++p) {
+    const int64_t src = block_mapping[2 * p], dst = block_mapping[2 * p + 1];
+    if (src < 0 || src >= g->num_blocks || dst < 0 || dst >= g->num_blocks) continue;
+    for (int32_t h = 0; h < g->num_kv_heads; ++h)
+      for (int32_t t = 0; t < g->block_size; ++t)
+        for (int32_t d = 0; d < g->head_dim; ++d) {
+          memcpy((char*)k_cache + e * pa_ref_k_offset(g, dst, h, t, d),
+                 (const char*)k_cache + e * pa_ref_k_offset(g, src, h, t, d), e);
+          memcpy((char*)v_cache + e * pa_ref_v_offset(g, dst, h, t, d),
+                 (const char*)v_cache + e * pa_ref_v_offset(g, src, h, t, d), e);
+        }
+  }
+  return 0;
+}
+
 /* ---------------------------------------------------------------- row bookkeeping */
 
 typedef struct {

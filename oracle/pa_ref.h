@@ -73,6 +73,14 @@ void pa_ref_to_double(const void* src, int32_t dtype, int64_t n, double* dst);
 int32_t pa_ref_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
                                  const int64_t* slot_mapping, int64_t num_tokens, const pa_ref_geom* g);
 
+/* Copy-on-write block copy ([AR1] §4.3.2: a forked sample that must write into a block other
+ * sequences still share first gets a private copy of it).  For every pair p, every element
+ * (kv head, token, dim) of physical block block_mapping[2p] is copied to block
+ * block_mapping[2p+1], in both pools, in pair order.  Pairs with an id outside
+ * [0, num_blocks) are skipped.  Returns 0, or -1 on bad arguments. */
+int32_t pa_ref_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping,
+                           int64_t num_pairs, const pa_ref_geom* g);
+
 /* Paged attention ([DD] §2.2, §3.3, §6.2): for each selected query row r and query head h,
  * out[k][h][:] = softmax(scale * q . K^T) . V over the row's visible keys, gathered through
  * block_tables; lse[k][h] = max + ln(sum).  query_start_loc may be NULL (row r = seq r).

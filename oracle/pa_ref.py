@@ -47,6 +47,8 @@ def lib():
         L.pa_ref_reshape_and_cache.restype = ctypes.c_int32
         L.pa_ref_reshape_and_cache.argtypes = [_vp, _vp, _vp, _vp, _i64p, ctypes.c_int64,
                                                ctypes.POINTER(Geom)]
+        L.pa_ref_copy_blocks.restype = ctypes.c_int32
+        L.pa_ref_copy_blocks.argtypes = [_vp, _vp, _i64p, ctypes.c_int64, ctypes.POINTER(Geom)]
         L.pa_ref_paged_attention.restype = ctypes.c_int32
         L.pa_ref_paged_attention.argtypes = [_f64p, _f64p, _vp, _vp, _vp, _i32p, _i32p, _i32p,
                                              ctypes.c_int32, ctypes.c_double, ctypes.POINTER(Geom),
@@ -109,6 +111,16 @@ def reshape_and_cache(key, value, k_pool, v_pool, slot_mapping, g):
                                         ctypes.byref(g))
     if rc != 0:
         raise ValueError("oracle reshape_and_cache: slot outside the pool")
+
+
+def copy_blocks(k_pool, v_pool, block_mapping, g):
+    """In-place copy of whole blocks: block_mapping int64 [n, 2] of (source, destination)."""
+    assert k_pool.flags.c_contiguous and v_pool.flags.c_contiguous
+    m = _contig(block_mapping, np.int64).reshape(-1, 2)
+    rc = lib().pa_ref_copy_blocks(_vp(k_pool.ctypes.data), _vp(v_pool.ctypes.data),
+                                  _ptr(m, _i64p), m.shape[0], ctypes.byref(g))
+    if rc != 0:
+        raise ValueError("oracle copy_blocks: bad arguments")
 
 
 def paged_attention(q, k_pool, v_pool, block_tables, context_lens, query_start_loc, scale, g,

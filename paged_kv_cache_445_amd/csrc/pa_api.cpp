@@ -253,6 +253,25 @@ pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_cache
   return hip_status(pa::launch_reshape(g->kv_dtype, a, (hipStream_t)stream));
 }
 
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping,
+                         int64_t num_pairs, const pa_geom* g, void* stream) {
+  const pa_status gs = check_geom(g);
+  if (gs != PA_OK) return gs;
+  if (num_pairs < 0) return PA_ERR_SHAPE;
+  if (num_pairs == 0) return PA_OK;
+  if (!k_cache || !v_cache || !block_mapping) return PA_ERR_NULL;
+  pa::CopyBlocksArgs a{};
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_mapping = block_mapping;
+  a.num_pairs = num_pairs;
+  a.block_bytes = (int64_t)g->num_kv_heads * g->block_size * g->head_dim * elem_bytes(g->kv_dtype);
+  a.num_blocks = g->num_blocks;
+  const int64_t pieces = (a.block_bytes + 16383) / 16384;
+  if (num_pairs * 2 * pieces > 0x7fffffffLL) return PA_ERR_SHAPE;
+  return hip_status(pa::launch_copy_blocks(a, (hipStream_t)stream));
+}
+
 size_t pa_workspace_size(const pa_geom* g, int32_t num_q_rows) {
   if (check_geom(g) != PA_OK || num_q_rows < 0) return 0;
   return even_workspace_bytes(g, split_grid(g, pa::MODE_EVEN));

@@ -61,6 +61,15 @@ struct ReshapeArgs {
   int32_t head_dim;
 };
 
+struct CopyBlocksArgs {
+  void* k_cache;
+  void* v_cache;
+  const int64_t* block_mapping;  // [num_pairs][2]: source block, destination block
+  int64_t num_pairs;
+  int64_t block_bytes;           // one block of one pool: Hkv * 16 * D * elem
+  int64_t num_blocks;
+};
+
 struct PartReduceArgs {
   void* out;
   const float* tmp_out;
@@ -81,6 +90,7 @@ int valu_decode_max_blocks_per_cu(int dt, int head_dim, int hpw, int mode, int l
 hipError_t launch_mfma_decode(int dt, int mode, const DecodeArgs& a, int grid, hipStream_t st);
 int mfma_decode_max_blocks_per_cu(int dt, int head_dim, int mode, int lds_bytes);
 hipError_t launch_part_reduce(int dt, const PartReduceArgs& a, hipStream_t st);
+hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t st);
 
 // resident workgroups per CU at most (32 waves of 64 lanes): bounds the even split's grid
 constexpr int kMaxWgPerCu = 8;

@@ -49,6 +49,8 @@ _lib.pa_workspace_size.restype = ctypes.c_size_t
 _lib.pa_workspace_size.argtypes = [_G, ctypes.c_int32]
 _lib.pa_reshape_and_cache.restype = ctypes.c_int
 _lib.pa_reshape_and_cache.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_int64, _G, _vp]
+_lib.pa_copy_blocks.restype = ctypes.c_int
+_lib.pa_copy_blocks.argtypes = [_vp, _vp, _vp, ctypes.c_int64, _G, _vp]
 _lib.pa_decode.restype = ctypes.c_int
 _lib.pa_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_float,
                            _vp, ctypes.c_size_t, _G, _vp]
@@ -105,6 +107,14 @@ def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, g: Geom, strea
            _lib.pa_reshape_and_cache(_p(key), _p(value), _p(k_cache), _p(v_cache),
                                      _p(slot_mapping), int(slot_mapping.numel()),
                                      ctypes.byref(g), _stream(stream)))
+
+
+def copy_blocks(k_cache, v_cache, block_mapping, g: Geom, stream=None):
+    """block_mapping: int64 tensor [num_pairs, 2] of (source, destination) block ids."""
+    _check("pa_copy_blocks",
+           _lib.pa_copy_blocks(_p(k_cache), _p(v_cache), _p(block_mapping),
+                               int(block_mapping.shape[0]) if block_mapping.numel() else 0,
+                               ctypes.byref(g), _stream(stream)))
 
 
 def decode(out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc, scale,

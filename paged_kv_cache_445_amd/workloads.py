@@ -280,12 +280,36 @@ def mixed_chunked_bf16(seed: int = 4454, num_chunk: int = 8, num_decode: int = 1
                        max_blocks_per_seq=500)
 
 
+def spec_verify_f16(seed: int = 4455, num_seqs: int = 32, num_draft: int = 5) -> Batch:
+    """Speculative-decoding verify step on the LLaMA-7B shape ("vLLM 深度拆解" §5.1: the
+    target model checks num_draft drafted tokens in one pass): every sequence runs the last
+    accepted token plus its num_draft drafts as num_draft + 1 causal query rows over a
+    prior context U[256, 2048]."""
+    rng = np.random.default_rng(seed)
+    n = num_draft + 1
+    prior = rng.integers(256, 2049, size=num_seqs)
+    return build_batch("spec_verify_f16", "f16", prior + n, np.full(num_seqs, n), 32, 32, 128,
+                       rng, num_blocks=8192, max_blocks_per_seq=129)
+
+
+def spec_verify_gqa_bf16(seed: int = 4456, num_seqs: int = 64, num_draft: int = 3) -> Batch:
+    """The verify step on a GQA shape (32 query / 8 KV heads): 4 causal rows per sequence,
+    prior context U[512, 4096]."""
+    rng = np.random.default_rng(seed)
+    n = num_draft + 1
+    prior = rng.integers(512, 4097, size=num_seqs)
+    return build_batch("spec_verify_gqa_bf16", "bf16", prior + n, np.full(num_seqs, n), 32, 8,
+                       128, rng, max_blocks_per_seq=257)
+
+
 PRESETS = {
     "tiny_f32": tiny_f32,
     "llama7b_f16": llama7b_f16,
     "gqa_long_bf16": gqa_long_bf16,
     "prefix_shared_f16": prefix_shared_f16,
     "mixed_chunked_bf16": mixed_chunked_bf16,
+    "spec_verify_f16": spec_verify_f16,
+    "spec_verify_gqa_bf16": spec_verify_gqa_bf16,
 }
 
 

@@ -28,6 +28,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for fn in ("pa_reshape_and_cache", "pa_decode", "pa_decode_partitioned", "pa_decode_reduce",
+               "pa_copy_blocks",
                "pa_workspace_size", "pa_kv_cache_bytes", "pa_status_str"):
         assert fn in names
 
@@ -118,3 +119,10 @@ def test_host_checks_return_codes_without_launching(lib):
                                                 ctypes.POINTER(Geom), vp]
     assert lib.pa_decode_reduce(dummy, dummy, dummy, None, 4, 4, ctypes.byref(g), None) == -1
     assert lib.pa_decode_reduce(dummy, dummy, dummy, dummy, 4, 0, ctypes.byref(g), None) == -2
+
+    lib.pa_copy_blocks.restype = ctypes.c_int
+    lib.pa_copy_blocks.argtypes = [vp] * 3 + [ctypes.c_int64, ctypes.POINTER(Geom), vp]
+    assert lib.pa_copy_blocks(dummy, None, dummy, 2, ctypes.byref(g), None) == -1
+    assert lib.pa_copy_blocks(dummy, dummy, dummy, -1, ctypes.byref(g), None) == -2
+    assert lib.pa_copy_blocks(None, None, None, 0, ctypes.byref(g), None) == 0
+    assert lib.pa_copy_blocks(dummy, dummy, dummy, 2, ctypes.byref(_g(head_dim=80)), None) == -3

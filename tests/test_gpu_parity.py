@@ -322,3 +322,61 @@ def test_mixed_chunked_bf16(dev):
 def test_mixed_chunked_bf16_prior_zero(dev):
     b = W.make("mixed_chunked_bf16", prior_zero=True)
     parity(dev, b, rows=_mixed_rows(b))
+
+
+# ----------------------------------------------------------------- copy-on-write block copy
+
+def _bits_pool(shape, dtype, rng):
+    if dtype == "f32":
+        return rng.integers(0, 1 << 32, size=shape, dtype=np.uint32).view(np.float32)
+    bits = rng.integers(0, 1 << 16, size=shape, dtype=np.uint16)
+    return bits.view(np.float16) if dtype == "f16" else bits
+
+
+@pytest.mark.parametrize("dtype,Hkv,D,npairs", [("f16", 32, 128, 200), ("bf16", 8, 128, 77),
+                                                ("f32", 4, 64, 33), ("f16", 1, 64, 5),
+                                                ("bf16", 3, 128, 1)])
+def test_copy_blocks_bitwise(dev, dtype, Hkv, D, npairs):
+    """pa_copy_blocks against the oracle's copy over every byte of both pools: random bit
+    patterns, sources reused, distinct destinations, and pairs outside the pool skipped."""
+    import torch
+    import oracle
+    from paged_kv_cache_445_amd import pa
+    from paged_kv_cache_445_amd.device_batch import TORCH_DTYPE, to_device
+    _log(f"[copy_blocks] {dtype} Hkv={Hkv} D={D} pairs={npairs}")
+    rng = np.random.default_rng(31 + Hkv + D)
+    NB, X = 2 * npairs + 40, 16 // W.ELEM_BYTES[dtype]
+    kp = _bits_pool((NB, Hkv, D // X, 16, X), dtype, rng)
+    vp = _bits_pool((NB, Hkv, D, 16), dtype, rng)
+    src = rng.integers(0, NB // 2, size=npairs)
+    dst = NB // 2 + rng.permutation(NB - NB // 2)[:npairs]
+    pairs = np.stack([src, dst], axis=1).astype(np.int64)
+    pairs = np.concatenate([pairs, [[-1, NB - 1], [0, NB], [NB, 1]]]).astype(np.int64)
+    k_dev, v_dev = to_device(kp, dtype, "cuda"), to_device(vp, dtype, "cuda")
+    g = pa.geom(1, Hkv, Hkv, D, NB, 1, TORCH_DTYPE[dtype])
+    pa.copy_blocks(k_dev, v_dev, torch.from_numpy(pairs).cuda(), g)
+    torch.cuda.synchronize()
+    oracle.copy_blocks(kp, vp, pairs, oracle.make_geom(1, Hkv, Hkv, D, NB, 1, dtype))
+    for got, want in ((k_dev, kp), (v_dev, vp)):
+        c = got.cpu()
+        c = c.view(torch.int16).numpy() if dtype == "bf16" else c.numpy()
+        assert np.array_equal(c.view(np.uint8), want.view(np.uint8))
+
+
+# ----------------------------------------------------------------- speculative verify rows
+
+@pytest.mark.parametrize("name", ["spec_verify_f16", "spec_verify_gqa_bf16"])
+def test_spec_verify(dev, name):
+    """Every sequence runs k + 1 causal rows (the verify pass of speculative decoding)."""
+    parity(dev, W.make(name))
+
+
+def test_spec_verify_mixed_with_decode_rows(dev):
+    """Verify rows of 2..6 per sequence interleaved with plain decode rows, short contexts
+    included (a row whose causal range is inside the first block)."""
+    rng = np.random.default_rng(606)
+    n = np.array([6, 1, 2, 1, 4, 3, 1, 5, 2, 6])
+    prior = np.array([0, 9, 1, 300, 14, 2000, 1, 31, 700, 45])
+    for dtype, Hq, Hkv in (("f16", 16, 16), ("bf16", 16, 4), ("bf16", 8, 1)):
+        b = W.build_batch("verify_mix", dtype, prior + n, n, Hq, Hkv, 128, rng)
+        parity(dev, b)

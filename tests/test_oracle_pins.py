@@ -446,3 +446,58 @@ def test_partition_overflow_is_an_error():
     with pytest.raises(ValueError):
         oracle.partition_attention(b.q, kp, vp, b.block_tables, b.context_lens, None, b.scale,
                                    H.geom(b), 16, 3)
+
+
+# ----------------------------------------------------------------- copy-on-write block copy
+
+def _random_pool_bits(shape, dtype, rng):
+    """Pool of random bit patterns (NaNs and infinities included) in the storage dtype."""
+    if dtype == "f32":
+        return rng.integers(0, 1 << 32, size=shape, dtype=np.uint32).view(np.float32)
+    bits = rng.integers(0, 1 << 16, size=shape, dtype=np.uint16)
+    return bits.view(np.float16) if dtype == "f16" else bits
+
+
+@pytest.mark.parametrize("dtype,D,Hkv", [("f32", 64, 2), ("f16", 128, 3), ("bf16", 64, 1)])
+def test_copy_blocks_matches_block_axis_assignment(dtype, D, Hkv):
+    """The oracle's element-by-element copy through the layout functions equals numpy's
+    assignment along the block axis of the declared pool shapes, pair by pair; pairs with an
+    id outside the pool change nothing."""
+    rng = np.random.default_rng(21)
+    NB, X = 12, 16 // W.ELEM_BYTES[dtype]
+    g = oracle.make_geom(1, Hkv, Hkv, D, NB, 1, dtype)
+    kp = _random_pool_bits((NB, Hkv, D // X, 16, X), dtype, rng)
+    vp = _random_pool_bits((NB, Hkv, D, 16), dtype, rng)
+    pairs = np.array([[3, 7], [0, 5], [3, 9], [11, 2], [-1, 4], [4, NB], [NB + 3, 1]],
+                     dtype=np.int64)
+    wk, wv = kp.copy(), vp.copy()
+    for s, d in pairs:
+        if 0 <= s < NB and 0 <= d < NB:
+            wk[d] = wk[s]
+            wv[d] = wv[s]
+    oracle.copy_blocks(kp, vp, pairs, g)
+    assert np.array_equal(kp.view(np.uint8), wk.view(np.uint8))
+    assert np.array_equal(vp.view(np.uint8), wv.view(np.uint8))
+
+
+def test_copy_on_write_fork_keeps_attention_bitwise():
+    """A sequence forked onto copies of its blocks ("vLLM 架构源码解析 第1篇" §4.3.2) attends
+    exactly as the original: same keys, same order, same bits."""
+    import copy
+    rng = np.random.default_rng(23)
+    b = W.build_batch("fork", "bf16", [70, 33], np.ones(2), 8, 2, 128, rng)
+    kp, vp = H.oracle_pools(b)
+    used = set(np.unique(b.block_tables).tolist())
+    free = [x for x in range(b.num_blocks) if x not in used]
+    nblk = -(-int(b.context_lens[0]) // 16)
+    # fork sequence 0 into a third row: shared leading blocks, its last block copied
+    c = copy.copy(b)
+    c.num_seqs = 3
+    c.block_tables = np.concatenate([b.block_tables, b.block_tables[:1]]).copy()
+    c.block_tables[2, nblk - 1] = free[0]
+    c.context_lens = np.concatenate([b.context_lens, b.context_lens[:1]])
+    c.q = np.concatenate([b.q, b.q[:1]])
+    c.query_start_loc = None
+    oracle.copy_blocks(kp, vp, np.array([[b.block_tables[0, nblk - 1], free[0]]]), H.geom(c))
+    out, lse = H.oracle_attention(c, kp, vp)
+    assert np.array_equal(out[2], out[0]) and np.array_equal(lse[2], lse[0])
