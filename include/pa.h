@@ -54,7 +54,8 @@ typedef enum {
   PA_ERR_SHAPE = -2,       /* inconsistent sizes (negative counts, Hq % Hkv != 0, ...) */
   PA_ERR_UNSUPPORTED = -3, /* a valid but unimplemented combination (head_dim, dtype, ...) */
   PA_ERR_WORKSPACE = -4,   /* workspace missing or smaller than pa_workspace_size() */
-  PA_ERR_HIP = -5          /* a HIP launch failed (hipGetLastError after the launch) */
+  PA_ERR_HIP = -5,         /* a HIP launch failed (hipGetLastError after the launch) */
+  PA_ERR_NO_BLOCKS = -6    /* the block pool has too few free blocks (block manager) */
 } pa_status;
 
 /* Geometry shared by all calls (host struct, read during the call only). */

@@ -4,7 +4,9 @@
 // other requests' decode rows, and §3.3.2 marks each request's rows with query_start_loc.
 // A sequence s with n > 1 rows has its context_lens entry counting those rows (they were
 // written by reshape_and_cache first, §3.3.3); row j sits at position ctx - n + j and attends
-// keys [0, ctx - n + j] (causal).  Decode rows (n = 1) are left to the decode kernels.
+// keys [0, ctx - n + j] (causal).  Sequences with few rows (a decode row, or on the
+// matrix-core path up to 16 / G rows, as in a speculative verify step) are left to the decode
+// kernels.
 //
 // Work item = (sequence, KV head g, block of 128 query columns), a column being one (row,
 // head) pair: 128 / G consecutive rows x the G query heads of g.  The workgroup stages each
@@ -32,13 +34,15 @@ struct ChunkPlanIn {
   const int32_t* qsl;
   int32_t num_seqs;
   int32_t rows_per_item;
+  int32_t min_rows;  // sequences with fewer rows are the decode kernel's
 };
 
-// work items per sequence: ceil(n / rows_per_item) for multi-row sequences, else 0
+// work items per sequence: ceil(n / rows_per_item) for sequences of at least min_rows rows,
+// else 0
 __device__ inline void build_chunk_plan(int32_t* base, const ChunkPlanIn& p) {
   wave_plan(base, p.num_seqs, [&](int s) {
     const int32_t n = p.qsl[s + 1] - p.qsl[s];
-    return n > 1 ? (n + p.rows_per_item - 1) / p.rows_per_item : 0;
+    return n >= p.min_rows ? (n + p.rows_per_item - 1) / p.rows_per_item : 0;
   });
 }
 
@@ -245,7 +249,7 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(2))) void c
   const int G = a.num_q_heads / a.num_kv_heads;
   const int S = a.num_seqs;
   const int Hkv = a.num_kv_heads;
-  ChunkPlanIn pin{a.qsl, S, kItemCols / G};
+  ChunkPlanIn pin{a.qsl, S, kItemCols / G, a.max_rows + 1};
   build_chunk_plan(base, pin);
   const int64_t per_head = base[S];
   const int64_t total = per_head * Hkv;

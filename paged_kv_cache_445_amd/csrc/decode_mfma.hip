@@ -6,7 +6,10 @@
 // head are scored together: per 32-token unit (two 16-token blocks) the wavefront runs
 //   S^T = K . Q^T  as 2 x (D/32) MFMA 16x16x32  (M = 16 tokens, N = 16 head columns, G used)
 //   O  += P . V    as (D/16) MFMA 16x16x32     (M = 16 head rows, N = 16 dims, K = 32 tokens)
-// Each K and V byte is read once for all G heads.
+// Each K and V byte is read once for all G heads.  The 16 MFMA columns hold (row, head)
+// pairs, so a sequence with nr <= 16 / G causal query rows (the verify pass of speculative
+// decoding, "vLLM 深度拆解" §5.1: the target model checks several drafted tokens in one pass)
+// is one segment of nr * G columns whose K and V are also read once.
 //
 // Operand layouts, the token permutation that keeps scores in place, and the hi/lo split
 // of P are described in pa_mfma.h.
@@ -16,9 +19,13 @@
 
 namespace pa {
 
-// All query heads of KV head g for sequence s over the units [u0, u1) (32 tokens each).
-template <int DT, int D>
-__device__ void mfma_attend(const DecodeArgs& a, int s, int g, int u0, int u1, int ctx,
+// All query columns of KV head g for sequence s over the units [u0, u1) (32 tokens each).
+// Without MULTI the columns are the G query heads of one decode row (nr = 1).  With MULTI a
+// column is one (row, query head) pair: column c is row qsl[s] + c / G, head g * G + c % G,
+// and the nr * G <= 16 columns of the sequence's nr rows are scored together.  Row j sits at
+// position ctx - nr + j and sees keys [0, ctx - nr + j].
+template <int DT, int D, bool MULTI>
+__device__ void mfma_attend(const DecodeArgs& a, int s, int g, int u0, int u1, int ctx, int nr,
                             MfmaState<DT, D>& st) {
   using C = MfmaCfg<DT, D>;
   using T = op8_t<DT>;
@@ -31,15 +38,20 @@ __device__ void mfma_attend(const DecodeArgs& a, int s, int g, int u0, int u1, i
   u1 = __builtin_amdgcn_readfirstlane(u1);
   ctx = __builtin_amdgcn_readfirstlane(ctx);
   const int G = a.num_q_heads / a.num_kv_heads;
-  const int row = __builtin_amdgcn_readfirstlane(a.qsl ? a.qsl[s] : s);
+  const int row0 = __builtin_amdgcn_readfirstlane(a.qsl ? a.qsl[s] : s);
+  // this lane's column: row offset and head
+  const int jr = MULTI ? n / G : 0;
+  const int hc = MULTI ? n - jr * G : n;
+  if constexpr (MULTI) nr = __builtin_amdgcn_readfirstlane(nr);
 
   T qb[C::NKK];
   {
     const char* qp = reinterpret_cast<const char*>(a.q) +
-                     ((int64_t)row * a.num_q_heads + (int64_t)g * G + n) * D * C::E;
+                     ((int64_t)(row0 + jr) * a.num_q_heads + (int64_t)g * G + hc) * D * C::E;
+    const bool live = MULTI ? jr < nr : n < G;
 #pragma unroll
     for (int kk = 0; kk < C::NKK; ++kk) {
-      const uint4 v = n < G ? ld16(qp + (4 * kk + r) * 16) : make_uint4(0, 0, 0, 0);
+      const uint4 v = live ? ld16(qp + (4 * kk + r) * 16) : make_uint4(0, 0, 0, 0);
       qb[kk] = __builtin_bit_cast(T, v);
     }
   }
@@ -48,30 +60,45 @@ __device__ void mfma_attend(const DecodeArgs& a, int s, int g, int u0, int u1, i
 #pragma unroll
   for (int j = 0; j < C::NJ; ++j) st.acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  mfma_stream<DT, D>(a, s, g, u0, u1, ctx, [&](MfmaK<DT, D>& kb, MfmaV<DT, D>& vb, int u) {
-    const int valid = ctx - u * kMfmaUnit;
-    if (valid >= kMfmaUnit)
-      mfma_unit<DT, D, false, false>(st, kb, vb, qb, a.scale_log2, kMfmaUnit - 1, kMfmaUnit);
-    else
-      mfma_unit<DT, D, true, false>(st, kb, vb, qb, a.scale_log2, valid - 1, valid);
-  });
+  if constexpr (!MULTI) {
+    mfma_stream<DT, D>(a, s, g, u0, u1, ctx, [&](MfmaK<DT, D>& kb, MfmaV<DT, D>& vb, int u) {
+      const int valid = ctx - u * kMfmaUnit;
+      if (valid >= kMfmaUnit)
+        mfma_unit<DT, D, false, false>(st, kb, vb, qb, a.scale_log2, kMfmaUnit - 1, kMfmaUnit);
+      else
+        mfma_unit<DT, D, true, false>(st, kb, vb, qb, a.scale_log2, valid - 1, valid);
+    });
+  } else {
+    const int last0 = ctx - nr;                 // last visible key of the first row
+    const int mine = min(last0 + jr, ctx - 1);  // ... of this lane's column (padding: ctx - 1)
+    mfma_stream<DT, D>(a, s, g, u0, u1, ctx, [&](MfmaK<DT, D>& kb, MfmaV<DT, D>& vb, int u) {
+      const int t0 = u * kMfmaUnit;
+      if (last0 - t0 >= kMfmaUnit - 1)  // every column sees the whole unit
+        mfma_unit<DT, D, false, false>(st, kb, vb, qb, a.scale_log2, kMfmaUnit - 1, kMfmaUnit);
+      else  // per-column limits; a column may see no key of this piece yet
+        mfma_unit<DT, D, true, true>(st, kb, vb, qb, a.scale_log2, mine - t0, ctx - t0);
+    });
+  }
 }
 
-// A piece of a split segment (all G heads of one KV head): publish it, or, as the
-// segment's last arrival, merge every piece and write the output.  Each lane merges its own
-// head column n and dimensions 16 j + 4 r .. + 3, so no lanes interact.
-template <int DT, int D>
-__device__ void m_split_finish(const DecodeArgs& a, const MfmaState<DT, D>& st, int G,
+// A piece of a split segment (the ncols query columns of one KV head): publish it, or, as
+// the segment's last arrival, merge every piece and write the output (the segment's first
+// column at ob).  Each lane merges its own column n and dimensions 16 j + 4 r .. + 3, so no lanes
+// interact.  Partial slots hold a.cols columns.
+template <int DT, int D, bool MULTI>
+__device__ void m_split_finish(const DecodeArgs& a, const MfmaState<DT, D>& st, int ncols,
                                const SplitSeg& sg, int64_t self, int32_t* cnt, int seen,
                                int64_t ob) {
   using C = MfmaCfg<DT, D>;
   constexpr int NE = 4 * C::NJ;
   const int lane = lane_id();
   const int r = lane >> 4, n = lane & 15;
-  const bool col = n < G;
+  const bool col = n < ncols;
+  const int CS = MULTI ? a.cols : ncols;
   // this piece's partial as published: normalised output, max (natural log), sum
   const float ltot = cross_rows_sum(st.l);  // sum of column n over the four lane rows
-  const float inv = 1.f / ltot;
+  // with several rows a piece may hold no key of a column
+  const float inv = MULTI ? (ltot > 0.f ? 1.f / ltot : 0.f) : 1.f / ltot;
   const float mine_m = st.m * 0.69314718055994531f;
   f32x4_t mine_o[C::NJ];
 #pragma unroll
@@ -79,12 +106,12 @@ __device__ void m_split_finish(const DecodeArgs& a, const MfmaState<DT, D>& st, 
   const bool last = split_arrive(cnt, (int)(sg.k1 - sg.k0), seen, [&] {
     const int64_t slot = piece_slot(sg, self);
     if (col) {
-      float* po = a.part_o + slot * G * D;  // wave-uniform base of the slot
+      float* po = a.part_o + slot * CS * D;  // wave-uniform base of the slot
 #pragma unroll
       for (int j = 0; j < C::NJ; ++j) coh_store4(po, n * D + 16 * j + 4 * r, mine_o[j]);
       if (r == 0) {
-        coh_store(a.part_m + slot * G + n, mine_m);
-        coh_store(a.part_l + slot * G + n, ltot);
+        coh_store(a.part_m + slot * CS + n, mine_m);
+        coh_store(a.part_l + slot * CS + n, ltot);
       }
     }
   }, [] {});
@@ -102,9 +129,9 @@ __device__ void m_split_finish(const DecodeArgs& a, const MfmaState<DT, D>& st, 
       return;
     }
     const int64_t slot = piece_slot(sg, k);
-    m[0] = coh_load(a.part_m + slot * G + n);
-    lk[0] = coh_load(a.part_l + slot * G + n);
-    const float* po = a.part_o + slot * G * D;  // wave-uniform base of the slot
+    m[0] = coh_load(a.part_m + slot * CS + n);
+    lk[0] = coh_load(a.part_l + slot * CS + n);
+    const float* po = a.part_o + slot * CS * D;  // wave-uniform base of the slot
 #pragma unroll
     for (int j = 0; j < C::NJ; ++j) {
       const f32x4_t v = coh_load4(po, n * D + 16 * j + 4 * r);
@@ -113,17 +140,21 @@ __device__ void m_split_finish(const DecodeArgs& a, const MfmaState<DT, D>& st, 
     }
   });
   if (col) {
+    // column n: row offset n / G, head n % G (one row without MULTI)
+    const int G = a.num_q_heads / a.num_kv_heads;
+    const int jr = MULTI ? n / G : 0, hc = MULTI ? n - jr * G : n;
+    const int64_t ocol = ob + ((int64_t)jr * a.num_q_heads + hc) * D;
     const float rinv = 1.f / L[0];
 #pragma unroll
     for (int j = 0; j < C::NJ; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        store_out<DT>(a.out, ob + (int64_t)n * D + 16 * j + 4 * r + i, U[0][4 * j + i] * rinv, a.out_f32);
+        store_out<DT>(a.out, ocol + 16 * j + 4 * r + i, U[0][4 * j + i] * rinv, a.out_f32);
   }
   counter_reset(cnt);
 }
 
-template <int DT, int D, int MODE>
+template <int DT, int D, int MODE, bool MULTI>
 __global__ __launch_bounds__(kWG) void mfma_decode_kernel(DecodeArgs a) {
   extern __shared__ int32_t lds[];
   int32_t* base = lds;
@@ -136,7 +167,7 @@ __global__ __launch_bounds__(kWG) void mfma_decode_kernel(DecodeArgs a) {
   const int64_t w = (int64_t)blockIdx.x * kWavesPerWG + wave;
 
   if constexpr (MODE == MODE_EVEN) {
-    PlanIn pin{a.context_lens, a.qsl, S, kMfmaUnit, a.seg_extra};
+    PlanIn pin{a.context_lens, a.qsl, S, kMfmaUnit, a.seg_extra, a.max_rows};
     build_plan(base, pin);
     zero_empty_rows<DT>(pin, a.out, a.num_q_heads, D, w, W, a.out_f32);
     // units: (sequence, group of kWavesPerWG KV heads, unit); wave i runs KV head i of each
@@ -157,7 +188,7 @@ __global__ __launch_bounds__(kWG) void mfma_decode_kernel(DecodeArgs a) {
         if (g < a.num_kv_heads && u0 < nu) {
           const int ctx = a.context_lens[s];
           const int row = a.qsl ? a.qsl[s] : s;
-          const int64_t ob = ((int64_t)row * a.num_q_heads + (int64_t)g * G) * D;
+          const int nr = MULTI ? a.qsl[s + 1] - row : 1;
           const bool whole = u0 == 0 && u1 == nu;
           SplitSeg sg{};
           int32_t* cnt = nullptr;
@@ -168,11 +199,14 @@ __global__ __launch_bounds__(kWG) void mfma_decode_kernel(DecodeArgs a) {
             seen = counter_peek(cnt);  // consumed after the units
           }
           MfmaState<DT, D> st;
-          mfma_attend<DT, D>(a, s, g, u0, u1, ctx, st);
+          mfma_attend<DT, D, MULTI>(a, s, g, u0, u1, ctx, nr, st);
+          // the segment's first column in `out`; column c is row + c / G, head g * G + c % G
+          const int64_t ob = ((int64_t)row * a.num_q_heads + (int64_t)g * G) * D;
           if (whole)
-            mfma_emit<DT, D>(st, G, nullptr, nullptr, nullptr, D, a.out, ob, D, a.out_f32);
+            mfma_emit<DT, D>(st, nr * G, nullptr, nullptr, nullptr, D, a.out, ob, MULTI ? G : 16,
+                             (int64_t)a.num_q_heads * D, D, a.out_f32);
           else
-            m_split_finish<DT, D>(a, st, G, sg, o, cnt, seen, ob);
+            m_split_finish<DT, D, MULTI>(a, st, nr * G, sg, o, cnt, seen, ob);
         }
         i = pe;
       }
@@ -180,7 +214,7 @@ __global__ __launch_bounds__(kWG) void mfma_decode_kernel(DecodeArgs a) {
   } else {
     const int PU = a.partition_units;  // 32-token units per partition
     const int P = a.max_partitions;
-    PlanIn pin{a.context_lens, nullptr, S, PU * kMfmaUnit, 0};
+    PlanIn pin{a.context_lens, nullptr, S, PU * kMfmaUnit, 0, 1};
     build_plan(base, pin);
     const int64_t nent = (int64_t)S * a.num_q_heads * P;
     for (int64_t e = (int64_t)blockIdx.x * kWG + threadIdx.x; e < nent; e += (int64_t)gridDim.x * kWG) {
@@ -202,33 +236,37 @@ __global__ __launch_bounds__(kWG) void mfma_decode_kernel(DecodeArgs a) {
       const int nu = (ctx + kMfmaUnit - 1) / kMfmaUnit;
       const int u0 = p * PU, u1 = min(nu, u0 + PU);
       MfmaState<DT, D> st;
-      mfma_attend<DT, D>(a, s, g, u0, u1, ctx, st);
+      mfma_attend<DT, D, false>(a, s, g, u0, u1, ctx, 1, st);
       // tmp_out [row][h][P][D]: consecutive heads are P * D apart
       const int64_t e0 = ((int64_t)s * a.num_q_heads + (int64_t)g * G) * P + p;
       mfma_emit<DT, D>(st, G, a.part_o + e0 * D, a.part_m + e0, a.part_l + e0, (int64_t)P * D,
-                       nullptr, 0, 0, false);
+                       nullptr, 0, 16, 0, 0, false);
     }
   }
   (void)lane;
 }
 
-template <int DT, int MODE>
+template <int DT, int MODE, bool MULTI>
 static hipError_t launch_d(const DecodeArgs& a, int grid, hipStream_t st) {
   const size_t lds = (size_t)(a.num_seqs + 1) * sizeof(int32_t);
   if (a.head_dim == 64)
-    hipLaunchKernelGGL((mfma_decode_kernel<DT, 64, MODE>), dim3(grid), dim3(kWG), lds, st, a);
+    hipLaunchKernelGGL((mfma_decode_kernel<DT, 64, MODE, MULTI>), dim3(grid), dim3(kWG), lds, st, a);
   else
-    hipLaunchKernelGGL((mfma_decode_kernel<DT, 128, MODE>), dim3(grid), dim3(kWG), lds, st, a);
+    hipLaunchKernelGGL((mfma_decode_kernel<DT, 128, MODE, MULTI>), dim3(grid), dim3(kWG), lds, st, a);
   return hipGetLastError();
 }
 
+// MODE_EVEN with a.max_rows > 1 runs the multi-row (verify) columns
 hipError_t launch_mfma_decode(int dt, int mode, const DecodeArgs& a, int grid, hipStream_t st) {
   if (mode == MODE_EVEN) {
-    if (dt == DT_F16) return launch_d<DT_F16, MODE_EVEN>(a, grid, st);
-    return launch_d<DT_BF16, MODE_EVEN>(a, grid, st);
+    if (a.max_rows > 1)
+      return dt == DT_F16 ? launch_d<DT_F16, MODE_EVEN, true>(a, grid, st)
+                          : launch_d<DT_BF16, MODE_EVEN, true>(a, grid, st);
+    return dt == DT_F16 ? launch_d<DT_F16, MODE_EVEN, false>(a, grid, st)
+                        : launch_d<DT_BF16, MODE_EVEN, false>(a, grid, st);
   }
-  if (dt == DT_F16) return launch_d<DT_F16, MODE_PARTITION>(a, grid, st);
-  return launch_d<DT_BF16, MODE_PARTITION>(a, grid, st);
+  return dt == DT_F16 ? launch_d<DT_F16, MODE_PARTITION, false>(a, grid, st)
+                      : launch_d<DT_BF16, MODE_PARTITION, false>(a, grid, st);
 }
 
 template <int DT, int MODE>
@@ -236,9 +274,9 @@ static int occ(int head_dim, int lds) {
   int nb = 0;
   hipError_t e;
   if (head_dim == 64)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, mfma_decode_kernel<DT, 64, MODE>, kWG, lds);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, mfma_decode_kernel<DT, 64, MODE, false>, kWG, lds);
   else
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, mfma_decode_kernel<DT, 128, MODE>, kWG, lds);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, mfma_decode_kernel<DT, 128, MODE, false>, kWG, lds);
   return e == hipSuccess && nb > 0 ? nb : 1;
 }
 

@@ -401,7 +401,7 @@ __global__ __launch_bounds__(kWG) void valu_decode_kernel(DecodeArgs a) {
   const int64_t w = (int64_t)blockIdx.x * kWavesPerWG + wave;
 
   if constexpr (MODE == MODE_EVEN) {
-    PlanIn pin{a.context_lens, a.qsl, S, kValuUnit, a.seg_extra};
+    PlanIn pin{a.context_lens, a.qsl, S, kValuUnit, a.seg_extra, 1};
     build_plan(base, pin);
     zero_empty_rows<DT>(pin, a.out, a.num_q_heads, D, w, W, a.out_f32);
     // units: (sequence, group of 4 HPW heads, tile); wave i runs heads i + 4 j of each group
@@ -493,7 +493,7 @@ __global__ __launch_bounds__(kWG) void valu_decode_kernel(DecodeArgs a) {
     // fixed partitions; rows are sequences (no query_start_loc in this mode)
     const int PU = a.partition_units;  // tiles per partition
     const int P = a.max_partitions;
-    PlanIn pin{a.context_lens, nullptr, S, PU * kBlock, 0};
+    PlanIn pin{a.context_lens, nullptr, S, PU * kBlock, 0, 1};
     build_plan(base, pin);
     // partitions past the context: max_logits = -inf, exp_sums = 0
     const int64_t nent = (int64_t)S * a.num_q_heads * P;

@@ -94,6 +94,27 @@ bool use_mfma(const pa_geom* g) {
   return g->kv_dtype != PA_F32 && g->num_q_heads / g->num_kv_heads >= 2;
 }
 
+// Which decode kernel runs a pa_decode call, and which sequences it takes.
+//  - GQA (16-bit, G >= 2): the matrix-core kernel; with query_start_loc it also takes the
+//    sequences of up to 16 / G rows (a speculative verify step), nr * G columns at once.
+//  - MHA 16-bit with more rows than sequences: the matrix-core kernel too (G = 1, up to 16
+//    rows a sequence), so verify rows read their K and V once instead of through the
+//    chunk kernel's 128-column items.
+//  - otherwise the vector kernel, one row per sequence.
+// Longer sequences go to the chunk kernel.  cols: query columns per partial slot.
+struct Route {
+  int path;      // 0: vector kernel, 1: matrix-core kernel
+  int max_rows;  // rows per sequence the decode kernel takes
+  int cols;
+};
+
+Route route(const pa_geom* g, bool multi_row, int32_t num_q_rows) {
+  const int G = g->num_q_heads / g->num_kv_heads;
+  if (use_mfma(g)) return {1, multi_row ? 16 / G : 1, multi_row ? 16 / G * G : G};
+  if (g->kv_dtype != PA_F32 && multi_row && num_q_rows > g->num_seqs) return {1, 16, 16};
+  return {0, 1, 1};
+}
+
 // LDS of the split kernels: the per-sequence plan (num_seqs + 1 ints).
 // Occupancy is evaluated for num_seqs rounded up to a power of two, so a handful of cached
 // values covers every batch size.
@@ -135,10 +156,9 @@ int heads_per_wave(const pa_geom* g) {
 int hpw_index(int hpw) { return hpw == 8 ? 3 : hpw == 4 ? 2 : hpw == 2 ? 1 : 0; }
 
 // workgroups of the split kernel: every CU full at the kernel's occupancy
-int split_grid(const pa_geom* g, int mode) {
+int split_grid(const pa_geom* g, int mode, int path) {
   static std::atomic<int> cache[kMaxDevices][2][3][2][2][4][15];
   const int dev = current_device();
-  const int path = use_mfma(g) ? 1 : 0;
   const int di = g->head_dim == 64 ? 0 : 1;
   const int bk = seq_bucket(g->num_seqs);
   const int hpw = path == 0 && mode == pa::MODE_EVEN ? heads_per_wave(g) : 1;
@@ -159,31 +179,24 @@ int split_grid(const pa_geom* g, int mode) {
   return cu_count() * want;
 }
 
-struct SplitShape {
-  int segs, heads_per_seg, unit;
-};
-
-SplitShape split_shape(const pa_geom* g) {
-  if (use_mfma(g)) return {g->num_kv_heads, g->num_q_heads / g->num_kv_heads, pa::kMfmaUnit};
-  const int hpw = heads_per_wave(g);
-  return {g->num_q_heads / hpw, hpw, pa::kValuUnit};
-}
-
 // pa_decode's workspace: one arrival counter per wave of the largest split grid the device
 // can have (so the counters sit at the same place for every geometry and stay zero between
-// calls), then two partial slots per wave of this geometry's grid: o [W][2][G][D],
-// m [W][2][G], l [W][2][G] (G: heads per wave).
+// calls), then two partial slots per wave of this geometry's grid: o [W][2][C][D],
+// m [W][2][C], l [W][2][C] (C: query columns per wave: heads per wave on the vector path,
+// Route::cols on the matrix-core path).
 size_t counter_bytes() {
   const size_t n = (size_t)cu_count() * pa::kMaxWgPerCu * pa::kWavesPerWG * sizeof(int32_t);
   return (n + 255) / 256 * 256;
 }
 
-size_t even_slots(const pa_geom* g, int grid) {
-  return (size_t)grid * pa::kWavesPerWG * 2 * split_shape(g).heads_per_seg;
+size_t even_slots(const pa_geom* g, int grid, const Route& r) {
+  const int cols = r.path ? r.cols : heads_per_wave(g);
+  return (size_t)grid * pa::kWavesPerWG * 2 * cols;
 }
 
-size_t even_workspace_bytes(const pa_geom* g, int grid) {
-  return counter_bytes() + even_slots(g, grid) * ((size_t)g->head_dim + 2) * sizeof(float);
+size_t even_workspace_bytes(const pa_geom* g, const Route& r) {
+  const int grid = split_grid(g, pa::MODE_EVEN, r.path);
+  return counter_bytes() + even_slots(g, grid, r) * ((size_t)g->head_dim + 2) * sizeof(float);
 }
 
 pa_status hip_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
@@ -227,6 +240,7 @@ const char* pa_status_str(pa_status s) {
     case PA_ERR_UNSUPPORTED: return "unsupported head_dim / block_size / dtype / group combination";
     case PA_ERR_WORKSPACE: return "workspace missing or too small";
     case PA_ERR_HIP: return "HIP launch failed";
+    case PA_ERR_NO_BLOCKS: return "not enough free blocks in the pool";
   }
   return "unknown status";
 }
@@ -274,7 +288,10 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapp
 
 size_t pa_workspace_size(const pa_geom* g, int32_t num_q_rows) {
   if (check_geom(g) != PA_OK || num_q_rows < 0) return 0;
-  return even_workspace_bytes(g, split_grid(g, pa::MODE_EVEN));
+  // enough for the call with and without query_start_loc
+  const size_t a = even_workspace_bytes(g, route(g, true, num_q_rows));
+  const size_t b = even_workspace_bytes(g, route(g, false, num_q_rows));
+  return a > b ? a : b;
 }
 
 pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -292,10 +309,11 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   if (query_start_loc && (g->kv_dtype == PA_F32 || 16 % G != 0)) return PA_ERR_UNSUPPORTED;
   hipStream_t st = (hipStream_t)stream;
 
-  const int grid = split_grid(g, pa::MODE_EVEN);
-  const size_t need = even_workspace_bytes(g, grid);
+  const Route rt = route(g, query_start_loc != nullptr, num_q_rows);
+  const int grid = split_grid(g, pa::MODE_EVEN, rt.path);
+  const size_t need = even_workspace_bytes(g, rt);
   if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
-  const size_t slots = even_slots(g, grid);
+  const size_t slots = even_slots(g, grid, rt);
   int32_t* counters = static_cast<int32_t*>(workspace);
   float* part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + counter_bytes());
   float* part_m = part_o + slots * g->head_dim;
@@ -320,16 +338,19 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   a.max_blocks_per_seq = g->max_blocks_per_seq;
   a.out_f32 = g->out_dtype == PA_F32 && g->kv_dtype != PA_F32;
   a.scale_log2 = scale_to_log2(scale);
-  const int path = use_mfma(g) ? 1 : 0;
-  a.seg_extra = seg_extra_override() >= 0 ? seg_extra_override() : kSegExtra[path];
-  a.heads_per_wave = path == 0 ? heads_per_wave(g) : 1;
+  a.seg_extra = seg_extra_override() >= 0 ? seg_extra_override() : kSegExtra[rt.path];
+  a.heads_per_wave = rt.path == 0 ? heads_per_wave(g) : 1;
   a.odd_skew = odd_skew();
+  a.max_rows = rt.max_rows;
+  a.cols = rt.cols;
 
   auto decode = [&] {
-    return use_mfma(g) ? pa::launch_mfma_decode(g->kv_dtype, pa::MODE_EVEN, a, grid, st)
-                       : pa::launch_valu_decode(g->kv_dtype, pa::MODE_EVEN, a, grid, st);
+    return rt.path ? pa::launch_mfma_decode(g->kv_dtype, pa::MODE_EVEN, a, grid, st)
+                   : pa::launch_valu_decode(g->kv_dtype, pa::MODE_EVEN, a, grid, st);
   };
-  if (!query_start_loc) return hip_status(decode());
+  // without query_start_loc, or when no sequence can have more rows than the decode kernel
+  // takes, there is no chunk work
+  if (!query_start_loc || num_q_rows <= rt.max_rows) return hip_status(decode());
 
   // multi-row sequences: the chunk kernel on the side stream, forked from and joined back
   // into the caller's stream around the decode kernel
@@ -380,7 +401,9 @@ pa_status pa_decode_partitioned(float* tmp_out, float* max_logits, float* exp_su
   a.max_partitions = max_partitions;
   const bool mf = use_mfma(g);
   a.partition_units = partition_size / (mf ? pa::kMfmaUnit : pa::kValuUnit);
-  const int grid = split_grid(g, pa::MODE_PARTITION);
+  a.max_rows = 1;
+  a.cols = g->num_q_heads / g->num_kv_heads;
+  const int grid = split_grid(g, pa::MODE_PARTITION, mf ? 1 : 0);
   hipError_t e = mf ? pa::launch_mfma_decode(g->kv_dtype, pa::MODE_PARTITION, a, grid, (hipStream_t)stream)
                     : pa::launch_valu_decode(g->kv_dtype, pa::MODE_PARTITION, a, grid, (hipStream_t)stream);
   return hip_status(e);

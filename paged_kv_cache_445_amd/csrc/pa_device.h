@@ -172,6 +172,7 @@ struct PlanIn {
   int32_t num_seqs;
   int32_t unit_tokens;
   int32_t extra;       // balancing units appended to every non-empty segment (no work)
+  int32_t max_rows;    // sequences with more query rows are left to the chunk kernel
 };
 
 // units of sequence s in the flattened list: its real units ceil(ctx / unit_tokens), plus
@@ -180,7 +181,7 @@ struct PlanIn {
 // nothing to do for that segment)
 __device__ __forceinline__ int32_t seq_units(const PlanIn& p, int s) {
   const int32_t rows = p.qsl ? p.qsl[s + 1] - p.qsl[s] : 1;
-  if (rows != 1) return 0;  // multi-row sequences are not split-context work
+  if (rows < 1 || rows > p.max_rows) return 0;  // no rows, or rows for the chunk kernel
   const int32_t ctx = p.context_lens[s];
   return ctx > 0 ? (ctx + p.unit_tokens - 1) / p.unit_tokens + p.extra : 0;
 }

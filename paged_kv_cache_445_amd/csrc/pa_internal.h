@@ -48,6 +48,9 @@ struct DecodeArgs {
   int32_t seg_extra;        // MODE_EVEN: balancing units per segment (see PlanIn)
   int32_t heads_per_wave;   // MODE_EVEN, vector kernel: query heads per wave (1, 2, 4, 8)
   int32_t odd_skew;         // MODE_EVEN: per mille of work moved from odd to even workgroups
+  int32_t max_rows;         // MODE_EVEN: query rows per sequence the decode kernel takes (1, or
+                            // 16 / G on the matrix-core path); longer sequences: chunk kernel
+  int32_t cols;             // MODE_EVEN, matrix-core path: query columns per partial slot
 };
 
 struct ReshapeArgs {

@@ -280,20 +280,23 @@ __device__ __forceinline__ void mfma_stream(const DecodeArgs& a, int s, int g, i
   }
 }
 
-// Write the first G query columns of a finished piece: the normalised output (to `out`,
-// column c at out_base + c * out_col_stride, or to a partial slot, column c at
-// po + c * po_col_stride), plus each column's max / sum for partial slots.  A column that
-// saw no key writes 0.
+// Write the first ncols query columns of a finished piece: the normalised output (to `out`,
+// column c at out_base + (c / group) * out_row_stride + (c % group) * out_col_stride, or to a
+// partial slot, column c at po + c * po_col_stride), plus each column's max / sum for partial
+// slots.  A column that saw no key writes 0.  (group = 16: column c at out_base + c * stride.)
 template <int DT, int D>
-__device__ __forceinline__ void mfma_emit(const MfmaState<DT, D>& st, int G, float* po, float* pm,
-                                          float* pl, int64_t po_col_stride, void* out,
-                                          int64_t out_base, int64_t out_col_stride, bool out_f32) {
+__device__ __forceinline__ void mfma_emit(const MfmaState<DT, D>& st, int ncols, float* po,
+                                          float* pm, float* pl, int64_t po_col_stride, void* out,
+                                          int64_t out_base, int group, int64_t out_row_stride,
+                                          int64_t out_col_stride, bool out_f32) {
   using C = MfmaCfg<DT, D>;
   const int lane = lane_id();
   const int r = lane >> 4, n = lane & 15;
   const float ltot = cross_rows_sum(st.l);  // sum of column n over the four lane rows
   const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-  if (n < G) {
+  if (n < ncols) {
+    const int64_t ocol = out_base + (int64_t)(n / group) * out_row_stride +
+                         (int64_t)(n % group) * out_col_stride;
 #pragma unroll
     for (int j = 0; j < C::NJ; ++j) {
       const int d = 16 * j + 4 * r;  // this lane's four consecutive dimensions
@@ -302,15 +305,13 @@ __device__ __forceinline__ void mfma_emit(const MfmaState<DT, D>& st, int G, flo
         *reinterpret_cast<f32x4_t*>(po + n * po_col_stride + d) = v;
       } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          store_out<DT>(out, out_base + (int64_t)n * out_col_stride + d + i, v[i], out_f32);
+        for (int i = 0; i < 4; ++i) store_out<DT>(out, ocol + d + i, v[i], out_f32);
       }
     }
   }
-  if (pm && r == 0 && n < G) {
+  if (pm && r == 0 && n < ncols) {
     pm[n * (po_col_stride / D)] = st.m * 0.69314718055994531f;
     pl[n * (po_col_stride / D)] = ltot;
   }
 }
-
 }  // namespace pa

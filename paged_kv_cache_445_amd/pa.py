@@ -21,7 +21,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 PA_F32, PA_F16, PA_BF16 = 0, 1, 2
 DTYPE_CODE = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
 STATUS = {0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_UNSUPPORTED",
-          -4: "PA_ERR_WORKSPACE", -5: "PA_ERR_HIP"}
+          -4: "PA_ERR_WORKSPACE", -5: "PA_ERR_HIP", -6: "PA_ERR_NO_BLOCKS"}
 
 
 class Geom(ctypes.Structure):

@@ -380,3 +380,69 @@ def test_spec_verify_mixed_with_decode_rows(dev):
     for dtype, Hq, Hkv in (("f16", 16, 16), ("bf16", 16, 4), ("bf16", 8, 1)):
         b = W.build_batch("verify_mix", dtype, prior + n, n, Hq, Hkv, 128, rng)
         parity(dev, b)
+
+
+# ----------------------------------------------------------------- block manager end to end
+
+@pytest.mark.parametrize("dtype,G", [("f16", 1), ("bf16", 4), ("f32", 2)])
+def test_block_manager_scenario(dev, dtype, G):
+    """Tables, slots and copy-on-write pairs from the host block manager (prefix hits,
+    forks, frees) replayed through pa_copy_blocks and pa_reshape_and_cache: pools bit-exact
+    with the oracle's replay, then pa_decode over the live sequences against the oracle."""
+    import torch
+    import oracle
+    from paged_kv_cache_445_amd import pa
+    from paged_kv_cache_445_amd.device_batch import TORCH_DTYPE, nan_fill_, to_device
+    from tests.bm_scenario import Scenario
+    from tests.test_block_manager import _replay_on_oracle
+    _log(f"[block_manager] {dtype} G={G}")
+    sc = Scenario(seed=7 + G)
+    H, D, NB, MB = sc.kv_heads, sc.head_dim, sc.bm.num_blocks, sc.bm.max_blocks_per_seq
+    X = 16 // W.ELEM_BYTES[dtype]
+    dt = TORCH_DTYPE[dtype]
+    kc = nan_fill_(torch.empty((NB, H, D // X, 16, X), dtype=dt, device="cuda"), dtype)
+    vc = nan_fill_(torch.empty((NB, H, D, 16), dtype=dt, device="cuda"), dtype)
+    ids = sc.seq_ids
+    S = len(ids)
+    g = pa.geom(S, H * G, H, D, NB, MB, dt, torch.float32)
+    for copies, slots, keys, vals in sc.steps:
+        if len(copies):
+            pa.copy_blocks(kc, vc, torch.from_numpy(copies).cuda(), g)
+        if len(slots):
+            pa.reshape_and_cache(to_device(W.to_storage(keys, dtype), dtype, "cuda"),
+                                 to_device(W.to_storage(vals, dtype), dtype, "cuda"), kc, vc,
+                                 torch.from_numpy(slots).cuda(), g)
+    kp, vp = _replay_on_oracle(sc, dtype)
+    for got, want in ((kc, kp), (vc, vp)):
+        c = got.cpu()
+        c = c.view(torch.int16).numpy() if dtype == "bf16" else c.numpy()
+        assert np.array_equal(c.view(np.uint8), want.view(np.uint8))
+    bt, lens = sc.bm.block_tables(ids, pad_block=0)
+    q = W.to_storage(np.random.default_rng(G).standard_normal((S, H * G, D)).astype(np.float32),
+                     dtype)
+    out = torch.zeros((S, H * G, D), dtype=torch.float32, device="cuda")
+    ws = torch.zeros(pa.workspace_size(g, S), dtype=torch.uint8, device="cuda")
+    scale = float(np.float32(1 / np.sqrt(D)))
+    pa.decode(out, to_device(q, dtype, "cuda"), kc, vc, torch.from_numpy(bt).cuda(),
+              torch.from_numpy(lens).cuda(), None, scale, ws, g)
+    torch.cuda.synchronize()
+    og = oracle.make_geom(S, H * G, H, D, NB, MB, dtype)
+    want, _ = oracle.paged_attention(q, kp, vp, bt, lens, None, scale, og)
+    check_out(out.cpu().numpy().astype(np.float64), want, TOL[dtype], "block manager")
+
+
+def test_spec_verify_long_split(dev):
+    """Verify rows on long contexts cut into many pieces by the even split, with contexts
+    whose last unit starts past the first rows' last keys (a piece may then hold no key of
+    some columns), for the GQA tile (4 rows x 4 heads) and the MHA tile (6 rows)."""
+    import torch
+    rng = np.random.default_rng(717)
+    prior = np.array([29999, 12001, 50, 7775, 20002, 1])
+    for dtype, Hq, Hkv, n in (("bf16", 16, 4, 4), ("f16", 8, 8, 6), ("bf16", 16, 2, 2)):
+        rows = np.full(len(prior), n)
+        b = W.build_batch("verify_long", dtype, prior + rows, rows, Hq, Hkv, 128, rng)
+        db, got, want = parity(dev, b)
+        for _ in range(3):
+            db.attend()
+            torch.cuda.synchronize()
+            assert np.array_equal(db.out_host(), got)
