@@ -16,7 +16,43 @@
 #include <string.h>
 #include <unistd.h>
 
-static int elem_bytes(int32_t dtype) { return dtype == PA_REF_F32 ? 4 : 2; }
+static int elem_bytes(int32_t dtype) {
+  return dtype == PA_REF_F32 ? 4 : dtype == PA_REF_FP8_E4M3 ? 1 : 2;
+}
+
+/* element type of q, key and value */
+static int32_t q_type(const pa_ref_geom* g) { return g->q_dtype >= 0 ? g->q_dtype : g->dtype; }
+
+/* ---------------------------------------------------------------- FP8 E4M3 */
+
+double pa_ref_fp8_decode(uint8_t code) {
+  const int sign = code >> 7, e = (code >> 3) & 15, m = code & 7;
+  double v;
+  if (e == 15 && m == 7)
+    v = NAN;
+  else if (e == 0)
+    v = ldexp((double)m, -9); /* subnormal: m/8 * 2^(1-7) */
+  else
+    v = ldexp(1.0 + m / 8.0, e - 7);
+  return sign ? -v : v;
+}
+
+uint8_t pa_ref_fp8_encode(float x) {
+  const uint8_t sign = signbit(x) ? 0x80 : 0x00;
+  if (isnan(x)) return sign | 0x7F;
+  const double a = fabs((double)x);
+  if (a >= 448.0) return sign | 0x7E; /* saturate at the largest finite value */
+  if (a < ldexp(1.0, -6)) {
+    /* subnormal range: multiples of 2^-9; nearbyint rounds half to even (default mode).
+     * m = 8 is the smallest normal number, whose code is 0x08 as well. */
+    return sign | (uint8_t)nearbyint(a * 512.0);
+  }
+  int e;
+  const double fr = frexp(a, &e); /* a = fr * 2^e, fr in [0.5, 1) */
+  const int E = e - 1;            /* a = (2 fr) * 2^E, 2 fr in [1, 2), E in [-6, 8] */
+  const int q = (int)nearbyint((2.0 * fr - 1.0) * 8.0); /* 3 fraction bits, 0..8 */
+  return sign | (uint8_t)(((E + 7) << 3) + q);          /* q = 8 carries into the exponent */
+}
 
 /* ---------------------------------------------------------------- element conversion */
 
@@ -47,6 +83,7 @@ static double load_elem(const void* base, int32_t dtype, int64_t idx) {
     memcpy(&f, (const char*)base + 4 * idx, 4);
     return (double)f;
   }
+  if (dtype == PA_REF_FP8_E4M3) return pa_ref_fp8_decode(((const uint8_t*)base)[idx]);
   uint16_t h;
   memcpy(&h, (const char*)base + 2 * idx, 2);
   return dtype == PA_REF_F16 ? f16_bits_to_double(h) : bf16_bits_to_double(h);
@@ -76,7 +113,10 @@ static int geom_ok(const pa_ref_geom* g) {
   if (!g || g->num_seqs < 0 || g->num_q_heads <= 0 || g->num_kv_heads <= 0 || g->head_dim <= 0 ||
       g->block_size <= 0 || g->num_blocks <= 0 || g->max_blocks_per_seq < 0)
     return 0;
-  if (g->dtype < PA_REF_F32 || g->dtype > PA_REF_BF16) return 0;
+  if (g->dtype < PA_REF_F32 || g->dtype > PA_REF_FP8_E4M3) return 0;
+  if (g->q_dtype >= 0 && g->q_dtype != g->dtype && g->dtype != PA_REF_FP8_E4M3) return 0;
+  if (g->dtype == PA_REF_FP8_E4M3 && (q_type(g) < PA_REF_F32 || q_type(g) > PA_REF_BF16)) return 0;
+  if (g->dtype == PA_REF_FP8_E4M3 && !(g->k_scale > 0.0 && g->v_scale > 0.0)) return 0;
   if (g->num_q_heads % g->num_kv_heads) return 0;
   if (g->head_dim % (16 / elem_bytes(g->dtype))) return 0;
   return 1;
@@ -99,10 +139,18 @@ int32_t pa_ref_reshape_and_cache(const void* key, const void* value, void* k_cac
     for (int32_t h = 0; h < g->num_kv_heads; ++h) {
       for (int32_t d = 0; d < g->head_dim; ++d) {
         const int64_t src = (i * g->num_kv_heads + h) * (int64_t)g->head_dim + d;
-        memcpy((char*)k_cache + e * pa_ref_k_offset(g, block, h, offset, d),
-               (const char*)key + e * src, e);
-        memcpy((char*)v_cache + e * pa_ref_v_offset(g, block, h, offset, d),
-               (const char*)value + e * src, e);
+        const int64_t ko = pa_ref_k_offset(g, block, h, offset, d);
+        const int64_t vo = pa_ref_v_offset(g, block, h, offset, d);
+        if (g->dtype == PA_REF_FP8_E4M3) {
+          /* quantise: the fp32 quotient by the pool's scale, rounded to E4M3 */
+          const float kq = (float)load_elem(key, q_type(g), src) / (float)g->k_scale;
+          const float vq = (float)load_elem(value, q_type(g), src) / (float)g->v_scale;
+          ((uint8_t*)k_cache)[ko] = pa_ref_fp8_encode(kq);
+          ((uint8_t*)v_cache)[vo] = pa_ref_fp8_encode(vq);
+        } else {
+          memcpy((char*)k_cache + e * ko, (const char*)key + e * src, e);
+          memcpy((char*)v_cache + e * vo, (const char*)value + e * src, e);
+        }
       }
     }
   }
@@ -169,12 +217,14 @@ static int find_row(const int32_t* context_lens, const int32_t* qsl, int32_t num
 /* Keys [t0, t1) of sequence s, KV head kvh: scores x[t - t0] = scale * q . k_t. */
 static void scores(double* x, const double* qv, const void* k_cache, const int32_t* bt_row,
                    int32_t kvh, int32_t t0, int32_t t1, double scale, const pa_ref_geom* g) {
+  const double kscale = g->dtype == PA_REF_FP8_E4M3 ? g->k_scale : 1.0;
   for (int32_t t = t0; t < t1; ++t) {
     const int64_t block = bt_row[t / g->block_size]; /* logical block -> physical block */
     const int32_t off = t % g->block_size;
     double dot = 0.0;
     for (int32_t d = 0; d < g->head_dim; ++d)
-      dot += qv[d] * load_elem(k_cache, g->dtype, pa_ref_k_offset(g, block, kvh, off, d));
+      dot += qv[d] * (load_elem(k_cache, g->dtype, pa_ref_k_offset(g, block, kvh, off, d)) *
+                      kscale);
     x[t - t0] = scale * dot;
   }
 }
@@ -184,6 +234,7 @@ static void softmax_v(double* out, double* m_out, double* l_out, const double* x
                       const void* v_cache, const int32_t* bt_row, int32_t kvh, int32_t t0,
                       int32_t n, const pa_ref_geom* g) {
   const int32_t D = g->head_dim;
+  const double vscale = g->dtype == PA_REF_FP8_E4M3 ? g->v_scale : 1.0;
   for (int32_t d = 0; d < D; ++d) out[d] = 0.0;
   if (n <= 0) {
     *m_out = -INFINITY;
@@ -203,7 +254,8 @@ static void softmax_v(double* out, double* m_out, double* l_out, const double* x
     const int64_t block = bt_row[t / g->block_size];
     const int32_t off = t % g->block_size;
     for (int32_t d = 0; d < D; ++d)
-      out[d] += w[i] * load_elem(v_cache, g->dtype, pa_ref_v_offset(g, block, kvh, off, d));
+      out[d] += w[i] * (load_elem(v_cache, g->dtype, pa_ref_v_offset(g, block, kvh, off, d)) *
+                        vscale);
   }
   for (int32_t d = 0; d < D; ++d) out[d] /= l;
   *m_out = m;
@@ -250,7 +302,7 @@ static void* run_job(void* arg) {
     const int32_t* bt_row = J->block_tables + (int64_t)ri.seq * g->max_blocks_per_seq;
     const int32_t kvh = h / grp; /* GQA: contiguous groups of query heads share a KV head */
     for (int32_t d = 0; d < D; ++d)
-      qv[d] = load_elem(J->q, g->dtype, ((int64_t)r * Hq + h) * D + d);
+      qv[d] = load_elem(J->q, q_type(g), ((int64_t)r * Hq + h) * D + d);
     const int32_t nkeys = ri.last_key >= 0 ? ri.last_key + 1 : 0;
     if (J->partition_size <= 0) {
       double m, l;

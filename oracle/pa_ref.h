@@ -36,6 +36,9 @@
  * The V layout is the pages' [num_blocks, num_heads, head_size, block_size] ([DD] §6.2);
  * K splits head_size into 16-byte chunks so that one token's chunk is 16 bytes.
  *
+ * FP8 pools (dtype PA_REF_FP8_E4M3): one byte per element, X = 16, the same layout; q, key
+ * and value keep q_dtype; a K / V element's value is decode(byte) * k_scale / v_scale.
+ *
  * Precision: every stored element is converted exactly to double; scores, the
  * softmax and the weighted sum are evaluated in double in ascending key order.
  */
@@ -47,7 +50,7 @@
 extern "C" {
 #endif
 
-enum { PA_REF_F32 = 0, PA_REF_F16 = 1, PA_REF_BF16 = 2 };
+enum { PA_REF_F32 = 0, PA_REF_F16 = 1, PA_REF_BF16 = 2, PA_REF_FP8_E4M3 = 3 };
 
 typedef struct {
   int32_t num_seqs;
@@ -57,8 +60,21 @@ typedef struct {
   int32_t block_size;
   int32_t num_blocks;
   int32_t max_blocks_per_seq; /* block_tables row stride */
-  int32_t dtype;              /* PA_REF_F32 / PA_REF_F16 / PA_REF_BF16: q, K, V, key, value */
+  int32_t dtype;              /* the pools' element type; also q, key, value unless q_dtype >= 0 */
+  int32_t q_dtype;            /* FP8 pools: element type of q, key and value; -1: dtype */
+  double k_scale;             /* FP8 pools: a stored K element means its decoded value * k_scale */
+  double v_scale;             /* ... and a stored V element its decoded value * v_scale */
 } pa_ref_geom;
+
+/* FP8 E4M3 (OCP "E4M3FN"): 1 sign, 4 exponent bits (bias 7), 3 mantissa bits, no infinity,
+ * S.1111.111 is NaN, largest finite 448.  Used for KV pools ("vLLM 深度拆解" §10.1 names FP8
+ * support with calibrated scales).  Readings: one scale per pool (per tensor); an element x
+ * is stored as encode(fp32(x) / fp32(scale)) with the quotient an IEEE fp32 division,
+ * rounded to the nearest E4M3 value, ties to even, magnitudes at or above 448 saturating to
+ * 448 and NaN staying NaN.
+ * decode: the exact value of a code; encode: the code of an fp32 value. */
+double pa_ref_fp8_decode(uint8_t code);
+uint8_t pa_ref_fp8_encode(float x);
 
 /* Element offset (in elements, not bytes) of K[block][kv_head][token][dim] / V[...]. */
 int64_t pa_ref_k_offset(const pa_ref_geom* g, int64_t block, int32_t kv_head, int32_t token, int32_t dim);

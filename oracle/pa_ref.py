@@ -12,7 +12,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libpa_ref.so")
 
-DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2}
+DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2, "fp8": 3}
 
 _i32p = ctypes.POINTER(ctypes.c_int32)
 _i64p = ctypes.POINTER(ctypes.c_int64)
@@ -24,7 +24,9 @@ class Geom(ctypes.Structure):
     _fields_ = [("num_seqs", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("block_size", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
-                ("max_blocks_per_seq", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("max_blocks_per_seq", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("q_dtype", ctypes.c_int32), ("k_scale", ctypes.c_double),
+                ("v_scale", ctypes.c_double)]
 
 
 _lib = None
@@ -47,6 +49,10 @@ def lib():
         L.pa_ref_reshape_and_cache.restype = ctypes.c_int32
         L.pa_ref_reshape_and_cache.argtypes = [_vp, _vp, _vp, _vp, _i64p, ctypes.c_int64,
                                                ctypes.POINTER(Geom)]
+        L.pa_ref_fp8_decode.restype = ctypes.c_double
+        L.pa_ref_fp8_decode.argtypes = [ctypes.c_uint8]
+        L.pa_ref_fp8_encode.restype = ctypes.c_uint8
+        L.pa_ref_fp8_encode.argtypes = [ctypes.c_float]
         L.pa_ref_copy_blocks.restype = ctypes.c_int32
         L.pa_ref_copy_blocks.argtypes = [_vp, _vp, _i64p, ctypes.c_int64, ctypes.POINTER(Geom)]
         L.pa_ref_paged_attention.restype = ctypes.c_int32
@@ -70,9 +76,11 @@ def lib():
 
 
 def make_geom(num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, max_blocks_per_seq,
-              dtype, block_size=16):
+              dtype, block_size=16, q_dtype=None, k_scale=1.0, v_scale=1.0):
+    """dtype: the pools' element type; q_dtype (FP8 pools): that of q, key and value."""
     return Geom(int(num_seqs), int(num_q_heads), int(num_kv_heads), int(head_dim),
-                int(block_size), int(num_blocks), int(max_blocks_per_seq), DTYPE_CODE[dtype])
+                int(block_size), int(num_blocks), int(max_blocks_per_seq), DTYPE_CODE[dtype],
+                -1 if q_dtype is None else DTYPE_CODE[q_dtype], float(k_scale), float(v_scale))
 
 
 def _ptr(a, t):
@@ -111,6 +119,14 @@ def reshape_and_cache(key, value, k_pool, v_pool, slot_mapping, g):
                                         ctypes.byref(g))
     if rc != 0:
         raise ValueError("oracle reshape_and_cache: slot outside the pool")
+
+
+def fp8_decode(code: int) -> float:
+    return float(lib().pa_ref_fp8_decode(int(code)))
+
+
+def fp8_encode(x: float) -> int:
+    return int(lib().pa_ref_fp8_encode(float(x)))
 
 
 def copy_blocks(k_pool, v_pool, block_mapping, g):

@@ -501,3 +501,90 @@ def test_copy_on_write_fork_keeps_attention_bitwise():
     oracle.copy_blocks(kp, vp, np.array([[b.block_tables[0, nblk - 1], free[0]]]), H.geom(c))
     out, lse = H.oracle_attention(c, kp, vp)
     assert np.array_equal(out[2], out[0]) and np.array_equal(lse[2], lse[0])
+
+
+# ----------------------------------------------------------------- FP8 E4M3 pools
+
+def test_fp8_decode_all_codes_match_torch():
+    """The oracle's E4M3 decode of all 256 codes equals torch's float8_e4m3fn (NaN for
+    S.1111.111, no infinities, 448 the largest value)."""
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    want = codes.view(torch.float8_e4m3fn).double().numpy()
+    got = np.array([oracle.fp8_decode(c) for c in range(256)])
+    np.testing.assert_array_equal(got, want)
+    assert oracle.fp8_decode(0x7E) == 448.0 and oracle.fp8_decode(0x01) == 2.0 ** -9
+
+
+def test_fp8_encode_matches_torch_in_range_and_saturates():
+    """Encoding every finite fp16 value below 448 in magnitude (round to nearest, ties to
+    even: fp16 holds every E4M3 midpoint) equals torch's conversion; larger magnitudes
+    saturate to 448 (the reading taken), NaN stays NaN."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    x = bits.view(np.float16).astype(np.float32)
+    fin = np.isfinite(x) & (np.abs(x) < 448)
+    want = torch.from_numpy(x[fin]).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([oracle.fp8_encode(v) for v in x[fin]], dtype=np.uint8)
+    np.testing.assert_array_equal(got, want)
+    for v, code in ((448.0, 0x7E), (449.0, 0x7E), (1e6, 0x7E), (-1e30, 0xFE), (-448.0, 0xFE)):
+        assert oracle.fp8_encode(v) == code
+    assert oracle.fp8_encode(float("nan")) & 0x7F == 0x7F
+    # round trip of every finite code
+    for c in range(256):
+        if c & 0x7F != 0x7F:
+            assert oracle.fp8_encode(oracle.fp8_decode(c)) == c
+
+
+def _fp8_batch(seed, ctx, Hq, Hkv, D, k_scale, v_scale):
+    rng = np.random.default_rng(seed)
+    b = W.build_batch("fp8", "f16", ctx, np.ones(len(ctx)), Hq, Hkv, D, rng)
+    g = oracle.make_geom(b.num_seqs, Hq, Hkv, D, b.num_blocks, b.max_blocks_per_seq, "fp8",
+                         q_dtype="f16", k_scale=k_scale, v_scale=v_scale)
+    kp = np.full((b.num_blocks, Hkv, D // 16, 16, 16), 0x7F, dtype=np.uint8)
+    vp = np.full((b.num_blocks, Hkv, D, 16), 0x7F, dtype=np.uint8)
+    oracle.reshape_and_cache(b.key, b.value, kp, vp, b.slot, g)
+    return b, g, kp, vp
+
+
+def test_fp8_reshape_stores_scaled_codes_at_declared_positions():
+    """FP8 pools: K [NB][Hkv][D/16][16][16] and V [NB][Hkv][D][16] bytes; every written
+    element is the code of fp32(x) / fp32(scale), placed by numpy's ravel over those shapes;
+    untouched bytes keep the NaN code."""
+    ks, vs = np.float32(6.0 / 448), np.float32(5.5 / 448)
+    b, g, kp, vp = _fp8_batch(41, [37, 5, 16], 4, 2, 64, ks, vs)
+    D, H = 64, 2
+    written = np.zeros(kp.shape, bool), np.zeros(vp.shape, bool)
+    x = W.storage_to_float32(b.key, "f16")
+    y = W.storage_to_float32(b.value, "f16")
+    for t in range(len(b.slot)):
+        blk, off = divmod(int(b.slot[t]), 16)
+        for h in range(H):
+            for d in range(D):
+                kc = kp[blk, h, d // 16, off, d % 16]
+                vc = vp[blk, h, d, off]
+                assert kc == oracle.fp8_encode(np.float32(x[t, h, d]) / ks)
+                assert vc == oracle.fp8_encode(np.float32(y[t, h, d]) / vs)
+                written[0][blk, h, d // 16, off, d % 16] = True
+                written[1][blk, h, d, off] = True
+    assert (kp[~written[0]] == 0x7F).all() and (vp[~written[1]] == 0x7F).all()
+
+
+def test_fp8_attention_matches_torch_sdpa_on_dequantised_values():
+    """Attention over FP8 pools equals torch's fp64 attention over the decoded values times
+    the scales (GQA groups included)."""
+    ks, vs = np.float32(6.0 / 448), np.float32(5.5 / 448)
+    b, g, kp, vp = _fp8_batch(43, [1, 70, 200], 8, 2, 128, ks, vs)
+    out, _ = oracle.paged_attention(b.q, kp, vp, b.block_tables, b.context_lens, None, b.scale,
+                                    g)
+    lut = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn)
+    lut = lut.double().numpy()
+    q = H.q_f64(b)
+    for s in range(b.num_seqs):
+        n = int(b.context_lens[s])
+        tok = np.arange(n)
+        blk = b.block_tables[s, tok // 16]
+        # [n, Hkv, D/16, 16] -> [Hkv, n, D]
+        k = lut[kp[blk, :, :, tok % 16, :]].reshape(n, 2, 128).transpose(1, 0, 2) * float(ks)
+        v = lut[vp[blk, :, :, tok % 16]].transpose(1, 0, 2) * float(vs)
+        want = _sdpa(np.ascontiguousarray(q[s][:, None, :]), np.ascontiguousarray(k),
+                     np.ascontiguousarray(v), float(b.scale), gqa=True)
+        np.testing.assert_allclose(out[s], want[:, 0, :], rtol=0, atol=1e-12)
