@@ -47,6 +47,9 @@ DESCRIPTIONS = {
     "mixed_chunked_bf16": "mixed step: 8 x 512-row causal chunks + 120 decode rows, 32 q / 8 kv "
                           "heads, head_dim 128, bf16 KV",
     "tiny_f32": "tiny decode: 4 seqs x 4 heads, head_dim 64, fp32 KV",
+    "llama7b_fp8": "LLaMA-7B-shaped decode with FP8 E4M3 KV (per-pool scales 6.5/448): 32 seqs "
+                   "x 32 heads (MHA), head_dim 128, fp16 q, block 16, ctx U[256,2048], "
+                   "8192-block pool, permuted block table",
     "spec_verify_f16": "speculative verify step: 32 seqs x 6 causal rows (last token + 5 "
                        "drafts) x 32 heads (MHA), head_dim 128, fp16 KV, prior ctx U[256,2048]",
     "spec_verify_gqa_bf16": "speculative verify step: 64 seqs x 4 causal rows, 32 q / 8 kv "
@@ -102,10 +105,12 @@ def cpu_baseline(b, min_seconds, threads, max_key_heads=3e8):
     import numpy as np
     import oracle
     from paged_kv_cache_445_amd import workloads as W
+    fp8 = b.pool_dtype == "fp8"
     g = oracle.make_geom(b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim, b.num_blocks,
-                         b.max_blocks_per_seq, b.dtype, b.block_size)
-    kp = W.nan_pool(b.k_pool_shape(), b.dtype)
-    vp = W.nan_pool(b.v_pool_shape(), b.dtype)
+                         b.max_blocks_per_seq, b.pool_dtype, b.block_size,
+                         q_dtype=b.dtype if fp8 else None, k_scale=b.k_scale, v_scale=b.v_scale)
+    kp = W.nan_pool(b.k_pool_shape(), b.pool_dtype)
+    vp = W.nan_pool(b.v_pool_shape(), b.pool_dtype)
     oracle.reshape_and_cache(b.key, b.value, kp, vp, b.slot, g)
     keys = row_keys(b)
     total = float(keys.sum()) * b.num_q_heads
@@ -358,7 +363,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16" if b.dtype == "f16" else b.dtype,
+        "dtype": "fp8_e4m3 KV, f16 q" if b.pool_dtype == "fp8" else b.dtype,
         "data": "synthetic",
         "config": {
             "workload": args.workload,
@@ -366,7 +371,7 @@ def main():
             "num_seqs": b.num_seqs, "num_q_rows": b.num_q_rows,
             "num_q_heads": b.num_q_heads, "num_kv_heads": b.num_kv_heads,
             "head_dim": b.head_dim, "block_size": b.block_size,
-            "kv_dtype": b.dtype, "accumulate": "f32",
+            "kv_dtype": b.pool_dtype, "accumulate": "f32",
             "context_tokens": int(b.context_lens.astype(np.int64).sum()),
             "kv_bytes_per_step": kv_bytes,
             "kv_unique_bytes_per_step": hbm_bytes,

@@ -20,7 +20,8 @@
  *     Device-resident values (block ids < num_blocks, context_lens <= max_blocks_per_seq
  *     * block_size, unique slots) are the caller's contract and are not checked.
  *   - block_size is 16 ("vLLM 架构源码解析 第1篇" §4.2: 16-token blocks).  head_dim is 64 or 128.
- *     kv_dtype is PA_F32, PA_F16 or PA_BF16; q, key, value and both pools share it.
+ *     kv_dtype is PA_F32, PA_F16 or PA_BF16 (q, key, value and both pools share it), or
+ *     PA_FP8_E4M3 (see "FP8 pools").
  *
  * Pool layout (part of this ABI).  elem = 4 (fp32) or 2 bytes, X = 16 / elem:
  *   k_cache: [num_blocks][num_kv_heads][head_dim / X][block_size][X]
@@ -28,6 +29,15 @@
  * v_cache is the pages' [num_blocks, num_heads, head_size, block_size] ("vLLM 深度拆解"
  * §6.2); k_cache splits head_size into 16-byte chunks so one token's chunk is one 16-byte
  * load and the 16 tokens of a chunk are 256 contiguous bytes.
+ *
+ * FP8 pools ("vLLM 深度拆解" §10.1 names FP8 KV with calibrated scales).  kv_dtype
+ * PA_FP8_E4M3: one byte per element in the layout above with elem = 1, X = 16; q, key and
+ * value are fp16 (q_dtype PA_F16), out is fp16 or fp32.  Each pool has one scale:
+ * reshape_and_cache stores e4m3(fp32(x) / scale), the fp32 quotient rounded to the nearest
+ * E4M3 ("E4M3FN": bias 7, no infinity, largest 448) with ties to even, magnitudes from 448
+ * up saturating to 448; attention reads an element as its E4M3 value times the scale.
+ * Supported by pa_reshape_and_cache, pa_copy_blocks and pa_decode (one row per sequence);
+ * pa_decode with query_start_loc and pa_decode_partitioned return PA_ERR_UNSUPPORTED.
  *
  * Rows and positions.  query_start_loc ("vLLM 架构源码解析 第1篇" §3.3.2) is NULL when every sequence has one
  * query row (row r belongs to sequence r, num_q_rows == num_seqs), else an int32 [S + 1]
@@ -46,7 +56,7 @@
 extern "C" {
 #endif
 
-typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2, PA_FP8_E4M3 = 3 } pa_dtype;
 
 typedef enum {
   PA_OK = 0,
@@ -67,8 +77,11 @@ typedef struct {
   int32_t block_size;         /* tokens per physical block: 16 */
   int32_t num_blocks;         /* NB: blocks in each pool */
   int32_t max_blocks_per_seq; /* MB: row stride of block_tables */
-  int32_t kv_dtype;           /* pa_dtype of q, key, value, k_cache, v_cache */
-  int32_t out_dtype;          /* pa_dtype of out: kv_dtype or PA_F32 */
+  int32_t kv_dtype;           /* pa_dtype of k_cache, v_cache (and of q, key, value unless FP8) */
+  int32_t out_dtype;          /* pa_dtype of out: q_dtype or PA_F32 */
+  int32_t q_dtype;            /* pa_dtype of q, key, value: kv_dtype, or PA_F16 for FP8 pools */
+  float k_scale;              /* FP8 pools: stored K = e4m3(fp32(key) / k_scale); else ignored */
+  float v_scale;              /* FP8 pools: stored V = e4m3(fp32(value) / v_scale); else ignored */
 } pa_geom;
 
 /* Bytes of one pool (K or V): num_blocks * num_kv_heads * head_dim * block_size * elem.

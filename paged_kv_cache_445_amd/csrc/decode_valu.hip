@@ -36,11 +36,14 @@ template <int DT, int D>
 struct VCfg {
   static constexpr int E = DtInfo<DT>::bytes;
   static constexpr int X = DtInfo<DT>::x;
+  static constexpr int QE = DtInfo<DT>::qbytes;  // query element bytes
   static constexpr int TILE = 16 * D * E;  // bytes of one K or V tile
   static constexpr int NK = TILE / 1024;   // K loads per lane per tile
   static constexpr int NV = TILE / 1024;   // V loads per lane per tile
-  static constexpr int LPD = 16 * E / 16;  // lanes sharing one V dimension row
+  static constexpr int LPD = 16 * E / 16;  // lanes sharing one V dimension row (>= 1)
   static constexpr int DPL = 64 / LPD;     // dimensions covered by one V load
+  static constexpr int NQC = X * QE / 16;  // 16-byte query pieces per K chunk
+  static constexpr int NQ = NK * NQC;      // 16-byte query pieces per head and lane
 };
 
 template <int DT, int D>
@@ -96,6 +99,17 @@ __device__ __forceinline__ void mask_piece(uint4& v, int first_token, int valid)
   v.w &= m[3];
 }
 
+// FP8 V piece: the 16 tokens of one dimension row as two chunks of 8 fp16 values (2^-8 times
+// the stored values), with the tokens >= valid zeroed (MASK).
+template <bool MASK>
+__device__ __forceinline__ void fp8_v_piece(const uint4& v, uint4& h0, uint4& h1, int valid) {
+  fp8x16_to_f16(v, h0, h1);
+  if (MASK) {
+    mask_piece<DT_F16>(h0, 0, valid);
+    mask_piece<DT_F16>(h1, 8, valid);
+  }
+}
+
 // One 16-token tile.  MASK: only tokens < valid exist.
 template <int DT, int D, bool MASK>
 __device__ __forceinline__ void v_tile(VState<DT, D>& st, VTile<DT, D>& t, const uint4* qv,
@@ -103,8 +117,20 @@ __device__ __forceinline__ void v_tile(VState<DT, D>& st, VTile<DT, D>& t, const
   using C = VCfg<DT, D>;
   const int lane = lane_id();
   float part = 0.f;
+  if constexpr (DT == DT_FP8) {
+    // each 16-byte K chunk is 16 E4M3 values: widen to fp16 (2^-8 times the value; the
+    // score factor restores it) and dot with the chunk's 16 fp16 query elements
 #pragma unroll
-  for (int i = 0; i < C::NK; ++i) part = dot16<DT>(t.k[i], qv[i], part);
+    for (int i = 0; i < C::NK; ++i) {
+      uint4 h0, h1;
+      fp8x16_to_f16(t.k[i], h0, h1);
+      part = dot16<DT_F16>(h0, qv[2 * i], part);
+      part = dot16<DT_F16>(h1, qv[2 * i + 1], part);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < C::NK; ++i) part = dot16<DT>(t.k[i], qv[i], part);
+  }
   float sc = cross_rows_sum(part) * scale_log2;
   if (MASK && (lane & 15) >= valid) sc = -INFINITY;
   const float mnew = fmaxf(st.m, row16_max(sc));
@@ -127,10 +153,19 @@ __device__ __forceinline__ void v_tile(VState<DT, D>& st, VTile<DT, D>& t, const
   __builtin_amdgcn_wave_barrier();
 #pragma unroll
   for (int j = 0; j < C::NV; ++j) {
-    if (MASK) mask_piece<DT>(t.v[j], C::X * g, valid);
     float a = st.acc[j] * alpha;
+    if constexpr (DT == DT_FP8) {
+      uint4 h0, h1;
+      fp8_v_piece<MASK>(t.v[j], h0, h1, valid);
 #pragma unroll
-    for (int k = 0; k < C::X; ++k) a = fmaf(w[k], v_elem<DT>(t.v[j], k), a);
+      for (int k = 0; k < 8; ++k) a = fmaf(w[k], elem16<DT_F16>(h0, k), a);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) a = fmaf(w[8 + k], elem16<DT_F16>(h1, k), a);
+    } else {
+      if (MASK) mask_piece<DT>(t.v[j], C::X * g, valid);
+#pragma unroll
+      for (int k = 0; k < C::X; ++k) a = fmaf(w[k], v_elem<DT>(t.v[j], k), a);
+    }
     st.acc[j] = a;
   }
 }
@@ -147,7 +182,7 @@ struct VPiece {
 template <int DT, int D, int HPW>
 struct VStart {
   int win0, win1;  // entries t0 + lane and t0 + 64 + lane of the block table
-  uint4 q[HPW][VCfg<DT, D>::NK];
+  uint4 q[HPW][VCfg<DT, D>::NQ];
   VTile<DT, D> first;
 };
 
@@ -177,9 +212,13 @@ __device__ __forceinline__ void v_start(const DecodeArgs& a, const VPiece& p,
 #pragma unroll
   for (int j = 0; j < HPW; ++j) {
     const char* qp = reinterpret_cast<const char*>(a.q) +
-                     ((int64_t)row * a.num_q_heads + p.h0 + 4 * j) * D * C::E;
+                     ((int64_t)row * a.num_q_heads + p.h0 + 4 * j) * D * C::QE;
+    // the query elements of this lane's K chunks 4 i + lane / 16 (X elements each)
 #pragma unroll
-    for (int i = 0; i < C::NK; ++i) vs.q[j][i] = ld16(qp + 16 * (4 * i + (lane >> 4)));
+    for (int i = 0; i < C::NK; ++i)
+#pragma unroll
+      for (int c = 0; c < C::NQC; ++c)
+        vs.q[j][C::NQC * i + c] = ld16(qp + C::X * C::QE * (4 * i + (lane >> 4)) + 16 * c);
   }
   const int64_t blk = readlane(vs.win0, 0);
   const int64_t off = blk * a.num_kv_heads * C::TILE;
@@ -286,14 +325,17 @@ __device__ void valu_run(const DecodeArgs& a, VPiece p, VStart<DT, D, HPW>& vs,
 }
 
 // Finish a piece: combine the lanes of each dimension row and the per-token sums; returns
-// the total l (every lane).  Afterwards every lane holds full sums for its dimensions.
+// the total l (every lane).  Afterwards every lane holds full sums for its dimensions.  FP8
+// pools: the sums are also multiplied by vfac (256 * v_scale: the widened V values are 2^-8
+// times the stored ones, which stand for the stored value times v_scale).
 template <int DT, int D>
-__device__ __forceinline__ float v_finish(VState<DT, D>& st) {
+__device__ __forceinline__ float v_finish(VState<DT, D>& st, float vfac) {
   using C = VCfg<DT, D>;
 #pragma unroll
   for (int j = 0; j < C::NV; ++j) {
-    st.acc[j] += dpp_mov<0xB1>(st.acc[j]);    // quad_perm [1,0,3,2]: partner lane ^ 1
+    if constexpr (C::LPD >= 2) st.acc[j] += dpp_mov<0xB1>(st.acc[j]);  // [1,0,3,2]: lane ^ 1
     if constexpr (C::LPD == 4) st.acc[j] += dpp_mov<0x4E>(st.acc[j]);  // [2,3,0,1]: ^ 2
+    if constexpr (DT == DT_FP8) st.acc[j] *= vfac;
   }
   return row16_sum(st.l);
 }
@@ -468,7 +510,7 @@ __global__ __launch_bounds__(kWG) void valu_decode_kernel(DecodeArgs a) {
           valu_run<DT, D, HPW>(a, cur.p, vs, st, pw);
           float l[HPW];
 #pragma unroll
-          for (int j = 0; j < HPW; ++j) l[j] = v_finish<DT, D>(st[j]);
+          for (int j = 0; j < HPW; ++j) l[j] = v_finish<DT, D>(st[j], a.v_factor);
           if (whole) {
 #pragma unroll
             for (int j = 0; j < HPW; ++j)
@@ -522,7 +564,7 @@ __global__ __launch_bounds__(kWG) void valu_decode_kernel(DecodeArgs a) {
       v_window(a, pc, vs.win0, vs.win1);
       v_start<DT, D, 1>(a, pc, vs);
       valu_run<DT, D, 1>(a, pc, vs, st, pw);
-      const float l = v_finish<DT, D>(st[0]);
+      const float l = v_finish<DT, D>(st[0], a.v_factor);
       const float inv = 1.f / l;
       const int64_t e = ((int64_t)s * a.num_q_heads + h) * P + p;
       v_store_f32<DT, D>(st[0], inv, a.part_o + e * D);
@@ -566,10 +608,12 @@ static hipError_t launch_d(const DecodeArgs& a, int grid, hipStream_t st) {
   return hipGetLastError();
 }
 
+// FP8 pools run in MODE_EVEN only (pa_decode_partitioned rejects them)
 hipError_t launch_valu_decode(int dt, int mode, const DecodeArgs& a, int grid, hipStream_t st) {
   if (mode == MODE_EVEN) {
     if (dt == DT_F32) return launch_d<DT_F32, MODE_EVEN>(a, grid, st);
     if (dt == DT_F16) return launch_d<DT_F16, MODE_EVEN>(a, grid, st);
+    if (dt == DT_FP8) return launch_d<DT_FP8, MODE_EVEN>(a, grid, st);
     return launch_d<DT_BF16, MODE_EVEN>(a, grid, st);
   }
   if (dt == DT_F32) return launch_d<DT_F32, MODE_PARTITION>(a, grid, st);
@@ -606,6 +650,7 @@ int valu_decode_max_blocks_per_cu(int dt, int head_dim, int hpw, int mode, int l
   if (mode == MODE_EVEN) {
     if (dt == DT_F32) return occ<DT_F32, MODE_EVEN>(head_dim, hpw, lds);
     if (dt == DT_F16) return occ<DT_F16, MODE_EVEN>(head_dim, hpw, lds);
+    if (dt == DT_FP8) return occ<DT_FP8, MODE_EVEN>(head_dim, hpw, lds);
     return occ<DT_BF16, MODE_EVEN>(head_dim, hpw, lds);
   }
   if (dt == DT_F32) return occ<DT_F32, MODE_PARTITION>(head_dim, 1, lds);

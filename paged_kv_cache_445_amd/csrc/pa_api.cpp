@@ -19,7 +19,7 @@ namespace {
 constexpr int kMaxSeqs = 8192;  // the split kernels keep one int per sequence in LDS
 constexpr int kMaxDevices = 64;
 
-size_t elem_bytes(int dt) { return dt == PA_F32 ? 4 : 2; }
+size_t elem_bytes(int dt) { return dt == PA_F32 ? 4 : dt == PA_FP8_E4M3 ? 1 : 2; }
 
 bool dtype_ok(int dt) { return dt == PA_F32 || dt == PA_F16 || dt == PA_BF16; }
 
@@ -29,8 +29,16 @@ pa_status check_geom(const pa_geom* g) {
       g->block_size <= 0 || g->num_blocks <= 0 || g->max_blocks_per_seq <= 0)
     return PA_ERR_SHAPE;
   if (g->num_q_heads % g->num_kv_heads) return PA_ERR_SHAPE;
-  if (!dtype_ok(g->kv_dtype) || !dtype_ok(g->out_dtype)) return PA_ERR_UNSUPPORTED;
-  if (g->out_dtype != g->kv_dtype && g->out_dtype != PA_F32) return PA_ERR_UNSUPPORTED;
+  if (g->kv_dtype == PA_FP8_E4M3) {
+    if (g->q_dtype != PA_F16) return PA_ERR_UNSUPPORTED;
+    if (!(std::isfinite(g->k_scale) && g->k_scale > 0.f && std::isfinite(g->v_scale) &&
+          g->v_scale > 0.f))
+      return PA_ERR_SHAPE;
+  } else if (g->q_dtype != g->kv_dtype) {
+    return dtype_ok(g->kv_dtype) ? PA_ERR_SHAPE : PA_ERR_UNSUPPORTED;
+  }
+  if (!dtype_ok(g->q_dtype) || !dtype_ok(g->out_dtype)) return PA_ERR_UNSUPPORTED;
+  if (g->out_dtype != g->q_dtype && g->out_dtype != PA_F32) return PA_ERR_UNSUPPORTED;
   if (g->block_size != pa::kBlock) return PA_ERR_UNSUPPORTED;
   if (g->head_dim != 64 && g->head_dim != 128) return PA_ERR_UNSUPPORTED;
   if (g->num_q_heads / g->num_kv_heads > 16) return PA_ERR_UNSUPPORTED;
@@ -91,7 +99,7 @@ int odd_skew() {
 }
 
 bool use_mfma(const pa_geom* g) {
-  return g->kv_dtype != PA_F32 && g->num_q_heads / g->num_kv_heads >= 2;
+  return (g->kv_dtype == PA_F16 || g->kv_dtype == PA_BF16) && g->num_q_heads / g->num_kv_heads >= 2;
 }
 
 // Which decode kernel runs a pa_decode call, and which sequences it takes.
@@ -111,7 +119,8 @@ struct Route {
 Route route(const pa_geom* g, bool multi_row, int32_t num_q_rows) {
   const int G = g->num_q_heads / g->num_kv_heads;
   if (use_mfma(g)) return {1, multi_row ? 16 / G : 1, multi_row ? 16 / G * G : G};
-  if (g->kv_dtype != PA_F32 && multi_row && num_q_rows > g->num_seqs) return {1, 16, 16};
+  if ((g->kv_dtype == PA_F16 || g->kv_dtype == PA_BF16) && multi_row && num_q_rows > g->num_seqs)
+    return {1, 16, 16};
   return {0, 1, 1};
 }
 
@@ -157,7 +166,7 @@ int hpw_index(int hpw) { return hpw == 8 ? 3 : hpw == 4 ? 2 : hpw == 2 ? 1 : 0; 
 
 // workgroups of the split kernel: every CU full at the kernel's occupancy
 int split_grid(const pa_geom* g, int mode, int path) {
-  static std::atomic<int> cache[kMaxDevices][2][3][2][2][4][15];
+  static std::atomic<int> cache[kMaxDevices][2][4][2][2][4][15];
   const int dev = current_device();
   const int di = g->head_dim == 64 ? 0 : 1;
   const int bk = seq_bucket(g->num_seqs);
@@ -263,7 +272,7 @@ pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_cache
   const int64_t threads = num_tokens * g->num_kv_heads * (g->head_dim / X + g->head_dim);
   if ((threads + 255) / 256 > 0x7fffffffLL) return PA_ERR_SHAPE;
   pa::ReshapeArgs a{key, value, k_cache, v_cache, slot_mapping, num_tokens, g->num_kv_heads,
-                    g->head_dim};
+                    g->head_dim, g->k_scale, g->v_scale};
   return hip_status(pa::launch_reshape(g->kv_dtype, a, (hipStream_t)stream));
 }
 
@@ -306,7 +315,8 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_NULL;
   if (!std::isfinite(scale)) return PA_ERR_SHAPE;
   const int G = g->num_q_heads / g->num_kv_heads;
-  if (query_start_loc && (g->kv_dtype == PA_F32 || 16 % G != 0)) return PA_ERR_UNSUPPORTED;
+  if (query_start_loc && (g->kv_dtype == PA_F32 || g->kv_dtype == PA_FP8_E4M3 || 16 % G != 0))
+    return PA_ERR_UNSUPPORTED;
   hipStream_t st = (hipStream_t)stream;
 
   const Route rt = route(g, query_start_loc != nullptr, num_q_rows);
@@ -338,6 +348,11 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   a.max_blocks_per_seq = g->max_blocks_per_seq;
   a.out_f32 = g->out_dtype == PA_F32 && g->kv_dtype != PA_F32;
   a.scale_log2 = scale_to_log2(scale);
+  if (g->kv_dtype == PA_FP8_E4M3) {
+    // the kernel widens E4M3 to fp16 at 2^-8 times the value (see decode_valu.hip)
+    a.scale_log2 *= g->k_scale * 256.f;
+    a.v_factor = g->v_scale * 256.f;
+  }
   a.seg_extra = seg_extra_override() >= 0 ? seg_extra_override() : kSegExtra[rt.path];
   a.heads_per_wave = rt.path == 0 ? heads_per_wave(g) : 1;
   a.odd_skew = odd_skew();
@@ -374,6 +389,7 @@ pa_status pa_decode_partitioned(float* tmp_out, float* max_logits, float* exp_su
   const pa_status gs = check_geom(g);
   if (gs != PA_OK) return gs;
   if (num_q_rows != g->num_seqs) return PA_ERR_SHAPE;
+  if (g->kv_dtype == PA_FP8_E4M3) return PA_ERR_UNSUPPORTED;
   if (partition_size <= 0 || partition_size % pa::kMfmaUnit || max_partitions <= 0)
     return PA_ERR_SHAPE;
   if ((int64_t)max_partitions * partition_size < (int64_t)g->max_blocks_per_seq * g->block_size)
@@ -415,6 +431,7 @@ pa_status pa_decode_reduce(void* out, const float* tmp_out, const float* max_log
   const pa_status gs = check_geom(g);
   if (gs != PA_OK) return gs;
   if (num_q_rows < 0 || max_partitions <= 0) return PA_ERR_SHAPE;
+  if (g->kv_dtype == PA_FP8_E4M3) return PA_ERR_UNSUPPORTED;
   if (num_q_rows == 0) return PA_OK;
   if (!out || !tmp_out || !max_logits || !exp_sums) return PA_ERR_NULL;
   pa::PartReduceArgs a{};

@@ -18,8 +18,9 @@ namespace pa {
 
 template <int DT>
 struct DtInfo {
-  static constexpr int bytes = DT == DT_F32 ? 4 : 2;
+  static constexpr int bytes = DT == DT_F32 ? 4 : DT == DT_FP8 ? 1 : 2;  // pool element
   static constexpr int x = 16 / bytes;  // elements per 16-byte chunk
+  static constexpr int qbytes = DT == DT_F32 ? 4 : 2;  // query / key / value / out element
 };
 
 typedef __attribute__((ext_vector_type(2))) _Float16 half2_t;
@@ -55,6 +56,54 @@ __device__ __forceinline__ float elem16(const uint4& v, int k) {
     return (k & 1) ? f16_hi(w) : f16_lo(w);
 }
 
+// ---------------------------------------------------------------- FP8 E4M3
+//
+// E4M3 ("E4M3FN": bias 7, 3 fraction bits, no infinity, largest finite 448).  Widening to
+// fp16 moves the 7 magnitude bits under the fp16 exponent field: the fp16 number with
+// exponent field e and fraction m << 7 is 2^(e-15) (1 + m/8) = 2^-8 * 2^(e-7) (1 + m/8), and
+// for e = 0 the fp16 subnormal (m << 7) * 2^-24 = 2^-8 * m * 2^-9 -- so the widened value is
+// exactly 2^-8 times the E4M3 value, for every finite code.  The kernels carry the 2^8 in
+// their score and output factors.
+//
+// Four E4M3 bytes of w -> two fp16 pairs (bytes 0, 1 -> lo; bytes 2, 3 -> hi), each 2^-8 times
+// the byte's value.
+__device__ __forceinline__ void fp8x4_to_f16x4(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  // each byte into the high byte of a 16-bit half: a = (b1 << 24) | (b0 << 8), b likewise
+  const uint32_t a = ((w & 0xFFu) << 8) | ((w & 0xFF00u) << 16);
+  const uint32_t b = ((w >> 8) & 0xFF00u) | (w & 0xFF000000u);
+  // sign stays at bit 15; the 7 magnitude bits move down by one, to bits 7..13
+  lo = ((a >> 1) & 0x3F803F80u) | (a & 0x80008000u);
+  hi = ((b >> 1) & 0x3F803F80u) | (b & 0x80008000u);
+}
+
+// the 16 E4M3 bytes of a chunk as 16 fp16 values (two chunks of 8), each 2^-8 times its value
+__device__ __forceinline__ void fp8x16_to_f16(const uint4& v, uint4& h0, uint4& h1) {
+  fp8x4_to_f16x4(v.x, h0.x, h0.y);
+  fp8x4_to_f16x4(v.y, h0.z, h0.w);
+  fp8x4_to_f16x4(v.z, h1.x, h1.y);
+  fp8x4_to_f16x4(v.w, h1.z, h1.w);
+}
+
+// The E4M3 code of an fp32 value: round to nearest, ties to even; magnitudes from 448 up
+// saturate to 448, NaN stays NaN.  Bit arithmetic on the fp32 encoding.
+__device__ __forceinline__ uint32_t f32_to_fp8(float f) {
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return sign | 0x7Fu;  // NaN
+  if (a >= 0x43E00000u) return sign | 0x7Eu;  // >= 448 (and infinity): saturate
+  if (a < 0x3C800000u) {                      // below 2^-6: multiples of 2^-9
+    // a * 2^9 is exact (a power-of-two factor); rintf rounds half to even; 8 is the
+    // smallest normal number, code 0x08
+    return sign | (uint32_t)rintf(__uint_as_float(a) * 512.0f);
+  }
+  const uint32_t e = (a >> 23) - 127 + 7;    // biased E4M3 exponent, 1..15
+  uint32_t q = (a >> 20) & 7u;                // top three fraction bits
+  const uint32_t rest = a & 0xFFFFFu;         // the 20 bits below them
+  if (rest > 0x80000u || (rest == 0x80000u && (q & 1u))) ++q;  // to nearest, ties to even
+  return sign | ((e << 3) + q);               // q = 8 carries into the exponent
+}
+
 // dot of two 16-byte chunks (8 x 16-bit or 4 x fp32), accumulated in fp32
 template <int DT>
 __device__ __forceinline__ float dot16(const uint4& a, const uint4& b, float acc) {
@@ -77,12 +126,13 @@ __device__ __forceinline__ float dot16(const uint4& a, const uint4& b, float acc
   return acc;
 }
 
-// store one output element in the output dtype (round to nearest even for 16-bit)
+// store one output element in the output dtype (round to nearest even for 16-bit; FP8
+// pools have fp16 outputs)
 template <int DT>
 __device__ __forceinline__ void store_out(void* out, int64_t idx, float v, bool out_f32) {
   if (out_f32 || DT == DT_F32) {
     reinterpret_cast<float*>(out)[idx] = v;
-  } else if constexpr (DT == DT_F16) {
+  } else if constexpr (DT == DT_F16 || DT == DT_FP8) {
     reinterpret_cast<_Float16*>(out)[idx] = (_Float16)v;
   } else {
     reinterpret_cast<__bf16*>(out)[idx] = (__bf16)v;

@@ -11,7 +11,8 @@ constexpr int kWavesPerWG = 4;
 constexpr int kWG = kWave * kWavesPerWG;
 constexpr int kBlock = 16;  // tokens per physical block
 
-enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
+// element types; DT_FP8: FP8 E4M3 pools with fp16 queries, keys and values
+enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_FP8 = 3 };
 
 // How a split kernel distributes and emits its work.
 enum SplitMode : int {
@@ -51,6 +52,7 @@ struct DecodeArgs {
   int32_t max_rows;         // MODE_EVEN: query rows per sequence the decode kernel takes (1, or
                             // 16 / G on the matrix-core path); longer sequences: chunk kernel
   int32_t cols;             // MODE_EVEN, matrix-core path: query columns per partial slot
+  float v_factor;           // DT_FP8: the outputs' factor (256 * v_scale; see decode_valu.hip)
 };
 
 struct ReshapeArgs {
@@ -62,6 +64,8 @@ struct ReshapeArgs {
   int64_t num_tokens;
   int32_t num_kv_heads;
   int32_t head_dim;
+  float k_scale;  // DT_FP8: stored K = e4m3(key / k_scale)
+  float v_scale;  // DT_FP8: stored V = e4m3(value / v_scale)
 };
 
 struct CopyBlocksArgs {

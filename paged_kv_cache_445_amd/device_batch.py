@@ -11,7 +11,7 @@ from . import workloads as W
 
 TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 _NAN_FILL = {"f32": (torch.int32, W.NAN_BITS["f32"]), "f16": (torch.int16, W.NAN_BITS["f16"]),
-             "bf16": (torch.int16, W.NAN_BITS["bf16"])}
+             "bf16": (torch.int16, W.NAN_BITS["bf16"]), "fp8": (torch.uint8, W.NAN_BITS["fp8"])}
 
 
 def to_device(a: np.ndarray, dtype: str, device) -> torch.Tensor:
@@ -47,11 +47,16 @@ class DeviceBatch:
         self.context_lens = torch.from_numpy(b.context_lens.astype(np.int32)).to(dev)
         self.qsl = None if b.query_start_loc is None else \
             torch.from_numpy(b.query_start_loc.astype(np.int32)).to(dev)
-        self.k_cache = nan_fill_(torch.empty(b.k_pool_shape(), dtype=dt, device=dev), b.dtype)
-        self.v_cache = nan_fill_(torch.empty(b.v_pool_shape(), dtype=dt, device=dev), b.dtype)
+        fp8 = b.pool_dtype == "fp8"
+        pool_dt = torch.uint8 if fp8 else dt  # FP8 pools: raw E4M3 bytes
+        self.k_cache = nan_fill_(torch.empty(b.k_pool_shape(), dtype=pool_dt, device=dev),
+                                 b.pool_dtype)
+        self.v_cache = nan_fill_(torch.empty(b.v_pool_shape(), dtype=pool_dt, device=dev),
+                                 b.pool_dtype)
         out_dt = torch.float32 if out_f32 else dt
         self.geom = pa.geom(b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim, b.num_blocks,
-                            b.max_blocks_per_seq, dt, out_dt, b.block_size)
+                            b.max_blocks_per_seq, pa.PA_FP8_E4M3 if fp8 else dt, out_dt,
+                            b.block_size, q_dtype=dt, k_scale=b.k_scale, v_scale=b.v_scale)
         self.out = torch.zeros((b.num_q_rows, b.num_q_heads, b.head_dim), dtype=out_dt,
                                device=dev)
         ws = pa.workspace_size(self.geom, b.num_q_rows)
@@ -84,7 +89,7 @@ class DeviceBatch:
         out = []
         for t in (self.k_cache, self.v_cache):
             c = t.detach().cpu()
-            if self.b.dtype == "bf16":
+            if self.b.pool_dtype == "bf16":
                 out.append(c.view(torch.int16).numpy().view(np.uint16))
             else:
                 out.append(c.numpy())

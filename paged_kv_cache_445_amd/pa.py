@@ -18,7 +18,7 @@ if not os.path.exists(LIB_PATH):
 
 _lib = ctypes.CDLL(LIB_PATH)
 
-PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2, 3
 DTYPE_CODE = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
 STATUS = {0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_UNSUPPORTED",
           -4: "PA_ERR_WORKSPACE", -5: "PA_ERR_HIP", -6: "PA_ERR_NO_BLOCKS"}
@@ -29,7 +29,8 @@ class Geom(ctypes.Structure):
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("block_size", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
                 ("max_blocks_per_seq", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
-                ("out_dtype", ctypes.c_int32)]
+                ("out_dtype", ctypes.c_int32), ("q_dtype", ctypes.c_int32),
+                ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float)]
 
 
 class PAError(RuntimeError):
@@ -65,15 +66,22 @@ def lib():
     return _lib
 
 
+def _code(dt):
+    return DTYPE_CODE[dt] if isinstance(dt, torch.dtype) else int(dt)
+
+
 def geom(num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, max_blocks_per_seq,
-         kv_dtype, out_dtype=None, block_size=16) -> Geom:
-    kv = DTYPE_CODE[kv_dtype] if isinstance(kv_dtype, torch.dtype) else int(kv_dtype)
-    if out_dtype is None:
-        od = kv
-    else:
-        od = DTYPE_CODE[out_dtype] if isinstance(out_dtype, torch.dtype) else int(out_dtype)
+         kv_dtype, out_dtype=None, block_size=16, q_dtype=None, k_scale=1.0,
+         v_scale=1.0) -> Geom:
+    """kv_dtype: the pools' type (a torch dtype or a pa_dtype code, PA_FP8_E4M3 for FP8
+    pools); q_dtype: that of q, key and value (default: kv_dtype; fp16 for FP8 pools);
+    out_dtype: q_dtype or float32 (default q_dtype)."""
+    kv = _code(kv_dtype)
+    qd = (PA_F16 if kv == PA_FP8_E4M3 else kv) if q_dtype is None else _code(q_dtype)
+    od = qd if out_dtype is None else _code(out_dtype)
     return Geom(int(num_seqs), int(num_q_heads), int(num_kv_heads), int(head_dim),
-                int(block_size), int(num_blocks), int(max_blocks_per_seq), kv, od)
+                int(block_size), int(num_blocks), int(max_blocks_per_seq), kv, od, qd,
+                float(k_scale), float(v_scale))
 
 
 def _p(t):

@@ -38,9 +38,9 @@ import numpy as np
 
 BLOCK_SIZE = 16
 
-STORAGE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}
-ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
-NAN_BITS = {"f32": 0x7FC00000, "f16": 0x7E00, "bf16": 0x7FC0}
+STORAGE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16, "fp8": np.uint8}
+ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
+NAN_BITS = {"f32": 0x7FC00000, "f16": 0x7E00, "bf16": 0x7FC0, "fp8": 0x7F}
 
 
 def to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
@@ -64,6 +64,8 @@ def nan_pool(shape, dtype: str) -> np.ndarray:
     pool = np.empty(shape, dtype=STORAGE[dtype])
     if dtype == "f32":
         pool.view(np.uint32).fill(NAN_BITS[dtype])
+    elif dtype == "fp8":
+        pool.fill(NAN_BITS[dtype])
     else:
         pool.view(np.uint16).fill(NAN_BITS[dtype])
     return pool
@@ -104,6 +106,13 @@ class Batch:
     block_size: int = BLOCK_SIZE
     partition_size: int = 512
     meta: dict = field(default_factory=dict)
+    kv_dtype: str = ""      # the pools' element type when it differs from dtype ("fp8")
+    k_scale: float = 1.0    # FP8 pools: per-pool scales (calibration inputs)
+    v_scale: float = 1.0
+
+    @property
+    def pool_dtype(self) -> str:
+        return self.kv_dtype or self.dtype
 
     @property
     def num_q_rows(self) -> int:
@@ -112,7 +121,7 @@ class Batch:
     @property
     def x(self) -> int:
         """Elements per 16-byte chunk of the K pool's innermost dimension."""
-        return 16 // ELEM_BYTES[self.dtype]
+        return 16 // ELEM_BYTES[self.pool_dtype]
 
     def k_pool_shape(self):
         D, X = self.head_dim, self.x
@@ -130,13 +139,14 @@ class Batch:
         """Algorithmic KV bytes of one decode pass: every context token's K and V read once
         per KV head (GQA sharing not multiplied)."""
         return int(self.context_lens.astype(np.int64).sum()) * self.num_kv_heads * \
-            self.head_dim * 2 * ELEM_BYTES[self.dtype]
+            self.head_dim * 2 * ELEM_BYTES[self.pool_dtype]
 
     def kv_unique_bytes(self) -> int:
         """KV bytes of the distinct cached tokens a pass reads: a token shared by several
         sequences (a common prefix block) counts once."""
         distinct = np.unique(np.concatenate(self.seq_tokens)) if self.num_seqs else []
-        return int(len(distinct)) * self.num_kv_heads * self.head_dim * 2 * ELEM_BYTES[self.dtype]
+        return int(len(distinct)) * self.num_kv_heads * self.head_dim * 2 * \
+            ELEM_BYTES[self.pool_dtype]
 
     def step_slots(self) -> np.ndarray:
         return self.slot[self.new]
@@ -280,6 +290,17 @@ def mixed_chunked_bf16(seed: int = 4454, num_chunk: int = 8, num_decode: int = 1
                        max_blocks_per_seq=500)
 
 
+def llama7b_fp8(seed: int = 4451, num_seqs: int = 32) -> Batch:
+    """The LLaMA-7B-shaped batch (same draws) with FP8 E4M3 pools: fp16 q, keys and values,
+    quantised by the cache write with per-pool scales 6.5 / 448 (N(0, 1) values beyond 6.5
+    saturate; none is expected at this size)."""
+    b = llama7b_f16(seed, num_seqs)
+    b.name = "llama7b_fp8"
+    b.kv_dtype = "fp8"
+    b.k_scale = b.v_scale = float(np.float32(6.5 / 448))
+    return b
+
+
 def spec_verify_f16(seed: int = 4455, num_seqs: int = 32, num_draft: int = 5) -> Batch:
     """Speculative-decoding verify step on the LLaMA-7B shape ("vLLM 深度拆解" §5.1: the
     target model checks num_draft drafted tokens in one pass): every sequence runs the last
@@ -308,6 +329,7 @@ PRESETS = {
     "gqa_long_bf16": gqa_long_bf16,
     "prefix_shared_f16": prefix_shared_f16,
     "mixed_chunked_bf16": mixed_chunked_bf16,
+    "llama7b_fp8": llama7b_fp8,
     "spec_verify_f16": spec_verify_f16,
     "spec_verify_gqa_bf16": spec_verify_gqa_bf16,
 }

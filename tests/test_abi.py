@@ -47,13 +47,17 @@ def test_binding_exposes_the_same_names():
 class Geom(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "num_seqs", "num_q_heads", "num_kv_heads", "head_dim", "block_size", "num_blocks",
-        "max_blocks_per_seq", "kv_dtype", "out_dtype")]
+        "max_blocks_per_seq", "kv_dtype", "out_dtype", "q_dtype")] + \
+        [("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float)]
 
 
 def _g(**kw):
     d = dict(num_seqs=4, num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
-             num_blocks=64, max_blocks_per_seq=8, kv_dtype=2, out_dtype=0)
+             num_blocks=64, max_blocks_per_seq=8, kv_dtype=2, out_dtype=0, k_scale=1.0,
+             v_scale=1.0)
     d.update(kw)
+    if "q_dtype" not in kw:
+        d["q_dtype"] = 1 if d["kv_dtype"] == 3 else d["kv_dtype"]
     return Geom(**d)
 
 
@@ -64,8 +68,12 @@ def test_kv_cache_bytes_and_validation(lib):
     assert lib.pa_kv_cache_bytes(ctypes.byref(g)) == 8448 * 32 * 128 * 16 * 2
     for bad in (_g(head_dim=96), _g(block_size=32), _g(num_q_heads=6, num_kv_heads=4),
                 _g(kv_dtype=7), _g(out_dtype=1), _g(num_q_heads=64, num_kv_heads=2),
-                _g(num_seqs=-1)):
+                _g(num_seqs=-1), _g(q_dtype=1), _g(kv_dtype=3, q_dtype=2),
+                _g(kv_dtype=3, k_scale=0.0), _g(kv_dtype=3, v_scale=float("inf"))):
         assert lib.pa_kv_cache_bytes(ctypes.byref(bad)) == 0
+    # FP8 pools: one byte per element
+    g8 = _g(num_kv_heads=32, num_q_heads=32, num_blocks=8448, kv_dtype=3, out_dtype=1)
+    assert lib.pa_kv_cache_bytes(ctypes.byref(g8)) == 8448 * 32 * 128 * 16
 
 
 def test_status_strings(lib):
@@ -100,10 +108,13 @@ def test_host_checks_return_codes_without_launching(lib):
     g0 = _g(num_seqs=0)
     assert lib.pa_decode(None, None, None, None, None, None, None, 0, 0.1, None, 0,
                          ctypes.byref(g0), None) == 0
-    # fp32 with multi-row sequences is not implemented
+    # fp32 or FP8 pools with multi-row sequences are not implemented
     gf = _g(kv_dtype=0, out_dtype=0)
     assert lib.pa_decode(dummy, dummy, dummy, dummy, dummy, dummy, dummy, 9, 0.1, dummy, 1 << 30,
                          ctypes.byref(gf), None) == -3
+    g8 = _g(kv_dtype=3, out_dtype=1, num_q_heads=4, num_kv_heads=4)
+    assert lib.pa_decode(dummy, dummy, dummy, dummy, dummy, dummy, dummy, 9, 0.1, dummy, 1 << 30,
+                         ctypes.byref(g8), None) == -3
 
     lib.pa_decode_partitioned.restype = ctypes.c_int
     lib.pa_decode_partitioned.argtypes = [vp] * 8 + [ctypes.c_int32, ctypes.c_float,

@@ -446,3 +446,45 @@ def test_spec_verify_long_split(dev):
             db.attend()
             torch.cuda.synchronize()
             assert np.array_equal(db.out_host(), got)
+
+
+# ----------------------------------------------------------------- FP8 E4M3 pools
+
+def _fp8(b, k_scale=6.0 / 448, v_scale=5.0 / 448):
+    b.kv_dtype = "fp8"
+    b.k_scale, b.v_scale = float(np.float32(k_scale)), float(np.float32(v_scale))
+    return b
+
+
+@pytest.mark.parametrize("Hq,Hkv,D", [(4, 4, 128), (8, 8, 64), (8, 2, 128), (32, 32, 128),
+                                      (16, 16, 64)])
+def test_fp8_decode_ragged(dev, Hq, Hkv, D):
+    """FP8 pools: the cache write's E4M3 codes bit for bit (quantisation included) and the
+    decode against the oracle over the same codes, on the edge-case context lengths."""
+    rng = np.random.default_rng(2000 + Hq + D)
+    ctx = np.array(EDGE_CTX + list(rng.integers(1, 2200, size=6)))
+    parity(dev, _fp8(W.build_batch("fp8_ragged", "f16", ctx, np.ones(len(ctx)), Hq, Hkv, D,
+                                   rng)))
+
+
+def test_fp8_saturation_and_small_scales(dev):
+    """Scales that push part of N(0, 1) past 448 (saturation) and into the E4M3 subnormals,
+    with fp16 output."""
+    rng = np.random.default_rng(2100)
+    b = W.build_batch("fp8_sat", "f16", rng.integers(1, 900, size=9), np.ones(9), 8, 8, 128,
+                      rng)
+    parity(dev, _fp8(b, k_scale=1.0 / 256, v_scale=0.75), out_f32=False)
+
+
+def test_fp8_many_sequences(dev):
+    """300 sequences: split segments merged in-kernel, 2, 4 or 8 heads per wave (contexts
+    kept short: the oracle quantises every element of the history)."""
+    rng = np.random.default_rng(2200)
+    for Hq, D in ((8, 128), (16, 64), (32, 64)):
+        b = W.build_batch("fp8_many", "f16", rng.integers(1, 301, size=300), np.ones(300), Hq,
+                          Hq, D, rng)
+        parity(dev, _fp8(b))
+
+
+def test_llama7b_fp8(dev):
+    parity(dev, W.make("llama7b_fp8"))
