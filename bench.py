@@ -283,7 +283,7 @@ def main():
     def decode(i):
         kc, vc = pools[i % copies]
         pa.decode(db.out, db.q, kc, vc, db.block_tables, db.context_lens, db.qsl, db.scale,
-                  db.workspace, db.geom)
+                  db.workspace, db.geom, max_query_len=db.max_query_len)
 
     print(f"[bench] warmup {args.warmup} steps, {copies} pool copies", file=sys.stderr,
           flush=True)

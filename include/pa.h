@@ -148,8 +148,9 @@ size_t pa_workspace_size(const pa_geom* geom, int32_t num_q_rows);
  */
 pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
                     const int32_t* block_tables, const int32_t* context_lens,
-                    const int32_t* query_start_loc, int32_t num_q_rows, float scale,
-                    void* workspace, size_t workspace_bytes, const pa_geom* geom, void* stream);
+                    const int32_t* query_start_loc, int32_t num_q_rows, int32_t max_query_len,
+                    float scale, void* workspace, size_t workspace_bytes, const pa_geom* geom,
+                    void* stream);
 
 /*
  * Split-context partials (flash-decoding) for decode rows: one query row per sequence

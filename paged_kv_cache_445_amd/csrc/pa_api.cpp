@@ -102,12 +102,13 @@ bool use_mfma(const pa_geom* g) {
   return (g->kv_dtype == PA_F16 || g->kv_dtype == PA_BF16) && g->num_q_heads / g->num_kv_heads >= 2;
 }
 
-// Which decode kernel runs a pa_decode call, and which sequences it takes.
-//  - GQA (16-bit, G >= 2): the matrix-core kernel; with query_start_loc it also takes the
-//    sequences of up to 16 / G rows (a speculative verify step), nr * G columns at once.
-//  - MHA 16-bit with more rows than sequences: the matrix-core kernel too (G = 1, up to 16
-//    rows a sequence), so verify rows read their K and V once instead of through the
-//    chunk kernel's 128-column items.
+// Which decode kernel runs a pa_decode call, and which sequences it takes (max_len: an upper
+// bound of the rows of any sequence; 1 without query_start_loc).
+//  - GQA (16-bit, G >= 2): the matrix-core kernel; when sequences may have several rows it
+//    also takes those of up to 16 / G rows (a speculative verify step), nr * G columns at once.
+//  - MHA 16-bit with sequences of several rows: the matrix-core kernel too (G = 1, up to 16
+//    rows a sequence), so verify rows read their K and V once instead of through the chunk
+//    kernel's 128-column items.
 //  - otherwise the vector kernel, one row per sequence.
 // Longer sequences go to the chunk kernel.  cols: query columns per partial slot.
 struct Route {
@@ -116,11 +117,11 @@ struct Route {
   int cols;
 };
 
-Route route(const pa_geom* g, bool multi_row, int32_t num_q_rows) {
+Route route(const pa_geom* g, int32_t max_len) {
   const int G = g->num_q_heads / g->num_kv_heads;
-  if (use_mfma(g)) return {1, multi_row ? 16 / G : 1, multi_row ? 16 / G * G : G};
-  if ((g->kv_dtype == PA_F16 || g->kv_dtype == PA_BF16) && multi_row && num_q_rows > g->num_seqs)
-    return {1, 16, 16};
+  const bool multi = max_len > 1;
+  if (use_mfma(g)) return {1, multi ? 16 / G : 1, multi ? 16 / G * G : G};
+  if ((g->kv_dtype == PA_F16 || g->kv_dtype == PA_BF16) && multi) return {1, 16, 16};
   return {0, 1, 1};
 }
 
@@ -298,18 +299,19 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapp
 size_t pa_workspace_size(const pa_geom* g, int32_t num_q_rows) {
   if (check_geom(g) != PA_OK || num_q_rows < 0) return 0;
   // enough for the call with and without query_start_loc
-  const size_t a = even_workspace_bytes(g, route(g, true, num_q_rows));
-  const size_t b = even_workspace_bytes(g, route(g, false, num_q_rows));
+  const size_t a = even_workspace_bytes(g, route(g, num_q_rows));
+  const size_t b = even_workspace_bytes(g, route(g, 1));
   return a > b ? a : b;
 }
 
 pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
                     const int32_t* block_tables, const int32_t* context_lens,
-                    const int32_t* query_start_loc, int32_t num_q_rows, float scale,
-                    void* workspace, size_t workspace_bytes, const pa_geom* g, void* stream) {
+                    const int32_t* query_start_loc, int32_t num_q_rows, int32_t max_query_len,
+                    float scale, void* workspace, size_t workspace_bytes, const pa_geom* g,
+                    void* stream) {
   const pa_status gs = check_geom(g);
   if (gs != PA_OK) return gs;
-  if (num_q_rows < 0) return PA_ERR_SHAPE;
+  if (num_q_rows < 0 || max_query_len < 0) return PA_ERR_SHAPE;
   if (!query_start_loc && num_q_rows != g->num_seqs) return PA_ERR_SHAPE;
   if (g->num_seqs == 0 || num_q_rows == 0) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_NULL;
@@ -319,7 +321,11 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
     return PA_ERR_UNSUPPORTED;
   hipStream_t st = (hipStream_t)stream;
 
-  const Route rt = route(g, query_start_loc != nullptr, num_q_rows);
+  // rows of the longest sequence: at most max_query_len (0: unknown) and num_q_rows
+  int32_t max_len = 1;
+  if (query_start_loc)
+    max_len = max_query_len > 0 && max_query_len < num_q_rows ? max_query_len : num_q_rows;
+  const Route rt = route(g, max_len);
   const int grid = split_grid(g, pa::MODE_EVEN, rt.path);
   const size_t need = even_workspace_bytes(g, rt);
   if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
@@ -363,9 +369,9 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
     return rt.path ? pa::launch_mfma_decode(g->kv_dtype, pa::MODE_EVEN, a, grid, st)
                    : pa::launch_valu_decode(g->kv_dtype, pa::MODE_EVEN, a, grid, st);
   };
-  // without query_start_loc, or when no sequence can have more rows than the decode kernel
-  // takes, there is no chunk work
-  if (!query_start_loc || num_q_rows <= rt.max_rows) return hip_status(decode());
+  // without query_start_loc, or when no sequence has more rows than the decode kernel takes,
+  // there is no chunk work
+  if (!query_start_loc || max_len <= rt.max_rows) return hip_status(decode());
 
   // multi-row sequences: the chunk kernel on the side stream, forked from and joined back
   // into the caller's stream around the decode kernel

@@ -63,6 +63,7 @@ class DeviceBatch:
         # zeroed once: pa_decode keeps its arrival counters at zero between calls
         self.workspace = torch.zeros(max(ws, 16), dtype=torch.uint8, device=dev)
         self.scale = float(b.scale)
+        self.max_query_len = int(b.rows_per_seq().max()) if b.num_seqs else 0
 
     # ------------------------------------------------------------------ the method
     def prefill(self, stream=None):
@@ -76,7 +77,8 @@ class DeviceBatch:
 
     def attend(self, stream=None):
         pa.decode(self.out, self.q, self.k_cache, self.v_cache, self.block_tables,
-                  self.context_lens, self.qsl, self.scale, self.workspace, self.geom, stream)
+                  self.context_lens, self.qsl, self.scale, self.workspace, self.geom, stream,
+                  max_query_len=self.max_query_len)
 
     def step(self, stream=None):
         """One pass of the hot path: cache write of this step's tokens, then attention."""

@@ -53,8 +53,8 @@ _lib.pa_reshape_and_cache.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_int64, _
 _lib.pa_copy_blocks.restype = ctypes.c_int
 _lib.pa_copy_blocks.argtypes = [_vp, _vp, _vp, ctypes.c_int64, _G, _vp]
 _lib.pa_decode.restype = ctypes.c_int
-_lib.pa_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_float,
-                           _vp, ctypes.c_size_t, _G, _vp]
+_lib.pa_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_int32,
+                           ctypes.c_float, _vp, ctypes.c_size_t, _G, _vp]
 _lib.pa_decode_partitioned.restype = ctypes.c_int
 _lib.pa_decode_partitioned.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32,
                                        ctypes.c_float, ctypes.c_int32, ctypes.c_int32, _G, _vp]
@@ -126,12 +126,14 @@ def copy_blocks(k_cache, v_cache, block_mapping, g: Geom, stream=None):
 
 
 def decode(out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc, scale,
-           workspace, g: Geom, stream=None):
+           workspace, g: Geom, stream=None, max_query_len: int = 0):
+    """max_query_len: with query_start_loc, an upper bound of any sequence's rows (0: unknown)."""
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("pa_decode",
            _lib.pa_decode(_p(out), _p(q), _p(k_cache), _p(v_cache), _p(block_tables),
-                          _p(context_lens), _p(query_start_loc), int(q.shape[0]), float(scale),
-                          _p(workspace), ws_bytes, ctypes.byref(g), _stream(stream)))
+                          _p(context_lens), _p(query_start_loc), int(q.shape[0]),
+                          int(max_query_len), float(scale), _p(workspace), ws_bytes,
+                          ctypes.byref(g), _stream(stream)))
 
 
 def decode_partitioned(tmp_out, max_logits, exp_sums, q, k_cache, v_cache, block_tables,

@@ -97,23 +97,26 @@ def test_host_checks_return_codes_without_launching(lib):
     assert lib.pa_reshape_and_cache(dummy, dummy, dummy, dummy, dummy, 3, None, None) == -1
 
     lib.pa_decode.restype = ctypes.c_int
-    lib.pa_decode.argtypes = [vp] * 7 + [ctypes.c_int32, ctypes.c_float, vp, ctypes.c_size_t,
-                                         ctypes.POINTER(Geom), vp]
+    lib.pa_decode.argtypes = [vp] * 7 + [ctypes.c_int32, ctypes.c_int32, ctypes.c_float, vp,
+                                         ctypes.c_size_t, ctypes.POINTER(Geom), vp]
     # without query_start_loc the row count must equal the sequence count
-    assert lib.pa_decode(dummy, dummy, dummy, dummy, dummy, dummy, None, 3, 0.1, dummy, 1 << 30,
+    assert lib.pa_decode(dummy, dummy, dummy, dummy, dummy, dummy, None, 3, 0, 0.1, dummy, 1 << 30,
                          ctypes.byref(g), None) == -2
-    assert lib.pa_decode(dummy, None, dummy, dummy, dummy, dummy, None, 4, 0.1, dummy, 1 << 30,
+    assert lib.pa_decode(dummy, None, dummy, dummy, dummy, dummy, None, 4, 0, 0.1, dummy, 1 << 30,
                          ctypes.byref(g), None) == -1
+    # a negative max_query_len is rejected
+    assert lib.pa_decode(dummy, dummy, dummy, dummy, dummy, dummy, None, 4, -1, 0.1, dummy, 1 << 30,
+                         ctypes.byref(g), None) == -2
     # an empty batch is a no-op
     g0 = _g(num_seqs=0)
-    assert lib.pa_decode(None, None, None, None, None, None, None, 0, 0.1, None, 0,
+    assert lib.pa_decode(None, None, None, None, None, None, None, 0, 0, 0.1, None, 0,
                          ctypes.byref(g0), None) == 0
     # fp32 or FP8 pools with multi-row sequences are not implemented
     gf = _g(kv_dtype=0, out_dtype=0)
-    assert lib.pa_decode(dummy, dummy, dummy, dummy, dummy, dummy, dummy, 9, 0.1, dummy, 1 << 30,
+    assert lib.pa_decode(dummy, dummy, dummy, dummy, dummy, dummy, dummy, 9, 0, 0.1, dummy, 1 << 30,
                          ctypes.byref(gf), None) == -3
     g8 = _g(kv_dtype=3, out_dtype=1, num_q_heads=4, num_kv_heads=4)
-    assert lib.pa_decode(dummy, dummy, dummy, dummy, dummy, dummy, dummy, 9, 0.1, dummy, 1 << 30,
+    assert lib.pa_decode(dummy, dummy, dummy, dummy, dummy, dummy, dummy, 9, 0, 0.1, dummy, 1 << 30,
                          ctypes.byref(g8), None) == -3
 
     lib.pa_decode_partitioned.restype = ctypes.c_int

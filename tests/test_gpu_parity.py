@@ -488,3 +488,21 @@ def test_fp8_many_sequences(dev):
 
 def test_llama7b_fp8(dev):
     parity(dev, W.make("llama7b_fp8"))
+
+
+def test_max_query_len_unknown_or_loose(dev):
+    """pa_decode with max_query_len 0 (unknown: every kernel that might be needed runs) or an
+    upper bound above the true longest sequence gives the same rows as the exact value."""
+    import torch
+    rng = np.random.default_rng(808)
+    n = np.array([3, 1, 40, 2, 1, 4])
+    prior = np.array([100, 7, 300, 1, 2000, 33])
+    for dtype, Hq, Hkv in (("bf16", 16, 4), ("f16", 8, 8)):
+        b = W.build_batch("mql", dtype, prior + n, n, Hq, Hkv, 128, rng)
+        db, got, want = parity(dev, b)
+        for mql in (0, 100):
+            db.max_query_len = mql
+            db.out.zero_()
+            db.attend()
+            torch.cuda.synchronize()
+            check_out(db.out_host(), want, TOL[dtype], f"max_query_len {mql}")
