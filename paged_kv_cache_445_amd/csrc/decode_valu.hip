@@ -99,15 +99,22 @@ __device__ __forceinline__ void mask_piece(uint4& v, int first_token, int valid)
   v.w &= m[3];
 }
 
-// FP8 V piece: the 16 tokens of one dimension row as two chunks of 8 fp16 values (2^-8 times
-// the stored values), with the tokens >= valid zeroed (MASK).
-template <bool MASK>
-__device__ __forceinline__ void fp8_v_piece(const uint4& v, uint4& h0, uint4& h1, int valid) {
-  fp8x16_to_f16(v, h0, h1);
-  if (MASK) {
-    mask_piece<DT_F16>(h0, 0, valid);
-    mask_piece<DT_F16>(h1, 8, valid);
+// FP8: scale_log2 * (q . k) over a 16-byte K chunk of 16 E4M3 values, each widened to fp32
+// and multiplied with its fp16 query element (q0: elements 0-7, q1: 8-15) in fp32.
+__device__ __forceinline__ float dot_fp8(const uint4& k, const uint4& q0, const uint4& q1,
+                                         float acc) {
+  const uint32_t kw[4] = {k.x, k.y, k.z, k.w};
+  const uint32_t qw[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    float f[4];
+    fp8x4_to_f32(kw[m], f);
+    acc = fmaf(f16_lo(qw[2 * m]), f[0], acc);
+    acc = fmaf(f16_hi(qw[2 * m]), f[1], acc);
+    acc = fmaf(f16_lo(qw[2 * m + 1]), f[2], acc);
+    acc = fmaf(f16_hi(qw[2 * m + 1]), f[3], acc);
   }
+  return acc;
 }
 
 // One 16-token tile.  MASK: only tokens < valid exist.
@@ -118,15 +125,10 @@ __device__ __forceinline__ void v_tile(VState<DT, D>& st, VTile<DT, D>& t, const
   const int lane = lane_id();
   float part = 0.f;
   if constexpr (DT == DT_FP8) {
-    // each 16-byte K chunk is 16 E4M3 values: widen to fp16 (2^-8 times the value; the
-    // score factor restores it) and dot with the chunk's 16 fp16 query elements
+    // each 16-byte K chunk is 16 E4M3 values, dotted with the chunk's 16 fp16 query
+    // elements (k_scale is in the score factor)
 #pragma unroll
-    for (int i = 0; i < C::NK; ++i) {
-      uint4 h0, h1;
-      fp8x16_to_f16(t.k[i], h0, h1);
-      part = dot16<DT_F16>(h0, qv[2 * i], part);
-      part = dot16<DT_F16>(h1, qv[2 * i + 1], part);
-    }
+    for (int i = 0; i < C::NK; ++i) part = dot_fp8(t.k[i], qv[2 * i], qv[2 * i + 1], part);
   } else {
 #pragma unroll
     for (int i = 0; i < C::NK; ++i) part = dot16<DT>(t.k[i], qv[i], part);
@@ -155,12 +157,18 @@ __device__ __forceinline__ void v_tile(VState<DT, D>& st, VTile<DT, D>& t, const
   for (int j = 0; j < C::NV; ++j) {
     float a = st.acc[j] * alpha;
     if constexpr (DT == DT_FP8) {
-      uint4 h0, h1;
-      fp8_v_piece<MASK>(t.v[j], h0, h1, valid);
+      // the 16 tokens of one dimension row; tokens >= valid are zeroed (MASK)
+      const uint32_t vw[4] = {t.v[j].x, t.v[j].y, t.v[j].z, t.v[j].w};
 #pragma unroll
-      for (int k = 0; k < 8; ++k) a = fmaf(w[k], elem16<DT_F16>(h0, k), a);
+      for (int m = 0; m < 4; ++m) {
+        float f[4];
+        fp8x4_to_f32(vw[m], f);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) a = fmaf(w[8 + k], elem16<DT_F16>(h1, k), a);
+        for (int k = 0; k < 4; ++k) {
+          if (MASK && 4 * m + k >= valid) f[k] = 0.f;
+          a = fmaf(w[4 * m + k], f[k], a);
+        }
+      }
     } else {
       if (MASK) mask_piece<DT>(t.v[j], C::X * g, valid);
 #pragma unroll
@@ -326,8 +334,8 @@ __device__ void valu_run(const DecodeArgs& a, VPiece p, VStart<DT, D, HPW>& vs,
 
 // Finish a piece: combine the lanes of each dimension row and the per-token sums; returns
 // the total l (every lane).  Afterwards every lane holds full sums for its dimensions.  FP8
-// pools: the sums are also multiplied by vfac (256 * v_scale: the widened V values are 2^-8
-// times the stored ones, which stand for the stored value times v_scale).
+// pools: the sums are also multiplied by vfac (v_scale: a stored V value stands for its E4M3
+// value times v_scale).
 template <int DT, int D>
 __device__ __forceinline__ float v_finish(VState<DT, D>& st, float vfac) {
   using C = VCfg<DT, D>;
@@ -588,9 +596,12 @@ static void launch_k(const DecodeArgs& a, int grid, size_t lds, hipStream_t st) 
 template <int DT, int D, int MODE>
 static void launch_hpw(const DecodeArgs& a, int grid, size_t lds, hipStream_t st) {
   if constexpr (MODE == MODE_EVEN) {
-    // fp32 queries fill twice the registers: at most two heads per wave
-    if constexpr (DT != DT_F32) {
+    // fp32 queries fill twice the registers: at most two heads per wave; FP8 widens to
+    // fp32 in registers: at most four
+    if constexpr (DT != DT_F32 && DT != DT_FP8) {
       if (a.heads_per_wave == 8) return launch_k<DT, D, MODE, 8>(a, grid, lds, st);
+    }
+    if constexpr (DT != DT_F32) {
       if (a.heads_per_wave == 4) return launch_k<DT, D, MODE, 4>(a, grid, lds, st);
     }
     if (a.heads_per_wave == 2) return launch_k<DT, D, MODE, 2>(a, grid, lds, st);
@@ -636,8 +647,10 @@ static int occ_k(int head_dim, int lds) {
 template <int DT, int MODE>
 static int occ(int head_dim, int hpw, int lds) {
   if constexpr (MODE == MODE_EVEN) {
-    if constexpr (DT != DT_F32) {
+    if constexpr (DT != DT_F32 && DT != DT_FP8) {
       if (hpw == 8) return occ_k<DT, MODE, 8>(head_dim, lds);
+    }
+    if constexpr (DT != DT_F32) {
       if (hpw == 4) return occ_k<DT, MODE, 4>(head_dim, lds);
     }
     if (hpw == 2) return occ_k<DT, MODE, 2>(head_dim, lds);

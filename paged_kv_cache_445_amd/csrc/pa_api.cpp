@@ -145,14 +145,14 @@ constexpr int kEvenWgPerCu[2] = {1, 2};
 // longer segments, and once there are fewer segments than workgroups every segment is cut
 // into several pieces whose merge costs more than the locality gains.  So: the largest of
 // 8, 4, 2 whose head groups tile num_q_heads exactly and leave at least one segment per
-// workgroup (fp32: at most 2, its queries fill twice the registers), else 1; optional cap
-// for tuning.
+// workgroup (fp32: at most 2, its queries fill twice the registers; FP8: at most 4, its
+// values are widened to fp32 in registers), else 1; optional cap for tuning.
 int heads_per_wave(const pa_geom* g) {
   static const int v = [] {
     const char* s = getenv("PA_DECODE_HPW");
     return s ? atoi(s) : 0;
   }();
-  const int cap = g->kv_dtype == PA_F32 ? 2 : 8;
+  const int cap = g->kv_dtype == PA_F32 ? 2 : g->kv_dtype == PA_FP8_E4M3 ? 4 : 8;
   const int o = wg_per_cu_override();
   const int64_t workgroups = (int64_t)cu_count() * (o > 0 ? o : kEvenWgPerCu[0]);
   for (int h = 8; h >= 2; h /= 2) {
@@ -355,9 +355,9 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   a.out_f32 = g->out_dtype == PA_F32 && g->kv_dtype != PA_F32;
   a.scale_log2 = scale_to_log2(scale);
   if (g->kv_dtype == PA_FP8_E4M3) {
-    // the kernel widens E4M3 to fp16 at 2^-8 times the value (see decode_valu.hip)
-    a.scale_log2 *= g->k_scale * 256.f;
-    a.v_factor = g->v_scale * 256.f;
+    // a stored element stands for its E4M3 value times the pool's scale
+    a.scale_log2 *= g->k_scale;
+    a.v_factor = g->v_scale;
   }
   a.seg_extra = seg_extra_override() >= 0 ? seg_extra_override() : kSegExtra[rt.path];
   a.heads_per_wave = rt.path == 0 ? heads_per_wave(g) : 1;

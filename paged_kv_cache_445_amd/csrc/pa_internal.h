@@ -52,7 +52,7 @@ struct DecodeArgs {
   int32_t max_rows;         // MODE_EVEN: query rows per sequence the decode kernel takes (1, or
                             // 16 / G on the matrix-core path); longer sequences: chunk kernel
   int32_t cols;             // MODE_EVEN, matrix-core path: query columns per partial slot
-  float v_factor;           // DT_FP8: the outputs' factor (256 * v_scale; see decode_valu.hip)
+  float v_factor;           // DT_FP8: the outputs' factor (v_scale)
 };
 
 struct ReshapeArgs {
