@@ -95,18 +95,26 @@ void pa_ref_to_double(const void* src, int32_t dtype, int64_t n, double* dst) {
 
 /* ---------------------------------------------------------------- pool layout */
 
+/* A block of block_size tokens is R sub-blocks of T tokens (T = block_size up to 16, else 16;
+ * R = block_size / T), each holding every KV head: K [NB][R][Hkv][D/X][T][X],
+ * V [NB][R][Hkv][D][T].  For block_size 16 (R = 1) this is [NB][Hkv][D/X][16][X] and
+ * [NB][Hkv][D][16]. */
+static int32_t sub_tokens(const pa_ref_geom* g) { return g->block_size < 16 ? g->block_size : 16; }
+
 int64_t pa_ref_k_offset(const pa_ref_geom* g, int64_t block, int32_t kv_head, int32_t token,
                         int32_t dim) {
   const int64_t x = 16 / elem_bytes(g->dtype);
   const int64_t chunks = g->head_dim / x;
-  return (((block * g->num_kv_heads + kv_head) * chunks + dim / x) * g->block_size + token) * x +
-         dim % x;
+  const int32_t T = sub_tokens(g), R = g->block_size / T;
+  const int64_t sub = block * R + token / T; /* sub-block index in the pool */
+  return (((sub * g->num_kv_heads + kv_head) * chunks + dim / x) * T + token % T) * x + dim % x;
 }
 
 int64_t pa_ref_v_offset(const pa_ref_geom* g, int64_t block, int32_t kv_head, int32_t token,
                         int32_t dim) {
-  return ((block * g->num_kv_heads + kv_head) * (int64_t)g->head_dim + dim) * g->block_size +
-         token;
+  const int32_t T = sub_tokens(g), R = g->block_size / T;
+  const int64_t sub = block * R + token / T;
+  return ((sub * g->num_kv_heads + kv_head) * (int64_t)g->head_dim + dim) * T + token % T;
 }
 
 static int geom_ok(const pa_ref_geom* g) {
@@ -119,6 +127,7 @@ static int geom_ok(const pa_ref_geom* g) {
   if (g->dtype == PA_REF_FP8_E4M3 && !(g->k_scale > 0.0 && g->v_scale > 0.0)) return 0;
   if (g->num_q_heads % g->num_kv_heads) return 0;
   if (g->head_dim % (16 / elem_bytes(g->dtype))) return 0;
+  if (g->block_size > 16 && g->block_size % 16) return 0;
   return 1;
 }
 

@@ -30,9 +30,13 @@
  *   - slot = physical_block * block_size + offset; slot < 0 means "skip this token".
  *
  * Pool layout (the GPU library's ABI defines the same layout; written out here on
- * its own).  elem = 4 (fp32) or 2 (fp16, bf16) bytes, X = 16 / elem:
- *   K pool: [num_blocks][num_kv_heads][head_dim / X][block_size][X]
- *   V pool: [num_blocks][num_kv_heads][head_dim][block_size]
+ * its own).  elem = 4 (fp32) or 2 (fp16, bf16) bytes, X = 16 / elem.  A block of block_size
+ * tokens is R = block_size / T sub-blocks of T tokens (T = block_size up to 16, else 16, and
+ * block_size a multiple of 16):
+ *   K pool: [num_blocks][R][num_kv_heads][head_dim / X][T][X]
+ *   V pool: [num_blocks][R][num_kv_heads][head_dim][T]
+ * For the 16-token blocks of the pages R = 1: [num_blocks][num_kv_heads][head_dim / X][16][X]
+ * and [num_blocks][num_kv_heads][head_dim][16].
  * The V layout is the pages' [num_blocks, num_heads, head_size, block_size] ([DD] §6.2);
  * K splits head_size into 16-byte chunks so that one token's chunk is 16 bytes.
  *

@@ -124,11 +124,21 @@ class Batch:
         return 16 // ELEM_BYTES[self.pool_dtype]
 
     def k_pool_shape(self):
+        """[NB][Hkv][D/X][16][X] for 16-token blocks; a larger block is R = block_size / 16
+        sub-blocks of 16 tokens, [NB][R][Hkv][D/X][16][X] (the pool layout of the ABI)."""
         D, X = self.head_dim, self.x
-        return (self.num_blocks, self.num_kv_heads, D // X, self.block_size, X)
+        T = min(self.block_size, 16)
+        R = self.block_size // T
+        if R == 1:
+            return (self.num_blocks, self.num_kv_heads, D // X, T, X)
+        return (self.num_blocks, R, self.num_kv_heads, D // X, T, X)
 
     def v_pool_shape(self):
-        return (self.num_blocks, self.num_kv_heads, self.head_dim, self.block_size)
+        T = min(self.block_size, 16)
+        R = self.block_size // T
+        if R == 1:
+            return (self.num_blocks, self.num_kv_heads, self.head_dim, T)
+        return (self.num_blocks, R, self.num_kv_heads, self.head_dim, T)
 
     def rows_per_seq(self) -> np.ndarray:
         if self.query_start_loc is None:
@@ -156,9 +166,9 @@ def build_batch(name: str, dtype: str, context_lens, rows_per_seq, num_q_heads: 
                 num_kv_heads: int, head_dim: int, rng, sigma: float = 1.0,
                 num_blocks: int | None = None, max_blocks_per_seq: int | None = None,
                 shared_prefix_blocks: int = 0, partition_size: int = 512,
-                force_qsl: bool = False) -> Batch:
+                force_qsl: bool = False, block_size: int = BLOCK_SIZE) -> Batch:
     """Assemble a batch from already-drawn context lengths (rng continues from there)."""
-    BS = BLOCK_SIZE
+    BS = int(block_size)
     ctx = np.asarray(context_lens, dtype=np.int64)
     nrows = np.asarray(rows_per_seq, dtype=np.int64)
     S = len(ctx)
@@ -243,7 +253,7 @@ def build_batch(name: str, dtype: str, context_lens, rows_per_seq, num_q_heads: 
                  q=q, key=key, value=value, slot=slot,
                  history=np.arange(num_history, dtype=np.int64),
                  new=np.arange(num_history, R, dtype=np.int64), seq_tokens=seq_tokens,
-                 sentinel_block=sentinel, partition_size=partition_size)
+                 sentinel_block=sentinel, partition_size=partition_size, block_size=BS)
 
 
 # --------------------------------------------------------------------------- presets

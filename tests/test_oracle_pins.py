@@ -42,21 +42,28 @@ def test_bf16_conversion_matches_bit_shift_all_bit_patterns():
 
 # ----------------------------------------------------------------- pool layout
 
-@pytest.mark.parametrize("dtype,D", [("f32", 8), ("f16", 16), ("bf16", 32)])
-def test_pool_layout_matches_declared_shapes(dtype, D):
-    """K is [NB][Hkv][D/X][BS][X], V is [NB][Hkv][D][BS] in row-major order (numpy's
-    ravel_multi_index over those shapes is the independent check)."""
-    NB, Hkv, BS = 3, 2, 16
+@pytest.mark.parametrize("dtype,D,BS", [("f32", 8, 16), ("f16", 16, 16), ("bf16", 32, 16),
+                                        ("f16", 16, 32), ("bf16", 32, 64), ("fp8", 32, 32),
+                                        ("f32", 8, 8)])
+def test_pool_layout_matches_declared_shapes(dtype, D, BS):
+    """K is [NB][R][Hkv][D/X][T][X], V is [NB][R][Hkv][D][T] in row-major order, a block of BS
+    tokens being R = BS / T sub-blocks of T = min(BS, 16) tokens (for BS = 16:
+    [NB][Hkv][D/X][16][X], [NB][Hkv][D][16]); numpy's ravel_multi_index over those shapes is
+    the independent check."""
+    NB, Hkv = 3, 2
     X = 16 // W.ELEM_BYTES[dtype]
-    g = oracle.make_geom(1, Hkv, Hkv, D, NB, 1, dtype, BS)
+    T = min(BS, 16)
+    R = BS // T
+    g = oracle.make_geom(1, Hkv, Hkv, D, NB, 1, dtype, BS,
+                         q_dtype="f16" if dtype == "fp8" else None)
     rng = np.random.default_rng(7)
     for _ in range(200):
         b, h, t, d = (int(rng.integers(NB)), int(rng.integers(Hkv)), int(rng.integers(BS)),
                       int(rng.integers(D)))
         assert oracle.k_offset(g, b, h, t, d) == np.ravel_multi_index(
-            (b, h, d // X, t, d % X), (NB, Hkv, D // X, BS, X))
-        assert oracle.v_offset(g, b, h, t, d) == np.ravel_multi_index((b, h, d, t),
-                                                                      (NB, Hkv, D, BS))
+            (b, t // T, h, d // X, t % T, d % X), (NB, R, Hkv, D // X, T, X))
+        assert oracle.v_offset(g, b, h, t, d) == np.ravel_multi_index(
+            (b, t // T, h, d, t % T), (NB, R, Hkv, D, T))
 
 
 def test_block_bytes_match_page_formula():
@@ -273,16 +280,19 @@ def test_causal_chunk_rows_match_torch_sdpa(prior):
 
 # ----------------------------------------------------------------- paged == dense
 
-@pytest.mark.parametrize("dtype,G,rows", [("f32", 1, 1), ("f16", 1, 1), ("bf16", 4, 1),
-                                          ("bf16", 4, 7), ("f16", 8, 3)])
-def test_paged_equals_dense_bitwise(dtype, G, rows):
+@pytest.mark.parametrize("dtype,G,rows,BS", [("f32", 1, 1, 16), ("f16", 1, 1, 16),
+                                             ("bf16", 4, 1, 16), ("bf16", 4, 7, 16),
+                                             ("f16", 8, 3, 16), ("f16", 1, 1, 32),
+                                             ("bf16", 4, 5, 64), ("f32", 2, 1, 32)])
+def test_paged_equals_dense_bitwise(dtype, G, rows, BS):
     """The paged walk (block table + layout + reshape_and_cache) equals the dense routine on
-    the generator's unpaged keys bit for bit: same operations in the same order."""
+    the generator's unpaged keys bit for bit: same operations in the same order, for 16-token
+    blocks and for 32- and 64-token blocks of 16-token sub-blocks."""
     rng = np.random.default_rng(51)
     D = 64 if dtype == "f32" else 128
     S = 5
-    ctx = rng.integers(rows, 75, size=S)
-    b = W.build_batch("pd", dtype, ctx, np.full(S, rows), 2 * G, 2, D, rng)
+    ctx = rng.integers(rows, 75 if BS == 16 else 200, size=S)
+    b = W.build_batch("pd", dtype, ctx, np.full(S, rows), 2 * G, 2, D, rng, block_size=BS)
     kp, vp = H.oracle_pools(b)
     out, lse = H.oracle_attention(b, kp, vp)
     q = H.q_f64(b)
