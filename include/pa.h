@@ -19,16 +19,21 @@
  *     pa_status; nothing is launched on error.  A failed launch returns PA_ERR_HIP.
  *     Device-resident values (block ids < num_blocks, context_lens <= max_blocks_per_seq
  *     * block_size, unique slots) are the caller's contract and are not checked.
- *   - block_size is 16 ("vLLM 架构源码解析 第1篇" §4.2: 16-token blocks).  head_dim is 64 or 128.
+ *   - block_size is 16 ("vLLM 架构源码解析 第1篇" §4.2: 16-token blocks), 32 or 64 (§5.1 shows
+ *     block_size = 32 as a configuration choice).  head_dim is 64 or 128.
  *     kv_dtype is PA_F32, PA_F16 or PA_BF16 (q, key, value and both pools share it), or
  *     PA_FP8_E4M3 (see "FP8 pools").
  *
- * Pool layout (part of this ABI).  elem = 4 (fp32) or 2 bytes, X = 16 / elem:
- *   k_cache: [num_blocks][num_kv_heads][head_dim / X][block_size][X]
- *   v_cache: [num_blocks][num_kv_heads][head_dim][block_size]
- * v_cache is the pages' [num_blocks, num_heads, head_size, block_size] ("vLLM 深度拆解"
- * §6.2); k_cache splits head_size into 16-byte chunks so one token's chunk is one 16-byte
- * load and the 16 tokens of a chunk are 256 contiguous bytes.
+ * Pool layout (part of this ABI).  elem = 4 (fp32), 2 (fp16, bf16) or 1 (FP8) bytes,
+ * X = 16 / elem, R = block_size / 16:
+ *   k_cache: [num_blocks][R][num_kv_heads][head_dim / X][16][X]
+ *   v_cache: [num_blocks][R][num_kv_heads][head_dim][16]
+ * For 16-token blocks (R = 1) v_cache is the pages' [num_blocks, num_heads, head_size,
+ * block_size] ("vLLM 深度拆解" §6.2); k_cache splits head_size into 16-byte chunks so one
+ * token's chunk is one 16-byte load and the 16 tokens of a chunk are 256 contiguous bytes.
+ * A larger block is R consecutive 16-token sub-blocks in that layout, token t of the block
+ * in sub-block t / 16 at position t % 16 (so slot / 16 names a sub-block for every block
+ * size).
  *
  * FP8 pools ("vLLM 深度拆解" §10.1 names FP8 KV with calibrated scales).  kv_dtype
  * PA_FP8_E4M3: one byte per element in the layout above with elem = 1, X = 16; q, key and
@@ -74,7 +79,7 @@ typedef struct {
   int32_t num_q_heads;        /* Hq */
   int32_t num_kv_heads;       /* Hkv; Hq % Hkv == 0, Hq / Hkv <= 16 */
   int32_t head_dim;           /* D: 64 or 128 */
-  int32_t block_size;         /* tokens per physical block: 16 */
+  int32_t block_size;         /* tokens per physical block: 16, 32 or 64 */
   int32_t num_blocks;         /* NB: blocks in each pool */
   int32_t max_blocks_per_seq; /* MB: row stride of block_tables */
   int32_t kv_dtype;           /* pa_dtype of k_cache, v_cache (and of q, key, value unless FP8) */

@@ -125,8 +125,8 @@ __device__ void chunk_item(const DecodeArgs& a, int s, int g, int cb, char* lds_
     const int e = 2 * u;
     if (wbase < 0 || e >= wbase + 128) {  // uniform; happens every 64 units
       wbase = e;
-      win0 = (e + lane < nblk) ? bt_row[e + lane] : 0;
-      win1 = (e + 64 + lane < nblk) ? bt_row[e + 64 + lane] : 0;
+      win0 = (e + lane < nblk) ? tile_block(bt_row, e + lane, a.blk_shift) : 0;
+      win1 = (e + 64 + lane < nblk) ? tile_block(bt_row, e + 64 + lane, a.blk_shift) : 0;
     }
     const int ia = e - wbase;
     const int64_t ba = ia < 64 ? readlane(win0, ia) : readlane(win1, ia - 64);

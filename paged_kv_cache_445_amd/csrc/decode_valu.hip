@@ -200,8 +200,8 @@ __device__ __forceinline__ void v_window(const DecodeArgs& a, const VPiece& p, i
   const int lane = lane_id();
   const int32_t* bt_row = a.block_tables + (int64_t)p.s * a.max_blocks_per_seq;
   const int c1 = min(p.t1, p.t0 + 128);
-  win0 = (p.t0 + lane < c1) ? bt_row[p.t0 + lane] : 0;
-  win1 = (p.t0 + 64 + lane < c1) ? bt_row[p.t0 + 64 + lane] : 0;
+  win0 = (p.t0 + lane < c1) ? tile_block(bt_row, p.t0 + lane, a.blk_shift) : 0;
+  win1 = (p.t0 + 64 + lane < c1) ? tile_block(bt_row, p.t0 + 64 + lane, a.blk_shift) : 0;
 }
 
 template <int DT, int D>
@@ -326,8 +326,8 @@ __device__ void valu_run(const DecodeArgs& a, VPiece p, VStart<DT, D, HPW>& vs,
   chunk(p.t0, min(p.t1, p.t0 + 128), vs.win0, vs.win1, std::true_type{});
   for (int c0 = p.t0 + 128; c0 < p.t1; c0 += 128) {
     const int c1 = min(p.t1, c0 + 128);
-    const int win0 = (c0 + lane < c1) ? bt_row[c0 + lane] : 0;
-    const int win1 = (c0 + 64 + lane < c1) ? bt_row[c0 + 64 + lane] : 0;
+    const int win0 = (c0 + lane < c1) ? tile_block(bt_row, c0 + lane, a.blk_shift) : 0;
+    const int win1 = (c0 + 64 + lane < c1) ? tile_block(bt_row, c0 + 64 + lane, a.blk_shift) : 0;
     chunk(c0, c1, win0, win1, std::false_type{});
   }
 }

@@ -39,12 +39,17 @@ pa_status check_geom(const pa_geom* g) {
   }
   if (!dtype_ok(g->q_dtype) || !dtype_ok(g->out_dtype)) return PA_ERR_UNSUPPORTED;
   if (g->out_dtype != g->q_dtype && g->out_dtype != PA_F32) return PA_ERR_UNSUPPORTED;
-  if (g->block_size != pa::kBlock) return PA_ERR_UNSUPPORTED;
+  if (g->block_size != 16 && g->block_size != 32 && g->block_size != 64) return PA_ERR_UNSUPPORTED;
+  // the kernels number 16-token sub-blocks in int32
+  if ((int64_t)g->num_blocks * (g->block_size / pa::kBlock) > 0x7fffffffLL) return PA_ERR_SHAPE;
   if (g->head_dim != 64 && g->head_dim != 128) return PA_ERR_UNSUPPORTED;
   if (g->num_q_heads / g->num_kv_heads > 16) return PA_ERR_UNSUPPORTED;
   if (g->num_seqs > kMaxSeqs) return PA_ERR_UNSUPPORTED;
   return PA_OK;
 }
+
+// log2 of the 16-token sub-blocks per block
+int blk_shift(const pa_geom* g) { return g->block_size == 64 ? 2 : g->block_size == 32 ? 1 : 0; }
 
 int current_device() {
   int dev = 0;
@@ -364,6 +369,7 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   a.odd_skew = odd_skew();
   a.max_rows = rt.max_rows;
   a.cols = rt.cols;
+  a.blk_shift = blk_shift(g);
 
   auto decode = [&] {
     return rt.path ? pa::launch_mfma_decode(g->kv_dtype, pa::MODE_EVEN, a, grid, st)
@@ -425,6 +431,7 @@ pa_status pa_decode_partitioned(float* tmp_out, float* max_logits, float* exp_su
   a.partition_units = partition_size / (mf ? pa::kMfmaUnit : pa::kValuUnit);
   a.max_rows = 1;
   a.cols = g->num_q_heads / g->num_kv_heads;
+  a.blk_shift = blk_shift(g);
   const int grid = split_grid(g, pa::MODE_PARTITION, mf ? 1 : 0);
   hipError_t e = mf ? pa::launch_mfma_decode(g->kv_dtype, pa::MODE_PARTITION, a, grid, (hipStream_t)stream)
                     : pa::launch_valu_decode(g->kv_dtype, pa::MODE_PARTITION, a, grid, (hipStream_t)stream);

@@ -1,9 +1,10 @@
 // pa_device.h — device-side helpers shared by the gfx950 kernels of libpa.so.
 //
 // Pool layout (the ABI of include/pa.h): elem E bytes, X = 16 / E elements per 16-byte chunk,
-//   K tile of (block, kv_head): [D / X chunks][16 tokens][X]   = 16 * D * E bytes
-//   V tile of (block, kv_head): [D dims][16 tokens]            = 16 * D * E bytes
-// Tiles of consecutive kv heads of one block are adjacent.
+//   K tile of (16-token sub-block, kv_head): [D / X chunks][16 tokens][X]   = 16 * D * E bytes
+//   V tile of (16-token sub-block, kv_head): [D dims][16 tokens]            = 16 * D * E bytes
+// Tiles of consecutive kv heads of one sub-block are adjacent; a block of 16 R tokens is R
+// consecutive sub-blocks.  The kernels address sub-blocks ("blocks" below: 16 tokens).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -30,6 +31,16 @@ typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// ---------------------------------------------------------------- block table
+
+// Pool sub-block of a sequence's 16-token tile j.  A block of 16 R tokens (R = 1 << shift) is
+// R consecutive 16-token sub-blocks of the pool, so table entry j >> shift names sub-blocks
+// R * entry .. R * entry + R - 1 and tile j is the (j mod R)-th of them.  shift = 0: the
+// table entry itself.
+__device__ __forceinline__ int32_t tile_block(const int32_t* bt_row, int j, int shift) {
+  return (bt_row[j >> shift] << shift) | (j & ((1 << shift) - 1));
+}
 
 // ---------------------------------------------------------------- 16-byte global loads
 

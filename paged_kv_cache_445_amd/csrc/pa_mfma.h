@@ -248,8 +248,8 @@ __device__ __forceinline__ void mfma_stream(const DecodeArgs& a, int s, int g, i
   for (int c0 = u0; c0 < u1; c0 += 64) {
     const int c1 = min(u1, c0 + 64);
     const int b0 = 2 * c0, bend = min(nblk, 2 * c1);
-    const int win0 = (b0 + lane < bend) ? bt_row[b0 + lane] : 0;
-    const int win1 = (b0 + 64 + lane < bend) ? bt_row[b0 + 64 + lane] : 0;
+    const int win0 = (b0 + lane < bend) ? tile_block(bt_row, b0 + lane, a.blk_shift) : 0;
+    const int win1 = (b0 + 64 + lane < bend) ? tile_block(bt_row, b0 + 64 + lane, a.blk_shift) : 0;
     auto blk = [&](int e) -> int64_t { return e < 64 ? readlane(win0, e) : readlane(win1, e - 64); };
     auto issue = [&](MfmaK<DT, D>& kb, MfmaV<DT, D>& vb, int u) {
       const int e = 2 * (u - c0);

@@ -66,11 +66,15 @@ def test_kv_cache_bytes_and_validation(lib):
     g = _g(num_kv_heads=32, num_q_heads=32, num_blocks=8448, kv_dtype=1, out_dtype=1)
     # 8448 blocks x 32 heads x 128 x 16 x 2 bytes per pool
     assert lib.pa_kv_cache_bytes(ctypes.byref(g)) == 8448 * 32 * 128 * 16 * 2
-    for bad in (_g(head_dim=96), _g(block_size=32), _g(num_q_heads=6, num_kv_heads=4),
+    for bad in (_g(head_dim=96), _g(block_size=48), _g(block_size=8), _g(block_size=128),
+                _g(num_q_heads=6, num_kv_heads=4),
                 _g(kv_dtype=7), _g(out_dtype=1), _g(num_q_heads=64, num_kv_heads=2),
                 _g(num_seqs=-1), _g(q_dtype=1), _g(kv_dtype=3, q_dtype=2),
                 _g(kv_dtype=3, k_scale=0.0), _g(kv_dtype=3, v_scale=float("inf"))):
         assert lib.pa_kv_cache_bytes(ctypes.byref(bad)) == 0
+    # 32- and 64-token blocks
+    assert lib.pa_kv_cache_bytes(ctypes.byref(_g(block_size=32))) == 64 * 2 * 128 * 32 * 2
+    assert lib.pa_kv_cache_bytes(ctypes.byref(_g(block_size=64))) == 64 * 2 * 128 * 64 * 2
     # FP8 pools: one byte per element
     g8 = _g(num_kv_heads=32, num_q_heads=32, num_blocks=8448, kv_dtype=3, out_dtype=1)
     assert lib.pa_kv_cache_bytes(ctypes.byref(g8)) == 8448 * 32 * 128 * 16
