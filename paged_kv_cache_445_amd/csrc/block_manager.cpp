@@ -72,12 +72,18 @@ struct pa_block_manager {
     return k;
   }
 
-  // register a full block under (parent, tokens) unless that key already names a block
-  void remember(int32_t block, int32_t parent, const int32_t* tokens) {
-    std::vector<int32_t> k = key(parent, tokens);
-    if (cache.count(k) || !key_of[block].empty()) return;
-    cache.emplace(k, block);
-    key_of[block] = std::move(k);
+  // register a full block under (parent, tokens) unless that key already names a block; the
+  // cache only saves recomputation, so a block that cannot be registered (no host memory) is
+  // simply not shared
+  void remember(int32_t block, int32_t parent, const int32_t* tokens) noexcept {
+    try {
+      std::vector<int32_t> k = key(parent, tokens);
+      if (cache.count(k) || !key_of[block].empty()) return;
+      std::vector<int32_t> mine = k;
+      cache.emplace(std::move(k), block);
+      key_of[block] = std::move(mine);
+    } catch (const std::bad_alloc&) {
+    }
   }
 
   Seq* seq(int32_t id) {
@@ -157,14 +163,18 @@ pa_status pa_bm_add_sequence(pa_block_manager* bm, const int32_t* token_ids, int
     }
     const int64_t fresh = nblk - (int64_t)hits.size();
     if (fresh > (int64_t)bm->free_list.size()) return PA_ERR_NO_BLOCKS;
-    bm->seqs.reserve(bm->seqs.size() + 1);  // the only allocations that may throw come first
-    const int32_t id = bm->new_seq_id();
-    Seq& s = bm->seqs[id];
-    s = Seq();
+    // build the sequence aside, then commit: nothing below the reservations can throw
+    Seq s;
     s.live = true;
     s.track = token_ids != nullptr;
     s.len = num_tokens;
     s.blocks.reserve(nblk);
+    if (token_ids) {
+      s.tail.reserve(BS);
+      s.tail.assign(token_ids + (int64_t)(num_tokens / BS) * BS, token_ids + num_tokens);
+    }
+    bm->seqs.reserve(bm->seqs.size() + 1);
+    const int32_t id = bm->new_seq_id();
     for (int32_t b : hits) {
       ++bm->ref[b];
       s.blocks.push_back(b);
@@ -175,8 +185,7 @@ pa_status pa_bm_add_sequence(pa_block_manager* bm, const int32_t* token_ids, int
       if (token_ids && (j + 1) * BS <= num_tokens)
         bm->remember(b, j ? s.blocks[j - 1] : -1, token_ids + j * BS);
     }
-    if (token_ids)
-      s.tail.assign(token_ids + (int64_t)(num_tokens / BS) * BS, token_ids + num_tokens);
+    bm->seqs[id] = std::move(s);
     *seq_id = id;
     *num_cached_tokens = (int32_t)hits.size() * BS;
     return PA_OK;
@@ -189,10 +198,11 @@ pa_status pa_bm_fork(pa_block_manager* bm, int32_t parent, int32_t* child_id) {
   if (!bm || !child_id) return PA_ERR_NULL;
   if (!bm->seq(parent)) return PA_ERR_SHAPE;
   try {
+    Seq c = bm->seqs[parent];  // same blocks, length and pending tail tokens
+    bm->seqs.reserve(bm->seqs.size() + 1);
     const int32_t id = bm->new_seq_id();
-    Seq& c = bm->seqs[id];
-    c = bm->seqs[parent];  // same blocks, length and pending tail tokens
     for (int32_t b : c.blocks) ++bm->ref[b];
+    bm->seqs[id] = std::move(c);
     *child_id = id;
     return PA_OK;
   } catch (const std::bad_alloc&) {
