@@ -285,28 +285,11 @@ def main():
         pa.decode(db.out, db.q, kc, vc, db.block_tables, db.context_lens, db.qsl, db.scale,
                   db.workspace, db.geom, max_query_len=db.max_query_len)
 
-    # one query row per sequence: the step is pa_decode_append (the cache write runs beside
-    # the decode); with multi-row sequences it is the cache write, then pa_decode
-    append = b.query_start_loc is None
-
-    def decode_append(i):
-        kc, vc = pools[i % copies]
-        pa.decode_append(db.out, db.q, db.key_new, db.value_new, db.slot_new, kc, vc,
-                         db.block_tables, db.context_lens, db.scale, db.workspace, db.geom)
-
-    def step(i):
-        if append:
-            decode_append(i)
-        else:
-            write(i)
-            decode(i)
-
-    timed_call = decode_append if append else decode
-
     print(f"[bench] warmup {args.warmup} steps, {copies} pool copies", file=sys.stderr,
           flush=True)
     for i in range(args.warmup):
-        step(i)
+        write(i)
+        decode(i)
     torch.cuda.synchronize()
 
     # timed region: K whole steps (cache write + decode), nothing else on the stream
@@ -315,21 +298,21 @@ def main():
     t0 = time.perf_counter()
     ev_steps[0].record(stream)
     for i in range(args.steps):
-        step(args.warmup + i)
+        write(args.warmup + i)
+        decode(args.warmup + i)
     ev_steps[1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     print(f"[bench] timed {args.steps} steps in {wall:.4f} s "
           f"(events: {ev_steps[0].elapsed_time(ev_steps[1]):.3f} ms)", file=sys.stderr, flush=True)
 
-    # the decode call's own duration (pa_decode_append or pa_decode): the same calls back to
-    # back between one pair of HIP events on the stream it runs on (an event between two
-    # kernels stalls the next dispatch, so per-call events would add their own gap to every
-    # call)
+    # pa_decode's own duration: the same calls back to back between one pair of HIP events
+    # on the stream it runs on (an event between two kernels stalls the next dispatch, so
+    # per-call events would add their own gap to every call)
     ev_dec = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
     ev_dec[0].record(stream)
     for i in range(args.steps):
-        timed_call(args.warmup + i)
+        decode(args.warmup + i)
     ev_dec[1].record(stream)
     torch.cuda.synchronize()
     dec_ms = [ev_dec[0].elapsed_time(ev_dec[1]) / args.steps]
@@ -400,9 +383,8 @@ def main():
         "pa_decode_us": round(dec_avg_ms * 1e3, 3),
         "roofline": {
             "bound": bound,
-            "kernel": ("pa_decode_append (decode kernel with in-kernel split merge; the cache "
-                       "write runs beside it on a second stream)" if append else
-                       "pa_decode (decode kernel with in-kernel split merge + chunk kernel)"),
+            "kernel": "pa_decode (decode kernel with in-kernel split merge"
+                      + (" + chunk kernel)" if b.query_start_loc is not None else ")"),
             "achieved": round(achieved, 2),
             "peak": peak,
             "unit": punit,

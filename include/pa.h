@@ -158,26 +158,6 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
                     void* stream);
 
 /*
- * One decode step with its cache write ("vLLM 架构源码解析 第1篇" §3.3.3: reshape_and_cache,
- * then paged_attention), one query row per sequence: the same result as
- * pa_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, num_seqs) followed by
- * pa_decode(..., query_start_loc = NULL, ...).
- *   key, value     [num_seqs][num_kv_heads][head_dim]: row s is the token at position
- *                  context_lens[s] - 1 of sequence s (this step's token), stored at
- *                  slot_mapping[s] (int64 [num_seqs]; negative: no new token for s)
- *   the rest       as in pa_decode
- * On the vector path (MHA or fp32 pools; 16-bit or fp32) the cache write runs on a second
- * stream beside the decode, which reads each sequence's newest key and value from key /
- * value instead of the pools; the caller's stream waits for both.  Other geometries (the
- * matrix-core path, FP8 pools) run the two calls in stream order.
- */
-pa_status pa_decode_append(void* out, const void* q, const void* key, const void* value,
-                           const int64_t* slot_mapping, void* k_cache, void* v_cache,
-                           const int32_t* block_tables, const int32_t* context_lens, float scale,
-                           void* workspace, size_t workspace_bytes, const pa_geom* geom,
-                           void* stream);
-
-/*
  * Split-context partials (flash-decoding) for decode rows: one query row per sequence
  * (row r = sequence r, num_q_rows == num_seqs).  Partition p of a row is its key positions
  * [p * partition_size, (p + 1) * partition_size) below context_lens[r].

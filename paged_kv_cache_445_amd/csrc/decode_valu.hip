@@ -50,27 +50,7 @@ template <int DT, int D>
 struct VTile {
   uint4 k[VCfg<DT, D>::NK];
   uint4 v[VCfg<DT, D>::NV];
-  uint32_t pv[VCfg<DT, D>::NV];  // MODE_APPEND: the new token's V element of each V load
 };
-
-// replace element e (uniform) of a 16-byte V piece by the bits of `x` (elem E bytes)
-template <int DT>
-__device__ __forceinline__ void set_elem(uint4& v, int e, uint32_t x) {
-  if constexpr (DtInfo<DT>::bytes == 4) {
-    if (e == 0) v.x = x;
-    else if (e == 1) v.y = x;
-    else if (e == 2) v.z = x;
-    else v.w = x;
-  } else {
-    const int w = e >> 1;
-    const uint32_t keep = (e & 1) ? 0x0000ffffu : 0xffff0000u;
-    const uint32_t put = (e & 1) ? (x << 16) : (x & 0xffffu);
-    if (w == 0) v.x = (v.x & keep) | put;
-    else if (w == 1) v.y = (v.y & keep) | put;
-    else if (w == 2) v.z = (v.z & keep) | put;
-    else v.w = (v.w & keep) | put;
-  }
-}
 
 template <int DT, int D>
 struct VState {
@@ -259,7 +239,7 @@ __device__ __forceinline__ void v_start(const DecodeArgs& a, const VPiece& p,
 // loop (the first chunk's come with vs), so the loop itself only waits for tile loads.  A
 // step is one tile of one head; the loads of the next step are in flight while a step is
 // computed.
-template <int DT, int D, int HPW, bool APPEND = false>
+template <int DT, int D, int HPW>
 __device__ void valu_run(const DecodeArgs& a, VPiece p, VStart<DT, D, HPW>& vs,
                          VState<DT, D> (&st)[HPW], float* pw) {
   using C = VCfg<DT, D>;
@@ -285,56 +265,14 @@ __device__ void valu_run(const DecodeArgs& a, VPiece p, VStart<DT, D, HPW>& vs,
   const int64_t blk_stride = (int64_t)a.num_kv_heads * C::TILE;
   const int32_t* bt_row = a.block_tables + (int64_t)p.s * a.max_blocks_per_seq;
 
-  // MODE_APPEND: the tile holding position ctx - 1 takes that token from the step's new key
-  // and value rows.  K: the four lanes of that token load their chunks from the key row
-  // (16 bytes apart, 4 chunks per load step) instead of the pool.  V: the lanes whose token
-  // group holds it load its element of their dimension, which replaces the pooled one.
-  const int new_tile = APPEND && p.ctx > 0 && p.t1 * kBlock >= p.ctx &&
-                               a.new_slots[p.s] >= 0 ? (p.ctx - 1) / kBlock : -1;
-  const int new_tok = (p.ctx - 1) & (kBlock - 1);
-  const bool k_new = (lane & 15) == new_tok;                 // this lane's K token
-  const bool v_new = (lane % C::LPD) == new_tok / C::X;      // this lane's V token group
-  auto new_row = [&](const void* base, int j) {
-    const int64_t kvh = (p.h0 + 4 * j) / (a.num_q_heads / a.num_kv_heads);
-    return reinterpret_cast<const char*>(base) +
-           ((int64_t)p.s * a.num_kv_heads + kvh) * D * C::E;
-  };
-
   // one chunk [c0, c1); FIRST: its first step is already in flight in vs.first
   auto chunk = [&](int c0, int c1, int win0, int win1, auto first) {
     auto issue = [&](VTile<DT, D>& t, int tt, int j) {
       const int idx = tt - c0;
       const int64_t blk = idx < 64 ? readlane(win0, idx) : readlane(win1, idx - 64);
-      if constexpr (APPEND) {
-        const bool nt = tt == new_tile;  // uniform
-        const char* kp = kc[j] + blk * blk_stride + off;
-        const bool kn = nt && k_new;
-        const char* kb = kn ? new_row(a.new_key, j) + 16 * (lane >> 4) : kp;
-        const int ks = kn ? 64 : 1024;
-#pragma unroll
-        for (int i = 0; i < C::NK; ++i) t.k[i] = ld16(kb + ks * i);
-        const char* vp = vc[j] + blk * blk_stride + off;
-#pragma unroll
-        for (int e = 0; e < C::NV; ++e) t.v[e] = ld16(vp + 1024 * e);
-        const bool vn = nt && v_new;
-        const char* vr = new_row(a.new_value, j) + C::E * (lane / C::LPD);
-#pragma unroll
-        for (int e = 0; e < C::NV; ++e) {
-          const char* ve = vr + C::E * e * C::DPL;
-          if constexpr (C::E == 4)
-            t.pv[e] = vn ? *reinterpret_cast<const uint32_t*>(ve) : 0u;
-          else
-            t.pv[e] = vn ? (uint32_t)*reinterpret_cast<const uint16_t*>(ve) : 0u;
-        }
-      } else {
-        v_issue<DT, D>(t, kc[j] + blk * blk_stride, vc[j] + blk * blk_stride, off);
-      }
+      v_issue<DT, D>(t, kc[j] + blk * blk_stride, vc[j] + blk * blk_stride, off);
     };
     auto step = [&](VTile<DT, D>& t, int tt, int j) {
-      if (APPEND && tt == new_tile && v_new) {
-#pragma unroll
-        for (int e = 0; e < C::NV; ++e) set_elem<DT>(t.v[e], new_tok % C::X, t.pv[e]);
-      }
       const int valid = p.ctx - tt * kBlock;
       if (valid >= kBlock)
         v_tile<DT, D, false>(st[j], t, vs.q[j], a.scale_log2, kBlock, pw);
@@ -346,10 +284,7 @@ __device__ void valu_run(const DecodeArgs& a, VPiece p, VStart<DT, D, HPW>& vs,
     // only that step; the last tiles of the chunk are peeled.
     VTile<DT, D>& ta = vs.first;
     VTile<DT, D> tb;
-    if constexpr (!decltype(first)::value)
-      issue(ta, c0, 0);
-    else if (APPEND && c0 == new_tile)  // the early first step read the pool: load it again
-      issue(ta, c0, 0);
+    if constexpr (!decltype(first)::value) issue(ta, c0, 0);
     int tt = c0;
     if constexpr (HPW == 1) {
       for (; tt + 2 < c1; tt += 2) {
@@ -515,7 +450,7 @@ __global__ __launch_bounds__(kWG) void valu_decode_kernel(DecodeArgs a) {
   const int64_t W = (int64_t)gridDim.x * kWavesPerWG;
   const int64_t w = (int64_t)blockIdx.x * kWavesPerWG + wave;
 
-  if constexpr (MODE != MODE_PARTITION) {
+  if constexpr (MODE == MODE_EVEN) {
     PlanIn pin{a.context_lens, a.qsl, S, kValuUnit, a.seg_extra, 1};
     build_plan(base, pin);
     zero_empty_rows<DT>(pin, a.out, a.num_q_heads, D, w, W, a.out_f32);
@@ -580,7 +515,7 @@ __global__ __launch_bounds__(kWG) void valu_decode_kernel(DecodeArgs a) {
             seen = counter_peek(cnt);  // consumed after the tiles
           }
           VState<DT, D> st[HPW];
-          valu_run<DT, D, HPW, MODE == MODE_APPEND>(a, cur.p, vs, st, pw);
+          valu_run<DT, D, HPW>(a, cur.p, vs, st, pw);
           float l[HPW];
 #pragma unroll
           for (int j = 0; j < HPW; ++j) l[j] = v_finish<DT, D>(st[j], a.v_factor);
@@ -660,10 +595,10 @@ static void launch_k(const DecodeArgs& a, int grid, size_t lds, hipStream_t st) 
 
 template <int DT, int D, int MODE>
 static void launch_hpw(const DecodeArgs& a, int grid, size_t lds, hipStream_t st) {
-  if constexpr (MODE != MODE_PARTITION) {
+  if constexpr (MODE == MODE_EVEN) {
     // fp32 queries fill twice the registers: at most two heads per wave; FP8 widens to
-    // fp32 in registers, and MODE_APPEND holds the new token's values: at most four
-    if constexpr (DT != DT_F32 && DT != DT_FP8 && MODE != MODE_APPEND) {
+    // fp32 in registers: at most four
+    if constexpr (DT != DT_F32 && DT != DT_FP8) {
       if (a.heads_per_wave == 8) return launch_k<DT, D, MODE, 8>(a, grid, lds, st);
     }
     if constexpr (DT != DT_F32) {
@@ -684,14 +619,8 @@ static hipError_t launch_d(const DecodeArgs& a, int grid, hipStream_t st) {
   return hipGetLastError();
 }
 
-// FP8 pools run in MODE_EVEN only (pa_decode_partitioned rejects them, pa_decode_append
-// writes them first); MODE_APPEND for 16-bit and fp32 pools
+// FP8 pools run in MODE_EVEN only (pa_decode_partitioned rejects them)
 hipError_t launch_valu_decode(int dt, int mode, const DecodeArgs& a, int grid, hipStream_t st) {
-  if (mode == MODE_APPEND) {
-    if (dt == DT_F32) return launch_d<DT_F32, MODE_APPEND>(a, grid, st);
-    if (dt == DT_F16) return launch_d<DT_F16, MODE_APPEND>(a, grid, st);
-    return launch_d<DT_BF16, MODE_APPEND>(a, grid, st);
-  }
   if (mode == MODE_EVEN) {
     if (dt == DT_F32) return launch_d<DT_F32, MODE_EVEN>(a, grid, st);
     if (dt == DT_F16) return launch_d<DT_F16, MODE_EVEN>(a, grid, st);

@@ -393,81 +393,6 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   return e == hipSuccess && ed == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
-pa_status pa_decode_append(void* out, const void* q, const void* key, const void* value,
-                           const int64_t* slot_mapping, void* k_cache, void* v_cache,
-                           const int32_t* block_tables, const int32_t* context_lens, float scale,
-                           void* workspace, size_t workspace_bytes, const pa_geom* g,
-                           void* stream) {
-  const pa_status gs = check_geom(g);
-  if (gs != PA_OK) return gs;
-  if (g->num_seqs == 0) return PA_OK;
-  if (!key || !value || !slot_mapping || !k_cache || !v_cache) return PA_ERR_NULL;
-  hipStream_t st = (hipStream_t)stream;
-  const Route rt = route(g, 1);
-  if (rt.path != 0 || g->kv_dtype == PA_FP8_E4M3) {
-    // matrix-core route (its tiles are not patched) and FP8 pools (the new values must be
-    // quantised first): the cache write, then the decode, in stream order
-    const pa_status w = pa_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping,
-                                             g->num_seqs, g, stream);
-    if (w != PA_OK) return w;
-    return pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, nullptr, g->num_seqs,
-                     0, scale, workspace, workspace_bytes, g, stream);
-  }
-  if (!out || !q || !block_tables || !context_lens) return PA_ERR_NULL;
-  if (!std::isfinite(scale)) return PA_ERR_SHAPE;
-  const int grid = split_grid(g, pa::MODE_EVEN, rt.path);
-  const size_t need = even_workspace_bytes(g, rt);
-  if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
-  const size_t slots = even_slots(g, grid, rt);
-  pa::DecodeArgs a{};
-  a.out = out;
-  a.q = q;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
-  a.block_tables = block_tables;
-  a.context_lens = context_lens;
-  a.counters = static_cast<int32_t*>(workspace);
-  a.part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + counter_bytes());
-  a.part_m = a.part_o + slots * g->head_dim;
-  a.part_l = a.part_m + slots;
-  a.num_seqs = g->num_seqs;
-  a.num_q_heads = g->num_q_heads;
-  a.num_kv_heads = g->num_kv_heads;
-  a.head_dim = g->head_dim;
-  a.max_blocks_per_seq = g->max_blocks_per_seq;
-  a.out_f32 = g->out_dtype == PA_F32 && g->kv_dtype != PA_F32;
-  a.scale_log2 = scale_to_log2(scale);
-  a.seg_extra = seg_extra_override() >= 0 ? seg_extra_override() : kSegExtra[0];
-  // the append kernels keep the new token's values in registers: at most 4 heads per wave
-  // (fewer heads per wave use fewer of the workspace's partial slots)
-  a.heads_per_wave = heads_per_wave(g) > 4 ? 4 : heads_per_wave(g);
-  a.odd_skew = odd_skew();
-  a.max_rows = 1;
-  a.cols = 1;
-  a.blk_shift = blk_shift(g);
-  a.new_key = key;
-  a.new_value = value;
-  a.new_slots = slot_mapping;
-  const int64_t X = 16 / (int64_t)elem_bytes(g->kv_dtype);
-  if (((int64_t)g->num_seqs * g->num_kv_heads * (g->head_dim / X + g->head_dim) + 255) / 256 >
-      0x7fffffffLL)
-    return PA_ERR_SHAPE;
-  pa::ReshapeArgs w{key, value, k_cache, v_cache, slot_mapping, g->num_seqs, g->num_kv_heads,
-                    g->head_dim, g->k_scale, g->v_scale};
-  // the cache write on the side stream, beside the decode that reads the new tokens from key
-  // and value; the caller's stream waits for both
-  SideStream* side = side_stream(current_device());
-  if (!side) return PA_ERR_HIP;
-  std::lock_guard<std::mutex> lock(side->mu);
-  hipError_t e = hipEventRecord(side->fork, st);
-  if (e == hipSuccess) e = hipStreamWaitEvent(side->stream, side->fork, 0);
-  if (e == hipSuccess) e = pa::launch_reshape(g->kv_dtype, w, side->stream);
-  const hipError_t ed = pa::launch_valu_decode(g->kv_dtype, pa::MODE_APPEND, a, grid, st);
-  if (e == hipSuccess) e = hipEventRecord(side->join, side->stream);
-  if (e == hipSuccess) e = hipStreamWaitEvent(st, side->join, 0);
-  return e == hipSuccess && ed == hipSuccess ? PA_OK : PA_ERR_HIP;
-}
-
 pa_status pa_decode_partitioned(float* tmp_out, float* max_logits, float* exp_sums,
                                 const void* q, const void* k_cache, const void* v_cache,
                                 const int32_t* block_tables, const int32_t* context_lens,

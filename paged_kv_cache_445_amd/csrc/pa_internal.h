@@ -23,10 +23,6 @@ enum SplitMode : int {
   // pa_decode_partitioned: fixed partitions of `partition_units` units; every (seq,
   // segment, partition) is one item, written to tmp_out / max_logits / exp_sums.
   MODE_PARTITION = 1,
-  // pa_decode_append (vector kernel): MODE_EVEN, and each sequence's newest key and value
-  // (position ctx - 1) are taken from new_key / new_value rather than from the pools, which
-  // a concurrent cache write may still be filling.
-  MODE_APPEND = 2,
 };
 
 struct DecodeArgs {
@@ -58,9 +54,6 @@ struct DecodeArgs {
   int32_t cols;             // MODE_EVEN, matrix-core path: query columns per partial slot
   float v_factor;           // DT_FP8: the outputs' factor (v_scale)
   int32_t blk_shift;        // log2(block_size / 16): table entries name 2^blk_shift sub-blocks
-  const void* new_key;      // MODE_APPEND: [num_seqs][Hkv][D], row s = position ctx_s - 1
-  const void* new_value;
-  const int64_t* new_slots; // MODE_APPEND: [num_seqs]; a negative slot: no new token
 };
 
 struct ReshapeArgs {

@@ -55,9 +55,6 @@ _lib.pa_copy_blocks.argtypes = [_vp, _vp, _vp, ctypes.c_int64, _G, _vp]
 _lib.pa_decode.restype = ctypes.c_int
 _lib.pa_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_int32,
                            ctypes.c_float, _vp, ctypes.c_size_t, _G, _vp]
-_lib.pa_decode_append.restype = ctypes.c_int
-_lib.pa_decode_append.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float,
-                                  _vp, ctypes.c_size_t, _G, _vp]
 _lib.pa_decode_partitioned.restype = ctypes.c_int
 _lib.pa_decode_partitioned.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32,
                                        ctypes.c_float, ctypes.c_int32, ctypes.c_int32, _G, _vp]
@@ -137,17 +134,6 @@ def decode(out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc
                           _p(context_lens), _p(query_start_loc), int(q.shape[0]),
                           int(max_query_len), float(scale), _p(workspace), ws_bytes,
                           ctypes.byref(g), _stream(stream)))
-
-
-def decode_append(out, q, key, value, slot_mapping, k_cache, v_cache, block_tables,
-                  context_lens, scale, workspace, g: Geom, stream=None):
-    """Cache write of each sequence's newest token plus the decode step (one row each)."""
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check("pa_decode_append",
-           _lib.pa_decode_append(_p(out), _p(q), _p(key), _p(value), _p(slot_mapping),
-                                 _p(k_cache), _p(v_cache), _p(block_tables), _p(context_lens),
-                                 float(scale), _p(workspace), ws_bytes, ctypes.byref(g),
-                                 _stream(stream)))
 
 
 def decode_partitioned(tmp_out, max_logits, exp_sums, q, k_cache, v_cache, block_tables,

@@ -168,18 +168,3 @@ def test_block_manager_null_and_size_checks(lib):
     lib.pa_bm_add_sequence.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                                        ctypes.c_void_p, ctypes.c_void_p]
     assert lib.pa_bm_add_sequence(None, None, 3, None, None) == -1
-
-
-def test_decode_append_host_checks(lib):
-    vp = ctypes.c_void_p
-    g = _g()
-    dummy = vp(16)  # never dereferenced: every call below fails its host checks first
-    lib.pa_decode_append.restype = ctypes.c_int
-    lib.pa_decode_append.argtypes = [vp] * 9 + [ctypes.c_float, vp, ctypes.c_size_t,
-                                                ctypes.POINTER(Geom), vp]
-    assert lib.pa_decode_append(dummy, dummy, None, dummy, dummy, dummy, dummy, dummy, dummy, 0.1,
-                                dummy, 1 << 30, ctypes.byref(g), None) == -1
-    assert lib.pa_decode_append(*([dummy] * 9), 0.1, dummy, 1 << 30,
-                                ctypes.byref(_g(head_dim=80)), None) == -3
-    assert lib.pa_decode_append(*([None] * 9), 0.1, None, 0, ctypes.byref(_g(num_seqs=0)),
-                                None) == 0
