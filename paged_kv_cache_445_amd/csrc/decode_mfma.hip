@@ -24,7 +24,7 @@ namespace pa {
 // column is one (row, query head) pair: column c is row qsl[s] + c / G, head g * G + c % G,
 // and the nr * G <= 16 columns of the sequence's nr rows are scored together.  Row j sits at
 // position ctx - nr + j and sees keys [0, ctx - nr + j].
-template <int DT, int D, bool MULTI>
+template <int DT, int D, bool MULTI, bool LEAN = false>
 __device__ void mfma_attend(const DecodeArgs& a, int s, int g, int u0, int u1, int ctx, int nr,
                             MfmaState<DT, D>& st) {
   using C = MfmaCfg<DT, D>;
@@ -71,13 +71,27 @@ __device__ void mfma_attend(const DecodeArgs& a, int s, int g, int u0, int u1, i
   } else {
     const int last0 = ctx - nr;                 // last visible key of the first row
     const int mine = min(last0 + jr, ctx - 1);  // ... of this lane's column (padding: ctx - 1)
-    mfma_stream<DT, D>(a, s, g, u0, u1, ctx, [&](MfmaK<DT, D>& kb, MfmaV<DT, D>& vb, int u) {
+    auto scores = [&](MfmaK<DT, D>& kb, int u) {
       const int t0 = u * kMfmaUnit;
       if (last0 - t0 >= kMfmaUnit - 1)  // every column sees the whole unit
-        mfma_unit<DT, D, false, false>(st, kb, vb, qb, a.scale_log2, kMfmaUnit - 1, kMfmaUnit);
-      else  // per-column limits; a column may see no key of this piece yet
-        mfma_unit<DT, D, true, true>(st, kb, vb, qb, a.scale_log2, mine - t0, ctx - t0);
-    });
+        return mfma_scores<DT, D, false, false>(st, kb, qb, a.scale_log2, kMfmaUnit - 1);
+      // per-column limits; a column may see no key of this piece yet
+      return mfma_scores<DT, D, true, true>(st, kb, qb, a.scale_log2, mine - t0);
+    };
+    auto pv = [&](MfmaV<DT, D>& vb, const MfmaP<DT>& p, int u) {
+      const int t0 = u * kMfmaUnit;
+      if (last0 - t0 >= kMfmaUnit - 1)
+        mfma_pv<DT, D, false>(st, vb, p, kMfmaUnit);
+      else
+        mfma_pv<DT, D, true>(st, vb, p, ctx - t0);
+    };
+    if constexpr (LEAN) {
+      mfma_stream_lean<DT, D>(a, s, g, u0, u1, ctx, scores, pv);
+    } else {
+      mfma_stream<DT, D>(a, s, g, u0, u1, ctx, [&](MfmaK<DT, D>& kb, MfmaV<DT, D>& vb, int u) {
+        pv(vb, scores(kb, u), u);
+      });
+    }
   }
 }
 
@@ -154,8 +168,13 @@ __device__ void m_split_finish(const DecodeArgs& a, const MfmaState<DT, D>& st, 
   counter_reset(cnt);
 }
 
-template <int DT, int D, int MODE, bool MULTI>
-__global__ __launch_bounds__(kWG) void mfma_decode_kernel(DecodeArgs a) {
+// LEAN (multi-row batches whose chunk kernel runs beside this one) streams with one operand
+// buffer and is built for two waves per SIMD: with ~340 registers per wave the decode
+// kernel's waves keep the chunk kernel's off the CUs, and the two then run one after the
+// other (mixed chunked-prefill step: 788 -> 646 us).  Alone, the two-buffer stream is faster.
+template <int DT, int D, int MODE, bool MULTI, bool LEAN>
+__global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(LEAN ? 2 : 1))) void
+mfma_decode_kernel(DecodeArgs a) {
   extern __shared__ int32_t lds[];
   int32_t* base = lds;
   const int wave = threadIdx.x / kWave;
@@ -199,7 +218,7 @@ __global__ __launch_bounds__(kWG) void mfma_decode_kernel(DecodeArgs a) {
             seen = counter_peek(cnt);  // consumed after the units
           }
           MfmaState<DT, D> st;
-          mfma_attend<DT, D, MULTI>(a, s, g, u0, u1, ctx, nr, st);
+          mfma_attend<DT, D, MULTI, LEAN>(a, s, g, u0, u1, ctx, nr, st);
           // the segment's first column in `out`; column c is row + c / G, head g * G + c % G
           const int64_t ob = ((int64_t)row * a.num_q_heads + (int64_t)g * G) * D;
           if (whole)
@@ -246,27 +265,32 @@ __global__ __launch_bounds__(kWG) void mfma_decode_kernel(DecodeArgs a) {
   (void)lane;
 }
 
-template <int DT, int MODE, bool MULTI>
+template <int DT, int MODE, bool MULTI, bool LEAN = false>
 static hipError_t launch_d(const DecodeArgs& a, int grid, hipStream_t st) {
   const size_t lds = (size_t)(a.num_seqs + 1) * sizeof(int32_t);
   if (a.head_dim == 64)
-    hipLaunchKernelGGL((mfma_decode_kernel<DT, 64, MODE, MULTI>), dim3(grid), dim3(kWG), lds, st, a);
+    hipLaunchKernelGGL((mfma_decode_kernel<DT, 64, MODE, MULTI, LEAN>), dim3(grid), dim3(kWG), lds, st, a);
   else
-    hipLaunchKernelGGL((mfma_decode_kernel<DT, 128, MODE, MULTI>), dim3(grid), dim3(kWG), lds, st, a);
+    hipLaunchKernelGGL((mfma_decode_kernel<DT, 128, MODE, MULTI, LEAN>), dim3(grid), dim3(kWG), lds, st, a);
   return hipGetLastError();
 }
 
-// MODE_EVEN with a.max_rows > 1 runs the multi-row (verify) columns
+// MODE_EVEN with a.max_rows > 1 runs the multi-row (verify) columns, with a.lean the lean
+// stream (when the chunk kernel runs beside it)
 hipError_t launch_mfma_decode(int dt, int mode, const DecodeArgs& a, int grid, hipStream_t st) {
+  const bool f16 = dt == DT_F16;
   if (mode == MODE_EVEN) {
+    if (a.max_rows > 1 && a.lean)
+      return f16 ? launch_d<DT_F16, MODE_EVEN, true, true>(a, grid, st)
+                 : launch_d<DT_BF16, MODE_EVEN, true, true>(a, grid, st);
     if (a.max_rows > 1)
-      return dt == DT_F16 ? launch_d<DT_F16, MODE_EVEN, true>(a, grid, st)
-                          : launch_d<DT_BF16, MODE_EVEN, true>(a, grid, st);
-    return dt == DT_F16 ? launch_d<DT_F16, MODE_EVEN, false>(a, grid, st)
-                        : launch_d<DT_BF16, MODE_EVEN, false>(a, grid, st);
+      return f16 ? launch_d<DT_F16, MODE_EVEN, true>(a, grid, st)
+                 : launch_d<DT_BF16, MODE_EVEN, true>(a, grid, st);
+    return f16 ? launch_d<DT_F16, MODE_EVEN, false>(a, grid, st)
+               : launch_d<DT_BF16, MODE_EVEN, false>(a, grid, st);
   }
-  return dt == DT_F16 ? launch_d<DT_F16, MODE_PARTITION, false>(a, grid, st)
-                      : launch_d<DT_BF16, MODE_PARTITION, false>(a, grid, st);
+  return f16 ? launch_d<DT_F16, MODE_PARTITION, false>(a, grid, st)
+             : launch_d<DT_BF16, MODE_PARTITION, false>(a, grid, st);
 }
 
 template <int DT, int MODE>
@@ -274,9 +298,9 @@ static int occ(int head_dim, int lds) {
   int nb = 0;
   hipError_t e;
   if (head_dim == 64)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, mfma_decode_kernel<DT, 64, MODE, false>, kWG, lds);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, mfma_decode_kernel<DT, 64, MODE, false, false>, kWG, lds);
   else
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, mfma_decode_kernel<DT, 128, MODE, false>, kWG, lds);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, mfma_decode_kernel<DT, 128, MODE, false, false>, kWG, lds);
   return e == hipSuccess && nb > 0 ? nb : 1;
 }
 

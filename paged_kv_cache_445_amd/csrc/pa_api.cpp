@@ -378,6 +378,8 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   // without query_start_loc, or when no sequence has more rows than the decode kernel takes,
   // there is no chunk work
   if (!query_start_loc || max_len <= rt.max_rows) return hip_status(decode());
+  // the chunk kernel runs beside the decode kernel: the lean matrix-core decode shares the CUs
+  a.lean = 1;
 
   // multi-row sequences: the chunk kernel on the side stream, forked from and joined back
   // into the caller's stream around the decode kernel

@@ -54,6 +54,7 @@ struct DecodeArgs {
   int32_t cols;             // MODE_EVEN, matrix-core path: query columns per partial slot
   float v_factor;           // DT_FP8: the outputs' factor (v_scale)
   int32_t blk_shift;        // log2(block_size / 16): table entries name 2^blk_shift sub-blocks
+  int32_t lean;             // MODE_EVEN, matrix-core path with several rows: the lean stream
 };
 
 struct ReshapeArgs {

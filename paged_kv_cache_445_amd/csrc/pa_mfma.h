@@ -280,6 +280,66 @@ __device__ __forceinline__ void mfma_stream(const DecodeArgs& a, int s, int g, i
   }
 }
 
+// The lean form of mfma_stream: one K and one V operand buffer instead of two of each, so a
+// wave needs about half the operand registers and two waves fit on a SIMD.  Unit u + 1's K
+// loads go out as soon as unit u's scores have read K, its V loads as soon as unit u's P . V
+// has read V; the in-order load counter then lets each wait cover only the operand it needs.
+// scores(kb, u) returns the unit's weights, pv(vb, p, u) adds P . V.  All arguments must be
+// wave-uniform.
+template <int DT, int D, class S, class PV>
+__device__ __forceinline__ void mfma_stream_lean(const DecodeArgs& a, int s, int g, int u0,
+                                                 int u1, int ctx, S&& scores, PV&& pv) {
+  using C = MfmaCfg<DT, D>;
+  const int lane = lane_id();
+  const MfmaLaneOffsets<DT, D> o = mfma_offsets<DT, D>();
+  const int64_t blk_stride = (int64_t)a.num_kv_heads * C::TILE;
+  const char* kc = reinterpret_cast<const char*>(a.k_cache) + (int64_t)g * C::TILE;
+  const char* vc = reinterpret_cast<const char*>(a.v_cache) + (int64_t)g * C::TILE;
+  const int32_t* bt_row = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+  const int nblk = (ctx + kBlock - 1) / kBlock;
+  for (int c0 = u0; c0 < u1; c0 += 64) {
+    const int c1 = min(u1, c0 + 64);
+    const int b0 = 2 * c0, bend = min(nblk, 2 * c1);
+    const int win0 = (b0 + lane < bend) ? tile_block(bt_row, b0 + lane, a.blk_shift) : 0;
+    const int win1 = (b0 + 64 + lane < bend) ? tile_block(bt_row, b0 + 64 + lane, a.blk_shift) : 0;
+    auto blk = [&](int e) -> int64_t { return e < 64 ? readlane(win0, e) : readlane(win1, e - 64); };
+    // a unit whose second block lies past the context reads its first block again (all of its
+    // tokens are masked)
+    auto bases = [&](int u, int64_t& ba, int64_t& bb) {
+      const int e = 2 * (u - c0);
+      ba = blk(e);
+      bb = (2 * u + 1 < nblk) ? blk(e + 1) : ba;
+    };
+    auto issue_k = [&](MfmaK<DT, D>& kb, int u) {
+      int64_t ba, bb;
+      bases(u, ba, bb);
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const char* kt = kc + (o.kt[b] ? bb : ba) * blk_stride;
+#pragma unroll
+        for (int kk = 0; kk < C::NKK; ++kk) kb[b][kk] = ld16(kt + o.koff(b, kk));
+      }
+    };
+    auto issue_v = [&](MfmaV<DT, D>& vb, int u) {
+      int64_t ba, bb;
+      bases(u, ba, bb);
+      const char* vt = vc + (o.vt ? bb : ba) * blk_stride;
+#pragma unroll
+      for (int j = 0; j < C::NJ; ++j) vb[j] = ld16(vt + o.voff(j));
+    };
+    MfmaK<DT, D> kb;
+    MfmaV<DT, D> vb;
+    issue_k(kb, c0);
+    issue_v(vb, c0);
+    for (int u = c0; u < c1; ++u) {
+      const MfmaP<DT> p = scores(kb, u);
+      if (u + 1 < c1) issue_k(kb, u + 1);
+      pv(vb, p, u);
+      if (u + 1 < c1) issue_v(vb, u + 1);
+    }
+  }
+}
+
 // Write the first ncols query columns of a finished piece: the normalised output (to `out`,
 // column c at out_base + (c / group) * out_row_stride + (c % group) * out_col_stride, or to a
 // partial slot, column c at po + c * po_col_stride), plus each column's max / sum for partial
