@@ -50,6 +50,8 @@ DESCRIPTIONS = {
     "llama7b_fp8": "LLaMA-7B-shaped decode with FP8 E4M3 KV (per-pool scales 6.5/448): 32 seqs "
                    "x 32 heads (MHA), head_dim 128, fp16 q, block 16, ctx U[256,2048], "
                    "8192-block pool, permuted block table",
+    "gqa_long_fp8": "GQA decode with FP8 E4M3 KV (per-pool scales 3.25/448): 64 seqs, 64 q / 8 kv "
+                    "heads, head_dim 128, fp16 q, block 16, ctx log-uniform [128,32768]",
     "spec_verify_f16": "speculative verify step: 32 seqs x 6 causal rows (last token + 5 "
                        "drafts) x 32 heads (MHA), head_dim 128, fp16 KV, prior ctx U[256,2048]",
     "spec_verify_gqa_bf16": "speculative verify step: 64 seqs x 4 causal rows, 32 q / 8 kv "

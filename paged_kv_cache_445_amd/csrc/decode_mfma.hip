@@ -47,7 +47,7 @@ __device__ void mfma_attend(const DecodeArgs& a, int s, int g, int u0, int u1, i
   T qb[C::NKK];
   {
     const char* qp = reinterpret_cast<const char*>(a.q) +
-                     ((int64_t)(row0 + jr) * a.num_q_heads + (int64_t)g * G + hc) * D * C::E;
+                     ((int64_t)(row0 + jr) * a.num_q_heads + (int64_t)g * G + hc) * D * 2;
     const bool live = MULTI ? jr < nr : n < G;
 #pragma unroll
     for (int kk = 0; kk < C::NKK; ++kk) {
@@ -68,6 +68,11 @@ __device__ void mfma_attend(const DecodeArgs& a, int s, int g, int u0, int u1, i
       else
         mfma_unit<DT, D, true, false>(st, kb, vb, qb, a.scale_log2, valid - 1, valid);
     });
+    if constexpr (DT == DT_FP8) {
+      // a stored V value stands for its E4M3 value times v_scale (k_scale is in scale_log2)
+#pragma unroll
+      for (int j = 0; j < C::NJ; ++j) st.acc[j] *= a.v_factor;
+    }
   } else {
     const int last0 = ctx - nr;                 // last visible key of the first row
     const int mine = min(last0 + jr, ctx - 1);  // ... of this lane's column (padding: ctx - 1)
@@ -279,6 +284,8 @@ static hipError_t launch_d(const DecodeArgs& a, int grid, hipStream_t st) {
 // stream (when the chunk kernel runs beside it)
 hipError_t launch_mfma_decode(int dt, int mode, const DecodeArgs& a, int grid, hipStream_t st) {
   const bool f16 = dt == DT_F16;
+  if (dt == DT_FP8)  // one row per sequence, MODE_EVEN (the host rejects the rest)
+    return launch_d<DT_FP8, MODE_EVEN, false>(a, grid, st);
   if (mode == MODE_EVEN) {
     if (a.max_rows > 1 && a.lean)
       return f16 ? launch_d<DT_F16, MODE_EVEN, true, true>(a, grid, st)
@@ -305,6 +312,7 @@ static int occ(int head_dim, int lds) {
 }
 
 int mfma_decode_max_blocks_per_cu(int dt, int head_dim, int mode, int lds_bytes) {
+  if (dt == DT_FP8) return occ<DT_FP8, MODE_EVEN>(head_dim, lds_bytes);
   if (mode == MODE_EVEN)
     return dt == DT_F16 ? occ<DT_F16, MODE_EVEN>(head_dim, lds_bytes)
                         : occ<DT_BF16, MODE_EVEN>(head_dim, lds_bytes);

@@ -104,7 +104,7 @@ int odd_skew() {
 }
 
 bool use_mfma(const pa_geom* g) {
-  return (g->kv_dtype == PA_F16 || g->kv_dtype == PA_BF16) && g->num_q_heads / g->num_kv_heads >= 2;
+  return g->kv_dtype != PA_F32 && g->num_q_heads / g->num_kv_heads >= 2;
 }
 
 // Which decode kernel runs a pa_decode call, and which sequences it takes (max_len: an upper

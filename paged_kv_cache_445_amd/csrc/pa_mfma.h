@@ -17,6 +17,9 @@
 //     16j + 4r + i (i < 4) of its column.
 //   * K tiles are [D/8][16][8]: a token's 8-element chunk, the A operand of S^T, is one
 //     16-byte load.
+//   * FP8 pools (tiles of bytes, K [D/16][16][16]): the same operands are 8-byte loads (half a
+//     K chunk; 8 tokens of a V row), widened to f16 in registers, which holds every E4M3
+//     value exactly; the matrix cores then run in f16 with fp16 queries.
 // P is fed to the matrix core as hi + lo 16-bit parts (two products), which keeps the
 // rounding of the weights near 2^-16 relative instead of 2^-8 (bf16) or 2^-11 (fp16).
 #pragma once
@@ -31,15 +34,50 @@ namespace pa {
 
 template <int DT, int D>
 struct MfmaCfg {
-  static constexpr int E = 2;
+  static constexpr int E = DT == DT_FP8 ? 1 : 2;  // pool element bytes (queries: 2)
   static constexpr int NKK = D / 32;  // MFMAs over the head dimension per S-block
   static constexpr int NJ = D / 16;   // MFMAs over output dims per unit
   static constexpr int64_t TILE = 16LL * D * E;
   static constexpr int DEPTH = 2;
 };
 
+// matrix-core operand type: bf16 or f16 (FP8 pools are widened to f16, which holds every
+// E4M3 value exactly)
 template <int DT>
 using op8_t = typename std::conditional<DT == DT_BF16, bf16x8_t, f16x8_t>::type;
+
+// What an operand load brings in: the 8-element operand itself (16-bit pools), or 8 E4M3
+// bytes (FP8 pools), widened when the operand is used.
+template <int DT>
+struct MfmaRaw {
+  using type = uint4;
+};
+template <>
+struct MfmaRaw<DT_FP8> {
+  using type = uint2;
+};
+
+template <int DT>
+__device__ __forceinline__ typename MfmaRaw<DT>::type ld_raw(const char* p) {
+  return *reinterpret_cast<const typename MfmaRaw<DT>::type*>(p);
+}
+
+template <int DT>
+__device__ __forceinline__ op8_t<DT> operand(const typename MfmaRaw<DT>::type& r) {
+  if constexpr (DT == DT_FP8) {
+    float f[4];
+    f16x8_t o;
+    fp8x4_to_f32(r.x, f);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = (_Float16)f[i];
+    fp8x4_to_f32(r.y, f);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[4 + i] = (_Float16)f[i];
+    return o;
+  } else {
+    return __builtin_bit_cast(op8_t<DT>, r);
+  }
+}
 
 template <int DT>
 __device__ __forceinline__ f32x4_t mfma(const op8_t<DT>& a, const op8_t<DT>& b, f32x4_t c) {
@@ -57,9 +95,9 @@ struct MfmaState {
 };
 
 template <int DT, int D>
-using MfmaK = uint4[2][MfmaCfg<DT, D>::NKK];
+using MfmaK = typename MfmaRaw<DT>::type[2][MfmaCfg<DT, D>::NKK];
 template <int DT, int D>
-using MfmaV = uint4[MfmaCfg<DT, D>::NJ];
+using MfmaV = typename MfmaRaw<DT>::type[MfmaCfg<DT, D>::NJ];
 template <int DT, int D>
 using MfmaQ = op8_t<DT>[MfmaCfg<DT, D>::NKK];
 
@@ -72,7 +110,9 @@ struct MfmaLaneOffsets {
   int kt[2];  // which tile of the unit (0 / 1) S-block b's token is in
   int v;      // offset inside the V tile of piece j = 0
   int vt;     // which tile of the unit this lane's V tokens are in
-  __device__ __forceinline__ int koff(int b, int kk) const { return k[b] + 1024 * kk; }
+  __device__ __forceinline__ int koff(int b, int kk) const {
+    return k[b] + 512 * MfmaCfg<DT, D>::E * kk;
+  }
   __device__ __forceinline__ int voff(int j) const { return v + 256 * MfmaCfg<DT, D>::E * j; }
 };
 
@@ -85,11 +125,11 @@ __device__ __forceinline__ void mfma_load(MfmaK<DT, D>& kb, MfmaV<DT, D>& vb, co
   for (int b = 0; b < 2; ++b) {
     const char* kt = o.kt[b] ? k1 : k0;
 #pragma unroll
-    for (int kk = 0; kk < C::NKK; ++kk) kb[b][kk] = ld16(kt + o.koff(b, kk));
+    for (int kk = 0; kk < C::NKK; ++kk) kb[b][kk] = ld_raw<DT>(kt + o.koff(b, kk));
   }
   const char* vt = o.vt ? v1 : v0;
 #pragma unroll
-  for (int j = 0; j < C::NJ; ++j) vb[j] = ld16(vt + o.voff(j));
+  for (int j = 0; j < C::NJ; ++j) vb[j] = ld_raw<DT>(vt + o.voff(j));
 }
 
 // The two halves of one unit for one 16-column block.  mfma_scores computes S^T = K . Q^T,
@@ -116,8 +156,8 @@ __device__ __forceinline__ MfmaP<DT> mfma_scores(MfmaState<DT, D>& st, const Mfm
   f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kk = 0; kk < C::NKK; ++kk) {
-    s0 = mfma<DT>(__builtin_bit_cast(T, kb[0][kk]), qb[kk], s0);
-    s1 = mfma<DT>(__builtin_bit_cast(T, kb[1][kk]), qb[kk], s1);
+    s0 = mfma<DT>(operand<DT>(kb[0][kk]), qb[kk], s0);
+    s1 = mfma<DT>(operand<DT>(kb[1][kk]), qb[kk], s1);
   }
   // raw scores q . k; the scale enters through the exponent's fma, and the largest scaled
   // score is the scale times the largest raw score (the smallest one for a negative scale)
@@ -169,6 +209,9 @@ __device__ __forceinline__ void mfma_pv(MfmaState<DT, D>& st, MfmaV<DT, D>& vb,
                                         const MfmaP<DT>& p, int vvalid) {
   using C = MfmaCfg<DT, D>;
   using T = op8_t<DT>;
+  T vo[C::NJ];
+#pragma unroll
+  for (int j = 0; j < C::NJ; ++j) vo[j] = operand<DT>(vb[j]);
   if (MASK) {
     // zero the V elements of tokens past the written context (0 * NaN is NaN)
     const int r = lane_id() >> 4;
@@ -179,10 +222,12 @@ __device__ __forceinline__ void mfma_pv(MfmaState<DT, D>& st, MfmaV<DT, D>& vb,
     const uint32_t m3 = (6 < kv ? 0xffffu : 0u) | (7 < kv ? 0xffff0000u : 0u);
 #pragma unroll
     for (int j = 0; j < C::NJ; ++j) {
-      vb[j].x &= m0;
-      vb[j].y &= m1;
-      vb[j].z &= m2;
-      vb[j].w &= m3;
+      uint4 w = __builtin_bit_cast(uint4, vo[j]);
+      w.x &= m0;
+      w.y &= m1;
+      w.z &= m2;
+      w.w &= m3;
+      vo[j] = __builtin_bit_cast(T, w);
     }
   }
   // rescale this column's outputs by its own alpha (skipped when no column's max moved, as
@@ -196,11 +241,10 @@ __device__ __forceinline__ void mfma_pv(MfmaState<DT, D>& st, MfmaV<DT, D>& vb,
   }
 #pragma unroll
   for (int j = 0; j < C::NJ; ++j) {
-    st.acc[j] = mfma<DT>(__builtin_bit_cast(T, vb[j]), p.hi, st.acc[j]);
-    st.acc[j] = mfma<DT>(__builtin_bit_cast(T, vb[j]), p.lo, st.acc[j]);
+    st.acc[j] = mfma<DT>(vo[j], p.hi, st.acc[j]);
+    st.acc[j] = mfma<DT>(vo[j], p.lo, st.acc[j]);
   }
 }
-
 // One unit: scores, softmax update and P . V for one 16-column block.
 template <int DT, int D, bool MASK, bool SAFE>
 __device__ __forceinline__ void mfma_unit(MfmaState<DT, D>& st, const MfmaK<DT, D>& kb,
@@ -221,7 +265,10 @@ __device__ __forceinline__ MfmaLaneOffsets<DT, D> mfma_offsets() {
   for (int b = 0; b < 2; ++b) {
     const int t = 8 * (n >> 2) + 4 * b + (n & 3);  // unit token of S-block row n
     o.kt[b] = t >> 4;
-    o.k[b] = (r * 16 + (t & 15)) * 16;  // chunk 4 kk + r of token t: + 1 KiB per kk
+    if constexpr (C::E == 2)
+      o.k[b] = (r * 16 + (t & 15)) * 16;  // chunk 4 kk + r of token t: + 1 KiB per kk
+    else  // 16-element chunks: dims 8 r .. of block kk are half r & 1 of chunk 2 kk + r / 2
+      o.k[b] = ((r >> 1) * 16 + (t & 15)) * 16 + 8 * (r & 1);
   }
   o.vt = r >> 1;
   o.v = (n * 16 + 8 * (r & 1)) * C::E;  // dimension 16 j + n: + 256 elements per j
@@ -317,7 +364,7 @@ __device__ __forceinline__ void mfma_stream_lean(const DecodeArgs& a, int s, int
       for (int b = 0; b < 2; ++b) {
         const char* kt = kc + (o.kt[b] ? bb : ba) * blk_stride;
 #pragma unroll
-        for (int kk = 0; kk < C::NKK; ++kk) kb[b][kk] = ld16(kt + o.koff(b, kk));
+        for (int kk = 0; kk < C::NKK; ++kk) kb[b][kk] = ld_raw<DT>(kt + o.koff(b, kk));
       }
     };
     auto issue_v = [&](MfmaV<DT, D>& vb, int u) {
@@ -325,7 +372,7 @@ __device__ __forceinline__ void mfma_stream_lean(const DecodeArgs& a, int s, int
       bases(u, ba, bb);
       const char* vt = vc + (o.vt ? bb : ba) * blk_stride;
 #pragma unroll
-      for (int j = 0; j < C::NJ; ++j) vb[j] = ld16(vt + o.voff(j));
+      for (int j = 0; j < C::NJ; ++j) vb[j] = ld_raw<DT>(vt + o.voff(j));
     };
     MfmaK<DT, D> kb;
     MfmaV<DT, D> vb;

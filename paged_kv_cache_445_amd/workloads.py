@@ -311,6 +311,19 @@ def llama7b_fp8(seed: int = 4451, num_seqs: int = 32) -> Batch:
     return b
 
 
+def gqa_long_fp8(seed: int = 4452, num_seqs: int = 64, max_ctx: int = 32768) -> Batch:
+    """The GQA long-context batch's shape (64 q / 8 KV heads, log-uniform contexts to 32768)
+    with FP8 E4M3 pools and fp16 q, keys and values (N(0, 0.5); per-pool scales 3.25 / 448)."""
+    rng = np.random.default_rng(seed)
+    u = rng.uniform(math.log(128), math.log(max_ctx), size=num_seqs)
+    ctx = np.clip(np.rint(np.exp(u)), 128, max_ctx).astype(np.int64)
+    b = build_batch("gqa_long_fp8", "f16", ctx, np.ones(num_seqs), 64, 8, 128, rng, sigma=0.5,
+                    max_blocks_per_seq=(max_ctx + 15) // 16, partition_size=512)
+    b.kv_dtype = "fp8"
+    b.k_scale = b.v_scale = float(np.float32(3.25 / 448))
+    return b
+
+
 def spec_verify_f16(seed: int = 4455, num_seqs: int = 32, num_draft: int = 5) -> Batch:
     """Speculative-decoding verify step on the LLaMA-7B shape ("vLLM 深度拆解" §5.1: the
     target model checks num_draft drafted tokens in one pass): every sequence runs the last
@@ -340,6 +353,7 @@ PRESETS = {
     "prefix_shared_f16": prefix_shared_f16,
     "mixed_chunked_bf16": mixed_chunked_bf16,
     "llama7b_fp8": llama7b_fp8,
+    "gqa_long_fp8": gqa_long_fp8,
     "spec_verify_f16": spec_verify_f16,
     "spec_verify_gqa_bf16": spec_verify_gqa_bf16,
 }

@@ -490,6 +490,21 @@ def test_llama7b_fp8(dev):
     parity(dev, W.make("llama7b_fp8"))
 
 
+@pytest.mark.parametrize("Hq,Hkv,D", [(64, 8, 128), (16, 2, 64), (32, 16, 128)])
+def test_fp8_gqa_matrix_cores(dev, Hq, Hkv, D):
+    """FP8 pools on the matrix-core path (GQA): 8-byte operand loads widened to f16, long and
+    edge-case contexts split over workgroups."""
+    rng = np.random.default_rng(2300 + Hq + D)
+    ctx = np.array(EDGE_CTX + list(rng.integers(1, 12000, size=10)))
+    parity(dev, _fp8(W.build_batch("fp8_gqa", "f16", ctx, np.ones(len(ctx)), Hq, Hkv, D, rng)))
+
+
+def test_gqa_long_fp8(dev):
+    b = W.make("gqa_long_fp8")
+    rows = np.arange(0, b.num_q_rows, 3, dtype=np.int32)
+    parity(dev, b, rows=rows)
+
+
 def test_max_query_len_unknown_or_loose(dev):
     """pa_decode with max_query_len 0 (unknown: every kernel that might be needed runs) or an
     upper bound above the true longest sequence gives the same rows as the exact value."""
