@@ -37,7 +37,7 @@
  *
  * FP8 pools ("vLLM 深度拆解" §10.1 names FP8 KV with calibrated scales).  kv_dtype
  * PA_FP8_E4M3: one byte per element in the layout above with elem = 1, X = 16; q, key and
- * value are fp16 (q_dtype PA_F16), out is fp16 or fp32.  Each pool has one scale:
+ * value are fp16 or bf16 (q_dtype PA_F16 or PA_BF16), out is q_dtype or fp32.  Each pool has one scale:
  * reshape_and_cache stores e4m3(fp32(x) / scale), the fp32 quotient rounded to the nearest
  * E4M3 ("E4M3FN": bias 7, no infinity, largest 448) with ties to even, magnitudes from 448
  * up saturating to 448; attention reads an element as its E4M3 value times the scale.
@@ -84,7 +84,7 @@ typedef struct {
   int32_t max_blocks_per_seq; /* MB: row stride of block_tables */
   int32_t kv_dtype;           /* pa_dtype of k_cache, v_cache (and of q, key, value unless FP8) */
   int32_t out_dtype;          /* pa_dtype of out: q_dtype or PA_F32 */
-  int32_t q_dtype;            /* pa_dtype of q, key, value: kv_dtype, or PA_F16 for FP8 pools */
+  int32_t q_dtype;            /* pa_dtype of q, key, value: kv_dtype, or PA_F16 / PA_BF16 for FP8 pools */
   float k_scale;              /* FP8 pools: stored K = e4m3(fp32(key) / k_scale); else ignored */
   float v_scale;              /* FP8 pools: stored V = e4m3(fp32(value) / v_scale); else ignored */
 } pa_geom;

@@ -68,7 +68,7 @@ __device__ void mfma_attend(const DecodeArgs& a, int s, int g, int u0, int u1, i
       else
         mfma_unit<DT, D, true, false>(st, kb, vb, qb, a.scale_log2, valid - 1, valid);
     });
-    if constexpr (DT == DT_FP8) {
+    if constexpr (is_fp8(DT)) {
       // a stored V value stands for its E4M3 value times v_scale (k_scale is in scale_log2)
 #pragma unroll
       for (int j = 0; j < C::NJ; ++j) st.acc[j] *= a.v_factor;
@@ -284,8 +284,9 @@ static hipError_t launch_d(const DecodeArgs& a, int grid, hipStream_t st) {
 // stream (when the chunk kernel runs beside it)
 hipError_t launch_mfma_decode(int dt, int mode, const DecodeArgs& a, int grid, hipStream_t st) {
   const bool f16 = dt == DT_F16;
-  if (dt == DT_FP8)  // one row per sequence, MODE_EVEN (the host rejects the rest)
-    return launch_d<DT_FP8, MODE_EVEN, false>(a, grid, st);
+  // FP8 pools: one row per sequence, MODE_EVEN (the host rejects the rest)
+  if (dt == DT_FP8) return launch_d<DT_FP8, MODE_EVEN, false>(a, grid, st);
+  if (dt == DT_FP8B) return launch_d<DT_FP8B, MODE_EVEN, false>(a, grid, st);
   if (mode == MODE_EVEN) {
     if (a.max_rows > 1 && a.lean)
       return f16 ? launch_d<DT_F16, MODE_EVEN, true, true>(a, grid, st)
@@ -313,6 +314,7 @@ static int occ(int head_dim, int lds) {
 
 int mfma_decode_max_blocks_per_cu(int dt, int head_dim, int mode, int lds_bytes) {
   if (dt == DT_FP8) return occ<DT_FP8, MODE_EVEN>(head_dim, lds_bytes);
+  if (dt == DT_FP8B) return occ<DT_FP8B, MODE_EVEN>(head_dim, lds_bytes);
   if (mode == MODE_EVEN)
     return dt == DT_F16 ? occ<DT_F16, MODE_EVEN>(head_dim, lds_bytes)
                         : occ<DT_BF16, MODE_EVEN>(head_dim, lds_bytes);

@@ -99,20 +99,24 @@ __device__ __forceinline__ void mask_piece(uint4& v, int first_token, int valid)
   v.w &= m[3];
 }
 
-// FP8: scale_log2 * (q . k) over a 16-byte K chunk of 16 E4M3 values, each widened to fp32
-// and multiplied with its fp16 query element (q0: elements 0-7, q1: 8-15) in fp32.
+// FP8: q . k over a 16-byte K chunk of 16 E4M3 values, each widened to fp32 and multiplied
+// with its 16-bit query element (q0: elements 0-7, q1: 8-15; fp16 for DT_FP8, bf16 for
+// DT_FP8B) in fp32.
+template <int DT>
 __device__ __forceinline__ float dot_fp8(const uint4& k, const uint4& q0, const uint4& q1,
                                          float acc) {
+  auto lo = [](uint32_t w) { return DT == DT_FP8B ? bf16_lo(w) : f16_lo(w); };
+  auto hi = [](uint32_t w) { return DT == DT_FP8B ? bf16_hi(w) : f16_hi(w); };
   const uint32_t kw[4] = {k.x, k.y, k.z, k.w};
   const uint32_t qw[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
     float f[4];
     fp8x4_to_f32(kw[m], f);
-    acc = fmaf(f16_lo(qw[2 * m]), f[0], acc);
-    acc = fmaf(f16_hi(qw[2 * m]), f[1], acc);
-    acc = fmaf(f16_lo(qw[2 * m + 1]), f[2], acc);
-    acc = fmaf(f16_hi(qw[2 * m + 1]), f[3], acc);
+    acc = fmaf(lo(qw[2 * m]), f[0], acc);
+    acc = fmaf(hi(qw[2 * m]), f[1], acc);
+    acc = fmaf(lo(qw[2 * m + 1]), f[2], acc);
+    acc = fmaf(hi(qw[2 * m + 1]), f[3], acc);
   }
   return acc;
 }
@@ -124,11 +128,11 @@ __device__ __forceinline__ void v_tile(VState<DT, D>& st, VTile<DT, D>& t, const
   using C = VCfg<DT, D>;
   const int lane = lane_id();
   float part = 0.f;
-  if constexpr (DT == DT_FP8) {
-    // each 16-byte K chunk is 16 E4M3 values, dotted with the chunk's 16 fp16 query
-    // elements (k_scale is in the score factor)
+  if constexpr (is_fp8(DT)) {
+    // each 16-byte K chunk is 16 E4M3 values, dotted with the chunk's 16 query elements
+    // (k_scale is in the score factor)
 #pragma unroll
-    for (int i = 0; i < C::NK; ++i) part = dot_fp8(t.k[i], qv[2 * i], qv[2 * i + 1], part);
+    for (int i = 0; i < C::NK; ++i) part = dot_fp8<DT>(t.k[i], qv[2 * i], qv[2 * i + 1], part);
   } else {
 #pragma unroll
     for (int i = 0; i < C::NK; ++i) part = dot16<DT>(t.k[i], qv[i], part);
@@ -156,7 +160,7 @@ __device__ __forceinline__ void v_tile(VState<DT, D>& st, VTile<DT, D>& t, const
 #pragma unroll
   for (int j = 0; j < C::NV; ++j) {
     float a = st.acc[j] * alpha;
-    if constexpr (DT == DT_FP8) {
+    if constexpr (is_fp8(DT)) {
       // the 16 tokens of one dimension row; tokens >= valid are zeroed (MASK)
       const uint32_t vw[4] = {t.v[j].x, t.v[j].y, t.v[j].z, t.v[j].w};
 #pragma unroll
@@ -343,7 +347,7 @@ __device__ __forceinline__ float v_finish(VState<DT, D>& st, float vfac) {
   for (int j = 0; j < C::NV; ++j) {
     if constexpr (C::LPD >= 2) st.acc[j] += dpp_mov<0xB1>(st.acc[j]);  // [1,0,3,2]: lane ^ 1
     if constexpr (C::LPD == 4) st.acc[j] += dpp_mov<0x4E>(st.acc[j]);  // [2,3,0,1]: ^ 2
-    if constexpr (DT == DT_FP8) st.acc[j] *= vfac;
+    if constexpr (is_fp8(DT)) st.acc[j] *= vfac;
   }
   return row16_sum(st.l);
 }
@@ -598,7 +602,7 @@ static void launch_hpw(const DecodeArgs& a, int grid, size_t lds, hipStream_t st
   if constexpr (MODE == MODE_EVEN) {
     // fp32 queries fill twice the registers: at most two heads per wave; FP8 widens to
     // fp32 in registers: at most four
-    if constexpr (DT != DT_F32 && DT != DT_FP8) {
+    if constexpr (DT != DT_F32 && !is_fp8(DT)) {
       if (a.heads_per_wave == 8) return launch_k<DT, D, MODE, 8>(a, grid, lds, st);
     }
     if constexpr (DT != DT_F32) {
@@ -625,6 +629,7 @@ hipError_t launch_valu_decode(int dt, int mode, const DecodeArgs& a, int grid, h
     if (dt == DT_F32) return launch_d<DT_F32, MODE_EVEN>(a, grid, st);
     if (dt == DT_F16) return launch_d<DT_F16, MODE_EVEN>(a, grid, st);
     if (dt == DT_FP8) return launch_d<DT_FP8, MODE_EVEN>(a, grid, st);
+    if (dt == DT_FP8B) return launch_d<DT_FP8B, MODE_EVEN>(a, grid, st);
     return launch_d<DT_BF16, MODE_EVEN>(a, grid, st);
   }
   if (dt == DT_F32) return launch_d<DT_F32, MODE_PARTITION>(a, grid, st);
@@ -647,7 +652,7 @@ static int occ_k(int head_dim, int lds) {
 template <int DT, int MODE>
 static int occ(int head_dim, int hpw, int lds) {
   if constexpr (MODE == MODE_EVEN) {
-    if constexpr (DT != DT_F32 && DT != DT_FP8) {
+    if constexpr (DT != DT_F32 && !is_fp8(DT)) {
       if (hpw == 8) return occ_k<DT, MODE, 8>(head_dim, lds);
     }
     if constexpr (DT != DT_F32) {
@@ -664,6 +669,7 @@ int valu_decode_max_blocks_per_cu(int dt, int head_dim, int hpw, int mode, int l
     if (dt == DT_F32) return occ<DT_F32, MODE_EVEN>(head_dim, hpw, lds);
     if (dt == DT_F16) return occ<DT_F16, MODE_EVEN>(head_dim, hpw, lds);
     if (dt == DT_FP8) return occ<DT_FP8, MODE_EVEN>(head_dim, hpw, lds);
+    if (dt == DT_FP8B) return occ<DT_FP8B, MODE_EVEN>(head_dim, hpw, lds);
     return occ<DT_BF16, MODE_EVEN>(head_dim, hpw, lds);
   }
   if (dt == DT_F32) return occ<DT_F32, MODE_PARTITION>(head_dim, 1, lds);

@@ -30,7 +30,7 @@ pa_status check_geom(const pa_geom* g) {
     return PA_ERR_SHAPE;
   if (g->num_q_heads % g->num_kv_heads) return PA_ERR_SHAPE;
   if (g->kv_dtype == PA_FP8_E4M3) {
-    if (g->q_dtype != PA_F16) return PA_ERR_UNSUPPORTED;
+    if (g->q_dtype != PA_F16 && g->q_dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
     if (!(std::isfinite(g->k_scale) && g->k_scale > 0.f && std::isfinite(g->v_scale) &&
           g->v_scale > 0.f))
       return PA_ERR_SHAPE;
@@ -46,6 +46,12 @@ pa_status check_geom(const pa_geom* g) {
   if (g->num_q_heads / g->num_kv_heads > 16) return PA_ERR_UNSUPPORTED;
   if (g->num_seqs > kMaxSeqs) return PA_ERR_UNSUPPORTED;
   return PA_OK;
+}
+
+// element type code of the kernels: the pool's, FP8 pools split by their query type
+int kdt(const pa_geom* g) {
+  if (g->kv_dtype != PA_FP8_E4M3) return g->kv_dtype;
+  return g->q_dtype == PA_BF16 ? pa::DT_FP8B : pa::DT_FP8;
 }
 
 // log2 of the 16-token sub-blocks per block
@@ -172,17 +178,17 @@ int hpw_index(int hpw) { return hpw == 8 ? 3 : hpw == 4 ? 2 : hpw == 2 ? 1 : 0; 
 
 // workgroups of the split kernel: every CU full at the kernel's occupancy
 int split_grid(const pa_geom* g, int mode, int path) {
-  static std::atomic<int> cache[kMaxDevices][2][4][2][2][4][15];
+  static std::atomic<int> cache[kMaxDevices][2][5][2][2][4][15];
   const int dev = current_device();
   const int di = g->head_dim == 64 ? 0 : 1;
   const int bk = seq_bucket(g->num_seqs);
   const int hpw = path == 0 && mode == pa::MODE_EVEN ? heads_per_wave(g) : 1;
-  std::atomic<int>& c = cache[dev][path][g->kv_dtype][di][mode][hpw_index(hpw)][bk];
+  std::atomic<int>& c = cache[dev][path][kdt(g)][di][mode][hpw_index(hpw)][bk];
   int occ = c.load(std::memory_order_relaxed);
   if (occ <= 0) {
     const int lds = bucket_lds_bytes(bk);
-    occ = path ? pa::mfma_decode_max_blocks_per_cu(g->kv_dtype, g->head_dim, mode, lds)
-               : pa::valu_decode_max_blocks_per_cu(g->kv_dtype, g->head_dim, hpw, mode, lds);
+    occ = path ? pa::mfma_decode_max_blocks_per_cu(kdt(g), g->head_dim, mode, lds)
+               : pa::valu_decode_max_blocks_per_cu(kdt(g), g->head_dim, hpw, mode, lds);
     c.store(occ, std::memory_order_relaxed);
   }
   // The even split streams best with few resident workgroups per CU: each of them reads
@@ -279,7 +285,7 @@ pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_cache
   if ((threads + 255) / 256 > 0x7fffffffLL) return PA_ERR_SHAPE;
   pa::ReshapeArgs a{key, value, k_cache, v_cache, slot_mapping, num_tokens, g->num_kv_heads,
                     g->head_dim, g->k_scale, g->v_scale};
-  return hip_status(pa::launch_reshape(g->kv_dtype, a, (hipStream_t)stream));
+  return hip_status(pa::launch_reshape(kdt(g), a, (hipStream_t)stream));
 }
 
 pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping,
@@ -372,8 +378,8 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   a.blk_shift = blk_shift(g);
 
   auto decode = [&] {
-    return rt.path ? pa::launch_mfma_decode(g->kv_dtype, pa::MODE_EVEN, a, grid, st)
-                   : pa::launch_valu_decode(g->kv_dtype, pa::MODE_EVEN, a, grid, st);
+    return rt.path ? pa::launch_mfma_decode(kdt(g), pa::MODE_EVEN, a, grid, st)
+                   : pa::launch_valu_decode(kdt(g), pa::MODE_EVEN, a, grid, st);
   };
   // without query_start_loc, or when no sequence has more rows than the decode kernel takes,
   // there is no chunk work

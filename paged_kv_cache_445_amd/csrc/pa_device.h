@@ -19,7 +19,7 @@ namespace pa {
 
 template <int DT>
 struct DtInfo {
-  static constexpr int bytes = DT == DT_F32 ? 4 : DT == DT_FP8 ? 1 : 2;  // pool element
+  static constexpr int bytes = DT == DT_F32 ? 4 : is_fp8(DT) ? 1 : 2;  // pool element
   static constexpr int x = 16 / bytes;  // elements per 16-byte chunk
   static constexpr int qbytes = DT == DT_F32 ? 4 : 2;  // query / key / value / out element
 };
@@ -128,7 +128,7 @@ __device__ __forceinline__ float dot16(const uint4& a, const uint4& b, float acc
 }
 
 // store one output element in the output dtype (round to nearest even for 16-bit; FP8
-// pools have fp16 outputs)
+// pools have the outputs of their queries: fp16 or bf16)
 template <int DT>
 __device__ __forceinline__ void store_out(void* out, int64_t idx, float v, bool out_f32) {
   if (out_f32 || DT == DT_F32) {

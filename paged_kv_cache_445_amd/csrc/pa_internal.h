@@ -11,8 +11,10 @@ constexpr int kWavesPerWG = 4;
 constexpr int kWG = kWave * kWavesPerWG;
 constexpr int kBlock = 16;  // tokens per physical block
 
-// element types; DT_FP8: FP8 E4M3 pools with fp16 queries, keys and values
-enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_FP8 = 3 };
+// element types; DT_FP8 / DT_FP8B: FP8 E4M3 pools with fp16 / bf16 queries, keys and values
+enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_FP8 = 3, DT_FP8B = 4 };
+
+constexpr bool is_fp8(int dt) { return dt == DT_FP8 || dt == DT_FP8B; }
 
 // How a split kernel distributes and emits its work.
 enum SplitMode : int {

@@ -34,17 +34,21 @@ namespace pa {
 
 template <int DT, int D>
 struct MfmaCfg {
-  static constexpr int E = DT == DT_FP8 ? 1 : 2;  // pool element bytes (queries: 2)
+  static constexpr int E = is_fp8(DT) ? 1 : 2;  // pool element bytes (queries: 2)
   static constexpr int NKK = D / 32;  // MFMAs over the head dimension per S-block
   static constexpr int NJ = D / 16;   // MFMAs over output dims per unit
   static constexpr int64_t TILE = 16LL * D * E;
   static constexpr int DEPTH = 2;
 };
 
-// matrix-core operand type: bf16 or f16 (FP8 pools are widened to f16, which holds every
-// E4M3 value exactly)
+// matrix-core operand type: bf16 or f16 (FP8 pools are widened to the query type, f16 or bf16,
+// either of which holds every E4M3 value exactly)
 template <int DT>
-using op8_t = typename std::conditional<DT == DT_BF16, bf16x8_t, f16x8_t>::type;
+constexpr bool bf16_core() {
+  return DT == DT_BF16 || DT == DT_FP8B;
+}
+template <int DT>
+using op8_t = typename std::conditional<bf16_core<DT>(), bf16x8_t, f16x8_t>::type;
 
 // What an operand load brings in: the 8-element operand itself (16-bit pools), or 8 E4M3
 // bytes (FP8 pools), widened when the operand is used.
@@ -56,6 +60,10 @@ template <>
 struct MfmaRaw<DT_FP8> {
   using type = uint2;
 };
+template <>
+struct MfmaRaw<DT_FP8B> {
+  using type = uint2;
+};
 
 template <int DT>
 __device__ __forceinline__ typename MfmaRaw<DT>::type ld_raw(const char* p) {
@@ -64,15 +72,16 @@ __device__ __forceinline__ typename MfmaRaw<DT>::type ld_raw(const char* p) {
 
 template <int DT>
 __device__ __forceinline__ op8_t<DT> operand(const typename MfmaRaw<DT>::type& r) {
-  if constexpr (DT == DT_FP8) {
+  if constexpr (is_fp8(DT)) {
+    using E = typename std::conditional<bf16_core<DT>(), __bf16, _Float16>::type;
     float f[4];
-    f16x8_t o;
+    op8_t<DT> o;
     fp8x4_to_f32(r.x, f);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = (_Float16)f[i];
+    for (int i = 0; i < 4; ++i) o[i] = (E)f[i];
     fp8x4_to_f32(r.y, f);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o[4 + i] = (_Float16)f[i];
+    for (int i = 0; i < 4; ++i) o[4 + i] = (E)f[i];
     return o;
   } else {
     return __builtin_bit_cast(op8_t<DT>, r);
@@ -81,7 +90,7 @@ __device__ __forceinline__ op8_t<DT> operand(const typename MfmaRaw<DT>::type& r
 
 template <int DT>
 __device__ __forceinline__ f32x4_t mfma(const op8_t<DT>& a, const op8_t<DT>& b, f32x4_t c) {
-  if constexpr (DT == DT_BF16)
+  if constexpr (bf16_core<DT>())
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   else
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -189,7 +198,7 @@ __device__ __forceinline__ MfmaP<DT> mfma_scores(MfmaState<DT, D>& st, const Mfm
   for (int k = 0; k < 8; ++k) {
     const float w = __builtin_amdgcn_exp2f(fmaf(s[k], scale_log2, -mref));
     psum += w;
-    if constexpr (DT == DT_BF16) {
+    if constexpr (bf16_core<DT>()) {
       const __bf16 h = (__bf16)w;
       p.hi[k] = h;
       p.lo[k] = (__bf16)(w - (float)h);

@@ -57,11 +57,14 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(ReshapeArgs a) {
   }
 }
 
-// FP8 pools ("vLLM 深度拆解" §10.1 names FP8 with calibrated scales): the fp16 inputs are
+// FP8 pools ("vLLM 深度拆解" §10.1 names FP8 with calibrated scales): the fp16 or bf16 inputs are
 // quantised on the way in, element x -> e4m3(fp32(x) / scale) with one scale per pool.  One
 // thread per 16-byte K chunk (16 elements: two 16-byte input loads, one 16-byte store), then
 // one thread per V element (a byte store into the token's column of its dimension row).
+template <int DT>  // DT_FP8: fp16 inputs; DT_FP8B: bf16 inputs
 __global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(ReshapeArgs a) {
+  auto lo = [](uint32_t w) { return DT == DT_FP8B ? bf16_lo(w) : f16_lo(w); };
+  auto hi = [](uint32_t w) { return DT == DT_FP8B ? bf16_hi(w) : f16_hi(w); };
   constexpr int X = 16;
   const int H = a.num_kv_heads, D = a.head_dim, NCH = D / X;
   const int64_t nk = a.num_tokens * H * NCH;
@@ -82,9 +85,8 @@ __global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(ReshapeArgs 
     for (int k = 0; k < 4; ++k) {
       const uint4& h = k < 2 ? h0 : h1;
       const uint32_t p0 = (k & 1) ? h.z : h.x, p1 = (k & 1) ? h.w : h.y;
-      w[k] = f32_to_fp8(f16_lo(p0) / a.k_scale) | (f32_to_fp8(f16_hi(p0) / a.k_scale) << 8) |
-             (f32_to_fp8(f16_lo(p1) / a.k_scale) << 16) |
-             (f32_to_fp8(f16_hi(p1) / a.k_scale) << 24);
+      w[k] = f32_to_fp8(lo(p0) / a.k_scale) | (f32_to_fp8(hi(p0) / a.k_scale) << 8) |
+             (f32_to_fp8(lo(p1) / a.k_scale) << 16) | (f32_to_fp8(hi(p1) / a.k_scale) << 24);
     }
     typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
     char* dst = reinterpret_cast<char*>(a.k_cache) + ((((blk * H + g) * NCH + c) * kBlock + off) * 16);
@@ -98,18 +100,22 @@ __global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(ReshapeArgs 
     if (slot < 0) return;
     const int64_t blk = slot / kBlock;
     const int off = (int)(slot - blk * kBlock);
-    const float x = (float)reinterpret_cast<const _Float16*>(a.value)[e];
+    const uint32_t xb = reinterpret_cast<const uint16_t*>(a.value)[e];
+    const float x = DT == DT_FP8B ? bf16_lo(xb) : f16_lo(xb);
     __builtin_nontemporal_store((uint8_t)f32_to_fp8(x / a.v_scale),
                                 reinterpret_cast<uint8_t*>(a.v_cache) + ((blk * H + g) * D + d) * kBlock + off);
   }
 }
 
 hipError_t launch_reshape(int dt, const ReshapeArgs& a, hipStream_t st) {
-  if (dt == DT_FP8) {
+  if (is_fp8(dt)) {
     const int64_t threads = a.num_tokens * a.num_kv_heads * (a.head_dim / 16 + a.head_dim);
     const int64_t grid = (threads + 255) / 256;
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL(reshape_and_cache_fp8_kernel, dim3((unsigned)grid), dim3(256), 0, st, a);
+    if (dt == DT_FP8B)
+      hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<DT_FP8B>, dim3((unsigned)grid), dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<DT_FP8>, dim3((unsigned)grid), dim3(256), 0, st, a);
     return hipGetLastError();
   }
   const int X = dt == DT_F32 ? 4 : 8;

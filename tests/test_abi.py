@@ -69,7 +69,7 @@ def test_kv_cache_bytes_and_validation(lib):
     for bad in (_g(head_dim=96), _g(block_size=48), _g(block_size=8), _g(block_size=128),
                 _g(num_q_heads=6, num_kv_heads=4),
                 _g(kv_dtype=7), _g(out_dtype=1), _g(num_q_heads=64, num_kv_heads=2),
-                _g(num_seqs=-1), _g(q_dtype=1), _g(kv_dtype=3, q_dtype=2),
+                _g(num_seqs=-1), _g(q_dtype=1), _g(kv_dtype=3, q_dtype=0),
                 _g(kv_dtype=3, k_scale=0.0), _g(kv_dtype=3, v_scale=float("inf"))):
         assert lib.pa_kv_cache_bytes(ctypes.byref(bad)) == 0
     # 32- and 64-token blocks

@@ -499,6 +499,17 @@ def test_fp8_gqa_matrix_cores(dev, Hq, Hkv, D):
     parity(dev, _fp8(W.build_batch("fp8_gqa", "f16", ctx, np.ones(len(ctx)), Hq, Hkv, D, rng)))
 
 
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (32, 4)])
+def test_fp8_bf16_queries(dev, Hq, Hkv):
+    """FP8 pools behind bf16 queries, keys and values (cache write from bf16, vector and
+    matrix-core decode), fp32 and bf16 outputs."""
+    rng = np.random.default_rng(2400 + Hq)
+    ctx = np.array(EDGE_CTX + list(rng.integers(1, 5000, size=6)))
+    b = _fp8(W.build_batch("fp8_bf16", "bf16", ctx, np.ones(len(ctx)), Hq, Hkv, 128, rng))
+    parity(dev, b)
+    parity(dev, b, out_f32=False)
+
+
 def test_gqa_long_fp8(dev):
     b = W.make("gqa_long_fp8")
     rows = np.arange(0, b.num_q_rows, 3, dtype=np.int32)
