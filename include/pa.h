@@ -41,8 +41,9 @@
  * reshape_and_cache stores e4m3(fp32(x) / scale), the fp32 quotient rounded to the nearest
  * E4M3 ("E4M3FN": bias 7, no infinity, largest 448) with ties to even, magnitudes from 448
  * up saturating to 448; attention reads an element as its E4M3 value times the scale.
- * Supported by pa_reshape_and_cache, pa_copy_blocks and pa_decode (one row per sequence);
- * pa_decode with query_start_loc and pa_decode_partitioned return PA_ERR_UNSUPPORTED.
+ * Supported by pa_reshape_and_cache, pa_copy_blocks, pa_decode (one row per sequence),
+ * pa_decode_partitioned and pa_decode_reduce (out in q_dtype or fp32); pa_decode with
+ * query_start_loc returns PA_ERR_UNSUPPORTED.
  *
  * Rows and positions.  query_start_loc ("vLLM 架构源码解析 第1篇" §3.3.2) is NULL when every sequence has one
  * query row (row r belongs to sequence r, num_q_rows == num_seqs), else an int32 [S + 1]

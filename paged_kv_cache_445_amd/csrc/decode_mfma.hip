@@ -284,9 +284,13 @@ static hipError_t launch_d(const DecodeArgs& a, int grid, hipStream_t st) {
 // stream (when the chunk kernel runs beside it)
 hipError_t launch_mfma_decode(int dt, int mode, const DecodeArgs& a, int grid, hipStream_t st) {
   const bool f16 = dt == DT_F16;
-  // FP8 pools: one row per sequence, MODE_EVEN (the host rejects the rest)
-  if (dt == DT_FP8) return launch_d<DT_FP8, MODE_EVEN, false>(a, grid, st);
-  if (dt == DT_FP8B) return launch_d<DT_FP8B, MODE_EVEN, false>(a, grid, st);
+  // FP8 pools: one row per sequence (the host rejects multi-row batches)
+  if (dt == DT_FP8)
+    return mode == MODE_EVEN ? launch_d<DT_FP8, MODE_EVEN, false>(a, grid, st)
+                             : launch_d<DT_FP8, MODE_PARTITION, false>(a, grid, st);
+  if (dt == DT_FP8B)
+    return mode == MODE_EVEN ? launch_d<DT_FP8B, MODE_EVEN, false>(a, grid, st)
+                             : launch_d<DT_FP8B, MODE_PARTITION, false>(a, grid, st);
   if (mode == MODE_EVEN) {
     if (a.max_rows > 1 && a.lean)
       return f16 ? launch_d<DT_F16, MODE_EVEN, true, true>(a, grid, st)
@@ -313,8 +317,12 @@ static int occ(int head_dim, int lds) {
 }
 
 int mfma_decode_max_blocks_per_cu(int dt, int head_dim, int mode, int lds_bytes) {
-  if (dt == DT_FP8) return occ<DT_FP8, MODE_EVEN>(head_dim, lds_bytes);
-  if (dt == DT_FP8B) return occ<DT_FP8B, MODE_EVEN>(head_dim, lds_bytes);
+  if (dt == DT_FP8)
+    return mode == MODE_EVEN ? occ<DT_FP8, MODE_EVEN>(head_dim, lds_bytes)
+                             : occ<DT_FP8, MODE_PARTITION>(head_dim, lds_bytes);
+  if (dt == DT_FP8B)
+    return mode == MODE_EVEN ? occ<DT_FP8B, MODE_EVEN>(head_dim, lds_bytes)
+                             : occ<DT_FP8B, MODE_PARTITION>(head_dim, lds_bytes);
   if (mode == MODE_EVEN)
     return dt == DT_F16 ? occ<DT_F16, MODE_EVEN>(head_dim, lds_bytes)
                         : occ<DT_BF16, MODE_EVEN>(head_dim, lds_bytes);

@@ -623,7 +623,6 @@ static hipError_t launch_d(const DecodeArgs& a, int grid, hipStream_t st) {
   return hipGetLastError();
 }
 
-// FP8 pools run in MODE_EVEN only (pa_decode_partitioned rejects them)
 hipError_t launch_valu_decode(int dt, int mode, const DecodeArgs& a, int grid, hipStream_t st) {
   if (mode == MODE_EVEN) {
     if (dt == DT_F32) return launch_d<DT_F32, MODE_EVEN>(a, grid, st);
@@ -634,6 +633,8 @@ hipError_t launch_valu_decode(int dt, int mode, const DecodeArgs& a, int grid, h
   }
   if (dt == DT_F32) return launch_d<DT_F32, MODE_PARTITION>(a, grid, st);
   if (dt == DT_F16) return launch_d<DT_F16, MODE_PARTITION>(a, grid, st);
+  if (dt == DT_FP8) return launch_d<DT_FP8, MODE_PARTITION>(a, grid, st);
+  if (dt == DT_FP8B) return launch_d<DT_FP8B, MODE_PARTITION>(a, grid, st);
   return launch_d<DT_BF16, MODE_PARTITION>(a, grid, st);
 }
 
@@ -674,6 +675,8 @@ int valu_decode_max_blocks_per_cu(int dt, int head_dim, int hpw, int mode, int l
   }
   if (dt == DT_F32) return occ<DT_F32, MODE_PARTITION>(head_dim, 1, lds);
   if (dt == DT_F16) return occ<DT_F16, MODE_PARTITION>(head_dim, 1, lds);
+  if (dt == DT_FP8) return occ<DT_FP8, MODE_PARTITION>(head_dim, 1, lds);
+  if (dt == DT_FP8B) return occ<DT_FP8B, MODE_PARTITION>(head_dim, 1, lds);
   return occ<DT_BF16, MODE_PARTITION>(head_dim, 1, lds);
 }
 

@@ -409,7 +409,6 @@ pa_status pa_decode_partitioned(float* tmp_out, float* max_logits, float* exp_su
   const pa_status gs = check_geom(g);
   if (gs != PA_OK) return gs;
   if (num_q_rows != g->num_seqs) return PA_ERR_SHAPE;
-  if (g->kv_dtype == PA_FP8_E4M3) return PA_ERR_UNSUPPORTED;
   if (partition_size <= 0 || partition_size % pa::kMfmaUnit || max_partitions <= 0)
     return PA_ERR_SHAPE;
   if ((int64_t)max_partitions * partition_size < (int64_t)g->max_blocks_per_seq * g->block_size)
@@ -434,6 +433,10 @@ pa_status pa_decode_partitioned(float* tmp_out, float* max_logits, float* exp_su
   a.head_dim = g->head_dim;
   a.max_blocks_per_seq = g->max_blocks_per_seq;
   a.scale_log2 = scale_to_log2(scale);
+  if (g->kv_dtype == PA_FP8_E4M3) {
+    a.scale_log2 *= g->k_scale;  // a stored key stands for its E4M3 value times k_scale
+    a.v_factor = g->v_scale;
+  }
   a.max_partitions = max_partitions;
   const bool mf = use_mfma(g);
   a.partition_units = partition_size / (mf ? pa::kMfmaUnit : pa::kValuUnit);
@@ -441,8 +444,8 @@ pa_status pa_decode_partitioned(float* tmp_out, float* max_logits, float* exp_su
   a.cols = g->num_q_heads / g->num_kv_heads;
   a.blk_shift = blk_shift(g);
   const int grid = split_grid(g, pa::MODE_PARTITION, mf ? 1 : 0);
-  hipError_t e = mf ? pa::launch_mfma_decode(g->kv_dtype, pa::MODE_PARTITION, a, grid, (hipStream_t)stream)
-                    : pa::launch_valu_decode(g->kv_dtype, pa::MODE_PARTITION, a, grid, (hipStream_t)stream);
+  hipError_t e = mf ? pa::launch_mfma_decode(kdt(g), pa::MODE_PARTITION, a, grid, (hipStream_t)stream)
+                    : pa::launch_valu_decode(kdt(g), pa::MODE_PARTITION, a, grid, (hipStream_t)stream);
   return hip_status(e);
 }
 
@@ -452,7 +455,6 @@ pa_status pa_decode_reduce(void* out, const float* tmp_out, const float* max_log
   const pa_status gs = check_geom(g);
   if (gs != PA_OK) return gs;
   if (num_q_rows < 0 || max_partitions <= 0) return PA_ERR_SHAPE;
-  if (g->kv_dtype == PA_FP8_E4M3) return PA_ERR_UNSUPPORTED;
   if (num_q_rows == 0) return PA_OK;
   if (!out || !tmp_out || !max_logits || !exp_sums) return PA_ERR_NULL;
   pa::PartReduceArgs a{};
@@ -464,7 +466,8 @@ pa_status pa_decode_reduce(void* out, const float* tmp_out, const float* max_log
   a.head_dim = g->head_dim;
   a.max_partitions = max_partitions;
   a.out_f32 = g->out_dtype == PA_F32 && g->kv_dtype != PA_F32;
-  return hip_status(pa::launch_part_reduce(g->kv_dtype, a, (hipStream_t)stream));
+  // the merged rows take the queries' type (fp16 or bf16 behind FP8 pools) unless fp32
+  return hip_status(pa::launch_part_reduce(g->q_dtype, a, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -131,6 +131,8 @@ def test_host_checks_return_codes_without_launching(lib):
     assert lib.pa_decode_partitioned(*([dummy] * 8), 4, 0.1, 48, 8, ctypes.byref(g), None) == -2
     assert lib.pa_decode_partitioned(*([dummy] * 8), 4, 0.1, 32, 3, ctypes.byref(g), None) == -2
     assert lib.pa_decode_partitioned(*([dummy] * 7), None, 4, 0.1, 32, 4, ctypes.byref(g), None) == -1
+    # FP8 pools are accepted (the missing pointer is what fails)
+    assert lib.pa_decode_partitioned(*([dummy] * 7), None, 4, 0.1, 32, 4, ctypes.byref(g8), None) == -1
 
     lib.pa_decode_reduce.restype = ctypes.c_int
     lib.pa_decode_reduce.argtypes = [vp] * 4 + [ctypes.c_int32, ctypes.c_int32,

@@ -243,14 +243,20 @@ def test_many_ragged_sequences(dev, dtype, Hq, Hkv, D):
 @pytest.mark.parametrize("dtype,Hq,Hkv,ps", [("bf16", 16, 2, 512), ("f16", 8, 8, 256),
                                              ("f32", 4, 4, 64), ("bf16", 8, 8, 32)])
 def test_partitioned_and_reduce(dev, dtype, Hq, Hkv, ps):
-    import torch
-    import oracle
-    from paged_kv_cache_445_amd import pa
     rng = np.random.default_rng(ps + Hq)
     D = 64 if dtype == "f32" else 128
     b = W.build_batch("part", dtype, rng.integers(1, 3000, size=10), np.ones(10), Hq, Hkv, D, rng)
+    check_partitioned(dev, b, ps)
+
+
+def check_partitioned(dev, b, ps):
+    """pa_decode_partitioned's partials against the oracle's, then pa_decode_reduce's merge."""
+    import torch
+    import oracle
+    from paged_kv_cache_445_amd import pa
+    Hq, D = b.num_q_heads, b.head_dim
     db = run_gpu(dev, b)
-    P = -(-b.max_blocks_per_seq * 16 // ps)
+    P = -(-b.max_blocks_per_seq * b.block_size // ps)
     R = b.num_q_rows
     tmp = torch.full((R, Hq, P, D), 7.0, device=db.device)
     ml = torch.zeros((R, Hq, P), device=db.device)
@@ -267,7 +273,7 @@ def test_partitioned_and_reduce(dev, dtype, Hq, Hkv, ps):
     nonempty = l > 0
     assert np.array_equal(gl > 0, nonempty)
     assert np.isneginf(gm[~nonempty]).all()
-    tol = TOL[dtype]
+    tol = TOL[b.dtype]
     check_out(gm[nonempty].astype(np.float64), m[nonempty], tol, "max_logits")
     # exp_sums are sums of up to ps terms <= 1: compare relative to the sum
     rel = np.abs(gl[nonempty] - l[nonempty]) / l[nonempty]
@@ -508,6 +514,17 @@ def test_fp8_bf16_queries(dev, Hq, Hkv):
     b = _fp8(W.build_batch("fp8_bf16", "bf16", ctx, np.ones(len(ctx)), Hq, Hkv, 128, rng))
     parity(dev, b)
     parity(dev, b, out_f32=False)
+
+
+@pytest.mark.parametrize("qdt,Hq,Hkv,ps", [("f16", 8, 8, 256), ("bf16", 16, 2, 512),
+                                           ("f16", 32, 4, 64)])
+def test_fp8_partitioned_and_reduce(dev, qdt, Hq, Hkv, ps):
+    """FP8 pools through the fixed partitions (vector path for MHA, matrix cores for GQA) and
+    the merge, with fp16 or bf16 queries."""
+    rng = np.random.default_rng(2400 + ps + Hq)
+    b = W.build_batch("fp8_part", qdt, rng.integers(1, 3000, size=10), np.ones(10), Hq, Hkv,
+                      128, rng)
+    check_partitioned(dev, _fp8(b), ps)
 
 
 def test_gqa_long_fp8(dev):
