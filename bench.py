@@ -56,6 +56,9 @@ DESCRIPTIONS = {
                        "drafts) x 32 heads (MHA), head_dim 128, fp16 KV, prior ctx U[256,2048]",
     "spec_verify_gqa_bf16": "speculative verify step: 64 seqs x 4 causal rows, 32 q / 8 kv "
                             "heads, head_dim 128, bf16 KV, prior ctx U[512,4096]",
+    "spec_verify_fp8": "speculative verify step with FP8 E4M3 KV (per-pool scales 6.5/448): "
+                       "32 seqs x 6 causal rows x 32 heads (MHA), head_dim 128, fp16 q, prior "
+                       "ctx U[256,2048]",
     "cow_copy_f16": "copy-on-write block copies: 256 (source, destination) pairs of LLaMA-7B "
                     "blocks (32 kv heads x 128 x 16 tokens fp16, 128 KiB per pool) in an "
                     "8192-block pool",

@@ -68,11 +68,6 @@ __device__ void mfma_attend(const DecodeArgs& a, int s, int g, int u0, int u1, i
       else
         mfma_unit<DT, D, true, false>(st, kb, vb, qb, a.scale_log2, valid - 1, valid);
     });
-    if constexpr (is_fp8(DT)) {
-      // a stored V value stands for its E4M3 value times v_scale (k_scale is in scale_log2)
-#pragma unroll
-      for (int j = 0; j < C::NJ; ++j) st.acc[j] *= a.v_factor;
-    }
   } else {
     const int last0 = ctx - nr;                 // last visible key of the first row
     const int mine = min(last0 + jr, ctx - 1);  // ... of this lane's column (padding: ctx - 1)
@@ -97,6 +92,11 @@ __device__ void mfma_attend(const DecodeArgs& a, int s, int g, int u0, int u1, i
         pv(vb, scores(kb, u), u);
       });
     }
+  }
+  if constexpr (is_fp8(DT)) {
+    // a stored V value stands for its E4M3 value times v_scale (k_scale is in scale_log2)
+#pragma unroll
+    for (int j = 0; j < C::NJ; ++j) st.acc[j] *= a.v_factor;
   }
 }
 
@@ -284,13 +284,18 @@ static hipError_t launch_d(const DecodeArgs& a, int grid, hipStream_t st) {
 // stream (when the chunk kernel runs beside it)
 hipError_t launch_mfma_decode(int dt, int mode, const DecodeArgs& a, int grid, hipStream_t st) {
   const bool f16 = dt == DT_F16;
-  // FP8 pools: one row per sequence (the host rejects multi-row batches)
-  if (dt == DT_FP8)
-    return mode == MODE_EVEN ? launch_d<DT_FP8, MODE_EVEN, false>(a, grid, st)
-                             : launch_d<DT_FP8, MODE_PARTITION, false>(a, grid, st);
-  if (dt == DT_FP8B)
-    return mode == MODE_EVEN ? launch_d<DT_FP8B, MODE_EVEN, false>(a, grid, st)
-                             : launch_d<DT_FP8B, MODE_PARTITION, false>(a, grid, st);
+  // FP8 pools: decode and verify rows (the host rejects batches that need the chunk kernel,
+  // so the lean stream is never asked for)
+  if (dt == DT_FP8) {
+    if (mode == MODE_PARTITION) return launch_d<DT_FP8, MODE_PARTITION, false>(a, grid, st);
+    return a.max_rows > 1 ? launch_d<DT_FP8, MODE_EVEN, true>(a, grid, st)
+                          : launch_d<DT_FP8, MODE_EVEN, false>(a, grid, st);
+  }
+  if (dt == DT_FP8B) {
+    if (mode == MODE_PARTITION) return launch_d<DT_FP8B, MODE_PARTITION, false>(a, grid, st);
+    return a.max_rows > 1 ? launch_d<DT_FP8B, MODE_EVEN, true>(a, grid, st)
+                          : launch_d<DT_FP8B, MODE_EVEN, false>(a, grid, st);
+  }
   if (mode == MODE_EVEN) {
     if (a.max_rows > 1 && a.lean)
       return f16 ? launch_d<DT_F16, MODE_EVEN, true, true>(a, grid, st)

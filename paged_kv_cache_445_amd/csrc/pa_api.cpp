@@ -115,9 +115,9 @@ bool use_mfma(const pa_geom* g) {
 
 // Which decode kernel runs a pa_decode call, and which sequences it takes (max_len: an upper
 // bound of the rows of any sequence; 1 without query_start_loc).
-//  - GQA (16-bit, G >= 2): the matrix-core kernel; when sequences may have several rows it
+//  - GQA (16-bit or FP8, G >= 2): the matrix-core kernel; when sequences may have several rows it
 //    also takes those of up to 16 / G rows (a speculative verify step), nr * G columns at once.
-//  - MHA 16-bit with sequences of several rows: the matrix-core kernel too (G = 1, up to 16
+//  - MHA 16-bit or FP8 with sequences of several rows: the matrix-core kernel too (G = 1, up to 16
 //    rows a sequence), so verify rows read their K and V once instead of through the chunk
 //    kernel's 128-column items.
 //  - otherwise the vector kernel, one row per sequence.
@@ -132,7 +132,7 @@ Route route(const pa_geom* g, int32_t max_len) {
   const int G = g->num_q_heads / g->num_kv_heads;
   const bool multi = max_len > 1;
   if (use_mfma(g)) return {1, multi ? 16 / G : 1, multi ? 16 / G * G : G};
-  if ((g->kv_dtype == PA_F16 || g->kv_dtype == PA_BF16) && multi) return {1, 16, 16};
+  if (g->kv_dtype != PA_F32 && multi) return {1, 16, 16};
   return {0, 1, 1};
 }
 
@@ -328,8 +328,7 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_NULL;
   if (!std::isfinite(scale)) return PA_ERR_SHAPE;
   const int G = g->num_q_heads / g->num_kv_heads;
-  if (query_start_loc && (g->kv_dtype == PA_F32 || g->kv_dtype == PA_FP8_E4M3 || 16 % G != 0))
-    return PA_ERR_UNSUPPORTED;
+  if (query_start_loc && (g->kv_dtype == PA_F32 || 16 % G != 0)) return PA_ERR_UNSUPPORTED;
   hipStream_t st = (hipStream_t)stream;
 
   // rows of the longest sequence: at most max_query_len (0: unknown) and num_q_rows
@@ -337,6 +336,8 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   if (query_start_loc)
     max_len = max_query_len > 0 && max_query_len < num_q_rows ? max_query_len : num_q_rows;
   const Route rt = route(g, max_len);
+  // FP8 pools: no chunk kernel, so every sequence must fit the decode kernel's rows
+  if (g->kv_dtype == PA_FP8_E4M3 && max_len > rt.max_rows) return PA_ERR_UNSUPPORTED;
   const int grid = split_grid(g, pa::MODE_EVEN, rt.path);
   const size_t need = even_workspace_bytes(g, rt);
   if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;

@@ -120,8 +120,14 @@ def test_host_checks_return_codes_without_launching(lib):
     assert lib.pa_decode(dummy, dummy, dummy, dummy, dummy, dummy, dummy, 9, 0, 0.1, dummy, 1 << 30,
                          ctypes.byref(gf), None) == -3
     g8 = _g(kv_dtype=3, out_dtype=1, num_q_heads=4, num_kv_heads=4)
-    assert lib.pa_decode(dummy, dummy, dummy, dummy, dummy, dummy, dummy, 9, 0, 0.1, dummy, 1 << 30,
+    # FP8 rows: more than 16 / G rows in a sequence (unknown max_query_len: num_q_rows)
+    assert lib.pa_decode(dummy, dummy, dummy, dummy, dummy, dummy, dummy, 17, 0, 0.1, dummy, 1 << 30,
                          ctypes.byref(g8), None) == -3
+    assert lib.pa_decode(dummy, dummy, dummy, dummy, dummy, dummy, dummy, 40, 17, 0.1, dummy, 1 << 30,
+                         ctypes.byref(g8), None) == -3
+    g8q = _g(kv_dtype=3, out_dtype=1, num_q_heads=8, num_kv_heads=2)
+    assert lib.pa_decode(dummy, dummy, dummy, dummy, dummy, dummy, dummy, 40, 5, 0.1, dummy, 1 << 30,
+                         ctypes.byref(g8q), None) == -3
 
     lib.pa_decode_partitioned.restype = ctypes.c_int
     lib.pa_decode_partitioned.argtypes = [vp] * 8 + [ctypes.c_int32, ctypes.c_float,

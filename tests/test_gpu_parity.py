@@ -527,6 +527,19 @@ def test_fp8_partitioned_and_reduce(dev, qdt, Hq, Hkv, ps):
     check_partitioned(dev, _fp8(b), ps)
 
 
+def test_fp8_verify_rows(dev):
+    """FP8 pools with speculative verify rows (the matrix-core columns are (row, head) pairs):
+    the LLaMA-7B verify step, and mixes of 1..16/G rows a sequence with decode rows, short and
+    long contexts, fp16 and bf16 queries."""
+    parity(dev, W.make("spec_verify_fp8"))
+    rng = np.random.default_rng(2500)
+    prior = np.array([0, 9, 1, 300, 14, 2000, 1, 31, 700, 45, 9000, 5])
+    for qdt, Hq, Hkv, top in (("f16", 8, 8, 16), ("bf16", 16, 4, 4), ("f16", 16, 2, 2)):
+        n = rng.integers(1, top + 1, size=len(prior))
+        n[0] = top
+        parity(dev, _fp8(W.build_batch("fp8_verify", qdt, prior + n, n, Hq, Hkv, 128, rng)))
+
+
 def test_gqa_long_fp8(dev):
     b = W.make("gqa_long_fp8")
     rows = np.arange(0, b.num_q_rows, 3, dtype=np.int32)
