@@ -59,6 +59,8 @@ DESCRIPTIONS = {
     "spec_verify_fp8": "speculative verify step with FP8 E4M3 KV (per-pool scales 6.5/448): "
                        "32 seqs x 6 causal rows x 32 heads (MHA), head_dim 128, fp16 q, prior "
                        "ctx U[256,2048]",
+    "mixed_chunked_fp8": "mixed step with FP8 E4M3 KV (per-pool scales 6.5/448): 8 x 512-row "
+                         "causal chunks + 120 decode rows, 32 q / 8 kv heads, head_dim 128, bf16 q",
     "cow_copy_f16": "copy-on-write block copies: 256 (source, destination) pairs of LLaMA-7B "
                     "blocks (32 kv heads x 128 x 16 tokens fp16, 128 KiB per pool) in an "
                     "8192-block pool",
@@ -368,7 +370,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8_e4m3 KV, f16 q" if b.pool_dtype == "fp8" else b.dtype,
+        "dtype": f"fp8_e4m3 KV, {b.dtype} q" if b.pool_dtype == "fp8" else b.dtype,
         "data": "synthetic",
         "config": {
             "workload": args.workload,

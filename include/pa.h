@@ -41,10 +41,7 @@
  * reshape_and_cache stores e4m3(fp32(x) / scale), the fp32 quotient rounded to the nearest
  * E4M3 ("E4M3FN": bias 7, no infinity, largest 448) with ties to even, magnitudes from 448
  * up saturating to 448; attention reads an element as its E4M3 value times the scale.
- * Supported by pa_reshape_and_cache, pa_copy_blocks, pa_decode, pa_decode_partitioned and
- * pa_decode_reduce (out in q_dtype or fp32).  With query_start_loc, pa_decode takes FP8
- * pools only when no sequence has more than 16 / G rows (speculative verify rows), which
- * max_query_len (or num_q_rows when it is 0) must show; otherwise PA_ERR_UNSUPPORTED.
+ * Supported by every entry point; out is q_dtype or fp32.
  *
  * Rows and positions.  query_start_loc ("vLLM 架构源码解析 第1篇" §3.3.2) is NULL when every sequence has one
  * query row (row r belongs to sequence r, num_q_rows == num_seqs), else an int32 [S + 1]
@@ -150,9 +147,8 @@ size_t pa_workspace_size(const pa_geom* geom, int32_t num_q_rows);
  * context crossing a split boundary is computed in pieces, and the piece that finishes last
  * merges them by log-sum-exp inside the same kernel.  A second kernel runs the multi-row
  * sequences when query_start_loc is given.
- * Sequences with several rows (query_start_loc) need a 16-bit or FP8 kv_dtype (FP8: at most
- * 16 / G rows a sequence) and a query group G = Hq / Hkv that divides 16; otherwise
- * PA_ERR_UNSUPPORTED.
+ * Sequences with several rows (query_start_loc) need a 16-bit or FP8 kv_dtype and a query
+ * group G = Hq / Hkv that divides 16; otherwise PA_ERR_UNSUPPORTED.
  */
 pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
                     const int32_t* block_tables, const int32_t* context_lens,

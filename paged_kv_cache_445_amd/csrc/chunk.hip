@@ -12,6 +12,11 @@
 // head) pair: 128 / G consecutive rows x the G query heads of g.  The workgroup stages each
 // 32-token K/V unit in LDS once and its four waves each run 32 columns over it through the
 // matrix-core step of pa_mfma.h, so one unit read from memory serves 128 columns.
+//
+// FP8 pools ("vLLM 深度拆解" §10.1) take the same path: each 8-byte half of an E4M3 chunk is
+// widened to the query's 16-bit type (exact for every E4M3 value) on its way into LDS, where
+// the unit then has the 16-bit layout; k_scale is in the score factor and v_scale multiplies
+// the output.
 #include "pa_device.h"
 #include "pa_internal.h"
 #include "pa_mfma.h"
@@ -50,8 +55,9 @@ __device__ inline void build_chunk_plan(int32_t* base, const ChunkPlanIn& p) {
 // workgroup streams the item's keys in 32-token units: every unit (K and V of two blocks) is
 // loaded once by the whole workgroup, two units ahead, into one of two LDS buffers, and each
 // wave then runs its 32 query columns (two 16-column MFMA blocks, per-column causal limits)
-// over it.
-template <int DT, int D>
+// over it.  DT is the 16-bit type of the queries and of the staged unit; F8: the pools hold
+// E4M3 bytes.
+template <int DT, int D, bool F8>
 __device__ void chunk_item(const DecodeArgs& a, int s, int g, int cb, char* lds_units) {
   using C = MfmaCfg<DT, D>;
   using CT = ChunkTile<D>;
@@ -104,24 +110,34 @@ __device__ void chunk_item(const DecodeArgs& a, int s, int g, int cb, char* lds_
   }
 
   const MfmaLaneOffsets<DT, D> o = mfma_offsets<DT, D>();
-  const int64_t blk_stride = (int64_t)a.num_kv_heads * C::TILE;
-  const char* kc = reinterpret_cast<const char*>(a.k_cache) + (int64_t)g * C::TILE;
-  const char* vc = reinterpret_cast<const char*>(a.v_cache) + (int64_t)g * C::TILE;
+  constexpr int64_t PTILE = F8 ? C::TILE / 2 : C::TILE;  // a block of one KV head in the pool
+  const int64_t blk_stride = (int64_t)a.num_kv_heads * PTILE;
+  const char* kc = reinterpret_cast<const char*>(a.k_cache) + (int64_t)g * PTILE;
+  const char* vc = reinterpret_cast<const char*>(a.v_cache) + (int64_t)g * PTILE;
   const int32_t* bt_row = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
   const int nblk = (nkeys_g + kBlock - 1) / kBlock;
   const int nu = (nkeys_g + kMfmaUnit - 1) / kMfmaUnit;
 
   // this thread's share of a unit: chunk k * kWG + threadIdx.x of the four tiles
   // [K block a, K block b, V block a, V block b]
-  int ld_tile[CT::LOADS], ld_off[CT::LOADS];
+  // (16-bit chunk c of a tile; FP8: its 8 source bytes, half of E4M3 K chunk
+  // (c / 32) * 16 + c % 16, or bytes 8c.. of the V tile)
+  int ld_tile[CT::LOADS], ld_off[CT::LOADS], src_off[CT::LOADS];
 #pragma unroll
   for (int k = 0; k < CT::LOADS; ++k) {
     const int c = k * kWG + threadIdx.x;
     ld_tile[k] = c / CT::CPT;
-    ld_off[k] = (c % CT::CPT) * 16;
+    const int cc = c % CT::CPT;
+    ld_off[k] = cc * 16;
+    if constexpr (F8)
+      src_off[k] = ld_tile[k] & 2 ? cc * 8 : (((cc >> 5) << 4) + (cc & 15)) * 16 + 8 * ((cc >> 4) & 1);
+    else
+      src_off[k] = cc * 16;
   }
+  using Raw = typename std::conditional<F8, uint2, uint4>::type;
+  constexpr int WDT = DT == DT_BF16 ? DT_FP8B : DT_FP8;  // widening of FP8 staged bytes
   int win0 = 0, win1 = 0, wbase = -1;  // block-table windows of 64 entries: [wbase, wbase + 128)
-  auto load_unit = [&](uint4* regs, int u) {
+  auto load_unit = [&](Raw* regs, int u) {
     const int e = 2 * u;
     if (wbase < 0 || e >= wbase + 128) {  // uniform; happens every 64 units
       wbase = e;
@@ -136,13 +152,19 @@ __device__ void chunk_item(const DecodeArgs& a, int s, int g, int cb, char* lds_
     for (int k = 0; k < CT::LOADS; ++k) {
       const int t = ld_tile[k];
       const char* base = (t & 2 ? vc : kc) + (t & 1 ? bb : ba) * blk_stride;
-      regs[k] = ld16(base + ld_off[k]);
+      regs[k] = *reinterpret_cast<const Raw*>(base + src_off[k]);
     }
   };
-  auto store_unit = [&](const uint4* regs, int buf) {
+  auto store_unit = [&](const Raw* regs, int buf) {
 #pragma unroll
-    for (int k = 0; k < CT::LOADS; ++k)
-      *reinterpret_cast<uint4*>(lds_units + buf * CT::UNIT + ld_tile[k] * CT::TILE + ld_off[k]) = regs[k];
+    for (int k = 0; k < CT::LOADS; ++k) {
+      uint4 v;
+      if constexpr (F8)
+        v = __builtin_bit_cast(uint4, operand<WDT>(regs[k]));
+      else
+        v = regs[k];
+      *reinterpret_cast<uint4*>(lds_units + buf * CT::UNIT + ld_tile[k] * CT::TILE + ld_off[k]) = v;
+    }
   };
 
   // Unit pipeline: the loads of unit u + 2 go out at the start of step u, unit u is computed
@@ -191,7 +213,7 @@ __device__ void chunk_item(const DecodeArgs& a, int s, int g, int cb, char* lds_
       }
     }
   };
-  uint4 ra[CT::LOADS], rb[CT::LOADS];
+  Raw ra[CT::LOADS], rb[CT::LOADS];
   load_unit(ra, 0);
   load_unit(rb, min(1, ulast));
   store_unit(ra, 0);
@@ -213,7 +235,8 @@ __device__ void chunk_item(const DecodeArgs& a, int s, int g, int cb, char* lds_
 #pragma unroll
   for (int c = 0; c < NCB; ++c) {
     const float ltot = cross_rows_sum(st[c].l);
-    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+    // FP8: a stored V value stands for its E4M3 value times v_scale
+    const float inv = ltot > 0.f ? (F8 ? a.v_factor : 1.f) / ltot : 0.f;
     const int col = 16 * c + n;
     const int jr = j0 + col / G, hr = col % G;
     if (jr < jend) {
@@ -237,7 +260,7 @@ constexpr int kMaxOrdered = 256;
 // of one (sequence, column block) consecutively.  With more than kMaxOrdered multi-row
 // sequences the items keep the sequence order instead, KV head slowest, numbered XCD-locally
 // so that each XCD works through mostly one KV head.
-template <int DT, int D>
+template <int DT, int D, bool F8>
 __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(2))) void chunk_kernel(DecodeArgs a) {
   extern __shared__ __align__(16) char lds_raw[];
   char* lds_units = lds_raw;  // two unit buffers
@@ -302,11 +325,21 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(2))) void c
       const int nb = base[s + 1] - base[s];
       cb = nb - 1 - (int)(k - base[s]);
     }
-    chunk_item<DT, D>(a, s, g, cb, lds_units);
+    chunk_item<DT, D, F8>(a, s, g, cb, lds_units);
     __syncthreads();  // the unit buffers are reused by the next item
   }
 }
 
+template <int DT, bool F8>
+static hipError_t launch_c(const DecodeArgs& a, int grid, size_t lds, hipStream_t st) {
+  if (a.head_dim == 64)
+    hipLaunchKernelGGL((chunk_kernel<DT, 64, F8>), dim3(grid), dim3(kWG), lds, st, a);
+  else
+    hipLaunchKernelGGL((chunk_kernel<DT, 128, F8>), dim3(grid), dim3(kWG), lds, st, a);
+  return hipGetLastError();
+}
+
+// dt: DT_F16 / DT_BF16 pools, or DT_FP8 / DT_FP8B (FP8 pools behind fp16 / bf16 queries)
 hipError_t launch_chunk(int dt, const DecodeArgs& a, int num_q_rows, hipStream_t st) {
   // one workgroup per work item: at most ceil(rows / rows_per_item) + num_seqs items per KV
   // head; a multiple of the XCD count keeps the XCD-local numbering on
@@ -317,18 +350,10 @@ hipError_t launch_chunk(int dt, const DecodeArgs& a, int num_q_rows, hipStream_t
   const size_t lds = (size_t)2 * (a.head_dim == 64 ? ChunkTile<64>::UNIT : ChunkTile<128>::UNIT) +
                      (size_t)(a.num_seqs + 1 + 3 * kMaxOrdered + 2) * sizeof(int32_t);
   if (grid <= 0) return hipSuccess;
-  if (dt == DT_F16) {
-    if (a.head_dim == 64)
-      hipLaunchKernelGGL((chunk_kernel<DT_F16, 64>), dim3(grid), dim3(kWG), lds, st, a);
-    else
-      hipLaunchKernelGGL((chunk_kernel<DT_F16, 128>), dim3(grid), dim3(kWG), lds, st, a);
-  } else {
-    if (a.head_dim == 64)
-      hipLaunchKernelGGL((chunk_kernel<DT_BF16, 64>), dim3(grid), dim3(kWG), lds, st, a);
-    else
-      hipLaunchKernelGGL((chunk_kernel<DT_BF16, 128>), dim3(grid), dim3(kWG), lds, st, a);
-  }
-  return hipGetLastError();
+  if (dt == DT_F16) return launch_c<DT_F16, false>(a, grid, lds, st);
+  if (dt == DT_BF16) return launch_c<DT_BF16, false>(a, grid, lds, st);
+  if (dt == DT_FP8) return launch_c<DT_F16, true>(a, grid, lds, st);
+  return launch_c<DT_BF16, true>(a, grid, lds, st);
 }
 
 }  // namespace pa

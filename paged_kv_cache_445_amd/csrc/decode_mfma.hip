@@ -284,15 +284,15 @@ static hipError_t launch_d(const DecodeArgs& a, int grid, hipStream_t st) {
 // stream (when the chunk kernel runs beside it)
 hipError_t launch_mfma_decode(int dt, int mode, const DecodeArgs& a, int grid, hipStream_t st) {
   const bool f16 = dt == DT_F16;
-  // FP8 pools: decode and verify rows (the host rejects batches that need the chunk kernel,
-  // so the lean stream is never asked for)
   if (dt == DT_FP8) {
     if (mode == MODE_PARTITION) return launch_d<DT_FP8, MODE_PARTITION, false>(a, grid, st);
+    if (a.max_rows > 1 && a.lean) return launch_d<DT_FP8, MODE_EVEN, true, true>(a, grid, st);
     return a.max_rows > 1 ? launch_d<DT_FP8, MODE_EVEN, true>(a, grid, st)
                           : launch_d<DT_FP8, MODE_EVEN, false>(a, grid, st);
   }
   if (dt == DT_FP8B) {
     if (mode == MODE_PARTITION) return launch_d<DT_FP8B, MODE_PARTITION, false>(a, grid, st);
+    if (a.max_rows > 1 && a.lean) return launch_d<DT_FP8B, MODE_EVEN, true, true>(a, grid, st);
     return a.max_rows > 1 ? launch_d<DT_FP8B, MODE_EVEN, true>(a, grid, st)
                           : launch_d<DT_FP8B, MODE_EVEN, false>(a, grid, st);
   }

@@ -336,8 +336,6 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   if (query_start_loc)
     max_len = max_query_len > 0 && max_query_len < num_q_rows ? max_query_len : num_q_rows;
   const Route rt = route(g, max_len);
-  // FP8 pools: no chunk kernel, so every sequence must fit the decode kernel's rows
-  if (g->kv_dtype == PA_FP8_E4M3 && max_len > rt.max_rows) return PA_ERR_UNSUPPORTED;
   const int grid = split_grid(g, pa::MODE_EVEN, rt.path);
   const size_t need = even_workspace_bytes(g, rt);
   if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
@@ -395,7 +393,7 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   std::lock_guard<std::mutex> lock(side->mu);
   hipError_t e = hipEventRecord(side->fork, st);
   if (e == hipSuccess) e = hipStreamWaitEvent(side->stream, side->fork, 0);
-  if (e == hipSuccess) e = pa::launch_chunk(g->kv_dtype, a, num_q_rows, side->stream);
+  if (e == hipSuccess) e = pa::launch_chunk(kdt(g), a, num_q_rows, side->stream);
   const hipError_t ed = decode();
   if (e == hipSuccess) e = hipEventRecord(side->join, side->stream);
   if (e == hipSuccess) e = hipStreamWaitEvent(st, side->join, 0);

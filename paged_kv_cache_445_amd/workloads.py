@@ -346,6 +346,16 @@ def spec_verify_gqa_bf16(seed: int = 4456, num_seqs: int = 64, num_draft: int = 
                        128, rng, max_blocks_per_seq=257)
 
 
+def mixed_chunked_fp8(seed: int = 4454) -> Batch:
+    """The mixed chunked-prefill step (same draws) with FP8 E4M3 pools behind bf16 queries,
+    per-pool scales 6.5 / 448."""
+    b = mixed_chunked_bf16(seed)
+    b.name = "mixed_chunked_fp8"
+    b.kv_dtype = "fp8"
+    b.k_scale = b.v_scale = float(np.float32(6.5 / 448))
+    return b
+
+
 def spec_verify_fp8(seed: int = 4455, num_seqs: int = 32, num_draft: int = 5) -> Batch:
     """The LLaMA-7B verify step (same draws) with FP8 E4M3 pools at per-pool scales
     6.5 / 448."""
@@ -367,6 +377,7 @@ PRESETS = {
     "spec_verify_f16": spec_verify_f16,
     "spec_verify_gqa_bf16": spec_verify_gqa_bf16,
     "spec_verify_fp8": spec_verify_fp8,
+    "mixed_chunked_fp8": mixed_chunked_fp8,
 }
 
 

@@ -115,17 +115,16 @@ def test_host_checks_return_codes_without_launching(lib):
     g0 = _g(num_seqs=0)
     assert lib.pa_decode(None, None, None, None, None, None, None, 0, 0, 0.1, None, 0,
                          ctypes.byref(g0), None) == 0
-    # fp32 or FP8 pools with multi-row sequences are not implemented
+    # fp32 pools with multi-row sequences are not implemented
     gf = _g(kv_dtype=0, out_dtype=0)
     assert lib.pa_decode(dummy, dummy, dummy, dummy, dummy, dummy, dummy, 9, 0, 0.1, dummy, 1 << 30,
                          ctypes.byref(gf), None) == -3
     g8 = _g(kv_dtype=3, out_dtype=1, num_q_heads=4, num_kv_heads=4)
-    # FP8 rows: more than 16 / G rows in a sequence (unknown max_query_len: num_q_rows)
-    assert lib.pa_decode(dummy, dummy, dummy, dummy, dummy, dummy, dummy, 17, 0, 0.1, dummy, 1 << 30,
-                         ctypes.byref(g8), None) == -3
-    assert lib.pa_decode(dummy, dummy, dummy, dummy, dummy, dummy, dummy, 40, 17, 0.1, dummy, 1 << 30,
-                         ctypes.byref(g8), None) == -3
-    g8q = _g(kv_dtype=3, out_dtype=1, num_q_heads=8, num_kv_heads=2)
+    # FP8 pools take multi-row sequences (the missing pointer is what fails); a group that
+    # does not divide 16 does not
+    assert lib.pa_decode(dummy, None, dummy, dummy, dummy, dummy, dummy, 40, 0, 0.1, dummy, 1 << 30,
+                         ctypes.byref(g8), None) == -1
+    g8q = _g(kv_dtype=3, out_dtype=1, num_q_heads=12, num_kv_heads=4)
     assert lib.pa_decode(dummy, dummy, dummy, dummy, dummy, dummy, dummy, 40, 5, 0.1, dummy, 1 << 30,
                          ctypes.byref(g8q), None) == -3
 

@@ -540,6 +540,23 @@ def test_fp8_verify_rows(dev):
         parity(dev, _fp8(W.build_batch("fp8_verify", qdt, prior + n, n, Hq, Hkv, 128, rng)))
 
 
+def test_fp8_chunked_prefill(dev):
+    """FP8 pools under chunked-prefill rows (the chunk kernel widens each staged unit to the
+    query type) beside decode and verify rows, MHA and GQA, fp16 and bf16 queries, with
+    max_query_len given and unknown."""
+    import torch
+    rng = np.random.default_rng(2600)
+    n = np.array([300, 1, 3, 129, 1, 64, 2, 17])
+    prior = np.array([0, 700, 40, 1500, 5, 2100, 33, 0])
+    for qdt, Hq, Hkv in (("f16", 8, 8), ("bf16", 16, 4), ("f16", 16, 2)):
+        b = _fp8(W.build_batch("fp8_chunk", qdt, prior + n, n, Hq, Hkv, 128, rng))
+        db, got, want = parity(dev, b)
+        db.max_query_len = 0
+        db.attend()
+        torch.cuda.synchronize()
+        check_out(db.out_host(), want, TOL[qdt], "max_query_len unknown")
+
+
 def test_gqa_long_fp8(dev):
     b = W.make("gqa_long_fp8")
     rows = np.arange(0, b.num_q_rows, 3, dtype=np.int32)
