@@ -37,6 +37,16 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_{workload}.txt")
 KERNEL_SOURCES = ["pa_device.h", "pa_internal.h", "pa_mfma.h", "decode_valu.hip",
                   "decode_mfma.hip", "reduce.hip", "chunk.hip", "pa_api.cpp"]
 
+def runs_chunk_kernel(b) -> bool:
+    """Whether pa_decode launches its multi-row kernel for this batch: the decode kernel
+    takes sequences of up to 16 / G rows (G = query heads per KV head) on 16-bit and FP8
+    pools, one row on fp32 pools."""
+    if b.query_start_loc is None:
+        return False
+    takes = 16 // (b.num_q_heads // b.num_kv_heads) if b.pool_dtype != "f32" else 1
+    return int(b.rows_per_seq().max()) > takes
+
+
 DESCRIPTIONS = {
     "llama7b_f16": "LLaMA-7B-shaped decode: 32 seqs x 32 heads (MHA), head_dim 128, fp16 KV, "
                    "block 16, ctx U[256,2048], 8192-block pool, permuted block table",
@@ -391,7 +401,7 @@ def main():
         "roofline": {
             "bound": bound,
             "kernel": "pa_decode (decode kernel with in-kernel split merge"
-                      + (" + chunk kernel)" if b.query_start_loc is not None else ")"),
+                      + (" + chunk kernel)" if runs_chunk_kernel(b) else ")"),
             "achieved": round(achieved, 2),
             "peak": peak,
             "unit": punit,
