@@ -516,14 +516,17 @@ def test_fp8_bf16_queries(dev, Hq, Hkv):
     parity(dev, b, out_f32=False)
 
 
-@pytest.mark.parametrize("qdt,Hq,Hkv,ps", [("f16", 8, 8, 256), ("bf16", 16, 2, 512),
-                                           ("f16", 32, 4, 64)])
-def test_fp8_partitioned_and_reduce(dev, qdt, Hq, Hkv, ps):
+@pytest.mark.parametrize("qdt,Hq,Hkv,D,ps,bs", [("f16", 8, 8, 128, 256, 16),
+                                                ("bf16", 16, 2, 128, 512, 32),
+                                                ("f16", 32, 4, 64, 64, 64),
+                                                ("bf16", 4, 4, 64, 128, 16)])
+def test_fp8_partitioned_and_reduce(dev, qdt, Hq, Hkv, D, ps, bs):
     """FP8 pools through the fixed partitions (vector path for MHA, matrix cores for GQA) and
-    the merge, with fp16 or bf16 queries."""
+    the merge, with fp16 or bf16 queries, head_dim 64 or 128 and 16-, 32- or 64-token
+    blocks."""
     rng = np.random.default_rng(2400 + ps + Hq)
     b = W.build_batch("fp8_part", qdt, rng.integers(1, 3000, size=10), np.ones(10), Hq, Hkv,
-                      128, rng)
+                      D, rng, block_size=bs)
     check_partitioned(dev, _fp8(b), ps)
 
 
@@ -548,8 +551,10 @@ def test_fp8_chunked_prefill(dev):
     rng = np.random.default_rng(2600)
     n = np.array([300, 1, 3, 129, 1, 64, 2, 17])
     prior = np.array([0, 700, 40, 1500, 5, 2100, 33, 0])
-    for qdt, Hq, Hkv in (("f16", 8, 8), ("bf16", 16, 4), ("f16", 16, 2)):
-        b = _fp8(W.build_batch("fp8_chunk", qdt, prior + n, n, Hq, Hkv, 128, rng))
+    for qdt, Hq, Hkv, D, bs in (("f16", 8, 8, 128, 16), ("bf16", 16, 4, 128, 16),
+                                ("f16", 16, 2, 128, 32), ("bf16", 8, 2, 64, 64),
+                                ("f16", 4, 4, 64, 16)):
+        b = _fp8(W.build_batch("fp8_chunk", qdt, prior + n, n, Hq, Hkv, D, rng, block_size=bs))
         db, got, want = parity(dev, b)
         db.max_query_len = 0
         db.attend()
