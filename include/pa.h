@@ -123,6 +123,28 @@ pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_cache
 pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping,
                          int64_t num_pairs, const pa_geom* geom, void* stream);
 
+/*
+ * Block swap between the device pools and a host copy of them (preemption by swapping,
+ * "vLLM 架构源码解析 第1篇" §1.1: a preempted request's KV blocks go to CPU memory and come
+ * back to the GPU when it resumes).  direction PA_SWAP_OUT: for every pair p, device block
+ * block_mapping[2p] of k_cache / v_cache is copied bit for bit onto host block
+ * block_mapping[2p + 1] of host_k / host_v; PA_SWAP_IN: host block block_mapping[2p] onto
+ * device block block_mapping[2p + 1].  A block is all KV heads of one block id.
+ *   k_cache, v_cache  the device pools (geom->num_blocks blocks, layout above)
+ *   host_k, host_v    host memory holding host_num_blocks blocks in the same layout; allocate
+ *                     it pinned (hipHostMalloc) for the copies to run asynchronously
+ *   block_mapping     host memory, int64 [num_pairs][2]: source, destination
+ * Every id is checked against its pool before anything is queued (PA_ERR_SHAPE).  Pairs
+ * whose source and destination ids both continue the previous pair's are copied as one run.
+ * The copies are queued on stream and the caller keeps both sides alive until they finish.
+ * Destinations must be distinct (not checked).  num_pairs == 0 is a no-op.
+ */
+typedef enum { PA_SWAP_OUT = 0, PA_SWAP_IN = 1 } pa_swap_direction;
+pa_status pa_swap_blocks(void* k_cache, void* v_cache, void* host_k, void* host_v,
+                         int64_t host_num_blocks, const int64_t* block_mapping,
+                         int64_t num_pairs, int32_t direction, const pa_geom* geom,
+                         void* stream);
+
 /* Workspace bytes pa_decode needs for this geometry and row count (0 is never returned
  * for a valid geometry; returns 0 for an invalid one). */
 size_t pa_workspace_size(const pa_geom* geom, int32_t num_q_rows);

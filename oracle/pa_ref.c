@@ -187,6 +187,32 @@ int32_t pa_ref_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_ma
   return 0;
 }
 
+/* ---------------------------------------------------------------- swap to / from host */
+
+int32_t pa_ref_swap_blocks(void* dst_k, void* dst_v, int64_t dst_num_blocks, const void* src_k,
+                           const void* src_v, int64_t src_num_blocks,
+                           const int64_t* block_mapping, int64_t num_pairs,
+                           const pa_ref_geom* g) {
+  if (!geom_ok(g) || num_pairs < 0 || dst_num_blocks < 0 || src_num_blocks < 0) return -1;
+  for (int64_t p = 0; p < num_pairs; ++p) {
+    const int64_t src = block_mapping[2 * p], dst = block_mapping[2 * p + 1];
+    if (src < 0 || src >= src_num_blocks || dst < 0 || dst >= dst_num_blocks) return -1;
+  }
+  const int e = elem_bytes(g->dtype);
+  for (int64_t p = 0; p < num_pairs; ++p) {
+    const int64_t src = block_mapping[2 * p], dst = block_mapping[2 * p + 1];
+    for (int32_t h = 0; h < g->num_kv_heads; ++h)
+      for (int32_t t = 0; t < g->block_size; ++t)
+        for (int32_t d = 0; d < g->head_dim; ++d) {
+          memcpy((char*)dst_k + e * pa_ref_k_offset(g, dst, h, t, d),
+                 (const char*)src_k + e * pa_ref_k_offset(g, src, h, t, d), e);
+          memcpy((char*)dst_v + e * pa_ref_v_offset(g, dst, h, t, d),
+                 (const char*)src_v + e * pa_ref_v_offset(g, src, h, t, d), e);
+        }
+  }
+  return 0;
+}
+
 /* ---------------------------------------------------------------- row bookkeeping */
 
 typedef struct {

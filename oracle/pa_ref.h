@@ -101,6 +101,17 @@ int32_t pa_ref_reshape_and_cache(const void* key, const void* value, void* k_cac
 int32_t pa_ref_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping,
                            int64_t num_pairs, const pa_ref_geom* g);
 
+/* Block swap between two pools of the same layout ([AR1] §1.1's preemption by swapping: the
+ * blocks of a preempted request go to CPU memory and come back when it resumes).  src has
+ * src_num_blocks blocks, dst has dst_num_blocks; for every pair p, every element (kv head,
+ * token, dim) of block block_mapping[2p] of src is copied to block block_mapping[2p+1] of
+ * dst, in both pools, in pair order.  g gives everything but the block counts.  Returns 0,
+ * or -1 on bad arguments or any id outside its pool (then nothing is copied). */
+int32_t pa_ref_swap_blocks(void* dst_k, void* dst_v, int64_t dst_num_blocks, const void* src_k,
+                           const void* src_v, int64_t src_num_blocks,
+                           const int64_t* block_mapping, int64_t num_pairs,
+                           const pa_ref_geom* g);
+
 /* Paged attention ([DD] §2.2, §3.3, §6.2): for each selected query row r and query head h,
  * out[k][h][:] = softmax(scale * q . K^T) . V over the row's visible keys, gathered through
  * block_tables; lse[k][h] = max + ln(sum).  query_start_loc may be NULL (row r = seq r).

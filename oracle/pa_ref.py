@@ -54,6 +54,9 @@ def lib():
         L.pa_ref_fp8_encode.restype = ctypes.c_uint8
         L.pa_ref_fp8_encode.argtypes = [ctypes.c_float]
         L.pa_ref_copy_blocks.restype = ctypes.c_int32
+        L.pa_ref_swap_blocks.restype = ctypes.c_int32
+        L.pa_ref_swap_blocks.argtypes = [_vp, _vp, ctypes.c_int64, _vp, _vp, ctypes.c_int64,
+                                         _i64p, ctypes.c_int64, ctypes.POINTER(Geom)]
         L.pa_ref_copy_blocks.argtypes = [_vp, _vp, _i64p, ctypes.c_int64, ctypes.POINTER(Geom)]
         L.pa_ref_paged_attention.restype = ctypes.c_int32
         L.pa_ref_paged_attention.argtypes = [_f64p, _f64p, _vp, _vp, _vp, _i32p, _i32p, _i32p,
@@ -137,6 +140,20 @@ def copy_blocks(k_pool, v_pool, block_mapping, g):
                                   _ptr(m, _i64p), m.shape[0], ctypes.byref(g))
     if rc != 0:
         raise ValueError("oracle copy_blocks: bad arguments")
+
+
+def swap_blocks(dst_k, dst_v, src_k, src_v, block_mapping, g):
+    """Copies whole blocks from the src pools onto the dst pools (their own block counts, the
+    first axis): block_mapping int64 [n, 2] of (source, destination)."""
+    for a in (dst_k, dst_v, src_k, src_v):
+        assert a.flags.c_contiguous
+    m = _contig(block_mapping, np.int64).reshape(-1, 2)
+    rc = lib().pa_ref_swap_blocks(_vp(dst_k.ctypes.data), _vp(dst_v.ctypes.data),
+                                  dst_k.shape[0], _vp(src_k.ctypes.data),
+                                  _vp(src_v.ctypes.data), src_k.shape[0], _ptr(m, _i64p),
+                                  m.shape[0], ctypes.byref(g))
+    if rc != 0:
+        raise ValueError("oracle swap_blocks: bad arguments")
 
 
 def paged_attention(q, k_pool, v_pool, block_tables, context_lens, query_start_loc, scale, g,

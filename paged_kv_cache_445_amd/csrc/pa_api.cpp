@@ -307,6 +307,44 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapp
   return hip_status(pa::launch_copy_blocks(a, (hipStream_t)stream));
 }
 
+pa_status pa_swap_blocks(void* k_cache, void* v_cache, void* host_k, void* host_v,
+                         int64_t host_num_blocks, const int64_t* block_mapping,
+                         int64_t num_pairs, int32_t direction, const pa_geom* g,
+                         void* stream) {
+  const pa_status gs = check_geom(g);
+  if (gs != PA_OK) return gs;
+  if (num_pairs < 0 || host_num_blocks < 0) return PA_ERR_SHAPE;
+  if (direction != PA_SWAP_OUT && direction != PA_SWAP_IN) return PA_ERR_SHAPE;
+  if (num_pairs == 0) return PA_OK;
+  if (!k_cache || !v_cache || !host_k || !host_v || !block_mapping) return PA_ERR_NULL;
+  const bool out = direction == PA_SWAP_OUT;
+  const int64_t src_n = out ? g->num_blocks : host_num_blocks;
+  const int64_t dst_n = out ? host_num_blocks : g->num_blocks;
+  for (int64_t p = 0; p < num_pairs; ++p) {
+    const int64_t s = block_mapping[2 * p], d = block_mapping[2 * p + 1];
+    if (s < 0 || s >= src_n || d < 0 || d >= dst_n) return PA_ERR_SHAPE;
+  }
+  const size_t bb = (size_t)g->num_kv_heads * g->block_size * g->head_dim * elem_bytes(g->kv_dtype);
+  const hipMemcpyKind kind = out ? hipMemcpyDeviceToHost : hipMemcpyHostToDevice;
+  char* dk = static_cast<char*>(out ? host_k : k_cache);
+  char* dv = static_cast<char*>(out ? host_v : v_cache);
+  const char* sk = static_cast<const char*>(out ? k_cache : host_k);
+  const char* sv = static_cast<const char*>(out ? v_cache : host_v);
+  hipStream_t st = (hipStream_t)stream;
+  for (int64_t p = 0; p < num_pairs;) {
+    const int64_t s = block_mapping[2 * p], d = block_mapping[2 * p + 1];
+    int64_t n = 1;  // pairs continuing both runs
+    while (p + n < num_pairs && block_mapping[2 * (p + n)] == s + n &&
+           block_mapping[2 * (p + n) + 1] == d + n)
+      ++n;
+    hipError_t e = hipMemcpyAsync(dk + d * bb, sk + s * bb, n * bb, kind, st);
+    if (e == hipSuccess) e = hipMemcpyAsync(dv + d * bb, sv + s * bb, n * bb, kind, st);
+    if (e != hipSuccess) return PA_ERR_HIP;
+    p += n;
+  }
+  return PA_OK;
+}
+
 size_t pa_workspace_size(const pa_geom* g, int32_t num_q_rows) {
   if (check_geom(g) != PA_OK || num_q_rows < 0) return 0;
   // enough for the call with and without query_start_loc

@@ -52,6 +52,9 @@ _lib.pa_reshape_and_cache.restype = ctypes.c_int
 _lib.pa_reshape_and_cache.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_int64, _G, _vp]
 _lib.pa_copy_blocks.restype = ctypes.c_int
 _lib.pa_copy_blocks.argtypes = [_vp, _vp, _vp, ctypes.c_int64, _G, _vp]
+_lib.pa_swap_blocks.restype = ctypes.c_int
+_lib.pa_swap_blocks.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int64, _vp, ctypes.c_int64,
+                                ctypes.c_int32, _G, _vp]
 _lib.pa_decode.restype = ctypes.c_int
 _lib.pa_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_int32,
                            ctypes.c_float, _vp, ctypes.c_size_t, _G, _vp]
@@ -122,6 +125,26 @@ def copy_blocks(k_cache, v_cache, block_mapping, g: Geom, stream=None):
     _check("pa_copy_blocks",
            _lib.pa_copy_blocks(_p(k_cache), _p(v_cache), _p(block_mapping),
                                int(block_mapping.shape[0]) if block_mapping.numel() else 0,
+                               ctypes.byref(g), _stream(stream)))
+
+
+SWAP_OUT, SWAP_IN = 0, 1
+
+
+def swap_blocks(k_cache, v_cache, host_k, host_v, block_mapping, direction, g: Geom,
+                stream=None):
+    """Copies whole blocks between the device pools and host pools of the same layout
+    (host_k / host_v: CPU tensors, pinned for asynchronous copies).  block_mapping: a CPU
+    int64 tensor [num_pairs, 2] of (source, destination) ids; direction SWAP_OUT (device to
+    host) or SWAP_IN (host to device)."""
+    if block_mapping.device.type != "cpu" or host_k.device.type != "cpu" or \
+            host_v.device.type != "cpu":
+        raise ValueError("swap_blocks: block_mapping and the host pools live in host memory")
+    m = block_mapping.contiguous()
+    _check("pa_swap_blocks",
+           _lib.pa_swap_blocks(_p(k_cache), _p(v_cache), _p(host_k), _p(host_v),
+                               int(host_k.shape[0]), _p(m),
+                               int(m.shape[0]) if m.numel() else 0, int(direction),
                                ctypes.byref(g), _stream(stream)))
 
 

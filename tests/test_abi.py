@@ -28,7 +28,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for fn in ("pa_reshape_and_cache", "pa_decode", "pa_decode_partitioned", "pa_decode_reduce",
-               "pa_copy_blocks",
+               "pa_copy_blocks", "pa_swap_blocks",
                "pa_workspace_size", "pa_kv_cache_bytes", "pa_status_str"):
         assert fn in names
 
@@ -151,6 +151,20 @@ def test_host_checks_return_codes_without_launching(lib):
     assert lib.pa_copy_blocks(dummy, dummy, dummy, -1, ctypes.byref(g), None) == -2
     assert lib.pa_copy_blocks(None, None, None, 0, ctypes.byref(g), None) == 0
     assert lib.pa_copy_blocks(dummy, dummy, dummy, 2, ctypes.byref(_g(head_dim=80)), None) == -3
+
+    # swap: every id is checked on the host before anything is queued
+    lib.pa_swap_blocks.restype = ctypes.c_int
+    lib.pa_swap_blocks.argtypes = [vp] * 4 + [ctypes.c_int64, vp, ctypes.c_int64, ctypes.c_int32,
+                                              ctypes.POINTER(Geom), vp]
+    pairs = (ctypes.c_int64 * 4)(1, 2, 63, 5)   # geometry: 64 device blocks
+    assert lib.pa_swap_blocks(dummy, dummy, dummy, dummy, 5, pairs, 2, 0, ctypes.byref(g), None) == -2
+    bad = (ctypes.c_int64 * 4)(1, 2, 64, 0)
+    assert lib.pa_swap_blocks(dummy, dummy, dummy, dummy, 6, bad, 2, 0, ctypes.byref(g), None) == -2
+    back = (ctypes.c_int64 * 2)(6, 1)            # host block 6 of 6
+    assert lib.pa_swap_blocks(dummy, dummy, dummy, dummy, 6, back, 1, 1, ctypes.byref(g), None) == -2
+    assert lib.pa_swap_blocks(dummy, dummy, dummy, dummy, 6, pairs, 2, 2, ctypes.byref(g), None) == -2
+    assert lib.pa_swap_blocks(dummy, dummy, None, dummy, 6, pairs, 2, 0, ctypes.byref(g), None) == -1
+    assert lib.pa_swap_blocks(None, None, None, None, 0, None, 0, 0, ctypes.byref(g), None) == 0
 
 
 BM_HEADER = os.path.join(ROOT, "include", "pa_block_manager.h")

@@ -490,6 +490,48 @@ def test_copy_blocks_matches_block_axis_assignment(dtype, D, Hkv):
     assert np.array_equal(vp.view(np.uint8), wv.view(np.uint8))
 
 
+@pytest.mark.parametrize("dtype,D,Hkv,bs", [("f16", 128, 2, 16), ("fp8", 64, 3, 32),
+                                           ("f32", 64, 1, 64)])
+def test_swap_blocks_pins(dtype, D, Hkv, bs):
+    """Swap out and in ("vLLM 架构源码解析 第1篇" §1.1's preemption by swapping) against numpy
+    assignment along the block axis of two pools with their own block counts, and against
+    the C copy_blocks: out to host then in to other device blocks is a device block copy.
+    An id outside its pool is an error that copies nothing."""
+    rng = np.random.default_rng(29)
+    NB, NH = 10, 6
+    X = 16 // W.ELEM_BYTES[dtype]
+    R = bs // 16
+    g = oracle.make_geom(1, Hkv, Hkv, D, NB, 1, dtype, bs,
+                         q_dtype="f16" if dtype == "fp8" else None)
+    kshape, vshape = (Hkv, D // X, 16, X), (Hkv, D, 16)
+
+    def pool(n, shape):
+        bits = rng.integers(0, 256, size=(n, R) + shape + (W.ELEM_BYTES[dtype],),
+                            dtype=np.uint8)
+        return bits.reshape(n, R, *shape[:-1], shape[-1] * W.ELEM_BYTES[dtype])
+
+    dk, dv = pool(NB, kshape), pool(NB, vshape)
+    hk, hv = pool(NH, kshape), pool(NH, vshape)
+    out_pairs = np.array([[2, 0], [3, 1], [4, 2], [9, 5]], dtype=np.int64)
+    wk, wv = hk.copy(), hv.copy()
+    for s_, d_ in out_pairs:
+        wk[d_], wv[d_] = dk[s_], dv[s_]
+    oracle.swap_blocks(hk, hv, dk, dv, out_pairs, g)
+    assert np.array_equal(hk, wk) and np.array_equal(hv, wv)
+    # back in to blocks 6, 7, 8, 0: the same as copying device blocks 2, 3, 4, 9 there
+    in_pairs = np.array([[0, 6], [1, 7], [2, 8], [5, 0]], dtype=np.int64)
+    ck, cv = dk.copy(), dv.copy()
+    oracle.copy_blocks(ck, cv, np.array([[2, 6], [3, 7], [4, 8], [9, 0]]), g)
+    oracle.swap_blocks(dk, dv, hk, hv, in_pairs, g)
+    assert np.array_equal(dk, ck) and np.array_equal(dv, cv)
+    before = hk.copy()
+    with pytest.raises(ValueError):
+        oracle.swap_blocks(hk, hv, dk, dv, np.array([[1, 1], [NB, 0]]), g)
+    with pytest.raises(ValueError):
+        oracle.swap_blocks(hk, hv, dk, dv, np.array([[1, NH]]), g)
+    assert np.array_equal(hk, before)
+
+
 def test_copy_on_write_fork_keeps_attention_bitwise():
     """A sequence forked onto copies of its blocks ("vLLM 架构源码解析 第1篇" §4.3.2) attends
     exactly as the original: same keys, same order, same bits."""
