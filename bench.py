@@ -71,6 +71,8 @@ DESCRIPTIONS = {
                        "ctx U[256,2048]",
     "mixed_chunked_fp8": "mixed step with FP8 E4M3 KV (per-pool scales 6.5/448): 8 x 512-row "
                          "causal chunks + 120 decode rows, 32 q / 8 kv heads, head_dim 128, bf16 q",
+    "swap_f16": "block swap: 256 scattered LLaMA-7B blocks (128 KiB per pool) out to a pinned "
+                "host pool and 256 back in onto scattered device blocks, per step",
     "cow_copy_f16": "copy-on-write block copies: 256 (source, destination) pairs of LLaMA-7B "
                     "blocks (32 kv heads x 128 x 16 tokens fp16, 128 KiB per pool) in an "
                     "8192-block pool",
@@ -238,6 +240,76 @@ def bench_copy(args):
     print(json.dumps(line), flush=True)
 
 
+PCIE_PEAK_GBS = 64.0  # PCIe 5.0 x16, one direction (32 GT/s x 16 lanes, 128b/130b)
+
+
+def bench_swap(args):
+    """pa_swap_blocks alone: one step swaps SWAP_PAIRS LLaMA-7B blocks (scattered device ids)
+    out to a pinned host pool and another SWAP_PAIRS back in onto scattered free device
+    blocks; value is the bytes that cross PCIe per second (both pools, both directions)."""
+    import numpy as np
+    import torch
+    from paged_kv_cache_445_amd import pa
+    dev = torch.device("cuda:0")
+    NB, NH, Hkv, D, pairs = 8192, 1024, 32, 128, 256
+    rng = np.random.default_rng(4458)
+    g = pa.geom(1, Hkv, Hkv, D, NB, 1, torch.float16)
+    shape_k, shape_v = (Hkv, D // 8, 16, 8), (Hkv, D, 16)
+    kc = torch.randn((NB,) + shape_k, device=dev, dtype=torch.float16)
+    vc = torch.randn((NB,) + shape_v, device=dev, dtype=torch.float16)
+    hk = torch.empty((NH,) + shape_k, dtype=torch.float16, pin_memory=True)
+    hv = torch.empty((NH,) + shape_v, dtype=torch.float16, pin_memory=True)
+    hk.normal_()
+    hv.normal_()
+    maps = []
+    for i in range(4):
+        dsrc = rng.choice(NB // 2, size=pairs, replace=False)  # out: scattered device blocks
+        hdst = (i % 2) * (NH // 2) + np.arange(pairs)          # ... to a run of host blocks
+        hsrc = ((i + 1) % 2) * (NH // 2) + rng.permutation(pairs)  # in: the other host half
+        ddst = NB // 2 + rng.choice(NB // 2, size=pairs, replace=False)
+        maps.append((torch.from_numpy(np.stack([dsrc, hdst], 1).astype(np.int64)),
+                     torch.from_numpy(np.stack([hsrc, ddst], 1).astype(np.int64))))
+    block_bytes = Hkv * 16 * D * 2
+    moved = 2 * pairs * 2 * block_bytes  # out and in, K and V
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        mo, mi = maps[i % len(maps)]
+        pa.swap_blocks(kc, vc, hk, hv, mo, pa.SWAP_OUT, g)
+        pa.swap_blocks(kc, vc, hk, hv, mi, pa.SWAP_IN, g)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    call_ms = ev[0].elapsed_time(ev[1]) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+    achieved = moved / (call_ms * 1e-3) / 1e9
+    line = {
+        "metric": "KV block swap to and from host memory: PCIe GB/s (both directions)",
+        "value": round(moved / (ms_per_step * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "swap_f16", "description": DESCRIPTIONS["swap_f16"],
+                   "pairs_each_way": pairs, "bytes_per_step": moved},
+        "pa_swap_blocks_us": round(call_ms * 1e3, 3),
+        "roofline": {"bound": "pcie", "kernel": "pa_swap_blocks (copy engine, one copy per pool "
+                     "per run of consecutive ids)", "achieved": round(achieved, 2),
+                     "peak": PCIE_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PCIE_PEAK_GBS, 4), "traffic": None},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -276,6 +348,8 @@ def main():
     torch.cuda.set_device(dev)
     if args.workload == "cow_copy_f16":
         return bench_copy(args)
+    if args.workload == "swap_f16":
+        return bench_swap(args)
 
     print(f"[bench] building workload {args.workload}", file=sys.stderr, flush=True)
     b = W.make(args.workload)
