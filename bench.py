@@ -301,8 +301,8 @@ def bench_swap(args):
         "config": {"workload": "swap_f16", "description": DESCRIPTIONS["swap_f16"],
                    "pairs_each_way": pairs, "bytes_per_step": moved},
         "pa_swap_blocks_us": round(call_ms * 1e3, 3),
-        "roofline": {"bound": "pcie", "kernel": "pa_swap_blocks (copy engine, one copy per pool "
-                     "per run of consecutive ids)", "achieved": round(achieved, 2),
+        "roofline": {"bound": "pcie", "kernel": "pa_swap_blocks (one kernel per 224 pairs over "
+                     "device-mapped pinned host memory)", "achieved": round(achieved, 2),
                      "peak": PCIE_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / PCIE_PEAK_GBS, 4), "traffic": None},
         "cpu_baseline": None,

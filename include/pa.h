@@ -131,11 +131,13 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapp
  * block_mapping[2p + 1] of host_k / host_v; PA_SWAP_IN: host block block_mapping[2p] onto
  * device block block_mapping[2p + 1].  A block is all KV heads of one block id.
  *   k_cache, v_cache  the device pools (geom->num_blocks blocks, layout above)
- *   host_k, host_v    host memory holding host_num_blocks blocks in the same layout; allocate
- *                     it pinned (hipHostMalloc) for the copies to run asynchronously
+ *   host_k, host_v    host memory holding host_num_blocks blocks in the same layout.  Pinned
+ *                     memory (hipHostMalloc) is read or written by one kernel over PCIe for
+ *                     all pairs; other host memory goes through one copy per run
  *   block_mapping     host memory, int64 [num_pairs][2]: source, destination
- * Every id is checked against its pool before anything is queued (PA_ERR_SHAPE).  Pairs
- * whose source and destination ids both continue the previous pair's are copied as one run.
+ * Every id is checked against its pool before anything is queued (PA_ERR_SHAPE).  Without a
+ * device mapping, pairs whose source and destination ids both continue the previous pair's
+ * are copied as one run.
  * The copies are queued on stream and the caller keeps both sides alive until they finish.
  * Destinations must be distinct (not checked).  num_pairs == 0 is a no-op.
  */

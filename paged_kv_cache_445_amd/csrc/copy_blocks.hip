@@ -48,6 +48,41 @@ __global__ __launch_bounds__(kWG) void copy_blocks_kernel(CopyBlocksArgs a) {
   }
 }
 
+// Swap ("vLLM 架构源码解析 第1篇" §1.1, preemption by swapping): the same pieces between a
+// device pool and a pinned host pool mapped into the device's address space, so that one
+// launch moves every pair over PCIe instead of one copy-engine transfer per block.
+__global__ __launch_bounds__(kWG) void swap_blocks_kernel(SwapArgs a) {
+  typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+  const int64_t pieces = (a.block_bytes + kCopyPiece - 1) / kCopyPiece;
+  const int64_t w = blockIdx.x;
+  const int64_t pair = w / (2 * pieces);
+  const int pool = (int)(w / pieces) & 1;
+  const int64_t piece = w % pieces;
+  if (pair >= a.num_pairs) return;
+  const char* s = (pool ? a.src_v : a.src_k) + a.pairs[pair][0] * a.block_bytes;
+  char* d = (pool ? a.dst_v : a.dst_k) + a.pairs[pair][1] * a.block_bytes;
+  const int64_t off0 = piece * kCopyPiece + (int64_t)threadIdx.x * 16;
+  u32x4 v[kCopyLoads];
+#pragma unroll
+  for (int k = 0; k < kCopyLoads; ++k) {
+    const int64_t off = off0 + (int64_t)k * kWG * 16;
+    if (off < a.block_bytes) v[k] = *reinterpret_cast<const u32x4*>(s + off);
+  }
+#pragma unroll
+  for (int k = 0; k < kCopyLoads; ++k) {
+    const int64_t off = off0 + (int64_t)k * kWG * 16;
+    if (off < a.block_bytes) __builtin_nontemporal_store(v[k], reinterpret_cast<u32x4*>(d + off));
+  }
+}
+
+hipError_t launch_swap_blocks(const SwapArgs& a, hipStream_t st) {
+  const int64_t pieces = (a.block_bytes + kCopyPiece - 1) / kCopyPiece;
+  const int64_t grid = (int64_t)a.num_pairs * 2 * pieces;
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL(swap_blocks_kernel, dim3((unsigned)grid), dim3(kWG), 0, st, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t st) {
   const int64_t pieces = (a.block_bytes + kCopyPiece - 1) / kCopyPiece;
   const int64_t grid = a.num_pairs * 2 * pieces;

@@ -4,6 +4,7 @@
 #include <stdlib.h>
 
 #include <atomic>
+#include <algorithm>
 #include <cmath>
 #include <mutex>
 
@@ -325,12 +326,39 @@ pa_status pa_swap_blocks(void* k_cache, void* v_cache, void* host_k, void* host_
     if (s < 0 || s >= src_n || d < 0 || d >= dst_n) return PA_ERR_SHAPE;
   }
   const size_t bb = (size_t)g->num_kv_heads * g->block_size * g->head_dim * elem_bytes(g->kv_dtype);
+  hipStream_t st = (hipStream_t)stream;
+
+  // pinned host pools are mapped into the device's address space: one kernel per
+  // kSwapPairs pairs moves every block over PCIe
+  void* hk_dev = nullptr;
+  void* hv_dev = nullptr;
+  if (hipHostGetDevicePointer(&hk_dev, host_k, 0) == hipSuccess &&
+      hipHostGetDevicePointer(&hv_dev, host_v, 0) == hipSuccess && hk_dev && hv_dev) {
+    pa::SwapArgs a{};
+    a.src_k = static_cast<const char*>(out ? k_cache : hk_dev);
+    a.src_v = static_cast<const char*>(out ? v_cache : hv_dev);
+    a.dst_k = static_cast<char*>(out ? hk_dev : k_cache);
+    a.dst_v = static_cast<char*>(out ? hv_dev : v_cache);
+    a.block_bytes = (int64_t)bb;
+    for (int64_t p0 = 0; p0 < num_pairs; p0 += pa::kSwapPairs) {
+      const int64_t n = std::min<int64_t>(pa::kSwapPairs, num_pairs - p0);
+      a.num_pairs = (int32_t)n;
+      for (int64_t i = 0; i < n; ++i) {
+        a.pairs[i][0] = block_mapping[2 * (p0 + i)];
+        a.pairs[i][1] = block_mapping[2 * (p0 + i) + 1];
+      }
+      if (pa::launch_swap_blocks(a, st) != hipSuccess) return PA_ERR_HIP;
+    }
+    return PA_OK;
+  }
+  (void)hipGetLastError();  // the failed lookup (pageable host memory) is not an error here
+
+  // pageable host pools: one copy-engine transfer per run of consecutive ids
   const hipMemcpyKind kind = out ? hipMemcpyDeviceToHost : hipMemcpyHostToDevice;
   char* dk = static_cast<char*>(out ? host_k : k_cache);
   char* dv = static_cast<char*>(out ? host_v : v_cache);
   const char* sk = static_cast<const char*>(out ? k_cache : host_k);
   const char* sv = static_cast<const char*>(out ? v_cache : host_v);
-  hipStream_t st = (hipStream_t)stream;
   for (int64_t p = 0; p < num_pairs;) {
     const int64_t s = block_mapping[2 * p], d = block_mapping[2 * p + 1];
     int64_t n = 1;  // pairs continuing both runs

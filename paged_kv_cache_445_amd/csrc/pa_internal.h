@@ -81,6 +81,20 @@ struct CopyBlocksArgs {
   int64_t num_blocks;
 };
 
+// Block swap between device pools and device-mapped pinned host pools: one launch takes up
+// to kSwapPairs pairs, carried in the kernel arguments (the host mapping need not be
+// device-visible).
+constexpr int kSwapPairs = 224;
+struct SwapArgs {
+  const char* src_k;
+  const char* src_v;
+  char* dst_k;
+  char* dst_v;
+  int64_t block_bytes;  // one block of one pool
+  int32_t num_pairs;    // <= kSwapPairs
+  int64_t pairs[kSwapPairs][2];  // source, destination (checked by the host)
+};
+
 struct PartReduceArgs {
   void* out;
   const float* tmp_out;
@@ -102,6 +116,7 @@ hipError_t launch_mfma_decode(int dt, int mode, const DecodeArgs& a, int grid, h
 int mfma_decode_max_blocks_per_cu(int dt, int head_dim, int mode, int lds_bytes);
 hipError_t launch_part_reduce(int dt, const PartReduceArgs& a, hipStream_t st);
 hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t st);
+hipError_t launch_swap_blocks(const SwapArgs& a, hipStream_t st);
 
 // resident workgroups per CU at most (32 waves of 64 lanes): bounds the even split's grid
 constexpr int kMaxWgPerCu = 8;

@@ -369,12 +369,15 @@ def test_copy_blocks_bitwise(dev, dtype, Hkv, D, npairs):
         assert np.array_equal(c.view(np.uint8), want.view(np.uint8))
 
 
-@pytest.mark.parametrize("dtype,bs,fp8", [("f16", 16, False), ("bf16", 32, False),
-                                          ("f16", 16, True)])
-def test_swap_blocks_out_and_in(dev, dtype, bs, fp8):
-    """pa_swap_blocks: the blocks of half the sequences go out to pinned host pools (with a
-    run of consecutive ids and single pairs) and come back onto free device blocks, bit for
-    bit as the oracle's swap; attention over the remapped tables then matches the oracle."""
+@pytest.mark.parametrize("dtype,bs,fp8,pinned", [("f16", 16, False, True),
+                                                 ("bf16", 32, False, True),
+                                                 ("f16", 16, True, True),
+                                                 ("bf16", 16, False, False)])
+def test_swap_blocks_out_and_in(dev, dtype, bs, fp8, pinned):
+    """pa_swap_blocks: the blocks of half the sequences go out to host pools (pinned: the
+    swap kernel over mapped memory; pageable: copies per run, with a run of consecutive ids
+    and single pairs) and come back onto free device blocks, bit for bit as the oracle's
+    swap; attention over the remapped tables then matches the oracle."""
     import torch
     import oracle
     from paged_kv_cache_445_amd import pa
@@ -383,7 +386,7 @@ def test_swap_blocks_out_and_in(dev, dtype, bs, fp8):
                       block_size=bs)
     if fp8:
         _fp8(b)
-    _log(f"[swap_blocks] {b.pool_dtype} block {bs}")
+    _log(f"[swap_blocks] {b.pool_dtype} block {bs} pinned {pinned}")
     db = run_gpu(dev, b)
     g = H.geom(b)
     dk, dv = (x.view(np.uint8) for x in db.pools_host())
@@ -396,8 +399,10 @@ def test_swap_blocks_out_and_in(dev, dtype, bs, fp8):
     hk0 = rng.integers(0, 256, size=(NH,) + dk.shape[1:], dtype=np.uint8)
     hv0 = rng.integers(0, 256, size=(NH,) + dv.shape[1:], dtype=np.uint8)
     tdt = db.k_cache.dtype
-    hk = torch.from_numpy(hk0).view(tdt).pin_memory()
-    hv = torch.from_numpy(hv0).view(tdt).pin_memory()
+    hk = torch.from_numpy(hk0.copy()).view(tdt)
+    hv = torch.from_numpy(hv0.copy()).view(tdt)
+    if pinned:
+        hk, hv = hk.pin_memory(), hv.pin_memory()
     pa.swap_blocks(db.k_cache, db.v_cache, hk, hv, torch.from_numpy(out_pairs), pa.SWAP_OUT,
                    db.geom)
     torch.cuda.synchronize()
