@@ -434,6 +434,42 @@ def test_swap_blocks_out_and_in(dev, dtype, bs, fp8, pinned):
     check_out(db.out_host(), want, TOL[b.dtype], "after swap in")
 
 
+@pytest.mark.parametrize("pinned", [True, False])
+def test_swap_blocks_many_pairs(dev, pinned):
+    """500 pairs each way (several kernel launches of at most 224 pairs on the pinned path),
+    random bit patterns, against the oracle's swap over every byte of both pools."""
+    import torch
+    import oracle
+    from paged_kv_cache_445_amd import pa
+    from paged_kv_cache_445_amd.device_batch import TORCH_DTYPE, to_device
+    rng = np.random.default_rng(2800 + pinned)
+    NB, NH, Hkv, D, n = 1200, 700, 1, 64, 500
+    kp = _bits_pool((NB, Hkv, D // 8, 16, 8), "f16", rng)
+    vp = _bits_pool((NB, Hkv, D, 16), "f16", rng)
+    hk0 = _bits_pool((NH, Hkv, D // 8, 16, 8), "f16", rng)
+    hv0 = _bits_pool((NH, Hkv, D, 16), "f16", rng)
+    k_dev, v_dev = to_device(kp, "f16", "cuda"), to_device(vp, "f16", "cuda")
+    hk, hv = torch.from_numpy(hk0.copy()), torch.from_numpy(hv0.copy())
+    if pinned:
+        hk, hv = hk.pin_memory(), hv.pin_memory()
+    g = pa.geom(1, Hkv, Hkv, D, NB, 1, TORCH_DTYPE["f16"])
+    og = oracle.make_geom(1, Hkv, Hkv, D, NB, 1, "f16")
+    out_pairs = np.stack([rng.choice(NB, size=n, replace=False),
+                          rng.choice(NH, size=n, replace=False)], 1).astype(np.int64)
+    in_pairs = np.stack([rng.choice(NH, size=n, replace=False),
+                         rng.choice(NB, size=n, replace=False)], 1).astype(np.int64)
+    pa.swap_blocks(k_dev, v_dev, hk, hv, torch.from_numpy(out_pairs), pa.SWAP_OUT, g)
+    torch.cuda.synchronize()
+    oracle.swap_blocks(hk0, hv0, kp, vp, out_pairs, og)
+    assert np.array_equal(hk.numpy().view(np.uint8), hk0.view(np.uint8))
+    assert np.array_equal(hv.numpy().view(np.uint8), hv0.view(np.uint8))
+    pa.swap_blocks(k_dev, v_dev, hk, hv, torch.from_numpy(in_pairs), pa.SWAP_IN, g)
+    torch.cuda.synchronize()
+    oracle.swap_blocks(kp, vp, hk0, hv0, in_pairs, og)
+    assert np.array_equal(k_dev.cpu().numpy().view(np.uint8), kp.view(np.uint8))
+    assert np.array_equal(v_dev.cpu().numpy().view(np.uint8), vp.view(np.uint8))
+
+
 # ----------------------------------------------------------------- speculative verify rows
 
 @pytest.mark.parametrize("name", ["spec_verify_f16", "spec_verify_gqa_bf16"])
