@@ -37,11 +37,11 @@
  *
  * FP8 pools ("vLLM 深度拆解" §10.1 names FP8 KV with calibrated scales).  kv_dtype
  * PA_FP8_E4M3: one byte per element in the layout above with elem = 1, X = 16; q, key and
- * value are fp16 or bf16 (q_dtype PA_F16 or PA_BF16), out is q_dtype or fp32.  Each pool has one scale:
- * reshape_and_cache stores e4m3(fp32(x) / scale), the fp32 quotient rounded to the nearest
+ * value are fp16 or bf16 (q_dtype PA_F16 or PA_BF16), out is q_dtype or fp32.  Each pool
+ * has one scale: reshape_and_cache stores e4m3(fp32(x) / scale), the fp32 quotient rounded to the nearest
  * E4M3 ("E4M3FN": bias 7, no infinity, largest 448) with ties to even, magnitudes from 448
  * up saturating to 448; attention reads an element as its E4M3 value times the scale.
- * Supported by every entry point; out is q_dtype or fp32.
+ * Every entry point takes FP8 pools.
  *
  * Rows and positions.  query_start_loc ("vLLM 架构源码解析 第1篇" §3.3.2) is NULL when every sequence has one
  * query row (row r belongs to sequence r, num_q_rows == num_seqs), else an int32 [S + 1]
