@@ -32,6 +32,11 @@
  *     Appending into a partly filled last block that another sequence still references first
  *     moves the appending sequence onto a fresh block and records the pair (shared block,
  *     fresh block) for pa_copy_blocks, which must run before the new tokens are written.
+ *   - Preemption by swapping ("vLLM 架构源码解析 第1篇" §1.1): a sequence's blocks can move to
+ *     a pool of host blocks (their own LIFO free list) and back; each move returns the
+ *     (source, destination) pairs for pa_swap_blocks.  While swapped out, a sequence keeps
+ *     its length and tokens but holds no device block, and only pa_bm_swap_in,
+ *     pa_bm_free_sequence and pa_bm_seq_len accept it.
  *
  * Errors: every call checks its arguments and returns a pa_status; a call that fails
  * changes nothing.  The manager is not thread-safe: one caller at a time.
@@ -96,8 +101,33 @@ pa_status pa_bm_slots(const pa_block_manager* bm, int32_t seq, int32_t first, in
                       int64_t* slots_out);
 
 /* Release a sequence: one reference of each of its blocks is dropped (last block first);
- * blocks that reach zero return to the free list and leave the prefix cache. */
+ * blocks that reach zero return to the free list and leave the prefix cache.  A swapped-out
+ * sequence returns its host blocks to the host free list. */
 pa_status pa_bm_free_sequence(pa_block_manager* bm, int32_t seq);
+
+/* Size the host block pool [0, num_host_blocks) for swapped-out sequences (0 at creation);
+ * PA_ERR_SHAPE while any sequence is swapped out. */
+pa_status pa_bm_set_host_blocks(pa_block_manager* bm, int32_t num_host_blocks);
+/* Free host blocks, or -1 on NULL. */
+int32_t pa_bm_num_free_host_blocks(const pa_block_manager* bm);
+/* Swap a sequence out: each of its device blocks, in logical order, gets a host block (taken
+ * from the host free list) and the pair (device block, host block) is written to pairs_out
+ * (int64 [max_pairs][2], pa_swap_blocks's PA_SWAP_OUT mapping); then one reference of each
+ * device block is dropped as by pa_bm_free_sequence (blocks still shared stay for the other
+ * sequences).  *num_pairs = the sequence's block count.  The copies must run before anything
+ * else is written into the released blocks, and queued copy-on-write pairs that involve the
+ * sequence before the swap.  PA_ERR_NO_BLOCKS if the host pool has too few free blocks,
+ * PA_ERR_SHAPE if the sequence is unknown or swapped out or max_pairs is too small. */
+pa_status pa_bm_swap_out(pa_block_manager* bm, int32_t seq, int64_t* pairs_out,
+                         int64_t max_pairs, int64_t* num_pairs);
+/* Swap a sequence back in: each host block, in logical order, gets a fresh device block and
+ * the pair (host block, device block) is written to pairs_out (pa_swap_blocks's PA_SWAP_IN
+ * mapping); the host blocks return to the host free list.  The sequence's table holds the
+ * new blocks (none shared, none in the prefix cache).  PA_ERR_NO_BLOCKS if the device pool
+ * has too few free blocks, PA_ERR_SHAPE if the sequence is not swapped out or max_pairs is
+ * too small. */
+pa_status pa_bm_swap_in(pa_block_manager* bm, int32_t seq, int64_t* pairs_out,
+                        int64_t max_pairs, int64_t* num_pairs);
 
 /* Number of queued copy pairs. */
 int64_t pa_bm_num_pending_copies(const pa_block_manager* bm);

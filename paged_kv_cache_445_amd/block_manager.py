@@ -40,6 +40,13 @@ _L.pa_bm_num_pending_copies.restype = ctypes.c_int64
 _L.pa_bm_num_pending_copies.argtypes = [_vp]
 _L.pa_bm_take_copies.restype = ctypes.c_int64
 _L.pa_bm_take_copies.argtypes = [_vp, _i64p, ctypes.c_int64]
+_L.pa_bm_set_host_blocks.restype = ctypes.c_int
+_L.pa_bm_set_host_blocks.argtypes = [_vp, _i32]
+_L.pa_bm_num_free_host_blocks.restype = ctypes.c_int32
+_L.pa_bm_num_free_host_blocks.argtypes = [_vp]
+for _fn in (_L.pa_bm_swap_out, _L.pa_bm_swap_in):
+    _fn.restype = ctypes.c_int
+    _fn.argtypes = [_vp, _i32, _i64p, ctypes.c_int64, _i64p]
 _L.pa_bm_block_tables.restype = ctypes.c_int
 _L.pa_bm_block_tables.argtypes = [_vp, _i32p, _i32, _i32, _i32p, _i32p]
 
@@ -120,6 +127,29 @@ class BlockManager:
 
     def free_sequence(self, seq: int):
         _check("pa_bm_free_sequence", _L.pa_bm_free_sequence(self._h, int(seq)))
+
+    # ------------------------------------------------------------------ swapping
+    def set_host_blocks(self, num_host_blocks: int):
+        _check("pa_bm_set_host_blocks", _L.pa_bm_set_host_blocks(self._h, int(num_host_blocks)))
+
+    def num_free_host_blocks(self) -> int:
+        return int(_L.pa_bm_num_free_host_blocks(self._h))
+
+    def swap_out(self, seq: int) -> np.ndarray:
+        """Move `seq` to host blocks; returns (device block, host block) pairs, int64 [n, 2],
+        for pa_swap_blocks(..., SWAP_OUT)."""
+        out, n = np.empty((self.max_blocks_per_seq, 2), dtype=np.int64), ctypes.c_int64()
+        _check("pa_bm_swap_out", _L.pa_bm_swap_out(self._h, int(seq), out.ctypes.data_as(_i64p),
+                                                   out.shape[0], ctypes.byref(n)))
+        return out[:n.value].copy()
+
+    def swap_in(self, seq: int) -> np.ndarray:
+        """Bring `seq` back onto fresh device blocks; returns (host block, device block)
+        pairs, int64 [n, 2], for pa_swap_blocks(..., SWAP_IN)."""
+        out, n = np.empty((self.max_blocks_per_seq, 2), dtype=np.int64), ctypes.c_int64()
+        _check("pa_bm_swap_in", _L.pa_bm_swap_in(self._h, int(seq), out.ctypes.data_as(_i64p),
+                                                 out.shape[0], ctypes.byref(n)))
+        return out[:n.value].copy()
 
     # ------------------------------------------------------------------ outputs
     def take_copies(self) -> np.ndarray:

@@ -29,10 +29,12 @@ struct KeyHash {
 
 struct Seq {
   bool live = false;
+  bool swapped = false;           // its blocks are in host memory (host), not on the device
   bool track = true;              // every token so far came with an id: full blocks may be cached
   int32_t len = 0;
   std::vector<int32_t> blocks;    // logical block j -> physical block
   std::vector<int32_t> tail;      // token ids of the partly filled last block (when tracked)
+  std::vector<int32_t> host;      // while swapped: logical block j -> host block
 };
 
 }  // namespace
@@ -46,6 +48,8 @@ struct pa_block_manager {
   std::unordered_map<std::vector<int32_t>, int32_t, KeyHash> cache;  // key -> block
   std::vector<std::vector<int32_t>> key_of;  // block -> its key in the cache (empty: none)
   std::vector<int64_t> copies;     // queued (source, destination) pairs, flattened
+  int32_t num_host = 0;            // host blocks for swapped-out sequences
+  std::vector<int32_t> host_free;  // free host blocks, taken from and returned to the back
   size_t copies_head = 0;          // pairs before this index have been taken
 
   int32_t take_block() {
@@ -86,10 +90,21 @@ struct pa_block_manager {
     }
   }
 
+  // a sequence whose blocks are on the device (what every call but the swap, free and length
+  // queries works on)
   Seq* seq(int32_t id) {
-    return id >= 0 && id < (int32_t)seqs.size() && seqs[id].live ? &seqs[id] : nullptr;
+    Seq* s = any_seq(id);
+    return s && !s->swapped ? s : nullptr;
   }
   const Seq* seq(int32_t id) const {
+    const Seq* s = any_seq(id);
+    return s && !s->swapped ? s : nullptr;
+  }
+  // a live sequence, on the device or swapped out
+  Seq* any_seq(int32_t id) {
+    return id >= 0 && id < (int32_t)seqs.size() && seqs[id].live ? &seqs[id] : nullptr;
+  }
+  const Seq* any_seq(int32_t id) const {
     return id >= 0 && id < (int32_t)seqs.size() && seqs[id].live ? &seqs[id] : nullptr;
   }
 
@@ -137,7 +152,7 @@ int32_t pa_bm_ref_count(const pa_block_manager* bm, int32_t block) {
 }
 
 int32_t pa_bm_seq_len(const pa_block_manager* bm, int32_t seq) {
-  const Seq* s = bm ? bm->seq(seq) : nullptr;
+  const Seq* s = bm ? bm->any_seq(seq) : nullptr;
   return s ? s->len : -1;
 }
 
@@ -277,17 +292,95 @@ pa_status pa_bm_slots(const pa_block_manager* bm, int32_t seq, int32_t first, in
 
 pa_status pa_bm_free_sequence(pa_block_manager* bm, int32_t seq) {
   if (!bm) return PA_ERR_NULL;
-  Seq* s = bm->seq(seq);
+  Seq* s = bm->any_seq(seq);
   if (!s) return PA_ERR_SHAPE;
   try {
     bm->free_ids.reserve(bm->free_ids.size() + 1);
   } catch (const std::bad_alloc&) {
     return PA_ERR_NO_BLOCKS;
   }
+  // host blocks go back in reverse (capacity for all of them was reserved at creation)
+  for (size_t j = s->host.size(); j-- > 0;) bm->host_free.push_back(s->host[j]);
   // last block first: a block is never freed before the blocks that follow it in a table
   for (size_t j = s->blocks.size(); j-- > 0;) bm->drop_ref(s->blocks[j]);
   *s = Seq();
   bm->free_ids.push_back(seq);
+  return PA_OK;
+}
+
+pa_status pa_bm_set_host_blocks(pa_block_manager* bm, int32_t num_host_blocks) {
+  if (!bm) return PA_ERR_NULL;
+  if (num_host_blocks < 0) return PA_ERR_SHAPE;
+  for (const Seq& s : bm->seqs)
+    if (s.live && s.swapped) return PA_ERR_SHAPE;  // host blocks in use
+  try {
+    std::vector<int32_t> f((size_t)num_host_blocks);
+    for (int32_t i = 0; i < num_host_blocks; ++i) f[i] = i;
+    bm->host_free = std::move(f);
+  } catch (const std::bad_alloc&) {
+    return PA_ERR_NO_BLOCKS;
+  }
+  bm->num_host = num_host_blocks;
+  return PA_OK;
+}
+
+int32_t pa_bm_num_free_host_blocks(const pa_block_manager* bm) {
+  return bm ? (int32_t)bm->host_free.size() : -1;
+}
+
+pa_status pa_bm_swap_out(pa_block_manager* bm, int32_t seq, int64_t* pairs_out,
+                         int64_t max_pairs, int64_t* num_pairs) {
+  if (!bm || !num_pairs) return PA_ERR_NULL;
+  Seq* s = bm->seq(seq);
+  if (!s) return PA_ERR_SHAPE;
+  const size_t nb = s->blocks.size();
+  if (nb > bm->host_free.size()) return PA_ERR_NO_BLOCKS;
+  if ((int64_t)nb > max_pairs) return PA_ERR_SHAPE;
+  if (nb > 0 && !pairs_out) return PA_ERR_NULL;
+  try {
+    s->host.reserve(nb);
+  } catch (const std::bad_alloc&) {
+    return PA_ERR_NO_BLOCKS;
+  }
+  for (size_t j = 0; j < nb; ++j) {
+    const int32_t h = bm->host_free.back();
+    bm->host_free.pop_back();
+    s->host.push_back(h);
+    pairs_out[2 * j] = s->blocks[j];
+    pairs_out[2 * j + 1] = h;
+  }
+  // the device blocks are released like a free (last first); shared ones stay with the others
+  for (size_t j = nb; j-- > 0;) bm->drop_ref(s->blocks[j]);
+  s->blocks.clear();
+  s->swapped = true;
+  *num_pairs = (int64_t)nb;
+  return PA_OK;
+}
+
+pa_status pa_bm_swap_in(pa_block_manager* bm, int32_t seq, int64_t* pairs_out,
+                        int64_t max_pairs, int64_t* num_pairs) {
+  if (!bm || !num_pairs) return PA_ERR_NULL;
+  Seq* s = bm->any_seq(seq);
+  if (!s || !s->swapped) return PA_ERR_SHAPE;
+  const size_t nb = s->host.size();
+  if (nb > bm->free_list.size()) return PA_ERR_NO_BLOCKS;
+  if ((int64_t)nb > max_pairs) return PA_ERR_SHAPE;
+  if (nb > 0 && !pairs_out) return PA_ERR_NULL;
+  try {
+    s->blocks.reserve(nb);
+  } catch (const std::bad_alloc&) {
+    return PA_ERR_NO_BLOCKS;
+  }
+  for (size_t j = 0; j < nb; ++j) {
+    const int32_t b = bm->take_block();
+    s->blocks.push_back(b);
+    pairs_out[2 * j] = s->host[j];
+    pairs_out[2 * j + 1] = b;
+  }
+  for (size_t j = nb; j-- > 0;) bm->host_free.push_back(s->host[j]);
+  s->host.clear();
+  s->swapped = false;
+  *num_pairs = (int64_t)nb;
   return PA_OK;
 }
 

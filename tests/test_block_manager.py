@@ -230,3 +230,91 @@ def test_scenario_attention_equals_dense_per_sequence(seed):
                                               k[:, h].astype(np.float64),
                                               v[:, h].astype(np.float64), 0.125)
             np.testing.assert_array_equal(out[i, h], want)
+
+
+# ----------------------------------------------------------------- preemption by swapping
+
+def test_swap_out_and_in_bookkeeping():
+    """"vLLM 架构源码解析 第1篇" §1.1 (preemption by swapping): a swapped-out sequence holds
+    host blocks instead of device ones (shared device blocks stay with the other holders),
+    keeps its length, is refused by every call but swap-in / free / length, and comes back
+    onto fresh device blocks with the same tokens."""
+    bm = BlockManager(32, 16, 8)
+    bm.set_host_blocks(6)
+    a, _ = bm.add_sequence(40, list(range(40)))
+    b = bm.fork(a)
+    ta = tables(bm, a)[0]
+    free0 = bm.num_free_blocks()
+    out = bm.swap_out(a)
+    # host blocks are taken from the tail of their own free list: 5, 4, 3
+    assert out.tolist() == [[ta[0], 5], [ta[1], 4], [ta[2], 3]]
+    assert [bm.ref_count(x) for x in ta] == [1, 1, 1]
+    assert bm.num_free_blocks() == free0 and bm.num_free_host_blocks() == 3
+    assert bm.seq_len(a) == 40
+    for call in (lambda: bm.append(a, 1), lambda: bm.slots(a, 0, 1), lambda: bm.fork(a),
+                 lambda: bm.block_tables([a]), lambda: bm.swap_out(a),
+                 lambda: bm.set_host_blocks(10)):
+        with pytest.raises(PAError):
+            call()
+    back = bm.swap_in(a)
+    tb = tables(bm, a)[0]
+    assert back.tolist() == [[5, tb[0]], [4, tb[1]], [3, tb[2]]]
+    assert set(tb).isdisjoint(ta) and bm.num_free_host_blocks() == 6
+    assert bm.num_free_blocks() == free0 - 3
+    assert bm.slots(a, 39, 1)[0] == tb[2] * 16 + 7
+    with pytest.raises(PAError):
+        bm.swap_in(a)
+    # the sequence grows in place again (its last block is its own)
+    assert bm.append(a, 1)[0] == tb[2] * 16 + 8 and bm.take_copies().shape == (0, 2)
+    assert tables(bm, b)[0] == ta
+
+
+def test_swap_failures_change_nothing_and_free_returns_host_blocks():
+    bm = BlockManager(16, 16, 8)
+    bm.set_host_blocks(2)
+    a, _ = bm.add_sequence(40)
+    ta, free0 = tables(bm, a), bm.num_free_blocks()
+    with pytest.raises(PAError):
+        bm.swap_out(a)  # three blocks, two host blocks
+    assert tables(bm, a) == ta and bm.num_free_blocks() == free0
+    assert bm.num_free_host_blocks() == 2
+    c, _ = bm.add_sequence(20)
+    bm.swap_out(c)
+    assert bm.num_free_host_blocks() == 0
+    # the device fills up while c is out: swapping it back in must wait
+    while bm.num_free_blocks():
+        bm.add_sequence(16 * min(8, bm.num_free_blocks()))
+    with pytest.raises(PAError):
+        bm.swap_in(c)
+    assert bm.num_free_host_blocks() == 0
+    bm.free_sequence(c)
+    assert bm.num_free_host_blocks() == 2 and bm.seq_len(c) == -1
+
+
+def test_swap_round_trip_keeps_attention_bitwise():
+    """The block manager's swap pairs replayed through the oracle's swap: the sequence's
+    device blocks are reused by another sequence while it is out, and after the swap back
+    its attention over the new table equals the attention before, bit for bit."""
+    rng = np.random.default_rng(41)
+    b = W.build_batch("swap_bm", "f16", [70], np.ones(1), 8, 2, 64, rng)
+    g = oracle.make_geom(1, 8, 2, 64, 24, 8, "f16")
+    bm = BlockManager(24, 16, 8)
+    bm.set_host_blocks(8)
+    a, _ = bm.add_sequence(70)
+    kp = W.nan_pool((24,) + b.k_pool_shape()[1:], "f16")
+    vp = W.nan_pool((24,) + b.v_pool_shape()[1:], "f16")
+    oracle.reshape_and_cache(b.key, b.value, kp, vp, bm.slots(a, 0, 70), g)
+    t, n = bm.block_tables([a])
+    before, _ = oracle.paged_attention(b.q, kp, vp, t, n, None, b.scale, g)
+    hk = W.nan_pool((8,) + b.k_pool_shape()[1:], "f16")
+    hv = W.nan_pool((8,) + b.v_pool_shape()[1:], "f16")
+    oracle.swap_blocks(hk, hv, kp, vp, bm.swap_out(a), g)
+    # another sequence takes the released blocks and overwrites them
+    o, _ = bm.add_sequence(70)
+    junk = rng.standard_normal((70, 2, 64)).astype(np.float16)
+    oracle.reshape_and_cache(junk, junk, kp, vp, bm.slots(o, 0, 70), g)
+    bm.free_sequence(o)
+    oracle.swap_blocks(kp, vp, hk, hv, bm.swap_in(a), g)
+    t2, n2 = bm.block_tables([a])
+    after, _ = oracle.paged_attention(b.q, kp, vp, t2, n2, None, b.scale, g)
+    assert np.array_equal(before, after)
