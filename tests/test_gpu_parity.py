@@ -470,6 +470,59 @@ def test_swap_blocks_many_pairs(dev, pinned):
     assert np.array_equal(v_dev.cpu().numpy().view(np.uint8), vp.view(np.uint8))
 
 
+def test_block_manager_swap_round_trip(dev):
+    """Preemption by swapping end to end: the block manager's swap-out pairs run through
+    pa_swap_blocks into pinned host pools, another sequence takes and overwrites the
+    released device blocks, the swap-in pairs bring the blocks back onto other ids, and the
+    decode over the new table equals the decode before, bit for bit, and the oracle."""
+    import torch
+    import oracle
+    from paged_kv_cache_445_amd import pa
+    from paged_kv_cache_445_amd.block_manager import BlockManager
+    _log("[bm swap] f16 70 tokens, 8/2 heads, D 64")
+    rng = np.random.default_rng(42)
+    b = W.build_batch("bm_swap", "f16", [70], np.ones(1), 8, 2, 64, rng)
+    NB, NH = 24, 8
+    bm = BlockManager(NB, 16, 8)
+    bm.set_host_blocks(NH)
+    a, _ = bm.add_sequence(70)
+    g = pa.geom(1, 8, 2, 64, NB, 8, torch.float16, out_dtype=torch.float32)
+    kshape, vshape = (NB,) + b.k_pool_shape()[1:], (NB,) + b.v_pool_shape()[1:]
+    kc = torch.full(kshape, float("nan"), dtype=torch.float16, device="cuda")
+    vc = torch.full(vshape, float("nan"), dtype=torch.float16, device="cuda")
+    key = torch.from_numpy(b.key).cuda()
+    val = torch.from_numpy(b.value).cuda()
+    pa.reshape_and_cache(key, val, kc, vc, torch.from_numpy(bm.slots(a, 0, 70)).cuda(), g)
+    q = torch.from_numpy(b.q).cuda()
+    ws = torch.zeros(max(pa.workspace_size(g, 1), 16), dtype=torch.uint8, device="cuda")
+
+    def attend():
+        t, n = bm.block_tables([a])
+        out = torch.zeros((1, 8, 64), device="cuda")
+        pa.decode(out, q, kc, vc, torch.from_numpy(t).cuda(), torch.from_numpy(n).cuda(), None,
+                  b.scale, ws, g)
+        torch.cuda.synchronize()
+        return out.cpu().numpy(), t, n
+
+    before, t1, n1 = attend()
+    hk = torch.full((NH,) + kshape[1:], float("nan"), dtype=torch.float16).pin_memory()
+    hv = torch.full((NH,) + vshape[1:], float("nan"), dtype=torch.float16).pin_memory()
+    pa.swap_blocks(kc, vc, hk, hv, torch.from_numpy(bm.swap_out(a)), pa.SWAP_OUT, g)
+    o, _ = bm.add_sequence(70)
+    junk = torch.randn((70, 2, 64), dtype=torch.float16, device="cuda")
+    pa.reshape_and_cache(junk, junk, kc, vc, torch.from_numpy(bm.slots(o, 0, 70)).cuda(), g)
+    # o still holds a's old blocks, so a comes back onto other ids
+    pa.swap_blocks(kc, vc, hk, hv, torch.from_numpy(bm.swap_in(a)), pa.SWAP_IN, g)
+    bm.free_sequence(o)
+    after, t2, n2 = attend()
+    assert not np.array_equal(t1, t2)
+    assert np.array_equal(before, after)
+    og = oracle.make_geom(1, 8, 2, 64, NB, 8, "f16")
+    kp, vp = kc.cpu().numpy(), vc.cpu().numpy()
+    want, _ = oracle.paged_attention(b.q, kp, vp, t2, n2, None, b.scale, og)
+    check_out(after.astype(np.float64), want, TOL["f16"], "after the swap round trip")
+
+
 # ----------------------------------------------------------------- speculative verify rows
 
 @pytest.mark.parametrize("name", ["spec_verify_f16", "spec_verify_gqa_bf16"])
