@@ -181,6 +181,29 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
                     void* stream);
 
 /*
+ * pa_decode without a workspace, for callers that cannot allocate device memory: code under
+ * HIP graph capture, serving loops that must not call hipMalloc, harnesses that forbid it.
+ * Arguments, results and errors are pa_decode's, less workspace and workspace_bytes.  The
+ * split-context partials and arrival counters live in a static device array of
+ * PA_DECODE_SCRATCH_BYTES bytes that the library holds on every device it runs on until the
+ * process ends; the call allocates, frees and creates nothing.  The first call on a device
+ * looks up the array's device address and clears its arrival counters with one small kernel
+ * on `stream`; every call leaves them at zero again, as pa_decode does with a workspace.
+ * All calls on one device share that array: calls that may run at the same time on one
+ * device (different streams, or threads without ordering) race on it and must not be
+ * issued; calls queued on one stream are ordered and safe.  Sequences with several rows
+ * run their chunk kernel on `stream` before the decode kernel (pa_decode runs the two side
+ * by side on a second stream).  PA_ERR_WORKSPACE: this geometry and row count need more
+ * than PA_DECODE_SCRATCH_BYTES (pa_workspace_size gives the need).
+ */
+#define PA_DECODE_SCRATCH_BYTES ((size_t)36 << 20)
+pa_status pa_decode_scratch(void* out, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, const int32_t* context_lens,
+                            const int32_t* query_start_loc, int32_t num_q_rows,
+                            int32_t max_query_len, float scale, const pa_geom* geom,
+                            void* stream);
+
+/*
  * Split-context partials (flash-decoding) for decode rows: one query row per sequence
  * (row r = sequence r, num_q_rows == num_seqs).  Partition p of a row is its key positions
  * [p * partition_size, (p + 1) * partition_size) below context_lens[r].

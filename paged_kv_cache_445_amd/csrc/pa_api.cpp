@@ -250,6 +250,59 @@ SideStream* side_stream(int dev) {
 
 float scale_to_log2(float scale) { return scale * 1.4426950408889634f; }
 
+// ---- the workspace of pa_decode_scratch: a static device array (no allocation) ----
+// Each device the library runs on holds its own copy until the process ends.  Host code
+// never passes `scratch` itself to a kernel or a copy (in host code the name is a host-side
+// stand-in, not a device address): it looks the device address up once per device with
+// hipGetSymbolAddress and uses that pointer.
+constexpr size_t kScratchBytes = PA_DECODE_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+__global__ void scratch_clear_kernel(int32_t* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0;
+}
+
+struct ScratchSlot {
+  std::once_flag once;
+  hipError_t err = hipSuccess;
+  void* ptr = nullptr;  // this device's copy of `scratch`
+};
+
+// The device address of `scratch` on the current device (dev), looked up on the first call
+// on that device, which also clears the arrival counters at its start with a small kernel on
+// `st` (a kernel rather than a memset, so that a caller may capture the call in a graph).
+// Every decode call returns the counters to zero, so later calls find them cleared.
+void* scratch_ptr(int dev, hipStream_t st) {
+  static ScratchSlot slots[kMaxDevices];
+  ScratchSlot& s = slots[dev];
+  std::call_once(s.once, [&] {
+    void* p = nullptr;
+    s.err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (s.err != hipSuccess || !p) {
+      if (s.err == hipSuccess) s.err = hipErrorInvalidSymbol;
+      return;
+    }
+    const int64_t n = (int64_t)(counter_bytes() / sizeof(int32_t));
+    hipLaunchKernelGGL(scratch_clear_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                       static_cast<int32_t*>(p), n);
+    s.err = hipGetLastError();
+    if (s.err == hipSuccess) s.ptr = p;
+  });
+  return s.err == hipSuccess ? s.ptr : nullptr;
+}
+
+// pa_decode and pa_decode_scratch.  side_by_side: run the multi-row (chunk) kernel on a
+// second stream beside the decode kernel (pa_decode); otherwise both run on `st`, one after
+// the other (pa_decode_scratch: no stream or event is created).
+pa_status decode_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* context_lens,
+                      const int32_t* query_start_loc, int32_t num_q_rows,
+                      int32_t max_query_len, float scale, void* workspace,
+                      size_t workspace_bytes, const pa_geom* g, hipStream_t st,
+                      bool use_scratch);
+
 }  // namespace
 
 extern "C" {
@@ -386,6 +439,30 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
                     const int32_t* query_start_loc, int32_t num_q_rows, int32_t max_query_len,
                     float scale, void* workspace, size_t workspace_bytes, const pa_geom* g,
                     void* stream) {
+  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc,
+                     num_q_rows, max_query_len, scale, workspace, workspace_bytes, g,
+                     (hipStream_t)stream, false);
+}
+
+pa_status pa_decode_scratch(void* out, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, const int32_t* context_lens,
+                            const int32_t* query_start_loc, int32_t num_q_rows,
+                            int32_t max_query_len, float scale, const pa_geom* g,
+                            void* stream) {
+  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc,
+                     num_q_rows, max_query_len, scale, nullptr, 0, g, (hipStream_t)stream, true);
+}
+
+}  // extern "C"
+
+namespace {
+
+pa_status decode_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* context_lens,
+                      const int32_t* query_start_loc, int32_t num_q_rows,
+                      int32_t max_query_len, float scale, void* workspace,
+                      size_t workspace_bytes, const pa_geom* g, hipStream_t st,
+                      bool use_scratch) {
   const pa_status gs = check_geom(g);
   if (gs != PA_OK) return gs;
   if (num_q_rows < 0 || max_query_len < 0) return PA_ERR_SHAPE;
@@ -395,7 +472,6 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   if (!std::isfinite(scale)) return PA_ERR_SHAPE;
   const int G = g->num_q_heads / g->num_kv_heads;
   if (query_start_loc && (g->kv_dtype == PA_F32 || 16 % G != 0)) return PA_ERR_UNSUPPORTED;
-  hipStream_t st = (hipStream_t)stream;
 
   // rows of the longest sequence: at most max_query_len (0: unknown) and num_q_rows
   int32_t max_len = 1;
@@ -404,6 +480,12 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   const Route rt = route(g, max_len);
   const int grid = split_grid(g, pa::MODE_EVEN, rt.path);
   const size_t need = even_workspace_bytes(g, rt);
+  if (use_scratch) {
+    if (need > kScratchBytes) return PA_ERR_WORKSPACE;
+    workspace = scratch_ptr(current_device(), st);
+    if (!workspace) return PA_ERR_HIP;
+    workspace_bytes = kScratchBytes;
+  }
   if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
   const size_t slots = even_slots(g, grid, rt);
   int32_t* counters = static_cast<int32_t*>(workspace);
@@ -449,6 +531,12 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   // without query_start_loc, or when no sequence has more rows than the decode kernel takes,
   // there is no chunk work
   if (!query_start_loc || max_len <= rt.max_rows) return hip_status(decode());
+  if (use_scratch) {
+    // one stream: the chunk kernel, then the decode kernel
+    const hipError_t ec = pa::launch_chunk(kdt(g), a, num_q_rows, st);
+    if (ec != hipSuccess) return PA_ERR_HIP;
+    return hip_status(decode());
+  }
   // the chunk kernel runs beside the decode kernel: the lean matrix-core decode shares the CUs
   a.lean = 1;
 
@@ -465,6 +553,10 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   if (e == hipSuccess) e = hipStreamWaitEvent(st, side->join, 0);
   return e == hipSuccess && ed == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
+
+}  // namespace
+
+extern "C" {
 
 pa_status pa_decode_partitioned(float* tmp_out, float* max_logits, float* exp_sums,
                                 const void* q, const void* k_cache, const void* v_cache,

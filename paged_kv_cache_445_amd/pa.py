@@ -58,6 +58,9 @@ _lib.pa_swap_blocks.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int64, _vp, ctypes.
 _lib.pa_decode.restype = ctypes.c_int
 _lib.pa_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_int32,
                            ctypes.c_float, _vp, ctypes.c_size_t, _G, _vp]
+_lib.pa_decode_scratch.restype = ctypes.c_int
+_lib.pa_decode_scratch.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32,
+                                   ctypes.c_int32, ctypes.c_float, _G, _vp]
 _lib.pa_decode_partitioned.restype = ctypes.c_int
 _lib.pa_decode_partitioned.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32,
                                        ctypes.c_float, ctypes.c_int32, ctypes.c_int32, _G, _vp]
@@ -157,6 +160,20 @@ def decode(out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc
                           _p(context_lens), _p(query_start_loc), int(q.shape[0]),
                           int(max_query_len), float(scale), _p(workspace), ws_bytes,
                           ctypes.byref(g), _stream(stream)))
+
+
+DECODE_SCRATCH_BYTES = 36 << 20  # PA_DECODE_SCRATCH_BYTES
+
+
+def decode_scratch(out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc, scale,
+                   g: Geom, stream=None, max_query_len: int = 0):
+    """pa_decode_scratch: pa_decode with the library's static device workspace (allocates
+    nothing; calls that overlap on one device race)."""
+    _check("pa_decode_scratch",
+           _lib.pa_decode_scratch(_p(out), _p(q), _p(k_cache), _p(v_cache), _p(block_tables),
+                                  _p(context_lens), _p(query_start_loc), int(q.shape[0]),
+                                  int(max_query_len), float(scale), ctypes.byref(g),
+                                  _stream(stream)))
 
 
 def decode_partitioned(tmp_out, max_logits, exp_sums, q, k_cache, v_cache, block_tables,
