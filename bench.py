@@ -50,6 +50,9 @@ def runs_chunk_kernel(b) -> bool:
 DESCRIPTIONS = {
     "llama7b_f16": "LLaMA-7B-shaped decode: 32 seqs x 32 heads (MHA), head_dim 128, fp16 KV, "
                    "block 16, ctx U[256,2048], 8192-block pool, permuted block table",
+    "llama7b_f16_bs8": "LLaMA-7B-shaped decode with 8-token blocks: 32 seqs x 32 heads (MHA), "
+                       "head_dim 128, fp16 KV, block 8, ctx U[256,2048], 8192-block pool, "
+                       "permuted block table",
     "gqa_long_bf16": "GQA decode: 64 seqs, 64 q / 8 kv heads, head_dim 128, bf16 KV, block 16, "
                      "ctx log-uniform [128,32768]",
     "prefix_shared_f16": "prefix-shared decode: 128 seqs x 32 heads, head_dim 128, fp16 KV, "
@@ -57,6 +60,8 @@ DESCRIPTIONS = {
     "mixed_chunked_bf16": "mixed step: 8 x 512-row causal chunks + 120 decode rows, 32 q / 8 kv "
                           "heads, head_dim 128, bf16 KV",
     "tiny_f32": "tiny decode: 4 seqs x 4 heads, head_dim 64, fp32 KV",
+    "prefill_chunks_bf16": "the mixed step's chunked-prefill rows alone: 8 x 512-row causal "
+                           "chunks over prior U[0,7488], 32 q / 8 kv heads, head_dim 128, bf16 KV",
     "llama7b_fp8": "LLaMA-7B-shaped decode with FP8 E4M3 KV (per-pool scales 6.5/448): 32 seqs "
                    "x 32 heads (MHA), head_dim 128, fp16 q, block 16, ctx U[256,2048], "
                    "8192-block pool, permuted block table",
@@ -76,7 +81,15 @@ DESCRIPTIONS = {
     "cow_copy_f16": "copy-on-write block copies: 256 (source, destination) pairs of LLaMA-7B "
                     "blocks (32 kv heads x 128 x 16 tokens fp16, 128 KiB per pool) in an "
                     "8192-block pool",
+    "hbm_read_ceiling": "HBM read ceiling: a contiguous 640 MiB buffer read front to back per "
+                        "step, three buffers rotated (1.9 GiB, past the 256 MB last-level "
+                        "cache)",
+    "tile_replay_llama7b_f16": "HBM read ceiling of the LLaMA-7B decode's access pattern: every "
+                               "4 KiB K and V tile of the llama7b_f16 batch (585 MB) read in "
+                               "(sequence, block, head) order with no arithmetic, split evenly "
+                               "over the waves; three pool copies rotated",
 }
+MEASURE_WORKLOADS = ("cow_copy_f16", "swap_f16", "hbm_read_ceiling", "tile_replay_llama7b_f16")
 
 
 def sources_digest():
@@ -117,8 +130,9 @@ def attention_flops(b):
     return int(row_keys(b).sum()) * b.num_q_heads * 4 * b.head_dim
 
 
-def cpu_baseline(b, min_seconds, threads, max_key_heads=3e8):
-    """fp64 oracle over the batch, repeated until min_seconds have passed.  The oracle's
+def cpu_baseline(b, min_seconds, threads, max_key_heads=3e8, single_seconds=3.0):
+    """fp64 oracle over the batch, repeated until min_seconds have passed, on `threads`
+    threads; then on one thread for single_seconds on a smaller row sample.  The oracle's
     pools are written by its own cache write from the batch's token records.  Batches
     larger than max_key_heads (row, head, key) triples run on an evenly spaced row sample."""
     import numpy as np
@@ -151,12 +165,33 @@ def cpu_baseline(b, min_seconds, threads, max_key_heads=3e8):
     what = (f"the whole {b.name} batch ({b.num_q_rows} rows" if rows is None else
             f"every {int(rows[1] - rows[0]) if len(rows) > 1 else 1}th row of {b.name} "
             f"({len(rows)} of {b.num_q_rows} rows, {100 * frac:.1f}% of the key-heads")
+    # one thread, on every k-th row so that a pass takes about a tenth of single_seconds
+    single = None
+    if single_seconds > 0:
+        per_row = per / b.num_q_rows * threads  # one thread's seconds per row, roughly
+        k = max(1, int(np.ceil(per_row * b.num_q_rows / (single_seconds / 10))))
+        rows1 = np.arange(0, b.num_q_rows, k, dtype=np.int32)
+        frac1 = float(keys[rows1].sum()) / float(keys.sum())
+        reps1, t1 = 0, time.perf_counter()
+        while True:
+            oracle.paged_attention(b.q, kp, vp, b.block_tables, b.context_lens,
+                                   b.query_start_loc, b.scale, g, rows=rows1, threads=1)
+            reps1 += 1
+            el1 = time.perf_counter() - t1
+            if el1 >= single_seconds:
+                break
+        per1 = el1 / reps1 / frac1
+        single = {"value": round(b.kv_bytes() / per1 / 1e9, 4), "unit": "GB/s", "threads": 1,
+                  "sample": f"every {k}th row ({len(rows1)} rows, {100 * frac1:.2f}% of the "
+                            f"key-heads), {reps1} passes in {el1:.1f} s; "
+                            f"{per1 * 1e3:.0f} ms per whole batch"}
     return {"value": round(b.kv_bytes() / per / 1e9, 4), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
+            "threads": threads, "host_cores": os.cpu_count(), "kind": "oracle",
             "sample": f"{what} x {b.num_q_heads} heads, {b.kv_bytes() / 1e6:.1f} MB of KV in "
-                      f"the batch), {reps} passes in {el:.1f} s; scaled to the whole batch: "
-                      f"{per * 1e3:.1f} ms per pass, {b.num_q_rows * b.num_q_heads / per:.0f} "
-                      f"row-heads/s"}
+                      f"the batch), {reps} passes in {el:.1f} s on {threads} threads; scaled to "
+                      f"the whole batch: {per * 1e3:.1f} ms per pass, "
+                      f"{b.num_q_rows * b.num_q_heads / per:.0f} row-heads/s",
+            "single_thread": single}
 
 
 def bench_copy(args):
@@ -310,6 +345,93 @@ def bench_swap(args):
     print(json.dumps(line), flush=True)
 
 
+def _timed(args, step, stream):
+    """Warm-up steps, then args.steps steps between one pair of HIP events on `stream`;
+    returns (wall seconds, event milliseconds per step)."""
+    import torch
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0, ev[0].elapsed_time(ev[1]) / args.steps
+
+
+def _ceiling_line(args, workload, moved, wall, call_ms, kernel, extra):
+    ms_per_step = wall * 1e3 / args.steps
+    achieved = moved / (call_ms * 1e-3) / 1e9
+    line = {
+        "metric": "HBM read ceiling: GB/s of a read-only kernel",
+        "value": round(moved / (ms_per_step * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u8",
+        "data": "synthetic",
+        "config": dict({"workload": workload, "description": DESCRIPTIONS[workload],
+                        "bytes_per_step": moved}, **extra),
+        "kernel_us": round(call_ms * 1e3, 3),
+        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def bench_read_ceiling(args):
+    """pa_measure_stream_read over one of three 640 MiB buffers per step."""
+    import torch
+    from paged_kv_cache_445_amd import pa
+    dev = torch.device("cuda:0")
+    n = 640 << 20
+    copies = args.copies or 3
+    bufs = [torch.empty(n, dtype=torch.uint8, device=dev).fill_(i + 1) for i in range(copies)]
+    sink = torch.zeros(1 << 16, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    wall, call_ms = _timed(args, lambda i: pa.measure_stream_read(bufs[i % copies], sink), stream)
+    _ceiling_line(args, "hbm_read_ceiling", n, wall, call_ms,
+                  "pa_measure_stream_read (eight 256-thread workgroups per CU)",
+                  {"buffer_bytes": n, "buffers_rotated": copies})
+
+
+def bench_tile_replay(args):
+    """pa_measure_tile_read over the K and V tiles of the llama7b_f16 batch: for every
+    sequence, 16-token block and KV head, the block's K tile then its V tile."""
+    import numpy as np
+    import torch
+    from paged_kv_cache_445_amd import pa
+    from paged_kv_cache_445_amd import workloads as W
+    dev = torch.device("cuda:0")
+    b = W.make("llama7b_f16")
+    H, D = b.num_kv_heads, b.head_dim
+    tile = 16 * D * 2
+    pool = b.num_blocks * H * tile  # bytes of one pool
+    offs = []
+    for s in range(b.num_seqs):
+        nblk = -(-int(b.context_lens[s]) // 16)
+        blk = b.block_tables[s, :nblk].astype(np.int64)
+        o = (blk[:, None] * H + np.arange(H)[None, :]) * tile  # [block][head]
+        offs.append(np.stack([o, o + pool], axis=-1).reshape(-1))  # K then V (second pool)
+    offs = np.concatenate(offs)
+    moved = len(offs) * tile
+    copies = args.copies or 3
+    pools = [torch.empty(2 * pool, dtype=torch.uint8, device=dev).fill_(i + 1)
+             for i in range(copies)]
+    off_t = torch.from_numpy(offs).to(dev)
+    sink = torch.zeros(1 << 16, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    wall, call_ms = _timed(args, lambda i: pa.measure_tile_read(pools[i % copies], off_t, tile,
+                                                                sink), stream)
+    _ceiling_line(args, "tile_replay_llama7b_f16", moved, wall, call_ms,
+                  "pa_measure_tile_read (one 256-thread workgroup per CU)",
+                  {"tiles": int(len(offs)), "tile_bytes": tile, "pool_copies_rotated": copies,
+                   "algorithmic_kv_bytes_of_the_batch": b.kv_bytes()})
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -323,6 +445,9 @@ def main():
                     help="wall time of the CPU-oracle leg (0 skips it)")
     ap.add_argument("--cpu-threads", type=int, default=0,
                     help="oracle threads (0: min(16, host cores))")
+    ap.add_argument("--partitioned", type=int, default=0, metavar="PS",
+                    help="time pa_decode_partitioned with PS-token partitions + pa_decode_reduce "
+                         "in place of pa_decode")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the timed steps, copy a MIB-sized device buffer 3 times "
                          "(a reference kernel of known traffic for HBM byte counters)")
@@ -350,6 +475,10 @@ def main():
         return bench_copy(args)
     if args.workload == "swap_f16":
         return bench_swap(args)
+    if args.workload == "hbm_read_ceiling":
+        return bench_read_ceiling(args)
+    if args.workload == "tile_replay_llama7b_f16":
+        return bench_tile_replay(args)
 
     print(f"[bench] building workload {args.workload}", file=sys.stderr, flush=True)
     b = W.make(args.workload)
@@ -371,10 +500,23 @@ def main():
         kc, vc = pools[i % copies]
         pa.reshape_and_cache(db.key_new, db.value_new, kc, vc, db.slot_new, db.geom)
 
+    PS = args.partitioned
+    if PS:
+        P = -(-b.max_blocks_per_seq * b.block_size // PS)
+        tmp = torch.empty((b.num_q_rows, b.num_q_heads, P, b.head_dim), dtype=torch.float32,
+                          device=dev)
+        ml = torch.empty((b.num_q_rows, b.num_q_heads, P), dtype=torch.float32, device=dev)
+        es = torch.empty_like(ml)
+
     def decode(i):
         kc, vc = pools[i % copies]
-        pa.decode(db.out, db.q, kc, vc, db.block_tables, db.context_lens, db.qsl, db.scale,
-                  db.workspace, db.geom, max_query_len=db.max_query_len)
+        if PS:
+            pa.decode_partitioned(tmp, ml, es, db.q, kc, vc, db.block_tables, db.context_lens,
+                                  db.qsl, db.scale, PS, P, db.geom)
+            pa.decode_reduce(db.out, tmp, ml, es, P, db.geom)
+        else:
+            pa.decode(db.out, db.q, kc, vc, db.block_tables, db.context_lens, db.qsl, db.scale,
+                      db.workspace, db.geom, max_query_len=db.max_query_len)
 
     print(f"[bench] warmup {args.warmup} steps, {copies} pool copies", file=sys.stderr,
           flush=True)
@@ -407,6 +549,15 @@ def main():
     ev_dec[1].record(stream)
     torch.cuda.synchronize()
     dec_ms = [ev_dec[0].elapsed_time(ev_dec[1]) / args.steps]
+    # the same calls on one pool copy (no rotation): part of the pools stays in the
+    # last-level cache from call to call
+    ev_hot = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    ev_hot[0].record(stream)
+    for i in range(args.steps):
+        decode(0)
+    ev_hot[1].record(stream)
+    torch.cuda.synchronize()
+    hot_ms = ev_hot[0].elapsed_time(ev_hot[1]) / args.steps
 
     ms_per_step = wall * 1e3 / args.steps
     dec_avg_ms = float(np.mean(dec_ms))
@@ -425,7 +576,8 @@ def main():
     else:
         bound, achieved, peak, punit = "hbm", hbm_bytes / (dec_avg_ms * 1e-3) / 1e9, \
             HBM_PEAK_GBS, "GB/s"
-    traffic = read_traffic(args.workload) if bound == "hbm" else None
+    traffic_name = args.workload + (f"_part{PS}" if PS else "")
+    traffic = read_traffic(traffic_name) if bound == "hbm" else None
 
     if args.copy_calibration > 0:
         n = args.copy_calibration << 20
@@ -468,14 +620,19 @@ def main():
             "kv_unique_bytes_per_step": hbm_bytes,
             "attention_flops_per_step": flops,
             "pool_copies_rotated": copies,
+            "path": f"pa_decode_partitioned({PS}) + pa_decode_reduce" if PS else "pa_decode",
         },
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "seq_heads_per_s": round(seq_heads / (ms_per_step * 1e-3), 1),
         "pa_decode_us": round(dec_avg_ms * 1e3, 3),
+        "pa_decode_hot_us": round(hot_ms * 1e3, 3),
         "roofline": {
             "bound": bound,
-            "kernel": "pa_decode (decode kernel with in-kernel split merge"
-                      + (" + chunk kernel)" if runs_chunk_kernel(b) else ")"),
+            "kernel": (f"pa_decode_partitioned ({PS}-token partitions) + pa_decode_reduce"
+                       + (" (+ chunk kernel)" if b.query_start_loc is not None else "")
+                       if PS else
+                       "pa_decode (decode kernel with in-kernel split merge"
+                       + (" + chunk kernel)" if runs_chunk_kernel(b) else ")")),
             "achieved": round(achieved, 2),
             "peak": peak,
             "unit": punit,

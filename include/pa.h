@@ -19,21 +19,22 @@
  *     pa_status; nothing is launched on error.  A failed launch returns PA_ERR_HIP.
  *     Device-resident values (block ids < num_blocks, context_lens <= max_blocks_per_seq
  *     * block_size, unique slots) are the caller's contract and are not checked.
- *   - block_size is 16 ("vLLM 架构源码解析 第1篇" §4.2: 16-token blocks), 32 or 64 (§5.1 shows
- *     block_size = 32 as a configuration choice).  head_dim is 64 or 128.
+ *   - block_size is 16 ("vLLM 架构源码解析 第1篇" §4.2: 16-token blocks), 8, 32 or 64 (§5.1
+ *     weighs block sizes 8, 16 and 32 against each other).  head_dim is 64 or 128.
  *     kv_dtype is PA_F32, PA_F16 or PA_BF16 (q, key, value and both pools share it), or
  *     PA_FP8_E4M3 (see "FP8 pools").
  *
  * Pool layout (part of this ABI).  elem = 4 (fp32), 2 (fp16, bf16) or 1 (FP8) bytes,
- * X = 16 / elem, R = block_size / 16:
- *   k_cache: [num_blocks][R][num_kv_heads][head_dim / X][16][X]
- *   v_cache: [num_blocks][R][num_kv_heads][head_dim][16]
+ * X = 16 / elem, T = min(block_size, 16) tokens per tile, R = block_size / T:
+ *   k_cache: [num_blocks][R][num_kv_heads][head_dim / X][T][X]
+ *   v_cache: [num_blocks][R][num_kv_heads][head_dim][T]
  * For 16-token blocks (R = 1) v_cache is the pages' [num_blocks, num_heads, head_size,
  * block_size] ("vLLM 深度拆解" §6.2); k_cache splits head_size into 16-byte chunks so one
  * token's chunk is one 16-byte load and the 16 tokens of a chunk are 256 contiguous bytes.
  * A larger block is R consecutive 16-token sub-blocks in that layout, token t of the block
  * in sub-block t / 16 at position t % 16 (so slot / 16 names a sub-block for every block
- * size).
+ * size from 16 up).  An 8-token block is one tile of T = 8 (its V is the pages' layout with
+ * block_size 8).
  *
  * FP8 pools ("vLLM 深度拆解" §10.1 names FP8 KV with calibrated scales).  kv_dtype
  * PA_FP8_E4M3: one byte per element in the layout above with elem = 1, X = 16; q, key and
@@ -148,7 +149,14 @@ pa_status pa_swap_blocks(void* k_cache, void* v_cache, void* host_k, void* host_
                          void* stream);
 
 /* Workspace bytes pa_decode needs for this geometry and row count (0 is never returned
- * for a valid geometry; returns 0 for an invalid one). */
+ * for a valid geometry; returns 0 for an invalid one).  The workspace holds the partials of
+ * the context splits pa_decode makes inside one kernel (see pa_decode): two partial slots
+ * per wave of that kernel's grid plus one arrival counter per wave of the largest grid the
+ * device can have.  Its size therefore depends on the device, the head size, the query
+ * group and whether sequences may have several rows, not on context lengths or a partition
+ * size.  The pages name a split-context kernel ("vLLM 架构源码解析 第1篇" §4.2,
+ * paged_attention_v2) without describing it; the split, its partials and their merge are
+ * this library's. */
 size_t pa_workspace_size(const pa_geom* geom, int32_t num_q_rows);
 
 /*
@@ -160,6 +168,16 @@ size_t pa_workspace_size(const pa_geom* geom, int32_t num_q_rows);
  *                 in physical block block_tables[s * max_blocks_per_seq + j]
  *   context_lens  int32 [num_seqs]
  *   query_start_loc  int32 [num_seqs + 1] or NULL (see "Rows and positions")
+ *   num_q_rows    rows of q and out (num_seqs without query_start_loc)
+ *   max_query_len with query_start_loc: an upper bound of any sequence's row count,
+ *                 qsl[s + 1] - qsl[s], or 0 when unknown (then num_q_rows is taken).  It
+ *                 picks the kernels from the host, which never reads device data: when the
+ *                 bound lets every sequence fit the decode kernel (one row; on the
+ *                 matrix-core path up to 16 / G rows), the multi-row kernel is not launched.
+ *                 A bound below some sequence's row count is a caller error: that
+ *                 sequence's rows are then written NaN (unless the multi-row kernel runs
+ *                 for another sequence, in which case they are computed), and the call
+ *                 returns PA_OK.  Ignored without query_start_loc; must be >= 0.
  *   scale         multiplies q . k (normally 1 / sqrt(head_dim))
  *   workspace     device scratch of at least pa_workspace_size(geom, num_q_rows) bytes for
  *                 split-context partials and their arrival counters.  Zero-fill it once
@@ -204,27 +222,39 @@ pa_status pa_decode_scratch(void* out, const void* q, const void* k_cache, const
                             void* stream);
 
 /*
- * Split-context partials (flash-decoding) for decode rows: one query row per sequence
- * (row r = sequence r, num_q_rows == num_seqs).  Partition p of a row is its key positions
- * [p * partition_size, (p + 1) * partition_size) below context_lens[r].
+ * Split-context partials (flash-decoding).  The pages name the split-context decode kernel
+ * only by its file ("vLLM 架构源码解析 第1篇" §4.2, paged_attention_v2); what it computes is
+ * this library's reading: the attention of "vLLM 深度拆解" §2.2 restricted to fixed key
+ * partitions, whose partials pa_decode_reduce merges by log-sum-exp into exactly the
+ * softmax over all keys.  Partition p of a row is the row's visible keys (see "Rows and
+ * positions") among positions [p * partition_size, (p + 1) * partition_size).
  *   tmp_out     float [num_q_rows][num_q_heads][max_partitions][head_dim]: the partition's
  *               softmax-normalised output
  *   max_logits  float [num_q_rows][num_q_heads][max_partitions]: max of scale * q . k over
  *               the partition's keys
  *   exp_sums    float [num_q_rows][num_q_heads][max_partitions]: sum of
  *               exp(scale * q . k - max_logits) over those keys
- * Partitions with no key get max_logits = -inf and exp_sums = 0; their tmp_out entries are
- * not written.  partition_size is a positive multiple of 32; max_partitions must cover the
- * longest possible context: max_partitions * partition_size >= max_blocks_per_seq * block_size.
+ *   query_start_loc  int32 [num_seqs + 1] or NULL (one row per sequence, num_q_rows ==
+ *               num_seqs); with it, sequences of several rows (chunked-prefill or verify
+ *               rows) get their partials from the multi-row kernel, which then runs after
+ *               the decode kernel on `stream`.  Needs a 16-bit or FP8 kv_dtype and a query
+ *               group G = Hq / Hkv that divides 16 (else PA_ERR_UNSUPPORTED), as pa_decode.
+ * Every max_logits / exp_sums entry is written; a partition with no key of the row gets
+ * max_logits = -inf and exp_sums = 0 and its tmp_out entries are not written.
+ * partition_size is a positive multiple of 32; max_partitions must cover the longest
+ * possible context: max_partitions * partition_size >= max_blocks_per_seq * block_size.
+ * Other arguments as pa_decode.
  */
 pa_status pa_decode_partitioned(float* tmp_out, float* max_logits, float* exp_sums,
                                 const void* q, const void* k_cache, const void* v_cache,
                                 const int32_t* block_tables, const int32_t* context_lens,
-                                int32_t num_q_rows, float scale, int32_t partition_size,
-                                int32_t max_partitions, const pa_geom* geom, void* stream);
+                                const int32_t* query_start_loc, int32_t num_q_rows,
+                                float scale, int32_t partition_size, int32_t max_partitions,
+                                const pa_geom* geom, void* stream);
 
 /*
- * Log-sum-exp merge of pa_decode_partitioned's output: over the partitions with
+ * Log-sum-exp merge of pa_decode_partitioned's output (the merge of its split-context
+ * partials; see there for what the pages say of it): over the partitions with
  * exp_sums > 0, M = max_p max_logits[p], w_p = exp_sums[p] * exp(max_logits[p] - M) and
  * out = sum_p w_p * tmp_out[p] / sum_p w_p.  Rows with no key get 0.  Arguments as in
  * pa_decode_partitioned; out [num_q_rows][num_q_heads][head_dim] in out_dtype.

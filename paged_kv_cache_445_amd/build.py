@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpa.so")
 SOURCES = ["pa_api.cpp", "reshape.hip", "decode_valu.hip", "decode_mfma.hip", "chunk.hip",
-           "reduce.hip", "copy_blocks.hip", "block_manager.cpp"]
+           "reduce.hip", "copy_blocks.hip", "block_manager.cpp", "measure.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

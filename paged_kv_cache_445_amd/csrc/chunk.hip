@@ -6,17 +6,38 @@
 // written by reshape_and_cache first, §3.3.3); row j sits at position ctx - n + j and attends
 // keys [0, ctx - n + j] (causal).  Sequences with few rows (a decode row, or on the
 // matrix-core path up to 16 / G rows, as in a speculative verify step) are left to the decode
-// kernels.
+// kernels of pa_decode; pa_decode_partitioned sends every sequence of several rows here.
 //
-// Work item = (sequence, KV head g, block of 128 query columns), a column being one (row,
-// head) pair: 128 / G consecutive rows x the G query heads of g.  The workgroup stages each
-// 32-token K/V unit in LDS once and its four waves each run 32 columns over it through the
-// matrix-core step of pa_mfma.h, so one unit read from memory serves 128 columns.
+// Work item = (sequence, KV head g, block of 128 query columns[, key partition]), a column
+// being one (row, head) pair: 128 / G consecutive rows x the G query heads of g.  The
+// workgroup stages each 32-token K/V unit in LDS once and its four waves each run 32
+// columns over it on the matrix cores (S^T = K . Q^T, then O^T += V^T . P^T, operand layouts
+// as in pa_mfma.h), so one unit read from memory serves 128 columns.
+//
+// The softmax between the two products is streamed with a lazy reference: a column's
+// weights are exp2(score - m) against a reference m that moves only when the column's
+// running max exceeds it by more than kLazy (2^8 in weight), so the rescale of the outputs
+// is rare after a column's first keys; weights then lie in [0, 2^8], well inside fp32 and
+// the 16-bit operand types.  The weight sum l comes out of the matrix core as well (P
+// multiplied by a block of ones), from the same 16-bit weights as the outputs, so every
+// column's output is a weighted mean whose weights sum to one up to fp32 rounding.  Feeding
+// P as one 16-bit operand rounds each weight by a relative d_t, |d_t| <= 2^-9 (bf16) or
+// 2^-11 (fp16); the output then errs by sum_t d_t w_t (v_t - o), w_t the final softmax
+// weights.  A single heavy key makes that error large (w = 0.35, |v - o| = 3: 2e-3 in
+// bf16), so a unit whose largest weight in some column of the block exceeds kHeavy of that
+// column's running sum including it feeds P as hi + lo 16-bit parts (two products, ~2^-17
+// relative).  Every weight fed as one part is then at most kHeavy of its column's final sum:
+// each key adds at most 2^-9 kHeavy |v_t - o| and the independent roundings add up to a
+// standard deviation of at most 2^-9 / sqrt(3) * sqrt(kHeavy) * rms_w(v - o).  The hi + lo
+// units are the first few of every column (while its sum is small) and units with a new
+// dominant key.
 //
 // FP8 pools ("vLLM 深度拆解" §10.1) take the same path: each 8-byte half of an E4M3 chunk is
 // widened to the query's 16-bit type (exact for every E4M3 value) on its way into LDS, where
 // the unit then has the 16-bit layout; k_scale is in the score factor and v_scale multiplies
 // the output.
+#include <algorithm>
+
 #include "pa_device.h"
 #include "pa_internal.h"
 #include "pa_mfma.h"
@@ -26,6 +47,8 @@ namespace pa {
 constexpr int kChunkBlocks = 2;                       // 16-column MFMA blocks per wave
 constexpr int kWaveCols = 16 * kChunkBlocks;          // query columns per wave
 constexpr int kItemCols = kWaveCols * kWavesPerWG;    // query columns per workgroup
+constexpr float kLazy = 8.f;                          // reference slack, base-2 exponent
+constexpr float kHeavy = 1.f / 64;                    // heavier weights: hi + lo parts
 
 template <int D>
 struct ChunkTile {
@@ -37,31 +60,135 @@ struct ChunkTile {
 
 struct ChunkPlanIn {
   const int32_t* qsl;
+  const int32_t* context_lens;
   int32_t num_seqs;
   int32_t rows_per_item;
-  int32_t min_rows;  // sequences with fewer rows are the decode kernel's
+  int32_t min_rows;   // sequences with fewer rows are the decode kernel's
+  int32_t part_tokens;  // > 0: one item per key partition of this many tokens as well
 };
 
-// work items per sequence: ceil(n / rows_per_item) for sequences of at least min_rows rows,
-// else 0
+// work items per sequence: ceil(n / rows_per_item) column blocks (times the key partitions
+// of its context with part_tokens) for sequences of at least min_rows rows, else 0
 __device__ inline void build_chunk_plan(int32_t* base, const ChunkPlanIn& p) {
   wave_plan(base, p.num_seqs, [&](int s) {
     const int32_t n = p.qsl[s + 1] - p.qsl[s];
-    return n >= p.min_rows ? (n + p.rows_per_item - 1) / p.rows_per_item : 0;
+    if (n < p.min_rows) return 0;
+    const int32_t cbs = (n + p.rows_per_item - 1) / p.rows_per_item;
+    if (p.part_tokens <= 0) return cbs;
+    const int32_t ctx = p.context_lens[s];
+    return cbs * ((ctx + p.part_tokens - 1) / p.part_tokens);
   });
 }
 
-// One work item: rows [j0, j0 + kItemCols / G) of multi-row sequence s for KV head g.  The
-// workgroup streams the item's keys in 32-token units: every unit (K and V of two blocks) is
-// loaded once by the whole workgroup, two units ahead, into one of two LDS buffers, and each
-// wave then runs its 32 query columns (two 16-column MFMA blocks, per-column causal limits)
-// over it.  DT is the 16-bit type of the queries and of the staged unit; F8: the pools hold
-// E4M3 bytes.
-template <int DT, int D, bool F8>
-__device__ void chunk_item(const DecodeArgs& a, int s, int g, int cb, char* lds_units) {
+// Per-lane state of one 16-column block: outputs O[column n][dims 16 j + 4 r ..], the
+// weight sum (all four entries equal), the weights' reference and the true running max
+// (both base 2, scaled scores).
+template <int D>
+struct ChunkCol {
+  f32x4_t acc[D / 16];
+  f32x4_t lsum;
+  float m;
+  float mx;
+};
+
+template <int DT>
+struct ChunkP {
+  op8_t<DT> hi, lo;
+  bool split;  // uniform: the weights are fed as hi + lo
+};
+
+// Scores of one column block over the unit (raw q . k from the matrix core), the lazy
+// softmax update and the block's weights.  sl > 0 is the score factor in the base-2 domain.
+// MASK: unit token 8 r + k exists for this lane's column only if 8 r + k <= lim.  The low
+// parts of the weights are formed when some column's largest weight is heavy (kHeavy).
+template <int DT, int D, bool MASK>
+__device__ __forceinline__ ChunkP<DT> chunk_scores(ChunkCol<D>& st, const MfmaK<DT, D>& kb,
+                                                   const MfmaQ<DT, D>& qb, float sl, int lim) {
+  using C = MfmaCfg<DT, D>;
+  using E = typename std::conditional<bf16_core<DT>(), __bf16, _Float16>::type;
+  const int r = lane_id() >> 4;
+  f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < C::NKK; ++kk) {
+    s0 = mfma<DT>(operand<DT>(kb[0][kk]), qb[kk], s0);
+    s1 = mfma<DT>(operand<DT>(kb[1][kk]), qb[kk], s1);
+  }
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[i] = s0[i];
+    x[4 + i] = s1[i];
+  }
+  if (MASK) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (8 * r + k > lim) x[k] = -INFINITY;
+  }
+  float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                   fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+  mx = cross_rows_max(mx);
+  const float ms = mx * sl;  // -inf when the column sees no key of the unit
+  st.mx = fmaxf(st.mx, ms);
+  // move the reference only when the max outgrows it by more than kLazy (and on a
+  // column's first visible keys, whose reference is -inf)
+  if (__builtin_amdgcn_ballot_w64(ms > st.m + kLazy)) {
+    const bool up = ms > st.m + kLazy;
+    const float mnew = up ? ms : st.m;
+    const float alpha = up ? __builtin_amdgcn_exp2f(st.m - mnew) : 1.f;
+#pragma unroll
+    for (int j = 0; j < C::NJ; ++j) st.acc[j] *= alpha;
+    st.lsum *= alpha;
+    st.m = mnew;
+  }
+  // a column with no visible key so far keeps the reference -inf: its weights are 0
+  const float mref = st.m == -INFINITY ? 0.f : st.m;
+  // the column's largest weight of the unit, p, against its sum so far l: heavy when
+  // p > kHeavy (l + p)
+  const float pmax = __builtin_amdgcn_exp2f(fmaf(mx, sl, -mref));
+  ChunkP<DT> out;
+  out.split = __builtin_amdgcn_ballot_w64(pmax * (1.f / kHeavy - 1.f) > st.lsum[0]) != 0;
+  float p[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) p[k] = __builtin_amdgcn_exp2f(fmaf(x[k], sl, -mref));
+#pragma unroll
+  for (int k = 0; k < 8; ++k) out.hi[k] = (E)p[k];
+  if (out.split) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) out.lo[k] = (E)(p[k] - (float)out.hi[k]);
+  }
+  return out;
+}
+
+// O^T += V^T . P^T for one column block, and the weight sum from the same 16-bit weights.
+template <int DT, int D>
+__device__ __forceinline__ void chunk_pv(ChunkCol<D>& st, const op8_t<DT> (&vo)[D / 16],
+                                         const ChunkP<DT>& p, const op8_t<DT>& ones) {
+  using C = MfmaCfg<DT, D>;
+#pragma unroll
+  for (int j = 0; j < C::NJ; ++j) st.acc[j] = mfma<DT>(vo[j], p.hi, st.acc[j]);
+  st.lsum = mfma<DT>(ones, p.hi, st.lsum);
+  if (p.split) {
+#pragma unroll
+    for (int j = 0; j < C::NJ; ++j) st.acc[j] = mfma<DT>(vo[j], p.lo, st.acc[j]);
+    st.lsum = mfma<DT>(ones, p.lo, st.lsum);
+  }
+}
+
+// One work item: rows [j0, j0 + kItemCols / G) of multi-row sequence s for KV head g over the
+// keys [kbeg, kend) (PART: one key partition; else every key the rows see).  The workgroup
+// streams the keys in 32-token units: every unit (K and V of two blocks) is loaded once by
+// the whole workgroup, two units ahead, into one of two LDS buffers, and each wave then runs
+// its 32 query columns (two 16-column MFMA blocks, per-column causal limits) over it.  DT is
+// the 16-bit type of the queries and of the staged unit; F8: the pools hold E4M3 bytes.
+// PART: the item writes the partition's partials (normalised output, max, sum) instead of
+// the output.
+template <int DT, int D, bool F8, bool PART, bool B8>
+__device__ void chunk_item(const DecodeArgs& a, int s, int g, int cb, int part,
+                           char* lds_units) {
   using C = MfmaCfg<DT, D>;
   using CT = ChunkTile<D>;
   using T = op8_t<DT>;
+  using E = typename std::conditional<bf16_core<DT>(), __bf16, _Float16>::type;
   constexpr int NCB = kChunkBlocks;
   const int lane = lane_id();
   const int wave = threadIdx.x / kWave;
@@ -75,8 +202,22 @@ __device__ void chunk_item(const DecodeArgs& a, int s, int g, int cb, char* lds_
   const int jendg = min(nrows, j0g + kItemCols / G);
   const int j0 = j0g + wave * RW;                  // first row of this wave
   const int jend = min(jendg, j0 + RW);
-  const int nkeys_g = ctx - nrows + jendg;         // keys any column of the item may see
-  const int nkeys_w = jend > j0 ? ctx - nrows + jend : 0;  // ... of this wave's columns
+  // keys [kbeg, kend) any column of the item may see; this wave's columns see keys below
+  // kend_w
+  const int kbeg = PART ? part * a.part_tokens : 0;
+  int kend = ctx - nrows + jendg;
+  int kend_w = jend > j0 ? ctx - nrows + jend : 0;
+  if (PART) {
+    kend = min(kend, kbeg + a.part_tokens);
+    kend_w = min(kend_w, kbeg + a.part_tokens);
+  }
+
+  // Scores are formed with the factor sl > 0: a negative factor is folded into q (sign
+  // flips are exact) and a zero factor makes every score 0 (q = 0, factor 1).
+  float sl = a.scale_log2;
+  const uint32_t qflip = sl < 0.f ? 0x80008000u : 0u;
+  const bool qzero = sl == 0.f;
+  sl = qzero ? 1.f : fabsf(sl);
 
   T qb[NCB][C::NKK];
   int pos[NCB];     // this lane's column's last visible key (-1: column past the rows)
@@ -96,62 +237,103 @@ __device__ void chunk_item(const DecodeArgs& a, int s, int g, int cb, char* lds_
                      ((int64_t)(q0 + jc) * a.num_q_heads + (int64_t)g * G + hc) * D * C::E;
 #pragma unroll
     for (int kk = 0; kk < C::NKK; ++kk) {
-      const uint4 v = ok ? ld16(qp + (4 * kk + r) * 16) : make_uint4(0, 0, 0, 0);
+      uint4 v = ok && !qzero ? ld16(qp + (4 * kk + r) * 16) : make_uint4(0, 0, 0, 0);
+      v.x ^= qflip;
+      v.y ^= qflip;
+      v.z ^= qflip;
+      v.w ^= qflip;
       qb[c][kk] = __builtin_bit_cast(T, v);
     }
   }
-  MfmaState<DT, D> st[NCB];
+  ChunkCol<D> st[NCB];
 #pragma unroll
   for (int c = 0; c < NCB; ++c) {
     st[c].m = -INFINITY;
-    st[c].l = 0.f;
+    st[c].mx = -INFINITY;
+    st[c].lsum = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < C::NJ; ++j) st[c].acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
+  T ones;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) ones[k] = (E)1.f;
 
   const MfmaLaneOffsets<DT, D> o = mfma_offsets<DT, D>();
-  constexpr int64_t PTILE = F8 ? C::TILE / 2 : C::TILE;  // a block of one KV head in the pool
+  // a pool tile of one KV head: 16 tokens (8 with 8-token blocks), 16-bit or E4M3 elements
+  constexpr int64_t PTILE = (F8 ? C::TILE / 2 : C::TILE) / (B8 ? 2 : 1);
   const int64_t blk_stride = (int64_t)a.num_kv_heads * PTILE;
   const char* kc = reinterpret_cast<const char*>(a.k_cache) + (int64_t)g * PTILE;
   const char* vc = reinterpret_cast<const char*>(a.v_cache) + (int64_t)g * PTILE;
   const int32_t* bt_row = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
-  const int nblk = (nkeys_g + kBlock - 1) / kBlock;
-  const int nu = (nkeys_g + kMfmaUnit - 1) / kMfmaUnit;
+  constexpr int TT = B8 ? 8 : kBlock;                    // tokens of one pool tile
+  constexpr int PER_UNIT = kMfmaUnit / TT;               // pool tiles per unit
+  const int nblk = (kend + TT - 1) / TT;
+  const int ubeg = kbeg / kMfmaUnit;                     // partitions are whole units
+  const int uend = (kend + kMfmaUnit - 1) / kMfmaUnit;
 
-  // this thread's share of a unit: chunk k * kWG + threadIdx.x of the four tiles
-  // [K block a, K block b, V block a, V block b]
-  // (16-bit chunk c of a tile; FP8: its 8 source bytes, half of E4M3 K chunk
-  // (c / 32) * 16 + c % 16, or bytes 8c.. of the V tile)
-  int ld_tile[CT::LOADS], ld_off[CT::LOADS], src_off[CT::LOADS];
+  // This thread's share of a unit: chunk k * kWG + threadIdx.x of the four 16-token tiles of
+  // the staged unit [K tokens 0-15, K tokens 16-31, V tokens 0-15, V tokens 16-31], read from
+  // pool tile ld_blk of the unit at byte src_off:
+  //  - 16-token tiles: 16-bit chunk c of the tile; FP8: its 8 source bytes, half of E4M3 K
+  //    chunk (c / 32) * 16 + c % 16, or bytes 8c.. of the V tile;
+  //  - 8-token blocks: K chunk c = (8-element chunk c / 16, token c % 16) comes from block
+  //    (c / 8) % 2 of the 16-token pair, V chunk c = (dimension c / 2, tokens 8 (c % 2) ..)
+  //    from block c % 2, in the 8-token layouts K [D/X][8][X], V [D][8].
+  int ld_tile[CT::LOADS], ld_off[CT::LOADS], src_off[CT::LOADS], ld_blk[CT::LOADS];
 #pragma unroll
   for (int k = 0; k < CT::LOADS; ++k) {
     const int c = k * kWG + threadIdx.x;
     ld_tile[k] = c / CT::CPT;
     const int cc = c % CT::CPT;
+    const bool vt = ld_tile[k] & 2;
     ld_off[k] = cc * 16;
-    if constexpr (F8)
-      src_off[k] = ld_tile[k] & 2 ? cc * 8 : (((cc >> 5) << 4) + (cc & 15)) * 16 + 8 * ((cc >> 4) & 1);
-    else
-      src_off[k] = cc * 16;
+    if constexpr (B8) {
+      const int half = vt ? cc & 1 : (cc >> 3) & 1;
+      ld_blk[k] = 2 * (ld_tile[k] & 1) + half;
+      const int ch = cc >> 4, tok = cc & 7;
+      if constexpr (F8)
+        src_off[k] = vt ? (cc >> 1) * 8 : (((ch >> 1) << 3) + tok) * 16 + 8 * (ch & 1);
+      else
+        src_off[k] = vt ? (cc >> 1) * 16 : ((ch << 3) + tok) * 16;
+    } else {
+      ld_blk[k] = ld_tile[k] & 1;
+      if constexpr (F8)
+        src_off[k] = vt ? cc * 8 : (((cc >> 5) << 4) + (cc & 15)) * 16 + 8 * ((cc >> 4) & 1);
+      else
+        src_off[k] = cc * 16;
+    }
   }
   using Raw = typename std::conditional<F8, uint2, uint4>::type;
   constexpr int WDT = DT == DT_BF16 ? DT_FP8B : DT_FP8;  // widening of FP8 staged bytes
-  int win0 = 0, win1 = 0, wbase = -1;  // block-table windows of 64 entries: [wbase, wbase + 128)
+  // block-table windows of 64 entries, [wbase, wbase + 128): pool tiles (16-token tiles of
+  // the table, or 8-token blocks); entries past the item's last tile hold 0 (masked tokens)
+  int win0 = 0, win1 = 0, wbase = -1;
   auto load_unit = [&](Raw* regs, int u) {
-    const int e = 2 * u;
-    if (wbase < 0 || e >= wbase + 128) {  // uniform; happens every 64 units
+    const int e = PER_UNIT * u;
+    if (wbase < 0 || e >= wbase + 128) {  // uniform; happens every 128 / PER_UNIT units
       wbase = e;
-      win0 = (e + lane < nblk) ? tile_block(bt_row, e + lane, a.blk_shift) : 0;
-      win1 = (e + 64 + lane < nblk) ? tile_block(bt_row, e + 64 + lane, a.blk_shift) : 0;
+      if constexpr (B8) {
+        win0 = (e + lane < nblk) ? bt_row[e + lane] : 0;
+        win1 = (e + 64 + lane < nblk) ? bt_row[e + 64 + lane] : 0;
+      } else {
+        win0 = (e + lane < nblk) ? tile_block(bt_row, e + lane, a.blk_shift) : 0;
+        win1 = (e + 64 + lane < nblk) ? tile_block(bt_row, e + 64 + lane, a.blk_shift) : 0;
+      }
     }
-    const int ia = e - wbase;
-    const int64_t ba = ia < 64 ? readlane(win0, ia) : readlane(win1, ia - 64);
-    // a second block past the keys is replaced by the first (its tokens are masked)
-    const int64_t bb = e + 1 < nblk ? (ia + 1 < 64 ? readlane(win0, ia + 1) : readlane(win1, ia + 1 - 64)) : ba;
+    const int ia = e - wbase;  // the unit's PER_UNIT entries share one register
+    int64_t bt[PER_UNIT];
+#pragma unroll
+    for (int i = 0; i < PER_UNIT; ++i)
+      bt[i] = ia < 64 ? readlane(win0, ia + i) : readlane(win1, ia + i - 64);
+    // 16-token tiles: a second tile past the keys is replaced by the first (its tokens are
+    // masked)
+    if (!B8 && e + 1 >= nblk) bt[PER_UNIT - 1] = bt[0];
 #pragma unroll
     for (int k = 0; k < CT::LOADS; ++k) {
-      const int t = ld_tile[k];
-      const char* base = (t & 2 ? vc : kc) + (t & 1 ? bb : ba) * blk_stride;
+      int64_t b = bt[0];
+#pragma unroll
+      for (int i = 1; i < PER_UNIT; ++i) b = ld_blk[k] == i ? bt[i] : b;
+      const char* base = (ld_tile[k] & 2 ? vc : kc) + b * blk_stride;
       regs[k] = *reinterpret_cast<const Raw*>(base + src_off[k]);
     }
   };
@@ -169,16 +351,16 @@ __device__ void chunk_item(const DecodeArgs& a, int s, int g, int cb, char* lds_
 
   // Unit pipeline: the loads of unit u + 2 go out at the start of step u, unit u is computed
   // from LDS buffer u % 2, and unit u + 1 (loaded since the start of step u - 1, so two
-  // compute phases ago) is stored into the other buffer at the end of the step.  Even units
-  // are staged in ra, odd ones in rb.  Loads and stores run on every step (past the last unit
+  // compute phases ago) is stored into the other buffer at the end of the step.  Even steps
+  // stage in ra, odd ones in rb.  Loads and stores run on every step (past the last unit
   // they repeat it and the result is never read), and the barrier between steps does not wait
   // for outstanding loads, so the compiler's wait before each store covers only that unit.
   auto barrier = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
-  const int ulast = nu - 1;
-  auto compute = [&](int u) {
+  const int ulast = uend - 1;
+  auto compute = [&](int u, int buf) {
     const int t0 = u * kMfmaUnit;
-    if (u < nu && t0 < nkeys_w) {  // uniform: this wave's columns see keys of this unit
-      const char* ub = lds_units + (u & 1) * CT::UNIT;
+    if (u < uend && t0 < kend_w) {  // uniform: this wave's columns see keys of this unit
+      const char* ub = lds_units + buf * CT::UNIT;
       // scores of both column blocks from K, then P . V from V: K and V are never live together
       MfmaK<DT, D> kb;
 #pragma unroll
@@ -186,61 +368,89 @@ __device__ void chunk_item(const DecodeArgs& a, int s, int g, int cb, char* lds_
 #pragma unroll
         for (int kk = 0; kk < C::NKK; ++kk)
           kb[b][kk] = *reinterpret_cast<const uint4*>(ub + o.kt[b] * CT::TILE + o.koff(b, kk));
-      bool masked[NCB];
-      MfmaP<DT> pp[NCB];
+      ChunkP<DT> pp[NCB];
 #pragma unroll
       for (int c = 0; c < NCB; ++c) {
-        masked[c] = !(t0 + kMfmaUnit - 1 <= first[c] && full[c]);
         if (!live[c]) continue;
-        if (!masked[c])
-          pp[c] = mfma_scores<DT, D, false, true>(st[c], kb, qb[c], a.scale_log2, kMfmaUnit - 1);
+        if (t0 + kMfmaUnit - 1 <= first[c] && full[c])
+          pp[c] = chunk_scores<DT, D, false>(st[c], kb, qb[c], sl, kMfmaUnit - 1);
         else
-          pp[c] = mfma_scores<DT, D, true, true>(st[c], kb, qb[c], a.scale_log2, pos[c] - t0);
+          pp[c] = chunk_scores<DT, D, true>(st[c], kb, qb[c], sl, pos[c] - t0);
       }
-      MfmaV<DT, D> vb;
+      T vo[C::NJ];
 #pragma unroll
       for (int j = 0; j < C::NJ; ++j)
-        vb[j] = *reinterpret_cast<const uint4*>(ub + (2 + o.vt) * CT::TILE + o.voff(j));
-      // V is masked in place for the first block that needs it; the masked tokens are the
-      // same for every column, so later blocks may use it either way
+        vo[j] = __builtin_bit_cast(T, *reinterpret_cast<const uint4*>(ub + (2 + o.vt) * CT::TILE + o.voff(j)));
+      if (t0 + kMfmaUnit > kend) {
+        // zero the V elements of tokens past the item's keys (0 * NaN is NaN); their
+        // weights are 0 in every column
+        const int kv = min(8, max(0, kend - t0 - 8 * r));
+        uint32_t mk[4];
 #pragma unroll
-      for (int c = 0; c < NCB; ++c) {
-        if (!live[c]) continue;
-        if (!masked[c])
-          mfma_pv<DT, D, false>(st[c], vb, pp[c], kMfmaUnit);
-        else
-          mfma_pv<DT, D, true>(st[c], vb, pp[c], nkeys_g - t0);
+        for (int w = 0; w < 4; ++w)
+          mk[w] = (2 * w < kv ? 0xffffu : 0u) | (2 * w + 1 < kv ? 0xffff0000u : 0u);
+#pragma unroll
+        for (int j = 0; j < C::NJ; ++j) {
+          uint4 w = __builtin_bit_cast(uint4, vo[j]);
+          w.x &= mk[0];
+          w.y &= mk[1];
+          w.z &= mk[2];
+          w.w &= mk[3];
+          vo[j] = __builtin_bit_cast(T, w);
+        }
       }
+#pragma unroll
+      for (int c = 0; c < NCB; ++c)
+        if (live[c]) chunk_pv<DT, D>(st[c], vo, pp[c], ones);
     }
   };
-  Raw ra[CT::LOADS], rb[CT::LOADS];
-  load_unit(ra, 0);
-  load_unit(rb, min(1, ulast));
-  store_unit(ra, 0);
-  barrier();
-  for (int u = 0; u < nu; u += 2) {
-    load_unit(ra, min(u + 2, ulast));
-    compute(u);
-    store_unit(rb, 1);
-    barrier();
-    load_unit(rb, min(u + 3, ulast));
-    compute(u + 1);
+  if (uend > ubeg) {  // uniform; PART: the item's rows may all lie before the partition
+    Raw ra[CT::LOADS], rb[CT::LOADS];
+    load_unit(ra, ubeg);
+    load_unit(rb, min(ubeg + 1, ulast));
     store_unit(ra, 0);
     barrier();
+    for (int u = ubeg; u < uend; u += 2) {
+      load_unit(ra, min(u + 2, ulast));
+      compute(u, 0);
+      store_unit(rb, 1);
+      barrier();
+      load_unit(rb, min(u + 3, ulast));
+      compute(u + 1, 1);
+      store_unit(ra, 0);
+      barrier();
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the repeated loads past the last unit
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the repeated loads past the last unit
 
   // emit: lane (r, n) holds dimensions 16 j + 4 r + i of column 16 c + n, which is
   // (row j0 + col / G, head col % G)
 #pragma unroll
   for (int c = 0; c < NCB; ++c) {
-    const float ltot = cross_rows_sum(st[c].l);
+    const float l = st[c].lsum[0];
     // FP8: a stored V value stands for its E4M3 value times v_scale
-    const float inv = ltot > 0.f ? (F8 ? a.v_factor : 1.f) / ltot : 0.f;
+    const float inv = l > 0.f ? (F8 ? a.v_factor : 1.f) / l : 0.f;
     const int col = 16 * c + n;
     const int jr = j0 + col / G, hr = col % G;
-    if (jr < jend) {
-      const int64_t ob = ((int64_t)(q0 + jr) * a.num_q_heads + (int64_t)g * G + hr) * D;
+    if (jr >= jend) continue;
+    const int64_t rowh = (int64_t)(q0 + jr) * a.num_q_heads + (int64_t)g * G + hr;
+    if constexpr (PART) {
+      // partials of partition `part`: normalised output, max (natural log) and sum taken
+      // against the true max; a column with no key in the partition: max -inf, sum 0,
+      // output not written
+      const int64_t e = rowh * a.max_partitions + part;
+      if (l > 0.f) {
+        float* po = a.part_o + e * D;
+#pragma unroll
+        for (int j = 0; j < C::NJ; ++j)
+          *reinterpret_cast<f32x4_t*>(po + 16 * j + 4 * r) = st[c].acc[j] * inv;
+      }
+      if (r == 0) {
+        a.part_m[e] = l > 0.f ? st[c].mx * 0.69314718055994531f : -INFINITY;
+        a.part_l[e] = l > 0.f ? l * __builtin_amdgcn_exp2f(st[c].m - st[c].mx) : 0.f;
+      }
+    } else {
+      const int64_t ob = rowh * D;
 #pragma unroll
       for (int j = 0; j < C::NJ; ++j)
 #pragma unroll
@@ -259,8 +469,9 @@ constexpr int kMaxOrdered = 256;
 // sequence column blocks last to first (the longest causal ranges first), and the KV heads
 // of one (sequence, column block) consecutively.  With more than kMaxOrdered multi-row
 // sequences the items keep the sequence order instead, KV head slowest, numbered XCD-locally
-// so that each XCD works through mostly one KV head.
-template <int DT, int D, bool F8>
+// so that each XCD works through mostly one KV head.  PART: items are (sequence, column
+// block, partition) of at most one partition each, in sequence order, KV head slowest.
+template <int DT, int D, bool F8, bool PART, bool B8>
 __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(2))) void chunk_kernel(DecodeArgs a) {
   extern __shared__ __align__(16) char lds_raw[];
   char* lds_units = lds_raw;  // two unit buffers
@@ -272,10 +483,24 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(2))) void c
   const int G = a.num_q_heads / a.num_kv_heads;
   const int S = a.num_seqs;
   const int Hkv = a.num_kv_heads;
-  ChunkPlanIn pin{a.qsl, S, kItemCols / G, a.max_rows + 1};
+  ChunkPlanIn pin{a.qsl, a.context_lens, S, kItemCols / G, a.max_rows + 1,
+                  PART ? a.part_tokens : 0};
   build_chunk_plan(base, pin);
   const int64_t per_head = base[S];
   const int64_t total = per_head * Hkv;
+
+  if constexpr (PART) {
+    for (int64_t i = xcd_local_block(blockIdx.x, gridDim.x); i < total; i += gridDim.x) {
+      const int gh = (int)(i / per_head);
+      const int64_t k = i - (int64_t)gh * per_head;
+      const int s = find_seq(base, S, k, 1);
+      const int np = (a.context_lens[s] + a.part_tokens - 1) / a.part_tokens;
+      const int idx = (int)(k - base[s]);
+      chunk_item<DT, D, F8, true, B8>(a, s, gh, idx / np, idx % np, lds_units);
+      __syncthreads();  // the unit buffers are reused by the next item
+    }
+    return;
+  }
 
   // collect the multi-row sequences (any order), then rank them by prior keys (ties: index)
   if (threadIdx.x == 0) *count = 0;
@@ -325,35 +550,58 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(2))) void c
       const int nb = base[s + 1] - base[s];
       cb = nb - 1 - (int)(k - base[s]);
     }
-    chunk_item<DT, D, F8>(a, s, g, cb, lds_units);
+    chunk_item<DT, D, F8, false, B8>(a, s, g, cb, 0, lds_units);
     __syncthreads();  // the unit buffers are reused by the next item
   }
 }
 
-template <int DT, bool F8>
-static hipError_t launch_c(const DecodeArgs& a, int grid, size_t lds, hipStream_t st) {
+template <int DT, bool F8, bool PART, bool B8>
+static void launch_cb(const DecodeArgs& a, int grid, size_t lds, hipStream_t st) {
   if (a.head_dim == 64)
-    hipLaunchKernelGGL((chunk_kernel<DT, 64, F8>), dim3(grid), dim3(kWG), lds, st, a);
+    hipLaunchKernelGGL((chunk_kernel<DT, 64, F8, PART, B8>), dim3(grid), dim3(kWG), lds, st, a);
   else
-    hipLaunchKernelGGL((chunk_kernel<DT, 128, F8>), dim3(grid), dim3(kWG), lds, st, a);
+    hipLaunchKernelGGL((chunk_kernel<DT, 128, F8, PART, B8>), dim3(grid), dim3(kWG), lds, st, a);
+}
+
+template <int DT, bool F8, bool PART>
+static hipError_t launch_c(const DecodeArgs& a, int grid, size_t lds, hipStream_t st) {
+  if (a.b8)
+    launch_cb<DT, F8, PART, true>(a, grid, lds, st);
+  else
+    launch_cb<DT, F8, PART, false>(a, grid, lds, st);
   return hipGetLastError();
 }
 
-// dt: DT_F16 / DT_BF16 pools, or DT_FP8 / DT_FP8B (FP8 pools behind fp16 / bf16 queries)
+template <bool PART>
+static hipError_t launch_dt(int dt, const DecodeArgs& a, int grid, size_t lds, hipStream_t st) {
+  if (dt == DT_F16) return launch_c<DT_F16, false, PART>(a, grid, lds, st);
+  if (dt == DT_BF16) return launch_c<DT_BF16, false, PART>(a, grid, lds, st);
+  if (dt == DT_FP8) return launch_c<DT_F16, true, PART>(a, grid, lds, st);
+  return launch_c<DT_BF16, true, PART>(a, grid, lds, st);
+}
+
+// dt: DT_F16 / DT_BF16 pools, or DT_FP8 / DT_FP8B (FP8 pools behind fp16 / bf16 queries).
+// a.part_tokens > 0: the partition mode of pa_decode_partitioned (every sequence with more
+// than a.max_rows rows, one item per key partition).
 hipError_t launch_chunk(int dt, const DecodeArgs& a, int num_q_rows, hipStream_t st) {
+  const int rpi = kItemCols / (a.num_q_heads / a.num_kv_heads);
+  const size_t lds = (size_t)2 * (a.head_dim == 64 ? ChunkTile<64>::UNIT : ChunkTile<128>::UNIT) +
+                     (size_t)(a.num_seqs + 1 + 3 * kMaxOrdered + 2) * sizeof(int32_t);
+  if (a.part_tokens > 0) {
+    // at most (ceil(rows / rows_per_item) + num_seqs) column blocks x max_partitions items per
+    // KV head, walked with a grid stride by a grid of up to 4096 workgroups
+    const int64_t items = ((int64_t)(num_q_rows + rpi - 1) / rpi + a.num_seqs) *
+                          a.max_partitions * a.num_kv_heads;
+    const int64_t wgs = (std::min<int64_t>(items, 4096) + kXcds - 1) / kXcds * kXcds;
+    return launch_dt<true>(dt, a, (int)wgs, lds, st);
+  }
   // one workgroup per work item: at most ceil(rows / rows_per_item) + num_seqs items per KV
   // head; a multiple of the XCD count keeps the XCD-local numbering on
-  const int rpi = kItemCols / (a.num_q_heads / a.num_kv_heads);
   const int64_t items = ((int64_t)(num_q_rows + rpi - 1) / rpi + a.num_seqs) * a.num_kv_heads;
   const int64_t wgs = (items + kXcds - 1) / kXcds * kXcds;
   const int grid = (int)(wgs < (1 << 20) ? wgs : (1 << 20) / kXcds * kXcds);
-  const size_t lds = (size_t)2 * (a.head_dim == 64 ? ChunkTile<64>::UNIT : ChunkTile<128>::UNIT) +
-                     (size_t)(a.num_seqs + 1 + 3 * kMaxOrdered + 2) * sizeof(int32_t);
   if (grid <= 0) return hipSuccess;
-  if (dt == DT_F16) return launch_c<DT_F16, false>(a, grid, lds, st);
-  if (dt == DT_BF16) return launch_c<DT_BF16, false>(a, grid, lds, st);
-  if (dt == DT_FP8) return launch_c<DT_F16, true>(a, grid, lds, st);
-  return launch_c<DT_BF16, true>(a, grid, lds, st);
+  return launch_dt<false>(dt, a, grid, lds, st);
 }
 
 }  // namespace pa

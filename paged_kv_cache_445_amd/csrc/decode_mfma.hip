@@ -24,7 +24,7 @@ namespace pa {
 // column is one (row, query head) pair: column c is row qsl[s] + c / G, head g * G + c % G,
 // and the nr * G <= 16 columns of the sequence's nr rows are scored together.  Row j sits at
 // position ctx - nr + j and sees keys [0, ctx - nr + j].
-template <int DT, int D, bool MULTI, bool LEAN = false>
+template <int DT, int D, bool MULTI, bool LEAN, bool B8>
 __device__ void mfma_attend(const DecodeArgs& a, int s, int g, int u0, int u1, int ctx, int nr,
                             MfmaState<DT, D>& st) {
   using C = MfmaCfg<DT, D>;
@@ -61,7 +61,7 @@ __device__ void mfma_attend(const DecodeArgs& a, int s, int g, int u0, int u1, i
   for (int j = 0; j < C::NJ; ++j) st.acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   if constexpr (!MULTI) {
-    mfma_stream<DT, D>(a, s, g, u0, u1, ctx, [&](MfmaK<DT, D>& kb, MfmaV<DT, D>& vb, int u) {
+    mfma_stream<DT, D, B8>(a, s, g, u0, u1, ctx, [&](MfmaK<DT, D>& kb, MfmaV<DT, D>& vb, int u) {
       const int valid = ctx - u * kMfmaUnit;
       if (valid >= kMfmaUnit)
         mfma_unit<DT, D, false, false>(st, kb, vb, qb, a.scale_log2, kMfmaUnit - 1, kMfmaUnit);
@@ -86,9 +86,9 @@ __device__ void mfma_attend(const DecodeArgs& a, int s, int g, int u0, int u1, i
         mfma_pv<DT, D, true>(st, vb, p, ctx - t0);
     };
     if constexpr (LEAN) {
-      mfma_stream_lean<DT, D>(a, s, g, u0, u1, ctx, scores, pv);
+      mfma_stream_lean<DT, D, B8>(a, s, g, u0, u1, ctx, scores, pv);
     } else {
-      mfma_stream<DT, D>(a, s, g, u0, u1, ctx, [&](MfmaK<DT, D>& kb, MfmaV<DT, D>& vb, int u) {
+      mfma_stream<DT, D, B8>(a, s, g, u0, u1, ctx, [&](MfmaK<DT, D>& kb, MfmaV<DT, D>& vb, int u) {
         pv(vb, scores(kb, u), u);
       });
     }
@@ -177,7 +177,7 @@ __device__ void m_split_finish(const DecodeArgs& a, const MfmaState<DT, D>& st, 
 // buffer and is built for two waves per SIMD: with ~340 registers per wave the decode
 // kernel's waves keep the chunk kernel's off the CUs, and the two then run one after the
 // other (mixed chunked-prefill step: 788 -> 646 us).  Alone, the two-buffer stream is faster.
-template <int DT, int D, int MODE, bool MULTI, bool LEAN>
+template <int DT, int D, int MODE, bool MULTI, bool LEAN, bool B8>
 __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(LEAN ? 2 : 1))) void
 mfma_decode_kernel(DecodeArgs a) {
   extern __shared__ int32_t lds[];
@@ -193,7 +193,7 @@ mfma_decode_kernel(DecodeArgs a) {
   if constexpr (MODE == MODE_EVEN) {
     PlanIn pin{a.context_lens, a.qsl, S, kMfmaUnit, a.seg_extra, a.max_rows};
     build_plan(base, pin);
-    zero_empty_rows<DT>(pin, a.out, a.num_q_heads, D, w, W, a.out_f32);
+    zero_empty_rows<DT>(pin, a.out, a.num_q_heads, D, w, W, a.out_f32, a.nan_rows);
     // units: (sequence, group of kWavesPerWG KV heads, unit); wave i runs KV head i of each
     // group
     const int groups = (a.num_kv_heads + kWavesPerWG - 1) / kWavesPerWG;
@@ -223,7 +223,7 @@ mfma_decode_kernel(DecodeArgs a) {
             seen = counter_peek(cnt);  // consumed after the units
           }
           MfmaState<DT, D> st;
-          mfma_attend<DT, D, MULTI, LEAN>(a, s, g, u0, u1, ctx, nr, st);
+          mfma_attend<DT, D, MULTI, LEAN, B8>(a, s, g, u0, u1, ctx, nr, st);
           // the segment's first column in `out`; column c is row + c / G, head g * G + c % G
           const int64_t ob = ((int64_t)row * a.num_q_heads + (int64_t)g * G) * D;
           if (whole)
@@ -236,19 +236,14 @@ mfma_decode_kernel(DecodeArgs a) {
       }
     });
   } else {
+    // fixed partitions of the sequences with one query row (with query_start_loc, the
+    // others are the chunk kernel's)
     const int PU = a.partition_units;  // 32-token units per partition
     const int P = a.max_partitions;
-    PlanIn pin{a.context_lens, nullptr, S, PU * kMfmaUnit, 0, 1};
+    PlanIn pin{a.context_lens, a.qsl, S, PU * kMfmaUnit, 0, 1};
     build_plan(base, pin);
-    const int64_t nent = (int64_t)S * a.num_q_heads * P;
-    for (int64_t e = (int64_t)blockIdx.x * kWG + threadIdx.x; e < nent; e += (int64_t)gridDim.x * kWG) {
-      const int p = (int)(e % P);
-      const int s = (int)(e / ((int64_t)P * a.num_q_heads));
-      if (p >= base[s + 1] - base[s]) {
-        a.part_m[e] = -INFINITY;
-        a.part_l[e] = 0.f;
-      }
-    }
+    fill_past_partitions(a.context_lens, a.qsl, S, a.qsl ? a.qsl[S] : S, a.num_q_heads, P,
+                         PU * kMfmaUnit, a.part_m, a.part_l, w, W);
     const int64_t total = (int64_t)base[S] * segs;
     for (int64_t i = w; i < total; i += W) {
       const int s = find_seq(base, S, i, segs);
@@ -260,9 +255,10 @@ mfma_decode_kernel(DecodeArgs a) {
       const int nu = (ctx + kMfmaUnit - 1) / kMfmaUnit;
       const int u0 = p * PU, u1 = min(nu, u0 + PU);
       MfmaState<DT, D> st;
-      mfma_attend<DT, D, false>(a, s, g, u0, u1, ctx, 1, st);
+      mfma_attend<DT, D, false, false, B8>(a, s, g, u0, u1, ctx, 1, st);
       // tmp_out [row][h][P][D]: consecutive heads are P * D apart
-      const int64_t e0 = ((int64_t)s * a.num_q_heads + (int64_t)g * G) * P + p;
+      const int64_t row = a.qsl ? a.qsl[s] : s;
+      const int64_t e0 = (row * a.num_q_heads + (int64_t)g * G) * P + p;
       mfma_emit<DT, D>(st, G, a.part_o + e0 * D, a.part_m + e0, a.part_l + e0, (int64_t)P * D,
                        nullptr, 0, 16, 0, 0, false);
     }
@@ -270,13 +266,21 @@ mfma_decode_kernel(DecodeArgs a) {
   (void)lane;
 }
 
+template <int DT, int MODE, bool MULTI, bool LEAN, bool B8>
+static void launch_b(const DecodeArgs& a, int grid, size_t lds, hipStream_t st) {
+  if (a.head_dim == 64)
+    hipLaunchKernelGGL((mfma_decode_kernel<DT, 64, MODE, MULTI, LEAN, B8>), dim3(grid), dim3(kWG), lds, st, a);
+  else
+    hipLaunchKernelGGL((mfma_decode_kernel<DT, 128, MODE, MULTI, LEAN, B8>), dim3(grid), dim3(kWG), lds, st, a);
+}
+
 template <int DT, int MODE, bool MULTI, bool LEAN = false>
 static hipError_t launch_d(const DecodeArgs& a, int grid, hipStream_t st) {
   const size_t lds = (size_t)(a.num_seqs + 1) * sizeof(int32_t);
-  if (a.head_dim == 64)
-    hipLaunchKernelGGL((mfma_decode_kernel<DT, 64, MODE, MULTI, LEAN>), dim3(grid), dim3(kWG), lds, st, a);
+  if (a.b8)
+    launch_b<DT, MODE, MULTI, LEAN, true>(a, grid, lds, st);
   else
-    hipLaunchKernelGGL((mfma_decode_kernel<DT, 128, MODE, MULTI, LEAN>), dim3(grid), dim3(kWG), lds, st, a);
+    launch_b<DT, MODE, MULTI, LEAN, false>(a, grid, lds, st);
   return hipGetLastError();
 }
 
@@ -315,9 +319,9 @@ static int occ(int head_dim, int lds) {
   int nb = 0;
   hipError_t e;
   if (head_dim == 64)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, mfma_decode_kernel<DT, 64, MODE, false, false>, kWG, lds);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, mfma_decode_kernel<DT, 64, MODE, false, false, false>, kWG, lds);
   else
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, mfma_decode_kernel<DT, 128, MODE, false, false>, kWG, lds);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, mfma_decode_kernel<DT, 128, MODE, false, false, false>, kWG, lds);
   return e == hipSuccess && nb > 0 ? nb : 1;
 }
 

@@ -68,6 +68,39 @@ __device__ __forceinline__ void v_issue(VTile<DT, D>& t, const char* kt, const c
   for (int j = 0; j < C::NV; ++j) t.v[j] = ld16(vt + off + 1024 * j);
 }
 
+// 8-token blocks: tokens 0-7 of a 16-token tile come from block tile (ka, va), tokens 8-15
+// from (kb, vb), each an 8-token pool tile (K [D/X][8][X], V [D][8]).  Every lane loads the
+// same pieces as from a 16-token tile, from its own block: K load i, lane l: chunk
+// 4 i + l / 16 of token l % 16 (block (l / 8) % 2); V load j: the lane's dimension and token
+// group of the 16-token layout (FP8: a dimension's 8 bytes from each block).
+template <int DT, int D>
+__device__ __forceinline__ void v_issue_b8(VTile<DT, D>& t, const char* ka, const char* kb,
+                                           const char* va, const char* vb) {
+  using C = VCfg<DT, D>;
+  const int lane = lane_id();
+  const char* kt = (lane & 8) ? kb : ka;
+  const int koff = (lane >> 4) * 128 + (lane & 7) * 16;
+#pragma unroll
+  for (int i = 0; i < C::NK; ++i) t.k[i] = ld16(kt + koff + 512 * i);
+  if constexpr (C::E == 1) {
+#pragma unroll
+    for (int j = 0; j < C::NV; ++j) {
+      const uint2 x = *reinterpret_cast<const uint2*>(va + 512 * j + 8 * lane);
+      const uint2 y = *reinterpret_cast<const uint2*>(vb + 512 * j + 8 * lane);
+      t.v[j] = make_uint4(x.x, x.y, y.x, y.y);
+    }
+  } else if constexpr (C::E == 2) {
+    const char* vt = (lane & 1) ? vb : va;
+#pragma unroll
+    for (int j = 0; j < C::NV; ++j) t.v[j] = ld16(vt + 512 * j + (lane >> 1) * 16);
+  } else {
+    const char* vt = ((lane >> 1) & 1) ? vb : va;
+#pragma unroll
+    for (int j = 0; j < C::NV; ++j)
+      t.v[j] = ld16(vt + 512 * j + (lane >> 2) * 32 + (lane & 1) * 16);
+  }
+}
+
 // element k of a 16-byte V piece as float
 template <int DT>
 __device__ __forceinline__ float v_elem(const uint4& v, int k) {
@@ -198,24 +231,30 @@ struct VStart {
   VTile<DT, D> first;
 };
 
-// Block-table window of the first chunk of p (tiles t0 .. t0 + 127).
+// tiles per block-table window chunk
+template <bool B8>
+constexpr int kValuChunk = B8 ? 64 : 128;
+
+// Block-table window of the first chunk of p (tiles t0 .. t0 + 127, or 63 with 8-token blocks).
+template <bool B8>
 __device__ __forceinline__ void v_window(const DecodeArgs& a, const VPiece& p, int& win0,
                                          int& win1) {
-  const int lane = lane_id();
   const int32_t* bt_row = a.block_tables + (int64_t)p.s * a.max_blocks_per_seq;
-  const int c1 = min(p.t1, p.t0 + 128);
-  win0 = (p.t0 + lane < c1) ? tile_block(bt_row, p.t0 + lane, a.blk_shift) : 0;
-  win1 = (p.t0 + 64 + lane < c1) ? tile_block(bt_row, p.t0 + 64 + lane, a.blk_shift) : 0;
+  load_window<B8>(bt_row, p.t0, min(p.t1, p.t0 + kValuChunk<B8>), p.ctx, a.blk_shift, win0, win1);
 }
 
-template <int DT, int D>
+// a pool tile of one KV head: 16 tokens, or 8 with 8-token blocks
+template <int DT, int D, bool B8>
+constexpr int64_t kPoolTile = B8 ? VCfg<DT, D>::TILE / 2 : VCfg<DT, D>::TILE;
+
+template <int DT, int D, bool B8>
 __device__ __forceinline__ const char* v_head_base(const void* pool, const DecodeArgs& a, int h) {
   const int64_t kvh = h / (a.num_q_heads / a.num_kv_heads);
-  return reinterpret_cast<const char*>(pool) + kvh * VCfg<DT, D>::TILE;
+  return reinterpret_cast<const char*>(pool) + kvh * kPoolTile<DT, D, B8>;
 }
 
 // Issue the query and first-step loads of p (vs.win0 / win1 already hold its window).
-template <int DT, int D, int HPW>
+template <int DT, int D, int HPW, bool B8>
 __device__ __forceinline__ void v_start(const DecodeArgs& a, const VPiece& p,
                                         VStart<DT, D, HPW>& vs) {
   using C = VCfg<DT, D>;
@@ -232,10 +271,17 @@ __device__ __forceinline__ void v_start(const DecodeArgs& a, const VPiece& p,
       for (int c = 0; c < C::NQC; ++c)
         vs.q[j][C::NQC * i + c] = ld16(qp + C::X * C::QE * (4 * i + (lane >> 4)) + 16 * c);
   }
-  const int64_t blk = readlane(vs.win0, 0);
-  const int64_t off = blk * a.num_kv_heads * C::TILE;
-  v_issue<DT, D>(vs.first, v_head_base<DT, D>(a.k_cache, a, p.h0) + off,
-                 v_head_base<DT, D>(a.v_cache, a, p.h0) + off, 16 * lane);
+  const int64_t stride = a.num_kv_heads * kPoolTile<DT, D, B8>;
+  const char* kh = v_head_base<DT, D, B8>(a.k_cache, a, p.h0);
+  const char* vh = v_head_base<DT, D, B8>(a.v_cache, a, p.h0);
+  if constexpr (B8) {
+    const int64_t ba = readlane(vs.win0, 0), bb = readlane(vs.win0, 1);
+    v_issue_b8<DT, D>(vs.first, kh + ba * stride, kh + bb * stride, vh + ba * stride,
+                      vh + bb * stride);
+  } else {
+    const int64_t off = readlane(vs.win0, 0) * stride;
+    v_issue<DT, D>(vs.first, kh + off, vh + off, 16 * lane);
+  }
 }
 
 // Attention of piece p, whose start loads vs are in flight.  The tiles are walked in chunks
@@ -243,7 +289,7 @@ __device__ __forceinline__ void v_start(const DecodeArgs& a, const VPiece& p,
 // loop (the first chunk's come with vs), so the loop itself only waits for tile loads.  A
 // step is one tile of one head; the loads of the next step are in flight while a step is
 // computed.
-template <int DT, int D, int HPW>
+template <int DT, int D, int HPW, bool B8>
 __device__ void valu_run(const DecodeArgs& a, VPiece p, VStart<DT, D, HPW>& vs,
                          VState<DT, D> (&st)[HPW], float* pw) {
   using C = VCfg<DT, D>;
@@ -259,22 +305,31 @@ __device__ void valu_run(const DecodeArgs& a, VPiece p, VStart<DT, D, HPW>& vs,
   const char* vc[HPW];
 #pragma unroll
   for (int j = 0; j < HPW; ++j) {
-    kc[j] = v_head_base<DT, D>(a.k_cache, a, p.h0 + 4 * j);
-    vc[j] = v_head_base<DT, D>(a.v_cache, a, p.h0 + 4 * j);
+    kc[j] = v_head_base<DT, D, B8>(a.k_cache, a, p.h0 + 4 * j);
+    vc[j] = v_head_base<DT, D, B8>(a.v_cache, a, p.h0 + 4 * j);
     st[j].m = -INFINITY;
     st[j].l = 0.f;
 #pragma unroll
     for (int e = 0; e < C::NV; ++e) st[j].acc[e] = 0.f;
   }
-  const int64_t blk_stride = (int64_t)a.num_kv_heads * C::TILE;
+  const int64_t blk_stride = (int64_t)a.num_kv_heads * kPoolTile<DT, D, B8>;
   const int32_t* bt_row = a.block_tables + (int64_t)p.s * a.max_blocks_per_seq;
+  constexpr int CH = kValuChunk<B8>;
 
   // one chunk [c0, c1); FIRST: its first step is already in flight in vs.first
   auto chunk = [&](int c0, int c1, int win0, int win1, auto first) {
     auto issue = [&](VTile<DT, D>& t, int tt, int j) {
       const int idx = tt - c0;
-      const int64_t blk = idx < 64 ? readlane(win0, idx) : readlane(win1, idx - 64);
-      v_issue<DT, D>(t, kc[j] + blk * blk_stride, vc[j] + blk * blk_stride, off);
+      if constexpr (B8) {
+        const int e = 2 * idx;  // blocks e and e + 1 (e even: both in one register)
+        const int64_t ba = e < 64 ? readlane(win0, e) : readlane(win1, e - 64);
+        const int64_t bb = e < 64 ? readlane(win0, e + 1) : readlane(win1, e - 63);
+        v_issue_b8<DT, D>(t, kc[j] + ba * blk_stride, kc[j] + bb * blk_stride,
+                          vc[j] + ba * blk_stride, vc[j] + bb * blk_stride);
+      } else {
+        const int64_t blk = idx < 64 ? readlane(win0, idx) : readlane(win1, idx - 64);
+        v_issue<DT, D>(t, kc[j] + blk * blk_stride, vc[j] + blk * blk_stride, off);
+      }
     };
     auto step = [&](VTile<DT, D>& t, int tt, int j) {
       const int valid = p.ctx - tt * kBlock;
@@ -327,13 +382,14 @@ __device__ void valu_run(const DecodeArgs& a, VPiece p, VStart<DT, D, HPW>& vs,
       });
     }
   };
-  chunk(p.t0, min(p.t1, p.t0 + 128), vs.win0, vs.win1, std::true_type{});
-  for (int c0 = p.t0 + 128; c0 < p.t1; c0 += 128) {
-    const int c1 = min(p.t1, c0 + 128);
-    const int win0 = (c0 + lane < c1) ? tile_block(bt_row, c0 + lane, a.blk_shift) : 0;
-    const int win1 = (c0 + 64 + lane < c1) ? tile_block(bt_row, c0 + 64 + lane, a.blk_shift) : 0;
+  chunk(p.t0, min(p.t1, p.t0 + CH), vs.win0, vs.win1, std::true_type{});
+  for (int c0 = p.t0 + CH; c0 < p.t1; c0 += CH) {
+    const int c1 = min(p.t1, c0 + CH);
+    int win0, win1;
+    load_window<B8>(bt_row, c0, c1, p.ctx, a.blk_shift, win0, win1);
     chunk(c0, c1, win0, win1, std::false_type{});
   }
+  (void)lane;
 }
 
 // Finish a piece: combine the lanes of each dimension row and the per-token sums; returns
@@ -441,7 +497,7 @@ __device__ void v_split_finish(const DecodeArgs& a, const VState<DT, D> (&st)[HP
   counter_reset(cnt);
 }
 
-template <int DT, int D, int MODE, int HPW>
+template <int DT, int D, int MODE, int HPW, bool B8>
 __global__ __launch_bounds__(kWG) void valu_decode_kernel(DecodeArgs a) {
   // LDS: one 16-float weight slot per wave (first, for 16-byte alignment), then the plan
   // (S + 1 ints)
@@ -457,7 +513,7 @@ __global__ __launch_bounds__(kWG) void valu_decode_kernel(DecodeArgs a) {
   if constexpr (MODE == MODE_EVEN) {
     PlanIn pin{a.context_lens, a.qsl, S, kValuUnit, a.seg_extra, 1};
     build_plan(base, pin);
-    zero_empty_rows<DT>(pin, a.out, a.num_q_heads, D, w, W, a.out_f32);
+    zero_empty_rows<DT>(pin, a.out, a.num_q_heads, D, w, W, a.out_f32, a.nan_rows);
     // units: (sequence, group of 4 HPW heads, tile); wave i runs heads i + 4 j of each group
     constexpr int GH = kWavesPerWG * HPW;
     const int groups = (a.num_q_heads + GH - 1) / GH;
@@ -489,8 +545,8 @@ __global__ __launch_bounds__(kWG) void valu_decode_kernel(DecodeArgs a) {
       VStart<DT, D, HPW> vs;
       Unit cur = at(lo);
       if (cur.run) {
-        v_window(a, cur.p, vs.win0, vs.win1);
-        v_start<DT, D, HPW>(a, cur.p, vs);
+        v_window<B8>(a, cur.p, vs.win0, vs.win1);
+        v_start<DT, D, HPW, B8>(a, cur.p, vs);
       }
       for (;;) {
         const bool more = cur.end < hi;
@@ -498,12 +554,12 @@ __global__ __launch_bounds__(kWG) void valu_decode_kernel(DecodeArgs a) {
         if (more) nxt = at(cur.end);
         const bool nrun = more && nxt.run;
         int nw0 = 0, nw1 = 0;  // the next piece's window, read before this piece's tiles
-        if (nrun) v_window(a, nxt.p, nw0, nw1);
+        if (nrun) v_window<B8>(a, nxt.p, nw0, nw1);
         auto start_next = [&] {
           if (nrun) {
             vs.win0 = nw0;
             vs.win1 = nw1;
-            v_start<DT, D, HPW>(a, nxt.p, vs);
+            v_start<DT, D, HPW, B8>(a, nxt.p, vs);
           }
         };
         if (cur.run) {
@@ -519,7 +575,7 @@ __global__ __launch_bounds__(kWG) void valu_decode_kernel(DecodeArgs a) {
             seen = counter_peek(cnt);  // consumed after the tiles
           }
           VState<DT, D> st[HPW];
-          valu_run<DT, D, HPW>(a, cur.p, vs, st, pw);
+          valu_run<DT, D, HPW, B8>(a, cur.p, vs, st, pw);
           float l[HPW];
 #pragma unroll
           for (int j = 0; j < HPW; ++j) l[j] = v_finish<DT, D>(st[j], a.v_factor);
@@ -544,21 +600,14 @@ __global__ __launch_bounds__(kWG) void valu_decode_kernel(DecodeArgs a) {
       }
     });
   } else {
-    // fixed partitions; rows are sequences (no query_start_loc in this mode)
+    // fixed partitions of the sequences with one query row (with query_start_loc, the
+    // others are the chunk kernel's)
     const int PU = a.partition_units;  // tiles per partition
     const int P = a.max_partitions;
-    PlanIn pin{a.context_lens, nullptr, S, PU * kBlock, 0, 1};
+    PlanIn pin{a.context_lens, a.qsl, S, PU * kBlock, 0, 1};
     build_plan(base, pin);
-    // partitions past the context: max_logits = -inf, exp_sums = 0
-    const int64_t nent = (int64_t)S * a.num_q_heads * P;
-    for (int64_t e = (int64_t)blockIdx.x * kWG + threadIdx.x; e < nent; e += (int64_t)gridDim.x * kWG) {
-      const int p = (int)(e % P);
-      const int s = (int)(e / ((int64_t)P * a.num_q_heads));
-      if (p >= base[s + 1] - base[s]) {
-        a.part_m[e] = -INFINITY;
-        a.part_l[e] = 0.f;
-      }
-    }
+    fill_past_partitions(a.context_lens, a.qsl, S, a.qsl ? a.qsl[S] : S, a.num_q_heads, P,
+                         PU * kBlock, a.part_m, a.part_l, w, W);
     const int segs = a.num_q_heads;
     const int64_t total = (int64_t)base[S] * segs;
     for (int64_t i = w; i < total; i += W) {
@@ -573,12 +622,13 @@ __global__ __launch_bounds__(kWG) void valu_decode_kernel(DecodeArgs a) {
       VState<DT, D> st[1];
       const VPiece pc{s, h, t0, t1, ctx};
       VStart<DT, D, 1> vs;
-      v_window(a, pc, vs.win0, vs.win1);
-      v_start<DT, D, 1>(a, pc, vs);
-      valu_run<DT, D, 1>(a, pc, vs, st, pw);
+      v_window<B8>(a, pc, vs.win0, vs.win1);
+      v_start<DT, D, 1, B8>(a, pc, vs);
+      valu_run<DT, D, 1, B8>(a, pc, vs, st, pw);
       const float l = v_finish<DT, D>(st[0], a.v_factor);
       const float inv = 1.f / l;
-      const int64_t e = ((int64_t)s * a.num_q_heads + h) * P + p;
+      const int64_t row = a.qsl ? a.qsl[s] : s;
+      const int64_t e = (row * a.num_q_heads + h) * P + p;
       v_store_f32<DT, D>(st[0], inv, a.part_o + e * D);
       if (lane == 0) {
         a.part_m[e] = st[0].m * 0.69314718055994531f;
@@ -592,13 +642,15 @@ static size_t valu_lds_bytes(int num_seqs) {
   return (size_t)(num_seqs + 1) * sizeof(int32_t) + kWavesPerWG * 16 * sizeof(float);
 }
 
-template <int DT, int D, int MODE, int HPW>
+template <int DT, int D, int MODE, int HPW, bool B8 = false>
 static void launch_k(const DecodeArgs& a, int grid, size_t lds, hipStream_t st) {
-  hipLaunchKernelGGL((valu_decode_kernel<DT, D, MODE, HPW>), dim3(grid), dim3(kWG), lds, st, a);
+  hipLaunchKernelGGL((valu_decode_kernel<DT, D, MODE, HPW, B8>), dim3(grid), dim3(kWG), lds, st, a);
 }
 
 template <int DT, int D, int MODE>
 static void launch_hpw(const DecodeArgs& a, int grid, size_t lds, hipStream_t st) {
+  // 8-token blocks: one head per wave
+  if (a.b8) return launch_k<DT, D, MODE, 1, true>(a, grid, lds, st);
   if constexpr (MODE == MODE_EVEN) {
     // fp32 queries fill twice the registers: at most two heads per wave; FP8 widens to
     // fp32 in registers: at most four
@@ -638,15 +690,16 @@ hipError_t launch_valu_decode(int dt, int mode, const DecodeArgs& a, int grid, h
   return launch_d<DT_BF16, MODE_PARTITION>(a, grid, st);
 }
 
-// resident workgroups per CU of the kernel that `hpw` selects
+// resident workgroups per CU of the kernel that `hpw` selects (the 8-token-block variants
+// are built for the same occupancy)
 template <int DT, int MODE, int HPW>
 static int occ_k(int head_dim, int lds) {
   int n = 0;
   hipError_t e;
   if (head_dim == 64)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, valu_decode_kernel<DT, 64, MODE, HPW>, kWG, lds);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, valu_decode_kernel<DT, 64, MODE, HPW, false>, kWG, lds);
   else
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, valu_decode_kernel<DT, 128, MODE, HPW>, kWG, lds);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, valu_decode_kernel<DT, 128, MODE, HPW, false>, kWG, lds);
   return e == hipSuccess && n > 0 ? n : 1;
 }
 

@@ -40,9 +40,12 @@ pa_status check_geom(const pa_geom* g) {
   }
   if (!dtype_ok(g->q_dtype) || !dtype_ok(g->out_dtype)) return PA_ERR_UNSUPPORTED;
   if (g->out_dtype != g->q_dtype && g->out_dtype != PA_F32) return PA_ERR_UNSUPPORTED;
-  if (g->block_size != 16 && g->block_size != 32 && g->block_size != 64) return PA_ERR_UNSUPPORTED;
-  // the kernels number 16-token sub-blocks in int32
-  if ((int64_t)g->num_blocks * (g->block_size / pa::kBlock) > 0x7fffffffLL) return PA_ERR_SHAPE;
+  if (g->block_size != 8 && g->block_size != 16 && g->block_size != 32 && g->block_size != 64)
+    return PA_ERR_UNSUPPORTED;
+  // the kernels number pool tiles (16-token sub-blocks, or 8-token blocks) in int32
+  if ((int64_t)g->num_blocks * (g->block_size > 16 ? g->block_size / pa::kBlock : 1) >
+      0x7fffffffLL)
+    return PA_ERR_SHAPE;
   if (g->head_dim != 64 && g->head_dim != 128) return PA_ERR_UNSUPPORTED;
   if (g->num_q_heads / g->num_kv_heads > 16) return PA_ERR_UNSUPPORTED;
   if (g->num_seqs > kMaxSeqs) return PA_ERR_UNSUPPORTED;
@@ -55,8 +58,11 @@ int kdt(const pa_geom* g) {
   return g->q_dtype == PA_BF16 ? pa::DT_FP8B : pa::DT_FP8;
 }
 
-// log2 of the 16-token sub-blocks per block
+// log2 of the 16-token sub-blocks per block (blocks of 16 tokens and up)
 int blk_shift(const pa_geom* g) { return g->block_size == 64 ? 2 : g->block_size == 32 ? 1 : 0; }
+
+// 8-token blocks: the kernels pair two blocks into each 16-token tile
+int b8(const pa_geom* g) { return g->block_size == 8 ? 1 : 0; }
 
 int current_device() {
   int dev = 0;
@@ -164,6 +170,7 @@ int heads_per_wave(const pa_geom* g) {
     const char* s = getenv("PA_DECODE_HPW");
     return s ? atoi(s) : 0;
   }();
+  if (b8(g)) return 1;  // 8-token blocks: one head per wave
   const int cap = g->kv_dtype == PA_F32 ? 2 : g->kv_dtype == PA_FP8_E4M3 ? 4 : 8;
   const int o = wg_per_cu_override();
   const int64_t workgroups = (int64_t)cu_count() * (o > 0 ? o : kEvenWgPerCu[0]);
@@ -338,7 +345,7 @@ pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_cache
   const int64_t threads = num_tokens * g->num_kv_heads * (g->head_dim / X + g->head_dim);
   if ((threads + 255) / 256 > 0x7fffffffLL) return PA_ERR_SHAPE;
   pa::ReshapeArgs a{key, value, k_cache, v_cache, slot_mapping, num_tokens, g->num_kv_heads,
-                    g->head_dim, g->k_scale, g->v_scale};
+                    g->head_dim, g->k_scale, g->v_scale, b8(g) ? 3 : 4};
   return hip_status(pa::launch_reshape(kdt(g), a, (hipStream_t)stream));
 }
 
@@ -523,6 +530,10 @@ pa_status decode_impl(void* out, const void* q, const void* k_cache, const void*
   a.max_rows = rt.max_rows;
   a.cols = rt.cols;
   a.blk_shift = blk_shift(g);
+  a.b8 = b8(g);
+  // no multi-row kernel runs: the rows of a sequence with more rows than max_query_len
+  // promised are written NaN
+  a.nan_rows = query_start_loc && max_len <= rt.max_rows ? 1 : 0;
 
   auto decode = [&] {
     return rt.path ? pa::launch_mfma_decode(kdt(g), pa::MODE_EVEN, a, grid, st)
@@ -561,26 +572,32 @@ extern "C" {
 pa_status pa_decode_partitioned(float* tmp_out, float* max_logits, float* exp_sums,
                                 const void* q, const void* k_cache, const void* v_cache,
                                 const int32_t* block_tables, const int32_t* context_lens,
-                                int32_t num_q_rows, float scale, int32_t partition_size,
-                                int32_t max_partitions, const pa_geom* g, void* stream) {
+                                const int32_t* query_start_loc, int32_t num_q_rows,
+                                float scale, int32_t partition_size, int32_t max_partitions,
+                                const pa_geom* g, void* stream) {
   const pa_status gs = check_geom(g);
   if (gs != PA_OK) return gs;
-  if (num_q_rows != g->num_seqs) return PA_ERR_SHAPE;
+  if (num_q_rows < 0) return PA_ERR_SHAPE;
+  if (!query_start_loc && num_q_rows != g->num_seqs) return PA_ERR_SHAPE;
   if (partition_size <= 0 || partition_size % pa::kMfmaUnit || max_partitions <= 0)
     return PA_ERR_SHAPE;
   if ((int64_t)max_partitions * partition_size < (int64_t)g->max_blocks_per_seq * g->block_size)
     return PA_ERR_SHAPE;
-  if (g->num_seqs == 0) return PA_OK;
+  if (g->num_seqs == 0 || num_q_rows == 0) return PA_OK;
   if (!tmp_out || !max_logits || !exp_sums || !q || !k_cache || !v_cache || !block_tables ||
       !context_lens)
     return PA_ERR_NULL;
   if (!std::isfinite(scale)) return PA_ERR_SHAPE;
+  const int G = g->num_q_heads / g->num_kv_heads;
+  if (query_start_loc && (g->kv_dtype == PA_F32 || 16 % G != 0)) return PA_ERR_UNSUPPORTED;
+  hipStream_t st = (hipStream_t)stream;
   pa::DecodeArgs a{};
   a.q = q;
   a.k_cache = k_cache;
   a.v_cache = v_cache;
   a.block_tables = block_tables;
   a.context_lens = context_lens;
+  a.qsl = query_start_loc;
   a.part_o = tmp_out;
   a.part_m = max_logits;
   a.part_l = exp_sums;
@@ -600,10 +617,17 @@ pa_status pa_decode_partitioned(float* tmp_out, float* max_logits, float* exp_su
   a.max_rows = 1;
   a.cols = g->num_q_heads / g->num_kv_heads;
   a.blk_shift = blk_shift(g);
+  a.b8 = b8(g);
   const int grid = split_grid(g, pa::MODE_PARTITION, mf ? 1 : 0);
-  hipError_t e = mf ? pa::launch_mfma_decode(kdt(g), pa::MODE_PARTITION, a, grid, (hipStream_t)stream)
-                    : pa::launch_valu_decode(kdt(g), pa::MODE_PARTITION, a, grid, (hipStream_t)stream);
-  return hip_status(e);
+  // sequences with one row: the decode kernel, which also marks every row's partitions past
+  // its context
+  hipError_t e = mf ? pa::launch_mfma_decode(kdt(g), pa::MODE_PARTITION, a, grid, st)
+                    : pa::launch_valu_decode(kdt(g), pa::MODE_PARTITION, a, grid, st);
+  if (e != hipSuccess || !query_start_loc) return hip_status(e);
+  // sequences with several rows: the chunk kernel, one item per (column block, partition)
+  a.part_tokens = partition_size;
+  a.max_rows = 1;
+  return hip_status(pa::launch_chunk(kdt(g), a, num_q_rows, st));
 }
 
 pa_status pa_decode_reduce(void* out, const float* tmp_out, const float* max_logits,

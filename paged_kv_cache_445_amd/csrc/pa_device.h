@@ -42,6 +42,26 @@ __device__ __forceinline__ int32_t tile_block(const int32_t* bt_row, int j, int 
   return (bt_row[j >> shift] << shift) | (j & ((1 << shift) - 1));
 }
 
+// Block-table window of a sequence's 16-token tiles [c0, c1), c1 - c0 <= (B8 ? 64 : 128),
+// held one entry per lane in two registers.  16-token tiles: w0 = entry for tile c0 + lane,
+// w1 = tile c0 + 64 + lane (sub-block ids, tile_block).  8-token blocks (B8): tile j is blocks
+// 2 j and 2 j + 1, so w0 / w1 hold the block ids of entries 2 c0 + lane / 2 c0 + 64 + lane;
+// entries at or past the context's last block (ceil(ctx / 8)) are never read and hold 0
+// (their tokens are masked).  Outside the window's range the registers hold 0.
+template <bool B8>
+__device__ __forceinline__ void load_window(const int32_t* bt_row, int c0, int c1, int ctx,
+                                            int shift, int& w0, int& w1) {
+  const int lane = __lane_id();
+  if constexpr (B8) {
+    const int e0 = 2 * c0, eend = min(2 * c1, (ctx + 7) >> 3);
+    w0 = e0 + lane < eend ? bt_row[e0 + lane] : 0;
+    w1 = e0 + 64 + lane < eend ? bt_row[e0 + 64 + lane] : 0;
+  } else {
+    w0 = (c0 + lane < c1) ? tile_block(bt_row, c0 + lane, shift) : 0;
+    w1 = (c0 + 64 + lane < c1) ? tile_block(bt_row, c0 + 64 + lane, shift) : 0;
+  }
+}
+
 // ---------------------------------------------------------------- 16-byte global loads
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
@@ -237,17 +257,57 @@ __device__ __forceinline__ int32_t seq_units(const PlanIn& p, int s) {
   return ctx > 0 ? (ctx + p.unit_tokens - 1) / p.unit_tokens + p.extra : 0;
 }
 
-// Decode rows (sequences with one query row) whose context is empty get a zero output;
-// wave w of W handles sequences w, w + W, ...
+// Decode rows (sequences with one query row) whose context is empty get a zero output.
+// nan_rows: no kernel of the call takes sequences with more than p.max_rows rows, whose rows
+// are written NaN instead of being left as they were.  Wave w of W handles sequences w,
+// w + W, ...
 template <int DT>
 __device__ void zero_empty_rows(const PlanIn& p, void* out, int Hq, int D, int64_t w, int64_t W,
-                                bool out_f32) {
+                                bool out_f32, bool nan_rows) {
   for (int64_t s = w; s < p.num_seqs; s += W) {
     const int32_t rows = p.qsl ? p.qsl[s + 1] - p.qsl[s] : 1;
-    if (rows != 1 || p.context_lens[s] > 0) continue;
+    const bool empty = rows == 1 && p.context_lens[s] <= 0;
+    const bool lost = nan_rows && rows > p.max_rows;
+    if (!empty && !lost) continue;
     const int64_t row = p.qsl ? p.qsl[s] : s;
-    for (int e = __lane_id(); e < Hq * D; e += kWave)
-      store_out<DT>(out, row * Hq * D + e, 0.f, out_f32);
+    const float v = empty ? 0.f : __builtin_nanf("");
+    for (int64_t e = __lane_id(); e < (int64_t)rows * Hq * D; e += kWave)
+      store_out<DT>(out, row * Hq * D + e, v, out_f32);
+  }
+}
+
+// pa_decode_partitioned: the partitions of a row that lie past its sequence's context get
+// max_logits = -inf and exp_sums = 0 (the row's partitions [0, ceil(ctx / part_tokens)) are
+// written by whichever kernel computes the row).  Rows are (row, head, partition) blocks of
+// Hq * P entries; wave w of W handles rows w, w + W, ... of the num_rows rows, each row's
+// sequence found by a binary search over qsl (NULL: row r is sequence r).
+__device__ inline void fill_past_partitions(const int32_t* context_lens, const int32_t* qsl,
+                                            int S, int64_t num_rows, int Hq, int P,
+                                            int part_tokens, float* pm, float* pl, int64_t w,
+                                            int64_t W) {
+  for (int64_t row = w; row < num_rows; row += W) {
+    int s = (int)row;
+    if (qsl) {  // the largest s with qsl[s] <= row
+      int lo = 0, hi = S - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (qsl[mid] <= row)
+          lo = mid;
+        else
+          hi = mid - 1;
+      }
+      s = lo;
+    }
+    const int np = (context_lens[s] + part_tokens - 1) / part_tokens;
+    if (np >= P) continue;
+    float* m = pm + row * Hq * P;
+    float* l = pl + row * Hq * P;
+    for (int e = __lane_id(); e < Hq * P; e += kWave) {
+      if (e % P >= np) {
+        m[e] = -INFINITY;
+        l[e] = 0.f;
+      }
+    }
   }
 }
 

@@ -57,6 +57,11 @@ struct DecodeArgs {
   float v_factor;           // DT_FP8: the outputs' factor (v_scale)
   int32_t blk_shift;        // log2(block_size / 16): table entries name 2^blk_shift sub-blocks
   int32_t lean;             // MODE_EVEN, matrix-core path with several rows: the lean stream
+  int32_t part_tokens;      // chunk kernel: > 0 for pa_decode_partitioned's key partitions
+  int32_t nan_rows;         // MODE_EVEN with qsl and no chunk kernel: rows of sequences with
+                            // more than max_rows rows are written NaN
+  int32_t b8;               // 8-token blocks: a 16-token tile is two blocks (table entries
+                            // 2 j and 2 j + 1), each a pool tile of 8 tokens
 };
 
 struct ReshapeArgs {
@@ -70,6 +75,7 @@ struct ReshapeArgs {
   int32_t head_dim;
   float k_scale;  // DT_FP8: stored K = e4m3(key / k_scale)
   float v_scale;  // DT_FP8: stored V = e4m3(value / v_scale)
+  int32_t tile_shift;  // log2 of the tokens of one pool tile: 3 (8-token blocks) or 4
 };
 
 struct CopyBlocksArgs {

@@ -125,22 +125,6 @@ struct MfmaLaneOffsets {
   __device__ __forceinline__ int voff(int j) const { return v + 256 * MfmaCfg<DT, D>::E * j; }
 };
 
-template <int DT, int D>
-__device__ __forceinline__ void mfma_load(MfmaK<DT, D>& kb, MfmaV<DT, D>& vb, const char* k0,
-                                          const char* k1, const char* v0, const char* v1,
-                                          const MfmaLaneOffsets<DT, D>& o) {
-  using C = MfmaCfg<DT, D>;
-#pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const char* kt = o.kt[b] ? k1 : k0;
-#pragma unroll
-    for (int kk = 0; kk < C::NKK; ++kk) kb[b][kk] = ld_raw<DT>(kt + o.koff(b, kk));
-  }
-  const char* vt = o.vt ? v1 : v0;
-#pragma unroll
-  for (int j = 0; j < C::NJ; ++j) vb[j] = ld_raw<DT>(vt + o.voff(j));
-}
-
 // The two halves of one unit for one 16-column block.  mfma_scores computes S^T = K . Q^T,
 // masks tokens 8r + k > lim (MASK; lim: last visible unit token of this lane's query column,
 // may differ per column), updates the running max and sum and returns the block's weights P
@@ -284,37 +268,126 @@ __device__ __forceinline__ MfmaLaneOffsets<DT, D> mfma_offsets() {
   return o;
 }
 
+// Addressing of the 32-token units of KV head g of sequence s (context ctx): the block-table
+// window of a chunk of units and the operand loads of one unit (see the layout notes at the
+// top of this file).
+//  - 16-token tiles: a unit is tiles 2 u and 2 u + 1; the window holds one tile per lane
+//    (chunks of 64 units) and every lane reads its operands from one of the two tiles, whose
+//    ids reach the scalar unit by readlane.  A unit whose second tile lies past the context
+//    reads its first tile again (all of its tokens are masked).
+//  - 8-token blocks (B8): a unit is blocks 4 u .. 4 u + 3; the window holds one block per
+//    lane (chunks of 32 units).  Lane (r, n) reads its K operand (unit token
+//    8 (n / 4) + 4 b + n % 4) from block n / 4 and its V operand (tokens 8 r .. 8 r + 7) from
+//    block r, each lane fetching its block id from the window with a lane shuffle.  Entries
+//    past the context's last block hold block 0 (masked).
+template <int DT, int D, bool B8>
+struct MfmaUnits {
+  using C = MfmaCfg<DT, D>;
+  static constexpr int CHUNK = B8 ? 32 : 64;              // units per window
+  static constexpr int64_t PTILE = B8 ? C::TILE / 2 : C::TILE;  // one pool tile of a KV head
+  const char* kc;
+  const char* vc;
+  const int32_t* bt_row;
+  int64_t blk_stride;
+  int ctx, nblk, shift;
+  MfmaLaneOffsets<DT, D> o;
+  int k8[2], v8;  // B8: this lane's offsets inside an 8-token tile (piece kk = 0, j = 0)
+  int c0 = 0;
+  int win0 = 0, win1 = 0;
+
+  __device__ __forceinline__ MfmaUnits(const DecodeArgs& a, int s, int g, int ctx_) {
+    kc = reinterpret_cast<const char*>(a.k_cache) + (int64_t)g * PTILE;
+    vc = reinterpret_cast<const char*>(a.v_cache) + (int64_t)g * PTILE;
+    bt_row = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+    blk_stride = (int64_t)a.num_kv_heads * PTILE;
+    ctx = ctx_;
+    shift = a.blk_shift;
+    nblk = B8 ? (ctx + 7) >> 3 : (ctx + kBlock - 1) / kBlock;
+    o = mfma_offsets<DT, D>();
+    const int lane = lane_id();
+    const int r = lane >> 4, n = lane & 15;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int t8 = 4 * b + (n & 3);  // token inside block n / 4
+      k8[b] = C::E == 2 ? 128 * r + 16 * t8 : 128 * (r >> 1) + 16 * t8 + 8 * (r & 1);
+    }
+    v8 = C::E == 2 ? 16 * n : 8 * n;
+  }
+  // the window of units [c0_, c1)
+  __device__ __forceinline__ void window(int c0_, int c1) {
+    c0 = c0_;
+    const int lane = lane_id();
+    if constexpr (B8) {
+      const int e0 = 4 * c0, eend = min(nblk, 4 * c1);
+      win0 = e0 + lane < eend ? bt_row[e0 + lane] : 0;
+      win1 = e0 + 64 + lane < eend ? bt_row[e0 + 64 + lane] : 0;
+    } else {
+      const int b0 = 2 * c0, bend = min(nblk, 2 * c1);
+      win0 = (b0 + lane < bend) ? tile_block(bt_row, b0 + lane, shift) : 0;
+      win1 = (b0 + 64 + lane < bend) ? tile_block(bt_row, b0 + 64 + lane, shift) : 0;
+    }
+  }
+  // B8: window entry e (per lane, e < 128)
+  __device__ __forceinline__ int64_t entry(int e) const {
+    const int x = __shfl(win0, e & 63, kWave), y = __shfl(win1, e & 63, kWave);
+    return e < 64 ? x : y;
+  }
+  // 16-token tiles: the tile ids of unit u (uniform)
+  __device__ __forceinline__ void tiles(int u, int64_t& ba, int64_t& bb) const {
+    const int e = 2 * (u - c0);
+    ba = e < 64 ? readlane(win0, e) : readlane(win1, e - 64);
+    bb = (2 * u + 1 < nblk) ? (e + 1 < 64 ? readlane(win0, e + 1) : readlane(win1, e + 1 - 64)) : ba;
+  }
+  __device__ __forceinline__ void issue_k(MfmaK<DT, D>& kb, int u) const {
+    if constexpr (B8) {
+      const int n = lane_id() & 15;
+      const char* kt = kc + entry(4 * (u - c0) + (n >> 2)) * blk_stride;
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int kk = 0; kk < C::NKK; ++kk) kb[b][kk] = ld_raw<DT>(kt + k8[b] + 256 * C::E * kk);
+    } else {
+      int64_t ba, bb;
+      tiles(u, ba, bb);
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const char* kt = kc + (o.kt[b] ? bb : ba) * blk_stride;
+#pragma unroll
+        for (int kk = 0; kk < C::NKK; ++kk) kb[b][kk] = ld_raw<DT>(kt + o.koff(b, kk));
+      }
+    }
+  }
+  __device__ __forceinline__ void issue_v(MfmaV<DT, D>& vb, int u) const {
+    if constexpr (B8) {
+      const int r = lane_id() >> 4;
+      const char* vt = vc + entry(4 * (u - c0) + r) * blk_stride;
+#pragma unroll
+      for (int j = 0; j < C::NJ; ++j) vb[j] = ld_raw<DT>(vt + v8 + 128 * C::E * j);
+    } else {
+      int64_t ba, bb;
+      tiles(u, ba, bb);
+      const char* vt = vc + (o.vt ? bb : ba) * blk_stride;
+#pragma unroll
+      for (int j = 0; j < C::NJ; ++j) vb[j] = ld_raw<DT>(vt + o.voff(j));
+    }
+  }
+};
+
 // Stream the 32-token units [u0, u1) of KV head g of sequence s (context ctx) through
-// unit(kb, vb, u).  Units are walked in chunks of 64: both 64-entry block-table windows of
-// a chunk are loaded before its loop, and the loop is a two-stage software pipeline (the
-// loads of unit u + 1 are in flight while unit u is computed) in which every path into a
-// unit has the same loads outstanding, so its wait covers only that unit.  All arguments
-// must be wave-uniform.
-template <int DT, int D, class F>
+// unit(kb, vb, u).  Units are walked in chunks (one block-table window each, loaded before
+// the chunk's loop), and the loop is a two-stage software pipeline (the loads of unit u + 1
+// are in flight while unit u is computed) in which every path into a unit has the same loads
+// outstanding, so its wait covers only that unit.  All arguments must be wave-uniform.
+template <int DT, int D, bool B8, class F>
 __device__ __forceinline__ void mfma_stream(const DecodeArgs& a, int s, int g, int u0, int u1,
                                             int ctx, F&& unit) {
-  using C = MfmaCfg<DT, D>;
-  const int lane = lane_id();
-  const MfmaLaneOffsets<DT, D> o = mfma_offsets<DT, D>();
-  const int64_t blk_stride = (int64_t)a.num_kv_heads * C::TILE;
-  const char* kc = reinterpret_cast<const char*>(a.k_cache) + (int64_t)g * C::TILE;
-  const char* vc = reinterpret_cast<const char*>(a.v_cache) + (int64_t)g * C::TILE;
-  const int32_t* bt_row = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
-  const int nblk = (ctx + kBlock - 1) / kBlock;
-  for (int c0 = u0; c0 < u1; c0 += 64) {
-    const int c1 = min(u1, c0 + 64);
-    const int b0 = 2 * c0, bend = min(nblk, 2 * c1);
-    const int win0 = (b0 + lane < bend) ? tile_block(bt_row, b0 + lane, a.blk_shift) : 0;
-    const int win1 = (b0 + 64 + lane < bend) ? tile_block(bt_row, b0 + 64 + lane, a.blk_shift) : 0;
-    auto blk = [&](int e) -> int64_t { return e < 64 ? readlane(win0, e) : readlane(win1, e - 64); };
+  MfmaUnits<DT, D, B8> U(a, s, g, ctx);
+  for (int c0 = u0; c0 < u1; c0 += U.CHUNK) {
+    const int c1 = min(u1, c0 + U.CHUNK);
+    U.window(c0, c1);
     auto issue = [&](MfmaK<DT, D>& kb, MfmaV<DT, D>& vb, int u) {
-      const int e = 2 * (u - c0);
-      const int64_t ba = blk(e);
-      // a unit whose second block lies past the context reads its first block again (all of
-      // its tokens are masked)
-      const int64_t bb = (2 * u + 1 < nblk) ? blk(e + 1) : ba;
-      mfma_load<DT, D>(kb, vb, kc + ba * blk_stride, kc + bb * blk_stride, vc + ba * blk_stride,
-                       vc + bb * blk_stride, o);
+      U.issue_k(kb, u);
+      U.issue_v(vb, u);
     };
     MfmaK<DT, D> ka, kb;
     MfmaV<DT, D> va, vb;
@@ -342,56 +415,22 @@ __device__ __forceinline__ void mfma_stream(const DecodeArgs& a, int s, int g, i
 // has read V; the in-order load counter then lets each wait cover only the operand it needs.
 // scores(kb, u) returns the unit's weights, pv(vb, p, u) adds P . V.  All arguments must be
 // wave-uniform.
-template <int DT, int D, class S, class PV>
+template <int DT, int D, bool B8, class S, class PV>
 __device__ __forceinline__ void mfma_stream_lean(const DecodeArgs& a, int s, int g, int u0,
                                                  int u1, int ctx, S&& scores, PV&& pv) {
-  using C = MfmaCfg<DT, D>;
-  const int lane = lane_id();
-  const MfmaLaneOffsets<DT, D> o = mfma_offsets<DT, D>();
-  const int64_t blk_stride = (int64_t)a.num_kv_heads * C::TILE;
-  const char* kc = reinterpret_cast<const char*>(a.k_cache) + (int64_t)g * C::TILE;
-  const char* vc = reinterpret_cast<const char*>(a.v_cache) + (int64_t)g * C::TILE;
-  const int32_t* bt_row = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
-  const int nblk = (ctx + kBlock - 1) / kBlock;
-  for (int c0 = u0; c0 < u1; c0 += 64) {
-    const int c1 = min(u1, c0 + 64);
-    const int b0 = 2 * c0, bend = min(nblk, 2 * c1);
-    const int win0 = (b0 + lane < bend) ? tile_block(bt_row, b0 + lane, a.blk_shift) : 0;
-    const int win1 = (b0 + 64 + lane < bend) ? tile_block(bt_row, b0 + 64 + lane, a.blk_shift) : 0;
-    auto blk = [&](int e) -> int64_t { return e < 64 ? readlane(win0, e) : readlane(win1, e - 64); };
-    // a unit whose second block lies past the context reads its first block again (all of its
-    // tokens are masked)
-    auto bases = [&](int u, int64_t& ba, int64_t& bb) {
-      const int e = 2 * (u - c0);
-      ba = blk(e);
-      bb = (2 * u + 1 < nblk) ? blk(e + 1) : ba;
-    };
-    auto issue_k = [&](MfmaK<DT, D>& kb, int u) {
-      int64_t ba, bb;
-      bases(u, ba, bb);
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const char* kt = kc + (o.kt[b] ? bb : ba) * blk_stride;
-#pragma unroll
-        for (int kk = 0; kk < C::NKK; ++kk) kb[b][kk] = ld_raw<DT>(kt + o.koff(b, kk));
-      }
-    };
-    auto issue_v = [&](MfmaV<DT, D>& vb, int u) {
-      int64_t ba, bb;
-      bases(u, ba, bb);
-      const char* vt = vc + (o.vt ? bb : ba) * blk_stride;
-#pragma unroll
-      for (int j = 0; j < C::NJ; ++j) vb[j] = ld_raw<DT>(vt + o.voff(j));
-    };
+  MfmaUnits<DT, D, B8> U(a, s, g, ctx);
+  for (int c0 = u0; c0 < u1; c0 += U.CHUNK) {
+    const int c1 = min(u1, c0 + U.CHUNK);
+    U.window(c0, c1);
     MfmaK<DT, D> kb;
     MfmaV<DT, D> vb;
-    issue_k(kb, c0);
-    issue_v(vb, c0);
+    U.issue_k(kb, c0);
+    U.issue_v(vb, c0);
     for (int u = c0; u < c1; ++u) {
       const MfmaP<DT> p = scores(kb, u);
-      if (u + 1 < c1) issue_k(kb, u + 1);
+      if (u + 1 < c1) U.issue_k(kb, u + 1);
       pv(vb, p, u);
-      if (u + 1 < c1) issue_v(vb, u + 1);
+      if (u + 1 < c1) U.issue_v(vb, u + 1);
     }
   }
 }

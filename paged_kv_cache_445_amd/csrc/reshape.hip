@@ -1,6 +1,9 @@
 // reshape.hip — the paged KV-cache write ("vLLM 架构源码解析 第1篇" §3.3.3: reshape_and_cache
 // scatters this step's K and V into the block pool at slot_mapping before attention; the
-// block / offset split of a slot is §4.2's `//` and `%` by the 16-token block size).
+// block / offset split of a slot is §4.2's `//` and `%` by the block size).  The pools are
+// addressed in tiles of T tokens: T = 8 for 8-token blocks, else 16 (a block of 32 or 64
+// tokens is 2 or 4 consecutive 16-token tiles, so slot / 16 names a tile for every block
+// size from 16 up).
 //
 // One thread per 16-byte K chunk, then one thread per V element.  Consecutive threads read
 // consecutive input bytes (coalesced loads); K chunk stores are 16-byte stores into the
@@ -30,13 +33,13 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(ReshapeArgs a) {
     const int g = rem / NCH, c = rem - g * NCH;
     const int64_t slot = a.slot_mapping[t];
     if (slot < 0) return;  // padding token
-    const int64_t blk = slot / kBlock;
-    const int off = (int)(slot - blk * kBlock);
+    const int64_t blk = slot >> a.tile_shift;  // tile of T = 2^tile_shift tokens
+    const int off = (int)(slot & ((1 << a.tile_shift) - 1));
     typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
     const u32x4 v = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(a.key) +
                                                      ((t * H + g) * D + c * X) * E);
     char* dst = reinterpret_cast<char*>(a.k_cache) +
-                ((((blk * H + g) * NCH + c) * kBlock + off) * 16);
+                ((((blk * H + g) * NCH + c) << a.tile_shift) + off) * 16;
     __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst));
   } else if (tid < nk + nv) {
     const int64_t e = tid - nk;
@@ -45,9 +48,9 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(ReshapeArgs a) {
     const int g = rem / D, d = rem - g * D;
     const int64_t slot = a.slot_mapping[t];
     if (slot < 0) return;
-    const int64_t blk = slot / kBlock;
-    const int off = (int)(slot - blk * kBlock);
-    const int64_t dst = ((blk * H + g) * D + d) * kBlock + off;
+    const int64_t blk = slot >> a.tile_shift;  // tile of T = 2^tile_shift tokens
+    const int off = (int)(slot & ((1 << a.tile_shift) - 1));
+    const int64_t dst = (((blk * H + g) * D + d) << a.tile_shift) + off;
     if constexpr (E == 4)
       __builtin_nontemporal_store(reinterpret_cast<const uint32_t*>(a.value)[e],
                                   reinterpret_cast<uint32_t*>(a.v_cache) + dst);
@@ -76,8 +79,8 @@ __global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(ReshapeArgs 
     const int g = rem / NCH, c = rem - g * NCH;
     const int64_t slot = a.slot_mapping[t];
     if (slot < 0) return;  // padding token
-    const int64_t blk = slot / kBlock;
-    const int off = (int)(slot - blk * kBlock);
+    const int64_t blk = slot >> a.tile_shift;  // tile of T = 2^tile_shift tokens
+    const int off = (int)(slot & ((1 << a.tile_shift) - 1));
     const char* src = reinterpret_cast<const char*>(a.key) + ((t * H + g) * D + c * X) * 2;
     const uint4 h0 = ld16(src), h1 = ld16(src + 16);
     uint32_t w[4];
@@ -89,7 +92,7 @@ __global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(ReshapeArgs 
              (f32_to_fp8(lo(p1) / a.k_scale) << 16) | (f32_to_fp8(hi(p1) / a.k_scale) << 24);
     }
     typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
-    char* dst = reinterpret_cast<char*>(a.k_cache) + ((((blk * H + g) * NCH + c) * kBlock + off) * 16);
+    char* dst = reinterpret_cast<char*>(a.k_cache) + ((((blk * H + g) * NCH + c) << a.tile_shift) + off) * 16;
     __builtin_nontemporal_store(u32x4{w[0], w[1], w[2], w[3]}, reinterpret_cast<u32x4*>(dst));
   } else if (tid < nk + nv) {
     const int64_t e = tid - nk;
@@ -98,12 +101,12 @@ __global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(ReshapeArgs 
     const int g = rem / D, d = rem - g * D;
     const int64_t slot = a.slot_mapping[t];
     if (slot < 0) return;
-    const int64_t blk = slot / kBlock;
-    const int off = (int)(slot - blk * kBlock);
+    const int64_t blk = slot >> a.tile_shift;  // tile of T = 2^tile_shift tokens
+    const int off = (int)(slot & ((1 << a.tile_shift) - 1));
     const uint32_t xb = reinterpret_cast<const uint16_t*>(a.value)[e];
     const float x = DT == DT_FP8B ? bf16_lo(xb) : f16_lo(xb);
     __builtin_nontemporal_store((uint8_t)f32_to_fp8(x / a.v_scale),
-                                reinterpret_cast<uint8_t*>(a.v_cache) + ((blk * H + g) * D + d) * kBlock + off);
+                                reinterpret_cast<uint8_t*>(a.v_cache) + (((blk * H + g) * D + d) << a.tile_shift) + off);
   }
 }
 

@@ -62,10 +62,18 @@ _lib.pa_decode_scratch.restype = ctypes.c_int
 _lib.pa_decode_scratch.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32,
                                    ctypes.c_int32, ctypes.c_float, _G, _vp]
 _lib.pa_decode_partitioned.restype = ctypes.c_int
-_lib.pa_decode_partitioned.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32,
-                                       ctypes.c_float, ctypes.c_int32, ctypes.c_int32, _G, _vp]
+_lib.pa_decode_partitioned.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                       ctypes.c_int32, ctypes.c_float, ctypes.c_int32,
+                                       ctypes.c_int32, _G, _vp]
 _lib.pa_decode_reduce.restype = ctypes.c_int
 _lib.pa_decode_reduce.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_int32, _G, _vp]
+
+
+_lib.pa_measure_stream_read.restype = ctypes.c_int
+_lib.pa_measure_stream_read.argtypes = [_vp, ctypes.c_size_t, _vp, ctypes.c_int32, _vp]
+_lib.pa_measure_tile_read.restype = ctypes.c_int
+_lib.pa_measure_tile_read.argtypes = [_vp, _vp, ctypes.c_int64, ctypes.c_int32, _vp,
+                                      ctypes.c_int32, _vp]
 
 
 def lib():
@@ -177,14 +185,15 @@ def decode_scratch(out, q, k_cache, v_cache, block_tables, context_lens, query_s
 
 
 def decode_partitioned(tmp_out, max_logits, exp_sums, q, k_cache, v_cache, block_tables,
-                       context_lens, scale, partition_size, max_partitions, g: Geom,
-                       stream=None):
+                       context_lens, query_start_loc, scale, partition_size, max_partitions,
+                       g: Geom, stream=None):
+    """query_start_loc: int32 [num_seqs + 1] or None (one row per sequence)."""
     _check("pa_decode_partitioned",
            _lib.pa_decode_partitioned(_p(tmp_out), _p(max_logits), _p(exp_sums), _p(q),
                                       _p(k_cache), _p(v_cache), _p(block_tables),
-                                      _p(context_lens), int(q.shape[0]), float(scale),
-                                      int(partition_size), int(max_partitions), ctypes.byref(g),
-                                      _stream(stream)))
+                                      _p(context_lens), _p(query_start_loc), int(q.shape[0]),
+                                      float(scale), int(partition_size), int(max_partitions),
+                                      ctypes.byref(g), _stream(stream)))
 
 
 def decode_reduce(out, tmp_out, max_logits, exp_sums, max_partitions, g: Geom, stream=None):
@@ -192,3 +201,21 @@ def decode_reduce(out, tmp_out, max_logits, exp_sums, max_partitions, g: Geom, s
            _lib.pa_decode_reduce(_p(out), _p(tmp_out), _p(max_logits), _p(exp_sums),
                                  int(out.shape[0]), int(max_partitions), ctypes.byref(g),
                                  _stream(stream)))
+
+
+# ---- read ceilings (include/pa_measure.h): measurement kernels, not the attention path
+
+def measure_stream_read(buf, sink, workgroups=0, stream=None):
+    """Reads every byte of the device tensor buf; sink: uint32 device tensor, one entry per
+    workgroup."""
+    _check("pa_measure_stream_read",
+           _lib.pa_measure_stream_read(_p(buf), buf.numel() * buf.element_size(), _p(sink),
+                                       int(workgroups), _stream(stream)))
+
+
+def measure_tile_read(base, tile_offsets, tile_bytes, sink, workgroups=0, stream=None):
+    """Reads tiles of tile_bytes at base + tile_offsets (int64 device tensor of byte offsets)."""
+    _check("pa_measure_tile_read",
+           _lib.pa_measure_tile_read(_p(base), _p(tile_offsets), int(tile_offsets.numel()),
+                                     int(tile_bytes), _p(sink), int(workgroups),
+                                     _stream(stream)))

@@ -272,6 +272,16 @@ def llama7b_f16(seed: int = 4451, num_seqs: int = 32) -> Batch:
                        num_blocks=8192, max_blocks_per_seq=128)
 
 
+def llama7b_f16_bs8(seed: int = 4451, num_seqs: int = 32) -> Batch:
+    """The LLaMA-7B-shaped batch (same context lengths and values) with 8-token blocks
+    ("vLLM 架构源码解析 第1篇" §5.1 weighs block sizes 8, 16 and 32): 8192 blocks of 8 tokens,
+    256 table entries per sequence."""
+    rng = np.random.default_rng(seed)
+    ctx = rng.integers(256, 2049, size=num_seqs)
+    return build_batch("llama7b_f16_bs8", "f16", ctx, np.ones(num_seqs), 32, 32, 128, rng,
+                       num_blocks=8192, max_blocks_per_seq=256, block_size=8)
+
+
 def gqa_long_bf16(seed: int = 4452, num_seqs: int = 64, max_ctx: int = 32768) -> Batch:
     rng = np.random.default_rng(seed)
     u = rng.uniform(math.log(128), math.log(max_ctx), size=num_seqs)
@@ -298,6 +308,16 @@ def mixed_chunked_bf16(seed: int = 4454, num_chunk: int = 8, num_decode: int = 1
     rows = np.concatenate([np.full(num_chunk, chunk), np.ones(num_decode, dtype=np.int64)])
     return build_batch("mixed_chunked_bf16", "bf16", ctx, rows, 32, 8, 128, rng,
                        max_blocks_per_seq=500)
+
+
+def prefill_chunks_bf16(seed: int = 4454, num_chunk: int = 8, chunk: int = 512) -> Batch:
+    """The chunked-prefill rows of the mixed step alone: 8 sequences of 512 causal rows over
+    prior contexts U[0, 7488] (the same prior draws), 32 q / 8 KV heads, head_dim 128, bf16."""
+    rng = np.random.default_rng(seed)
+    prior = rng.integers(0, 7489, size=num_chunk)
+    rng.integers(64, 4097, size=120)  # the mixed step's decode contexts, not used here
+    return build_batch("prefill_chunks_bf16", "bf16", prior + chunk, np.full(num_chunk, chunk),
+                       32, 8, 128, rng, max_blocks_per_seq=500)
 
 
 def llama7b_fp8(seed: int = 4451, num_seqs: int = 32) -> Batch:
@@ -369,6 +389,7 @@ def spec_verify_fp8(seed: int = 4455, num_seqs: int = 32, num_draft: int = 5) ->
 PRESETS = {
     "tiny_f32": tiny_f32,
     "llama7b_f16": llama7b_f16,
+    "llama7b_f16_bs8": llama7b_f16_bs8,
     "gqa_long_bf16": gqa_long_bf16,
     "prefix_shared_f16": prefix_shared_f16,
     "mixed_chunked_bf16": mixed_chunked_bf16,
@@ -378,6 +399,7 @@ PRESETS = {
     "spec_verify_gqa_bf16": spec_verify_gqa_bf16,
     "spec_verify_fp8": spec_verify_fp8,
     "mixed_chunked_fp8": mixed_chunked_fp8,
+    "prefill_chunks_bf16": prefill_chunks_bf16,
 }
 
 

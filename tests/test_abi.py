@@ -66,13 +66,14 @@ def test_kv_cache_bytes_and_validation(lib):
     g = _g(num_kv_heads=32, num_q_heads=32, num_blocks=8448, kv_dtype=1, out_dtype=1)
     # 8448 blocks x 32 heads x 128 x 16 x 2 bytes per pool
     assert lib.pa_kv_cache_bytes(ctypes.byref(g)) == 8448 * 32 * 128 * 16 * 2
-    for bad in (_g(head_dim=96), _g(block_size=48), _g(block_size=8), _g(block_size=128),
+    for bad in (_g(head_dim=96), _g(block_size=48), _g(block_size=4), _g(block_size=128),
                 _g(num_q_heads=6, num_kv_heads=4),
                 _g(kv_dtype=7), _g(out_dtype=1), _g(num_q_heads=64, num_kv_heads=2),
                 _g(num_seqs=-1), _g(q_dtype=1), _g(kv_dtype=3, q_dtype=0),
                 _g(kv_dtype=3, k_scale=0.0), _g(kv_dtype=3, v_scale=float("inf"))):
         assert lib.pa_kv_cache_bytes(ctypes.byref(bad)) == 0
-    # 32- and 64-token blocks
+    # 8-, 32- and 64-token blocks
+    assert lib.pa_kv_cache_bytes(ctypes.byref(_g(block_size=8))) == 64 * 2 * 128 * 8 * 2
     assert lib.pa_kv_cache_bytes(ctypes.byref(_g(block_size=32))) == 64 * 2 * 128 * 32 * 2
     assert lib.pa_kv_cache_bytes(ctypes.byref(_g(block_size=64))) == 64 * 2 * 128 * 64 * 2
     # FP8 pools: one byte per element
@@ -129,15 +130,39 @@ def test_host_checks_return_codes_without_launching(lib):
                          ctypes.byref(g8q), None) == -3
 
     lib.pa_decode_partitioned.restype = ctypes.c_int
-    lib.pa_decode_partitioned.argtypes = [vp] * 8 + [ctypes.c_int32, ctypes.c_float,
+    lib.pa_decode_partitioned.argtypes = [vp] * 9 + [ctypes.c_int32, ctypes.c_float,
                                                      ctypes.c_int32, ctypes.c_int32,
                                                      ctypes.POINTER(Geom), vp]
+    part = lib.pa_decode_partitioned
     # partition size must be a multiple of 32, and the partitions must cover a full table row
-    assert lib.pa_decode_partitioned(*([dummy] * 8), 4, 0.1, 48, 8, ctypes.byref(g), None) == -2
-    assert lib.pa_decode_partitioned(*([dummy] * 8), 4, 0.1, 32, 3, ctypes.byref(g), None) == -2
-    assert lib.pa_decode_partitioned(*([dummy] * 7), None, 4, 0.1, 32, 4, ctypes.byref(g), None) == -1
+    assert part(*([dummy] * 8), None, 4, 0.1, 48, 8, ctypes.byref(g), None) == -2
+    assert part(*([dummy] * 8), None, 4, 0.1, 32, 3, ctypes.byref(g), None) == -2
+    assert part(*([dummy] * 7), None, None, 4, 0.1, 32, 4, ctypes.byref(g), None) == -1
     # FP8 pools are accepted (the missing pointer is what fails)
-    assert lib.pa_decode_partitioned(*([dummy] * 7), None, 4, 0.1, 32, 4, ctypes.byref(g8), None) == -1
+    assert part(*([dummy] * 7), None, None, 4, 0.1, 32, 4, ctypes.byref(g8), None) == -1
+    # without query_start_loc the row count must equal the sequence count
+    assert part(*([dummy] * 8), None, 5, 0.1, 32, 4, ctypes.byref(g), None) == -2
+    assert part(*([dummy] * 8), dummy, -1, 0.1, 32, 4, ctypes.byref(g), None) == -2
+    # with query_start_loc: any row count; 16-bit or FP8 pools and a group dividing 16
+    assert part(*([dummy] * 7), None, dummy, 9, 0.1, 32, 4, ctypes.byref(g), None) == -1
+    assert part(*([dummy] * 8), dummy, 9, 0.1, 32, 4, ctypes.byref(gf), None) == -3
+    assert part(*([dummy] * 8), dummy, 9, 0.1, 32, 4, ctypes.byref(g8q), None) == -3
+    assert part(*([dummy] * 7), None, dummy, 9, 0.1, 32, 4, ctypes.byref(g8), None) == -1
+    g0 = _g(num_seqs=0)
+    assert part(*([None] * 9), 0, 0.1, 32, 4, ctypes.byref(g0), None) == 0
+
+    # pa_decode_scratch: pa_decode's checks, no workspace arguments
+    lib.pa_decode_scratch.restype = ctypes.c_int
+    lib.pa_decode_scratch.argtypes = [vp] * 7 + [ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
+                                                 ctypes.POINTER(Geom), vp]
+    scr = lib.pa_decode_scratch
+    assert scr(dummy, dummy, dummy, dummy, dummy, dummy, None, 3, 0, 0.1, ctypes.byref(g), None) == -2
+    assert scr(dummy, None, dummy, dummy, dummy, dummy, None, 4, 0, 0.1, ctypes.byref(g), None) == -1
+    assert scr(dummy, dummy, dummy, dummy, dummy, dummy, None, 4, -1, 0.1, ctypes.byref(g), None) == -2
+    assert scr(None, None, None, None, None, None, None, 0, 0, 0.1, ctypes.byref(g0), None) == 0
+    assert scr(dummy, dummy, dummy, dummy, dummy, dummy, dummy, 9, 0, 0.1, ctypes.byref(gf), None) == -3
+    assert scr(dummy, dummy, dummy, dummy, dummy, dummy, None, 4, 0, 0.1, ctypes.byref(_g(head_dim=80)),
+               None) == -3
 
     lib.pa_decode_reduce.restype = ctypes.c_int
     lib.pa_decode_reduce.argtypes = [vp] * 4 + [ctypes.c_int32, ctypes.c_int32,

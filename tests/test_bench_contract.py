@@ -23,7 +23,8 @@ def test_every_preset_has_a_bench_description():
     for name in W.PRESETS:
         assert name in bench.DESCRIPTIONS, name
     extra = set(bench.DESCRIPTIONS) - set(W.PRESETS)
-    assert extra == {"cow_copy_f16", "swap_f16"}
+    assert extra == set(bench.MEASURE_WORKLOADS)
+    assert {"hbm_read_ceiling", "tile_replay_llama7b_f16"} <= extra
 
 
 @pytest.mark.parametrize("dtype,Hq,Hkv,rows,fp8,chunk", [

@@ -263,25 +263,28 @@ def test_partitioned_and_reduce(dev, dtype, Hq, Hkv, ps):
 
 
 def check_partitioned(dev, b, ps):
-    """pa_decode_partitioned's partials against the oracle's, then pa_decode_reduce's merge."""
+    """pa_decode_partitioned's partials against the oracle's, then pa_decode_reduce's merge
+    (with query_start_loc when the batch has one)."""
     import torch
     import oracle
     from paged_kv_cache_445_amd import pa
     Hq, D = b.num_q_heads, b.head_dim
+    _log(f"[partitioned] {b.name} {b.pool_dtype} S={b.num_seqs} rows={b.num_q_rows} Hq={Hq} "
+         f"Hkv={b.num_kv_heads} D={D} bs={b.block_size} ps={ps}")
     db = run_gpu(dev, b)
     P = -(-b.max_blocks_per_seq * b.block_size // ps)
     R = b.num_q_rows
     tmp = torch.full((R, Hq, P, D), 7.0, device=db.device)
-    ml = torch.zeros((R, Hq, P), device=db.device)
-    es = torch.zeros((R, Hq, P), device=db.device)
+    ml = torch.full((R, Hq, P), 7.0, device=db.device)
+    es = torch.full((R, Hq, P), 7.0, device=db.device)
     pa.decode_partitioned(tmp, ml, es, db.q, db.k_cache, db.v_cache, db.block_tables,
-                          db.context_lens, db.scale, ps, P, db.geom)
+                          db.context_lens, db.qsl, db.scale, ps, P, db.geom)
     out = torch.zeros((R, Hq, D), device=db.device)
     pa.decode_reduce(out, tmp, ml, es, P, db.geom)
     torch.cuda.synchronize()
     kp, vp = H.oracle_pools(b)
-    o, m, l = oracle.partition_attention(b.q, kp, vp, b.block_tables, b.context_lens, None,
-                                         b.scale, H.geom(b), ps, P)
+    o, m, l = oracle.partition_attention(b.q, kp, vp, b.block_tables, b.context_lens,
+                                         b.query_start_loc, b.scale, H.geom(b), ps, P)
     gm, gl, go = ml.cpu().numpy(), es.cpu().numpy(), tmp.cpu().numpy()
     nonempty = l > 0
     assert np.array_equal(gl > 0, nonempty)
@@ -292,8 +295,52 @@ def check_partitioned(dev, b, ps):
     rel = np.abs(gl[nonempty] - l[nonempty]) / l[nonempty]
     assert rel.max() <= tol, rel.max()
     check_out(go[nonempty].astype(np.float64), o[nonempty], tol, "tmp_out")
+    # partitions with no key keep their tmp_out entries as they were
+    assert (go[~nonempty] == 7.0).all()
     want, _ = H.oracle_attention(b, kp, vp)
     check_out(out.cpu().numpy().astype(np.float64), want, tol, "reduce")
+
+
+@pytest.mark.parametrize("dtype,Hq,Hkv,D,ps,bs,fp8", [
+    ("bf16", 32, 8, 128, 512, 16, False), ("f16", 8, 8, 128, 64, 16, False),
+    ("bf16", 16, 4, 128, 32, 32, False), ("f16", 16, 2, 64, 96, 16, True),
+    ("bf16", 8, 2, 128, 256, 64, True)])
+def test_partitioned_multi_row(dev, dtype, Hq, Hkv, D, ps, bs, fp8):
+    """Fixed partitions with query_start_loc: chunked-prefill rows (the chunk kernel, one
+    item per key partition), verify rows and decode rows; partitions of 32 tokens start at
+    odd units.  Every partial and the merged output against the oracle."""
+    rng = np.random.default_rng(5100 + ps + Hq + bs)
+    n = np.array([130, 1, 4, 1, 37, 2, 1, 64])
+    prior = np.array([300, 55, 2000, 0, 0, 900, 1, 1500])
+    b = W.build_batch("part_rows", dtype, prior + n, n, Hq, Hkv, D, rng, block_size=bs)
+    if fp8:
+        _fp8(b)
+    check_partitioned(dev, b, ps)
+
+
+def test_max_query_len_understated_rows_are_nan(dev):
+    """pa_decode with max_query_len below some sequence's row count: that sequence's rows are
+    not computed and come back NaN (the call cannot read the device's row counts); every
+    other row is right."""
+    import torch
+    rng = np.random.default_rng(809)
+    n = np.array([3, 1, 40, 2, 1, 4])
+    prior = np.array([100, 7, 300, 1, 2000, 33])
+    for dtype, Hq, Hkv, mql in (("bf16", 16, 4, 4), ("f16", 8, 8, 6)):
+        b = W.build_batch("mql_low", dtype, prior + n, n, Hq, Hkv, 128, rng)
+        _log(f"[max_query_len understated] {dtype} Hq={Hq} Hkv={Hkv} max_query_len={mql}")
+        db = run_gpu(dev, b)
+        kp, vp = H.oracle_pools(b)
+        want, _ = H.oracle_attention(b, kp, vp)
+        db.max_query_len = mql
+        db.out.zero_()
+        db.attend()
+        torch.cuda.synchronize()
+        got = db.out_host()
+        long_rows = np.arange(b.query_start_loc[2], b.query_start_loc[3])
+        assert np.isnan(got[long_rows]).all()
+        rest = np.setdiff1d(np.arange(b.num_q_rows), long_rows)
+        check_out(got[rest], want[rest], TOL[dtype], f"max_query_len {mql}, other rows")
 
 
 # ----------------------------------------------------------------- the five workloads
@@ -818,9 +865,70 @@ def test_larger_blocks_partitioned(dev):
     ml = torch.zeros((R, Hq, P), device=db.device)
     es = torch.zeros((R, Hq, P), device=db.device)
     pa.decode_partitioned(tmp, ml, es, db.q, db.k_cache, db.v_cache, db.block_tables,
-                          db.context_lens, db.scale, ps, P, db.geom)
+                          db.context_lens, None, db.scale, ps, P, db.geom)
     out = torch.zeros((R, Hq, D), device=db.device)
     pa.decode_reduce(out, tmp, ml, es, P, db.geom)
     torch.cuda.synchronize()
     want, _ = H.oracle_attention(b, *H.oracle_pools(b))
     check_out(out.cpu().numpy().astype(np.float64), want, TOL["bf16"], "partitioned, 32-token blocks")
+
+
+# ----------------------------------------------------------------- 8-token blocks
+
+@pytest.mark.parametrize("dtype,Hq,Hkv,D", [("f16", 8, 8, 128), ("bf16", 16, 2, 128),
+                                            ("f32", 4, 4, 64), ("f16", 32, 32, 64),
+                                            ("bf16", 16, 4, 64), ("f16", 12, 4, 128)])
+def test_block8_decode(dev, dtype, Hq, Hkv, D):
+    """8-token blocks (two blocks per 16-token tile): cache write bit for bit and decode on the
+    edge-case contexts, vector path (MHA, fp32) and matrix-core path (GQA)."""
+    rng = np.random.default_rng(3300 + Hq + D)
+    ctx = np.array(EDGE_CTX + [7, 8, 9, 23, 24, 25] + list(rng.integers(1, 2200, size=6)))
+    parity(dev, W.build_batch("block8", dtype, ctx, np.ones(len(ctx)), Hq, Hkv, D, rng,
+                              block_size=8))
+
+
+@pytest.mark.parametrize("qdt,Hq,Hkv,D", [("f16", 8, 8, 128), ("bf16", 16, 2, 128),
+                                          ("f16", 32, 4, 64)])
+def test_block8_fp8(dev, qdt, Hq, Hkv, D):
+    """FP8 pools with 8-token blocks: the E4M3 codes bit for bit and the decode."""
+    rng = np.random.default_rng(3400 + Hq + D)
+    ctx = np.array(EDGE_CTX + [7, 8, 9] + list(rng.integers(1, 2200, size=6)))
+    parity(dev, _fp8(W.build_batch("block8_fp8", qdt, ctx, np.ones(len(ctx)), Hq, Hkv, D, rng,
+                                   block_size=8)))
+
+
+def test_block8_rows_splits_partitions_copies(dev):
+    """8-token blocks with chunked-prefill and verify rows (16-bit and FP8), 300 sequences whose
+    segments are split and merged in the kernel, fixed partitions with query_start_loc, and
+    block copies."""
+    import torch
+    import oracle
+    from paged_kv_cache_445_amd import pa
+    rng = np.random.default_rng(3500)
+    n = np.array([37, 1, 4, 1, 130, 2, 9])
+    prior = np.array([0, 55, 300, 17, 61, 900, 3])
+    parity(dev, W.build_batch("b8_rows", "bf16", prior + n, n, 16, 4, 128, rng, block_size=8))
+    parity(dev, _fp8(W.build_batch("b8_rows_fp8", "f16", prior + n, n, 8, 8, 128, rng,
+                                   block_size=8)))
+    for Hq, Hkv in ((16, 16), (16, 2)):
+        parity(dev, W.build_batch("b8_many", "f16", rng.integers(1, 3001, size=300),
+                                  np.ones(300), Hq, Hkv, 128, rng, block_size=8))
+    check_partitioned(dev, W.build_batch("b8_part", "bf16", prior + n, n, 16, 4, 128, rng,
+                                         block_size=8), 64)
+    check_partitioned(dev, W.build_batch("b8_part_mha", "f16", rng.integers(1, 3000, size=10),
+                                         np.ones(10), 8, 8, 128, rng, block_size=8), 32)
+    b = W.build_batch("b8_copy", "f16", rng.integers(40, 200, size=6), np.ones(6), 4, 4, 128,
+                      rng, block_size=8)
+    db = run_gpu(dev, b)
+    used = set(np.unique(b.block_tables).tolist())
+    free = [x for x in range(b.num_blocks) if x not in used][:4]
+    pairs = np.stack([b.block_tables[:4, 0], free], 1).astype(np.int64)
+    pa.copy_blocks(db.k_cache, db.v_cache, torch.from_numpy(pairs).cuda(), db.geom)
+    torch.cuda.synchronize()
+    kp, vp = H.oracle_pools(b)
+    oracle.copy_blocks(kp, vp, pairs, H.geom(b))
+    check_pools(db, kp, vp)
+
+
+def test_llama7b_f16_bs8(dev):
+    parity(dev, W.make("llama7b_f16_bs8"))

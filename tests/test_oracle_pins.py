@@ -44,7 +44,7 @@ def test_bf16_conversion_matches_bit_shift_all_bit_patterns():
 
 @pytest.mark.parametrize("dtype,D,BS", [("f32", 8, 16), ("f16", 16, 16), ("bf16", 32, 16),
                                         ("f16", 16, 32), ("bf16", 32, 64), ("fp8", 32, 32),
-                                        ("f32", 8, 8)])
+                                        ("f32", 8, 8), ("f16", 16, 8), ("fp8", 32, 8)])
 def test_pool_layout_matches_declared_shapes(dtype, D, BS):
     """K is [NB][R][Hkv][D/X][T][X], V is [NB][R][Hkv][D][T] in row-major order, a block of BS
     tokens being R = BS / T sub-blocks of T = min(BS, 16) tokens (for BS = 16:
@@ -81,11 +81,12 @@ def test_block_bytes_match_page_formula():
 
 # ----------------------------------------------------------------- reshape_and_cache
 
-@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
-def test_reshape_and_cache_round_trip_and_poison(dtype):
+@pytest.mark.parametrize("dtype,BS", [("f32", 16), ("f16", 16), ("bf16", 16), ("f16", 8),
+                                      ("f32", 8)])
+def test_reshape_and_cache_round_trip_and_poison(dtype, BS):
     rng = np.random.default_rng(11)
     b = W.build_batch("rt", dtype, rng.integers(1, 60, size=5), np.ones(5), 4, 2,
-                      64 if dtype == "f32" else 128, rng)
+                      64 if dtype == "f32" else 128, rng, block_size=BS)
     kp, vp = H.oracle_pools(b)
     K = kp.reshape(b.k_pool_shape())
     V = vp.reshape(b.v_pool_shape())
@@ -283,11 +284,13 @@ def test_causal_chunk_rows_match_torch_sdpa(prior):
 @pytest.mark.parametrize("dtype,G,rows,BS", [("f32", 1, 1, 16), ("f16", 1, 1, 16),
                                              ("bf16", 4, 1, 16), ("bf16", 4, 7, 16),
                                              ("f16", 8, 3, 16), ("f16", 1, 1, 32),
-                                             ("bf16", 4, 5, 64), ("f32", 2, 1, 32)])
+                                             ("bf16", 4, 5, 64), ("f32", 2, 1, 32),
+                                             ("f16", 1, 1, 8), ("bf16", 4, 3, 8),
+                                             ("f32", 1, 1, 8)])
 def test_paged_equals_dense_bitwise(dtype, G, rows, BS):
     """The paged walk (block table + layout + reshape_and_cache) equals the dense routine on
     the generator's unpaged keys bit for bit: same operations in the same order, for 16-token
-    blocks and for 32- and 64-token blocks of 16-token sub-blocks."""
+    blocks, for 32- and 64-token blocks of 16-token sub-blocks and for 8-token blocks."""
     rng = np.random.default_rng(51)
     D = 64 if dtype == "f32" else 128
     S = 5
