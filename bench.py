@@ -394,7 +394,7 @@ def bench_read_ceiling(args):
     stream = torch.cuda.current_stream()
     wall, call_ms = _timed(args, lambda i: pa.measure_stream_read(bufs[i % copies], sink), stream)
     _ceiling_line(args, "hbm_read_ceiling", n, wall, call_ms,
-                  "pa_measure_stream_read (eight 256-thread workgroups per CU)",
+                  "pa_measure_stream_read (two 256-thread workgroups per CU, 16 KiB in flight per wave)",
                   {"buffer_bytes": n, "buffers_rotated": copies})
 
 
@@ -427,7 +427,7 @@ def bench_tile_replay(args):
     wall, call_ms = _timed(args, lambda i: pa.measure_tile_read(pools[i % copies], off_t, tile,
                                                                 sink), stream)
     _ceiling_line(args, "tile_replay_llama7b_f16", moved, wall, call_ms,
-                  "pa_measure_tile_read (one 256-thread workgroup per CU)",
+                  "pa_measure_tile_read (two 256-thread workgroups per CU, 8 tiles in flight per wave)",
                   {"tiles": int(len(offs)), "tile_bytes": tile, "pool_copies_rotated": copies,
                    "algorithmic_kv_bytes_of_the_batch": b.kv_bytes()})
 

@@ -21,14 +21,15 @@
 extern "C" {
 #endif
 
-/* Reads bytes (a multiple of 16) of buf front to back.  sink: one uint32 per workgroup;
- * workgroups of 256 threads, 0: eight per CU. */
+/* Reads bytes (a multiple of 16) of buf, 16 KiB per wave at a time.  sink: one uint32 per
+ * workgroup; workgroups of 256 threads, 0: two per CU. */
 pa_status pa_measure_stream_read(const void* buf, size_t bytes, uint32_t* sink,
                                  int32_t workgroups, void* stream);
 
 /* Reads num_tiles tiles of tile_bytes (a multiple of 1024) at base + tile_offsets[t] (int64
  * byte offsets, 16-byte aligned), the list split evenly over the waves of the grid in its
- * order.  sink: one uint32 per workgroup; workgroups of 256 threads, 0: one per CU. */
+ * order, eight tiles in flight per wave.  sink: one uint32 per workgroup; workgroups of 256
+ * threads, 0: two per CU. */
 pa_status pa_measure_tile_read(const void* base, const int64_t* tile_offsets, int64_t num_tiles,
                                int32_t tile_bytes, uint32_t* sink, int32_t workgroups,
                                void* stream);

@@ -58,6 +58,17 @@ struct ChunkTile {
   static constexpr int CPT = TILE / 16;                    // 16-byte chunks per tile
 };
 
+// The staged unit in LDS is the 16-token layout (K tiles [D/8][16][8], V tiles [D][16]) with
+// its 16-byte pieces permuted inside each 256-byte row, so that the operand reads of a wave
+// hit distinct LDS banks in every group of 8 and of 16 lanes: K token tok of staged tile kt
+// sits at slot swz_k(kt, tok) of its chunk row (lanes n and n + 8 read tokens 16 apart,
+// which would share banks), and V's two 16-byte halves of dimension d are swapped when
+// swz_v(d) (lanes n and n + 4, n + 8 read rows 128 and 256 bytes apart).
+__device__ __forceinline__ int swz_k(int kt, int tok) {
+  return tok ^ ((((tok >> 3) ^ kt) & 1) << 2);
+}
+__device__ __forceinline__ int swz_v(int d) { return ((d >> 2) ^ (d >> 3)) & 1; }
+
 struct ChunkPlanIn {
   const int32_t* qsl;
   const int32_t* context_lens;
@@ -97,29 +108,40 @@ struct ChunkP {
   bool split;  // uniform: the weights are fed as hi + lo
 };
 
-// Scores of one column block over the unit (raw q . k from the matrix core), the lazy
-// softmax update and the block's weights.  sl > 0 is the score factor in the base-2 domain.
-// MASK: unit token 8 r + k exists for this lane's column only if 8 r + k <= lim.  The low
-// parts of the weights are formed when some column's largest weight is heavy (kHeavy).
-template <int DT, int D, bool MASK>
-__device__ __forceinline__ ChunkP<DT> chunk_scores(ChunkCol<D>& st, const MfmaK<DT, D>& kb,
-                                                   const MfmaQ<DT, D>& qb, float sl, int lim) {
-  using C = MfmaCfg<DT, D>;
+// Eight fp32 weights as one 16-bit MFMA operand, converted in pairs (round to nearest even).
+template <int DT>
+__device__ __forceinline__ op8_t<DT> pack8(const float (&p)[8]) {
   using E = typename std::conditional<bf16_core<DT>(), __bf16, _Float16>::type;
-  const int r = lane_id() >> 4;
-  f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+  typedef __attribute__((ext_vector_type(2))) E e2_t;
+  op8_t<DT> o;
 #pragma unroll
-  for (int kk = 0; kk < C::NKK; ++kk) {
-    s0 = mfma<DT>(operand<DT>(kb[0][kk]), qb[kk], s0);
-    s1 = mfma<DT>(operand<DT>(kb[1][kk]), qb[kk], s1);
+  for (int j = 0; j < 4; ++j) {
+    const e2_t v = __builtin_convertvector((f32x2_t){p[2 * j], p[2 * j + 1]}, e2_t);
+    o[2 * j] = v[0];
+    o[2 * j + 1] = v[1];
   }
+  return o;
+}
+
+// The lazy softmax update of one column block over a unit and the block's weights, from its
+// raw scores q . k (s0, s1: the two S-blocks of the unit from the matrix core; lane (r, n)
+// holds unit tokens 8 r .. 8 r + 7 of column n).  sl > 0 is the score factor in the base-2
+// domain.  masked (uniform): unit token 8 r + k exists for this lane's column only if
+// 8 r + k <= lim.  The low parts of the weights are formed when some column's largest
+// weight is heavy (kHeavy).
+template <int DT, int D>
+__device__ __forceinline__ ChunkP<DT> chunk_softmax(ChunkCol<D>& st, const f32x4_t& s0,
+                                                    const f32x4_t& s1, float sl, int lim,
+                                                    bool masked) {
+  using C = MfmaCfg<DT, D>;
+  const int r = lane_id() >> 4;
   float x[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     x[i] = s0[i];
     x[4 + i] = s1[i];
   }
-  if (MASK) {
+  if (masked) {
 #pragma unroll
     for (int k = 0; k < 8; ++k)
       if (8 * r + k > lim) x[k] = -INFINITY;
@@ -150,11 +172,13 @@ __device__ __forceinline__ ChunkP<DT> chunk_scores(ChunkCol<D>& st, const MfmaK<
   float p[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) p[k] = __builtin_amdgcn_exp2f(fmaf(x[k], sl, -mref));
-#pragma unroll
-  for (int k = 0; k < 8; ++k) out.hi[k] = (E)p[k];
+  out.hi = pack8<DT>(p);
   if (out.split) {
+    const op8_t<DT> h = out.hi;
+    float lo[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) out.lo[k] = (E)(p[k] - (float)out.hi[k]);
+    for (int k = 0; k < 8; ++k) lo[k] = p[k] - (float)h[k];
+    out.lo = pack8<DT>(lo);
   }
   return out;
 }
@@ -258,7 +282,6 @@ __device__ void chunk_item(const DecodeArgs& a, int s, int g, int cb, int part,
 #pragma unroll
   for (int k = 0; k < 8; ++k) ones[k] = (E)1.f;
 
-  const MfmaLaneOffsets<DT, D> o = mfma_offsets<DT, D>();
   // a pool tile of one KV head: 16 tokens (8 with 8-token blocks), 16-bit or E4M3 elements
   constexpr int64_t PTILE = (F8 ? C::TILE / 2 : C::TILE) / (B8 ? 2 : 1);
   const int64_t blk_stride = (int64_t)a.num_kv_heads * PTILE;
@@ -286,7 +309,8 @@ __device__ void chunk_item(const DecodeArgs& a, int s, int g, int cb, int part,
     ld_tile[k] = c / CT::CPT;
     const int cc = c % CT::CPT;
     const bool vt = ld_tile[k] & 2;
-    ld_off[k] = cc * 16;
+    ld_off[k] = vt ? ((cc >> 1) * 2 + ((cc & 1) ^ swz_v(cc >> 1))) * 16
+                   : ((cc >> 4) * 16 + swz_k(ld_tile[k] & 1, cc & 15)) * 16;
     if constexpr (B8) {
       const int half = vt ? cc & 1 : (cc >> 3) & 1;
       ld_blk[k] = 2 * (ld_tile[k] & 1) + half;
@@ -330,11 +354,18 @@ __device__ void chunk_item(const DecodeArgs& a, int s, int g, int cb, int part,
     if (!B8 && e + 1 >= nblk) bt[PER_UNIT - 1] = bt[0];
 #pragma unroll
     for (int k = 0; k < CT::LOADS; ++k) {
-      int64_t b = bt[0];
+      if constexpr (B8) {
+        int64_t b = bt[0];
 #pragma unroll
-      for (int i = 1; i < PER_UNIT; ++i) b = ld_blk[k] == i ? bt[i] : b;
-      const char* base = (ld_tile[k] & 2 ? vc : kc) + b * blk_stride;
-      regs[k] = *reinterpret_cast<const Raw*>(base + src_off[k]);
+        for (int i = 1; i < PER_UNIT; ++i) b = ld_blk[k] == i ? bt[i] : b;
+        const char* base = (ld_tile[k] & 2 ? vc : kc) + b * blk_stride;
+        regs[k] = *reinterpret_cast<const Raw*>(base + src_off[k]);
+      } else {
+        // a whole wave loads from one tile (256 or 128 threads per tile): a scalar base
+        const int t = __builtin_amdgcn_readfirstlane(ld_tile[k]);
+        const char* base = (t & 2 ? vc : kc) + (t & 1 ? bt[1] : bt[0]) * blk_stride;
+        regs[k] = *reinterpret_cast<const Raw*>(base + src_off[k]);
+      }
     }
   };
   auto store_unit = [&](const Raw* regs, int buf) {
@@ -357,30 +388,49 @@ __device__ void chunk_item(const DecodeArgs& a, int s, int g, int cb, int part,
   // for outstanding loads, so the compiler's wait before each store covers only that unit.
   auto barrier = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
   const int ulast = uend - 1;
+  // this lane's operand offsets in the staged unit (swizzled as staged; see swz_k, swz_v):
+  // K of S-block b at lk[b] + 1 KiB per kk, V at lv + 512 bytes per j
+  int lk[2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int t = 8 * (n >> 2) + 4 * b + (n & 3);  // unit token of S-block row n
+    lk[b] = (t >> 4) * CT::TILE + r * 256 + swz_k(t >> 4, t & 15) * 16;
+  }
+  const int lv = (2 + (r >> 1)) * CT::TILE + n * 32 + (((r & 1) ^ swz_v(n)) * 16);
   auto compute = [&](int u, int buf) {
     const int t0 = u * kMfmaUnit;
     if (u < uend && t0 < kend_w) {  // uniform: this wave's columns see keys of this unit
       const char* ub = lds_units + buf * CT::UNIT;
-      // scores of both column blocks from K, then P . V from V: K and V are never live together
-      MfmaK<DT, D> kb;
+      // scores of both column blocks from K (their MFMA chains interleaved), the softmax of
+      // each, then P . V from V: K and V are never live together
+      uint4 kb[2][C::NKK];
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int kk = 0; kk < C::NKK; ++kk)
-          kb[b][kk] = *reinterpret_cast<const uint4*>(ub + o.kt[b] * CT::TILE + o.koff(b, kk));
+          kb[b][kk] = *reinterpret_cast<const uint4*>(ub + lk[b] + 1024 * kk);
+      f32x4_t s0[NCB], s1[NCB];
+#pragma unroll
+      for (int c = 0; c < NCB; ++c) s0[c] = s1[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      // (a block with no real row has q = 0: its scores are computed and never used)
+#pragma unroll
+      for (int kk = 0; kk < C::NKK; ++kk)
+#pragma unroll
+        for (int c = 0; c < NCB; ++c) {
+          s0[c] = mfma<DT>(__builtin_bit_cast(T, kb[0][kk]), qb[c][kk], s0[c]);
+          s1[c] = mfma<DT>(__builtin_bit_cast(T, kb[1][kk]), qb[c][kk], s1[c]);
+        }
       ChunkP<DT> pp[NCB];
 #pragma unroll
       for (int c = 0; c < NCB; ++c) {
         if (!live[c]) continue;
-        if (t0 + kMfmaUnit - 1 <= first[c] && full[c])
-          pp[c] = chunk_scores<DT, D, false>(st[c], kb, qb[c], sl, kMfmaUnit - 1);
-        else
-          pp[c] = chunk_scores<DT, D, true>(st[c], kb, qb[c], sl, pos[c] - t0);
+        const bool masked = !(t0 + kMfmaUnit - 1 <= first[c] && full[c]);
+        pp[c] = chunk_softmax<DT, D>(st[c], s0[c], s1[c], sl, pos[c] - t0, masked);
       }
       T vo[C::NJ];
 #pragma unroll
       for (int j = 0; j < C::NJ; ++j)
-        vo[j] = __builtin_bit_cast(T, *reinterpret_cast<const uint4*>(ub + (2 + o.vt) * CT::TILE + o.voff(j)));
+        vo[j] = __builtin_bit_cast(T, *reinterpret_cast<const uint4*>(ub + lv + 512 * j));
       if (t0 + kMfmaUnit > kend) {
         // zero the V elements of tokens past the item's keys (0 * NaN is NaN); their
         // weights are 0 in every column

@@ -517,7 +517,11 @@ __global__ __launch_bounds__(kWG) void valu_decode_kernel(DecodeArgs a) {
     // units: (sequence, group of 4 HPW heads, tile); wave i runs heads i + 4 j of each group
     constexpr int GH = kWavesPerWG * HPW;
     const int groups = (a.num_q_heads + GH - 1) / GH;
-    const Part part = make_part((int64_t)base[S] * groups, gridDim.x, a.odd_skew);
+    // the list is (sequence, head group, tile), or with xcd_major (head group, sequence,
+    // tile) split over XCD-major owners, so that each XCD works through a few head groups of
+    // every sequence and keeps the blocks several sequences share in its own L2
+    const Part part = make_part((int64_t)base[S] * groups, gridDim.x, a.odd_skew, a.xcd_major);
+    const int64_t per_group = base[S];
     even_split_drive(part, [&](int64_t o, int64_t lo, int64_t hi) {
       // this wave's piece of the segment that unit i of the range belongs to
       struct Unit {
@@ -528,12 +532,20 @@ __global__ __launch_bounds__(kWG) void valu_decode_kernel(DecodeArgs a) {
       };
       auto at = [&](int64_t i) {
         Unit u;
-        u.p.s = find_seq(base, S, i, groups);
-        const int seglen = base[u.p.s + 1] - base[u.p.s];
+        int grp, seglen;
+        if (part.xcd) {
+          grp = (int)(i / per_group);
+          u.p.s = find_seq(base, S, i - grp * per_group, 1);
+          seglen = base[u.p.s + 1] - base[u.p.s];
+          u.seg0 = grp * per_group + base[u.p.s];
+        } else {
+          u.p.s = find_seq(base, S, i, groups);
+          seglen = base[u.p.s + 1] - base[u.p.s];
+          const int64_t sbase = (int64_t)base[u.p.s] * groups;
+          grp = (int)((i - sbase) / seglen);
+          u.seg0 = sbase + (int64_t)grp * seglen;
+        }
         u.nt = seglen - a.seg_extra;  // real tiles; the rest only balance the split
-        const int64_t sbase = (int64_t)base[u.p.s] * groups;
-        const int grp = (int)((i - sbase) / seglen);
-        u.seg0 = sbase + (int64_t)grp * seglen;
         u.end = min(hi, u.seg0 + seglen);
         u.p.h0 = grp * GH + wave;  // this wave's first head (HPW > 1: all exist)
         u.p.t0 = (int)(i - u.seg0);

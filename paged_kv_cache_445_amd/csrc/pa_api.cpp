@@ -116,6 +116,16 @@ int odd_skew() {
   return v >= 0 ? v : kOddSkew;
 }
 
+// The vector kernel's even split in (head group, sequence, tile) order over XCD-major
+// owners (see Part in pa_device.h); optional override for tuning (0 / 1)
+int xcd_major_override() {
+  static const int v = [] {
+    const char* s = getenv("PA_DECODE_XCD_MAJOR");
+    return s ? atoi(s) : -1;
+  }();
+  return v;
+}
+
 bool use_mfma(const pa_geom* g) {
   return g->kv_dtype != PA_F32 && g->num_q_heads / g->num_kv_heads >= 2;
 }
@@ -526,6 +536,7 @@ pa_status decode_impl(void* out, const void* q, const void* k_cache, const void*
   }
   a.seg_extra = seg_extra_override() >= 0 ? seg_extra_override() : kSegExtra[rt.path];
   a.heads_per_wave = rt.path == 0 ? heads_per_wave(g) : 1;
+  a.xcd_major = xcd_major_override() > 0 ? 1 : 0;
   a.odd_skew = odd_skew();
   a.max_rows = rt.max_rows;
   a.cols = rt.cols;

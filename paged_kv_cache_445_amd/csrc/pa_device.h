@@ -362,34 +362,47 @@ __device__ __forceinline__ int find_seq(const int32_t* base, int S, int64_t i, i
   return lo;
 }
 
-// The flattened (sequence, head group, unit) list [0, total) is split over the NK workgroups
-// that get work (NK = min(workgroups, total)): workgroup ("owner") o owns
-// [part_lo(o), part_lo(o + 1)), and wave i of it takes head i of every group of that range.
-// Shares are proportional to a weight per owner: we for even o, wo for odd o.  Workgroups
-// are dispatched to the XCDs round robin (workgroup o runs on XCD o mod 8), and on gfx950
-// the odd XCDs stream this access pattern measurably slower than the even ones, so the odd
-// owners get slightly less work; the weights stay equal unless every share keeps at least
-// four units, which keeps every share non-empty.
+// The flattened work list [0, total) is split over the NK workgroups that get work
+// (NK = min(workgroups, total)): workgroup ("owner") o owns [part_lo(o), part_lo(o + 1)),
+// and wave i of it takes head i of every group of that range.  Shares are proportional to
+// a weight per owner.  Workgroups are dispatched to the XCDs round robin (workgroup b runs
+// on XCD b mod 8), and on gfx950 the odd XCDs stream this access pattern measurably slower
+// than the even ones, so owners on odd XCDs get slightly less work; the weights stay equal
+// unless every share keeps at least four units, which keeps every share non-empty.
+//  - identity mapping: owner o is workgroup o, on XCD o mod 8; weights alternate per owner.
+//  - XCD-major mapping (xcd): owner o is the workgroup b with xcd_local_block(b) = o, so
+//    owners [x B, (x + 1) B) (B = NK / 8) all run on XCD x and consecutive stretches of the
+//    list stay on one XCD (and in its L2); weights alternate per block of B owners.  Used
+//    only when every workgroup is an owner and their count is a multiple of 8.
 struct Part {
   int64_t total;   // units
   int64_t NK;      // owners
-  int64_t we, wo;  // weights of even and odd owners
+  int64_t we, wo;  // weights of owners on even and odd XCDs
+  int64_t B;       // owners per weight block (1, or NK / 8 with xcd)
+  bool xcd;        // XCD-major owner mapping
 };
 
 // odd_skew: per mille taken from odd owners' weights and given to even owners'
-__device__ __forceinline__ Part make_part(int64_t total, int64_t workgroups, int odd_skew) {
+__device__ __forceinline__ Part make_part(int64_t total, int64_t workgroups, int odd_skew,
+                                          bool xcd_major = false) {
   Part p;
   p.total = total;
   p.NK = min(workgroups, total);
   const bool skew = odd_skew > 0 && odd_skew < 500 && total >= 4 * p.NK;
   p.we = skew ? 1000 + odd_skew : 1000;
   p.wo = skew ? 1000 - odd_skew : 1000;
+  p.xcd = xcd_major && p.NK == workgroups && workgroups % kXcds == 0;
+  p.B = p.xcd ? p.NK / kXcds : 1;
   return p;
 }
 
-// summed weight of owners [0, o)
+// summed weight of owners [0, o): f whole blocks of B owners (alternately even and odd
+// XCDs), then rem owners of block f
 __device__ __forceinline__ int64_t part_weight(const Part& p, int64_t o) {
-  return ((o + 1) >> 1) * p.we + (o >> 1) * p.wo;
+  const int64_t f = o / p.B, rem = o - f * p.B;
+  const int64_t even = ((f + 1) >> 1) * p.B + ((f & 1) ? 0 : rem);
+  const int64_t odd = (f >> 1) * p.B + ((f & 1) ? rem : 0);
+  return even * p.we + odd * p.wo;
 }
 
 // first unit of owner o (o in [0, NK]; part_lo(NK) == total)
@@ -400,10 +413,10 @@ __device__ __forceinline__ int64_t part_lo(const Part& p, int64_t o) {
 // part_weight(o) <= X below
 __device__ __forceinline__ int64_t part_owner(const Part& p, int64_t u) {
   const int64_t X = ((u + 1) * part_weight(p, p.NK) - 1) / p.total;
-  const int64_t pair = p.we + p.wo;
-  const int64_t m = X / pair;
-  const int64_t o = 2 * m + (X - m * pair >= p.we ? 1 : 0);
-  return min(o, p.NK - 1);
+  const int64_t pair = p.B * (p.we + p.wo);  // an even block and the odd one after it
+  const int64_t m = X / pair, r = X - m * pair;
+  const int64_t j = r < p.B * p.we ? r / p.we : p.B + (r - p.B * p.we) / p.wo;
+  return min(2 * m * p.B + j, p.NK - 1);
 }
 
 // Split-segment bookkeeping.  A segment (one sequence and head group) whose real units
@@ -436,7 +449,7 @@ __device__ __forceinline__ int64_t piece_slot(const SplitSeg& sg, int64_t k) {
 // own head.
 template <class F>
 __device__ __forceinline__ void even_split_drive(const Part& p, F&& range) {
-  const int64_t k = blockIdx.x;
+  const int64_t k = p.xcd ? xcd_local_block(blockIdx.x, gridDim.x) : blockIdx.x;
   if (k < p.NK) range(k, part_lo(p, k), part_lo(p, k + 1));
 }
 

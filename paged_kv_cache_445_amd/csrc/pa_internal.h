@@ -62,6 +62,8 @@ struct DecodeArgs {
                             // more than max_rows rows are written NaN
   int32_t b8;               // 8-token blocks: a 16-token tile is two blocks (table entries
                             // 2 j and 2 j + 1), each a pool tile of 8 tokens
+  int32_t xcd_major;        // MODE_EVEN, vector kernel: list in (head group, sequence, tile)
+                            // order with XCD-major owners (see Part)
 };
 
 struct ReshapeArgs {
