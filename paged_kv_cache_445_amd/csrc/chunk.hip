@@ -50,6 +50,11 @@ constexpr int kItemCols = kWaveCols * kWavesPerWG;    // query columns per workg
 constexpr float kLazy = 8.f;                          // reference slack, base-2 exponent
 constexpr float kHeavy = 1.f / 64;                    // heavier weights: hi + lo parts
 
+constexpr int kCuLdsBytes = 160 * 1024;               // LDS of one CU
+
+typedef __attribute__((address_space(1))) void gbl_void_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+
 template <int D>
 struct ChunkTile {
   static constexpr int TILE = 16 * D * 2;                  // one block of one KV head, bytes
@@ -201,14 +206,17 @@ __device__ __forceinline__ void chunk_pv(ChunkCol<D>& st, const op8_t<DT> (&vo)[
 // One work item: rows [j0, j0 + kItemCols / G) of multi-row sequence s for KV head g over the
 // keys [kbeg, kend) (PART: one key partition; else every key the rows see).  The workgroup
 // streams the keys in 32-token units: every unit (K and V of two blocks) is loaded once by
-// the whole workgroup, two units ahead, into one of two LDS buffers, and each wave then runs
-// its 32 query columns (two 16-column MFMA blocks, per-column causal limits) over it.  DT is
-// the 16-bit type of the queries and of the staged unit; F8: the pools hold E4M3 bytes.
-// PART: the item writes the partition's partials (normalised output, max, sum) instead of
-// the output.
-template <int DT, int D, bool F8, bool PART, bool B8>
+// the whole workgroup into LDS, and each wave then runs its 32 query columns (two 16-column
+// MFMA blocks, per-column causal limits) over it.  16-bit pools of 16-token tiles go straight
+// from memory into LDS, US units per barrier; FP8 pools (widened on the way) and 8-token
+// blocks (two blocks per staged tile) go through registers, one unit per barrier.  DT is the
+// 16-bit type of the queries and of the staged unit; F8: the pools hold E4M3 bytes.  PART:
+// the item writes the partition's partials (normalised output, max, sum) instead of the
+// output.
+template <int DT, int D, bool F8, bool PART, bool B8, int US>
 __device__ void chunk_item(const DecodeArgs& a, int s, int g, int cb, int part,
                            char* lds_units) {
+  constexpr bool DMA = !F8 && !B8;  // 16-bit pools of 16-token tiles: direct staging
   using C = MfmaCfg<DT, D>;
   using CT = ChunkTile<D>;
   using T = op8_t<DT>;
@@ -294,100 +302,6 @@ __device__ void chunk_item(const DecodeArgs& a, int s, int g, int cb, int part,
   const int ubeg = kbeg / kMfmaUnit;                     // partitions are whole units
   const int uend = (kend + kMfmaUnit - 1) / kMfmaUnit;
 
-  // This thread's share of a unit: chunk k * kWG + threadIdx.x of the four 16-token tiles of
-  // the staged unit [K tokens 0-15, K tokens 16-31, V tokens 0-15, V tokens 16-31], read from
-  // pool tile ld_blk of the unit at byte src_off:
-  //  - 16-token tiles: 16-bit chunk c of the tile; FP8: its 8 source bytes, half of E4M3 K
-  //    chunk (c / 32) * 16 + c % 16, or bytes 8c.. of the V tile;
-  //  - 8-token blocks: K chunk c = (8-element chunk c / 16, token c % 16) comes from block
-  //    (c / 8) % 2 of the 16-token pair, V chunk c = (dimension c / 2, tokens 8 (c % 2) ..)
-  //    from block c % 2, in the 8-token layouts K [D/X][8][X], V [D][8].
-  int ld_tile[CT::LOADS], ld_off[CT::LOADS], src_off[CT::LOADS], ld_blk[CT::LOADS];
-#pragma unroll
-  for (int k = 0; k < CT::LOADS; ++k) {
-    const int c = k * kWG + threadIdx.x;
-    ld_tile[k] = c / CT::CPT;
-    const int cc = c % CT::CPT;
-    const bool vt = ld_tile[k] & 2;
-    ld_off[k] = vt ? ((cc >> 1) * 2 + ((cc & 1) ^ swz_v(cc >> 1))) * 16
-                   : ((cc >> 4) * 16 + swz_k(ld_tile[k] & 1, cc & 15)) * 16;
-    if constexpr (B8) {
-      const int half = vt ? cc & 1 : (cc >> 3) & 1;
-      ld_blk[k] = 2 * (ld_tile[k] & 1) + half;
-      const int ch = cc >> 4, tok = cc & 7;
-      if constexpr (F8)
-        src_off[k] = vt ? (cc >> 1) * 8 : (((ch >> 1) << 3) + tok) * 16 + 8 * (ch & 1);
-      else
-        src_off[k] = vt ? (cc >> 1) * 16 : ((ch << 3) + tok) * 16;
-    } else {
-      ld_blk[k] = ld_tile[k] & 1;
-      if constexpr (F8)
-        src_off[k] = vt ? cc * 8 : (((cc >> 5) << 4) + (cc & 15)) * 16 + 8 * ((cc >> 4) & 1);
-      else
-        src_off[k] = cc * 16;
-    }
-  }
-  using Raw = typename std::conditional<F8, uint2, uint4>::type;
-  constexpr int WDT = DT == DT_BF16 ? DT_FP8B : DT_FP8;  // widening of FP8 staged bytes
-  // block-table windows of 64 entries, [wbase, wbase + 128): pool tiles (16-token tiles of
-  // the table, or 8-token blocks); entries past the item's last tile hold 0 (masked tokens)
-  int win0 = 0, win1 = 0, wbase = -1;
-  auto load_unit = [&](Raw* regs, int u) {
-    const int e = PER_UNIT * u;
-    if (wbase < 0 || e >= wbase + 128) {  // uniform; happens every 128 / PER_UNIT units
-      wbase = e;
-      if constexpr (B8) {
-        win0 = (e + lane < nblk) ? bt_row[e + lane] : 0;
-        win1 = (e + 64 + lane < nblk) ? bt_row[e + 64 + lane] : 0;
-      } else {
-        win0 = (e + lane < nblk) ? tile_block(bt_row, e + lane, a.blk_shift) : 0;
-        win1 = (e + 64 + lane < nblk) ? tile_block(bt_row, e + 64 + lane, a.blk_shift) : 0;
-      }
-    }
-    const int ia = e - wbase;  // the unit's PER_UNIT entries share one register
-    int64_t bt[PER_UNIT];
-#pragma unroll
-    for (int i = 0; i < PER_UNIT; ++i)
-      bt[i] = ia < 64 ? readlane(win0, ia + i) : readlane(win1, ia + i - 64);
-    // 16-token tiles: a second tile past the keys is replaced by the first (its tokens are
-    // masked)
-    if (!B8 && e + 1 >= nblk) bt[PER_UNIT - 1] = bt[0];
-#pragma unroll
-    for (int k = 0; k < CT::LOADS; ++k) {
-      if constexpr (B8) {
-        int64_t b = bt[0];
-#pragma unroll
-        for (int i = 1; i < PER_UNIT; ++i) b = ld_blk[k] == i ? bt[i] : b;
-        const char* base = (ld_tile[k] & 2 ? vc : kc) + b * blk_stride;
-        regs[k] = *reinterpret_cast<const Raw*>(base + src_off[k]);
-      } else {
-        // a whole wave loads from one tile (256 or 128 threads per tile): a scalar base
-        const int t = __builtin_amdgcn_readfirstlane(ld_tile[k]);
-        const char* base = (t & 2 ? vc : kc) + (t & 1 ? bt[1] : bt[0]) * blk_stride;
-        regs[k] = *reinterpret_cast<const Raw*>(base + src_off[k]);
-      }
-    }
-  };
-  auto store_unit = [&](const Raw* regs, int buf) {
-#pragma unroll
-    for (int k = 0; k < CT::LOADS; ++k) {
-      uint4 v;
-      if constexpr (F8)
-        v = __builtin_bit_cast(uint4, operand<WDT>(regs[k]));
-      else
-        v = regs[k];
-      *reinterpret_cast<uint4*>(lds_units + buf * CT::UNIT + ld_tile[k] * CT::TILE + ld_off[k]) = v;
-    }
-  };
-
-  // Unit pipeline: the loads of unit u + 2 go out at the start of step u, unit u is computed
-  // from LDS buffer u % 2, and unit u + 1 (loaded since the start of step u - 1, so two
-  // compute phases ago) is stored into the other buffer at the end of the step.  Even steps
-  // stage in ra, odd ones in rb.  Loads and stores run on every step (past the last unit
-  // they repeat it and the result is never read), and the barrier between steps does not wait
-  // for outstanding loads, so the compiler's wait before each store covers only that unit.
-  auto barrier = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
-  const int ulast = uend - 1;
   // this lane's operand offsets in the staged unit (swizzled as staged; see swz_k, swz_v):
   // K of S-block b at lk[b] + 1 KiB per kk, V at lv + 512 bytes per j
   int lk[2];
@@ -397,10 +311,12 @@ __device__ void chunk_item(const DecodeArgs& a, int s, int g, int cb, int part,
     lk[b] = (t >> 4) * CT::TILE + r * 256 + swz_k(t >> 4, t & 15) * 16;
   }
   const int lv = (2 + (r >> 1)) * CT::TILE + n * 32 + (((r & 1) ^ swz_v(n)) * 16);
-  auto compute = [&](int u, int buf) {
+
+  // (ub is restrict-qualified: LDS reads through it then carry alias information, which
+  // keeps the compiler from waiting for the direct loads of the other buffer before them)
+  auto compute = [&](int u, const char* __restrict__ ub) {
     const int t0 = u * kMfmaUnit;
     if (u < uend && t0 < kend_w) {  // uniform: this wave's columns see keys of this unit
-      const char* ub = lds_units + buf * CT::UNIT;
       // scores of both column blocks from K (their MFMA chains interleaved), the softmax of
       // each, then P . V from V: K and V are never live together
       uint4 kb[2][C::NKK];
@@ -454,23 +370,163 @@ __device__ void chunk_item(const DecodeArgs& a, int s, int g, int cb, int part,
         if (live[c]) chunk_pv<DT, D>(st[c], vo, pp[c], ones);
     }
   };
-  if (uend > ubeg) {  // uniform; PART: the item's rows may all lie before the partition
-    Raw ra[CT::LOADS], rb[CT::LOADS];
-    load_unit(ra, ubeg);
-    load_unit(rb, min(ubeg + 1, ulast));
-    store_unit(ra, 0);
-    barrier();
-    for (int u = ubeg; u < uend; u += 2) {
-      load_unit(ra, min(u + 2, ulast));
-      compute(u, 0);
-      store_unit(rb, 1);
-      barrier();
-      load_unit(rb, min(u + 3, ulast));
-      compute(u + 1, 1);
+
+  // block-table windows of 64 entries, [wbase, wbase + 128): pool tiles (16-token tiles of
+  // the table, or 8-token blocks); entries past the item's last tile hold 0 (masked tokens)
+  int win0 = 0, win1 = 0, wbase = -1;
+  // the pool tiles of unit u (uniform); 16-token tiles: a second tile past the keys is
+  // replaced by the first (its tokens are masked)
+  auto unit_tiles = [&](int u, int64_t (&bt)[PER_UNIT]) {
+    const int e = PER_UNIT * u;
+    if (wbase < 0 || e >= wbase + 128) {  // uniform; happens every 128 / PER_UNIT units
+      wbase = e;
+      if constexpr (B8) {
+        win0 = (e + lane < nblk) ? bt_row[e + lane] : 0;
+        win1 = (e + 64 + lane < nblk) ? bt_row[e + 64 + lane] : 0;
+      } else {
+        win0 = (e + lane < nblk) ? tile_block(bt_row, e + lane, a.blk_shift) : 0;
+        win1 = (e + 64 + lane < nblk) ? tile_block(bt_row, e + 64 + lane, a.blk_shift) : 0;
+      }
+    }
+    const int ia = e - wbase;  // the unit's PER_UNIT entries share one register
+#pragma unroll
+    for (int i = 0; i < PER_UNIT; ++i)
+      bt[i] = ia < 64 ? readlane(win0, ia + i) : readlane(win1, ia + i - 64);
+    if (!B8 && e + 1 >= nblk) bt[PER_UNIT - 1] = bt[0];
+  };
+  if constexpr (DMA) {
+    // Direct staging: wave w moves staged tile w of every unit [K tokens 0-15, K tokens
+    // 16-31, V tokens 0-15, V tokens 16-31] from the pool into LDS with global_load_lds (one
+    // KiB per instruction, lane i filling bytes 16 i .. 16 i + 15 of it), each lane reading
+    // the 16 pool bytes that the swizzle places at its slot (swz_k and the V swap are
+    // involutions): K slot (row, slot) holds token swz_k(kt, slot) of that row, V slot
+    // (d, half) the half (half ^ swz_v(d)) of dimension d.
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const int soff = wave_u < 2
+                         ? (lane >> 4) * 256 + swz_k(wave_u & 1, lane & 15) * 16
+                         : (lane >> 1) * 32 + ((lane & 1) ^ swz_v(lane >> 1)) * 16;
+    // Step pipeline, US units per step in one of two LDS buffers: the loads of step
+    // k + 1 go out before step k is computed, each wave waits for its own loads at the end of
+    // the step, and the barrier then publishes the next step and frees the buffer just read.
+    auto issue = [&](int u0, char* buf) {
+#pragma unroll
+      for (int i = 0; i < US; ++i) {
+        if (u0 + i >= uend) break;  // uniform
+        int64_t bt[PER_UNIT];
+        unit_tiles(u0 + i, bt);
+        const char* src = (wave_u & 2 ? vc : kc) + (wave_u & 1 ? bt[1] : bt[0]) * blk_stride;
+        char* dst = buf + i * CT::UNIT + wave_u * CT::TILE;
+#pragma unroll
+        for (int pt = 0; pt < CT::TILE / 1024; ++pt)
+          __builtin_amdgcn_global_load_lds((gbl_void_t*)(src + soff + 1024 * pt),
+                                           (lds_void_t*)(dst + 1024 * pt), 16, 0, 0);
+      }
+    };
+    if (uend > ubeg) {  // uniform; PART: the item's rows may all lie before the partition
+      const int steps = (uend - ubeg + US - 1) / US;
+      issue(ubeg, lds_units);
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+      for (int k = 0; k < steps; ++k) {
+        const int u0 = ubeg + US * k;
+        const char* cur = lds_units + (k & 1) * US * CT::UNIT;
+        if (k + 1 < steps) issue(u0 + US, lds_units + ((k + 1) & 1) * US * CT::UNIT);
+#pragma unroll
+        for (int i = 0; i < US; ++i) compute(u0 + i, cur + i * CT::UNIT);
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      }
+    }
+  } else {
+    // Register staging: this thread's share of a unit is chunk k * kWG + threadIdx.x of the
+    // four tiles of the staged unit, read from pool tile ld_blk of the unit at byte src_off:
+    //  - 16-token tiles: 16-bit chunk c of the tile; FP8: its 8 source bytes, half of E4M3 K
+    //    chunk (c / 32) * 16 + c % 16, or bytes 8c.. of the V tile;
+    //  - 8-token blocks: K chunk c = (8-element chunk c / 16, token c % 16) comes from block
+    //    (c / 8) % 2 of the 16-token pair, V chunk c = (dimension c / 2, tokens 8 (c % 2) ..)
+    //    from block c % 2, in the 8-token layouts K [D/X][8][X], V [D][8].
+    int ld_tile[CT::LOADS], ld_off[CT::LOADS], src_off[CT::LOADS], ld_blk[CT::LOADS];
+#pragma unroll
+    for (int k = 0; k < CT::LOADS; ++k) {
+      const int c = k * kWG + threadIdx.x;
+      ld_tile[k] = c / CT::CPT;
+      const int cc = c % CT::CPT;
+      const bool vt = ld_tile[k] & 2;
+      ld_off[k] = vt ? ((cc >> 1) * 2 + ((cc & 1) ^ swz_v(cc >> 1))) * 16
+                     : ((cc >> 4) * 16 + swz_k(ld_tile[k] & 1, cc & 15)) * 16;
+      if constexpr (B8) {
+        const int half = vt ? cc & 1 : (cc >> 3) & 1;
+        ld_blk[k] = 2 * (ld_tile[k] & 1) + half;
+        const int ch = cc >> 4, tok = cc & 7;
+        if constexpr (F8)
+          src_off[k] = vt ? (cc >> 1) * 8 : (((ch >> 1) << 3) + tok) * 16 + 8 * (ch & 1);
+        else
+          src_off[k] = vt ? (cc >> 1) * 16 : ((ch << 3) + tok) * 16;
+      } else {
+        ld_blk[k] = ld_tile[k] & 1;
+        if constexpr (F8)
+          src_off[k] = vt ? cc * 8 : (((cc >> 5) << 4) + (cc & 15)) * 16 + 8 * ((cc >> 4) & 1);
+        else
+          src_off[k] = cc * 16;
+      }
+    }
+    using Raw = typename std::conditional<F8, uint2, uint4>::type;
+    constexpr int WDT = DT == DT_BF16 ? DT_FP8B : DT_FP8;  // widening of FP8 staged bytes
+    auto load_unit = [&](Raw* regs, int u) {
+      int64_t bt[PER_UNIT];
+      unit_tiles(u, bt);
+#pragma unroll
+      for (int k = 0; k < CT::LOADS; ++k) {
+        if constexpr (B8) {
+          int64_t b = bt[0];
+#pragma unroll
+          for (int i = 1; i < PER_UNIT; ++i) b = ld_blk[k] == i ? bt[i] : b;
+          const char* base = (ld_tile[k] & 2 ? vc : kc) + b * blk_stride;
+          regs[k] = *reinterpret_cast<const Raw*>(base + src_off[k]);
+        } else {
+          // a whole wave loads from one tile (256 or 128 threads per tile): a scalar base
+          const int t = __builtin_amdgcn_readfirstlane(ld_tile[k]);
+          const char* base = (t & 2 ? vc : kc) + (t & 1 ? bt[1] : bt[0]) * blk_stride;
+          regs[k] = *reinterpret_cast<const Raw*>(base + src_off[k]);
+        }
+      }
+    };
+    auto store_unit = [&](const Raw* regs, int buf) {
+#pragma unroll
+      for (int k = 0; k < CT::LOADS; ++k) {
+        uint4 v;
+        if constexpr (F8)
+          v = __builtin_bit_cast(uint4, operand<WDT>(regs[k]));
+        else
+          v = regs[k];
+        *reinterpret_cast<uint4*>(lds_units + buf * CT::UNIT + ld_tile[k] * CT::TILE + ld_off[k]) = v;
+      }
+    };
+    // Unit pipeline: the loads of unit u + 2 go out at the start of step u, unit u is
+    // computed from LDS buffer u % 2, and unit u + 1 (loaded since the start of step u - 1,
+    // so two compute phases ago) is stored into the other buffer at the end of the step.  Even
+    // steps stage in ra, odd ones in rb.  Loads and stores run on every step (past the last
+    // unit they repeat it and the result is never read), and the barrier between steps does
+    // not wait for outstanding loads, so the compiler's wait before each store covers only
+    // that unit.
+    auto barrier = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+    const int ulast = uend - 1;
+    if (uend > ubeg) {  // uniform; PART: the item's rows may all lie before the partition
+      Raw ra[CT::LOADS], rb[CT::LOADS];
+      load_unit(ra, ubeg);
+      load_unit(rb, min(ubeg + 1, ulast));
       store_unit(ra, 0);
       barrier();
+      for (int u = ubeg; u < uend; u += 2) {
+        load_unit(ra, min(u + 2, ulast));
+        compute(u, lds_units);
+        store_unit(rb, 1);
+        barrier();
+        load_unit(rb, min(u + 3, ulast));
+        compute(u + 1, lds_units + CT::UNIT);
+        store_unit(ra, 0);
+        barrier();
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the repeated loads past the last unit
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the repeated loads past the last unit
   }
 
   // emit: lane (r, n) holds dimensions 16 j + 4 r + i of column 16 c + n, which is
@@ -521,11 +577,17 @@ constexpr int kMaxOrdered = 256;
 // sequences the items keep the sequence order instead, KV head slowest, numbered XCD-locally
 // so that each XCD works through mostly one KV head.  PART: items are (sequence, column
 // block, partition) of at most one partition each, in sequence order, KV head slowest.
-template <int DT, int D, bool F8, bool PART, bool B8>
+// LDS of the staged units: two buffers of US units (direct staging) or of one unit
+template <int D, bool F8, bool B8, int US>
+constexpr int chunk_stage_bytes() {
+  return 2 * (!F8 && !B8 ? US : 1) * ChunkTile<D>::UNIT;
+}
+
+template <int DT, int D, bool F8, bool PART, bool B8, int US>
 __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(2))) void chunk_kernel(DecodeArgs a) {
   extern __shared__ __align__(16) char lds_raw[];
-  char* lds_units = lds_raw;  // two unit buffers
-  int32_t* base = reinterpret_cast<int32_t*>(lds_raw + 2 * ChunkTile<D>::UNIT);
+  char* lds_units = lds_raw;  // the unit buffers
+  int32_t* base = reinterpret_cast<int32_t*>(lds_raw + chunk_stage_bytes<D, F8, B8, US>());
   int32_t* order = base + a.num_seqs + 1;  // [kMaxOrdered] multi-row sequences, longest first
   int32_t* rbase = order + kMaxOrdered;    // [kMaxOrdered + 1] item prefix in that order
   int32_t* pkeys = rbase + kMaxOrdered + 1;  // [kMaxOrdered] prior keys of order[] entries
@@ -546,7 +608,7 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(2))) void c
       const int s = find_seq(base, S, k, 1);
       const int np = (a.context_lens[s] + a.part_tokens - 1) / a.part_tokens;
       const int idx = (int)(k - base[s]);
-      chunk_item<DT, D, F8, true, B8>(a, s, gh, idx / np, idx % np, lds_units);
+      chunk_item<DT, D, F8, true, B8, US>(a, s, gh, idx / np, idx % np, lds_units);
       __syncthreads();  // the unit buffers are reused by the next item
     }
     return;
@@ -600,34 +662,59 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(2))) void c
       const int nb = base[s + 1] - base[s];
       cb = nb - 1 - (int)(k - base[s]);
     }
-    chunk_item<DT, D, F8, false, B8>(a, s, g, cb, 0, lds_units);
+    chunk_item<DT, D, F8, false, B8, US>(a, s, g, cb, 0, lds_units);
     __syncthreads();  // the unit buffers are reused by the next item
   }
 }
 
-template <int DT, bool F8, bool PART, bool B8>
-static void launch_cb(const DecodeArgs& a, int grid, size_t lds, hipStream_t st) {
-  if (a.head_dim == 64)
-    hipLaunchKernelGGL((chunk_kernel<DT, 64, F8, PART, B8>), dim3(grid), dim3(kWG), lds, st, a);
-  else
-    hipLaunchKernelGGL((chunk_kernel<DT, 128, F8, PART, B8>), dim3(grid), dim3(kWG), lds, st, a);
+int max_lds_per_block() {
+  static int v = [] {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+      n = 65536;
+    return n;
+  }();
+  return v;
 }
 
-template <int DT, bool F8, bool PART>
-static hipError_t launch_c(const DecodeArgs& a, int grid, size_t lds, hipStream_t st) {
-  if (a.b8)
-    launch_cb<DT, F8, PART, true>(a, grid, lds, st);
+// plan_lds: the plan arrays behind the unit buffers.  Direct staging takes two units per
+// barrier where two workgroups of that size still fit a CU's LDS (the chunk kernel runs two
+// per CU), else one.
+template <int DT, int D, bool F8, bool PART, bool B8>
+static hipError_t launch_us(const DecodeArgs& a, int grid, size_t plan_lds, hipStream_t st) {
+  constexpr int two = chunk_stage_bytes<D, F8, B8, 2>();
+  const bool us2 = !F8 && !B8 && 2 * (two + plan_lds) <= (size_t)kCuLdsBytes &&
+                   two + plan_lds <= (size_t)max_lds_per_block();
+  constexpr int one = chunk_stage_bytes<D, F8, B8, 1>();
+  if (us2)
+    hipLaunchKernelGGL((chunk_kernel<DT, D, F8, PART, B8, 2>), dim3(grid), dim3(kWG),
+                       two + plan_lds, st, a);
   else
-    launch_cb<DT, F8, PART, false>(a, grid, lds, st);
+    hipLaunchKernelGGL((chunk_kernel<DT, D, F8, PART, B8, 1>), dim3(grid), dim3(kWG),
+                       one + plan_lds, st, a);
   return hipGetLastError();
 }
 
+template <int DT, bool F8, bool PART, bool B8>
+static hipError_t launch_cb(const DecodeArgs& a, int grid, size_t plan_lds, hipStream_t st) {
+  if (a.head_dim == 64) return launch_us<DT, 64, F8, PART, B8>(a, grid, plan_lds, st);
+  return launch_us<DT, 128, F8, PART, B8>(a, grid, plan_lds, st);
+}
+
+template <int DT, bool F8, bool PART>
+static hipError_t launch_c(const DecodeArgs& a, int grid, size_t plan_lds, hipStream_t st) {
+  if (a.b8) return launch_cb<DT, F8, PART, true>(a, grid, plan_lds, st);
+  return launch_cb<DT, F8, PART, false>(a, grid, plan_lds, st);
+}
+
 template <bool PART>
-static hipError_t launch_dt(int dt, const DecodeArgs& a, int grid, size_t lds, hipStream_t st) {
-  if (dt == DT_F16) return launch_c<DT_F16, false, PART>(a, grid, lds, st);
-  if (dt == DT_BF16) return launch_c<DT_BF16, false, PART>(a, grid, lds, st);
-  if (dt == DT_FP8) return launch_c<DT_F16, true, PART>(a, grid, lds, st);
-  return launch_c<DT_BF16, true, PART>(a, grid, lds, st);
+static hipError_t launch_dt(int dt, const DecodeArgs& a, int grid, size_t plan_lds,
+                            hipStream_t st) {
+  if (dt == DT_F16) return launch_c<DT_F16, false, PART>(a, grid, plan_lds, st);
+  if (dt == DT_BF16) return launch_c<DT_BF16, false, PART>(a, grid, plan_lds, st);
+  if (dt == DT_FP8) return launch_c<DT_F16, true, PART>(a, grid, plan_lds, st);
+  return launch_c<DT_BF16, true, PART>(a, grid, plan_lds, st);
 }
 
 // dt: DT_F16 / DT_BF16 pools, or DT_FP8 / DT_FP8B (FP8 pools behind fp16 / bf16 queries).
@@ -635,15 +722,14 @@ static hipError_t launch_dt(int dt, const DecodeArgs& a, int grid, size_t lds, h
 // than a.max_rows rows, one item per key partition).
 hipError_t launch_chunk(int dt, const DecodeArgs& a, int num_q_rows, hipStream_t st) {
   const int rpi = kItemCols / (a.num_q_heads / a.num_kv_heads);
-  const size_t lds = (size_t)2 * (a.head_dim == 64 ? ChunkTile<64>::UNIT : ChunkTile<128>::UNIT) +
-                     (size_t)(a.num_seqs + 1 + 3 * kMaxOrdered + 2) * sizeof(int32_t);
+  const size_t plan_lds = (size_t)(a.num_seqs + 1 + 3 * kMaxOrdered + 2) * sizeof(int32_t);
   if (a.part_tokens > 0) {
     // at most (ceil(rows / rows_per_item) + num_seqs) column blocks x max_partitions items per
     // KV head, walked with a grid stride by a grid of up to 4096 workgroups
     const int64_t items = ((int64_t)(num_q_rows + rpi - 1) / rpi + a.num_seqs) *
                           a.max_partitions * a.num_kv_heads;
     const int64_t wgs = (std::min<int64_t>(items, 4096) + kXcds - 1) / kXcds * kXcds;
-    return launch_dt<true>(dt, a, (int)wgs, lds, st);
+    return launch_dt<true>(dt, a, (int)wgs, plan_lds, st);
   }
   // one workgroup per work item: at most ceil(rows / rows_per_item) + num_seqs items per KV
   // head; a multiple of the XCD count keeps the XCD-local numbering on
@@ -651,7 +737,7 @@ hipError_t launch_chunk(int dt, const DecodeArgs& a, int num_q_rows, hipStream_t
   const int64_t wgs = (items + kXcds - 1) / kXcds * kXcds;
   const int grid = (int)(wgs < (1 << 20) ? wgs : (1 << 20) / kXcds * kXcds);
   if (grid <= 0) return hipSuccess;
-  return launch_dt<false>(dt, a, grid, lds, st);
+  return launch_dt<false>(dt, a, grid, plan_lds, st);
 }
 
 }  // namespace pa
