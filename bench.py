@@ -448,6 +448,10 @@ def main():
     ap.add_argument("--partitioned", type=int, default=0, metavar="PS",
                     help="time pa_decode_partitioned with PS-token partitions + pa_decode_reduce "
                          "in place of pa_decode")
+    ap.add_argument("--path", choices=("auto", "decode", "shared_prefix"), default="auto",
+                    help="pa_decode, or pa_decode_shared_prefix with the batch's shared leading "
+                         "blocks as one group (auto: the latter for batches built with a shared "
+                         "prefix)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the timed steps, copy a MIB-sized device buffer 3 times "
                          "(a reference kernel of known traffic for HBM byte counters)")
@@ -508,9 +512,23 @@ def main():
         ml = torch.empty((b.num_q_rows, b.num_q_heads, P), dtype=torch.float32, device=dev)
         es = torch.empty_like(ml)
 
+    shared = int(b.meta.get("shared_prefix_blocks", 0))
+    use_prefix = not PS and (args.path == "shared_prefix" or (args.path == "auto" and shared > 0))
+    if use_prefix:
+        if shared <= 0:
+            print("bench.py: --path shared_prefix needs a batch with a shared prefix",
+                  file=sys.stderr)
+            sys.exit(2)
+        db.set_shared_prefix([0, b.num_seqs], [shared], shared)
+        pg, pk, pmax, pws = db.prefix
+
     def decode(i):
         kc, vc = pools[i % copies]
-        if PS:
+        if use_prefix:
+            pa.decode_shared_prefix(db.out, db.q, kc, vc, db.block_tables, db.context_lens,
+                                    db.qsl, pg, pk, pmax, db.scale, pws, db.geom,
+                                    max_query_len=db.max_query_len)
+        elif PS:
             pa.decode_partitioned(tmp, ml, es, db.q, kc, vc, db.block_tables, db.context_lens,
                                   db.qsl, db.scale, PS, P, db.geom)
             pa.decode_reduce(db.out, tmp, ml, es, P, db.geom)
@@ -576,7 +594,8 @@ def main():
     else:
         bound, achieved, peak, punit = "hbm", hbm_bytes / (dec_avg_ms * 1e-3) / 1e9, \
             HBM_PEAK_GBS, "GB/s"
-    traffic_name = args.workload + (f"_part{PS}" if PS else "")
+    traffic_name = args.workload + (f"_part{PS}" if PS else "_decode" if shared and not use_prefix
+                                    else "")
     traffic = read_traffic(traffic_name) if bound == "hbm" else None
 
     if args.copy_calibration > 0:
@@ -620,7 +639,8 @@ def main():
             "kv_unique_bytes_per_step": hbm_bytes,
             "attention_flops_per_step": flops,
             "pool_copies_rotated": copies,
-            "path": f"pa_decode_partitioned({PS}) + pa_decode_reduce" if PS else "pa_decode",
+            "path": (f"pa_decode_partitioned({PS}) + pa_decode_reduce" if PS else
+                     "pa_decode_shared_prefix (one group)" if use_prefix else "pa_decode"),
         },
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "seq_heads_per_s": round(seq_heads / (ms_per_step * 1e-3), 1),
@@ -631,6 +651,8 @@ def main():
             "kernel": (f"pa_decode_partitioned ({PS}-token partitions) + pa_decode_reduce"
                        + (" (+ chunk kernel)" if b.query_start_loc is not None else "")
                        if PS else
+                       "pa_decode_shared_prefix (prefix kernel + decode kernel with in-kernel "
+                       "split merge and prefix fold)" if use_prefix else
                        "pa_decode (decode kernel with in-kernel split merge"
                        + (" + chunk kernel)" if runs_chunk_kernel(b) else ")")),
             "achieved": round(achieved, 2),

@@ -263,6 +263,49 @@ pa_status pa_decode_reduce(void* out, const float* tmp_out, const float* max_log
                            const float* exp_sums, int32_t num_q_rows, int32_t max_partitions,
                            const pa_geom* geom, void* stream);
 
+/*
+ * Decode with shared prefixes.  "vLLM 深度拆解" §5.2 has many requests start with the same
+ * 512-token system prompt, and "vLLM 架构源码解析 第1篇" §4.3.1 keeps such prefix blocks
+ * once, in the block tables of every request that uses them (ref_cnt > 1).  The result is
+ * pa_decode's (every row's attention over its visible keys); what changes is the work: the
+ * keys of a group's shared leading blocks are read once per KV head for the rows of all the
+ * group's sequences (the matrix-core multi-row kernel, those rows as its columns, in
+ * partials of at least 128 keys), and the decode kernel then reads each sequence's keys
+ * past the prefix only and folds the prefix partials into its result by log-sum-exp.  The
+ * grouping is this library's addition; the pages describe the sharing, not how a kernel
+ * uses it.
+ *   prefix_groups  int32 [num_groups + 1] (device), increasing: group i is sequences
+ *                  [prefix_groups[i], prefix_groups[i + 1]); sequences outside every
+ *                  group are decoded as pa_decode does
+ *   prefix_blocks  int32 [num_groups] (device): leading block-table entries the group's
+ *                  sequences are said to share; at most max_prefix_blocks of them are used
+ *   max_prefix_blocks  bound of the shared blocks used (<= max_blocks_per_seq); sizes the
+ *                  workspace
+ * The claim is checked on the device: the prefix of group i is its first
+ * min(prefix_blocks[i], max_prefix_blocks) blocks cut down to whole 32-token units, and a
+ * sequence takes it only when it is a decode or verify sequence (the rows pa_decode's decode
+ * kernel takes), every one of its rows sees every prefix key (prefix <= context_len - rows)
+ * and its table entries over the prefix equal those of the group's first sequence, which
+ * must satisfy the same; any other sequence attends all its keys itself.  A wrong claim
+ * costs work, never correctness.  Needs a 16-bit or FP8 kv_dtype and G | 16 (else
+ * PA_ERR_UNSUPPORTED); the workspace (pa_shared_prefix_workspace_size bytes, device memory,
+ * the caller's) holds pa_decode's workspace, one int per sequence and the prefix partials
+ * (num_q_rows * num_q_heads * up to 8 partials of head_dim + 2 floats).  Other arguments,
+ * ordering and errors as pa_decode; PA_ERR_SHAPE: num_groups or max_prefix_blocks negative
+ * or max_prefix_blocks > max_blocks_per_seq; PA_ERR_NULL: num_groups > 0 without the group
+ * arrays.  Calls that share a workspace must be ordered.
+ */
+size_t pa_shared_prefix_workspace_size(const pa_geom* geom, int32_t num_q_rows,
+                                       int32_t max_prefix_blocks);
+pa_status pa_decode_shared_prefix(void* out, const void* q, const void* k_cache,
+                                  const void* v_cache, const int32_t* block_tables,
+                                  const int32_t* context_lens, const int32_t* query_start_loc,
+                                  int32_t num_q_rows, int32_t max_query_len,
+                                  const int32_t* prefix_groups, const int32_t* prefix_blocks,
+                                  int32_t num_groups, int32_t max_prefix_blocks, float scale,
+                                  void* workspace, size_t workspace_bytes,
+                                  const pa_geom* geom, void* stream);
+
 /* Static description of a status code. */
 const char* pa_status_str(pa_status status);
 

@@ -144,6 +144,23 @@ int64_t pa_bm_take_copies(pa_block_manager* bm, int64_t* pairs_out, int64_t max_
 pa_status pa_bm_block_tables(const pa_block_manager* bm, const int32_t* seq_ids, int32_t num_seqs,
                              int32_t pad_block, int32_t* tables_out, int32_t* context_lens_out);
 
+/*
+ * Groups of sequences for pa_decode_shared_prefix, over num_seqs sequences in the order of
+ * seq_ids (the order of the tables pa_bm_block_tables writes): runs of consecutive sequences
+ * each of which holds at least min_blocks leading blocks (the same physical blocks, shared
+ * through the prefix cache or a fork: "vLLM 架构源码解析 第1篇" §4.3.1) in common with the
+ * sequence before it, counting only blocks that end before the sequence's last token.  A
+ * group's count is the smallest of those overlaps (the blocks every member shares with the
+ * first); a sequence that overlaps its predecessor by fewer than min_blocks starts a new
+ * group, and a group of one sequence gets 0.  groups_out int32 [num_seqs + 1] (group i is
+ * sequences [groups_out[i], groups_out[i + 1]) of the order), blocks_out int32 [num_seqs],
+ * *num_groups_out = the number of groups.  PA_ERR_SHAPE on an unknown or swapped-out id or
+ * min_blocks < 1.
+ */
+pa_status pa_bm_prefix_groups(const pa_block_manager* bm, const int32_t* seq_ids,
+                              int32_t num_seqs, int32_t min_blocks, int32_t* groups_out,
+                              int32_t* blocks_out, int32_t* num_groups_out);
+
 #ifdef __cplusplus
 }
 #endif

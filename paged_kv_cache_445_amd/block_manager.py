@@ -49,6 +49,8 @@ for _fn in (_L.pa_bm_swap_out, _L.pa_bm_swap_in):
     _fn.argtypes = [_vp, _i32, _i64p, ctypes.c_int64, _i64p]
 _L.pa_bm_block_tables.restype = ctypes.c_int
 _L.pa_bm_block_tables.argtypes = [_vp, _i32p, _i32, _i32, _i32p, _i32p]
+_L.pa_bm_prefix_groups.restype = ctypes.c_int
+_L.pa_bm_prefix_groups.argtypes = [_vp, _i32p, _i32, _i32, _i32p, _i32p, _i32p]
 
 
 def _check(fn, code):
@@ -170,3 +172,16 @@ class BlockManager:
                                      int(pad_block), tables.ctypes.data_as(_i32p),
                                      lens.ctypes.data_as(_i32p)))
         return tables, lens
+
+    def prefix_groups(self, seq_ids, min_blocks: int = 1):
+        """(groups int32 [num_groups + 1], blocks int32 [num_groups]) for
+        pa_decode_shared_prefix over the sequences in the order of seq_ids."""
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int32)
+        groups = np.empty(ids.size + 1, dtype=np.int32)
+        blocks = np.empty(max(ids.size, 1), dtype=np.int32)
+        ng = ctypes.c_int32()
+        _check("pa_bm_prefix_groups",
+               _L.pa_bm_prefix_groups(self._h, ids.ctypes.data_as(_i32p), int(ids.size),
+                                      int(min_blocks), groups.ctypes.data_as(_i32p),
+                                      blocks.ctypes.data_as(_i32p), ctypes.byref(ng)))
+        return groups[:ng.value + 1].copy(), blocks[:ng.value].copy()

@@ -10,6 +10,7 @@
 
 #include <stdint.h>
 
+#include <algorithm>
 #include <new>
 #include <unordered_map>
 #include <vector>
@@ -417,6 +418,49 @@ pa_status pa_bm_block_tables(const pa_block_manager* bm, const int32_t* seq_ids,
     for (int32_t j = 0; j < MB; ++j) row[j] = j < n ? s.blocks[j] : pad_block;
     context_lens_out[i] = s.len;
   }
+  return PA_OK;
+}
+
+pa_status pa_bm_prefix_groups(const pa_block_manager* bm, const int32_t* seq_ids,
+                              int32_t num_seqs, int32_t min_blocks, int32_t* groups_out,
+                              int32_t* blocks_out, int32_t* num_groups_out) {
+  if (!bm || !num_groups_out) return PA_ERR_NULL;
+  if (num_seqs < 0 || min_blocks < 1) return PA_ERR_SHAPE;
+  if (num_seqs == 0) {
+    *num_groups_out = 0;
+    if (groups_out) groups_out[0] = 0;
+    return PA_OK;
+  }
+  if (!seq_ids || !groups_out || !blocks_out) return PA_ERR_NULL;
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    const Seq* s = bm->seq(seq_ids[i]);
+    if (!s || s->swapped) return PA_ERR_SHAPE;
+  }
+  // blocks that end before the sequence's last token
+  auto full = [&](const Seq& s) { return s.len > 0 ? (s.len - 1) / bm->block_size : 0; };
+  int32_t ng = 0, start = 0;
+  groups_out[0] = 0;
+  int32_t common = full(*bm->seq(seq_ids[0]));
+  auto close = [&](int32_t end) {
+    blocks_out[ng] = end - start > 1 ? common : 0;
+    groups_out[++ng] = end;
+    start = end;
+  };
+  for (int32_t i = 1; i < num_seqs; ++i) {
+    const Seq& a = *bm->seq(seq_ids[i - 1]);
+    const Seq& b = *bm->seq(seq_ids[i]);
+    const int32_t lim = std::min(std::min(full(a), full(b)), common);
+    int32_t l = 0;
+    while (l < lim && a.blocks[l] == b.blocks[l]) ++l;
+    if (l >= min_blocks) {
+      common = l;  // l <= common: the blocks every member shares with the first
+    } else {
+      close(i);
+      common = full(b);
+    }
+  }
+  close(num_seqs);
+  *num_groups_out = ng;
   return PA_OK;
 }
 

@@ -96,6 +96,75 @@ __device__ inline void build_chunk_plan(int32_t* base, const ChunkPlanIn& p) {
   });
 }
 
+// What a chunk-kernel launch computes.
+enum ChunkMode : int {
+  CM_ROWS = 0,    // pa_decode: every row of the multi-row sequences, causal, to `out`
+  CM_PART = 1,    // pa_decode_partitioned: per key partition, partials
+  CM_PREFIX = 2,  // shared prefixes: every row of a group over the group's shared keys,
+                  // per key partition, partials
+};
+
+// Group i of a shared-prefix call: its sequences [gs, ge) (clamped to the batch), their rows
+// [r0, r1), and `keys`: the keys of the group's claimed leading blocks (grp_blocks[i], at
+// most max_prefix_blocks) in whole 32-token units, 0 when the group is empty or when its
+// first sequence has a row that does not see all of them (then no table entry of the group
+// is ever used).
+struct PrefixGroup {
+  int gs, ge, r0, r1, keys;
+};
+
+__device__ inline PrefixGroup prefix_group(const DecodeArgs& a, int i) {
+  PrefixGroup p;
+  p.gs = min(max(a.grp_start[i], 0), a.num_seqs);
+  p.ge = min(max(a.grp_start[i + 1], p.gs), a.num_seqs);
+  p.r0 = a.qsl ? a.qsl[p.gs] : p.gs;
+  p.r1 = a.qsl ? a.qsl[p.ge] : p.ge;
+  const int blocks = min(a.grp_blocks[i], a.max_prefix_blocks);
+  p.keys = blocks > 0 ? blocks * a.block_size / kMfmaUnit * kMfmaUnit : 0;
+  if (p.ge > p.gs) {
+    const int rows = (a.qsl ? a.qsl[p.gs + 1] : p.gs + 1) - p.r0;
+    if (rows < 1 || p.keys > a.context_lens[p.gs] - rows) p.keys = 0;
+  } else {
+    p.keys = 0;
+  }
+  return p;
+}
+
+// skip_out[s] for every sequence s (prefix mode, waves w, w + W, ...): the keys of its
+// group's shared prefix when s is a sequence the decode kernel takes (1 .. max_rows rows),
+// each of its rows sees every key of the prefix and its table entries over the prefix are
+// those of the group's first sequence; else 0 (the decode or chunk kernel attends all its
+// keys).
+__device__ inline void write_skips(const DecodeArgs& a, int64_t w, int64_t W) {
+  const int lane = lane_id();
+  for (int64_t s = w; s < a.num_seqs; s += W) {
+    int sk = 0;
+    // the group of s: the largest i with grp_start[i] <= s
+    int lo = 0, hi = a.num_groups - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.grp_start[mid] <= s)
+        lo = mid;
+      else
+        hi = mid - 1;
+    }
+    const PrefixGroup pg = prefix_group(a, lo);
+    if (pg.keys > 0 && s >= pg.gs && s < pg.ge) {
+      const int row = a.qsl ? a.qsl[s] : (int)s;
+      const int rows = (a.qsl ? a.qsl[s + 1] : (int)s + 1) - row;
+      if (rows >= 1 && rows <= a.max_rows && pg.keys <= a.context_lens[s] - rows) {
+        const int nb = (pg.keys + a.block_size - 1) / a.block_size;
+        const int32_t* mine = a.block_tables + s * a.max_blocks_per_seq;
+        const int32_t* lead = a.block_tables + (int64_t)pg.gs * a.max_blocks_per_seq;
+        bool differ = false;
+        for (int j = lane; j < nb; j += kWave) differ |= mine[j] != lead[j];
+        if (!__builtin_amdgcn_ballot_w64(differ)) sk = pg.keys;
+      }
+    }
+    if (lane == 0) a.skip_out[s] = sk;
+  }
+}
+
 // Per-lane state of one 16-column block: outputs O[column n][dims 16 j + 4 r ..], the
 // weight sum (all four entries equal), the weights' reference and the true running max
 // (both base 2, scaled scores).
@@ -213,10 +282,12 @@ __device__ __forceinline__ void chunk_pv(ChunkCol<D>& st, const op8_t<DT> (&vo)[
 // 16-bit type of the queries and of the staged unit; F8: the pools hold E4M3 bytes.  PART:
 // the item writes the partition's partials (normalised output, max, sum) instead of the
 // output.
-template <int DT, int D, bool F8, bool PART, bool B8, int US>
+template <int DT, int D, bool F8, int CM, bool B8, int US>
 __device__ void chunk_item(const DecodeArgs& a, int s, int g, int cb, int part,
                            char* lds_units) {
   constexpr bool DMA = !F8 && !B8;  // 16-bit pools of 16-token tiles: direct staging
+  constexpr bool PART = CM != CM_ROWS;
+  constexpr bool PRE = CM == CM_PREFIX;
   using C = MfmaCfg<DT, D>;
   using CT = ChunkTile<D>;
   using T = op8_t<DT>;
@@ -226,9 +297,27 @@ __device__ void chunk_item(const DecodeArgs& a, int s, int g, int cb, int part,
   const int wave = threadIdx.x / kWave;
   const int r = lane >> 4, n = lane & 15;
   const int G = a.num_q_heads / a.num_kv_heads;
-  const int q0 = __builtin_amdgcn_readfirstlane(a.qsl[s]);
-  const int nrows = __builtin_amdgcn_readfirstlane(a.qsl[s + 1]) - q0;
-  const int ctx = __builtin_amdgcn_readfirstlane(a.context_lens[s]);
+  // the item's rows [q0, q0 + nrows), its keys [0, ctx) and the sequence whose table holds
+  // them: a sequence, or (PRE) group s, whose rows all see every shared key
+  int q0, nrows, ctx, bts;
+  if constexpr (PRE) {
+    const PrefixGroup pg = prefix_group(a, s);
+    q0 = pg.r0;
+    nrows = pg.r1 - pg.r0;
+    ctx = pg.keys;
+    bts = pg.gs;
+  } else {
+    q0 = a.qsl[s];
+    nrows = a.qsl[s + 1] - q0;
+    ctx = a.context_lens[s];
+    bts = s;
+  }
+  q0 = __builtin_amdgcn_readfirstlane(q0);
+  nrows = __builtin_amdgcn_readfirstlane(nrows);
+  ctx = __builtin_amdgcn_readfirstlane(ctx);
+  bts = __builtin_amdgcn_readfirstlane(bts);
+  // the last key row j sees: causal (position ctx - nrows + j), or every key (PRE)
+  auto vis = [&](int j) { return PRE ? ctx - 1 : ctx - nrows + j; };
   const int RW = kWaveCols / G;                    // rows per wave
   const int j0g = cb * (kItemCols / G);            // first row of the workgroup
   const int jendg = min(nrows, j0g + kItemCols / G);
@@ -237,8 +326,8 @@ __device__ void chunk_item(const DecodeArgs& a, int s, int g, int cb, int part,
   // keys [kbeg, kend) any column of the item may see; this wave's columns see keys below
   // kend_w
   const int kbeg = PART ? part * a.part_tokens : 0;
-  int kend = ctx - nrows + jendg;
-  int kend_w = jend > j0 ? ctx - nrows + jend : 0;
+  int kend = vis(jendg - 1) + 1;
+  int kend_w = jend > j0 ? vis(jend - 1) + 1 : 0;
   if (PART) {
     kend = min(kend, kbeg + a.part_tokens);
     kend_w = min(kend_w, kbeg + a.part_tokens);
@@ -261,8 +350,8 @@ __device__ void chunk_item(const DecodeArgs& a, int s, int g, int cb, int part,
     const int col = 16 * c + n;
     const int jc = j0 + col / G, hc = col % G;
     const bool ok = jc < jend;
-    pos[c] = ok ? ctx - nrows + jc : -1;
-    first[c] = ctx - nrows + j0 + (16 * c) / G;
+    pos[c] = ok ? vis(jc) : -1;
+    first[c] = vis(j0 + (16 * c) / G);
     full[c] = j0 + (16 * c + 15) / G < jend;
     live[c] = j0 + (16 * c) / G < jend;
     const char* qp = reinterpret_cast<const char*>(a.q) +
@@ -295,7 +384,7 @@ __device__ void chunk_item(const DecodeArgs& a, int s, int g, int cb, int part,
   const int64_t blk_stride = (int64_t)a.num_kv_heads * PTILE;
   const char* kc = reinterpret_cast<const char*>(a.k_cache) + (int64_t)g * PTILE;
   const char* vc = reinterpret_cast<const char*>(a.v_cache) + (int64_t)g * PTILE;
-  const int32_t* bt_row = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+  const int32_t* bt_row = a.block_tables + (int64_t)bts * a.max_blocks_per_seq;
   constexpr int TT = B8 ? 8 : kBlock;                    // tokens of one pool tile
   constexpr int PER_UNIT = kMfmaUnit / TT;               // pool tiles per unit
   const int nblk = (kend + TT - 1) / TT;
@@ -569,32 +658,64 @@ __device__ void chunk_item(const DecodeArgs& a, int s, int g, int cb, int part,
 // Most multi-row sequences whose items are ordered longest first (see chunk_kernel).
 constexpr int kMaxOrdered = 256;
 
-// Work items, one per workgroup.  Items differ in length by up to the longest context over
-// the shortest, and workgroups start in index order as earlier ones finish, so the items are
-// numbered longest first: multi-row sequences by decreasing number of prior keys, within a
-// sequence column blocks last to first (the longest causal ranges first), and the KV heads
-// of one (sequence, column block) consecutively.  With more than kMaxOrdered multi-row
-// sequences the items keep the sequence order instead, KV head slowest, numbered XCD-locally
-// so that each XCD works through mostly one KV head.  PART: items are (sequence, column
-// block, partition) of at most one partition each, in sequence order, KV head slowest.
 // LDS of the staged units: two buffers of US units (direct staging) or of one unit
 template <int D, bool F8, bool B8, int US>
 constexpr int chunk_stage_bytes() {
   return 2 * (!F8 && !B8 ? US : 1) * ChunkTile<D>::UNIT;
 }
 
-template <int DT, int D, bool F8, bool PART, bool B8, int US>
+// Work items, one per workgroup.  Items differ in length by up to the longest context over
+// the shortest, and workgroups start in index order as earlier ones finish, so the items are
+// numbered longest first: multi-row sequences by decreasing number of prior keys, within a
+// sequence column blocks last to first (the longest causal ranges first), and the KV heads
+// of one (sequence, column block) consecutively.  With more than kMaxOrdered multi-row
+// sequences the items keep the sequence order instead, KV head slowest, numbered XCD-locally
+// so that each XCD works through mostly one KV head.  CM_PART: items are (sequence, column
+// block, partition) of at most one partition each, in sequence order, KV head slowest;
+// CM_PREFIX the same over the groups' shared keys, and then the skips of every sequence.
+template <int DT, int D, bool F8, int CM, bool B8, int US>
 __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(2))) void chunk_kernel(DecodeArgs a) {
   extern __shared__ __align__(16) char lds_raw[];
   char* lds_units = lds_raw;  // the unit buffers
   int32_t* base = reinterpret_cast<int32_t*>(lds_raw + chunk_stage_bytes<D, F8, B8, US>());
+  const int G = a.num_q_heads / a.num_kv_heads;
+  const int S = a.num_seqs;
+  const int Hkv = a.num_kv_heads;
+
+  if constexpr (CM == CM_PREFIX) {
+    // items per group: column blocks x key partitions of its shared keys
+    const int NG = a.num_groups;
+    const int rpi = kItemCols / G;
+    wave_plan(base, NG, [&](int i) {
+      const PrefixGroup pg = prefix_group(a, i);
+      if (pg.keys <= 0 || pg.r1 <= pg.r0) return 0;
+      return (pg.r1 - pg.r0 + rpi - 1) / rpi * ((pg.keys + a.part_tokens - 1) / a.part_tokens);
+    });
+    const int64_t per_head = base[NG];
+    const int64_t total = per_head * Hkv;
+    for (int64_t i = xcd_local_block(blockIdx.x, gridDim.x); i < total; i += gridDim.x) {
+      const int gh = (int)(i / per_head);
+      const int64_t k = i - (int64_t)gh * per_head;
+      const int grp = find_seq(base, NG, k, 1);
+      const int np = (prefix_group(a, grp).keys + a.part_tokens - 1) / a.part_tokens;
+      const int idx = (int)(k - base[grp]);
+      chunk_item<DT, D, F8, CM_PREFIX, B8, US>(a, grp, gh, idx / np, idx % np, lds_units);
+      __syncthreads();  // the unit buffers are reused by the next item
+    }
+    // the skips last, off the items' path (the decode kernel that reads them runs after this
+    // kernel); the workgroups without items take them first
+    const int64_t items_wg = min(total, (int64_t)gridDim.x);
+    const int64_t rank = (xcd_local_block(blockIdx.x, gridDim.x) - items_wg + gridDim.x) %
+                         gridDim.x;
+    write_skips(a, rank * kWavesPerWG + threadIdx.x / kWave, (int64_t)gridDim.x * kWavesPerWG);
+    return;
+  }
+
   int32_t* order = base + a.num_seqs + 1;  // [kMaxOrdered] multi-row sequences, longest first
   int32_t* rbase = order + kMaxOrdered;    // [kMaxOrdered + 1] item prefix in that order
   int32_t* pkeys = rbase + kMaxOrdered + 1;  // [kMaxOrdered] prior keys of order[] entries
   int32_t* count = pkeys + kMaxOrdered;
-  const int G = a.num_q_heads / a.num_kv_heads;
-  const int S = a.num_seqs;
-  const int Hkv = a.num_kv_heads;
+  constexpr bool PART = CM == CM_PART;
   ChunkPlanIn pin{a.qsl, a.context_lens, S, kItemCols / G, a.max_rows + 1,
                   PART ? a.part_tokens : 0};
   build_chunk_plan(base, pin);
@@ -608,7 +729,7 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(2))) void c
       const int s = find_seq(base, S, k, 1);
       const int np = (a.context_lens[s] + a.part_tokens - 1) / a.part_tokens;
       const int idx = (int)(k - base[s]);
-      chunk_item<DT, D, F8, true, B8, US>(a, s, gh, idx / np, idx % np, lds_units);
+      chunk_item<DT, D, F8, CM_PART, B8, US>(a, s, gh, idx / np, idx % np, lds_units);
       __syncthreads();  // the unit buffers are reused by the next item
     }
     return;
@@ -662,7 +783,7 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(2))) void c
       const int nb = base[s + 1] - base[s];
       cb = nb - 1 - (int)(k - base[s]);
     }
-    chunk_item<DT, D, F8, false, B8, US>(a, s, g, cb, 0, lds_units);
+    chunk_item<DT, D, F8, CM_ROWS, B8, US>(a, s, g, cb, 0, lds_units);
     __syncthreads();  // the unit buffers are reused by the next item
   }
 }
@@ -681,40 +802,45 @@ int max_lds_per_block() {
 // plan_lds: the plan arrays behind the unit buffers.  Direct staging takes two units per
 // barrier where two workgroups of that size still fit a CU's LDS (the chunk kernel runs two
 // per CU), else one.
-template <int DT, int D, bool F8, bool PART, bool B8>
+template <int DT, int D, bool F8, int CM, bool B8>
 static hipError_t launch_us(const DecodeArgs& a, int grid, size_t plan_lds, hipStream_t st) {
-  constexpr int two = chunk_stage_bytes<D, F8, B8, 2>();
-  const bool us2 = !F8 && !B8 && 2 * (two + plan_lds) <= (size_t)kCuLdsBytes &&
-                   two + plan_lds <= (size_t)max_lds_per_block();
   constexpr int one = chunk_stage_bytes<D, F8, B8, 1>();
-  if (us2)
-    hipLaunchKernelGGL((chunk_kernel<DT, D, F8, PART, B8, 2>), dim3(grid), dim3(kWG),
-                       two + plan_lds, st, a);
-  else
-    hipLaunchKernelGGL((chunk_kernel<DT, D, F8, PART, B8, 1>), dim3(grid), dim3(kWG),
-                       one + plan_lds, st, a);
+  if constexpr (!F8 && !B8) {
+    constexpr int two = chunk_stage_bytes<D, F8, B8, 2>();
+    if (2 * (two + plan_lds) <= (size_t)kCuLdsBytes && two + plan_lds <= (size_t)max_lds_per_block()) {
+      hipLaunchKernelGGL((chunk_kernel<DT, D, F8, CM, B8, 2>), dim3(grid), dim3(kWG),
+                         two + plan_lds, st, a);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((chunk_kernel<DT, D, F8, CM, B8, 1>), dim3(grid), dim3(kWG), one + plan_lds,
+                     st, a);
   return hipGetLastError();
 }
 
-template <int DT, bool F8, bool PART, bool B8>
+template <int DT, bool F8, int CM, bool B8>
 static hipError_t launch_cb(const DecodeArgs& a, int grid, size_t plan_lds, hipStream_t st) {
-  if (a.head_dim == 64) return launch_us<DT, 64, F8, PART, B8>(a, grid, plan_lds, st);
-  return launch_us<DT, 128, F8, PART, B8>(a, grid, plan_lds, st);
+  if (a.head_dim == 64) return launch_us<DT, 64, F8, CM, B8>(a, grid, plan_lds, st);
+  return launch_us<DT, 128, F8, CM, B8>(a, grid, plan_lds, st);
 }
 
-template <int DT, bool F8, bool PART>
+template <int DT, bool F8, int CM>
 static hipError_t launch_c(const DecodeArgs& a, int grid, size_t plan_lds, hipStream_t st) {
-  if (a.b8) return launch_cb<DT, F8, PART, true>(a, grid, plan_lds, st);
-  return launch_cb<DT, F8, PART, false>(a, grid, plan_lds, st);
+  if (a.b8) return launch_cb<DT, F8, CM, true>(a, grid, plan_lds, st);
+  return launch_cb<DT, F8, CM, false>(a, grid, plan_lds, st);
 }
 
-template <bool PART>
+template <int CM>
 static hipError_t launch_dt(int dt, const DecodeArgs& a, int grid, size_t plan_lds,
                             hipStream_t st) {
-  if (dt == DT_F16) return launch_c<DT_F16, false, PART>(a, grid, plan_lds, st);
-  if (dt == DT_BF16) return launch_c<DT_BF16, false, PART>(a, grid, plan_lds, st);
-  if (dt == DT_FP8) return launch_c<DT_F16, true, PART>(a, grid, plan_lds, st);
-  return launch_c<DT_BF16, true, PART>(a, grid, plan_lds, st);
+  if (dt == DT_F16) return launch_c<DT_F16, false, CM>(a, grid, plan_lds, st);
+  if (dt == DT_BF16) return launch_c<DT_BF16, false, CM>(a, grid, plan_lds, st);
+  if (dt == DT_FP8) return launch_c<DT_F16, true, CM>(a, grid, plan_lds, st);
+  return launch_c<DT_BF16, true, CM>(a, grid, plan_lds, st);
+}
+
+static size_t plan_bytes(int entries) {
+  return (size_t)(entries + 1 + 3 * kMaxOrdered + 2) * sizeof(int32_t);
 }
 
 // dt: DT_F16 / DT_BF16 pools, or DT_FP8 / DT_FP8B (FP8 pools behind fp16 / bf16 queries).
@@ -722,14 +848,14 @@ static hipError_t launch_dt(int dt, const DecodeArgs& a, int grid, size_t plan_l
 // than a.max_rows rows, one item per key partition).
 hipError_t launch_chunk(int dt, const DecodeArgs& a, int num_q_rows, hipStream_t st) {
   const int rpi = kItemCols / (a.num_q_heads / a.num_kv_heads);
-  const size_t plan_lds = (size_t)(a.num_seqs + 1 + 3 * kMaxOrdered + 2) * sizeof(int32_t);
+  const size_t plan_lds = plan_bytes(a.num_seqs);
   if (a.part_tokens > 0) {
     // at most (ceil(rows / rows_per_item) + num_seqs) column blocks x max_partitions items per
     // KV head, walked with a grid stride by a grid of up to 4096 workgroups
     const int64_t items = ((int64_t)(num_q_rows + rpi - 1) / rpi + a.num_seqs) *
                           a.max_partitions * a.num_kv_heads;
     const int64_t wgs = (std::min<int64_t>(items, 4096) + kXcds - 1) / kXcds * kXcds;
-    return launch_dt<true>(dt, a, (int)wgs, plan_lds, st);
+    return launch_dt<CM_PART>(dt, a, (int)wgs, plan_lds, st);
   }
   // one workgroup per work item: at most ceil(rows / rows_per_item) + num_seqs items per KV
   // head; a multiple of the XCD count keeps the XCD-local numbering on
@@ -737,7 +863,22 @@ hipError_t launch_chunk(int dt, const DecodeArgs& a, int num_q_rows, hipStream_t
   const int64_t wgs = (items + kXcds - 1) / kXcds * kXcds;
   const int grid = (int)(wgs < (1 << 20) ? wgs : (1 << 20) / kXcds * kXcds);
   if (grid <= 0) return hipSuccess;
-  return launch_dt<false>(dt, a, grid, plan_lds, st);
+  return launch_dt<CM_ROWS>(dt, a, grid, plan_lds, st);
+}
+
+// The shared-prefix kernel: every group's rows over its shared keys, a.part_tokens keys per
+// partial (a.part_o / part_m / part_l with a.max_partitions slots per row and head), and
+// a.skip_out for every sequence.  At most (ceil(rows / rows_per_item) + num_groups) column
+// blocks x max_partitions items per KV head, walked with a grid stride by up to 4096
+// workgroups (at least one per XCD, which also write the skips).
+hipError_t launch_prefix(int dt, const DecodeArgs& a, int num_q_rows, hipStream_t st) {
+  const int rpi = kItemCols / (a.num_q_heads / a.num_kv_heads);
+  const int64_t items = ((int64_t)(num_q_rows + rpi - 1) / rpi + a.num_groups) *
+                        a.max_partitions * a.num_kv_heads;
+  const int64_t wgs = (std::max<int64_t>(std::min<int64_t>(items, 4096), 1) + kXcds - 1) /
+                      kXcds * kXcds;
+  return launch_dt<CM_PREFIX>(dt, a, (int)wgs, plan_bytes(std::max(a.num_seqs, a.num_groups)),
+                              st);
 }
 
 }  // namespace pa

@@ -100,14 +100,68 @@ __device__ void mfma_attend(const DecodeArgs& a, int s, int g, int u0, int u1, i
   }
 }
 
+// Folds the np shared-prefix partials of (row, query head h) into a merged column held as
+// (M, L, U): this lane's dimensions 16 j + 4 r + i are U[4 j + i].
+template <int D>
+__device__ __forceinline__ void m_fold(const DecodeArgs& a, float& M, float& L,
+                                       float (&U)[4 * (D / 16)], int64_t row, int h, int np) {
+  const int r = lane_id() >> 4;
+  const int64_t e = (row * a.num_q_heads + h) * a.pre_parts;
+  fold_prefix<4 * (D / 16), 2>(M, L, U, a.pre_m + e, a.pre_l + e, a.pre_o + e * D, D, np,
+                               [&](int k) { return 16 * (k >> 2) + 4 * r + (k & 3); });
+}
+
+// Column n of a segment's first query row row0 and KV head g: its row and query head (one
+// row without MULTI).
+template <bool MULTI>
+__device__ __forceinline__ void m_column(const DecodeArgs& a, int n, int row0, int g,
+                                         int64_t& row, int& h, int& jr, int& hc) {
+  const int G = a.num_q_heads / a.num_kv_heads;
+  jr = MULTI ? n / G : 0;
+  hc = MULTI ? n - jr * G : n;
+  row = (int64_t)row0 + jr;
+  h = g * G + hc;
+}
+
+// A whole segment of a sequence with a shared prefix: its keys past the prefix, folded with
+// the prefix partials of each column, written to `out` (the segment's first column at ob).
+template <int DT, int D, bool MULTI>
+__device__ void m_prefix_emit(const DecodeArgs& a, const MfmaState<DT, D>& st, int ncols,
+                              int row0, int g, int np, int64_t ob) {
+  using C = MfmaCfg<DT, D>;
+  constexpr int NE = 4 * C::NJ;
+  const int lane = lane_id();
+  const int r = lane >> 4, n = lane & 15;
+  float L = cross_rows_sum(st.l);
+  if (n >= ncols) return;
+  float M = st.m * 0.69314718055994531f;
+  float U[NE];
+#pragma unroll
+  for (int j = 0; j < C::NJ; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) U[4 * j + i] = st.acc[j][i];
+  int64_t row;
+  int h, jr, hc;
+  m_column<MULTI>(a, n, row0, g, row, h, jr, hc);
+  m_fold<D>(a, M, L, U, row, h, np);
+  const int64_t ocol = ob + ((int64_t)jr * a.num_q_heads + hc) * D;
+  const float rinv = 1.f / L;
+#pragma unroll
+  for (int j = 0; j < C::NJ; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      store_out<DT>(a.out, ocol + 16 * j + 4 * r + i, U[4 * j + i] * rinv, a.out_f32);
+}
+
 // A piece of a split segment (the ncols query columns of one KV head): publish it, or, as
 // the segment's last arrival, merge every piece and write the output (the segment's first
-// column at ob).  Each lane merges its own column n and dimensions 16 j + 4 r .. + 3, so no lanes
-// interact.  Partial slots hold a.cols columns.
+// column at ob; with np > 0 folded with the shared-prefix partials of each column, the
+// segment's first row being row0).  Each lane merges its own column n and dimensions
+// 16 j + 4 r .. + 3, so no lanes interact.  Partial slots hold a.cols columns.
 template <int DT, int D, bool MULTI>
 __device__ void m_split_finish(const DecodeArgs& a, const MfmaState<DT, D>& st, int ncols,
                                const SplitSeg& sg, int64_t self, int32_t* cnt, int seen,
-                               int64_t ob) {
+                               int64_t ob, int row0, int g, int np) {
   using C = MfmaCfg<DT, D>;
   constexpr int NE = 4 * C::NJ;
   const int lane = lane_id();
@@ -135,8 +189,8 @@ __device__ void m_split_finish(const DecodeArgs& a, const MfmaState<DT, D>& st, 
     }
   }, [] {});
   if (!last) return;
-  float L[1], U[1][NE];
-  merge_ordered<1, NE, 2>(L, U, sg.k0, sg.k1,
+  float M[1], L[1], U[1][NE];
+  merge_ordered<1, NE, 2>(M, L, U, sg.k0, sg.k1,
                           [&](int64_t k, float (&m)[1], float (&lk)[1], float (&ov)[1][NE]) {
     if (k == self || !col) {
       m[0] = mine_m;
@@ -160,8 +214,10 @@ __device__ void m_split_finish(const DecodeArgs& a, const MfmaState<DT, D>& st, 
   });
   if (col) {
     // column n: row offset n / G, head n % G (one row without MULTI)
-    const int G = a.num_q_heads / a.num_kv_heads;
-    const int jr = MULTI ? n / G : 0, hc = MULTI ? n - jr * G : n;
+    int64_t row;
+    int h, jr, hc;
+    m_column<MULTI>(a, n, row0, g, row, h, jr, hc);
+    if (np > 0) m_fold<D>(a, M[0], L[0], U[0], row, h, np);
     const int64_t ocol = ob + ((int64_t)jr * a.num_q_heads + hc) * D;
     const float rinv = 1.f / L[0];
 #pragma unroll
@@ -191,7 +247,7 @@ mfma_decode_kernel(DecodeArgs a) {
   const int64_t w = (int64_t)blockIdx.x * kWavesPerWG + wave;
 
   if constexpr (MODE == MODE_EVEN) {
-    PlanIn pin{a.context_lens, a.qsl, S, kMfmaUnit, a.seg_extra, a.max_rows};
+    PlanIn pin{a.context_lens, a.qsl, S, kMfmaUnit, a.seg_extra, a.max_rows, a.skip};
     build_plan(base, pin);
     zero_empty_rows<DT>(pin, a.out, a.num_q_heads, D, w, W, a.out_f32, a.nan_rows);
     // units: (sequence, group of kWavesPerWG KV heads, unit); wave i runs KV head i of each
@@ -211,6 +267,11 @@ mfma_decode_kernel(DecodeArgs a) {
         const int u0 = (int)(i - seg0), u1 = (int)min(pe - seg0, (int64_t)nu);
         if (g < a.num_kv_heads && u0 < nu) {
           const int ctx = a.context_lens[s];
+          // keys [0, sk) come from the shared-prefix partials (np of them): the units start
+          // past them
+          const int sk = a.skip ? a.skip[s] : 0;
+          const int us = sk / kMfmaUnit;
+          const int np = sk > 0 ? (sk + a.pre_tokens - 1) / a.pre_tokens : 0;
           const int row = a.qsl ? a.qsl[s] : s;
           const int nr = MULTI ? a.qsl[s + 1] - row : 1;
           const bool whole = u0 == 0 && u1 == nu;
@@ -223,14 +284,16 @@ mfma_decode_kernel(DecodeArgs a) {
             seen = counter_peek(cnt);  // consumed after the units
           }
           MfmaState<DT, D> st;
-          mfma_attend<DT, D, MULTI, LEAN, B8>(a, s, g, u0, u1, ctx, nr, st);
+          mfma_attend<DT, D, MULTI, LEAN, B8>(a, s, g, u0 + us, u1 + us, ctx, nr, st);
           // the segment's first column in `out`; column c is row + c / G, head g * G + c % G
           const int64_t ob = ((int64_t)row * a.num_q_heads + (int64_t)g * G) * D;
-          if (whole)
+          if (whole && np > 0)
+            m_prefix_emit<DT, D, MULTI>(a, st, nr * G, row, g, np, ob);
+          else if (whole)
             mfma_emit<DT, D>(st, nr * G, nullptr, nullptr, nullptr, D, a.out, ob, MULTI ? G : 16,
                              (int64_t)a.num_q_heads * D, D, a.out_f32);
           else
-            m_split_finish<DT, D, MULTI>(a, st, nr * G, sg, o, cnt, seen, ob);
+            m_split_finish<DT, D, MULTI>(a, st, nr * G, sg, o, cnt, seen, ob, row, g, np);
         }
         i = pe;
       }

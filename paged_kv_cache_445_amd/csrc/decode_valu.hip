@@ -431,15 +431,43 @@ __device__ __forceinline__ void v_store_f32(const VState<DT, D>& st, float inv, 
   }
 }
 
-// A piece of a split segment (heads h0 + 4 j): publish it, or (if it is the segment's last
-// arrival) merge every piece and write the output; `between` (the next piece's start loads)
-// runs once, as early as the arrival protocol allows.  Every lane holds full sums for its
-// dimensions after v_finish, so each lane reads and merges its own dimensions of every head.
-// Slot rows: head j of a piece is row (slot HPW + j) of the partial arrays.
+// Folds the np shared-prefix partials of (row, query head h) into a merged head held as
+// (M, L, U): U[e] is this lane's dimension e * DPL + lane / LPD.
+template <int DT, int D>
+__device__ __forceinline__ void v_fold(const DecodeArgs& a, float& M, float& L,
+                                       float (&U)[VCfg<DT, D>::NV], int64_t row, int h, int np) {
+  using C = VCfg<DT, D>;
+  const int dim0 = lane_id() / C::LPD;
+  const int64_t e = (row * a.num_q_heads + h) * a.pre_parts;
+  fold_prefix<C::NV, 4>(M, L, U, a.pre_m + e, a.pre_l + e, a.pre_o + e * D, D, np,
+                        [&](int k) { return k * C::DPL + dim0; });
+}
+
+// A finished head of a whole segment of a sequence with a shared prefix (row, query head h,
+// output at ob): its keys past the prefix folded with the np prefix partials.
+template <int DT, int D>
+__device__ __forceinline__ void v_prefix_store(const DecodeArgs& a, const VState<DT, D>& st,
+                                               float l, int64_t row, int h, int np,
+                                               int64_t ob) {
+  using C = VCfg<DT, D>;
+  float M = st.m * 0.69314718055994531f, L = l, U[C::NV];
+#pragma unroll
+  for (int e = 0; e < C::NV; ++e) U[e] = st.acc[e];
+  v_fold<DT, D>(a, M, L, U, row, h, np);
+  v_store<DT, D>(U, 1.f / L, a.out, ob, a.out_f32);
+}
+
+// A piece of a split segment (heads h0 + 4 j of row `row`): publish it, or (if it is the
+// segment's last arrival) merge every piece, fold in the np shared-prefix partials of each
+// head (np > 0) and write the output; `between` (the next piece's start loads) runs once, as
+// early as the arrival protocol allows.  Every lane holds full sums for its dimensions after
+// v_finish, so each lane reads and merges its own dimensions of every head.  Slot rows: head
+// j of a piece is row (slot HPW + j) of the partial arrays.
 template <int DT, int D, int HPW, class Between>
 __device__ void v_split_finish(const DecodeArgs& a, const VState<DT, D> (&st)[HPW],
                                const float (&l)[HPW], const SplitSeg& sg, int64_t self,
-                               int32_t* cnt, int seen, int64_t ob0, Between&& between) {
+                               int32_t* cnt, int seen, int64_t ob0, int64_t row, int h0, int np,
+                               Between&& between) {
   using C = VCfg<DT, D>;
   const int lane = lane_id();
   const int dim0 = lane / C::LPD;  // dimension e * DPL + dim0 of load e
@@ -468,9 +496,9 @@ __device__ void v_split_finish(const DecodeArgs& a, const VState<DT, D> (&st)[HP
     }
   }, between);
   if (!last) return;
-  float L[HPW], U[HPW][C::NV];
+  float M[HPW], L[HPW], U[HPW][C::NV];
   merge_ordered<HPW, C::NV, (HPW > 2 ? 1 : 2)>(
-      L, U, sg.k0, sg.k1,
+      M, L, U, sg.k0, sg.k1,
       [&](int64_t k, float (&m)[HPW], float (&lk)[HPW], float (&ov)[HPW][C::NV]) {
         if (k == self) {
 #pragma unroll
@@ -493,7 +521,10 @@ __device__ void v_split_finish(const DecodeArgs& a, const VState<DT, D> (&st)[HP
         }
       });
 #pragma unroll
-  for (int j = 0; j < HPW; ++j) v_store<DT, D>(U[j], 1.f / L[j], a.out, ob0 + 4 * j * D, a.out_f32);
+  for (int j = 0; j < HPW; ++j) {
+    if (np > 0) v_fold<DT, D>(a, M[j], L[j], U[j], row, h0 + 4 * j, np);
+    v_store<DT, D>(U[j], 1.f / L[j], a.out, ob0 + 4 * j * D, a.out_f32);
+  }
   counter_reset(cnt);
 }
 
@@ -511,7 +542,7 @@ __global__ __launch_bounds__(kWG) void valu_decode_kernel(DecodeArgs a) {
   const int64_t w = (int64_t)blockIdx.x * kWavesPerWG + wave;
 
   if constexpr (MODE == MODE_EVEN) {
-    PlanIn pin{a.context_lens, a.qsl, S, kValuUnit, a.seg_extra, 1};
+    PlanIn pin{a.context_lens, a.qsl, S, kValuUnit, a.seg_extra, 1, a.skip};
     build_plan(base, pin);
     zero_empty_rows<DT>(pin, a.out, a.num_q_heads, D, w, W, a.out_f32, a.nan_rows);
     // units: (sequence, group of 4 HPW heads, tile); wave i runs heads i + 4 j of each group
@@ -525,10 +556,12 @@ __global__ __launch_bounds__(kWG) void valu_decode_kernel(DecodeArgs a) {
     even_split_drive(part, [&](int64_t o, int64_t lo, int64_t hi) {
       // this wave's piece of the segment that unit i of the range belongs to
       struct Unit {
-        VPiece p;
-        int nt;           // real tiles of the segment
+        VPiece p;           // tiles [p.t0, p.t1) of the sequence
+        int nt;             // real tiles of the segment
+        int sk;             // keys [0, sk) come from the shared-prefix partials
         int64_t seg0, end;  // the segment's first unit, the piece's end in the range
         bool run;           // real heads and real tiles
+        bool whole;         // the piece is the whole segment
       };
       auto at = [&](int64_t i) {
         Unit u;
@@ -548,10 +581,14 @@ __global__ __launch_bounds__(kWG) void valu_decode_kernel(DecodeArgs a) {
         u.nt = seglen - a.seg_extra;  // real tiles; the rest only balance the split
         u.end = min(hi, u.seg0 + seglen);
         u.p.h0 = grp * GH + wave;  // this wave's first head (HPW > 1: all exist)
-        u.p.t0 = (int)(i - u.seg0);
-        u.p.t1 = (int)min(u.end - u.seg0, (int64_t)u.nt);
-        u.run = u.p.h0 < a.num_q_heads && u.p.t0 < u.nt;
+        const int t0 = (int)(i - u.seg0);  // the segment's tiles start past a shared prefix
+        const int t1 = (int)min(u.end - u.seg0, (int64_t)u.nt);
+        u.run = u.p.h0 < a.num_q_heads && t0 < u.nt;
+        u.whole = t0 == 0 && t1 == u.nt;
         u.p.ctx = u.run ? a.context_lens[u.p.s] : 0;
+        u.sk = u.run && a.skip ? a.skip[u.p.s] : 0;
+        u.p.t0 = t0 + u.sk / kValuUnit;
+        u.p.t1 = t1 + u.sk / kValuUnit;
         return u;
       };
       VStart<DT, D, HPW> vs;
@@ -577,7 +614,8 @@ __global__ __launch_bounds__(kWG) void valu_decode_kernel(DecodeArgs a) {
         if (cur.run) {
           const int row = a.qsl ? a.qsl[cur.p.s] : cur.p.s;
           const int64_t ob0 = ((int64_t)row * a.num_q_heads + cur.p.h0) * D;
-          const bool whole = cur.p.t0 == 0 && cur.p.t1 == cur.nt;
+          const bool whole = cur.whole;
+          const int np = cur.sk > 0 ? (cur.sk + a.pre_tokens - 1) / a.pre_tokens : 0;
           SplitSeg sg{};
           int32_t* cnt = nullptr;
           int seen = 0;
@@ -593,15 +631,21 @@ __global__ __launch_bounds__(kWG) void valu_decode_kernel(DecodeArgs a) {
           for (int j = 0; j < HPW; ++j) l[j] = v_finish<DT, D>(st[j], a.v_factor);
           if (whole) {
 #pragma unroll
-            for (int j = 0; j < HPW; ++j)
-              v_store<DT, D>(st[j].acc, 1.f / l[j], a.out, ob0 + 4 * j * D, a.out_f32);
+            for (int j = 0; j < HPW; ++j) {
+              if (np > 0)
+                v_prefix_store<DT, D>(a, st[j], l[j], row, cur.p.h0 + 4 * j, np, ob0 + 4 * j * D);
+              else
+                v_store<DT, D>(st[j].acc, 1.f / l[j], a.out, ob0 + 4 * j * D, a.out_f32);
+            }
             start_next();
           } else if constexpr (HPW <= 2) {
-            v_split_finish<DT, D, HPW>(a, st, l, sg, o, cnt, seen, ob0, start_next);
+            v_split_finish<DT, D, HPW>(a, st, l, sg, o, cnt, seen, ob0, row, cur.p.h0, np,
+                                       start_next);
           } else {
             // with four or more heads the next piece's queries and a merge do not fit in
             // the registers together: start it once this piece is done
-            v_split_finish<DT, D, HPW>(a, st, l, sg, o, cnt, seen, ob0, [] {});
+            v_split_finish<DT, D, HPW>(a, st, l, sg, o, cnt, seen, ob0, row, cur.p.h0, np,
+                                       [] {});
             start_next();
           }
         } else {

@@ -13,6 +13,7 @@
 
 namespace pa {
 hipError_t launch_chunk(int dt, const DecodeArgs& a, int num_q_rows, hipStream_t st);
+hipError_t launch_prefix(int dt, const DecodeArgs& a, int num_q_rows, hipStream_t st);
 }
 
 namespace {
@@ -166,6 +167,10 @@ int bucket_lds_bytes(int bucket) { return (1 << bucket) * (int)sizeof(int32_t); 
 
 // resident workgroups per CU for pa_decode's even split (vector path, matrix-core path)
 constexpr int kEvenWgPerCu[2] = {1, 2};
+// ... for the vector path of pa_decode_shared_prefix, whose sequences are left with their
+// (short) private tails: more waves in flight hide the start of more, shorter segments
+// (prefix-shared batch: 216 -> 210 us)
+constexpr int kSharedWgPerCu = 2;
 
 // Query heads per wave of the vector path's even split: a wave runs heads h0 + 4 j
 // (j < HPW), so a workgroup reads 4 HPW adjacent heads of a block back to back, which the
@@ -174,8 +179,9 @@ constexpr int kEvenWgPerCu[2] = {1, 2};
 // into several pieces whose merge costs more than the locality gains.  So: the largest of
 // 8, 4, 2 whose head groups tile num_q_heads exactly and leave at least one segment per
 // workgroup (fp32: at most 2, its queries fill twice the registers; FP8: at most 4, its
-// values are widened to fp32 in registers), else 1; optional cap for tuning.
-int heads_per_wave(const pa_geom* g) {
+// values are widened to fp32 in registers), else 1; optional cap for tuning.  wg: resident
+// workgroups per CU of the call (0: kEvenWgPerCu).
+int heads_per_wave(const pa_geom* g, int wg = 0) {
   static const int v = [] {
     const char* s = getenv("PA_DECODE_HPW");
     return s ? atoi(s) : 0;
@@ -183,7 +189,7 @@ int heads_per_wave(const pa_geom* g) {
   if (b8(g)) return 1;  // 8-token blocks: one head per wave
   const int cap = g->kv_dtype == PA_F32 ? 2 : g->kv_dtype == PA_FP8_E4M3 ? 4 : 8;
   const int o = wg_per_cu_override();
-  const int64_t workgroups = (int64_t)cu_count() * (o > 0 ? o : kEvenWgPerCu[0]);
+  const int64_t workgroups = (int64_t)cu_count() * (o > 0 ? o : wg > 0 ? wg : kEvenWgPerCu[0]);
   for (int h = 8; h >= 2; h /= 2) {
     if (h > cap || (v > 0 && h > v) || g->num_q_heads % (pa::kWavesPerWG * h)) continue;
     const int64_t segments = (int64_t)g->num_seqs * (g->num_q_heads / (pa::kWavesPerWG * h));
@@ -194,13 +200,14 @@ int heads_per_wave(const pa_geom* g) {
 
 int hpw_index(int hpw) { return hpw == 8 ? 3 : hpw == 4 ? 2 : hpw == 2 ? 1 : 0; }
 
-// workgroups of the split kernel: every CU full at the kernel's occupancy
-int split_grid(const pa_geom* g, int mode, int path) {
+// workgroups of the split kernel: every CU full at the kernel's occupancy (wg: the even
+// split's resident workgroups per CU on the vector path, 0: kEvenWgPerCu)
+int split_grid(const pa_geom* g, int mode, int path, int wg = 0) {
   static std::atomic<int> cache[kMaxDevices][2][5][2][2][4][15];
   const int dev = current_device();
   const int di = g->head_dim == 64 ? 0 : 1;
   const int bk = seq_bucket(g->num_seqs);
-  const int hpw = path == 0 && mode == pa::MODE_EVEN ? heads_per_wave(g) : 1;
+  const int hpw = path == 0 && mode == pa::MODE_EVEN ? heads_per_wave(g, wg) : 1;
   std::atomic<int>& c = cache[dev][path][kdt(g)][di][mode][hpw_index(hpw)][bk];
   int occ = c.load(std::memory_order_relaxed);
   if (occ <= 0) {
@@ -212,7 +219,10 @@ int split_grid(const pa_geom* g, int mode, int path) {
   // The even split streams best with few resident workgroups per CU: each of them reads
   // four adjacent heads of a block at a time, and more of them only add split pieces.
   const int o = wg_per_cu_override();
-  int want = o > 0 ? o : (mode == pa::MODE_EVEN ? kEvenWgPerCu[path] : occ);
+  int want = o > 0 ? o
+                   : mode != pa::MODE_EVEN ? occ
+                   : path == 0 && wg > 0 ? wg
+                                         : kEvenWgPerCu[path];
   if (want > occ) want = occ;
   if (want > pa::kMaxWgPerCu) want = pa::kMaxWgPerCu;  // the workspace's counters cover this
   return cu_count() * want;
@@ -228,14 +238,21 @@ size_t counter_bytes() {
   return (n + 255) / 256 * 256;
 }
 
-size_t even_slots(const pa_geom* g, int grid, const Route& r) {
-  const int cols = r.path ? r.cols : heads_per_wave(g);
+size_t even_slots(const pa_geom* g, int grid, const Route& r, int wg = 0) {
+  const int cols = r.path ? r.cols : heads_per_wave(g, wg);
   return (size_t)grid * pa::kWavesPerWG * 2 * cols;
 }
 
-size_t even_workspace_bytes(const pa_geom* g, const Route& r) {
-  const int grid = split_grid(g, pa::MODE_EVEN, r.path);
-  return counter_bytes() + even_slots(g, grid, r) * ((size_t)g->head_dim + 2) * sizeof(float);
+size_t even_workspace_bytes(const pa_geom* g, const Route& r, int wg = 0) {
+  const int grid = split_grid(g, pa::MODE_EVEN, r.path, wg);
+  return counter_bytes() + even_slots(g, grid, r, wg) * ((size_t)g->head_dim + 2) * sizeof(float);
+}
+
+// enough for the call with and without query_start_loc
+size_t decode_workspace_bytes(const pa_geom* g, int32_t num_q_rows, int wg = 0) {
+  const size_t a = even_workspace_bytes(g, route(g, num_q_rows), wg);
+  const size_t b = even_workspace_bytes(g, route(g, 1), wg);
+  return a > b ? a : b;
 }
 
 pa_status hip_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
@@ -310,15 +327,72 @@ void* scratch_ptr(int dev, hipStream_t st) {
   return s.err == hipSuccess ? s.ptr : nullptr;
 }
 
-// pa_decode and pa_decode_scratch.  side_by_side: run the multi-row (chunk) kernel on a
-// second stream beside the decode kernel (pa_decode); otherwise both run on `st`, one after
-// the other (pa_decode_scratch: no stream or event is created).
+// ---- shared prefixes (pa_decode_shared_prefix) ----
+// The groups' shared keys are attended in partials of `tokens` keys, at most `parts` per
+// (row, head): the longest prefix the call allows (max_prefix_blocks blocks, whole 32-token
+// units) in at most 8 partials of at least 128 keys.
+struct PrefixParts {
+  int tokens = 0;
+  int parts = 0;
+};
+
+// optional override of the least keys per partial, for tuning (a multiple of 32)
+int prefix_min_tokens() {
+  static const int v = [] {
+    const char* s = getenv("PA_PREFIX_MIN_TOKENS");
+    const int t = s ? atoi(s) : 0;
+    return t >= pa::kMfmaUnit && t % pa::kMfmaUnit == 0 ? t : 128;
+  }();
+  return v;
+}
+
+PrefixParts prefix_parts(const pa_geom* g, int32_t max_prefix_blocks) {
+  PrefixParts pp;
+  const int64_t keys = (int64_t)max_prefix_blocks * g->block_size / pa::kMfmaUnit * pa::kMfmaUnit;
+  if (keys <= 0) return pp;
+  const int64_t t = ((keys + 7) / 8 + pa::kMfmaUnit - 1) / pa::kMfmaUnit * pa::kMfmaUnit;
+  pp.tokens = (int)std::max<int64_t>(prefix_min_tokens(), t);
+  pp.parts = (int)((keys + pp.tokens - 1) / pp.tokens);
+  return pp;
+}
+
+size_t align256(size_t n) { return (n + 255) / 256 * 256; }
+
+// behind pa_decode's workspace: skip [S] int32, then the prefix partials o [rows][Hq][P][D],
+// m and l [rows][Hq][P] (fp32)
+struct PrefixSpace {
+  size_t skip, o, m, l, end;
+};
+
+PrefixSpace prefix_space(const pa_geom* g, int32_t num_q_rows, size_t even_bytes,
+                         const PrefixParts& pp) {
+  PrefixSpace w;
+  const size_t n = (size_t)num_q_rows * g->num_q_heads * pp.parts;
+  w.skip = align256(even_bytes);
+  w.o = align256(w.skip + (size_t)g->num_seqs * sizeof(int32_t));
+  w.m = align256(w.o + n * g->head_dim * sizeof(float));
+  w.l = align256(w.m + n * sizeof(float));
+  w.end = align256(w.l + n * sizeof(float));
+  return w;
+}
+
+struct PrefixIn {
+  const int32_t* groups;  // [num_groups + 1]
+  const int32_t* blocks;  // [num_groups]
+  int32_t num_groups;
+  int32_t max_prefix_blocks;
+};
+
+// pa_decode, pa_decode_scratch and pa_decode_shared_prefix.  pa_decode runs the multi-row
+// (chunk) kernel on a second stream beside the decode kernel; use_scratch: both run on `st`,
+// one after the other, in the static workspace (no stream or event is created).  pre: the
+// shared-prefix kernel runs first, on `st`.
 pa_status decode_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
                       const int32_t* block_tables, const int32_t* context_lens,
                       const int32_t* query_start_loc, int32_t num_q_rows,
                       int32_t max_query_len, float scale, void* workspace,
                       size_t workspace_bytes, const pa_geom* g, hipStream_t st,
-                      bool use_scratch);
+                      bool use_scratch, const PrefixIn* pre = nullptr);
 
 }  // namespace
 
@@ -445,10 +519,7 @@ pa_status pa_swap_blocks(void* k_cache, void* v_cache, void* host_k, void* host_
 
 size_t pa_workspace_size(const pa_geom* g, int32_t num_q_rows) {
   if (check_geom(g) != PA_OK || num_q_rows < 0) return 0;
-  // enough for the call with and without query_start_loc
-  const size_t a = even_workspace_bytes(g, route(g, num_q_rows));
-  const size_t b = even_workspace_bytes(g, route(g, 1));
-  return a > b ? a : b;
+  return decode_workspace_bytes(g, num_q_rows);
 }
 
 pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -470,6 +541,38 @@ pa_status pa_decode_scratch(void* out, const void* q, const void* k_cache, const
                      num_q_rows, max_query_len, scale, nullptr, 0, g, (hipStream_t)stream, true);
 }
 
+size_t pa_shared_prefix_workspace_size(const pa_geom* g, int32_t num_q_rows,
+                                       int32_t max_prefix_blocks) {
+  if (check_geom(g) != PA_OK || num_q_rows < 0 || max_prefix_blocks < 0 ||
+      max_prefix_blocks > g->max_blocks_per_seq)
+    return 0;
+  const size_t even = decode_workspace_bytes(g, num_q_rows, kSharedWgPerCu);
+  return prefix_space(g, num_q_rows, even, prefix_parts(g, max_prefix_blocks)).end;
+}
+
+pa_status pa_decode_shared_prefix(void* out, const void* q, const void* k_cache,
+                                  const void* v_cache, const int32_t* block_tables,
+                                  const int32_t* context_lens, const int32_t* query_start_loc,
+                                  int32_t num_q_rows, int32_t max_query_len,
+                                  const int32_t* prefix_groups, const int32_t* prefix_blocks,
+                                  int32_t num_groups, int32_t max_prefix_blocks, float scale,
+                                  void* workspace, size_t workspace_bytes, const pa_geom* g,
+                                  void* stream) {
+  const pa_status gs = check_geom(g);
+  if (gs != PA_OK) return gs;
+  if (num_groups < 0 || max_prefix_blocks < 0 || max_prefix_blocks > g->max_blocks_per_seq)
+    return PA_ERR_SHAPE;
+  if (num_groups > kMaxSeqs) return PA_ERR_UNSUPPORTED;
+  if (num_groups > 0 && (!prefix_groups || !prefix_blocks)) return PA_ERR_NULL;
+  // the prefix kernel is the chunk kernel's: 16-bit or FP8 pools, 16 % G == 0
+  if (g->kv_dtype == PA_F32 || 16 % (g->num_q_heads / g->num_kv_heads) != 0)
+    return PA_ERR_UNSUPPORTED;
+  const PrefixIn pre{prefix_groups, prefix_blocks, num_groups, max_prefix_blocks};
+  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc,
+                     num_q_rows, max_query_len, scale, workspace, workspace_bytes, g,
+                     (hipStream_t)stream, false, &pre);
+}
+
 }  // extern "C"
 
 namespace {
@@ -479,7 +582,7 @@ pa_status decode_impl(void* out, const void* q, const void* k_cache, const void*
                       const int32_t* query_start_loc, int32_t num_q_rows,
                       int32_t max_query_len, float scale, void* workspace,
                       size_t workspace_bytes, const pa_geom* g, hipStream_t st,
-                      bool use_scratch) {
+                      bool use_scratch, const PrefixIn* pre) {
   const pa_status gs = check_geom(g);
   if (gs != PA_OK) return gs;
   if (num_q_rows < 0 || max_query_len < 0) return PA_ERR_SHAPE;
@@ -495,8 +598,13 @@ pa_status decode_impl(void* out, const void* q, const void* k_cache, const void*
   if (query_start_loc)
     max_len = max_query_len > 0 && max_query_len < num_q_rows ? max_query_len : num_q_rows;
   const Route rt = route(g, max_len);
-  const int grid = split_grid(g, pa::MODE_EVEN, rt.path);
-  const size_t need = even_workspace_bytes(g, rt);
+  const int wg = pre ? kSharedWgPerCu : 0;
+  const int grid = split_grid(g, pa::MODE_EVEN, rt.path, wg);
+  const size_t even = even_workspace_bytes(g, rt, wg);
+  const PrefixParts pp = pre ? prefix_parts(g, pre->max_prefix_blocks) : PrefixParts{};
+  const bool prefix = pre && pre->num_groups > 0 && pp.parts > 0;
+  const PrefixSpace ps = prefix_space(g, num_q_rows, even, pp);
+  const size_t need = prefix ? ps.end : even;
   if (use_scratch) {
     if (need > kScratchBytes) return PA_ERR_WORKSPACE;
     workspace = scratch_ptr(current_device(), st);
@@ -504,7 +612,7 @@ pa_status decode_impl(void* out, const void* q, const void* k_cache, const void*
     workspace_bytes = kScratchBytes;
   }
   if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
-  const size_t slots = even_slots(g, grid, rt);
+  const size_t slots = even_slots(g, grid, rt, wg);
   int32_t* counters = static_cast<int32_t*>(workspace);
   float* part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + counter_bytes());
   float* part_m = part_o + slots * g->head_dim;
@@ -535,7 +643,7 @@ pa_status decode_impl(void* out, const void* q, const void* k_cache, const void*
     a.v_factor = g->v_scale;
   }
   a.seg_extra = seg_extra_override() >= 0 ? seg_extra_override() : kSegExtra[rt.path];
-  a.heads_per_wave = rt.path == 0 ? heads_per_wave(g) : 1;
+  a.heads_per_wave = rt.path == 0 ? heads_per_wave(g, wg) : 1;
   a.xcd_major = xcd_major_override() > 0 ? 1 : 0;
   a.odd_skew = odd_skew();
   a.max_rows = rt.max_rows;
@@ -545,6 +653,35 @@ pa_status decode_impl(void* out, const void* q, const void* k_cache, const void*
   // no multi-row kernel runs: the rows of a sequence with more rows than max_query_len
   // promised are written NaN
   a.nan_rows = query_start_loc && max_len <= rt.max_rows ? 1 : 0;
+
+  if (prefix) {
+    // the groups' shared keys first: partials for every row of a group, and each sequence's
+    // skip (the keys the decode kernel then leaves out and folds back from the partials)
+    char* ws = static_cast<char*>(workspace);
+    int32_t* skip = reinterpret_cast<int32_t*>(ws + ps.skip);
+    float* pre_o = reinterpret_cast<float*>(ws + ps.o);
+    float* pre_m = reinterpret_cast<float*>(ws + ps.m);
+    float* pre_l = reinterpret_cast<float*>(ws + ps.l);
+    pa::DecodeArgs pa_ = a;
+    pa_.part_tokens = pp.tokens;
+    pa_.max_partitions = pp.parts;
+    pa_.part_o = pre_o;
+    pa_.part_m = pre_m;
+    pa_.part_l = pre_l;
+    pa_.grp_start = pre->groups;
+    pa_.grp_blocks = pre->blocks;
+    pa_.num_groups = pre->num_groups;
+    pa_.max_prefix_blocks = pre->max_prefix_blocks;
+    pa_.block_size = g->block_size;
+    pa_.skip_out = skip;
+    if (pa::launch_prefix(kdt(g), pa_, num_q_rows, st) != hipSuccess) return PA_ERR_HIP;
+    a.skip = skip;
+    a.pre_o = pre_o;
+    a.pre_m = pre_m;
+    a.pre_l = pre_l;
+    a.pre_parts = pp.parts;
+    a.pre_tokens = pp.tokens;
+  }
 
   auto decode = [&] {
     return rt.path ? pa::launch_mfma_decode(kdt(g), pa::MODE_EVEN, a, grid, st)

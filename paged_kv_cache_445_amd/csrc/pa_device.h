@@ -244,6 +244,8 @@ struct PlanIn {
   int32_t unit_tokens;
   int32_t extra;       // balancing units appended to every non-empty segment (no work)
   int32_t max_rows;    // sequences with more query rows are left to the chunk kernel
+  const int32_t* skip = nullptr;  // leading keys of each sequence attended elsewhere (a
+                                  // multiple of unit_tokens, below the context), or NULL
 };
 
 // units of sequence s in the flattened list: its real units ceil(ctx / unit_tokens), plus
@@ -253,7 +255,7 @@ struct PlanIn {
 __device__ __forceinline__ int32_t seq_units(const PlanIn& p, int s) {
   const int32_t rows = p.qsl ? p.qsl[s + 1] - p.qsl[s] : 1;
   if (rows < 1 || rows > p.max_rows) return 0;  // no rows, or rows for the chunk kernel
-  const int32_t ctx = p.context_lens[s];
+  const int32_t ctx = p.context_lens[s] - (p.skip ? p.skip[s] : 0);
   return ctx > 0 ? (ctx + p.unit_tokens - 1) / p.unit_tokens + p.extra : 0;
 }
 
@@ -531,18 +533,17 @@ __device__ __forceinline__ void counter_reset(int32_t* c) {
 // registers it would have published.  The arithmetic depends only on the pieces' values and
 // the fixed order, so every call gives the same bits whichever piece merges.  Pieces are
 // fetched B at a time into two alternating batches, so the loads of the next batch are in
-// flight while the current one is combined.  Returns each row's merged output in U and its
-// sum in L (the output is U / L).
+// flight while the current one is combined.  Returns each row's merged output in U, its sum
+// in L and its max (natural-log domain) in M (the output is U / L).
 template <int R, int NE, int B>
 struct MergeBatch {
   float m[B][R], l[B][R], o[B][R][NE];
 };
 
 template <int R, int NE, int B, class Fetch>
-__device__ __forceinline__ void merge_ordered(float (&L)[R], float (&U)[R][NE], int64_t k0,
-                                              int64_t k1, Fetch&& fetch) {
+__device__ __forceinline__ void merge_ordered(float (&M)[R], float (&L)[R], float (&U)[R][NE],
+                                              int64_t k0, int64_t k1, Fetch&& fetch) {
   const int n = (int)(k1 - k0 + 1);
-  float M[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     M[r] = -INFINITY;
@@ -595,6 +596,60 @@ __device__ __forceinline__ void merge_ordered(float (&L)[R], float (&U)[R][NE], 
     if (q0 + 2 * B < n) load(ba, q0 + 2 * B);
     combine(bb);
   }
+}
+
+// Folds the shared-prefix partials of one (row, query head) into that row's merged result:
+// pm, pl, po point at its first partial (max in the natural-log domain, sum, D-float
+// normalised output), np <= kMaxPrefixParts partials follow one another, and (M, L, U) is
+// the running merge (max, sum, unnormalised output of this lane's NE dimensions dim(k)) that
+// the fold updates.  A partial without keys (l = 0) changes nothing.  Every max and sum is
+// loaded at once; with the merged max known, the outputs are weighted sums of independent
+// terms, loaded B partials at a time with all their loads in flight (partials past np are
+// read from partial 0 and weighted 0).
+constexpr int kMaxPrefixParts = 8;
+
+template <int NE, int B, class Dim>
+__device__ __forceinline__ void fold_prefix(float& M, float& L, float (&U)[NE], const float* pm,
+                                            const float* pl, const float* po, int D, int np,
+                                            Dim&& dim) {
+  static_assert(kMaxPrefixParts % B == 0, "whole batches");
+  float mp[kMaxPrefixParts], lp[kMaxPrefixParts];
+#pragma unroll
+  for (int p = 0; p < kMaxPrefixParts; ++p) {
+    const int q = p < np ? p : 0;
+    mp[p] = pm[q];
+    lp[p] = pl[q];
+  }
+  float mn = M;
+#pragma unroll
+  for (int p = 0; p < kMaxPrefixParts; ++p)
+    if (p < np && lp[p] > 0.f) mn = fmaxf(mn, mp[p]);
+  const float sa = M == -INFINITY ? 0.f : __expf(M - mn);
+  L *= sa;
+#pragma unroll
+  for (int k = 0; k < NE; ++k) U[k] *= sa;
+  float w[kMaxPrefixParts];
+#pragma unroll
+  for (int p = 0; p < kMaxPrefixParts; ++p) {
+    w[p] = p < np && lp[p] > 0.f ? lp[p] * __expf(mp[p] - mn) : 0.f;
+    L += w[p];
+  }
+#pragma unroll
+  for (int p0 = 0; p0 < kMaxPrefixParts; p0 += B) {
+    if (p0 >= np) break;  // uniform
+    float o[B][NE];
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const int q = p0 + b < np ? p0 + b : 0;
+#pragma unroll
+      for (int k = 0; k < NE; ++k) o[b][k] = po[(int64_t)q * D + dim(k)];
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b)
+#pragma unroll
+      for (int k = 0; k < NE; ++k) U[k] = fmaf(w[p0 + b], o[b][k], U[k]);
+  }
+  M = mn;
 }
 
 // Calls f(std::integral_constant<int, i>) for i = 0 .. N-1, unrolled: i is a constant in f.

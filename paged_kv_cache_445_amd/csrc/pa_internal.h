@@ -64,6 +64,26 @@ struct DecodeArgs {
                             // 2 j and 2 j + 1), each a pool tile of 8 tokens
   int32_t xcd_major;        // MODE_EVEN, vector kernel: list in (head group, sequence, tile)
                             // order with XCD-major owners (see Part)
+  // shared prefixes (pa_decode_shared_prefix).  Decode kernels: keys [0, skip[s]) of sequence
+  // s were attended by the prefix kernel, whose partials (normalised output, max in the
+  // natural-log domain, sum) for row r and query head h sit at pre_* [(r Hq + h) pre_parts +
+  // p], one per pre_tokens keys; the decode kernel folds them into the row's result.  NULL
+  // skip: no shared prefix.
+  const int32_t* skip;
+  const float* pre_o;
+  const float* pre_m;
+  const float* pre_l;
+  int32_t pre_parts;
+  int32_t pre_tokens;
+  // prefix kernel (chunk kernel, prefix mode): group i is sequences [grp_start[i],
+  // grp_start[i + 1]) sharing their first grp_blocks[i] table entries (at most
+  // max_prefix_blocks are used); it writes skip_out[s] for every sequence
+  const int32_t* grp_start;
+  const int32_t* grp_blocks;
+  int32_t num_groups;
+  int32_t max_prefix_blocks;
+  int32_t block_size;
+  int32_t* skip_out;
 };
 
 struct ReshapeArgs {

@@ -64,6 +64,18 @@ class DeviceBatch:
         self.workspace = torch.zeros(max(ws, 16), dtype=torch.uint8, device=dev)
         self.scale = float(b.scale)
         self.max_query_len = int(b.rows_per_seq().max()) if b.num_seqs else 0
+        self.prefix = None  # shared-prefix groups (set_shared_prefix)
+
+    def set_shared_prefix(self, groups, blocks, max_prefix_blocks: int):
+        """Decode through pa_decode_shared_prefix from now on: groups int [num_groups + 1]
+        (sequence ranges), blocks int [num_groups] (claimed shared leading blocks)."""
+        dev = self.device
+        g = torch.from_numpy(np.asarray(groups, dtype=np.int32)).to(dev)
+        k = torch.from_numpy(np.asarray(blocks, dtype=np.int32)).to(dev)
+        ws = pa.shared_prefix_workspace_size(self.geom, self.b.num_q_rows, max_prefix_blocks)
+        # zeroed once: the decode keeps its arrival counters at zero between calls
+        self.prefix = (g, k, int(max_prefix_blocks),
+                       torch.zeros(max(ws, 16), dtype=torch.uint8, device=dev))
 
     # ------------------------------------------------------------------ the method
     def prefill(self, stream=None):
@@ -76,6 +88,13 @@ class DeviceBatch:
                              self.slot_new, self.geom, stream)
 
     def attend(self, stream=None):
+        if self.prefix is not None:
+            g, k, mpb, ws = self.prefix
+            pa.decode_shared_prefix(self.out, self.q, self.k_cache, self.v_cache,
+                                    self.block_tables, self.context_lens, self.qsl, g, k, mpb,
+                                    self.scale, ws, self.geom, stream,
+                                    max_query_len=self.max_query_len)
+            return
         pa.decode(self.out, self.q, self.k_cache, self.v_cache, self.block_tables,
                   self.context_lens, self.qsl, self.scale, self.workspace, self.geom, stream,
                   max_query_len=self.max_query_len)

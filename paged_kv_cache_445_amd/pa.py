@@ -65,6 +65,13 @@ _lib.pa_decode_partitioned.restype = ctypes.c_int
 _lib.pa_decode_partitioned.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                        ctypes.c_int32, ctypes.c_float, ctypes.c_int32,
                                        ctypes.c_int32, _G, _vp]
+_lib.pa_shared_prefix_workspace_size.restype = ctypes.c_size_t
+_lib.pa_shared_prefix_workspace_size.argtypes = [_G, ctypes.c_int32, ctypes.c_int32]
+_lib.pa_decode_shared_prefix.restype = ctypes.c_int
+_lib.pa_decode_shared_prefix.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32,
+                                         ctypes.c_int32, _vp, _vp, ctypes.c_int32,
+                                         ctypes.c_int32, ctypes.c_float, _vp, ctypes.c_size_t,
+                                         _G, _vp]
 _lib.pa_decode_reduce.restype = ctypes.c_int
 _lib.pa_decode_reduce.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_int32, _G, _vp]
 
@@ -168,6 +175,29 @@ def decode(out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc
                           _p(context_lens), _p(query_start_loc), int(q.shape[0]),
                           int(max_query_len), float(scale), _p(workspace), ws_bytes,
                           ctypes.byref(g), _stream(stream)))
+
+
+def shared_prefix_workspace_size(g: Geom, num_q_rows: int, max_prefix_blocks: int) -> int:
+    return int(_lib.pa_shared_prefix_workspace_size(ctypes.byref(g), int(num_q_rows),
+                                                    int(max_prefix_blocks)))
+
+
+def decode_shared_prefix(out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc,
+                         prefix_groups, prefix_blocks, max_prefix_blocks, scale, workspace,
+                         g: Geom, stream=None, max_query_len: int = 0):
+    """pa_decode_shared_prefix.  prefix_groups: int32 [num_groups + 1] sequence ranges,
+    prefix_blocks: int32 [num_groups] claimed shared leading blocks (device tensors, or None
+    for no group)."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ng = 0 if prefix_blocks is None else int(prefix_blocks.numel())
+    _check("pa_decode_shared_prefix",
+           _lib.pa_decode_shared_prefix(_p(out), _p(q), _p(k_cache), _p(v_cache),
+                                        _p(block_tables), _p(context_lens),
+                                        _p(query_start_loc), int(q.shape[0]),
+                                        int(max_query_len), _p(prefix_groups),
+                                        _p(prefix_blocks), ng, int(max_prefix_blocks),
+                                        float(scale), _p(workspace), ws_bytes, ctypes.byref(g),
+                                        _stream(stream)))
 
 
 DECODE_SCRATCH_BYTES = 36 << 20  # PA_DECODE_SCRATCH_BYTES

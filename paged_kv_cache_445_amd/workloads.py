@@ -253,7 +253,8 @@ def build_batch(name: str, dtype: str, context_lens, rows_per_seq, num_q_heads: 
                  q=q, key=key, value=value, slot=slot,
                  history=np.arange(num_history, dtype=np.int64),
                  new=np.arange(num_history, R, dtype=np.int64), seq_tokens=seq_tokens,
-                 sentinel_block=sentinel, partition_size=partition_size, block_size=BS)
+                 sentinel_block=sentinel, partition_size=partition_size, block_size=BS,
+                 meta={"shared_prefix_blocks": shared} if shared else {})
 
 
 # --------------------------------------------------------------------------- presets

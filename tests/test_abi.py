@@ -28,6 +28,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for fn in ("pa_reshape_and_cache", "pa_decode", "pa_decode_partitioned", "pa_decode_reduce",
+               "pa_decode_shared_prefix", "pa_shared_prefix_workspace_size",
                "pa_copy_blocks", "pa_swap_blocks",
                "pa_workspace_size", "pa_kv_cache_bytes", "pa_status_str"):
         assert fn in names
@@ -163,6 +164,39 @@ def test_host_checks_return_codes_without_launching(lib):
     assert scr(dummy, dummy, dummy, dummy, dummy, dummy, dummy, 9, 0, 0.1, ctypes.byref(gf), None) == -3
     assert scr(dummy, dummy, dummy, dummy, dummy, dummy, None, 4, 0, 0.1, ctypes.byref(_g(head_dim=80)),
                None) == -3
+
+    # pa_decode_shared_prefix: its own checks, then pa_decode's
+    lib.pa_decode_shared_prefix.restype = ctypes.c_int
+    lib.pa_decode_shared_prefix.argtypes = [vp] * 7 + [ctypes.c_int32, ctypes.c_int32, vp, vp,
+                                                       ctypes.c_int32, ctypes.c_int32,
+                                                       ctypes.c_float, vp, ctypes.c_size_t,
+                                                       ctypes.POINTER(Geom), vp]
+    sp = lib.pa_decode_shared_prefix
+
+    def shp(geom, rows=4, qsl=None, groups=dummy, blocks=dummy, ng=1, mpb=4, q=dummy):
+        return sp(dummy, q, dummy, dummy, dummy, dummy, qsl, rows, 0, groups, blocks, ng, mpb,
+                  0.1, dummy, 1 << 30, ctypes.byref(geom), None)
+    assert shp(g, ng=-1) == -2
+    assert shp(g, mpb=-1) == -2
+    assert shp(g, mpb=9) == -2                 # more than max_blocks_per_seq (8)
+    assert shp(g, groups=None) == -1
+    assert shp(g, blocks=None) == -1
+    assert shp(g, ng=9000) == -3               # more groups than the kernels plan for
+    assert shp(gf) == -3                       # fp32 pools
+    assert shp(_g(num_q_heads=12, num_kv_heads=4)) == -3   # G = 3 does not divide 16
+    assert shp(g, rows=3) == -2                # pa_decode's row check
+    assert shp(g, q=None) == -1
+    assert shp(g0, rows=0) == 0
+    # no group: no group arrays needed (pa_decode's remaining checks still apply)
+    assert shp(g, groups=None, blocks=None, ng=0, q=None) == -1
+    lib.pa_shared_prefix_workspace_size.restype = ctypes.c_size_t
+    lib.pa_shared_prefix_workspace_size.argtypes = [ctypes.POINTER(Geom), ctypes.c_int32,
+                                                    ctypes.c_int32]
+    wsz = lib.pa_shared_prefix_workspace_size
+    assert wsz(ctypes.byref(_g(head_dim=80)), 4, 2) == 0
+    assert wsz(ctypes.byref(g), -1, 2) == 0
+    assert wsz(ctypes.byref(g), 4, -1) == 0
+    assert wsz(ctypes.byref(g), 4, 9) == 0
 
     lib.pa_decode_reduce.restype = ctypes.c_int
     lib.pa_decode_reduce.argtypes = [vp] * 4 + [ctypes.c_int32, ctypes.c_int32,
