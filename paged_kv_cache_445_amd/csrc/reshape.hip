@@ -117,20 +117,25 @@ __global__ __launch_bounds__(kReshapeThreads) void reshape_and_cache_kernel(Resh
     const bool start = tid >= 1 && tid <= T && s >= 0 && !cont;
     const uint64_t starts = __builtin_amdgcn_ballot_w64(start);
     const uint64_t conts = __builtin_amdgcn_ballot_w64(cont);
+    // a segment's length: its start and the run of continuing tokens after it
+    const uint64_t after = ~conts >> (tid + 1);
+    int len = start ? min(__builtin_ctzll(after | (1ull << 62)), T - 1) + 1 : 0;
+    // tokens of the segments before each one: an exclusive scan over the lanes
+    int incl = len;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int v = __shfl_up(incl, d, kWave);
+      if (tid >= d) incl += v;
+    }
     if (start) {
       const int k = __popcll(starts & ((1ull << tid) - 1));  // segments before this one
-      // its length: the run of continuing tokens after it
-      const uint64_t after = ~conts >> (tid + 1);
-      const int len = min(__builtin_ctzll(after | (1ull << 62)), T - 1) + 1;
       seg_t[k] = tid - 1;
-      seg_c[k + 1] = len;  // summed below
+      seg_c[k] = incl - len;
     }
-    if (tid == 0) nseg = __popcll(starts);
-  }
-  __syncthreads();
-  if (tid == 0) {
-    seg_c[0] = 0;
-    for (int k = 1; k <= nseg; ++k) seg_c[k] += seg_c[k - 1];
+    if (tid == kWave - 1) {
+      nseg = __popcll(starts);
+      seg_c[__popcll(starts)] = incl;  // every token of the workgroup
+    }
   }
   __syncthreads();
   const int ns = nseg;

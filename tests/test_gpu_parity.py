@@ -651,6 +651,20 @@ def test_block_manager_scenario(dev, dtype, G):
     og = oracle.make_geom(S, H * G, H, D, NB, MB, dtype)
     want, _ = oracle.paged_attention(q, kp, vp, bt, lens, None, scale, og)
     check_out(out.cpu().numpy().astype(np.float64), want, TOL[dtype], "block manager")
+    if dtype == "f32":  # the shared-prefix decode takes 16-bit and FP8 pools
+        return
+    # the same sequences through the shared-prefix decode, grouped by the manager
+    groups, blocks = sc.bm.prefix_groups(ids)
+    _log(f"[block_manager] prefix groups {groups.tolist()} blocks {blocks.tolist()}")
+    assert (blocks > 0).any()
+    out.zero_()
+    ws = torch.zeros(pa.shared_prefix_workspace_size(g, S, MB), dtype=torch.uint8, device="cuda")
+    pa.decode_shared_prefix(out, to_device(q, dtype, "cuda"), kc, vc, torch.from_numpy(bt).cuda(),
+                            torch.from_numpy(lens).cuda(), None,
+                            torch.from_numpy(groups).cuda(), torch.from_numpy(blocks).cuda(), MB,
+                            scale, ws, g)
+    torch.cuda.synchronize()
+    check_out(out.cpu().numpy().astype(np.float64), want, TOL[dtype], "block manager, shared prefix")
 
 
 def test_spec_verify_long_split(dev):
