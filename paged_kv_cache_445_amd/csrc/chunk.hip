@@ -120,7 +120,8 @@ __device__ inline PrefixGroup prefix_group(const DecodeArgs& a, int i) {
   p.r0 = a.qsl ? a.qsl[p.gs] : p.gs;
   p.r1 = a.qsl ? a.qsl[p.ge] : p.ge;
   const int blocks = min(a.grp_blocks[i], a.max_prefix_blocks);
-  p.keys = blocks > 0 ? blocks * a.block_size / kMfmaUnit * kMfmaUnit : 0;
+  const int64_t keys = blocks > 0 ? (int64_t)blocks * a.block_size / kMfmaUnit * kMfmaUnit : 0;
+  p.keys = (int)min(keys, (int64_t)0x7fffffe0);
   if (p.ge > p.gs) {
     const int rows = (a.qsl ? a.qsl[p.gs + 1] : p.gs + 1) - p.r0;
     if (rows < 1 || p.keys > a.context_lens[p.gs] - rows) p.keys = 0;
@@ -425,6 +426,12 @@ __device__ void chunk_item(const DecodeArgs& a, int s, int g, int cb, int part,
           s0[c] = mfma<DT>(__builtin_bit_cast(T, kb[0][kk]), qb[c][kk], s0[c]);
           s1[c] = mfma<DT>(__builtin_bit_cast(T, kb[1][kk]), qb[c][kk], s1[c]);
         }
+      // The softmax (vector ALU, mostly exponentials) runs at raised wave priority and the
+      // matrix products at the normal one: of the two waves on a SIMD, the one in its softmax
+      // issues first while the other's queued products keep the matrix core busy (chunk rows
+      // 438 -> 411 us; the placement of the switch back, before V's reads or before P . V,
+      // made no difference).
+      __builtin_amdgcn_s_setprio(1);
       ChunkP<DT> pp[NCB];
 #pragma unroll
       for (int c = 0; c < NCB; ++c) {
@@ -454,6 +461,7 @@ __device__ void chunk_item(const DecodeArgs& a, int s, int g, int cb, int part,
           vo[j] = __builtin_bit_cast(T, w);
         }
       }
+      __builtin_amdgcn_s_setprio(0);
 #pragma unroll
       for (int c = 0; c < NCB; ++c)
         if (live[c]) chunk_pv<DT, D>(st[c], vo, pp[c], ones);
