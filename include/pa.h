@@ -274,9 +274,10 @@ pa_status pa_decode_reduce(void* out, const float* tmp_out, const float* max_log
  * past the prefix only and folds the prefix partials into its result by log-sum-exp.  The
  * grouping is this library's addition; the pages describe the sharing, not how a kernel
  * uses it.
- *   prefix_groups  int32 [num_groups + 1] (device), increasing: group i is sequences
- *                  [prefix_groups[i], prefix_groups[i + 1]); sequences outside every
- *                  group are decoded as pa_decode does
+ *   prefix_groups  int32 [num_groups + 1] (device), non-decreasing: group i is sequences
+ *                  [prefix_groups[i], prefix_groups[i + 1]) (clamped to the batch);
+ *                  sequences outside every group are decoded as pa_decode does, and so is
+ *                  every sequence when the array decreases anywhere (overlapping groups)
  *   prefix_blocks  int32 [num_groups] (device): leading block-table entries the group's
  *                  sequences are said to share; at most max_prefix_blocks of them are used
  *   max_prefix_blocks  bound of the shared blocks used (<= max_blocks_per_seq); sizes the

@@ -135,11 +135,21 @@ __device__ inline PrefixGroup prefix_group(const DecodeArgs& a, int i) {
 // group's shared prefix when s is a sequence the decode kernel takes (1 .. max_rows rows),
 // each of its rows sees every key of the prefix and its table entries over the prefix are
 // those of the group's first sequence; else 0 (the decode or chunk kernel attends all its
-// keys).
+// keys).  With grp_start not non-decreasing, groups could overlap (a row with two prefixes):
+// then every skip is 0.
 __device__ inline void write_skips(const DecodeArgs& a, int64_t w, int64_t W) {
   const int lane = lane_id();
+  if (w >= a.num_seqs) return;
+  bool ordered = true;
+  for (int i = lane; i < a.num_groups; i += kWave)
+    ordered &= a.grp_start[i] <= a.grp_start[i + 1];
+  ordered = __builtin_amdgcn_ballot_w64(!ordered) == 0;
   for (int64_t s = w; s < a.num_seqs; s += W) {
     int sk = 0;
+    if (!ordered) {
+      if (lane == 0) a.skip_out[s] = 0;
+      continue;
+    }
     // the group of s: the largest i with grp_start[i] <= s
     int lo = 0, hi = a.num_groups - 1;
     while (lo < hi) {

@@ -131,6 +131,10 @@ def test_shared_prefix_groups_and_rejected_claims(dev):
     # the same with 16-bit output and a cap that cuts every claim to 10 blocks
     db = run_shared(dev, b, groups, blocks, 10, out_f32=False)
     check(b, db.out_host(), want, out_f32=False)
+    # group starts that decrease (groups [0, 10) and [5, 8) would overlap): no sequence takes
+    # a prefix, every row is still right
+    db = run_shared(dev, b, np.array([0, 10, 20, 2, 5, 8]), [24, 24, 24, 24, 24], 24)
+    check(b, db.out_host(), want)
 
 
 def test_shared_prefix_verify_and_chunk_rows(dev):
