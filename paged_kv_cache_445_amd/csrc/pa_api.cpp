@@ -82,9 +82,19 @@ int cu_count() {
   return n;
 }
 
-// balancing units per segment of pa_decode's even split (vector path, matrix-core path): the
-// cost of starting a piece, in units of work; optional override for tuning
-constexpr int kSegExtra[2] = {2, 1};
+// Balancing units per segment of pa_decode's even split: the cost of starting a piece
+// (query, table window, pipeline fill, partial) in the split's units of work.  That cost is
+// roughly a fixed time, about as long as streaming 16-32 KiB of one head's K and V, so it
+// is worth twice as many units over FP8 pools (half the bytes per unit).  Vector path
+// (16-token tiles): 4 for 16-bit pools (LLaMA-7B batch 107.1 -> 106.6 us against 2), 8 for
+// FP8 (63.2 -> 60.8 us), 2 for fp32.  Matrix-core path (32-token units): 1 for 16-bit (the
+// GQA batch is best at 1), 2 for FP8 (GQA FP8 batch 153.3 -> 147.2 us).  Optional override
+// for tuning.
+int seg_extra_default(const pa_geom* g, int path) {
+  const bool f8 = g->kv_dtype == PA_FP8_E4M3;
+  if (path) return f8 ? 2 : 1;
+  return g->kv_dtype == PA_F32 ? 2 : f8 ? 8 : 4;
+}
 int seg_extra_override() {
   static int v = [] {
     const char* s = getenv("PA_DECODE_SEG_EXTRA");
@@ -642,7 +652,7 @@ pa_status decode_impl(void* out, const void* q, const void* k_cache, const void*
     a.scale_log2 *= g->k_scale;
     a.v_factor = g->v_scale;
   }
-  a.seg_extra = seg_extra_override() >= 0 ? seg_extra_override() : kSegExtra[rt.path];
+  a.seg_extra = seg_extra_override() >= 0 ? seg_extra_override() : seg_extra_default(g, rt.path);
   a.heads_per_wave = rt.path == 0 ? heads_per_wave(g, wg) : 1;
   a.xcd_major = xcd_major_override() > 0 ? 1 : 0;
   a.odd_skew = odd_skew();
