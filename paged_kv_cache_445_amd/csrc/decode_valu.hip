@@ -132,24 +132,27 @@ __device__ __forceinline__ void mask_piece(uint4& v, int first_token, int valid)
   v.w &= m[3];
 }
 
-// FP8: q . k over a 16-byte K chunk of 16 E4M3 values, each widened to fp32 and multiplied
-// with its 16-bit query element (q0: elements 0-7, q1: 8-15; fp16 for DT_FP8, bf16 for
-// DT_FP8B) in fp32.
+// FP8: q . k over a 16-byte K chunk of 16 E4M3 values, each pair widened to the query's
+// 16-bit type (fp16 for DT_FP8, bf16 for DT_FP8B; exact) and dotted with its two query
+// elements (q0: elements 0-7, q1: 8-15) into the fp32 sum.
 template <int DT>
 __device__ __forceinline__ float dot_fp8(const uint4& k, const uint4& q0, const uint4& q1,
                                          float acc) {
-  auto lo = [](uint32_t w) { return DT == DT_FP8B ? bf16_lo(w) : f16_lo(w); };
-  auto hi = [](uint32_t w) { return DT == DT_FP8B ? bf16_hi(w) : f16_hi(w); };
+  constexpr bool BF = DT == DT_FP8B;
+  auto dot2 = [](uint32_t a, uint32_t b, float c) {
+    if constexpr (BF)
+      return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, a),
+                                             __builtin_bit_cast(bf162_t, b), c, false);
+    else
+      return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a),
+                                    __builtin_bit_cast(half2_t, b), c, false);
+  };
   const uint32_t kw[4] = {k.x, k.y, k.z, k.w};
   const uint32_t qw[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
-    float f[4];
-    fp8x4_to_f32(kw[m], f);
-    acc = fmaf(lo(qw[2 * m]), f[0], acc);
-    acc = fmaf(hi(qw[2 * m]), f[1], acc);
-    acc = fmaf(lo(qw[2 * m + 1]), f[2], acc);
-    acc = fmaf(hi(qw[2 * m + 1]), f[3], acc);
+    acc = dot2(fp8x2_to_16<BF, false>(kw[m]), qw[2 * m], acc);
+    acc = dot2(fp8x2_to_16<BF, true>(kw[m]), qw[2 * m + 1], acc);
   }
   return acc;
 }

@@ -105,6 +105,18 @@ __device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float (&f)[4]) {
   f[3] = hi[1];
 }
 
+// gfx950's v_cvt_scalef32_pk_{f16,bf16}_fp8 widens two E4M3 bytes of a word (bytes 0-1, or
+// 2-3 with HI) straight to two 16-bit values, times the scale's power of two (1 here): one
+// instruction per pair.  fp16 and bf16 both hold every E4M3 value (subnormals included)
+// exactly.
+template <bool BF16, bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_16(uint32_t w) {
+  if constexpr (BF16)
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, HI));
+  else
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.f, HI));
+}
+
 // The E4M3 code of an fp32 value: round to nearest, ties to even; magnitudes from 448 up
 // saturate to 448, NaN stays NaN.  Bit arithmetic on the fp32 encoding.
 __device__ __forceinline__ uint32_t f32_to_fp8(float f) {

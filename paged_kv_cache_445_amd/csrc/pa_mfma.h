@@ -73,16 +73,10 @@ __device__ __forceinline__ typename MfmaRaw<DT>::type ld_raw(const char* p) {
 template <int DT>
 __device__ __forceinline__ op8_t<DT> operand(const typename MfmaRaw<DT>::type& r) {
   if constexpr (is_fp8(DT)) {
-    using E = typename std::conditional<bf16_core<DT>(), __bf16, _Float16>::type;
-    float f[4];
-    op8_t<DT> o;
-    fp8x4_to_f32(r.x, f);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = (E)f[i];
-    fp8x4_to_f32(r.y, f);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) o[4 + i] = (E)f[i];
-    return o;
+    constexpr bool BF = bf16_core<DT>();
+    const uint4 o = {fp8x2_to_16<BF, false>(r.x), fp8x2_to_16<BF, true>(r.x),
+                     fp8x2_to_16<BF, false>(r.y), fp8x2_to_16<BF, true>(r.y)};
+    return __builtin_bit_cast(op8_t<DT>, o);
   } else {
     return __builtin_bit_cast(op8_t<DT>, r);
   }

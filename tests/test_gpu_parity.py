@@ -712,6 +712,61 @@ def test_fp8_saturation_and_small_scales(dev):
     parity(dev, _fp8(b, k_scale=1.0 / 256, v_scale=0.75), out_f32=False)
 
 
+@pytest.mark.parametrize("qdt,Hq,Hkv,rows", [("f16", 4, 4, 1), ("bf16", 4, 4, 1),
+                                              ("f16", 16, 4, 1), ("bf16", 16, 4, 1),
+                                              ("f16", 16, 4, 40), ("bf16", 8, 8, 40)])
+def test_fp8_every_code(dev, qdt, Hq, Hkv, rows):
+    """Every non-NaN E4M3 code widened by each path (vector decode for MHA, matrix-core decode
+    for GQA, the chunk tile for 40-row sequences): pools written byte by byte, the first
+    key's V row holding all 254 codes (and their negations' order reversed in the second
+    sequence).  A row that sees one key returns v_scale times that key's V row, so those rows
+    are compared to 1e-6 relative; the other rows to the usual tolerance."""
+    import torch
+    import oracle
+    from paged_kv_cache_445_amd import pa
+    from paged_kv_cache_445_amd.device_batch import TORCH_DTYPE, to_device
+    _log(f"[fp8_every_code] {qdt} Hq={Hq} Hkv={Hkv} rows={rows}")
+    rng = np.random.default_rng(2150 + Hq + rows)
+    S, D, NB = 2, 128, 8
+    MB = 4
+    codes = np.array([c for c in range(256) if c & 0x7F != 0x7F], dtype=np.uint8)
+    kp = rng.choice(codes, size=(NB, Hkv, D // 16, 16, 16)).astype(np.uint8)
+    vp = rng.choice(codes, size=(NB, Hkv, D, 16)).astype(np.uint8)
+    for s in range(S):  # block s holds the first key of sequence s
+        cyc = np.resize(codes if s == 0 else codes[::-1], Hkv * D)
+        vp[s, :, :, 0] = cyc.reshape(Hkv, D)
+    bt = np.zeros((S, MB), dtype=np.int32)
+    bt[:, 0] = np.arange(S)
+    bt[:, 1:] = (np.arange(S)[:, None] * (MB - 1) + np.arange(1, MB)[None, :]) % (NB - S) + S
+    lens = np.full(S, rows, dtype=np.int32)
+    qsl = np.arange(S + 1, dtype=np.int32) * rows
+    k_scale, v_scale = 1.0 / 2048, 1.0 / 448
+    q = W.to_storage(rng.standard_normal((S * rows, Hq, D)).astype(np.float32), qdt)
+    g = pa.geom(S, Hq, Hkv, D, NB, MB, pa.PA_FP8_E4M3, torch.float32, q_dtype=TORCH_DTYPE[qdt],
+                k_scale=k_scale, v_scale=v_scale)
+    out = torch.zeros((S * rows, Hq, D), dtype=torch.float32, device="cuda")
+    ws = torch.zeros(pa.workspace_size(g, S * rows), dtype=torch.uint8, device="cuda")
+    scale = float(np.float32(1 / np.sqrt(D)))
+    pa.decode(out, to_device(q, qdt, "cuda"), torch.from_numpy(kp).cuda(),
+              torch.from_numpy(vp).cuda(), torch.from_numpy(bt).cuda(),
+              torch.from_numpy(lens).cuda(), torch.from_numpy(qsl).cuda(), scale, ws, g,
+              max_query_len=rows)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    og = oracle.make_geom(S, Hq, Hkv, D, NB, MB, "fp8", q_dtype=qdt, k_scale=k_scale,
+                          v_scale=v_scale)
+    want, _ = oracle.paged_attention(q, kp, vp, bt, lens, qsl, scale, og)
+    first = qsl[:-1]  # the rows that see one key
+    G = Hq // Hkv
+    for s, r in enumerate(first):
+        exact = np.array([[oracle.fp8_decode(int(c)) * v_scale for c in vp[s, h // G, :, 0]]
+                          for h in range(Hq)])
+        assert np.array_equal(want[r], exact)
+        err = np.abs(got[r] - exact)
+        assert (err <= 1e-6 * np.abs(exact)).all(), f"row {r}: max err {err.max():.3e}"
+    check_out(got, want, TOL["f16"], "every code")
+
+
 def test_fp8_many_sequences(dev):
     """300 sequences: split segments merged in-kernel, 2, 4 or 8 heads per wave (contexts
     kept short: the oracle quantises every element of the history)."""
