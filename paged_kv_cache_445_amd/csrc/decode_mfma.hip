@@ -44,14 +44,22 @@ __device__ void mfma_attend(const DecodeArgs& a, int s, int g, int u0, int u1, i
   const int hc = MULTI ? n - jr * G : n;
   if constexpr (MULTI) nr = __builtin_amdgcn_readfirstlane(nr);
 
+  // Scores are formed with the factor sl > 0: a negative factor is folded into q (sign flips
+  // are exact) and a zero factor makes every score 0 (q = 0, factor 1).
+  const float sl = a.scale_log2 == 0.f ? 1.f : fabsf(a.scale_log2);
+  const uint32_t qflip = a.scale_log2 < 0.f ? 0x80008000u : 0u;
   T qb[C::NKK];
   {
     const char* qp = reinterpret_cast<const char*>(a.q) +
                      ((int64_t)(row0 + jr) * a.num_q_heads + (int64_t)g * G + hc) * D * 2;
-    const bool live = MULTI ? jr < nr : n < G;
+    const bool live = (MULTI ? jr < nr : n < G) && a.scale_log2 != 0.f;
 #pragma unroll
     for (int kk = 0; kk < C::NKK; ++kk) {
-      const uint4 v = live ? ld16(qp + (4 * kk + r) * 16) : make_uint4(0, 0, 0, 0);
+      uint4 v = live ? ld16(qp + (4 * kk + r) * 16) : make_uint4(0, 0, 0, 0);
+      v.x ^= qflip;
+      v.y ^= qflip;
+      v.z ^= qflip;
+      v.w ^= qflip;
       qb[kk] = __builtin_bit_cast(T, v);
     }
   }
@@ -64,9 +72,9 @@ __device__ void mfma_attend(const DecodeArgs& a, int s, int g, int u0, int u1, i
     mfma_stream<DT, D, B8>(a, s, g, u0, u1, ctx, [&](MfmaK<DT, D>& kb, MfmaV<DT, D>& vb, int u) {
       const int valid = ctx - u * kMfmaUnit;
       if (valid >= kMfmaUnit)
-        mfma_unit<DT, D, false, false>(st, kb, vb, qb, a.scale_log2, kMfmaUnit - 1, kMfmaUnit);
+        mfma_unit<DT, D, false, false>(st, kb, vb, qb, sl, kMfmaUnit - 1, kMfmaUnit);
       else
-        mfma_unit<DT, D, true, false>(st, kb, vb, qb, a.scale_log2, valid - 1, valid);
+        mfma_unit<DT, D, true, false>(st, kb, vb, qb, sl, valid - 1, valid);
     });
   } else {
     const int last0 = ctx - nr;                 // last visible key of the first row
@@ -74,9 +82,9 @@ __device__ void mfma_attend(const DecodeArgs& a, int s, int g, int u0, int u1, i
     auto scores = [&](MfmaK<DT, D>& kb, int u) {
       const int t0 = u * kMfmaUnit;
       if (last0 - t0 >= kMfmaUnit - 1)  // every column sees the whole unit
-        return mfma_scores<DT, D, false, false>(st, kb, qb, a.scale_log2, kMfmaUnit - 1);
+        return mfma_scores<DT, D, false, false>(st, kb, qb, sl, kMfmaUnit - 1);
       // per-column limits; a column may see no key of this piece yet
-      return mfma_scores<DT, D, true, true>(st, kb, qb, a.scale_log2, mine - t0);
+      return mfma_scores<DT, D, true, true>(st, kb, qb, sl, mine - t0);
     };
     auto pv = [&](MfmaV<DT, D>& vb, const MfmaP<DT>& p, int u) {
       const int t0 = u * kMfmaUnit;

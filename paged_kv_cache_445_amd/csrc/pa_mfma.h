@@ -146,9 +146,9 @@ __device__ __forceinline__ MfmaP<DT> mfma_scores(MfmaState<DT, D>& st, const Mfm
     s0 = mfma<DT>(operand<DT>(kb[0][kk]), qb[kk], s0);
     s1 = mfma<DT>(operand<DT>(kb[1][kk]), qb[kk], s1);
   }
-  // raw scores q . k; the scale enters through the exponent's fma, and the largest scaled
-  // score is the scale times the largest raw score (the smallest one for a negative scale)
-  const bool pos = scale_log2 >= 0.f;
+  // raw scores q . k; the scale (> 0: a negative or zero one is folded into q by the caller)
+  // enters through the exponent's fma, and the largest scaled score is the scale times the
+  // largest raw score
   float s[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -156,16 +156,14 @@ __device__ __forceinline__ MfmaP<DT> mfma_scores(MfmaState<DT, D>& st, const Mfm
     s[4 + i] = s1[i];
   }
   if (MASK) {
-    const float none = pos ? -INFINITY : INFINITY;  // scales to -inf: weight 0
 #pragma unroll
     for (int k = 0; k < 8; ++k)
-      if (8 * r + k > lim) s[k] = none;
+      if (8 * r + k > lim) s[k] = -INFINITY;  // weight 0
   }
   float ext = s[0];
 #pragma unroll
-  for (int k = 1; k < 8; ++k) ext = pos ? fmaxf(ext, s[k]) : fminf(ext, s[k]);
-  ext = pos ? cross_rows_max(ext) : -cross_rows_max(-ext);
-  const float mx = ext == (pos ? -INFINITY : INFINITY) ? -INFINITY : ext * scale_log2;
+  for (int k = 1; k < 8; ++k) ext = fmaxf(ext, s[k]);
+  const float mx = cross_rows_max(ext) * scale_log2;
   const float mnew = fmaxf(st.m, mx);
   // SAFE: a column with no visible key so far keeps m = -inf, weight 0, and alpha 1
   const float mref = (SAFE && mnew == -INFINITY) ? 0.f : mnew;

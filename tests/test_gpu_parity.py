@@ -667,6 +667,26 @@ def test_block_manager_scenario(dev, dtype, G):
     check_out(out.cpu().numpy().astype(np.float64), want, TOL[dtype], "block manager, shared prefix")
 
 
+@pytest.mark.parametrize("scale", [-0.3, 0.0])
+def test_negative_and_zero_scale(dev, scale):
+    """A negative softmax scale (the weights favour the smallest q . k) and a zero one
+    (uniform weights over the visible keys) on the vector decode (MHA), the matrix-core
+    decode (GQA decode rows, MHA verify rows, FP8 GQA), the chunk tile (40 rows) and the
+    fixed partitions."""
+    rng = np.random.default_rng(3100)
+    for dtype, Hq, Hkv, rows, fp8 in (("f16", 8, 8, 1, False), ("bf16", 16, 4, 1, False),
+                                      ("f16", 8, 8, 5, False), ("f16", 16, 2, 1, True),
+                                      ("bf16", 16, 4, 40, False)):
+        ctx = rng.integers(1, 1500, size=6) + rows
+        b = W.build_batch("scale_sign", dtype, ctx, np.full(6, rows), Hq, Hkv, 128, rng)
+        b.scale = np.float32(scale)
+        if fp8:
+            b = _fp8(b)
+        parity(dev, b)
+        if rows == 1:
+            check_partitioned(dev, b, 256)
+
+
 def test_spec_verify_long_split(dev):
     """Verify rows on long contexts cut into many pieces by the even split, with contexts
     whose last unit starts past the first rows' last keys (a piece may then hold no key of
