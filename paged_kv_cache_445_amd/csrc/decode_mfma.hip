@@ -165,8 +165,10 @@ __device__ void m_prefix_emit(const DecodeArgs& a, const MfmaState<DT, D>& st, i
 // the segment's last arrival, merge every piece and write the output (the segment's first
 // column at ob; with np > 0 folded with the shared-prefix partials of each column, the
 // segment's first row being row0).  Each lane merges its own column n and dimensions
-// 16 j + 4 r .. + 3, so no lanes interact.  Partial slots hold a.cols columns.
-template <int DT, int D, bool MULTI>
+// 16 j + 4 r .. + 3, so no lanes interact.  Partial slots hold a.cols columns.  The merge
+// loads MB pieces at a time (LEAN: one, which keeps it within the 256 registers of two waves
+// per SIMD).
+template <int DT, int D, bool MULTI, int MB>
 __device__ void m_split_finish(const DecodeArgs& a, const MfmaState<DT, D>& st, int ncols,
                                const SplitSeg& sg, int64_t self, int32_t* cnt, int seen,
                                int64_t ob, int row0, int g, int np) {
@@ -198,7 +200,7 @@ __device__ void m_split_finish(const DecodeArgs& a, const MfmaState<DT, D>& st, 
   }, [] {});
   if (!last) return;
   float M[1], L[1], U[1][NE];
-  merge_ordered<1, NE, 2>(M, L, U, sg.k0, sg.k1,
+  merge_ordered<1, NE, MB>(M, L, U, sg.k0, sg.k1,
                           [&](int64_t k, float (&m)[1], float (&lk)[1], float (&ov)[1][NE]) {
     if (k == self || !col) {
       m[0] = mine_m;
@@ -301,7 +303,7 @@ mfma_decode_kernel(DecodeArgs a) {
             mfma_emit<DT, D>(st, nr * G, nullptr, nullptr, nullptr, D, a.out, ob, MULTI ? G : 16,
                              (int64_t)a.num_q_heads * D, D, a.out_f32);
           else
-            m_split_finish<DT, D, MULTI>(a, st, nr * G, sg, o, cnt, seen, ob, row, g, np);
+            m_split_finish<DT, D, MULTI, LEAN ? 1 : 2>(a, st, nr * G, sg, o, cnt, seen, ob, row, g, np);
         }
         i = pe;
       }
