@@ -105,6 +105,37 @@ __global__ __launch_bounds__(kReshapeThreads) void reshape_and_cache_kernel(Resh
   __shared__ int seg_t[kMaxTile + 1];  // first token (offset from t0) of each segment
   __shared__ int seg_c[kMaxTile + 1];  // tokens of the segments before it
   __shared__ int nseg;
+  __shared__ int in_order;  // the workgroup writes tokens t0, t0 + 1, .. t0 + Ms - 1 in order
+  const char* key = static_cast<const char*>(a.key);
+  const char* val = static_cast<const char*>(a.value);
+  const int64_t row_in = (int64_t)D * R::IE;  // bytes of one (token, head) input row
+  constexpr int KU = 2, VU = 8;
+
+  // Loads issued before the slots are known: decode tokens (one-token segments) and chunks
+  // whose segments start at t0 make the workgroup write tokens t0 .. t0 + Ms - 1 in order,
+  // the j-th at offset j, so each thread loads its pieces of that order (K chunk c of token
+  // j: piece c Ms + j; V dimension d: piece d Ms + j) beside the slot loads and keeps them
+  // when the segment scan finds that order; otherwise the pieces are loaded again below.
+  const int Ms = (int)min((int64_t)T, a.num_tokens - t0);
+  uint4 kpre[KU];
+  uint32_t vpre[VU];
+#pragma unroll
+  for (int u = 0; u < KU; ++u) {
+    const int i = u * kReshapeThreads + tid;
+    if (i < NCH * Ms) {
+      const int c = i / Ms, j = i - c * Ms;
+      kpre[u] = pool_chunk<DT>(key + ((t0 + j) * H + g) * row_in + (int64_t)c * R::X * R::IE,
+                               a.k_scale);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < VU; ++u) {
+    const int i = u * kReshapeThreads + tid;
+    if (i < D * Ms) {
+      const int d = i / Ms, j = i - d * Ms;
+      vpre[u] = load_elem<DT>(val + ((t0 + j) * H + g) * row_in + (int64_t)d * R::IE);
+    }
+  }
   if (tid < kWave) {
     const int64_t t = t0 - 1 + tid;
     const int64_t s = tid < 2 * T && t >= 0 && t < a.num_tokens ? a.slot_mapping[t] : -1;
@@ -132,15 +163,44 @@ __global__ __launch_bounds__(kReshapeThreads) void reshape_and_cache_kernel(Resh
       seg_t[k] = tid - 1;
       seg_c[k] = incl - len;
     }
+    // in order: every segment starts where the ones before it end, and they hold Ms tokens
+    const uint64_t gaps = __builtin_amdgcn_ballot_w64(start && tid - 1 != incl - len);
     if (tid == kWave - 1) {
       nseg = __popcll(starts);
       seg_c[__popcll(starts)] = incl;  // every token of the workgroup
+      in_order = gaps == 0 && incl == Ms;
     }
   }
   __syncthreads();
   const int ns = nseg;
   const int M = seg_c[ns];  // tokens this workgroup writes
   if (M == 0) return;
+  char* kc = static_cast<char*>(a.k_cache);
+  char* vc = static_cast<char*>(a.v_cache);
+  if (in_order && NCH * M <= KU * kReshapeThreads && D * M <= VU * kReshapeThreads) {
+    // token j at offset j: the pieces loaded above, stored at their slots
+#pragma unroll
+    for (int u = 0; u < KU; ++u) {
+      const int i = u * kReshapeThreads + tid;
+      if (i < NCH * M) {
+        const int c = i / M, j = i - c * M;
+        const int64_t slot = sl[j + 1];
+        const int64_t dst = ((((slot >> shift) * H + g) * NCH + c) << shift) + (slot & (T - 1));
+        store16(kc + dst * 16, kpre[u]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < VU; ++u) {
+      const int i = u * kReshapeThreads + tid;
+      if (i < D * M) {
+        const int d = i / M, j = i - d * M;
+        const int64_t slot = sl[j + 1];
+        const int64_t dst = ((((slot >> shift) * H + g) * D + d) << shift) + (slot & (T - 1));
+        store_elem<DT>(vc + dst * R::OE, pool_elem<DT>(vpre[u], a.v_scale));
+      }
+    }
+    return;
+  }
   // j-th token of the workgroup (segments in order): its offset from t0 and its slot
   auto token = [&](int j, int& off, int64_t& slot) {
     int k = 0, hi = ns - 1;  // the last segment with seg_c[k] <= j
@@ -154,14 +214,7 @@ __global__ __launch_bounds__(kReshapeThreads) void reshape_and_cache_kernel(Resh
     off = seg_t[k] + (j - seg_c[k]);
     slot = sl[off + 1];
   };
-  const char* key = static_cast<const char*>(a.key);
-  const char* val = static_cast<const char*>(a.value);
-  char* kc = static_cast<char*>(a.k_cache);
-  char* vc = static_cast<char*>(a.v_cache);
-  const int64_t row_in = (int64_t)D * R::IE;  // bytes of one (token, head) input row
-
   // K: chunk c of token j is piece c * M + j
-  constexpr int KU = 2, VU = 8;
   for (int i0 = 0; i0 < NCH * M; i0 += KU * kReshapeThreads) {
     uint4 v[KU];
     int64_t dst[KU];
