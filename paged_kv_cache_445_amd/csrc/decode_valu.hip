@@ -63,9 +63,9 @@ template <int DT, int D>
 __device__ __forceinline__ void v_issue(VTile<DT, D>& t, const char* kt, const char* vt, int off) {
   using C = VCfg<DT, D>;
 #pragma unroll
-  for (int i = 0; i < C::NK; ++i) t.k[i] = ld16(kt + off + 1024 * i);
+  for (int i = 0; i < C::NK; ++i) t.k[i] = ld16_nt(kt + off + 1024 * i);
 #pragma unroll
-  for (int j = 0; j < C::NV; ++j) t.v[j] = ld16(vt + off + 1024 * j);
+  for (int j = 0; j < C::NV; ++j) t.v[j] = ld16_nt(vt + off + 1024 * j);
 }
 
 // 8-token blocks: tokens 0-7 of a 16-token tile come from block tile (ka, va), tokens 8-15
@@ -81,7 +81,7 @@ __device__ __forceinline__ void v_issue_b8(VTile<DT, D>& t, const char* ka, cons
   const char* kt = (lane & 8) ? kb : ka;
   const int koff = (lane >> 4) * 128 + (lane & 7) * 16;
 #pragma unroll
-  for (int i = 0; i < C::NK; ++i) t.k[i] = ld16(kt + koff + 512 * i);
+  for (int i = 0; i < C::NK; ++i) t.k[i] = ld16_nt(kt + koff + 512 * i);
   if constexpr (C::E == 1) {
 #pragma unroll
     for (int j = 0; j < C::NV; ++j) {
@@ -92,12 +92,12 @@ __device__ __forceinline__ void v_issue_b8(VTile<DT, D>& t, const char* ka, cons
   } else if constexpr (C::E == 2) {
     const char* vt = (lane & 1) ? vb : va;
 #pragma unroll
-    for (int j = 0; j < C::NV; ++j) t.v[j] = ld16(vt + 512 * j + (lane >> 1) * 16);
+    for (int j = 0; j < C::NV; ++j) t.v[j] = ld16_nt(vt + 512 * j + (lane >> 1) * 16);
   } else {
     const char* vt = ((lane >> 1) & 1) ? vb : va;
 #pragma unroll
     for (int j = 0; j < C::NV; ++j)
-      t.v[j] = ld16(vt + 512 * j + (lane >> 2) * 32 + (lane & 1) * 16);
+      t.v[j] = ld16_nt(vt + 512 * j + (lane >> 2) * 32 + (lane & 1) * 16);
   }
 }
 

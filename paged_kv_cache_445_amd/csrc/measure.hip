@@ -1,6 +1,7 @@
 // measure.hip — HBM read ceilings the benchmark compares the decode kernels with.  Not part
 // of the attention path: two read-only kernels that fetch bytes and fold them into a sink
-// so that the loads cannot be dropped.
+// so that the loads cannot be dropped.  Both load with the streaming (non-temporal) policy,
+// as the decode kernels do.
 //
 //  - stream: one contiguous buffer read in 16 KiB pieces, one per wave at a time with all 16
 //    of its one-KiB loads in flight, pieces striding over the buffer (the best case for HBM).
@@ -20,6 +21,12 @@ constexpr int kThreads = 256;
 
 __device__ __forceinline__ uint32_t fold(const uint4& v) { return v.x ^ v.y ^ v.z ^ v.w; }
 
+__device__ __forceinline__ uint4 ld_stream(const char* p) {
+  typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 // Each wave reads a contiguous 16 KiB piece per iteration (16 loads of one KiB in flight),
 // pieces handed out with a grid stride; the tail (bytes past the last whole piece) is read
 // 16 bytes per lane.
@@ -37,12 +44,12 @@ __global__ __launch_bounds__(kThreads) void stream_read_kernel(const char* p, in
     const char* q = p + k * kPiece + 16 * lane;
     uint4 v[kPieceLoads];
 #pragma unroll
-    for (int i = 0; i < kPieceLoads; ++i) v[i] = *reinterpret_cast<const uint4*>(q + 1024 * i);
+    for (int i = 0; i < kPieceLoads; ++i) v[i] = ld_stream(q + 1024 * i);
 #pragma unroll
     for (int i = 0; i < kPieceLoads; ++i) acc ^= fold(v[i]);
   }
   for (int64_t e = pieces * kPiece + (w * 64 + lane) * 16; e < bytes; e += W * 64 * 16)
-    acc ^= fold(*reinterpret_cast<const uint4*>(p + e));
+    acc ^= fold(ld_stream(p + e));
   // a store that practically never happens keeps every load alive
   if (acc == 0x9E3779B9u) sink[blockIdx.x] = acc;
 }
@@ -68,7 +75,7 @@ __global__ __launch_bounds__(kThreads) void tile_read_kernel(const char* base, c
       for (int j = 0; j < kTilesInFlight; ++j) {
         const char* a = base + off[t + j] + 16 * lane;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) v[j][k] = *reinterpret_cast<const uint4*>(a + 1024 * k);
+        for (int k = 0; k < 4; ++k) v[j][k] = ld_stream(a + 1024 * k);
       }
 #pragma unroll
       for (int j = 0; j < kTilesInFlight; ++j)
@@ -78,7 +85,7 @@ __global__ __launch_bounds__(kThreads) void tile_read_kernel(const char* base, c
   }
   for (; t < t1; ++t) {
     const char* a = base + off[t] + 16 * lane;
-    for (int k = 0; k < loads; ++k) acc ^= fold(*reinterpret_cast<const uint4*>(a + 1024 * k));
+    for (int k = 0; k < loads; ++k) acc ^= fold(ld_stream(a + 1024 * k));
   }
   if (acc == 0x9E3779B9u) sink[blockIdx.x] = acc;
 }

@@ -114,17 +114,21 @@ int wg_per_cu_override() {
 }
 
 // Per mille of the even split's work moved from the workgroups on odd XCDs to those on even
-// XCDs (see make_part).  On gfx950 the odd XCDs finish the decode's random 4 KiB tile reads
-// about 7% later than the even ones, whichever data they are given (measured per XCD with
-// the kernel's own read pattern); a sweep of this shift put the shortest decode at 5 to
-// 6.5%.  Optional override for tuning.
-constexpr int kOddSkew = 55;
-int odd_skew() {
+// XCDs (see make_part).  With cached loads the odd XCDs finished the decode's random 4 KiB
+// tile reads about 7% later than the even ones; with the streaming loads the decode now uses,
+// a sweep (0 / 20-30 / 55 / 80-100) puts the shortest call at 55 for the vector kernel on
+// 16-bit pools (LLaMA-7B 97.3 / 95.7 / 95.3 / 96.0 us; shared prefix 190.4 / 189.0 /
+// 187.3 us) and at 0 for FP8 pools on it (54.6 / 54.8 / 55.6 us) and for the matrix-core
+// kernel (GQA 238.5 / 241.9 / 246.6 us, verify 107.6 / 108.7 / 110.6 us).  Optional
+// override for tuning.
+constexpr int kOddSkewVector16 = 55;
+int odd_skew(const pa_geom* g, int path) {
   static const int v = [] {
     const char* s = getenv("PA_DECODE_ODD_SKEW");
     return s ? atoi(s) : -1;
   }();
-  return v >= 0 ? v : kOddSkew;
+  if (v >= 0) return v;
+  return path == 0 && g->kv_dtype != PA_FP8_E4M3 ? kOddSkewVector16 : 0;
 }
 
 // The vector kernel's even split in (head group, sequence, tile) order over XCD-major
@@ -655,7 +659,7 @@ pa_status decode_impl(void* out, const void* q, const void* k_cache, const void*
   a.seg_extra = seg_extra_override() >= 0 ? seg_extra_override() : seg_extra_default(g, rt.path);
   a.heads_per_wave = rt.path == 0 ? heads_per_wave(g, wg) : 1;
   a.xcd_major = xcd_major_override() > 0 ? 1 : 0;
-  a.odd_skew = odd_skew();
+  a.odd_skew = odd_skew(g, rt.path);
   a.max_rows = rt.max_rows;
   a.cols = rt.cols;
   a.blk_shift = blk_shift(g);

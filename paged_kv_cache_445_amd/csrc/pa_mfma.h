@@ -65,9 +65,18 @@ struct MfmaRaw<DT_FP8B> {
   using type = uint2;
 };
 
+// an operand's raw bytes, loaded with the streaming (non-temporal) policy: the decode reads
+// every K and V tile once per call
 template <int DT>
 __device__ __forceinline__ typename MfmaRaw<DT>::type ld_raw(const char* p) {
-  return *reinterpret_cast<const typename MfmaRaw<DT>::type*>(p);
+  using R = typename MfmaRaw<DT>::type;
+  if constexpr (sizeof(R) == 16) {
+    return ld16_nt(p);
+  } else {
+    typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_nt;
+    const u32x2_nt v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_nt*>(p));
+    return R{v[0], v[1]};
+  }
 }
 
 template <int DT>
