@@ -88,11 +88,12 @@ int cu_count() {
 // is worth twice as many units over FP8 pools (half the bytes per unit).  Vector path
 // (16-token tiles): 4 for 16-bit pools (LLaMA-7B batch 107.1 -> 106.6 us against 2), 8 for
 // FP8 (63.2 -> 60.8 us), 2 for fp32.  Matrix-core path (32-token units): 1 for 16-bit (the
-// GQA batch is best at 1), 2 for FP8 (GQA FP8 batch 153.3 -> 147.2 us).  Optional override
-// for tuning.
+// GQA batch is best at 1), 4 for FP8 (GQA FP8 batch 153.3 -> 147.2 us at 2 against 1; with
+// streaming tile loads the verify rows take 67.2 / 66.2 / 66.5 us at 2 / 4 / 6 and the GQA
+// batch 133.1 / 133.2 / 134.2 us).  Optional override for tuning.
 int seg_extra_default(const pa_geom* g, int path) {
   const bool f8 = g->kv_dtype == PA_FP8_E4M3;
-  if (path) return f8 ? 2 : 1;
+  if (path) return f8 ? 4 : 1;
   return g->kv_dtype == PA_F32 ? 2 : f8 ? 8 : 4;
 }
 int seg_extra_override() {
